@@ -1,0 +1,100 @@
+// Device-side building blocks of the decode megakernel (gfx950 / CDNA4).
+//
+//  * buffer-resource loads and stores with explicit cache policy;
+//  * the cross-workgroup visibility protocol;
+//  * hierarchical sync counters with a bounded wait;
+//  * the MFMA weight-streaming GEMV engine.
+//
+// Cross-workgroup data protocol.  Every value that one workgroup produces
+// for another (normalised activations, partial sums of squares, q/k/v,
+// attention partials, argmax candidates, router results) is written with a
+// device-coherent store (cache policy sc1: written through to the device
+// coherence point) and read with a device-coherent load (sc1: never served
+// from a stale copy in another XCD's L2).  A producer waits until its stores
+// have completed (s_waitcnt vmcnt(0)) before it increments a sync counter;
+// a consumer reads the data only after it has observed the counter.  Because
+// no cross-workgroup value ever sits dirty in an L2, no L2 write-back or
+// invalidate (the costly part of an agent-scope fence on this part) is needed.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace md {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr int NT = 256;      // threads per workgroup (4 waves of 64)
+constexpr int NW = 4;        // waves per workgroup
+constexpr int MAXB = 8;      // token rows per step (batch, or verify tokens)
+constexpr unsigned OOB = 0xFFFFFFF0u;  // buffer offset beyond any resource: loads return 0
+
+// cache-policy bits of buffer instructions on gfx950
+constexpr int CP_NT = 2;     // streaming (non-temporal)
+constexpr int CP_SC1 = 16;   // device scope: coherent across XCDs
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0]|expcnt[6:4]|lgkmcnt[11:8]|vmcnt_hi[15:14])
+constexpr int WAIT_VM0 = 0x0F70;
+constexpr int WAIT_LGKM0 = 0xC07F;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// ---- coherent scalar access (32-bit) through a resource
+__device__ __forceinline__ float ld_f32(rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CP_SC1));
+}
+__device__ __forceinline__ void st_f32(rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, CP_SC1);
+}
+__device__ __forceinline__ uint32_t ld_u32(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CP_SC1);
+}
+__device__ __forceinline__ void st_u32(rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, CP_SC1);
+}
+__device__ __forceinline__ void st_u16(rsrc_t r, uint32_t off, uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, CP_SC1);
+}
+template <int CP>
+__device__ __forceinline__ i32x4 ld_x4(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CP);
+}
+
+// ---- bf16 helpers
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi): about 16 significant bits.
+__device__ __forceinline__ void split_hilo(float x, uint16_t& hi, uint16_t& lo) {
+  hi = bf16_rne(x);
+  lo = bf16_rne(x - bf16_f32(hi));
+}
+
+// ---- wave reductions (fixed order, deterministic)
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ void wait_stores() {
+  __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+}  // namespace md

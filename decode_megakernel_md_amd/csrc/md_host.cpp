@@ -1,0 +1,416 @@
+// Host side of libmd.so: the C ABI declared in md.h.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "md.h"
+#include "md_model.h"
+
+namespace md {
+size_t megakernel_smem_bytes();
+hipError_t launch_megakernel(const Params& p, int grid, hipStream_t stream);
+hipError_t megakernel_occupancy(int* blocks_per_cu);
+}  // namespace md
+
+using namespace md;
+
+namespace {
+
+thread_local std::string g_err;
+
+md_status fail(md_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+constexpr int MAXB_ = 8;
+constexpr int GMAX = 1024;        // largest grid the workspace is sized for
+constexpr int CMAX = 256;         // largest number of KV chunks per (sequence, kv head)
+constexpr int SP_WORDS_ = 9 * 32;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Tensor {
+  std::string name;
+  int64_t rows, cols;
+};
+
+bool is_mla(const md_config* c, int l) { return c->attn_kind == 1 && (l % c->mla_every) == c->mla_every - 1; }
+
+// The weight inventory, in the order the caller passes pointers.
+std::vector<Tensor> inventory(const md_config* c) {
+  std::vector<Tensor> T;
+  auto mat = [&](std::string n, int64_t r, int64_t k) { T.push_back({n, r, k}); };
+  int64_t H = c->hidden;
+  mat("embed", c->vocab, H);
+  for (int l = 0; l < c->n_layers; ++l) {
+    std::string p = "L" + std::to_string(l) + ".";
+    mat(p + "attn_norm", 1, H);
+    if (c->attn_kind == 0) {
+      mat(p + "wq", (int64_t)c->n_q_heads * c->head_dim, H);
+      mat(p + "wk", (int64_t)c->n_kv_heads * c->head_dim, H);
+      mat(p + "wv", (int64_t)c->n_kv_heads * c->head_dim, H);
+      mat(p + "wo", H, (int64_t)c->n_q_heads * c->head_dim);
+    } else if (is_mla(c, l)) {
+      mat(p + "mla_wqa", c->q_lora, H);
+      mat(p + "mla_q_norm", 1, c->q_lora);
+      mat(p + "mla_wqb", (int64_t)c->mla_heads * (c->nope_dim + c->rope_dim), c->q_lora);
+      mat(p + "mla_wkva", c->kv_lora + c->rope_dim, H);
+      mat(p + "mla_kv_norm", 1, c->kv_lora);
+      mat(p + "mla_wkvb", (int64_t)c->mla_heads * (c->nope_dim + c->v_dim), c->kv_lora);
+      mat(p + "mla_wo", H, (int64_t)c->mla_heads * c->v_dim);
+    } else {
+      mat(p + "kda_wq", (int64_t)c->kda_heads * c->kda_dk, H);
+      mat(p + "kda_wk", (int64_t)c->kda_heads * c->kda_dk, H);
+      mat(p + "kda_wv", (int64_t)c->kda_heads * c->kda_dv, H);
+      mat(p + "kda_walpha", c->kda_heads, H);
+      mat(p + "kda_wbeta", c->kda_heads, H);
+      mat(p + "kda_wo", H, (int64_t)c->kda_heads * c->kda_dv);
+    }
+    mat(p + "ffn_norm", 1, H);
+    if (c->n_experts == 0) {
+      mat(p + "w_gate", c->ffn_dim, H);
+      mat(p + "w_up", c->ffn_dim, H);
+      mat(p + "w_down", H, c->ffn_dim);
+    } else {
+      mat(p + "router", c->n_experts, H);
+      for (int s = 0; s < c->n_shared; ++s) {
+        std::string q = p + "sh" + std::to_string(s) + "_";
+        mat(q + "gate", c->shared_ffn, H);
+        mat(q + "up", c->shared_ffn, H);
+        mat(q + "down", H, c->shared_ffn);
+      }
+      for (int e = 0; e < c->n_experts; ++e) {
+        std::string q = p + "e" + std::to_string(e) + "_";
+        mat(q + "gate", c->expert_ffn, H);
+        mat(q + "up", c->expert_ffn, H);
+        mat(q + "down", H, c->expert_ffn);
+      }
+    }
+  }
+  mat("final_norm", 1, H);
+  mat("lm_head", c->vocab, H);
+  return T;
+}
+
+md_status validate(const md_config* c) {
+  if (!c) return fail(MD_EINVAL, "config is NULL");
+  if (c->flags != 0) return fail(MD_EINVAL, "flags must be 0");
+  if (c->n_layers < 1 || c->hidden < 32 || c->vocab < 1 || c->max_ctx < 1)
+    return fail(MD_EINVAL, "n_layers, hidden, vocab and max_ctx must be positive");
+  if (c->max_batch < 1 || c->max_batch > MAXB_) return fail(MD_EINVAL, "max_batch must be in [1, 8]");
+  if (c->hidden % 32) return fail(MD_EUNSUPPORTED, "hidden must be a multiple of 32");
+  if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f)) return fail(MD_EINVAL, "rms_eps and rope_theta must be > 0");
+  if (c->attn_kind == 0) {
+    if (c->n_q_heads < 1 || c->n_kv_heads < 1 || c->n_q_heads % c->n_kv_heads)
+      return fail(MD_EINVAL, "n_q_heads must be a positive multiple of n_kv_heads");
+    if (c->n_q_heads / c->n_kv_heads > 8) return fail(MD_EUNSUPPORTED, "at most 8 query heads per kv head");
+    if (c->head_dim != 64 && c->head_dim != 128) return fail(MD_EUNSUPPORTED, "head_dim must be 64 or 128");
+  } else if (c->attn_kind == 1) {
+    return fail(MD_EUNSUPPORTED, "hybrid MLA / delta-rule layers are not built yet");
+  } else {
+    return fail(MD_EINVAL, "attn_kind must be 0 or 1");
+  }
+  if (c->n_experts == 0) {
+    if (c->ffn_dim < 32 || c->ffn_dim % 32) return fail(MD_EUNSUPPORTED, "ffn_dim must be a positive multiple of 32");
+  } else {
+    return fail(MD_EUNSUPPORTED, "MoE layers are not built yet");
+  }
+  return MD_OK;
+}
+
+struct WsLayout {
+  size_t layers, experts, x, u, ssq, qkv, attn, ou, h, cand, sync, err, total;
+  int n_sync, sync_attn_base;
+};
+
+WsLayout ws_layout(const md_config* c) {
+  WsLayout w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  int64_t H = c->hidden;
+  int64_t nqkv = c->attn_kind == 0 ? (int64_t)(c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim : 0;
+  int64_t attn_out = c->attn_kind == 0 ? (int64_t)c->n_q_heads * c->head_dim : 0;
+  int64_t F = c->ffn_dim;
+  if (c->expert_ffn > F) F = c->expert_ffn;
+  if (c->shared_ffn > F) F = c->shared_ffn;
+  w.layers = take(sizeof(LayerDesc) * (size_t)c->n_layers);
+  w.experts = take(sizeof(void*) * 3 * (size_t)c->n_layers * (size_t)(c->n_experts > 0 ? c->n_experts : 1));
+  w.x = take(4 * MAXB_ * H);
+  w.u = take(2 * 2 * MAXB_ * H);
+  w.ssq = take(4 * (size_t)GMAX * MAXB_);
+  w.qkv = take(4 * MAXB_ * (size_t)nqkv);
+  w.attn = take(4 * (size_t)MAXB_ * (c->n_q_heads > 0 ? c->n_q_heads : 1) * CMAX * (size_t)(c->head_dim + 2));
+  w.ou = take(2 * 2 * MAXB_ * (size_t)attn_out);
+  w.h = take(2 * 2 * MAXB_ * (size_t)F);
+  w.cand = take(8 * (size_t)GMAX * MAXB_);
+  w.sync_attn_base = 1 + 5 * c->n_layers + 2;
+  w.n_sync = w.sync_attn_base + c->n_layers + 2;
+  w.sync = take(4 * 2 * (size_t)w.n_sync * SP_WORDS_);
+  w.err = take(256);
+  w.total = o;
+  return w;
+}
+
+std::vector<size_t> kv_offsets(const md_config* c, size_t* total) {
+  std::vector<size_t> off;
+  size_t o = 0;
+  for (int l = 0; l < c->n_layers; ++l) {
+    off.push_back(o);
+    size_t n;
+    if (c->attn_kind == 0)
+      n = 2 * 2 * (size_t)c->max_batch * c->n_kv_heads * c->max_ctx * c->head_dim;
+    else if (is_mla(c, l))
+      n = 2 * (size_t)c->max_batch * c->max_ctx * (c->kv_lora + c->rope_dim);
+    else
+      n = 4 * (size_t)c->max_batch * c->kda_heads * c->kda_dk * c->kda_dv;
+    o = align256(o + n);
+  }
+  if (total) *total = o;
+  return off;
+}
+
+}  // namespace
+
+struct md_model {
+  md_config cfg;
+  WsLayout lay;
+  std::vector<const void*> weights;
+  std::vector<size_t> kv_off;
+  uint8_t* ws = nullptr;
+  size_t ws_bytes = 0;
+  int grid = 0;
+  int bank = 0;
+  hipStream_t last_stream = nullptr;
+};
+
+extern "C" {
+
+const char* md_last_error(void) { return g_err.c_str(); }
+
+size_t md_weight_count(const md_config* cfg) {
+  if (!cfg || cfg->n_layers < 1) return 0;
+  return inventory(cfg).size();
+}
+
+md_status md_weight_info(const md_config* cfg, size_t i, char* name, size_t name_cap, int64_t* rows, int64_t* cols) {
+  if (!cfg) return fail(MD_EINVAL, "config is NULL");
+  auto T = inventory(cfg);
+  if (i >= T.size()) return fail(MD_EINVAL, "tensor index %zu out of range (%zu tensors)", i, T.size());
+  if (name && name_cap) {
+    strncpy(name, T[i].name.c_str(), name_cap - 1);
+    name[name_cap - 1] = 0;
+  }
+  if (rows) *rows = T[i].rows;
+  if (cols) *cols = T[i].cols;
+  return MD_OK;
+}
+
+size_t md_workspace_bytes(const md_config* cfg) {
+  if (validate(cfg) != MD_OK) return 0;
+  return ws_layout(cfg).total;
+}
+
+size_t md_kv_bytes(const md_config* cfg) {
+  if (validate(cfg) != MD_OK) return 0;
+  size_t t = 0;
+  kv_offsets(cfg, &t);
+  return t;
+}
+
+md_status md_init_model(const md_config* cfg, const void* const* weights, size_t n_weights, void* workspace,
+                        size_t workspace_bytes, void* hip_stream, md_model** out) {
+  if (!out) return fail(MD_EINVAL, "out is NULL");
+  *out = nullptr;
+  md_status st = validate(cfg);
+  if (st != MD_OK) return st;
+  auto T = inventory(cfg);
+  if (!weights || n_weights != T.size())
+    return fail(MD_EINVAL, "expected %zu weight pointers, got %zu", T.size(), n_weights);
+  for (size_t i = 0; i < T.size(); ++i) {
+    if (!weights[i]) return fail(MD_EINVAL, "weight %zu (%s) is NULL", i, T[i].name.c_str());
+    if ((uintptr_t)weights[i] & 15) return fail(MD_EINVAL, "weight %zu (%s) is not 16-byte aligned", i, T[i].name.c_str());
+    if (T[i].rows * T[i].cols * 2 > (int64_t)0xFFFFFFF0LL)
+      return fail(MD_EUNSUPPORTED, "weight %s exceeds 4 GiB", T[i].name.c_str());
+  }
+  WsLayout lay = ws_layout(cfg);
+  if (!workspace || ((uintptr_t)workspace & 255)) return fail(MD_EINVAL, "workspace must be non-NULL and 256-byte aligned");
+  if (workspace_bytes < lay.total) return fail(MD_ENOMEM, "workspace needs %zu bytes, got %zu", lay.total, workspace_bytes);
+  if (lay.total > 0xFFFFFF00ull) return fail(MD_EUNSUPPORTED, "workspace exceeds 4 GiB");
+  // device checks
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MD_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return fail(MD_EHIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(MD_EUNSUPPORTED, "device is %s; the kernels are built for gfx950", prop.gcnArchName);
+  if (!prop.cooperativeLaunch) return fail(MD_EUNSUPPORTED, "device lacks cooperative launch");
+  int per_cu = 0;
+  e = megakernel_occupancy(&per_cu);
+  if (e != hipSuccess) return fail(MD_EHIP, "occupancy query: %s", hipGetErrorString(e));
+  if (per_cu < 1) return fail(MD_EUNSUPPORTED, "megakernel does not fit on a CU");
+  int grid = prop.multiProcessorCount;
+  if (grid > GMAX) grid = GMAX;
+
+  md_model* m = new md_model();
+  m->cfg = *cfg;
+  m->lay = lay;
+  m->weights.assign(weights, weights + n_weights);
+  m->kv_off = kv_offsets(cfg, nullptr);
+  m->ws = (uint8_t*)workspace;
+  m->ws_bytes = workspace_bytes;
+  m->grid = grid;
+
+  // layer table
+  std::vector<LayerDesc> L(cfg->n_layers);
+  std::vector<const void*> ex;
+  size_t wi = 1;  // after embed
+  auto W = [&]() { return (const uint16_t*)weights[wi++]; };
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    LayerDesc& d = L[l];
+    memset(&d, 0, sizeof d);
+    d.kv_off = m->kv_off[l];
+    d.attn_norm = W();
+    if (cfg->attn_kind == 0) {
+      d.kind = LK_GQA;
+      d.wq = W(); d.wk = W(); d.wv = W(); d.wo = W();
+    } else if (is_mla(cfg, l)) {
+      d.kind = LK_MLA;
+      d.mla_wqa = W(); d.mla_qnorm = W(); d.mla_wqb = W(); d.mla_wkva = W(); d.mla_kvnorm = W();
+      d.mla_wkvb = W(); d.mla_wo = W();
+    } else {
+      d.kind = LK_KDA;
+      d.kda_wq = W(); d.kda_wk = W(); d.kda_wv = W(); d.kda_wa = W(); d.kda_wb = W(); d.kda_wo = W();
+    }
+    d.ffn_norm = W();
+    if (cfg->n_experts == 0) {
+      d.w_gate = W(); d.w_up = W(); d.w_down = W();
+    } else {
+      d.router = W();
+      if (cfg->n_shared > 0) { d.sh_gate = W(); d.sh_up = W(); d.sh_down = W(); }
+      for (int s = 1; s < cfg->n_shared; ++s) { W(); W(); W(); }
+      d.experts = (const uint16_t* const*)(m->ws + lay.experts) + (size_t)l * cfg->n_experts * 3;
+      for (int x = 0; x < cfg->n_experts * 3; ++x) ex.push_back(weights[wi++]);
+    }
+  }
+  hipStream_t s = (hipStream_t)hip_stream;
+  e = hipMemcpyAsync(m->ws + lay.layers, L.data(), sizeof(LayerDesc) * L.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && !ex.empty())
+    e = hipMemcpyAsync(m->ws + lay.experts, ex.data(), sizeof(void*) * ex.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemsetAsync(m->ws + lay.sync, 0, lay.err + 256 - lay.sync, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    delete m;
+    return fail(MD_EHIP, "uploading the layer table: %s", hipGetErrorString(e));
+  }
+  *out = m;
+  return MD_OK;
+}
+
+static md_status fill_params(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv,
+                             float* out_logits, int32_t batch, int32_t* out_tokens, int32_t* out_ids, Params& p) {
+  if (!m) return fail(MD_EINVAL, "model is NULL");
+  const md_config* c = &m->cfg;
+  if (batch < 1 || batch > c->max_batch) return fail(MD_EINVAL, "batch %d outside [1, %d]", batch, c->max_batch);
+  if (!tokens || !positions || !kv || !out_logits) return fail(MD_EINVAL, "tokens, positions, kv_cache and out_logits must be non-NULL");
+  if (((uintptr_t)kv & 255) || ((uintptr_t)out_logits & 3) || ((uintptr_t)tokens & 3) || ((uintptr_t)positions & 3))
+    return fail(MD_EINVAL, "misaligned pointer (kv_cache needs 256-byte alignment)");
+  memset(&p, 0, sizeof p);
+  const WsLayout& w = m->lay;
+  p.layers = (const LayerDesc*)(m->ws + w.layers);
+  p.embed = (const uint16_t*)m->weights.front();
+  p.final_norm = (const uint16_t*)m->weights[m->weights.size() - 2];
+  p.lm_head = (const uint16_t*)m->weights.back();
+  p.n_layers = c->n_layers; p.H = c->hidden; p.V = c->vocab; p.max_batch = c->max_batch; p.max_ctx = c->max_ctx;
+  p.eps = c->rms_eps; p.theta = c->rope_theta;
+  p.nq = c->n_q_heads; p.nkv = c->n_kv_heads; p.hd = c->head_dim;
+  p.ffn = c->ffn_dim;
+  p.n_experts = c->n_experts; p.top_k = c->top_k; p.expert_ffn = c->expert_ffn; p.n_shared = c->n_shared;
+  p.shared_ffn = c->shared_ffn; p.norm_topk = c->norm_topk;
+  p.B = batch;
+  int pairs = batch * (c->n_kv_heads > 0 ? c->n_kv_heads : 1);
+  int C = m->grid / pairs;
+  if (C < 1) C = 1;
+  if (C > CMAX) C = CMAX;
+  p.attn_chunks = C;
+  p.tokens = tokens; p.positions = positions; p.kv = (uint8_t*)kv; p.logits = out_logits;
+  p.out_tokens = out_tokens; p.out_ids = out_ids;
+  p.ws = m->ws; p.ws_bytes = (uint32_t)w.total;
+  p.x = (float*)(m->ws + w.x);
+  p.off_u = (uint32_t)w.u; p.off_ssq = (uint32_t)w.ssq; p.off_qkv = (uint32_t)w.qkv; p.off_attn = (uint32_t)w.attn;
+  p.off_ou = (uint32_t)w.ou; p.off_h = (uint32_t)w.h; p.off_cand = (uint32_t)w.cand;
+  p.sync = (unsigned*)(m->ws + w.sync);
+  p.err = (int*)(m->ws + w.err);
+  p.n_sync = w.n_sync;
+  p.sync_attn_base = w.sync_attn_base;
+  p.spin_limit = 1u << 22;
+  return MD_OK;
+}
+
+md_status md_decode_step(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv_cache,
+                         float* out_logits, int32_t batch, int32_t* out_tokens, int32_t* out_expert_ids,
+                         void* hip_stream) {
+  Params p;
+  md_status st = fill_params(m, tokens, positions, kv_cache, out_logits, batch, out_tokens, out_expert_ids, p);
+  if (st != MD_OK) return st;
+  p.bank = m->bank;
+  hipError_t e = launch_megakernel(p, m->grid, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(MD_EHIP, "megakernel launch: %s", hipGetErrorString(e));
+  m->bank ^= 1;
+  m->last_stream = (hipStream_t)hip_stream;
+  return MD_OK;
+}
+
+md_status md_decode_step_multilaunch(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv_cache,
+                                     float* out_logits, int32_t batch, int32_t* out_tokens, int32_t* out_expert_ids,
+                                     void* hip_stream) {
+  (void)m; (void)tokens; (void)positions; (void)kv_cache; (void)out_logits; (void)batch; (void)out_tokens;
+  (void)out_expert_ids; (void)hip_stream;
+  return fail(MD_EUNSUPPORTED, "multi-launch step is not built yet");
+}
+
+md_status md_verify_step(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv_cache,
+                         float* out_logits, int32_t* out_accept_len, int32_t* out_next_token, int32_t batch,
+                         int32_t n_tok, void* hip_stream) {
+  (void)m; (void)tokens; (void)positions; (void)kv_cache; (void)out_logits; (void)out_accept_len;
+  (void)out_next_token; (void)batch; (void)n_tok; (void)hip_stream;
+  return fail(MD_EUNSUPPORTED, "verify step is not built yet");
+}
+
+md_status md_get_device_status(md_model* m) {
+  if (!m) return fail(MD_EINVAL, "model is NULL");
+  hipError_t e = m->last_stream ? hipStreamSynchronize(m->last_stream) : hipDeviceSynchronize();
+  if (e != hipSuccess) return fail(MD_EHIP, "synchronise: %s", hipGetErrorString(e));
+  int err = 0;
+  e = hipMemcpy(&err, m->ws + m->lay.err, sizeof err, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(MD_EHIP, "reading the device error word: %s", hipGetErrorString(e));
+  if (err) {
+    int zero = 0;
+    hipMemcpy(m->ws + m->lay.err, &zero, sizeof zero, hipMemcpyHostToDevice);
+    // a failed step leaves its counter bank in an unknown state: clear both
+    hipMemset(m->ws + m->lay.sync, 0, (size_t)4 * 2 * m->lay.n_sync * SP_WORDS_);
+    hipDeviceSynchronize();
+    return fail(MD_EDEVICE, "device error 0x%x:%s%s%s", err, (err & MDE_WATCHDOG) ? " sync wait exceeded its bound" : "",
+                (err & MDE_TOKEN) ? " token out of range" : "", (err & MDE_POSITION) ? " position out of range" : "");
+  }
+  return MD_OK;
+}
+
+void md_free_model(md_model* m) { delete m; }
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Kernel parameter block and per-layer table of the decode megakernel.
+#pragma once
+#include <stdint.h>
+
+namespace md {
+
+// device error bits (md_get_device_status)
+enum : int { MDE_WATCHDOG = 1, MDE_TOKEN = 2, MDE_POSITION = 4 };
+
+enum LayerKind : int { LK_GQA = 0, LK_MLA = 1, LK_KDA = 2 };
+
+// One entry per layer, in device memory (the workspace).  Pointers are the
+// caller's bf16 weight tensors; unused ones are null.
+struct LayerDesc {
+  int kind;
+  int pad_;
+  uint64_t kv_off;  // byte offset of this layer's region in the KV / state buffer
+  const uint16_t* attn_norm;
+  // GQA
+  const uint16_t *wq, *wk, *wv, *wo;
+  // MLA
+  const uint16_t *mla_wqa, *mla_qnorm, *mla_wqb, *mla_wkva, *mla_kvnorm, *mla_wkvb, *mla_wo;
+  // KDA
+  const uint16_t *kda_wq, *kda_wk, *kda_wv, *kda_wa, *kda_wb, *kda_wo;
+  // FFN
+  const uint16_t* ffn_norm;
+  const uint16_t *w_gate, *w_up, *w_down;   // dense
+  const uint16_t* router;                   // MoE
+  const uint16_t *sh_gate, *sh_up, *sh_down;
+  const uint16_t* const* experts;           // [n_experts][3] gate, up, down (device array)
+};
+
+struct Params {
+  // model
+  const LayerDesc* layers;
+  const uint16_t* embed;
+  const uint16_t* final_norm;
+  const uint16_t* lm_head;
+  int n_layers, H, V, max_batch, max_ctx;
+  float eps, theta;
+  int nq, nkv, hd;
+  int ffn;
+  int n_experts, top_k, expert_ffn, n_shared, shared_ffn, norm_topk;
+  // step
+  int B;
+  int attn_chunks;
+  const int32_t* tokens;
+  const int32_t* positions;
+  uint8_t* kv;
+  float* logits;
+  int32_t* out_tokens;
+  int32_t* out_ids;
+  // workspace
+  uint8_t* ws;
+  uint32_t ws_bytes;
+  float* x;           // residual fp32[MAXB][H] (rows owned by their workgroup)
+  uint32_t off_u;     // hi/lo bf16[2][MAXB][H]  next norm input (gain folded, not yet scaled)
+  uint32_t off_ssq;   // fp32[G][MAXB] partial sums of squares of x
+  uint32_t off_qkv;   // fp32[MAXB][nq+2nkv][hd]
+  uint32_t off_attn;  // attention partials
+  uint32_t off_ou;    // hi/lo bf16[2][MAXB][nq*hd]
+  uint32_t off_h;     // hi/lo bf16[2][MAXB][F]
+  uint32_t off_cand;  // argmax candidates {f32, i32}[G][MAXB]
+  unsigned* sync;     // counters, 2 banks
+  int* err;
+  int n_sync;
+  int sync_attn_base;
+  int bank;
+  unsigned spin_limit;
+};
+
+}  // namespace md

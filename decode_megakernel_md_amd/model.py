@@ -1,0 +1,145 @@
+"""Device-side model: weights, workspace and KV / state buffers in HBM
+(allocated through PyTorch), handed to libmd.so.
+
+Inputs come from the seeded `synth` generator, drawn straight into device
+memory.  Nothing here computes any part of the decode step."""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, Optional
+
+import numpy as np
+
+import synth
+from synth.workloads import Workload, kv_layout, tensor_inventory
+
+from . import _lib
+from ._lib import check, config_from, lib
+
+
+def _align(x: int, a: int = 256) -> int:
+    return (x + a - 1) // a * a
+
+
+class DeviceModel:
+    """One model instance on one GPU.
+
+    overrides: optional {tensor name: uint16 host array} replacing drawn
+    weights (used by tests that pin special cases)."""
+
+    def __init__(self, w: Workload, device: str = "cuda:0", overrides: Optional[Dict[str, np.ndarray]] = None):
+        import torch
+
+        self.torch = torch
+        self.w = w
+        self.device = torch.device(device)
+        self.cfg = config_from(w)
+        L = lib()
+        inv = _lib.weight_inventory(self.cfg)
+        specs = tensor_inventory(w)
+        if [(s.name, s.rows, s.cols) for s in specs] != inv:
+            raise RuntimeError("library weight inventory differs from the workload's tensor list")
+        self.specs = specs
+        self.offsets = []
+        off = 0
+        for s in specs:
+            self.offsets.append(off)
+            off = _align(off + s.numel * 2)
+        self.weight_bytes = sum(s.numel * 2 for s in specs)
+        stream = torch.cuda.current_stream(self.device)
+        sptr = stream.cuda_stream
+        self.wbuf = torch.empty(off, dtype=torch.uint8, device=self.device)
+        base = self.wbuf.data_ptr()
+        overrides = overrides or {}
+        for s, o in zip(specs, self.offsets):
+            if s.name in overrides:
+                a = np.ascontiguousarray(overrides[s.name], dtype=np.uint16).reshape(-1)
+                assert a.size == s.numel
+                self.wbuf[o:o + s.numel * 2].copy_(torch.from_numpy(a.view(np.uint8)))
+            elif s.kind == "gain" and s.sigma != 0.0:
+                a = synth.weight_host(w, s).reshape(-1)
+                self.wbuf[o:o + s.numel * 2].copy_(torch.from_numpy(a.view(np.uint8)))
+            else:
+                synth.weight_device(w, s, base + o, sptr)
+        self.ws_bytes = L.md_workspace_bytes(ctypes.byref(self.cfg))
+        if self.ws_bytes == 0:  # the configuration was rejected: surface the library's reason
+            check(L.md_init_model(ctypes.byref(self.cfg), None, 0, None, 0, None, ctypes.byref(ctypes.c_void_p())))
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        self.kv_bytes = L.md_kv_bytes(ctypes.byref(self.cfg))
+        lay, total = kv_layout(w)
+        if total != self.kv_bytes:
+            raise RuntimeError(f"KV layout mismatch: library {self.kv_bytes} vs workload {total}")
+        self.kv_layout = lay
+        self.kv = torch.empty(self.kv_bytes, dtype=torch.uint8, device=self.device)
+        self.reset_kv()
+        ptrs = (ctypes.c_void_p * len(specs))(*[base + o for o in self.offsets])
+        h = ctypes.c_void_p()
+        torch.cuda.synchronize(self.device)
+        check(L.md_init_model(ctypes.byref(self.cfg), ptrs, len(specs), ctypes.c_void_p(self.ws.data_ptr()),
+                              self.ws_bytes, ctypes.c_void_p(sptr), ctypes.byref(h)))
+        self.handle = h
+
+    # ------------------------------------------------------------------ state
+    def reset_kv(self) -> None:
+        """Redraw every layer's cache / state from the seeded generator."""
+        sptr = self.torch.cuda.current_stream(self.device).cuda_stream
+        base = self.kv.data_ptr()
+        for l, (kind, off, nbytes, shape, dt) in enumerate(self.kv_layout):
+            synth.kv_layer_device(self.w, l, base + off, sptr)
+
+    def kv_layer(self, l: int):
+        """Device tensor view of layer l's cache / state (shape per synth.kv_layout)."""
+        torch = self.torch
+        kind, off, nbytes, shape, dt = self.kv_layout[l]
+        raw = self.kv[off:off + nbytes]
+        if kind == "kda":
+            return raw.view(torch.float32).view(*shape)
+        if kind == "gqa":
+            return raw.view(torch.int16).view(2, *shape)
+        return raw.view(torch.int16).view(*shape)
+
+    def kv_host(self):
+        """Host copies of every layer's cache / state in the oracle's layout."""
+        out = []
+        for l in range(self.w.n_layers):
+            t = self.kv_layer(l).cpu().numpy()
+            if t.dtype == np.int16:
+                t = t.view(np.uint16)
+            out.append(np.ascontiguousarray(t))
+        return out
+
+    # ------------------------------------------------------------------ steps
+    def decode(self, tokens, positions, logits, out_tokens=None, out_ids=None, multilaunch=False, stream=None):
+        """Enqueue one decode step.  All tensors are device tensors."""
+        torch = self.torch
+        B = int(tokens.shape[0])
+        s = stream if stream is not None else torch.cuda.current_stream(self.device)
+        fn = lib().md_decode_step_multilaunch if multilaunch else lib().md_decode_step
+        check(fn(self.handle, ctypes.c_void_p(tokens.data_ptr()), ctypes.c_void_p(positions.data_ptr()),
+                 ctypes.c_void_p(self.kv.data_ptr()), ctypes.c_void_p(logits.data_ptr()), B,
+                 ctypes.c_void_p(out_tokens.data_ptr() if out_tokens is not None else 0),
+                 ctypes.c_void_p(out_ids.data_ptr() if out_ids is not None else 0),
+                 ctypes.c_void_p(s.cuda_stream)))
+
+    def verify(self, tokens, positions, logits, accept_len, next_token, stream=None):
+        torch = self.torch
+        B, n = int(tokens.shape[0]), int(tokens.shape[1])
+        s = stream if stream is not None else torch.cuda.current_stream(self.device)
+        check(lib().md_verify_step(self.handle, ctypes.c_void_p(tokens.data_ptr()),
+                                   ctypes.c_void_p(positions.data_ptr()), ctypes.c_void_p(self.kv.data_ptr()),
+                                   ctypes.c_void_p(logits.data_ptr()), ctypes.c_void_p(accept_len.data_ptr()),
+                                   ctypes.c_void_p(next_token.data_ptr()), B, n, ctypes.c_void_p(s.cuda_stream)))
+
+    def device_status(self) -> None:
+        check(lib().md_get_device_status(self.handle))
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            lib().md_free_model(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,156 @@
+/*
+ * md.h -- C ABI of the MI355X decode megakernel library (libmd.so).
+ *
+ * One decode step of a whole transformer / MoE decoder for a batch of 1..8
+ * sequences runs as ONE persistent HIP launch on gfx950: embedding, and per
+ * layer RMSNorm, attention (GQA, or multi-head latent attention / gated delta
+ * rule chosen by layer index), router, shared and routed SwiGLU experts and
+ * residual adds, then the final norm, LM head and greedy argmax.  This is the
+ * decode megakernel of Inferact, "700 TPS on Kimi K3: A Case for TPU
+ * Megakernels": section "Why megakernels?" (the whole decoder step inside one
+ * program so that weight loads are not tied to kernel boundaries and the HBM
+ * interface stays busy) and section "Our Kimi K3 megakernel" (one call over
+ * all layers; attention kind chosen by layer index; per layer attention,
+ * router, shared expert, routed experts).  Section "DSpark" defines the
+ * verify step: one launch scores an anchor and 7 proposed continuations.
+ *
+ * Conventions.
+ *  - All functions have C linkage; no C++ exception crosses this boundary.
+ *  - Every pointer marked "dev" is a device pointer owned by the caller; the
+ *    library never allocates or frees bulk device memory and keeps raw
+ *    pointers only until md_free_model.  "host" pointers are read during the
+ *    call only.
+ *  - Calls that take a stream enqueue work and return; results are valid once
+ *    the stream has synchronised.  A model handle is used by one stream at a
+ *    time; calls on one handle must not overlap.
+ *  - Return values are md_status codes.  On failure nothing is enqueued and
+ *    md_last_error() describes the cause.
+ *  - Weights are bf16, logical row-major [out][in], one device buffer per
+ *    tensor, in the order md_weight_info enumerates (16-byte aligned).
+ *  - Activations and accumulations are fp32; projections run on bf16 matrix
+ *    cores with each fp32 activation split into two bf16 halves (hi + lo),
+ *    which keeps about 16 significant bits of the activation.
+ */
+#ifndef MD_H
+#define MD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct md_model md_model; /* opaque; owned by the library */
+
+typedef enum {
+  MD_OK = 0,
+  MD_EINVAL = -1,       /* bad argument: size, pointer, alignment, range */
+  MD_EUNSUPPORTED = -2, /* device or configuration outside what the kernels support */
+  MD_ENOMEM = -3,       /* a caller-provided buffer is too small */
+  MD_EHIP = -4,         /* a HIP runtime call failed */
+  MD_EDEVICE = -5       /* the device reported an error (watchdog, bad token) */
+} md_status;
+
+/* Model shape.  attn_kind 0: GQA in every layer.  attn_kind 1: hybrid, layer
+ * l is multi-head latent attention when l % mla_every == mla_every - 1 and a
+ * gated delta-rule layer otherwise.  n_experts == 0 selects a dense SwiGLU FFN
+ * of width ffn_dim; otherwise each layer routes every token to top_k of
+ * n_experts SwiGLU experts of width expert_ffn (softmax over all experts,
+ * renormalised over the chosen ones when norm_topk) plus n_shared always-on
+ * experts of width shared_ffn. */
+typedef struct md_config {
+  int32_t n_layers, hidden, vocab, max_batch, max_ctx;
+  float rms_eps, rope_theta;
+  int32_t attn_kind;
+  int32_t n_q_heads, n_kv_heads, head_dim;
+  int32_t mla_every, mla_heads, q_lora, kv_lora, rope_dim, nope_dim, v_dim;
+  int32_t kda_heads, kda_dk, kda_dv, kda_qk_l2norm;
+  int32_t ffn_dim;
+  int32_t n_experts, top_k, expert_ffn, n_shared, shared_ffn, norm_topk;
+  int32_t flags; /* reserved, must be 0 */
+} md_config;
+
+/* Number of weight tensors the model expects. */
+size_t md_weight_count(const md_config* cfg);
+
+/* Name and logical shape [rows][cols] of weight tensor i (bf16).  name
+ * receives a NUL-terminated string truncated to name_cap.  Returns MD_EINVAL
+ * for i out of range. */
+md_status md_weight_info(const md_config* cfg, size_t i, char* name, size_t name_cap, int64_t* rows,
+                         int64_t* cols);
+
+/* Bytes of device workspace the library needs (layer table, activation
+ * buffers, partial results, sync counters).  The workspace is owned by the
+ * caller, must stay allocated while the model lives, and must not be touched
+ * by the caller. */
+size_t md_workspace_bytes(const md_config* cfg);
+
+/* Bytes of the KV / state buffer.  Per layer, in layer order, each region
+ * starting on a 256-byte boundary:
+ *   GQA layer: K bf16[max_batch][n_kv_heads][max_ctx][head_dim], then V (same shape)
+ *   MLA layer: latent rows bf16[max_batch][max_ctx][kv_lora + rope_dim]
+ *              (RMS-normalised latent, then the rotated key part)
+ *   KDA layer: state fp32[max_batch][kda_heads][kda_dk][kda_dv]
+ * Sequence b of a batch uses slot b. */
+size_t md_kv_bytes(const md_config* cfg);
+
+/* Validate cfg, check the device (gfx950, cooperative launch, LDS), record
+ * the weight pointers (dev, n_weights of them) and build the layer table in
+ * the workspace (dev, workspace_bytes >= md_workspace_bytes).  Copies are
+ * issued on hip_stream and complete before return. */
+md_status md_init_model(const md_config* cfg, const void* const* weights, size_t n_weights, void* workspace,
+                        size_t workspace_bytes, void* hip_stream, md_model** out);
+
+/* One decode step for `batch` sequences (1 <= batch <= max_batch).
+ *   tokens       dev int32[batch]     current token of each sequence (0 <= t < vocab)
+ *   positions    dev int32[batch]     number of cached positions before it; the new
+ *                                     key/value (or latent row) is written at this row,
+ *                                     so positions[b] < max_ctx is required
+ *   kv_cache     dev, md_kv_bytes     read and updated in place
+ *   out_logits   dev fp32[batch][vocab]
+ *   out_tokens   dev int32[batch] or NULL: greedy argmax (lowest index on ties)
+ *   out_expert_ids dev int32[n_layers][batch][top_k] or NULL (MoE only): experts
+ *                chosen per layer and token, in descending router order
+ * Token and position values live on the device and are checked there: an
+ * out-of-range value sets the device error word (md_get_device_status) and
+ * the step's outputs are undefined. */
+md_status md_decode_step(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv_cache,
+                         float* out_logits, int32_t batch, int32_t* out_tokens, int32_t* out_expert_ids,
+                         void* hip_stream);
+
+/* The same step as md_decode_step executed as one kernel launch per
+ * operation (no megakernel): the baseline that exposes the inter-kernel
+ * bubbles.  Same arguments and results. */
+md_status md_decode_step_multilaunch(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv_cache,
+                                     float* out_logits, int32_t batch, int32_t* out_tokens,
+                                     int32_t* out_expert_ids, void* hip_stream);
+
+/* Speculative verify of n_tok (2..8) tokens per sequence (section "DSpark":
+ * an anchor plus proposed continuations in one launch).
+ *   tokens     dev int32[batch][n_tok]  t_0 (anchor) .. t_{n-1} (drafts)
+ *   positions  dev int32[batch]         position of the anchor; rows p..p+n-1 are written
+ *   out_logits dev fp32[batch][n_tok][vocab]: row j is the next-token distribution after t_j
+ *   out_accept_len dev int32[batch]: a = 1 + m, m the largest j with t_i == argmax(row i-1)
+ *              for all 1 <= i <= j
+ *   out_next_token dev int32[batch]: argmax of row a-1
+ * Delta-rule states are committed as they stand after token a-1.  batch must
+ * be 1 and the model must satisfy max_batch >= n_tok. */
+md_status md_verify_step(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv_cache,
+                         float* out_logits, int32_t* out_accept_len, int32_t* out_next_token, int32_t batch,
+                         int32_t n_tok, void* hip_stream);
+
+/* Synchronises the model's last stream and reports the device error word:
+ * MD_OK, or MD_EDEVICE with md_last_error() naming the cause (a sync wait
+ * that exceeded its bound, an out-of-range token or position).  Clears it. */
+md_status md_get_device_status(md_model* m);
+
+/* Text of the calling thread's last error; valid until its next md_* call. */
+const char* md_last_error(void);
+
+void md_free_model(md_model* m);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MD_H */

@@ -1,0 +1,200 @@
+"""Decode-step benchmark of the MI355X megakernel.
+
+Workload: the 64-layer dense decoder shaped like a 27B model (hidden 5120,
+GQA 40/8 x 128, SwiGLU 17408, vocab 152064), seeded synthetic bf16 weights,
+context 4096, chained greedy decode steps (each step's argmax is the next
+step's token, on the device; no host synchronisation inside the timed loop).
+Batch 1 gives `value`; batch 8 is reported beside it.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+Prints one JSON line.  `roofline.achieved` = algorithmic bytes of one step
+(active weights + KV rows read) / mean duration of one megakernel launch,
+timed with HIP events on the launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0
+METRIC = "decode tok/s + step latency at batch 1/8; achieved HBM GB/s vs 8 TB/s peak"
+
+
+def algorithmic_bytes(w, B, positions_per_seq):
+    """Bytes a decode step must read: every weight the step touches (all
+    layer matrices, norm gains, LM head, B embedding rows) plus every cached
+    K/V row attended (positions 0..pos inclusive)."""
+    from synth.workloads import tensor_inventory
+    wb = 0
+    for t in tensor_inventory(w):
+        if t.name == "embed":
+            wb += B * t.cols * 2
+        else:
+            wb += t.numel * 2
+    kvb = 0
+    for l in range(w.n_layers):
+        if w.layer_kind(l) == "gqa":
+            for p in positions_per_seq:
+                kvb += 2 * w.n_kv_heads * w.head_dim * (int(p) + 1) * 2
+    return wb, kvb
+
+
+def time_steps(m, B, steps, warmup, multilaunch=False):
+    import torch
+    w = m.w
+    dev = m.device
+    stream = torch.cuda.current_stream(dev)
+    import synth
+    toks = torch.empty((steps + warmup + 1, B), dtype=torch.int32, device=dev)
+    toks[0] = torch.tensor(synth.tokens(w, B), device=dev)
+    base = w.context
+    pos = torch.tensor([[base + s] * B for s in range(steps + warmup)], dtype=torch.int32, device=dev)
+    logits = torch.empty((B, w.vocab), dtype=torch.float32, device=dev)
+    # warmup (positions base .. base+warmup-1), then the timed chain restarts at base
+    for s in range(warmup):
+        m.decode(toks[s], pos[s], logits, toks[s + 1], multilaunch=multilaunch)
+    torch.cuda.synchronize(dev)
+    m.device_status()
+    toks[0] = toks[warmup]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize(dev)
+    ev[0].record(stream)
+    for s in range(steps):
+        m.decode(toks[s], pos[s], logits, toks[s + 1], multilaunch=multilaunch)
+        ev[s + 1].record(stream)
+    torch.cuda.synchronize(dev)
+    m.device_status()
+    per = np.array([ev[s].elapsed_time(ev[s + 1]) for s in range(steps)], dtype=np.float64)
+    total = ev[0].elapsed_time(ev[steps])
+    return per, total, pos[:steps].cpu().numpy()
+
+
+def cpu_baseline(w, layers=8, B=1):
+    """Time the oracle on layers 0..layers-1 plus the final norm and LM head
+    for one token at the workload's context; extrapolate to all layers."""
+    import synth
+    from oracle import lib as olib, ptr
+    from oracle import step as ostep
+    from tests.harness import HostWeights
+
+    wsub = w.replace(n_layers=layers)
+    W = HostWeights(wsub)
+    for t in synth.tensor_inventory(wsub):
+        W(t.name)  # draw before timing
+    kv = [synth.kv_layer_host(wsub, l) for l in range(layers)]
+    toks = synth.tokens(w, B)
+    pos = np.array([w.context] * B)
+    t0 = time.perf_counter()
+    xs = np.empty((B, w.hidden))
+    for b in range(B):
+        olib().orc_embed(w.hidden, ptr(W("embed")), int(toks[b]), ptr(xs[b]))
+    for l in range(layers):
+        ostep._layer(wsub, W, l, xs, pos, kv[l], B, None, None)
+    t1 = time.perf_counter()
+    logits = np.empty((B, w.vocab), dtype=np.float32)
+    for b in range(B):
+        olib().orc_head(w.hidden, w.vocab, w.rms_eps, ptr(W("final_norm")), ptr(W("lm_head")), ptr(xs[b]),
+                        ptr(logits[b]))
+    t2 = time.perf_counter()
+    t_step = (t1 - t0) / layers * w.n_layers + (t2 - t1)
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    return {"value": B / t_step, "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 oracle, batch {B}, context {w.context}: layers 0-{layers - 1} ({t1 - t0:.2f} s) plus "
+                      f"final norm and LM head ({t2 - t1:.2f} s), extrapolated to {w.n_layers} layers "
+                      f"({t_step:.2f} s per step)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dense_27b")
+    ap.add_argument("--batches", default="1,8")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-multilaunch", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU: the multi-GPU path is designed, not built; "
+                                   "run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+    from synth import workloads as WL
+    from decode_megakernel_md_amd.model import DeviceModel
+
+    w = WL.get(args.workload)
+    batches = [int(b) for b in args.batches.split(",")]
+    max_steps = w.max_ctx - w.context
+    steps = min(args.steps, max_steps - args.warmup)
+    t0 = time.time()
+    m = DeviceModel(w)
+    torch.cuda.synchronize()
+    print(f"# model ready in {time.time() - t0:.1f} s ({m.weight_bytes / 1e9:.2f} GB weights)", file=sys.stderr,
+          flush=True)
+    res = {}
+    for B in batches:
+        per, total, pos = time_steps(m, B, steps, args.warmup)
+        wb, kvb = [], []
+        for s in range(steps):
+            a, b = algorithmic_bytes(w, B, pos[s])
+            wb.append(a)
+            kvb.append(b)
+        mean_ms = float(per.mean())
+        bytes_step = float(np.mean(np.array(wb) + np.array(kvb)))
+        gbs = bytes_step / (mean_ms * 1e-3) / 1e9
+        res[B] = {"tok_s": B * steps / (total * 1e-3), "ms_per_step": total / steps,
+                  "p50_ms": float(np.percentile(per, 50)), "p90_ms": float(np.percentile(per, 90)),
+                  "bytes_per_step": bytes_step, "weight_bytes": float(np.mean(wb)), "kv_bytes": float(np.mean(kvb)),
+                  "achieved_gbs": gbs, "frac": gbs / PEAK_GBS}
+        print(f"# B={B}: {res[B]['ms_per_step']:.3f} ms/step, {res[B]['tok_s']:.1f} tok/s, {gbs:.0f} GB/s "
+              f"({100 * gbs / PEAK_GBS:.1f}% of 8 TB/s)", file=sys.stderr, flush=True)
+    ml = {}
+    if not args.no_multilaunch:
+        for B in batches:
+            try:
+                per, total, pos = time_steps(m, B, min(steps, 16), 1, multilaunch=True)
+                ml[B] = {"ms_per_step": total / min(steps, 16), "tok_s": B * min(steps, 16) / (total * 1e-3)}
+            except Exception as e:  # not built for this configuration
+                ml[B] = {"error": str(e)[:120]}
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(w)
+        print(f"# cpu oracle: {cpu['value']:.4f} tok/s on {cpu['cores']} threads", file=sys.stderr, flush=True)
+    B0 = batches[0]
+    r0 = res[B0]
+    line = {
+        "metric": METRIC,
+        "value": r0["tok_s"],
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": r0["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B0, "context": w.context, "layers": w.n_layers,
+                   "hidden": w.hidden, "chained_greedy_steps": steps},
+        "roofline": {"bound": "hbm", "achieved": r0["achieved_gbs"], "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": r0["frac"], "traffic": None},
+        "cpu_baseline": cpu,
+        "batches": {str(B): res[B] for B in batches},
+        "multilaunch": {str(B): ml[B] for B in ml},
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

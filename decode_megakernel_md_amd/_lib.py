@@ -41,7 +41,7 @@ class MdError(RuntimeError):
 EXPORTS = [
     "md_weight_count", "md_weight_info", "md_workspace_bytes", "md_kv_bytes", "md_init_model",
     "md_decode_step", "md_decode_step_multilaunch", "md_verify_step", "md_get_device_status",
-    "md_last_error", "md_free_model",
+    "md_last_error", "md_free_model", "md_set_trace", "md_grid_size",
 ]
 
 _lib = None
@@ -76,6 +76,10 @@ def lib():
         L.md_get_device_status.argtypes = [P]
         L.md_last_error.restype = ctypes.c_char_p
         L.md_last_error.argtypes = []
+        L.md_set_trace.restype = I32
+        L.md_set_trace.argtypes = [P, P, I32]
+        L.md_grid_size.restype = I32
+        L.md_grid_size.argtypes = [P]
         L.md_free_model.restype = None
         L.md_free_model.argtypes = [P]
         _lib = L

@@ -43,6 +43,17 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
 
+// Resource from values the compiler cannot prove uniform (function
+// arguments, values loaded from memory): force them into scalar registers so
+// buffer instructions take the resource directly instead of looping over lanes.
+__device__ __forceinline__ rsrc_t make_rsrc_u(const void* base, uint32_t bytes) {
+  uint64_t a = (uint64_t)base;
+  uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  return make_rsrc((const void*)(((uint64_t)hi << 32) | lo), n);
+}
+
 // ---- coherent scalar access (32-bit) through a resource
 __device__ __forceinline__ float ld_f32(rsrc_t r, uint32_t off) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CP_SC1));

@@ -129,7 +129,7 @@ md_status validate(const md_config* c) {
 }
 
 struct WsLayout {
-  size_t layers, experts, x, u, ssq, qkv, attn, ou, h, cand, sync, err, total;
+  size_t layers, experts, x, u, ssq, qkv, attn, attn_ml, ou, h, cand, sync, err, total;
   int n_sync, sync_attn_base;
 };
 
@@ -153,7 +153,8 @@ WsLayout ws_layout(const md_config* c) {
   w.u = take(2 * 2 * MAXB_ * H);
   w.ssq = take(4 * (size_t)GMAX * MAXB_);
   w.qkv = take(4 * MAXB_ * (size_t)nqkv);
-  w.attn = take(4 * (size_t)MAXB_ * (c->n_q_heads > 0 ? c->n_q_heads : 1) * CMAX * (size_t)(c->head_dim + 2));
+  w.attn = take(4 * (size_t)MAXB_ * (c->n_q_heads > 0 ? c->n_q_heads : 1) * CMAX * (size_t)c->head_dim);
+  w.attn_ml = take(8 * (size_t)MAXB_ * (c->n_q_heads > 0 ? c->n_q_heads : 1) * CMAX);
   w.ou = take(2 * 2 * MAXB_ * (size_t)attn_out);
   w.h = take(2 * 2 * MAXB_ * (size_t)F);
   w.cand = take(8 * (size_t)GMAX * MAXB_);
@@ -195,6 +196,8 @@ struct md_model {
   int grid = 0;
   int bank = 0;
   hipStream_t last_stream = nullptr;
+  uint64_t* trace = nullptr;
+  int trace_n = 0;
 };
 
 extern "C" {
@@ -352,13 +355,15 @@ static md_status fill_params(md_model* m, const int32_t* tokens, const int32_t* 
   p.out_tokens = out_tokens; p.out_ids = out_ids;
   p.ws = m->ws; p.ws_bytes = (uint32_t)w.total;
   p.x = (float*)(m->ws + w.x);
-  p.off_u = (uint32_t)w.u; p.off_ssq = (uint32_t)w.ssq; p.off_qkv = (uint32_t)w.qkv; p.off_attn = (uint32_t)w.attn;
+  p.off_u = (uint32_t)w.u; p.off_ssq = (uint32_t)w.ssq; p.off_qkv = (uint32_t)w.qkv; p.off_attn = (uint32_t)w.attn; p.off_attn_ml = (uint32_t)w.attn_ml;
   p.off_ou = (uint32_t)w.ou; p.off_h = (uint32_t)w.h; p.off_cand = (uint32_t)w.cand;
   p.sync = (unsigned*)(m->ws + w.sync);
   p.err = (int*)(m->ws + w.err);
   p.n_sync = w.n_sync;
   p.sync_attn_base = w.sync_attn_base;
   p.spin_limit = 1u << 22;
+  p.trace = m->trace;
+  p.trace_n = m->trace_n;
   return MD_OK;
 }
 
@@ -410,6 +415,16 @@ md_status md_get_device_status(md_model* m) {
   }
   return MD_OK;
 }
+
+md_status md_set_trace(md_model* m, uint64_t* dev_buf, int32_t n_per_wg) {
+  if (!m) return fail(MD_EINVAL, "model is NULL");
+  if (dev_buf && n_per_wg < 2) return fail(MD_EINVAL, "n_per_wg must be >= 2");
+  m->trace = dev_buf;
+  m->trace_n = dev_buf ? n_per_wg : 0;
+  return MD_OK;
+}
+
+int32_t md_grid_size(const md_model* m) { return m ? m->grid : 0; }
 
 void md_free_model(md_model* m) { delete m; }
 

@@ -86,9 +86,16 @@ __device__ void wait_all(const Params& p, int idx) {
   __builtin_amdgcn_s_barrier();
 }
 
+__device__ __forceinline__ void stamp(const Params& p, int slot) {
+  if (p.trace && threadIdx.x == 0 && slot < p.trace_n) p.trace[(size_t)blockIdx.x * p.trace_n + slot] = wall_clock64();
+}
+
+// Sync point sidx: stamps 2*sidx (work done) and 2*sidx+1 (wait over).
 __device__ __forceinline__ void grid_sync(const Params& p, int& sidx) {
+  stamp(p, 2 * sidx);
   arrive(p, sidx);
   wait_all(p, sidx);
+  stamp(p, 2 * sidx + 1);
   ++sidx;
 }
 
@@ -112,6 +119,7 @@ __device__ void clear_next_bank(const Params& p) {
 // no bandwidth).  The four waves split the k-steps; each keeps DS k-steps
 // of weight and activation loads in flight.
 constexpr int MAXM = 3;
+constexpr int CMAX_DEV = 256;  // largest chunk count per (sequence, kv head)
 constexpr int MAXT = 8;
 
 struct GemvJob {
@@ -144,7 +152,8 @@ struct GemvSmem {
 // A planned GEMV: this workgroup's share of each matrix, cut into chunks of
 // up to MAXT tiles (local tile indices [i0, i1) of every matrix).
 struct GemvPlan {
-  rsrc_t rs[MAXM];
+  const void* wbase[MAXM];
+  uint32_t wbytes[MAXM];
   int r0[MAXM], nrows[MAXM];
   int nm, K, B, per, maxtiles;
   uint32_t u_off;
@@ -166,11 +175,13 @@ __device__ __forceinline__ GemvPlan plan_gemv(const Params& p, const GemvJob& jo
       g.nrows[m] = s.r1 - s.r0;
       int nt = (g.nrows[m] + 15) >> 4;
       g.maxtiles = nt > g.maxtiles ? nt : g.maxtiles;
-      g.rs[m] = make_rsrc(job.W[m] + (size_t)s.r0 * job.K, (uint32_t)((size_t)g.nrows[m] * job.K * 2));
+      g.wbase[m] = job.W[m] + (size_t)s.r0 * job.K;
+      g.wbytes[m] = (uint32_t)((size_t)g.nrows[m] * job.K * 2);
     } else {
       g.r0[m] = 0;
       g.nrows[m] = 0;
-      g.rs[m] = make_rsrc(p.ws, 0);
+      g.wbase[m] = p.ws;
+      g.wbytes[m] = 0;
     }
   }
   g.per = MAXT / job.nm;
@@ -190,8 +201,10 @@ __device__ __forceinline__ void gemv_sweep(const GemvPlan& g, int i0, rsrc_t urs
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     int m = t / g.per, i = i0 + t % g.per;
-    ars[t] = m == 0 ? g.rs[0] : (m == 1 ? g.rs[1] : (m == 2 ? g.rs[2] : make_rsrc(urs_base_dummy(), 0)));
-    if (m >= g.nm) ars[t] = make_rsrc(urs_base_dummy(), 0);
+    const void* wb = m == 0 ? g.wbase[0] : (m == 1 ? g.wbase[1] : g.wbase[2]);
+    uint32_t nb = m == 0 ? g.wbytes[0] : (m == 1 ? g.wbytes[1] : g.wbytes[2]);
+    if (m >= g.nm) nb = 0;
+    ars[t] = make_rsrc_u(wb, nb);
     aoff[t] = ((uint32_t)(i * 16) + (lane & 15)) * (uint32_t)K * 2u + (lane >> 4) * 16u + wv * 64u;
   }
   const int n = lane & 15, tok = n >> 1, part = n & 1;
@@ -244,7 +257,7 @@ __device__ __forceinline__ void gemv_sweep(const GemvPlan& g, int i0, rsrc_t urs
 
 // One chunk of a planned GEMV; leaves Y in sm.y (slot m*per + local tile).
 __device__ __noinline__ void gemv_chunk(const Params& p, const GemvPlan& g, int i0, GemvSmem& sm) {
-  rsrc_t urs = make_rsrc(p.ws, p.ws_bytes);
+  rsrc_t urs = make_rsrc_u(p.ws, p.ws_bytes);
   int i1 = i0 + g.per < g.maxtiles ? i0 + g.per : g.maxtiles;
   int cnt = (i1 - i0) * g.nm;
   GemvPlan gg = g;
@@ -285,7 +298,7 @@ __device__ __forceinline__ void run_gemv(const Params& p, const GemvJob& job, Ge
 __device__ __noinline__ void load_inv_rms(const Params& p, float* inv_rms, int n_feat) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    rsrc_t r = make_rsrc(p.ws, p.ws_bytes);
+    rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
     for (int t = 0; t < p.B; ++t) {
       float s = 0.f;
       for (int g = lane; g < (int)gridDim.x; g += 64) s += ld_f32(r, p.off_ssq + (uint32_t)(g * MAXB + t) * 4u);
@@ -314,7 +327,7 @@ struct SsqAcc {
 // --- embedding: x[t] = E[tok_t] on this WG's hidden rows
 __device__ __noinline__ void phase_embed(const Params& p, float* sm_f) {
   RowSplit s = rows_of(p.H, blockIdx.x, gridDim.x);
-  rsrc_t r = make_rsrc(p.ws, p.ws_bytes);
+  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   const uint16_t* g = p.layers[0].attn_norm;
   float* part = sm_f;  // [NT][MAXB]
   for (int t = 0; t < MAXB; ++t) part[threadIdx.x * MAXB + t] = 0.f;
@@ -352,7 +365,7 @@ __device__ __noinline__ void phase_qkv(const Params& p, const LayerDesc& L, char
   j.u_off = p.off_u;
   j.B = p.B;
   const int nqkv = (p.nq + 2 * p.nkv) * p.hd;
-  rsrc_t r = make_rsrc(p.ws, p.ws_bytes);
+  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   run_gemv(p, j, sm, [&](GemvSmem& s, const Chunk& c) {
     int per = c.i1 - c.i0;
     int col0[3] = {0, p.nq * p.hd, (p.nq + p.nkv) * p.hd};
@@ -377,25 +390,176 @@ __device__ __forceinline__ void rope_cs(int64_t pos, int i, int d, float theta, 
   s = (float)sd;
 }
 
-// --- GQA decode attention: split-KV partials, last arriver of each (b, kv
-// head) combines them into the hi/lo O-projection input.
+// --- GQA decode attention.  Task (b, kv head g, chunk c) covers cached
+// positions [c*P, (c+1)*P) of sequence b (positions 0..pos inclusive, the new
+// row included).  Each wave takes a quarter of the chunk in 32-position
+// blocks, with the next block's K and V rows in flight while the current one
+// is used: scores on the matrix cores (K rows as the A operand, the group's
+// rotated q heads as hi/lo B columns), an online softmax per head, and P.V on
+// the vector ALUs.  The chunk's partial (max, sum, o) per head goes to the
+// workspace; the last workgroup to finish a (b, g) combines the chunks.
 struct AttnSmem {
   float q[MAXB][128];           // rotated, scaled q of the group's heads
-  float s[NW][64][MAXB];        // per-wave scores of the current 64-position block
+  float s[NW][32][MAXB];        // per-wave scores / probabilities of a block
   float wm[NW][MAXB], wl[NW][MAXB];
   float wo[NW][MAXB][128];
-  float knew[128], vnew[128];
+  float cw[MAXB][CMAX_DEV];     // combine weights
+  float cl[MAXB];
   int last;
 };
 
-__device__ __noinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L, int layer, char* smem, int& sidx) {
-  AttnSmem& sm = *(AttnSmem*)smem;
+template <int HD>
+struct KVBlock {
+  i32x4 k[2][HD / 32];          // 2 tiles of 16 positions x HD/32 k-steps
+  i32x4 v[HD / 16];             // 32 positions x HD bf16 = HD/16 loads of 1 KB per wave
+};
+
+template <int HD>
+__device__ __forceinline__ void load_block(KVBlock<HD>& r, rsrc_t krs, rsrc_t vrs, int blk, int w1, int lane) {
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    int prow = blk + tt * 16 + (lane & 15);
+#pragma unroll
+    for (int s = 0; s < HD / 32; ++s) {
+      uint32_t off = (prow < w1 && blk < w1) ? (uint32_t)(prow * HD + s * 32 + (lane >> 4) * 8) * 2u : OOB;
+      r.k[tt][s] = ld_x4<0>(krs, off);
+    }
+  }
+  // V: lanes split a row into HD/8 chunks of 8 dims; one instruction covers 64/(HD/8) rows
+  constexpr int LPR = HD / 8;
+  constexpr int RPI = 64 / LPR;
+#pragma unroll
+  for (int q = 0; q < HD / 16; ++q) {
+    int t = blk + q * RPI + lane / LPR;
+    uint32_t off = (t < w1 && blk < w1) ? (uint32_t)(t * HD + (lane % LPR) * 8) * 2u : OOB;
+    r.v[q] = ld_x4<0>(vrs, off);
+  }
+}
+
+template <int HD>
+__device__ __noinline__ void attn_task_wave(const Params& p, AttnSmem& sm, int gs, const uint16_t* kc,
+                                            const uint16_t* vc, uint32_t nbytes, int w0, int w1) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const rsrc_t krs = make_rsrc_u(kc, nbytes), vrs = make_rsrc_u(vc, nbytes);
+  gs = __builtin_amdgcn_readfirstlane(gs);
+  w0 = __builtin_amdgcn_readfirstlane(w0);
+  w1 = __builtin_amdgcn_readfirstlane(w1);
+  const int nn = lane & 15, hh = nn >> 1, pp = nn & 1;
+  constexpr int LPR = HD / 8, RPI = 64 / LPR;
+  bf16x8 qb[HD / 32];
+#pragma unroll
+  for (int s = 0; s < HD / 32; ++s) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      int d = s * 32 + (lane >> 4) * 8 + k;
+      float v = hh < gs ? sm.q[hh][d] : 0.f;
+      uint16_t hi, lo;
+      split_hilo(v, hi, lo);
+      qb[s][k] = __builtin_bit_cast(__bf16, pp ? lo : hi);
+    }
+  }
+  float m_run[MAXB], l_run[MAXB], acc[MAXB][8];
+#pragma unroll
+  for (int h = 0; h < MAXB; ++h) {
+    m_run[h] = -INFINITY;
+    l_run[h] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
+  }
+  auto block = [&](const KVBlock<HD>& cur, int blk) __attribute__((always_inline)) {
+    // scores of the 32 positions
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < HD / 32; ++s)
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[tt][s]), qb[s], a, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = a[i] + __shfl_xor(a[i], 1, 64);
+        int pr = tt * 16 + 4 * (lane >> 4) + i;
+        if (!pp && hh < gs) sm.s[wv][pr][hh] = (blk + pr < w1) ? v : -INFINITY;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+    __builtin_amdgcn_wave_barrier();
+    // online softmax per head over this block; probabilities replace scores
+#pragma unroll
+    for (int h = 0; h < MAXB; ++h) {
+      if (h < gs) {
+        float sv = lane < 32 ? sm.s[wv][lane][h] : -INFINITY;
+        float mb = wave_max(sv);
+        float mn = fmaxf(m_run[h], mb);
+        float corr = __expf(m_run[h] - mn);
+        float pv = lane < 32 ? __expf(sv - mn) : 0.f;
+        l_run[h] = l_run[h] * corr + wave_sum(pv);
+        m_run[h] = mn;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[h][j] *= corr;
+        if (lane < 32) sm.s[wv][lane][h] = pv;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+    __builtin_amdgcn_wave_barrier();
+    // P.V: this lane holds 8 dims of the rows q*RPI + lane/LPR
+#pragma unroll
+    for (int q = 0; q < HD / 16; ++q) {
+      int t = q * RPI + lane / LPR;
+      uint32_t u[4] = {(uint32_t)cur.v[q][0], (uint32_t)cur.v[q][1], (uint32_t)cur.v[q][2], (uint32_t)cur.v[q][3]};
+      float vv[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        vv[2 * j] = __uint_as_float(u[j] << 16);
+        vv[2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int h = 0; h < MAXB; ++h) {
+        if (h < gs) {
+          float pw = sm.s[wv][t][h];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[h][j] += pw * vv[j];
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+  KVBlock<HD> ba, bb;
+  load_block<HD>(ba, krs, vrs, w0, w1, lane);
+  for (int blk = w0; blk < w1; blk += 64) {
+    load_block<HD>(bb, krs, vrs, blk + 32, w1, lane);
+    block(ba, blk);
+    if (blk + 32 >= w1) break;
+    load_block<HD>(ba, krs, vrs, blk + 64, w1, lane);
+    block(bb, blk + 32);
+  }
+  // sum the lane groups that hold the same dims (different rows)
+#pragma unroll
+  for (int h = 0; h < MAXB; ++h) {
+    if (h < gs) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float v = acc[h][j];
+#pragma unroll
+        for (int o = LPR; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+        acc[h][j] = v;
+      }
+      if (lane == 0) { sm.wm[wv][h] = m_run[h]; sm.wl[wv][h] = l_run[h]; }
+      if (lane < LPR) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sm.wo[wv][h][lane * 8 + j] = acc[h][j];
+      }
+    }
+  }
+}
+
+__device__ __noinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L, int layer, char* smem) {
+  AttnSmem& sm = *(AttnSmem*)smem;
+  const int wv = threadIdx.x >> 6;
   const int hd = p.hd, gs = p.nq / p.nkv, B = p.B;
   const int C = p.attn_chunks;
   const int ntask = B * p.nkv * C;
   const int nqkv = (p.nq + 2 * p.nkv) * hd;
-  rsrc_t wr = make_rsrc(p.ws, p.ws_bytes);
+  rsrc_t wr = make_rsrc_u(p.ws, p.ws_bytes);
   const float scale = 1.0f / sqrtf((float)hd);
   for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
     const int c = task % C, g = (task / C) % p.nkv, b = task / (C * p.nkv);
@@ -406,10 +570,9 @@ __device__ __noinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L,
     }
     const int n = pos + 1;
     const int P = (n + C - 1) / C;
-    const int a0 = c * P, a1 = (c + 1) * P < n ? (c + 1) * P : n;
+    const int a0 = c * P < n ? c * P : n, a1 = (c + 1) * P < n ? (c + 1) * P : n;
     uint16_t* kc = (uint16_t*)(p.kv + L.kv_off) + (size_t)(b * p.nkv + g) * p.max_ctx * hd;
     uint16_t* vc = kc + (size_t)p.max_batch * p.nkv * p.max_ctx * hd;
-    // q of the group's heads: rotate, scale
     for (int e = threadIdx.x; e < gs * (hd / 2); e += NT) {
       int h = e / (hd / 2), i = e % (hd / 2);
       int col = (g * gs + h) * hd;
@@ -420,7 +583,6 @@ __device__ __noinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L,
       sm.q[h][i] = (a * cs - bb * sn) * scale;
       sm.q[h][i + hd / 2] = (a * sn + bb * cs) * scale;
     }
-    // the new key / value row, written by the task that covers position pos
     if (a0 <= pos && pos < a1) {
       for (int i = threadIdx.x; i < hd / 2; i += NT) {
         int colk = p.nq * hd + g * hd;
@@ -438,107 +600,15 @@ __device__ __noinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L,
       wait_stores();
     }
     __syncthreads();
-    // each wave: a contiguous quarter of [a0, a1), in blocks of 64 positions
     const int len = a1 - a0;
-    const int wq = (len + NW - 1) / NW;
-    const int w0 = a0 + wv * wq, w1 = (w0 + wq < a1) ? w0 + wq : a1;
-    // B operand (q hi/lo) per k-step: column n = lane%16 -> head n/2, part n%2
-    const int nn = lane & 15, hh = nn >> 1, pp = nn & 1;
-    bf16x8 qb[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        int d = s * 32 + (lane >> 4) * 8 + k;
-        float v = (hh < gs && d < hd) ? sm.q[hh][d] : 0.f;
-        uint16_t hi, lo;
-        split_hilo(v, hi, lo);
-        uint16_t bits = pp ? lo : hi;
-        qb[s][k] = __builtin_bit_cast(__bf16, bits);
-      }
-    }
-    rsrc_t krs = make_rsrc(kc, (uint32_t)((size_t)n * hd * 2));
-    float m_run[MAXB], l_run[MAXB];
-    float o_run[MAXB][2];
-#pragma unroll
-    for (int h = 0; h < MAXB; ++h) { m_run[h] = -INFINITY; l_run[h] = 0.f; o_run[h][0] = o_run[h][1] = 0.f; }
-    const int dpl = hd / 64;  // dims per lane in P.V (1 or 2)
-    for (int blk = w0; blk < w1; blk += 64) {
-      // scores of positions blk..blk+63 (4 MFMA tiles of 16)
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        int prow = blk + tt * 16 + (lane & 15);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          if (s * 32 < hd) {
-            uint32_t off = (prow < w1) ? (uint32_t)(prow * hd + s * 32 + (lane >> 4) * 8) * 2u : OOB;
-            i32x4 kv4 = ld_x4<0>(krs, off);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv4), qb[s], acc, 0, 0, 0);
-          }
-        }
-        // lane holds S[pos 4*(lane/16)+i][col lane%16]; merge hi/lo columns
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = acc[i] + __shfl_xor(acc[i], 1, 64);
-          int pr = tt * 16 + 4 * (lane >> 4) + i;
-          if (!(nn & 1) && hh < gs) sm.s[wv][pr][hh] = (blk + pr < w1) ? v : -INFINITY;
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
-      __builtin_amdgcn_wave_barrier();
-      // online softmax update per head, then P.V for this block
-      int cnt = w1 - blk < 64 ? w1 - blk : 64;
-#pragma unroll
-      for (int h = 0; h < MAXB; ++h) {
-        if (h >= gs) break;
-        float sv = lane < cnt ? sm.s[wv][lane][h] : -INFINITY;
-        float mb = wave_max(sv);
-        float mn = fmaxf(m_run[h], mb);
-        float corr = __expf(m_run[h] - mn);
-        float pv = lane < cnt ? __expf(sv - mn) : 0.f;
-        float lb = wave_sum(pv);
-        l_run[h] = l_run[h] * corr + lb;
-        o_run[h][0] *= corr;
-        o_run[h][1] *= corr;
-        m_run[h] = mn;
-        sm.s[wv][lane][h] = pv;
-      }
-      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll 4
-      for (int t = 0; t < cnt; ++t) {
-        const uint16_t* vr = vc + (size_t)(blk + t) * hd;
-        float v0, v1 = 0.f;
-        if (dpl == 2) {
-          uint32_t two = *(const uint32_t*)(vr + 2 * lane);
-          v0 = __uint_as_float(two << 16);
-          v1 = __uint_as_float(two & 0xFFFF0000u);
-        } else {
-          v0 = bf16_f32(vr[lane]);
-        }
-#pragma unroll
-        for (int h = 0; h < MAXB; ++h) {
-          if (h < gs) {
-            float pw = sm.s[wv][t][h];
-            o_run[h][0] += pw * v0;
-            o_run[h][1] += pw * v1;
-          }
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
-    // combine the 4 waves of this WG
-#pragma unroll
-    for (int h = 0; h < MAXB; ++h) {
-      if (h >= gs) break;
-      if (lane == 0) { sm.wm[wv][h] = m_run[h]; sm.wl[wv][h] = l_run[h]; }
-      if (dpl == 2) { sm.wo[wv][h][2 * lane] = o_run[h][0]; sm.wo[wv][h][2 * lane + 1] = o_run[h][1]; }
-      else sm.wo[wv][h][lane] = o_run[h][0];
-    }
+    const int wq = ((len + NW - 1) / NW + 31) / 32 * 32;
+    const int w0 = a0 + wv * wq < a1 ? a0 + wv * wq : a1;
+    const int w1 = w0 + wq < a1 ? w0 + wq : a1;
+    const uint32_t nb = (uint32_t)((size_t)n * hd * 2);
+    if (hd == 128) attn_task_wave<128>(p, sm, gs, kc, vc, nb, w0, w1);
+    else attn_task_wave<64>(p, sm, gs, kc, vc, nb, w0, w1);
     __syncthreads();
-    // partial of this task: part[b][head][c] = {m, l, o[hd]}
-    const uint32_t pstride = (uint32_t)(hd + 2);
+    // this task's partial: m, l in part_ml[b][head][c]; o in part_o[b][head][c][hd]
     for (int e = threadIdx.x; e < gs * hd; e += NT) {
       int h = e / hd, d = e % hd;
       float M = -INFINITY;
@@ -549,13 +619,15 @@ __device__ __noinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L,
         o += f * sm.wo[w][h][d];
         l += f * sm.wl[w][h];
       }
-      uint32_t base = p.off_attn + ((uint32_t)((b * p.nq + g * gs + h) * C + c) * pstride) * 4u;
-      if (d == 0) { st_f32(wr, base, M); st_f32(wr, base + 4, l); }
-      st_f32(wr, base + 8 + d * 4, o);
+      uint32_t head = (uint32_t)((b * p.nq + g * gs + h) * C + c);
+      if (d == 0) {
+        st_f32(wr, p.off_attn_ml + head * 8u, M);
+        st_f32(wr, p.off_attn_ml + head * 8u + 4u, l);
+      }
+      st_f32(wr, p.off_attn + (head * (uint32_t)hd + d) * 4u, o);
     }
     wait_stores();
     __syncthreads();
-    // last arriver of (b, g) combines the C partials of each head
     if (threadIdx.x == 0) {
       unsigned* ctr = sync_pt(p, p.sync_attn_base + layer) + (b * p.nkv + g);
       unsigned old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -563,19 +635,52 @@ __device__ __noinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L,
     }
     __syncthreads();
     if (sm.last) {
-      for (int e = threadIdx.x; e < gs * hd; e += NT) {
-        int h = e / hd, d = e % hd;
-        uint32_t hb = p.off_attn + ((uint32_t)((b * p.nq + g * gs + h) * C) * pstride) * 4u;
+      // combine weights per head: w_c = exp(m_c - M), 1 / sum_c w_c l_c
+      for (int e = threadIdx.x; e < gs * C; e += NT) {
+        int h = e / C, cc = e % C;
+        uint32_t hb = (uint32_t)((b * p.nq + g * gs + h) * C);
+        sm.cw[h][cc] = ld_f32(wr, p.off_attn_ml + (hb + cc) * 8u);
+      }
+      __syncthreads();
+      if (threadIdx.x < gs) {
+        int h = threadIdx.x;
+        uint32_t hb = (uint32_t)((b * p.nq + g * gs + h) * C);
         float M = -INFINITY;
-        for (int cc = 0; cc < C; ++cc) M = fmaxf(M, ld_f32(wr, hb + cc * pstride * 4u));
-        float o = 0.f, l = 0.f;
+        for (int cc = 0; cc < C; ++cc) M = fmaxf(M, sm.cw[h][cc]);
+        float den = 0.f;
         for (int cc = 0; cc < C; ++cc) {
-          float mc = ld_f32(wr, hb + cc * pstride * 4u);
-          float f = mc == -INFINITY ? 0.f : __expf(mc - M);
-          l += f * ld_f32(wr, hb + cc * pstride * 4u + 4);
-          o += f * ld_f32(wr, hb + cc * pstride * 4u + 8 + d * 4);
+          float f = sm.cw[h][cc] == -INFINITY ? 0.f : __expf(sm.cw[h][cc] - M);
+          sm.cw[h][cc] = f;
+          den += f * ld_f32(wr, p.off_attn_ml + (hb + cc) * 8u + 4u);
         }
-        put_hilo(wr, p.off_ou, p.nq * hd, b, (g * gs + h) * hd + d, o / l);
+        sm.cl[h] = 1.0f / den;
+      }
+      __syncthreads();
+      // o = sum_c w_c o_c: thread per (head, 4 dims), 16 chunk loads in flight
+      for (int e = threadIdx.x; e < gs * (hd / 4); e += NT) {
+        int h = e / (hd / 4), d4 = (e % (hd / 4)) * 4;
+        uint32_t hb = (uint32_t)((b * p.nq + g * gs + h) * C);
+        float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+        for (int c0 = 0; c0 < C; c0 += 16) {
+          i32x4 v[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            v[u] = ld_x4<CP_SC1>(wr, c0 + u < C ? p.off_attn + ((hb + c0 + u) * (uint32_t)hd + d4) * 4u : OOB);
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            float f = c0 + u < C ? sm.cw[h][c0 + u] : 0.f;
+            o0 += f * __int_as_float(v[u][0]);
+            o1 += f * __int_as_float(v[u][1]);
+            o2 += f * __int_as_float(v[u][2]);
+            o3 += f * __int_as_float(v[u][3]);
+          }
+        }
+        float il = sm.cl[h];
+        int col = (g * gs + h) * hd + d4;
+        put_hilo(wr, p.off_ou, p.nq * hd, b, col + 0, o0 * il);
+        put_hilo(wr, p.off_ou, p.nq * hd, b, col + 1, o1 * il);
+        put_hilo(wr, p.off_ou, p.nq * hd, b, col + 2, o2 * il);
+        put_hilo(wr, p.off_ou, p.nq * hd, b, col + 3, o3 * il);
       }
     }
     __syncthreads();
@@ -594,7 +699,7 @@ __device__ __noinline__ void phase_residual_gemv(const Params& p, const uint16_t
   j.K = K;
   j.u_off = u_off;
   j.B = p.B;
-  rsrc_t r = make_rsrc(p.ws, p.ws_bytes);
+  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   for (int t = 0; t < MAXB; ++t) part[threadIdx.x * MAXB + t] = 0.f;
   run_gemv(p, j, sm, [&](GemvSmem& s, const Chunk& c) {
     int per = c.i1 - c.i0;
@@ -629,7 +734,7 @@ __device__ __noinline__ void phase_gateup(const Params& p, const uint16_t* Wg, c
   j.K = p.H;
   j.u_off = p.off_u;
   j.B = p.B;
-  rsrc_t r = make_rsrc(p.ws, p.ws_bytes);
+  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   run_gemv(p, j, sm, [&](GemvSmem& s, const Chunk& c) {
     int per = c.i1 - c.i0;
     for (int e = threadIdx.x; e < per * 16 * p.B; e += NT) {
@@ -658,7 +763,7 @@ __device__ __noinline__ void phase_lmhead(const Params& p, char* smem) {
   j.K = p.H;
   j.u_off = p.off_u;
   j.B = p.B;
-  rsrc_t r = make_rsrc(p.ws, p.ws_bytes);
+  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   run_gemv(p, j, sm, [&](GemvSmem& s, const Chunk& c) {
     int per = c.i1 - c.i0;
     for (int e = threadIdx.x; e < per * 16 * p.B; e += NT) {
@@ -690,7 +795,7 @@ __device__ __noinline__ void phase_lmhead(const Params& p, char* smem) {
 
 // final argmax over the WG candidates (one workgroup)
 __device__ __noinline__ void final_argmax(const Params& p) {
-  rsrc_t r = make_rsrc(p.ws, p.ws_bytes);
+  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     for (int t = 0; t < p.B; ++t) {
@@ -716,6 +821,7 @@ __device__ __noinline__ void final_argmax(const Params& p) {
 extern "C" __global__ __launch_bounds__(NT) void md_megakernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   if (p.B < 1 || p.B > MAXB) return;
+  if (p.trace && threadIdx.x == 0 && p.trace_n > 0) p.trace[(size_t)blockIdx.x * p.trace_n + p.trace_n - 1] = wall_clock64();
   clear_next_bank(p);
   int sidx = 0;
   phase_embed(p, (float*)smem);
@@ -725,7 +831,7 @@ extern "C" __global__ __launch_bounds__(NT) void md_megakernel(Params p) {
     const uint16_t* g_next = (l + 1 < p.n_layers) ? p.layers[l + 1].attn_norm : p.final_norm;
     phase_qkv(p, L, smem);
     grid_sync(p, sidx);
-    phase_attn_gqa(p, L, l, smem, sidx);
+    phase_attn_gqa(p, L, l, smem);
     grid_sync(p, sidx);
     phase_residual_gemv(p, L.wo, p.nq * p.hd, p.off_ou, L.ffn_norm, smem);
     grid_sync(p, sidx);

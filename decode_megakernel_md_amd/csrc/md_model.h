@@ -57,7 +57,8 @@ struct Params {
   uint32_t off_u;     // hi/lo bf16[2][MAXB][H]  next norm input (gain folded, not yet scaled)
   uint32_t off_ssq;   // fp32[G][MAXB] partial sums of squares of x
   uint32_t off_qkv;   // fp32[MAXB][nq+2nkv][hd]
-  uint32_t off_attn;  // attention partials
+  uint32_t off_attn;  // attention partial outputs fp32[MAXB][nq][C][hd]
+  uint32_t off_attn_ml; // attention partial (max, sum) fp32[MAXB][nq][C][2]
   uint32_t off_ou;    // hi/lo bf16[2][MAXB][nq*hd]
   uint32_t off_h;     // hi/lo bf16[2][MAXB][F]
   uint32_t off_cand;  // argmax candidates {f32, i32}[G][MAXB]
@@ -67,6 +68,8 @@ struct Params {
   int sync_attn_base;
   int bank;
   unsigned spin_limit;
+  uint64_t* trace;    // optional: per WG trace_n wall-clock stamps (phase end, then start after the wait)
+  int trace_n;
 };
 
 }  // namespace md

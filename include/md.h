@@ -145,6 +145,17 @@ md_status md_verify_step(md_model* m, const int32_t* tokens, const int32_t* posi
  * that exceeded its bound, an out-of-range token or position).  Clears it. */
 md_status md_get_device_status(md_model* m);
 
+/* Profiling aid.  When dev_buf is non-NULL, every later step records
+ * wall-clock stamps (hipDeviceAttributeWallClockRate ticks) into
+ * dev_buf[wg * n_per_wg + i]: slot 2s is when workgroup wg finished the work
+ * before sync point s, slot 2s+1 when its wait there ended, and the last
+ * slot when the workgroup started.  dev_buf holds md_grid_size(m) * n_per_wg
+ * uint64 values; NULL turns recording off. */
+md_status md_set_trace(md_model* m, uint64_t* dev_buf, int32_t n_per_wg);
+
+/* Number of workgroups (one per CU) a step launches. */
+int32_t md_grid_size(const md_model* m);
+
 /* Text of the calling thread's last error; valid until its next md_* call. */
 const char* md_last_error(void);
 

@@ -41,7 +41,8 @@ class MdError(RuntimeError):
 EXPORTS = [
     "md_weight_count", "md_weight_info", "md_workspace_bytes", "md_kv_bytes", "md_init_model",
     "md_decode_step", "md_decode_step_multilaunch", "md_verify_step", "md_get_device_status",
-    "md_last_error", "md_free_model", "md_set_trace", "md_grid_size",
+    "md_last_error", "md_free_model", "md_set_trace", "md_grid_size", "md_packed_bytes", "md_pack_weight",
+    "md_weight_layout",
 ]
 
 _lib = None
@@ -80,6 +81,12 @@ def lib():
         L.md_set_trace.argtypes = [P, P, I32]
         L.md_grid_size.restype = I32
         L.md_grid_size.argtypes = [P]
+        L.md_weight_layout.restype = I32
+        L.md_weight_layout.argtypes = [CFG, ctypes.c_size_t]
+        L.md_packed_bytes.restype = ctypes.c_size_t
+        L.md_packed_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
+        L.md_pack_weight.restype = I32
+        L.md_pack_weight.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, P]
         L.md_free_model.restype = None
         L.md_free_model.argtypes = [P]
         _lib = L

@@ -14,6 +14,7 @@ namespace md {
 size_t megakernel_smem_bytes();
 hipError_t launch_megakernel(const Params& p, int grid, hipStream_t stream);
 hipError_t megakernel_occupancy(int* blocks_per_cu);
+hipError_t launch_pack(const void* src, void* dst, int64_t rows, int64_t cols, hipStream_t stream);
 }  // namespace md
 
 using namespace md;
@@ -129,7 +130,7 @@ md_status validate(const md_config* c) {
 }
 
 struct WsLayout {
-  size_t layers, experts, x, u, ssq, qkv, attn, attn_ml, ou, h, cand, sync, err, total;
+  size_t layers, experts, x, u, ssq, qkv, attn, attn_ml, ou, h, cand, zero, sync, err, total;
   int n_sync, sync_attn_base;
 };
 
@@ -158,6 +159,7 @@ WsLayout ws_layout(const md_config* c) {
   w.ou = take(2 * 2 * MAXB_ * (size_t)attn_out);
   w.h = take(2 * 2 * MAXB_ * (size_t)F);
   w.cand = take(8 * (size_t)GMAX * MAXB_);
+  w.zero = take(1024);
   w.sync_attn_base = 1 + 5 * c->n_layers + 2;
   w.n_sync = w.sync_attn_base + c->n_layers + 2;
   w.sync = take(4 * 2 * (size_t)w.n_sync * SP_WORDS_);
@@ -222,6 +224,13 @@ md_status md_weight_info(const md_config* cfg, size_t i, char* name, size_t name
   return MD_OK;
 }
 
+int32_t md_weight_layout(const md_config* cfg, size_t i) {
+  if (!cfg) return -1;
+  auto T = inventory(cfg);
+  if (i >= T.size()) return -1;
+  return (i == 0 || T[i].rows == 1) ? 0 : 1;  // embedding table and norm gains stay row-major
+}
+
 size_t md_workspace_bytes(const md_config* cfg) {
   if (validate(cfg) != MD_OK) return 0;
   return ws_layout(cfg).total;
@@ -246,8 +255,9 @@ md_status md_init_model(const md_config* cfg, const void* const* weights, size_t
   for (size_t i = 0; i < T.size(); ++i) {
     if (!weights[i]) return fail(MD_EINVAL, "weight %zu (%s) is NULL", i, T[i].name.c_str());
     if ((uintptr_t)weights[i] & 15) return fail(MD_EINVAL, "weight %zu (%s) is not 16-byte aligned", i, T[i].name.c_str());
-    if (T[i].rows * T[i].cols * 2 > (int64_t)0xFFFFFFF0LL)
-      return fail(MD_EUNSUPPORTED, "weight %s exceeds 4 GiB", T[i].name.c_str());
+    if (md_weight_layout(cfg, i) == 1 && (T[i].cols % 32 || md_packed_bytes(T[i].rows, T[i].cols) > 0xFFFFFFF0ull))
+      return fail(MD_EUNSUPPORTED, "weight %s: columns must be a multiple of 32 and the packed size under 4 GiB",
+                  T[i].name.c_str());
   }
   WsLayout lay = ws_layout(cfg);
   if (!workspace || ((uintptr_t)workspace & 255)) return fail(MD_EINVAL, "workspace must be non-NULL and 256-byte aligned");
@@ -316,6 +326,7 @@ md_status md_init_model(const md_config* cfg, const void* const* weights, size_t
   if (e == hipSuccess && !ex.empty())
     e = hipMemcpyAsync(m->ws + lay.experts, ex.data(), sizeof(void*) * ex.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipMemsetAsync(m->ws + lay.sync, 0, lay.err + 256 - lay.sync, s);
+  if (e == hipSuccess) e = hipMemsetAsync(m->ws + lay.zero, 0, 1024, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     delete m;
@@ -356,7 +367,7 @@ static md_status fill_params(md_model* m, const int32_t* tokens, const int32_t* 
   p.ws = m->ws; p.ws_bytes = (uint32_t)w.total;
   p.x = (float*)(m->ws + w.x);
   p.off_u = (uint32_t)w.u; p.off_ssq = (uint32_t)w.ssq; p.off_qkv = (uint32_t)w.qkv; p.off_attn = (uint32_t)w.attn; p.off_attn_ml = (uint32_t)w.attn_ml;
-  p.off_ou = (uint32_t)w.ou; p.off_h = (uint32_t)w.h; p.off_cand = (uint32_t)w.cand;
+  p.off_ou = (uint32_t)w.ou; p.off_h = (uint32_t)w.h; p.off_cand = (uint32_t)w.cand; p.off_zero = (uint32_t)w.zero;
   p.sync = (unsigned*)(m->ws + w.sync);
   p.err = (int*)(m->ws + w.err);
   p.n_sync = w.n_sync;
@@ -425,6 +436,21 @@ md_status md_set_trace(md_model* m, uint64_t* dev_buf, int32_t n_per_wg) {
 }
 
 int32_t md_grid_size(const md_model* m) { return m ? m->grid : 0; }
+
+size_t md_packed_bytes(int64_t rows, int64_t cols) {
+  if (rows < 1 || cols < 32 || cols % 32) return 0;
+  return (size_t)((rows + 15) / 16) * (size_t)(cols / 32) * 1024;
+}
+
+md_status md_pack_weight(const void* src, void* dst, int64_t rows, int64_t cols, void* hip_stream) {
+  if (!src || !dst) return fail(MD_EINVAL, "src and dst must be non-NULL");
+  if (((uintptr_t)src & 15) || ((uintptr_t)dst & 15)) return fail(MD_EINVAL, "src and dst must be 16-byte aligned");
+  if (rows < 1 || cols < 32 || cols % 32) return fail(MD_EINVAL, "cols must be a positive multiple of 32");
+  if (md_packed_bytes(rows, cols) > 0xFFFFFFF0ull) return fail(MD_EUNSUPPORTED, "packed matrix exceeds 4 GiB");
+  hipError_t e = launch_pack(src, dst, rows, cols, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(MD_EHIP, "pack kernel: %s", hipGetErrorString(e));
+  return MD_OK;
+}
 
 void md_free_model(md_model* m) { delete m; }
 

@@ -109,18 +109,35 @@ __device__ void clear_next_bank(const Params& p) {
 }
 
 // ===================================================================== GEMV
-// Y[r][t] = sum_k W[r][k] * U[t][k] for this workgroup's rows of up to
-// MAXM matrices that share K.  W is bf16 [N][K] row-major; U is the
-// activation in "hi/lo" form: bf16[2][MAXB][K] (part, token, k) so that the
-// matrix-core B operand (32 k x 16 columns: token t hi at column 2t, lo at
-// 2t+1) is a single 16-byte load per lane.  Each workgroup owns rows
-// [N*w/G, N*(w+1)/G) of every matrix; rows are cut into 16-row tiles whose
-// tail rows fall outside the buffer resource and load as zero (no branch,
-// no bandwidth).  The four waves split the k-steps; each keeps DS k-steps
-// of weight and activation loads in flight.
+// Y[r][t] = sum_k W[r][k] * U[t][k] for this workgroup's rows of up to MAXM
+// matrices that share K.
+//
+// Weights are in the tiled layout md_pack_weight writes: 16-row tiles, and
+// within a tile one contiguous 1 KB block per 32-column k-step holding the
+// matrix-core A operand (lane l: row l%16, columns 8*(l/16)..+7), the block
+// ordered as four 256-byte quarters of 4 rows.  A tile's blocks are
+// consecutive, so every wave instruction reads 1 KB contiguous and each tile
+// is one sequential stream.
+//
+// U is the activation in hi/lo form, bf16[2][MAXB][K] (part, token, k): the
+// B operand (32 k x 16 columns: token t hi at column 2t, lo at 2t+1) is one
+// 16-byte load per lane.
+//
+// Work split: each matrix's rows are cut into 4-row quarters and workgroup w
+// owns quarters [Q*w/G, Q*(w+1)/G), so every workgroup streams the same
+// number of bytes.  Its rows form "slots" (tiles, possibly partial: lanes of
+// other quarters load nothing).  Slots are consumed in pairs; the four waves
+// split the k-steps of a pair and keep DS k-steps of loads in flight in one
+// continuous stream across pairs (no pipeline drain between tiles).
+// The workgroup's dynamic LDS.  Phases address it through this symbol (not
+// through a pointer argument) so that accesses compile to LDS instructions.
+extern __shared__ __attribute__((aligned(16))) char md_smem[];
+
 constexpr int MAXM = 3;
 constexpr int CMAX_DEV = 256;  // largest chunk count per (sequence, kv head)
-constexpr int MAXT = 8;
+constexpr int TG = 2;          // tiles consumed together (share one B operand load)
+constexpr int GDS = 16;        // k-steps in flight per wave
+constexpr int MAXSLOT = 64;    // slots per workgroup and phase (LM head: <= 41)
 
 struct GemvJob {
   const uint16_t* W[MAXM];
@@ -129,9 +146,8 @@ struct GemvJob {
   int K;
   uint32_t u_off;  // byte offset of U in the workspace
   int B;
+  bool pair;       // slot list interleaves matrices 0 and 1 tile by tile (SwiGLU)
 };
-
-__device__ __forceinline__ const void* urs_base_dummy() { return nullptr; }
 
 struct RowSplit {
   int r0, r1;
@@ -143,153 +159,199 @@ __device__ __forceinline__ RowSplit rows_of(int N, int w, int G) {
   return s;
 }
 
-// LDS layout used by the GEMV: per-wave partial tiles, then reduced Y.
+// One slot = one matrix-core tile of 16 output rows assembled from four
+// 4-row quarters, each from any matrix of the phase (a "virtual tile"): the
+// lanes of quarter position e read matrix m[e], global quarter gq[e]
+// (rows 4*gq .. 4*gq+3), through their own 64-bit addresses.  gq < 0: empty.
+struct Slot {
+  int8_t m[4];
+  int gq[4];
+};
+
 struct GemvSmem {
-  float red[NW][MAXT][16][16];
-  float y[MAXT][16][MAXB];
+  float red[NW][TG][16][16];
+  float y[TG][16][MAXB];
+  Slot slots[MAXSLOT];
+  int nslots;
 };
 
-// A planned GEMV: this workgroup's share of each matrix, cut into chunks of
-// up to MAXT tiles (local tile indices [i0, i1) of every matrix).
-struct GemvPlan {
-  const void* wbase[MAXM];
-  uint32_t wbytes[MAXM];
-  int r0[MAXM], nrows[MAXM];
-  int nm, K, B, per, maxtiles;
-  uint32_t u_off;
-};
-
-__device__ __forceinline__ GemvPlan plan_gemv(const Params& p, const GemvJob& job) {
-  GemvPlan g;
-  const int G = gridDim.x, w = blockIdx.x;
-  g.nm = job.nm;
-  g.K = job.K;
-  g.B = job.B;
-  g.u_off = job.u_off;
-  g.maxtiles = 0;
-#pragma unroll
-  for (int m = 0; m < MAXM; ++m) {
-    if (m < job.nm) {
-      RowSplit s = rows_of(job.N[m], w, G);
-      g.r0[m] = s.r0;
-      g.nrows[m] = s.r1 - s.r0;
-      int nt = (g.nrows[m] + 15) >> 4;
-      g.maxtiles = nt > g.maxtiles ? nt : g.maxtiles;
-      g.wbase[m] = job.W[m] + (size_t)s.r0 * job.K;
-      g.wbytes[m] = (uint32_t)((size_t)g.nrows[m] * job.K * 2);
+// Build this workgroup's slot list (thread 0) into LDS.  Normal mode packs
+// the workgroup's quarters of matrix 0, then 1, then 2, four per slot.  Pair
+// mode (SwiGLU) emits a slot of 4 gate quarters followed by the slot of the
+// same 4 up quarters.
+__device__ void build_slots(const GemvJob& job, GemvSmem& sm) {
+  if (threadIdx.x == 0) {
+    const int G = gridDim.x, w = blockIdx.x;
+    int n = 0, fill = 0;
+    Slot cur;
+    auto reset = [&]() {
+      for (int e = 0; e < 4; ++e) { cur.m[e] = 0; cur.gq[e] = -1; }
+      fill = 0;
+    };
+    reset();
+    if (job.pair) {
+      RowSplit q = rows_of((job.N[0] + 3) >> 2, w, G);
+      for (int g0 = q.r0; g0 < q.r1 && n + 2 <= MAXSLOT; g0 += 4) {
+        Slot a, b;
+        for (int e = 0; e < 4; ++e) {
+          int gq = g0 + e < q.r1 ? g0 + e : -1;
+          a.m[e] = 0; a.gq[e] = gq;
+          b.m[e] = 1; b.gq[e] = gq;
+        }
+        sm.slots[n++] = a;
+        sm.slots[n++] = b;
+      }
     } else {
-      g.r0[m] = 0;
-      g.nrows[m] = 0;
-      g.wbase[m] = p.ws;
-      g.wbytes[m] = 0;
+      for (int m = 0; m < job.nm; ++m) {
+        RowSplit q = rows_of((job.N[m] + 3) >> 2, w, G);
+        for (int gq = q.r0; gq < q.r1; ++gq) {
+          cur.m[fill] = (int8_t)m;
+          cur.gq[fill] = gq;
+          if (++fill == 4) {
+            if (n < MAXSLOT) sm.slots[n++] = cur;
+            reset();
+          }
+        }
+      }
+      if (fill > 0 && n < MAXSLOT) sm.slots[n++] = cur;
     }
-  }
-  g.per = MAXT / job.nm;
-  return g;
-}
-
-// Sweep K for T tile slots; slot t is local tile i0 + t % per of matrix
-// t / per (slots past the last matrix read nothing).
-template <int T, int DS>
-__device__ __forceinline__ void gemv_sweep(const GemvPlan& g, int i0, rsrc_t urs, GemvSmem& sm) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int K = g.K;
-  const int ksteps = K >> 5;
-  const int nks = (ksteps - wv + NW - 1) / NW;
-  rsrc_t ars[T];
-  uint32_t aoff[T];
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-    int m = t / g.per, i = i0 + t % g.per;
-    const void* wb = m == 0 ? g.wbase[0] : (m == 1 ? g.wbase[1] : g.wbase[2]);
-    uint32_t nb = m == 0 ? g.wbytes[0] : (m == 1 ? g.wbytes[1] : g.wbytes[2]);
-    if (m >= g.nm) nb = 0;
-    ars[t] = make_rsrc_u(wb, nb);
-    aoff[t] = ((uint32_t)(i * 16) + (lane & 15)) * (uint32_t)K * 2u + (lane >> 4) * 16u + wv * 64u;
-  }
-  const int n = lane & 15, tok = n >> 1, part = n & 1;
-  const uint32_t boff = tok < g.B ? g.u_off + (uint32_t)((part * MAXB + tok) * K) * 2u + (lane >> 4) * 16u + wv * 64u : OOB;
-  const uint32_t kstride = NW * 64u;
-  f32x4 acc[T];
-#pragma unroll
-  for (int t = 0; t < T; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  i32x4 ra[DS][T];
-  i32x4 rb[DS];
-#pragma unroll
-  for (int d = 0; d < DS; ++d) {
-    bool ok = d < nks;
-    uint32_t ko = (uint32_t)d * kstride;
-    rb[d] = ld_x4<CP_SC1>(urs, ok && boff != OOB ? boff + ko : OOB);
-#pragma unroll
-    for (int t = 0; t < T; ++t) ra[d][t] = ld_x4<CP_NT>(ars[t], ok ? aoff[t] + ko : OOB);
-  }
-  for (int base = 0; base < nks; base += DS) {
-#pragma unroll
-    for (int d = 0; d < DS; ++d) {
-      bf16x8 bop = __builtin_bit_cast(bf16x8, rb[d]);
-#pragma unroll
-      for (int t = 0; t < T; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ra[d][t]), bop, acc[t], 0, 0, 0);
-      int nx = base + d + DS;
-      bool ok = nx < nks;
-      uint32_t ko = (uint32_t)nx * kstride;
-      rb[d] = ld_x4<CP_SC1>(urs, ok && boff != OOB ? boff + ko : OOB);
-#pragma unroll
-      for (int t = 0; t < T; ++t) ra[d][t] = ld_x4<CP_NT>(ars[t], ok ? aoff[t] + ko : OOB);
-    }
-  }
-  // per-wave partial tiles -> LDS; lane holds rows 4*(lane/16)+i, column lane%16
-#pragma unroll
-  for (int t = 0; t < T; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sm.red[wv][t][4 * (lane >> 4) + i][n] = acc[t][i];
-  __syncthreads();
-  // reduce the waves and merge hi/lo columns: y[t][row][tok]
-  for (int e = threadIdx.x; e < T * 16 * MAXB; e += NT) {
-    int t = e / (16 * MAXB), r = (e / MAXB) % 16, k = e % MAXB;
-    float s = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) s += sm.red[w][t][r][2 * k] + sm.red[w][t][r][2 * k + 1];
-    sm.y[t][r][k] = s;
+    sm.nslots = n;
   }
   __syncthreads();
 }
 
-// One chunk of a planned GEMV; leaves Y in sm.y (slot m*per + local tile).
-__device__ __noinline__ void gemv_chunk(const Params& p, const GemvPlan& g, int i0, GemvSmem& sm) {
-  rsrc_t urs = make_rsrc_u(p.ws, p.ws_bytes);
-  int i1 = i0 + g.per < g.maxtiles ? i0 + g.per : g.maxtiles;
-  int cnt = (i1 - i0) * g.nm;
-  GemvPlan gg = g;
-  gg.per = i1 - i0;   // slots are packed: matrix m's tiles at m*(i1-i0)
-  if (cnt <= 1) gemv_sweep<1, 16>(gg, i0, urs, sm);
-  else if (cnt <= 2) gemv_sweep<2, 10>(gg, i0, urs, sm);
-  else if (cnt <= 4) gemv_sweep<4, 6>(gg, i0, urs, sm);
-  else gemv_sweep<8, 4>(gg, i0, urs, sm);
-}
-
-struct Chunk {
-  int i0, i1, nm;
-  int r0[MAXM], nrows[MAXM];
-};
-
-// Runs a GEMV over all of this WG's tiles; after each chunk `epi(sm, chunk)`
-// consumes sm.y, where slot m*(i1-i0) + (i - i0) holds local tile i of matrix m.
+// Run the GEMV; after each pair of slots epi(sm, slot_index0, count) reads
+// sm.y[i][row-in-slot][token] for slots slot_index0 + i (slot_row maps a row
+// of a slot back to its matrix and row).
 template <class Epi>
 __device__ __forceinline__ void run_gemv(const Params& p, const GemvJob& job, GemvSmem& sm, Epi&& epi) {
-  GemvPlan g = plan_gemv(p, job);
-  Chunk ch;
-  ch.nm = g.nm;
+  build_slots(job, sm);
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int K = job.K, KS = K >> 5;
+  const int nslots = __builtin_amdgcn_readfirstlane(sm.nslots);
+  const int ngroups = (nslots + TG - 1) / TG;
+  const int nks = (KS - wv + NW - 1) / NW;
+  const int total = ngroups * nks;
+  const rsrc_t urs = make_rsrc_u(p.ws, p.ws_bytes);
+  const int lq = (lane & 15) >> 2;  // this lane's quarter position in a slot
+  const uint32_t lchunk = (uint32_t)(((lane >> 4) * 4 + (lane & 3)) * 16);
+  const int n16 = lane & 15, tok = n16 >> 1, part = n16 & 1;
+  const uint32_t boff = tok < job.B ? job.u_off + (uint32_t)((part * MAXB + tok) * K) * 2u + (lane >> 4) * 16u : OOB;
+  const uint64_t tstride = (uint64_t)KS * 1024u;
+  const uint64_t zero_addr = (uint64_t)(p.ws + p.off_zero);
+  const uint32_t kstep_bytes = NW * 1024u;
+
+  const uint64_t w0 = (uint64_t)job.W[0], w1 = job.nm > 1 ? (uint64_t)job.W[1] : w0,
+                 w2 = job.nm > 2 ? (uint64_t)job.W[2] : w0;
+  // producer: per-lane address of each slot of the current group
+  int ig = 0, is = 0;
+  uint64_t pa[TG];
+  uint32_t pstep[TG];
+  auto set_group = [&](int g) __attribute__((always_inline)) {
 #pragma unroll
-  for (int m = 0; m < MAXM; ++m) { ch.r0[m] = g.r0[m]; ch.nrows[m] = g.nrows[m]; }
-  for (int i0 = 0; i0 < g.maxtiles; i0 += g.per) {
-    ch.i0 = i0;
-    ch.i1 = i0 + g.per < g.maxtiles ? i0 + g.per : g.maxtiles;
-    gemv_chunk(p, g, i0, sm);
-    epi(sm, ch);
+    for (int i = 0; i < TG; ++i) {
+      int si = g * TG + i;
+      bool v = si < nslots;
+      const Slot& sl = sm.slots[v ? si : 0];
+      int gq = v ? sl.gq[lq] : -1;
+      int m = sl.m[lq];
+      uint64_t W = m == 0 ? w0 : (m == 1 ? w1 : w2);
+      bool lv = gq >= 0;
+      pa[i] = lv ? W + (uint64_t)(gq >> 2) * tstride + (uint64_t)((gq & 3) * 256) + lchunk + (uint64_t)wv * 1024u
+                 : zero_addr;
+      pstep[i] = lv ? kstep_bytes : 0u;
+    }
+  };
+  set_group(0);
+  auto issue = [&](i32x4 (&ra)[TG], i32x4& rb) __attribute__((always_inline)) {
+    bool ok = ig < ngroups;
+#pragma unroll
+    for (int i = 0; i < TG; ++i) {
+      ra[i] = __builtin_nontemporal_load((const __attribute__((address_space(1))) i32x4*)(ok ? pa[i] : zero_addr));
+      pa[i] += pstep[i];
+    }
+    rb = ld_x4<CP_SC1>(urs, ok && boff != OOB ? boff + (uint32_t)(is * NW + wv) * 64u : OOB);
+    if (++is == nks) {
+      is = 0;
+      ++ig;
+      if (ig < ngroups) set_group(ig);
+    }
+  };
+  f32x4 acc[TG];
+#pragma unroll
+  for (int i = 0; i < TG; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  i32x4 ra[GDS][TG], rb[GDS];
+#pragma unroll
+  for (int d = 0; d < GDS; ++d) issue(ra[d], rb[d]);
+  int cg = 0, cs = 0;  // consumer group / k-step
+  // groups whose K sweep is finished by this wave are flushed in order; every
+  // wave passes the same number of group ends, so the barriers below match
+  auto flush = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < TG; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.red[wv][i][4 * (lane >> 4) + r][n16] = acc[i][r];
+#pragma unroll
+    for (int i = 0; i < TG; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     __syncthreads();
+    for (int e = threadIdx.x; e < TG * 16 * MAXB; e += NT) {
+      int i = e / (16 * MAXB), r = (e / MAXB) % 16, k = e % MAXB;
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) s += sm.red[w][i][r][2 * k] + sm.red[w][i][r][2 * k + 1];
+      sm.y[i][r][k] = s;
+    }
+    __syncthreads();
+    int n = nslots - cg * TG;
+    epi(sm, cg * TG, n < TG ? n : TG);
+    __syncthreads();
+  };
+  if (nks == 0) {
+    for (; cg < ngroups; ++cg) flush();
+    return;
+  }
+  for (int j0 = 0; j0 < total; j0 += GDS) {
+#pragma unroll
+    for (int d = 0; d < GDS; ++d) {
+      if (j0 + d < total) {
+        bf16x8 bop = __builtin_bit_cast(bf16x8, rb[d]);
+#pragma unroll
+        for (int i = 0; i < TG; ++i)
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ra[d][i]), bop, acc[i], 0, 0, 0);
+        issue(ra[d], rb[d]);
+        if (++cs == nks) {
+          cs = 0;
+          flush();
+          ++cg;
+        }
+      }
+    }
   }
 }
+
+// Row rr (0..15) of a slot: matrix and global row; false for an empty
+// quarter or a row past the matrix end.
+__device__ __forceinline__ bool slot_row(const Slot& sl, int rr, const int* N, int& m, int& row) {
+  int gq = sl.gq[rr >> 2];
+  if (gq < 0) return false;
+  m = sl.m[rr >> 2];
+  row = gq * 4 + (rr & 3);
+  return row < N[m];
+}
+
+// Rows of an N-row output this workgroup owns: 4-row quarters
+// [Q*w/G, Q*(w+1)/G), the split every projection uses.  The residual x is
+// private to the owner of its rows, so every phase that touches x must use
+// this same split.
+__device__ __forceinline__ RowSplit owned_rows(int N, int w, int G) {
+  RowSplit q = rows_of((N + 3) >> 2, w, G);
+  RowSplit r;
+  r.r0 = q.r0 * 4 < N ? q.r0 * 4 : N;
+  r.r1 = q.r1 * 4 < N ? q.r1 * 4 : N;
+  return r;
+}
+
 
 // ===================================================================== phases
 
@@ -325,11 +387,11 @@ struct SsqAcc {
 };
 
 // --- embedding: x[t] = E[tok_t] on this WG's hidden rows
-__device__ __noinline__ void phase_embed(const Params& p, float* sm_f) {
-  RowSplit s = rows_of(p.H, blockIdx.x, gridDim.x);
+__device__ __noinline__ void phase_embed(const Params& p) {
+  RowSplit s = owned_rows(p.H, blockIdx.x, gridDim.x);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   const uint16_t* g = p.layers[0].attn_norm;
-  float* part = sm_f;  // [NT][MAXB]
+  float* part = (float*)md_smem;  // [NT][MAXB]
   for (int t = 0; t < MAXB; ++t) part[threadIdx.x * MAXB + t] = 0.f;
   for (int e = threadIdx.x; e < (s.r1 - s.r0) * p.B; e += NT) {
     int t = e / (s.r1 - s.r0), i = s.r0 + e % (s.r1 - s.r0);
@@ -352,9 +414,9 @@ __device__ __noinline__ void phase_embed(const Params& p, float* sm_f) {
 }
 
 // --- QKV projection (GQA): raw q, k, v (RMS-normalised input) -> qkv[t][row]
-__device__ __noinline__ void phase_qkv(const Params& p, const LayerDesc& L, char* smem) {
-  GemvSmem& sm = *(GemvSmem*)smem;
-  float* inv = (float*)(smem + sizeof(GemvSmem));
+__device__ __noinline__ void phase_qkv(const Params& p, const LayerDesc& L) {
+  GemvSmem& sm = *(GemvSmem*)md_smem;
+  float* inv = (float*)(md_smem + sizeof(GemvSmem));
   load_inv_rms(p, inv, p.H);
   GemvJob j;
   j.nm = 3;
@@ -365,17 +427,16 @@ __device__ __noinline__ void phase_qkv(const Params& p, const LayerDesc& L, char
   j.u_off = p.off_u;
   j.B = p.B;
   const int nqkv = (p.nq + 2 * p.nkv) * p.hd;
+  j.pair = false;
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-  run_gemv(p, j, sm, [&](GemvSmem& s, const Chunk& c) {
-    int per = c.i1 - c.i0;
-    int col0[3] = {0, p.nq * p.hd, (p.nq + p.nkv) * p.hd};
-    for (int e = threadIdx.x; e < c.nm * per * 16 * p.B; e += NT) {
-      int t = e % p.B, rr = (e / p.B) % 16, slot = e / (p.B * 16);
-      int m = slot / per, i = c.i0 + slot % per;
-      int lr = i * 16 + rr;
-      if (lr >= c.nrows[m]) continue;
-      float v = s.y[slot][rr][t] * inv[t];
-      st_f32(r, p.off_qkv + (uint32_t)(t * nqkv + col0[m] + c.r0[m] + lr) * 4u, v);
+  run_gemv(p, j, sm, [&](GemvSmem& s, int slot0, int n) {
+    const int col0[3] = {0, p.nq * p.hd, (p.nq + p.nkv) * p.hd};
+    for (int e = threadIdx.x; e < n * 16 * p.B; e += NT) {
+      int t = e % p.B, rr = (e / p.B) % 16, i = e / (p.B * 16);
+      int m, row;
+      if (!slot_row(s.slots[slot0 + i], rr, j.N, m, row)) continue;
+      float v = s.y[i][rr][t] * inv[t];
+      st_f32(r, p.off_qkv + (uint32_t)(t * nqkv + col0[m] + row) * 4u, v);
     }
   });
 }
@@ -552,8 +613,8 @@ __device__ __noinline__ void attn_task_wave(const Params& p, AttnSmem& sm, int g
   }
 }
 
-__device__ __noinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L, int layer, char* smem) {
-  AttnSmem& sm = *(AttnSmem*)smem;
+__device__ __noinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L, int layer) {
+  AttnSmem& sm = *(AttnSmem*)md_smem;
   const int wv = threadIdx.x >> 6;
   const int hd = p.hd, gs = p.nq / p.nkv, B = p.B;
   const int C = p.attn_chunks;
@@ -689,9 +750,9 @@ __device__ __noinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L,
 
 // --- residual-owning projection: x[t][r] += W . U; next norm input + ssq
 __device__ __noinline__ void phase_residual_gemv(const Params& p, const uint16_t* W, int K, uint32_t u_off,
-                                    const uint16_t* g_next, char* smem) {
-  GemvSmem& sm = *(GemvSmem*)smem;
-  float* part = (float*)(smem + sizeof(GemvSmem));  // [NT][MAXB]
+                                    const uint16_t* g_next) {
+  GemvSmem& sm = *(GemvSmem*)md_smem;
+  float* part = (float*)(md_smem + sizeof(GemvSmem));  // [NT][MAXB]
   GemvJob j;
   j.nm = 1;
   j.W[0] = W;
@@ -700,15 +761,14 @@ __device__ __noinline__ void phase_residual_gemv(const Params& p, const uint16_t
   j.u_off = u_off;
   j.B = p.B;
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+  j.pair = false;
   for (int t = 0; t < MAXB; ++t) part[threadIdx.x * MAXB + t] = 0.f;
-  run_gemv(p, j, sm, [&](GemvSmem& s, const Chunk& c) {
-    int per = c.i1 - c.i0;
-    for (int e = threadIdx.x; e < per * 16 * p.B; e += NT) {
-      int t = e % p.B, rr = (e / p.B) % 16, slot = e / (p.B * 16);
-      int lr = (c.i0 + slot) * 16 + rr;
-      if (lr >= c.nrows[0]) continue;
-      int row = c.r0[0] + lr;
-      float x = p.x[t * p.H + row] + s.y[slot][rr][t];
+  run_gemv(p, j, sm, [&](GemvSmem& s, int slot0, int n) {
+    for (int e = threadIdx.x; e < n * 16 * p.B; e += NT) {
+      int t = e % p.B, rr = (e / p.B) % 16, i = e / (p.B * 16);
+      int m, row;
+      if (!slot_row(s.slots[slot0 + i], rr, j.N, m, row)) continue;
+      float x = p.x[t * p.H + row] + s.y[i][rr][t];
       p.x[t * p.H + row] = x;
       put_hilo(r, p.off_u, p.H, t, row, bf16_f32(g_next[row]) * x);
       part[threadIdx.x * MAXB + t] += x * x;
@@ -723,9 +783,9 @@ __device__ __noinline__ void phase_residual_gemv(const Params& p, const uint16_t
 }
 
 // --- dense SwiGLU gate/up: h = silu(inv*Wg U) * (inv*Wu U) -> hi/lo
-__device__ __noinline__ void phase_gateup(const Params& p, const uint16_t* Wg, const uint16_t* Wu, int F, char* smem) {
-  GemvSmem& sm = *(GemvSmem*)smem;
-  float* inv = (float*)(smem + sizeof(GemvSmem));
+__device__ __noinline__ void phase_gateup(const Params& p, const uint16_t* Wg, const uint16_t* Wu, int F) {
+  GemvSmem& sm = *(GemvSmem*)md_smem;
+  float* inv = (float*)(md_smem + sizeof(GemvSmem));
   load_inv_rms(p, inv, p.H);
   GemvJob j;
   j.nm = 2;
@@ -734,24 +794,25 @@ __device__ __noinline__ void phase_gateup(const Params& p, const uint16_t* Wg, c
   j.K = p.H;
   j.u_off = p.off_u;
   j.B = p.B;
+  j.pair = true;
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-  run_gemv(p, j, sm, [&](GemvSmem& s, const Chunk& c) {
-    int per = c.i1 - c.i0;
-    for (int e = threadIdx.x; e < per * 16 * p.B; e += NT) {
-      int t = e % p.B, rr = (e / p.B) % 16, li = e / (p.B * 16);
-      int lr = (c.i0 + li) * 16 + rr;
-      if (lr >= c.nrows[0]) continue;
-      float a = s.y[li][rr][t] * inv[t];
-      float u = s.y[per + li][rr][t] * inv[t];
-      put_hilo(r, p.off_h, F, t, c.r0[0] + lr, silu(a) * u);
+  run_gemv(p, j, sm, [&](GemvSmem& s, int slot0, int n) {
+    // slots come as (gate tile t, up tile t)
+    for (int e = threadIdx.x; e < 16 * p.B; e += NT) {
+      int t = e % p.B, rr = e / p.B;
+      int m, row;
+      if (n < 2 || !slot_row(s.slots[slot0], rr, j.N, m, row)) continue;
+      float a = s.y[0][rr][t] * inv[t];
+      float u = s.y[1][rr][t] * inv[t];
+      put_hilo(r, p.off_h, F, t, row, silu(a) * u);
     }
   });
 }
 
 // --- final norm + LM head: logits, per-WG argmax candidates
-__device__ __noinline__ void phase_lmhead(const Params& p, char* smem) {
-  GemvSmem& sm = *(GemvSmem*)smem;
-  float* inv = (float*)(smem + sizeof(GemvSmem));
+__device__ __noinline__ void phase_lmhead(const Params& p) {
+  GemvSmem& sm = *(GemvSmem*)md_smem;
+  float* inv = (float*)(md_smem + sizeof(GemvSmem));
   float* bv = inv + MAXB;                 // [NT][MAXB] best value
   int* bi = (int*)(bv + NT * MAXB);       // [NT][MAXB] best index
   load_inv_rms(p, inv, p.H);
@@ -763,15 +824,14 @@ __device__ __noinline__ void phase_lmhead(const Params& p, char* smem) {
   j.K = p.H;
   j.u_off = p.off_u;
   j.B = p.B;
+  j.pair = false;
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-  run_gemv(p, j, sm, [&](GemvSmem& s, const Chunk& c) {
-    int per = c.i1 - c.i0;
-    for (int e = threadIdx.x; e < per * 16 * p.B; e += NT) {
-      int t = e % p.B, rr = (e / p.B) % 16, slot = e / (p.B * 16);
-      int lr = (c.i0 + slot) * 16 + rr;
-      if (lr >= c.nrows[0]) continue;
-      int v = c.r0[0] + lr;
-      float lg = s.y[slot][rr][t] * inv[t];
+  run_gemv(p, j, sm, [&](GemvSmem& s, int slot0, int n) {
+    for (int e = threadIdx.x; e < n * 16 * p.B; e += NT) {
+      int t = e % p.B, rr = (e / p.B) % 16, i = e / (p.B * 16);
+      int m, v;
+      if (!slot_row(s.slots[slot0 + i], rr, j.N, m, v)) continue;
+      float lg = s.y[i][rr][t] * inv[t];
       p.logits[(size_t)t * p.V + v] = lg;
       float& cb = bv[threadIdx.x * MAXB + t];
       int& ci = bi[threadIdx.x * MAXB + t];
@@ -819,40 +879,68 @@ __device__ __noinline__ void final_argmax(const Params& p) {
 
 // ===================================================================== kernel
 extern "C" __global__ __launch_bounds__(NT) void md_megakernel(Params p) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
   if (p.B < 1 || p.B > MAXB) return;
   if (p.trace && threadIdx.x == 0 && p.trace_n > 0) p.trace[(size_t)blockIdx.x * p.trace_n + p.trace_n - 1] = wall_clock64();
   clear_next_bank(p);
   int sidx = 0;
-  phase_embed(p, (float*)smem);
+  phase_embed(p);
   grid_sync(p, sidx);
   for (int l = 0; l < p.n_layers; ++l) {
     const LayerDesc& L = p.layers[l];
     const uint16_t* g_next = (l + 1 < p.n_layers) ? p.layers[l + 1].attn_norm : p.final_norm;
-    phase_qkv(p, L, smem);
+    phase_qkv(p, L);
     grid_sync(p, sidx);
-    phase_attn_gqa(p, L, l, smem);
+    phase_attn_gqa(p, L, l);
     grid_sync(p, sidx);
-    phase_residual_gemv(p, L.wo, p.nq * p.hd, p.off_ou, L.ffn_norm, smem);
+    phase_residual_gemv(p, L.wo, p.nq * p.hd, p.off_ou, L.ffn_norm);
     grid_sync(p, sidx);
-    phase_gateup(p, L.w_gate, L.w_up, p.ffn, smem);
+    phase_gateup(p, L.w_gate, L.w_up, p.ffn);
     grid_sync(p, sidx);
-    phase_residual_gemv(p, L.w_down, p.ffn, p.off_h, g_next, smem);
+    phase_residual_gemv(p, L.w_down, p.ffn, p.off_h, g_next);
     grid_sync(p, sidx);
     if (dev_failed(p)) return;
   }
-  phase_lmhead(p, smem);
+  phase_lmhead(p);
   // the last workgroup to arrive reduces the argmax candidates
   bool last = arrive(p, sidx);
-  if (threadIdx.x == 0) ((int*)smem)[0] = last;
+  if (threadIdx.x == 0) ((int*)md_smem)[0] = last;
   __syncthreads();
-  if (((int*)smem)[0]) final_argmax(p);
+  if (((int*)md_smem)[0]) final_argmax(p);
 }
 
 }  // namespace md
 
 // ===================================================================== launch helpers
 namespace md {
+
+// Tiled weight layout (see the GEMV section): one thread per 16-byte chunk of
+// the packed output.  Chunk c of block (t, s) holds row t*16 + 4*(c/16) + c%4,
+// columns s*32 + 8*((c%16)/4) .. +7; rows past the matrix are zero.
+__global__ void k_pack_weight(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int64_t rows,
+                              int64_t cols) {
+  const int64_t S = cols / 32, T = (rows + 15) / 16;
+  const int64_t n = T * S * 64;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    int64_t blk = i >> 6;
+    int c = (int)(i & 63);
+    int64_t t = blk / S, s = blk % S;
+    int rr = (c >> 4) * 4 + (c & 3), j = (c & 15) >> 2;
+    int64_t r = t * 16 + rr;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < rows) v = *(const uint4*)(src + r * cols + s * 32 + j * 8);
+    *(uint4*)(dst + blk * 512 + c * 8) = v;
+  }
+}
+
+hipError_t launch_pack(const void* src, void* dst, int64_t rows, int64_t cols, hipStream_t stream) {
+  int64_t n = ((rows + 15) / 16) * (cols / 32) * 64;
+  int64_t g = (n + 255) / 256;
+  if (g > 65536) g = 65536;
+  if (g < 1) g = 1;
+  hipLaunchKernelGGL(k_pack_weight, dim3((unsigned)g), dim3(256), 0, stream, (const uint16_t*)src, (uint16_t*)dst,
+                     rows, cols);
+  return hipGetLastError();
+}
 
 size_t megakernel_smem_bytes() {
   size_t gemv = sizeof(GemvSmem) + MAXB * 4 + (size_t)NT * MAXB * 8 + 64;

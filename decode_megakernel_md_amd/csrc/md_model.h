@@ -62,6 +62,7 @@ struct Params {
   uint32_t off_ou;    // hi/lo bf16[2][MAXB][nq*hd]
   uint32_t off_h;     // hi/lo bf16[2][MAXB][F]
   uint32_t off_cand;  // argmax candidates {f32, i32}[G][MAXB]
+  uint32_t off_zero;  // 1 KB that stays zero (target of masked loads)
   unsigned* sync;     // counters, 2 banks
   int* err;
   int n_sync;

@@ -40,27 +40,37 @@ class DeviceModel:
         if [(s.name, s.rows, s.cols) for s in specs] != inv:
             raise RuntimeError("library weight inventory differs from the workload's tensor list")
         self.specs = specs
+        # matrices are stored tiled (md_pack_weight), norm gains as plain vectors
+        self.packed = [L.md_weight_layout(ctypes.byref(self.cfg), i) == 1 for i in range(len(specs))]
+        self.sizes = [L.md_packed_bytes(s.rows, s.cols) if pk else s.numel * 2 for s, pk in zip(specs, self.packed)]
         self.offsets = []
         off = 0
-        for s in specs:
+        for n in self.sizes:
             self.offsets.append(off)
-            off = _align(off + s.numel * 2)
+            off = _align(off + n)
         self.weight_bytes = sum(s.numel * 2 for s in specs)
         stream = torch.cuda.current_stream(self.device)
         sptr = stream.cuda_stream
         self.wbuf = torch.empty(off, dtype=torch.uint8, device=self.device)
         base = self.wbuf.data_ptr()
         overrides = overrides or {}
-        for s, o in zip(specs, self.offsets):
+        stage = torch.empty(max(s.numel * 2 for s in specs), dtype=torch.uint8, device=self.device)
+        for s, o, pk in zip(specs, self.offsets, self.packed):
+            dst = stage if pk else self.wbuf[o:o + s.numel * 2]
             if s.name in overrides:
                 a = np.ascontiguousarray(overrides[s.name], dtype=np.uint16).reshape(-1)
                 assert a.size == s.numel
-                self.wbuf[o:o + s.numel * 2].copy_(torch.from_numpy(a.view(np.uint8)))
+                dst[:s.numel * 2].copy_(torch.from_numpy(a.view(np.uint8)))
             elif s.kind == "gain" and s.sigma != 0.0:
                 a = synth.weight_host(w, s).reshape(-1)
-                self.wbuf[o:o + s.numel * 2].copy_(torch.from_numpy(a.view(np.uint8)))
+                dst[:s.numel * 2].copy_(torch.from_numpy(a.view(np.uint8)))
             else:
-                synth.weight_device(w, s, base + o, sptr)
+                synth.weight_device(w, s, dst.data_ptr(), sptr)
+            if pk:
+                check(L.md_pack_weight(ctypes.c_void_p(stage.data_ptr()), ctypes.c_void_p(base + o), s.rows, s.cols,
+                                       ctypes.c_void_p(sptr)))
+        torch.cuda.synchronize(self.device)
+        del stage
         self.ws_bytes = L.md_workspace_bytes(ctypes.byref(self.cfg))
         if self.ws_bytes == 0:  # the configuration was rejected: surface the library's reason
             check(L.md_init_model(ctypes.byref(self.cfg), None, 0, None, 0, None, ctypes.byref(ctypes.c_void_p())))

@@ -25,8 +25,11 @@
  *    time; calls on one handle must not overlap.
  *  - Return values are md_status codes.  On failure nothing is enqueued and
  *    md_last_error() describes the cause.
- *  - Weights are bf16, logical row-major [out][in], one device buffer per
- *    tensor, in the order md_weight_info enumerates (16-byte aligned).
+ *  - Weights are bf16, one device buffer per tensor, in the order
+ *    md_weight_info enumerates (16-byte aligned).  The embedding table and
+ *    the norm gains are plain row-major; every other matrix (logical
+ *    row-major [out][in]) is passed in the tiled layout md_pack_weight
+ *    writes (md_weight_layout tells which).
  *  - Activations and accumulations are fp32; projections run on bf16 matrix
  *    cores with each fp32 activation split into two bf16 halves (hi + lo),
  *    which keeps about 16 significant bits of the activation.
@@ -79,6 +82,26 @@ size_t md_weight_count(const md_config* cfg);
  * for i out of range. */
 md_status md_weight_info(const md_config* cfg, size_t i, char* name, size_t name_cap, int64_t* rows,
                          int64_t* cols);
+
+/* Layout tensor i must be passed in: 0 = plain row-major, 1 = tiled
+ * (md_pack_weight); -1 for an index out of range. */
+int32_t md_weight_layout(const md_config* cfg, size_t i);
+
+/* Tiled weight layout.  A matrix W[rows][cols] (cols a multiple of 32) is
+ * cut into tiles of 16 rows (the last one zero-padded) and each tile into
+ * k-steps of 32 columns.  Block (t, s) is 1024 contiguous bytes at offset
+ * (t * cols/32 + s) * 1024, made of 64 chunks of 16 bytes; chunk c holds the
+ * 8 bf16 values W[16t + 4*(c/16) + c%4][32s + 8*((c%16)/4) .. +7].  So a
+ * block is exactly the operand one wave's 16x16x32 matrix instruction needs,
+ * split into four 256-byte quarters of 4 rows, and a tile's blocks follow
+ * each other: streaming a tile is one sequential read.
+ * md_packed_bytes returns 0 for shapes the layout does not support. */
+size_t md_packed_bytes(int64_t rows, int64_t cols);
+
+/* Convert one row-major bf16 matrix (dev src) into the tiled layout (dev dst,
+ * md_packed_bytes(rows, cols) bytes, must not overlap src).  Enqueued on
+ * hip_stream. */
+md_status md_pack_weight(const void* src, void* dst, int64_t rows, int64_t cols, void* hip_stream);
 
 /* Bytes of device workspace the library needs (layer table, activation
  * buffers, partial results, sync counters).  The workspace is owned by the

@@ -23,12 +23,29 @@ def _model(w, overrides=None):
     return DeviceModel(w, overrides=overrides)
 
 
+def unpack_tiled(raw: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """Inverse of the tiled layout md.h documents, written from that text:
+    block (t, s) at (t*S + s)*1024 bytes, chunk c -> row 16t + 4*(c//16) + c%4,
+    columns 32s + 8*((c%16)//4) .. +7."""
+    S, T = cols // 32, (rows + 15) // 16
+    blocks = raw.view(np.uint16).reshape(T, S, 64, 8)
+    out = np.zeros((T * 16, cols), dtype=np.uint16)
+    for c in range(64):
+        rr = 4 * (c // 16) + c % 4
+        j = (c % 16) // 4
+        for t in range(T):
+            out[t * 16 + rr].reshape(S, 32)[:, 8 * j:8 * j + 8] = blocks[t, :, c, :]
+    assert not out[rows:].any(), "padding rows must be zero"
+    return out[:rows]
+
+
 def test_device_draws_match_host_draws(torch_cuda):
     torch = torch_cuda
     w = WL.mini_dense()
     m = _model(w)
-    for s, o in zip(m.specs[:6], m.offsets[:6]):
-        got = m.wbuf[o:o + s.numel * 2].cpu().numpy().view(np.uint16).reshape(s.rows, s.cols)
+    for s, o, n, pk in list(zip(m.specs, m.offsets, m.sizes, m.packed))[:8]:
+        raw = m.wbuf[o:o + n].cpu().numpy()
+        got = unpack_tiled(raw, s.rows, s.cols) if pk else raw.view(np.uint16).reshape(s.rows, s.cols)
         assert np.array_equal(got, synth.weight_host(w, s)), s.name
     kv = m.kv_host()
     for l in range(w.n_layers):

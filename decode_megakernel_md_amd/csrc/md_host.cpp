@@ -1,5 +1,6 @@
 // Host side of libmd.so: the C ABI declared in md.h.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -130,7 +131,8 @@ md_status validate(const md_config* c) {
 }
 
 struct WsLayout {
-  size_t layers, experts, x, u, ssq, qkv, attn, attn_ml, ou, h, cand, zero, sync, err, total;
+  size_t layers, experts, x, u, ssq, qkv, attn, attn_ml, ou, h, cand, zero, rope, sync, err, total;
+  int rope_d;
   int n_sync, sync_attn_base;
 };
 
@@ -160,6 +162,8 @@ WsLayout ws_layout(const md_config* c) {
   w.h = take(2 * 2 * MAXB_ * (size_t)F);
   w.cand = take(8 * (size_t)GMAX * MAXB_);
   w.zero = take(1024);
+  w.rope_d = c->attn_kind == 0 ? c->head_dim : c->rope_dim;
+  w.rope = take(sizeof(float) * 2 * (size_t)c->max_ctx * (size_t)(w.rope_d / 2));
   w.sync_attn_base = 1 + 5 * c->n_layers + 2;
   w.n_sync = w.sync_attn_base + c->n_layers + 2;
   w.sync = take(4 * 2 * (size_t)w.n_sync * SP_WORDS_);
@@ -321,8 +325,17 @@ md_status md_init_model(const md_config* cfg, const void* const* weights, size_t
       for (int x = 0; x < cfg->n_experts * 3; ++x) ex.push_back(weights[wi++]);
     }
   }
+  // rotary table: angle pos * theta^(-2i/d) in fp64, cos and sin rounded to fp32
+  std::vector<float> rope((size_t)cfg->max_ctx * (lay.rope_d / 2) * 2);
+  for (int pos = 0; pos < cfg->max_ctx; ++pos)
+    for (int i = 0; i < lay.rope_d / 2; ++i) {
+      double a = (double)pos * pow((double)cfg->rope_theta, -2.0 * i / (double)lay.rope_d);
+      rope[((size_t)pos * (lay.rope_d / 2) + i) * 2] = (float)cos(a);
+      rope[((size_t)pos * (lay.rope_d / 2) + i) * 2 + 1] = (float)sin(a);
+    }
   hipStream_t s = (hipStream_t)hip_stream;
   e = hipMemcpyAsync(m->ws + lay.layers, L.data(), sizeof(LayerDesc) * L.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(m->ws + lay.rope, rope.data(), sizeof(float) * rope.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess && !ex.empty())
     e = hipMemcpyAsync(m->ws + lay.experts, ex.data(), sizeof(void*) * ex.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipMemsetAsync(m->ws + lay.sync, 0, lay.err + 256 - lay.sync, s);
@@ -368,6 +381,7 @@ static md_status fill_params(md_model* m, const int32_t* tokens, const int32_t* 
   p.x = (float*)(m->ws + w.x);
   p.off_u = (uint32_t)w.u; p.off_ssq = (uint32_t)w.ssq; p.off_qkv = (uint32_t)w.qkv; p.off_attn = (uint32_t)w.attn; p.off_attn_ml = (uint32_t)w.attn_ml;
   p.off_ou = (uint32_t)w.ou; p.off_h = (uint32_t)w.h; p.off_cand = (uint32_t)w.cand; p.off_zero = (uint32_t)w.zero;
+  p.rope = (const float*)(m->ws + w.rope); p.rope_d = w.rope_d;
   p.sync = (unsigned*)(m->ws + w.sync);
   p.err = (int*)(m->ws + w.err);
   p.n_sync = w.n_sync;

@@ -90,6 +90,15 @@ __device__ __forceinline__ void stamp(const Params& p, int slot) {
   if (p.trace && threadIdx.x == 0 && slot < p.trace_n) p.trace[(size_t)blockIdx.x * p.trace_n + slot] = wall_clock64();
 }
 
+// Sub-phase stamps: slot trace_n/2 + 4*(phase index) + k, k < 4.
+__shared__ int md_cur_phase;
+__device__ __forceinline__ void sub_stamp(const Params& p, int k) {
+  if (p.trace && threadIdx.x == 0) {
+    int slot = p.trace_n / 2 + 4 * md_cur_phase + k;
+    if (slot < p.trace_n - 1) p.trace[(size_t)blockIdx.x * p.trace_n + slot] = wall_clock64();
+  }
+}
+
 // Sync point sidx: stamps 2*sidx (work done) and 2*sidx+1 (wait over).
 __device__ __forceinline__ void grid_sync(const Params& p, int& sidx) {
   stamp(p, 2 * sidx);
@@ -97,6 +106,7 @@ __device__ __forceinline__ void grid_sync(const Params& p, int& sidx) {
   wait_all(p, sidx);
   stamp(p, 2 * sidx + 1);
   ++sidx;
+  if (threadIdx.x == 0) md_cur_phase = sidx;
 }
 
 // clear this WG's share of the other bank (used by the next step)
@@ -136,8 +146,8 @@ extern __shared__ __attribute__((aligned(16))) char md_smem[];
 constexpr int MAXM = 3;
 constexpr int CMAX_DEV = 256;  // largest chunk count per (sequence, kv head)
 constexpr int TG = 2;          // tiles consumed together (share one B operand load)
-constexpr int GDS = 16;        // k-steps in flight per wave
-constexpr int MAXSLOT = 64;    // slots per workgroup and phase (LM head: <= 41)
+constexpr int GDS = 12;        // k-steps in flight per wave
+constexpr int MAXSLOT = 48;    // slots per workgroup and phase (LM head: <= 41)
 
 struct GemvJob {
   const uint16_t* W[MAXM];
@@ -169,10 +179,17 @@ struct Slot {
 };
 
 struct GemvSmem {
-  float red[NW][TG][16][16];
+  float red[NW][TG][16][16];   // also reused as [NT][MAXB] scratch after the stream
   float y[TG][16][MAXB];
   Slot slots[MAXSLOT];
   int nslots;
+  // epilogue staging, indexed [slot*16 + row-in-slot][token]: inputs read
+  // before the weight stream starts, outputs written after it ends, so the
+  // stream itself issues no other memory operation
+  float in[MAXSLOT * 16][MAXB];
+  float out[MAXSLOT * 16][MAXB];
+  float gain[MAXSLOT * 16];
+  float inv[MAXB];
 };
 
 // Build this workgroup's slot list (thread 0) into LDS.  Normal mode packs
@@ -223,111 +240,128 @@ __device__ void build_slots(const GemvJob& job, GemvSmem& sm) {
 // Run the GEMV; after each pair of slots epi(sm, slot_index0, count) reads
 // sm.y[i][row-in-slot][token] for slots slot_index0 + i (slot_row maps a row
 // of a slot back to its matrix and row).
+// The GEMV's LDS block, addressed through the LDS symbol itself (never
+// through a pointer held in a closure or passed by value), so that every
+// access compiles to an LDS instruction: a flat or scratch access inside the
+// stream would make the next wait drain the whole prefetch ring.
+#define GSM (*reinterpret_cast<GemvSmem*>(md_smem))
+
+// Per-lane source of one slot of the current group.
+__device__ __forceinline__ void slot_src(int si, int nslots, int lq, uint64_t w0, uint64_t w1, uint64_t w2,
+                                         uint64_t tstride, uint32_t lchunk, int wv, uint64_t zero_addr, uint64_t& pa,
+                                         uint32_t& pstep) {
+  bool v = si < nslots;
+  int gq = v ? GSM.slots[si].gq[lq] : -1;
+  int m = v ? GSM.slots[si].m[lq] : 0;
+  uint64_t W = m == 0 ? w0 : (m == 1 ? w1 : w2);
+  bool lv = gq >= 0;
+  pa = lv ? W + (uint64_t)(gq >> 2) * tstride + (uint64_t)((gq & 3) * 256) + lchunk + (uint64_t)wv * 1024u : zero_addr;
+  pstep = lv ? (uint32_t)(NW * 1024) : 0u;
+}
+
+// Reduce the four waves' partial tiles of a finished group into GSM.y.
+__device__ __forceinline__ void gemv_reduce(const f32x4 (&acc)[TG], int wv, int lane) {
+#pragma unroll
+  for (int i = 0; i < TG; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) GSM.red[wv][i][4 * (lane >> 4) + r][lane & 15] = acc[i][r];
+  __syncthreads();
+  for (int e = threadIdx.x; e < TG * 16 * MAXB; e += NT) {
+    int i = e / (16 * MAXB), r = (e / MAXB) % 16, k = e % MAXB;
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) s += GSM.red[w][i][r][2 * k] + GSM.red[w][i][r][2 * k + 1];
+    GSM.y[i][r][k] = s;
+  }
+  __syncthreads();
+}
+
+// Run the GEMV over GSM's slot list.  After each finished pair of slots,
+// epi(slot_index0, count) reads GSM.y[i][row-in-slot][token] (LDS only).
 template <class Epi>
-__device__ __forceinline__ void run_gemv(const Params& p, const GemvJob& job, GemvSmem& sm, Epi&& epi) {
-  build_slots(job, sm);
+__device__ __forceinline__ void run_gemv(const GemvJob& job, const uint8_t* ws, uint32_t ws_bytes, uint32_t off_zero,
+                                         Epi epi) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int K = job.K, KS = K >> 5;
-  const int nslots = __builtin_amdgcn_readfirstlane(sm.nslots);
+  const int nslots = __builtin_amdgcn_readfirstlane(GSM.nslots);
   const int ngroups = (nslots + TG - 1) / TG;
   const int nks = (KS - wv + NW - 1) / NW;
   const int total = ngroups * nks;
-  const rsrc_t urs = make_rsrc_u(p.ws, p.ws_bytes);
-  const int lq = (lane & 15) >> 2;  // this lane's quarter position in a slot
+  const rsrc_t urs = make_rsrc_u(ws, ws_bytes);
+  const int lq = (lane & 15) >> 2;
   const uint32_t lchunk = (uint32_t)(((lane >> 4) * 4 + (lane & 3)) * 16);
   const int n16 = lane & 15, tok = n16 >> 1, part = n16 & 1;
   const uint32_t boff = tok < job.B ? job.u_off + (uint32_t)((part * MAXB + tok) * K) * 2u + (lane >> 4) * 16u : OOB;
   const uint64_t tstride = (uint64_t)KS * 1024u;
-  const uint64_t zero_addr = (uint64_t)(p.ws + p.off_zero);
-  const uint32_t kstep_bytes = NW * 1024u;
-
+  const uint64_t zero_addr = (uint64_t)(ws + off_zero);
   const uint64_t w0 = (uint64_t)job.W[0], w1 = job.nm > 1 ? (uint64_t)job.W[1] : w0,
                  w2 = job.nm > 2 ? (uint64_t)job.W[2] : w0;
-  // producer: per-lane address of each slot of the current group
   int ig = 0, is = 0;
-  uint64_t pa[TG];
-  uint32_t pstep[TG];
-  auto set_group = [&](int g) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < TG; ++i) {
-      int si = g * TG + i;
-      bool v = si < nslots;
-      const Slot& sl = sm.slots[v ? si : 0];
-      int gq = v ? sl.gq[lq] : -1;
-      int m = sl.m[lq];
-      uint64_t W = m == 0 ? w0 : (m == 1 ? w1 : w2);
-      bool lv = gq >= 0;
-      pa[i] = lv ? W + (uint64_t)(gq >> 2) * tstride + (uint64_t)((gq & 3) * 256) + lchunk + (uint64_t)wv * 1024u
-                 : zero_addr;
-      pstep[i] = lv ? kstep_bytes : 0u;
-    }
-  };
-  set_group(0);
-  auto issue = [&](i32x4 (&ra)[TG], i32x4& rb) __attribute__((always_inline)) {
-    bool ok = ig < ngroups;
-#pragma unroll
-    for (int i = 0; i < TG; ++i) {
-      ra[i] = __builtin_nontemporal_load((const __attribute__((address_space(1))) i32x4*)(ok ? pa[i] : zero_addr));
-      pa[i] += pstep[i];
-    }
-    rb = ld_x4<CP_SC1>(urs, ok && boff != OOB ? boff + (uint32_t)(is * NW + wv) * 64u : OOB);
-    if (++is == nks) {
-      is = 0;
-      ++ig;
-      if (ig < ngroups) set_group(ig);
-    }
-  };
+  uint64_t pa0, pa1;
+  uint32_t ps0, ps1;
+  slot_src(0, nslots, lq, w0, w1, w2, tstride, lchunk, wv, zero_addr, pa0, ps0);
+  slot_src(1, nslots, lq, w0, w1, w2, tstride, lchunk, wv, zero_addr, pa1, ps1);
+  static_assert(TG == 2, "the stream handles slot pairs");
+#define GEMV_ISSUE(RA, RB)                                                                                      \
+  {                                                                                                             \
+    bool ok_ = ig < ngroups;                                                                                    \
+    RA[0] = __builtin_nontemporal_load((const __attribute__((address_space(1))) i32x4*)(ok_ ? pa0 : zero_addr)); \
+    RA[1] = __builtin_nontemporal_load((const __attribute__((address_space(1))) i32x4*)(ok_ ? pa1 : zero_addr)); \
+    pa0 += ps0;                                                                                                 \
+    pa1 += ps1;                                                                                                 \
+    RB = ld_x4<CP_SC1>(urs, ok_ && boff != OOB ? boff + (uint32_t)(is * NW + wv) * 64u : OOB);                  \
+    if (++is == nks) {                                                                                          \
+      is = 0;                                                                                                   \
+      ++ig;                                                                                                     \
+      if (ig < ngroups) {                                                                                       \
+        slot_src(ig * TG, nslots, lq, w0, w1, w2, tstride, lchunk, wv, zero_addr, pa0, ps0);                   \
+        slot_src(ig * TG + 1, nslots, lq, w0, w1, w2, tstride, lchunk, wv, zero_addr, pa1, ps1);               \
+      }                                                                                                         \
+    }                                                                                                           \
+  }
   f32x4 acc[TG];
 #pragma unroll
   for (int i = 0; i < TG; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   i32x4 ra[GDS][TG], rb[GDS];
 #pragma unroll
-  for (int d = 0; d < GDS; ++d) issue(ra[d], rb[d]);
-  int cg = 0, cs = 0;  // consumer group / k-step
-  // groups whose K sweep is finished by this wave are flushed in order; every
-  // wave passes the same number of group ends, so the barriers below match
-  auto flush = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < TG; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm.red[wv][i][4 * (lane >> 4) + r][n16] = acc[i][r];
-#pragma unroll
-    for (int i = 0; i < TG; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    __syncthreads();
-    for (int e = threadIdx.x; e < TG * 16 * MAXB; e += NT) {
-      int i = e / (16 * MAXB), r = (e / MAXB) % 16, k = e % MAXB;
-      float s = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) s += sm.red[w][i][r][2 * k] + sm.red[w][i][r][2 * k + 1];
-      sm.y[i][r][k] = s;
-    }
-    __syncthreads();
-    int n = nslots - cg * TG;
-    epi(sm, cg * TG, n < TG ? n : TG);
-    __syncthreads();
-  };
+  for (int d = 0; d < GDS; ++d) GEMV_ISSUE(ra[d], rb[d]);
+  int cg = 0, cs = 0;
   if (nks == 0) {
-    for (; cg < ngroups; ++cg) flush();
+    for (; cg < ngroups; ++cg) {
+      gemv_reduce(acc, wv, lane);
+      int n = nslots - cg * TG;
+      epi(cg * TG, n < TG ? n : TG);
+      __syncthreads();
+    }
     return;
   }
+  // The body is unconditional: steps past the end read the zero block and
+  // add nothing.  (A guarded body would make the compiler assume the later
+  // loads of the previous round may be missing and wait for all of them.)
   for (int j0 = 0; j0 < total; j0 += GDS) {
 #pragma unroll
     for (int d = 0; d < GDS; ++d) {
-      if (j0 + d < total) {
-        bf16x8 bop = __builtin_bit_cast(bf16x8, rb[d]);
+      bf16x8 bop = __builtin_bit_cast(bf16x8, rb[d]);
 #pragma unroll
-        for (int i = 0; i < TG; ++i)
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ra[d][i]), bop, acc[i], 0, 0, 0);
-        issue(ra[d], rb[d]);
+      for (int i = 0; i < TG; ++i)
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ra[d][i]), bop, acc[i], 0, 0, 0);
+      GEMV_ISSUE(ra[d], rb[d]);
+      if (j0 + d < total) {
         if (++cs == nks) {
           cs = 0;
-          flush();
+          gemv_reduce(acc, wv, lane);
+#pragma unroll
+          for (int i = 0; i < TG; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+          int n = nslots - cg * TG;
+          epi(cg * TG, n < TG ? n : TG);
+          __syncthreads();
           ++cg;
         }
       }
     }
   }
+#undef GEMV_ISSUE
 }
 
 // Row rr (0..15) of a slot: matrix and global row; false for an empty
@@ -358,15 +392,28 @@ __device__ __forceinline__ RowSplit owned_rows(int N, int w, int G) {
 // inv_rms[t] from the per-WG partial sums of squares (fixed order: identical
 // in every workgroup).  ssq: fp32[G][MAXB] at ws offset p.off_ssq.
 __device__ __noinline__ void load_inv_rms(const Params& p, float* inv_rms, int n_feat) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-    for (int t = 0; t < p.B; ++t) {
-      float s = 0.f;
-      for (int g = lane; g < (int)gridDim.x; g += 64) s += ld_f32(r, p.off_ssq + (uint32_t)(g * MAXB + t) * 4u);
-      s = wave_sum(s);
-      if (lane == 0) inv_rms[t] = 1.0f / sqrtf(s / (float)n_feat + p.eps);
+  // every thread fetches one workgroup's partials for all tokens (one round
+  // trip), then wave w reduces tokens 2w, 2w+1 in a fixed order
+  float* stage = (float*)(md_smem + sizeof(GemvSmem));  // [G][MAXB]
+  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+  for (int g = threadIdx.x; g < (int)gridDim.x; g += NT) {
+    i32x4 a = ld_x4<CP_SC1>(r, p.off_ssq + (uint32_t)(g * MAXB) * 4u);
+    i32x4 b = ld_x4<CP_SC1>(r, p.off_ssq + (uint32_t)(g * MAXB + 4) * 4u);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      stage[g * MAXB + k] = __int_as_float(a[k]);
+      stage[g * MAXB + 4 + k] = __int_as_float(b[k]);
     }
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    int t = 2 * wv + k;
+    float s = 0.f;
+    for (int g = lane; g < (int)gridDim.x; g += 64) s += stage[g * MAXB + t];
+    s = wave_sum(s);
+    if (lane == 0) inv_rms[t] = 1.0f / sqrtf(s / (float)n_feat + p.eps);
   }
   __syncthreads();
 }
@@ -416,8 +463,6 @@ __device__ __noinline__ void phase_embed(const Params& p) {
 // --- QKV projection (GQA): raw q, k, v (RMS-normalised input) -> qkv[t][row]
 __device__ __noinline__ void phase_qkv(const Params& p, const LayerDesc& L) {
   GemvSmem& sm = *(GemvSmem*)md_smem;
-  float* inv = (float*)(md_smem + sizeof(GemvSmem));
-  load_inv_rms(p, inv, p.H);
   GemvJob j;
   j.nm = 3;
   j.W[0] = L.wq; j.N[0] = p.nq * p.hd;
@@ -426,29 +471,36 @@ __device__ __noinline__ void phase_qkv(const Params& p, const LayerDesc& L) {
   j.K = p.H;
   j.u_off = p.off_u;
   j.B = p.B;
-  const int nqkv = (p.nq + 2 * p.nkv) * p.hd;
   j.pair = false;
-  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-  run_gemv(p, j, sm, [&](GemvSmem& s, int slot0, int n) {
-    const int col0[3] = {0, p.nq * p.hd, (p.nq + p.nkv) * p.hd};
-    for (int e = threadIdx.x; e < n * 16 * p.B; e += NT) {
-      int t = e % p.B, rr = (e / p.B) % 16, i = e / (p.B * 16);
-      int m, row;
-      if (!slot_row(s.slots[slot0 + i], rr, j.N, m, row)) continue;
-      float v = s.y[i][rr][t] * inv[t];
-      st_f32(r, p.off_qkv + (uint32_t)(t * nqkv + col0[m] + row) * 4u, v);
+  const int B = p.B;
+  build_slots(j, sm);
+  load_inv_rms(p, sm.inv, p.H);
+  sub_stamp(p, 0);
+  run_gemv(j, p.ws, p.ws_bytes, p.off_zero, [=](int slot0, int n) {
+    for (int e = threadIdx.x; e < n * 16 * B; e += NT) {
+      int t = e % B, rr = (e / B) % 16, i = e / (B * 16);
+      GSM.out[(slot0 + i) * 16 + rr][t] = GSM.y[i][rr][t] * GSM.inv[t];
     }
   });
+  sub_stamp(p, 2);
+  const int nqkv = (p.nq + 2 * p.nkv) * p.hd;
+  const int col0[3] = {0, p.nq * p.hd, (p.nq + p.nkv) * p.hd};
+  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+  for (int e = threadIdx.x; e < sm.nslots * 16 * B; e += NT) {
+    int t = e % B, sr = e / B;
+    int m, row;
+    if (!slot_row(sm.slots[sr >> 4], sr & 15, j.N, m, row)) continue;
+    st_f32(r, p.off_qkv + (uint32_t)(t * nqkv + col0[m] + row) * 4u, sm.out[sr][t]);
+  }
 }
 
-// RoPE angle for pair index i of a head of dim d at position pos, from fp64.
-__device__ __forceinline__ void rope_cs(int64_t pos, int i, int d, float theta, float& c, float& s) {
-  double inv = pow((double)theta, -2.0 * (double)i / (double)d);
-  double a = (double)pos * inv;
-  double sd, cd;
-  sincos(a, &sd, &cd);
-  c = (float)cd;
-  s = (float)sd;
+// RoPE rotation of pair i at position pos: (cos, sin) from the table the
+// host fills at init (angles pos * theta^(-2i/d) evaluated in fp64, rounded
+// to fp32), fp32[max_ctx][d/2][2].
+__device__ __forceinline__ void rope_cs(const Params& p, int pos, int i, float& c, float& s) {
+  const float* t = p.rope + ((size_t)pos * (p.rope_d / 2) + i) * 2;
+  c = t[0];
+  s = t[1];
 }
 
 // --- GQA decode attention.  Task (b, kv head g, chunk c) covers cached
@@ -497,12 +549,13 @@ __device__ __forceinline__ void load_block(KVBlock<HD>& r, rsrc_t krs, rsrc_t vr
   }
 }
 
-template <int HD>
-__device__ __noinline__ void attn_task_wave(const Params& p, AttnSmem& sm, int gs, const uint16_t* kc,
-                                            const uint16_t* vc, uint32_t nbytes, int w0, int w1) {
+#define ASM (*reinterpret_cast<AttnSmem*>(md_smem))
+
+template <int HD, int GS>
+__device__ __noinline__ void attn_task_wave(const uint16_t* kc, const uint16_t* vc, uint32_t nbytes, int w0, int w1) {
+  constexpr int gs = GS;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const rsrc_t krs = make_rsrc_u(kc, nbytes), vrs = make_rsrc_u(vc, nbytes);
-  gs = __builtin_amdgcn_readfirstlane(gs);
   w0 = __builtin_amdgcn_readfirstlane(w0);
   w1 = __builtin_amdgcn_readfirstlane(w1);
   const int nn = lane & 15, hh = nn >> 1, pp = nn & 1;
@@ -513,15 +566,15 @@ __device__ __noinline__ void attn_task_wave(const Params& p, AttnSmem& sm, int g
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       int d = s * 32 + (lane >> 4) * 8 + k;
-      float v = hh < gs ? sm.q[hh][d] : 0.f;
+      float v = hh < gs ? ASM.q[hh][d] : 0.f;
       uint16_t hi, lo;
       split_hilo(v, hi, lo);
       qb[s][k] = __builtin_bit_cast(__bf16, pp ? lo : hi);
     }
   }
-  float m_run[MAXB], l_run[MAXB], acc[MAXB][8];
+  float m_run[GS], l_run[GS], acc[GS][8];
 #pragma unroll
-  for (int h = 0; h < MAXB; ++h) {
+  for (int h = 0; h < GS; ++h) {
     m_run[h] = -INFINITY;
     l_run[h] = 0.f;
 #pragma unroll
@@ -539,16 +592,16 @@ __device__ __noinline__ void attn_task_wave(const Params& p, AttnSmem& sm, int g
       for (int i = 0; i < 4; ++i) {
         float v = a[i] + __shfl_xor(a[i], 1, 64);
         int pr = tt * 16 + 4 * (lane >> 4) + i;
-        if (!pp && hh < gs) sm.s[wv][pr][hh] = (blk + pr < w1) ? v : -INFINITY;
+        if (!pp && hh < gs) ASM.s[wv][pr][hh] = (blk + pr < w1) ? v : -INFINITY;
       }
     }
     __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
     __builtin_amdgcn_wave_barrier();
     // online softmax per head over this block; probabilities replace scores
 #pragma unroll
-    for (int h = 0; h < MAXB; ++h) {
-      if (h < gs) {
-        float sv = lane < 32 ? sm.s[wv][lane][h] : -INFINITY;
+    for (int h = 0; h < GS; ++h) {
+      {
+        float sv = lane < 32 ? ASM.s[wv][lane][h] : -INFINITY;
         float mb = wave_max(sv);
         float mn = fmaxf(m_run[h], mb);
         float corr = __expf(m_run[h] - mn);
@@ -557,7 +610,7 @@ __device__ __noinline__ void attn_task_wave(const Params& p, AttnSmem& sm, int g
         m_run[h] = mn;
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[h][j] *= corr;
-        if (lane < 32) sm.s[wv][lane][h] = pv;
+        if (lane < 32) ASM.s[wv][lane][h] = pv;
       }
     }
     __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
@@ -574,9 +627,9 @@ __device__ __noinline__ void attn_task_wave(const Params& p, AttnSmem& sm, int g
         vv[2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
       }
 #pragma unroll
-      for (int h = 0; h < MAXB; ++h) {
-        if (h < gs) {
-          float pw = sm.s[wv][t][h];
+      for (int h = 0; h < GS; ++h) {
+        {
+          float pw = ASM.s[wv][t][h];
 #pragma unroll
           for (int j = 0; j < 8; ++j) acc[h][j] += pw * vv[j];
         }
@@ -595,8 +648,8 @@ __device__ __noinline__ void attn_task_wave(const Params& p, AttnSmem& sm, int g
   }
   // sum the lane groups that hold the same dims (different rows)
 #pragma unroll
-  for (int h = 0; h < MAXB; ++h) {
-    if (h < gs) {
+  for (int h = 0; h < GS; ++h) {
+    {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float v = acc[h][j];
@@ -604,12 +657,26 @@ __device__ __noinline__ void attn_task_wave(const Params& p, AttnSmem& sm, int g
         for (int o = LPR; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
         acc[h][j] = v;
       }
-      if (lane == 0) { sm.wm[wv][h] = m_run[h]; sm.wl[wv][h] = l_run[h]; }
+      if (lane == 0) { ASM.wm[wv][h] = m_run[h]; ASM.wl[wv][h] = l_run[h]; }
       if (lane < LPR) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sm.wo[wv][h][lane * 8 + j] = acc[h][j];
+        for (int j = 0; j < 8; ++j) ASM.wo[wv][h][lane * 8 + j] = acc[h][j];
       }
     }
+  }
+}
+
+template <int HD>
+__device__ __forceinline__ void attn_dispatch(int gs, const uint16_t* kc, const uint16_t* vc, uint32_t nb, int w0, int w1) {
+  switch (gs) {
+    case 1: attn_task_wave<HD, 1>(kc, vc, nb, w0, w1); break;
+    case 2: attn_task_wave<HD, 2>(kc, vc, nb, w0, w1); break;
+    case 3: attn_task_wave<HD, 3>(kc, vc, nb, w0, w1); break;
+    case 4: attn_task_wave<HD, 4>(kc, vc, nb, w0, w1); break;
+    case 5: attn_task_wave<HD, 5>(kc, vc, nb, w0, w1); break;
+    case 6: attn_task_wave<HD, 6>(kc, vc, nb, w0, w1); break;
+    case 7: attn_task_wave<HD, 7>(kc, vc, nb, w0, w1); break;
+    default: attn_task_wave<HD, 8>(kc, vc, nb, w0, w1); break;
   }
 }
 
@@ -640,7 +707,7 @@ __device__ __noinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L,
       float a = ld_f32(wr, p.off_qkv + (uint32_t)(b * nqkv + col + i) * 4u);
       float bb = ld_f32(wr, p.off_qkv + (uint32_t)(b * nqkv + col + i + hd / 2) * 4u);
       float cs, sn;
-      rope_cs(pos, i, hd, p.theta, cs, sn);
+      rope_cs(p, pos, i, cs, sn);
       sm.q[h][i] = (a * cs - bb * sn) * scale;
       sm.q[h][i + hd / 2] = (a * sn + bb * cs) * scale;
     }
@@ -650,7 +717,7 @@ __device__ __noinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L,
         float a = ld_f32(wr, p.off_qkv + (uint32_t)(b * nqkv + colk + i) * 4u);
         float bb = ld_f32(wr, p.off_qkv + (uint32_t)(b * nqkv + colk + i + hd / 2) * 4u);
         float cs, sn;
-        rope_cs(pos, i, hd, p.theta, cs, sn);
+        rope_cs(p, pos, i, cs, sn);
         kc[(size_t)pos * hd + i] = bf16_rne(a * cs - bb * sn);
         kc[(size_t)pos * hd + i + hd / 2] = bf16_rne(a * sn + bb * cs);
       }
@@ -661,14 +728,16 @@ __device__ __noinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L,
       wait_stores();
     }
     __syncthreads();
+    sub_stamp(p, 0);
     const int len = a1 - a0;
     const int wq = ((len + NW - 1) / NW + 31) / 32 * 32;
     const int w0 = a0 + wv * wq < a1 ? a0 + wv * wq : a1;
     const int w1 = w0 + wq < a1 ? w0 + wq : a1;
     const uint32_t nb = (uint32_t)((size_t)n * hd * 2);
-    if (hd == 128) attn_task_wave<128>(p, sm, gs, kc, vc, nb, w0, w1);
-    else attn_task_wave<64>(p, sm, gs, kc, vc, nb, w0, w1);
+    if (hd == 128) attn_dispatch<128>(gs, kc, vc, nb, w0, w1);
+    else attn_dispatch<64>(gs, kc, vc, nb, w0, w1);
     __syncthreads();
+    sub_stamp(p, 3);
     // this task's partial: m, l in part_ml[b][head][c]; o in part_o[b][head][c][hd]
     for (int e = threadIdx.x; e < gs * hd; e += NT) {
       int h = e / hd, d = e % hd;
@@ -689,6 +758,7 @@ __device__ __noinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L,
     }
     wait_stores();
     __syncthreads();
+    sub_stamp(p, 1);
     if (threadIdx.x == 0) {
       unsigned* ctr = sync_pt(p, p.sync_attn_base + layer) + (b * p.nkv + g);
       unsigned old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -745,14 +815,14 @@ __device__ __noinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L,
       }
     }
     __syncthreads();
+    sub_stamp(p, 2);
   }
 }
 
 // --- residual-owning projection: x[t][r] += W . U; next norm input + ssq
 __device__ __noinline__ void phase_residual_gemv(const Params& p, const uint16_t* W, int K, uint32_t u_off,
-                                    const uint16_t* g_next) {
+                                                 const uint16_t* g_next) {
   GemvSmem& sm = *(GemvSmem*)md_smem;
-  float* part = (float*)(md_smem + sizeof(GemvSmem));  // [NT][MAXB]
   GemvJob j;
   j.nm = 1;
   j.W[0] = W;
@@ -760,20 +830,40 @@ __device__ __noinline__ void phase_residual_gemv(const Params& p, const uint16_t
   j.K = K;
   j.u_off = u_off;
   j.B = p.B;
-  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   j.pair = false;
-  for (int t = 0; t < MAXB; ++t) part[threadIdx.x * MAXB + t] = 0.f;
-  run_gemv(p, j, sm, [&](GemvSmem& s, int slot0, int n) {
-    for (int e = threadIdx.x; e < n * 16 * p.B; e += NT) {
-      int t = e % p.B, rr = (e / p.B) % 16, i = e / (p.B * 16);
-      int m, row;
-      if (!slot_row(s.slots[slot0 + i], rr, j.N, m, row)) continue;
-      float x = p.x[t * p.H + row] + s.y[i][rr][t];
-      p.x[t * p.H + row] = x;
-      put_hilo(r, p.off_u, p.H, t, row, bf16_f32(g_next[row]) * x);
-      part[threadIdx.x * MAXB + t] += x * x;
+  const int B = p.B, H = p.H;
+  build_slots(j, sm);
+  // stage the residual rows and next-norm gains this workgroup owns
+  for (int e = threadIdx.x; e < sm.nslots * 16 * B; e += NT) {
+    int t = e % B, sr = e / B;
+    int m, row;
+    if (!slot_row(sm.slots[sr >> 4], sr & 15, j.N, m, row)) continue;
+    sm.in[sr][t] = p.x[t * H + row];
+    if (t == 0) sm.gain[sr] = bf16_f32(g_next[row]);
+  }
+  __syncthreads();
+  sub_stamp(p, 0);
+  run_gemv(j, p.ws, p.ws_bytes, p.off_zero, [=](int slot0, int n) {
+    for (int e = threadIdx.x; e < n * 16 * B; e += NT) {
+      int t = e % B, rr = (e / B) % 16, i = e / (B * 16);
+      int sr = (slot0 + i) * 16 + rr;
+      GSM.out[sr][t] = GSM.in[sr][t] + GSM.y[i][rr][t];
     }
   });
+  sub_stamp(p, 2);
+  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+  static_assert(sizeof(GemvSmem::red) >= sizeof(float) * NT * MAXB, "partial sums reuse the reduction scratch");
+  float* part = (float*)sm.red;  // [NT][MAXB], reuses the reduction scratch
+  for (int t = 0; t < MAXB; ++t) part[threadIdx.x * MAXB + t] = 0.f;
+  for (int e = threadIdx.x; e < sm.nslots * 16 * B; e += NT) {
+    int t = e % B, sr = e / B;
+    int m, row;
+    if (!slot_row(sm.slots[sr >> 4], sr & 15, j.N, m, row)) continue;
+    float x = sm.out[sr][t];
+    p.x[t * H + row] = x;
+    put_hilo(r, p.off_u, H, t, row, sm.gain[sr] * x);
+    part[threadIdx.x * MAXB + t] += x * x;
+  }
   __syncthreads();
   if (threadIdx.x < MAXB) {
     float a = 0.f;
@@ -785,8 +875,6 @@ __device__ __noinline__ void phase_residual_gemv(const Params& p, const uint16_t
 // --- dense SwiGLU gate/up: h = silu(inv*Wg U) * (inv*Wu U) -> hi/lo
 __device__ __noinline__ void phase_gateup(const Params& p, const uint16_t* Wg, const uint16_t* Wu, int F) {
   GemvSmem& sm = *(GemvSmem*)md_smem;
-  float* inv = (float*)(md_smem + sizeof(GemvSmem));
-  load_inv_rms(p, inv, p.H);
   GemvJob j;
   j.nm = 2;
   j.W[0] = Wg; j.N[0] = F;
@@ -795,28 +883,34 @@ __device__ __noinline__ void phase_gateup(const Params& p, const uint16_t* Wg, c
   j.u_off = p.off_u;
   j.B = p.B;
   j.pair = true;
-  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-  run_gemv(p, j, sm, [&](GemvSmem& s, int slot0, int n) {
-    // slots come as (gate tile t, up tile t)
-    for (int e = threadIdx.x; e < 16 * p.B; e += NT) {
-      int t = e % p.B, rr = e / p.B;
-      int m, row;
-      if (n < 2 || !slot_row(s.slots[slot0], rr, j.N, m, row)) continue;
-      float a = s.y[0][rr][t] * inv[t];
-      float u = s.y[1][rr][t] * inv[t];
-      put_hilo(r, p.off_h, F, t, row, silu(a) * u);
+  const int B = p.B;
+  build_slots(j, sm);
+  load_inv_rms(p, sm.inv, p.H);
+  sub_stamp(p, 0);
+  // slots come as (gate quarters, the same up quarters); h goes to the gate slot's rows
+  run_gemv(j, p.ws, p.ws_bytes, p.off_zero, [=](int slot0, int n) {
+    for (int e = threadIdx.x; e < 16 * B; e += NT) {
+      int t = e % B, rr = e / B;
+      float a = GSM.y[0][rr][t] * GSM.inv[t];
+      float u = GSM.y[1][rr][t] * GSM.inv[t];
+      GSM.out[slot0 * 16 + rr][t] = silu(a) * u;
     }
   });
+  sub_stamp(p, 2);
+  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+  for (int e = threadIdx.x; e < sm.nslots * 16 * B; e += NT) {
+    int t = e % B, sr = e / B;
+    int slot = sr >> 4;
+    if (slot & 1) continue;  // up slots carry no output
+    int m, row;
+    if (!slot_row(sm.slots[slot], sr & 15, j.N, m, row)) continue;
+    put_hilo(r, p.off_h, F, t, row, sm.out[sr][t]);
+  }
 }
 
 // --- final norm + LM head: logits, per-WG argmax candidates
 __device__ __noinline__ void phase_lmhead(const Params& p) {
   GemvSmem& sm = *(GemvSmem*)md_smem;
-  float* inv = (float*)(md_smem + sizeof(GemvSmem));
-  float* bv = inv + MAXB;                 // [NT][MAXB] best value
-  int* bi = (int*)(bv + NT * MAXB);       // [NT][MAXB] best index
-  load_inv_rms(p, inv, p.H);
-  for (int t = 0; t < MAXB; ++t) { bv[threadIdx.x * MAXB + t] = -INFINITY; bi[threadIdx.x * MAXB + t] = 0x7FFFFFFF; }
   GemvJob j;
   j.nm = 1;
   j.W[0] = p.lm_head;
@@ -825,21 +919,34 @@ __device__ __noinline__ void phase_lmhead(const Params& p) {
   j.u_off = p.off_u;
   j.B = p.B;
   j.pair = false;
-  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-  run_gemv(p, j, sm, [&](GemvSmem& s, int slot0, int n) {
-    for (int e = threadIdx.x; e < n * 16 * p.B; e += NT) {
-      int t = e % p.B, rr = (e / p.B) % 16, i = e / (p.B * 16);
-      int m, v;
-      if (!slot_row(s.slots[slot0 + i], rr, j.N, m, v)) continue;
-      float lg = s.y[i][rr][t] * inv[t];
-      p.logits[(size_t)t * p.V + v] = lg;
-      float& cb = bv[threadIdx.x * MAXB + t];
-      int& ci = bi[threadIdx.x * MAXB + t];
-      if (lg > cb || (lg == cb && v < ci)) { cb = lg; ci = v; }
+  const int B = p.B;
+  build_slots(j, sm);
+  load_inv_rms(p, sm.inv, p.H);
+  sub_stamp(p, 0);
+  run_gemv(j, p.ws, p.ws_bytes, p.off_zero, [=](int slot0, int n) {
+    for (int e = threadIdx.x; e < n * 16 * B; e += NT) {
+      int t = e % B, rr = (e / B) % 16, i = e / (B * 16);
+      GSM.out[(slot0 + i) * 16 + rr][t] = GSM.y[i][rr][t] * GSM.inv[t];
     }
   });
+  sub_stamp(p, 2);
+  static_assert(sizeof(GemvSmem::in) >= 2 * sizeof(float) * NT * MAXB, "argmax scratch reuses the input staging");
+  float* bv = &sm.in[0][0];              // [NT][MAXB] best value (the input staging is unused here)
+  int* bi = (int*)(bv + NT * MAXB);      // [NT][MAXB] best index
+  for (int t = 0; t < MAXB; ++t) { bv[threadIdx.x * MAXB + t] = -INFINITY; bi[threadIdx.x * MAXB + t] = 0x7FFFFFFF; }
+  for (int e = threadIdx.x; e < sm.nslots * 16 * B; e += NT) {
+    int t = e % B, sr = e / B;
+    int m, v;
+    if (!slot_row(sm.slots[sr >> 4], sr & 15, j.N, m, v)) continue;
+    float lg = sm.out[sr][t];
+    p.logits[(size_t)t * p.V + v] = lg;
+    float& cb = bv[threadIdx.x * MAXB + t];
+    int& ci = bi[threadIdx.x * MAXB + t];
+    if (lg > cb || (lg == cb && v < ci)) { cb = lg; ci = v; }
+  }
   __syncthreads();
-  if (threadIdx.x < p.B) {
+  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+  if (threadIdx.x < B) {
     int t = threadIdx.x;
     float best = -INFINITY;
     int idx = 0x7FFFFFFF;
@@ -883,6 +990,7 @@ extern "C" __global__ __launch_bounds__(NT) void md_megakernel(Params p) {
   if (p.trace && threadIdx.x == 0 && p.trace_n > 0) p.trace[(size_t)blockIdx.x * p.trace_n + p.trace_n - 1] = wall_clock64();
   clear_next_bank(p);
   int sidx = 0;
+  if (threadIdx.x == 0) md_cur_phase = 0;
   phase_embed(p);
   grid_sync(p, sidx);
   for (int l = 0; l < p.n_layers; ++l) {
@@ -943,7 +1051,7 @@ hipError_t launch_pack(const void* src, void* dst, int64_t rows, int64_t cols, h
 }
 
 size_t megakernel_smem_bytes() {
-  size_t gemv = sizeof(GemvSmem) + MAXB * 4 + (size_t)NT * MAXB * 8 + 64;
+  size_t gemv = sizeof(GemvSmem) + (size_t)1024 * MAXB * 4 + 64;  // + partial-sum staging of up to 1024 workgroups
   size_t attn = sizeof(AttnSmem) + 64;
   return gemv > attn ? gemv : attn;
 }

@@ -63,6 +63,8 @@ struct Params {
   uint32_t off_h;     // hi/lo bf16[2][MAXB][F]
   uint32_t off_cand;  // argmax candidates {f32, i32}[G][MAXB]
   uint32_t off_zero;  // 1 KB that stays zero (target of masked loads)
+  const float* rope;  // (cos, sin) fp32[max_ctx][rope_d/2][2]
+  int rope_d;
   unsigned* sync;     // counters, 2 banks
   int* err;
   int n_sync;

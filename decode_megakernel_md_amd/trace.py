@@ -23,6 +23,7 @@ class Tracer:
         self.m = model
         self.G = lib().md_grid_size(model.handle)
         self.n = 2 * n_sync_max + 1
+        self.n = 16384
         self.buf = torch.zeros((self.G, self.n), dtype=torch.int64, device=model.device)
         check(lib().md_set_trace(model.handle, ctypes.c_void_p(self.buf.data_ptr()), self.n))
 
@@ -45,11 +46,21 @@ class Tracer:
             release[s] = np.median(wait_end) - end.max()
             prev = wait_end
         total = t[:, 2 * (ns - 1)].max() - start.min()
+        # sub-phase stamps (GEMV phases): 0 slots built, 1 first group flushed, 2 sweep done
+        sub = t[:, self.n // 2: self.n // 2 + 4 * ns].reshape(self.G, ns, 4)
         out = {}
+        prevs = [start] + [t[:, 2 * s + 1] for s in range(ns - 1)]
         for s, nm in enumerate(names):
-            d = out.setdefault(nm, {"n": 0, "med": 0.0, "max": 0.0, "release": 0.0})
+            d = out.setdefault(nm, {"n": 0, "med": 0.0, "max": 0.0, "release": 0.0, "to_slots": 0.0,
+                                    "to_first": 0.0, "to_sweep_end": 0.0, "k3": 0.0})
             d["n"] += 1
             d["med"] += float(np.median(work[:, s]))
             d["max"] += float(work[:, s].max())
             d["release"] += float(release[s])
+            if np.all(sub[:, s, 0] > 0):
+                d["to_slots"] += float(np.median(sub[:, s, 0] - prevs[s]))
+                d["to_first"] += float(np.median(sub[:, s, 1] - sub[:, s, 0]))
+                d["to_sweep_end"] += float(np.median(sub[:, s, 2] - sub[:, s, 0]))
+                if np.all(sub[:, s, 3] > 0):
+                    d["k3"] += float(np.median(sub[:, s, 3] - sub[:, s, 0]))
         return out, total

@@ -89,16 +89,63 @@ __device__ __forceinline__ void split_hilo(float x, uint16_t& hi, uint16_t& lo) 
   lo = bf16_rne(x - bf16_f32(hi));
 }
 
-// ---- wave reductions (fixed order, deterministic)
+// ---- cross-lane moves without LDS: DPP within a 16-lane row, and gfx950's
+// permlane16/32 swaps across rows.  permlane16_swap(v, v) yields
+// (rows 0,0,2,2) and (rows 1,1,3,3); permlane32_swap(v, v) yields (low half
+// twice) and (high half twice).
+constexpr int DPP_QXOR1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int DPP_QXOR2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int DPP_ROR4 = 0x124;   // row_ror:4
+constexpr int DPP_ROR8 = 0x128;   // row_ror:8 (within a row: lane i <-> i^8)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// The swaps are written as inline assembly: the compiler builtins fold the two
+// results of a swap whose inputs are equal into one value, which is wrong.
+// Both registers start as copies of v; two wait states separate the VALU
+// writes of the copies from the cross-lane read.
+__device__ __forceinline__ void swap16(float v, float& x, float& y) {
+  x = v;
+  y = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ void swap32(float v, float& x, float& y) {
+  x = v;
+  y = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+}
+
+// sum over the 4 rows of each column (lanes c, c+16, c+32, c+48)
+__device__ __forceinline__ float rows_sum(float v) {
+  float x, y;
+  swap16(v, x, y);
+  swap32(x + y, x, y);
+  return x + y;
+}
+__device__ __forceinline__ float rows_max(float v) {
+  float x, y;
+  swap16(v, x, y);
+  swap32(fmaxf(x, y), x, y);
+  return fmaxf(x, y);
+}
+
+// ---- wave reductions: every lane gets the result; the combination order is
+// fixed, so the result is deterministic
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_f<DPP_QXOR1>(v);
+  v += dpp_f<DPP_QXOR2>(v);
+  v += dpp_f<DPP_ROR4>(v);
+  v += dpp_f<DPP_ROR8>(v);
+  return rows_sum(v);
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp_f<DPP_QXOR1>(v));
+  v = fmaxf(v, dpp_f<DPP_QXOR2>(v));
+  v = fmaxf(v, dpp_f<DPP_ROR4>(v));
+  v = fmaxf(v, dpp_f<DPP_ROR8>(v));
+  return rows_max(v);
 }
 
 __device__ __forceinline__ void wait_stores() {

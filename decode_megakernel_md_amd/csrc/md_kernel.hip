@@ -590,7 +590,7 @@ __device__ __noinline__ void attn_task_wave(const uint16_t* kc, const uint16_t* 
         a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[tt][s]), qb[s], a, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float v = a[i] + __shfl_xor(a[i], 1, 64);
+        float v = a[i] + dpp_f<DPP_QXOR1>(a[i]);
         int pr = tt * 16 + 4 * (lane >> 4) + i;
         if (!pp && hh < gs) ASM.s[wv][pr][hh] = (blk + pr < w1) ? v : -INFINITY;
       }
@@ -653,9 +653,8 @@ __device__ __noinline__ void attn_task_wave(const uint16_t* kc, const uint16_t* 
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float v = acc[h][j];
-#pragma unroll
-        for (int o = LPR; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
-        acc[h][j] = v;
+        if (LPR == 8) v += dpp_f<DPP_ROR8>(v);  // lanes i and i^8 hold the same dims
+        acc[h][j] = rows_sum(v);
       }
       if (lane == 0) { ASM.wm[wv][h] = m_run[h]; ASM.wl[wv][h] = l_run[h]; }
       if (lane < LPR) {

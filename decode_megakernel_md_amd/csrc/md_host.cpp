@@ -38,6 +38,7 @@ constexpr int MAXB_ = 8;
 constexpr int GMAX = 1024;        // largest grid the workspace is sized for
 constexpr int CMAX = 256;         // largest number of KV chunks per (sequence, kv head)
 constexpr int SP_WORDS_ = 9 * 32;
+constexpr int PHASES_PER_LAYER = 8;  // upper bound on sync points per layer
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -122,16 +123,29 @@ md_status validate(const md_config* c) {
   } else {
     return fail(MD_EINVAL, "attn_kind must be 0 or 1");
   }
+  if (c->hidden < 128) return fail(MD_EUNSUPPORTED, "hidden must be at least 128");
+  if (c->attn_kind == 0 && c->n_q_heads * c->head_dim < 128)
+    return fail(MD_EUNSUPPORTED, "n_q_heads * head_dim must be at least 128");
+  auto width_ok = [](int f) { return f >= 128 && f % 32 == 0; };
   if (c->n_experts == 0) {
-    if (c->ffn_dim < 32 || c->ffn_dim % 32) return fail(MD_EUNSUPPORTED, "ffn_dim must be a positive multiple of 32");
+    if (!width_ok(c->ffn_dim)) return fail(MD_EUNSUPPORTED, "ffn_dim must be a multiple of 32, at least 128");
   } else {
-    return fail(MD_EUNSUPPORTED, "MoE layers are not built yet");
+    if (c->n_experts < 1 || c->n_experts > 64) return fail(MD_EUNSUPPORTED, "n_experts must be in [1, 64]");
+    if (c->top_k < 1 || c->top_k > 8 || c->top_k > c->n_experts)
+      return fail(MD_EINVAL, "top_k must be in [1, min(8, n_experts)]");
+    if (!width_ok(c->expert_ffn)) return fail(MD_EUNSUPPORTED, "expert_ffn must be a multiple of 32, at least 128");
+    if (c->n_shared < 0 || c->n_shared > 1) return fail(MD_EUNSUPPORTED, "n_shared must be 0 or 1");
+    if (c->n_shared == 1 && !width_ok(c->shared_ffn))
+      return fail(MD_EUNSUPPORTED, "shared_ffn must be a multiple of 32, at least 128");
+    if (c->norm_topk != 0 && c->norm_topk != 1) return fail(MD_EINVAL, "norm_topk must be 0 or 1");
+    int nu = c->n_experts < c->max_batch * c->top_k ? c->n_experts : c->max_batch * c->top_k;
+    if (2 * nu > 72) return fail(MD_EUNSUPPORTED, "too many distinct experts per step (2 * min(n_experts, max_batch * top_k) > 72)");
   }
   return MD_OK;
 }
 
 struct WsLayout {
-  size_t layers, experts, x, u, ssq, qkv, attn, attn_ml, ou, h, cand, zero, rope, sync, err, total;
+  size_t layers, experts, x, u, ssq, qkv, attn, attn_ml, ou, h, rl, hs, hr, hr_stride, cand, zero, rope, sync, err, total;
   int rope_d;
   int n_sync, sync_attn_base;
 };
@@ -160,11 +174,16 @@ WsLayout ws_layout(const md_config* c) {
   w.attn_ml = take(8 * (size_t)MAXB_ * (c->n_q_heads > 0 ? c->n_q_heads : 1) * CMAX);
   w.ou = take(2 * 2 * MAXB_ * (size_t)attn_out);
   w.h = take(2 * 2 * MAXB_ * (size_t)F);
+  w.rl = take(4 * (size_t)MAXB_ * (c->n_experts > 0 ? c->n_experts : 1));
+  w.hs = take(2 * 2 * MAXB_ * (size_t)(c->n_shared > 0 ? c->shared_ffn : 1));
+  int nu = c->n_experts < c->max_batch * c->top_k ? c->n_experts : c->max_batch * c->top_k;
+  w.hr_stride = align256(2 * 2 * MAXB_ * (size_t)(c->expert_ffn > 0 ? c->expert_ffn : 1));
+  w.hr = take(w.hr_stride * (size_t)(nu > 0 ? nu : 1));
   w.cand = take(8 * (size_t)GMAX * MAXB_);
   w.zero = take(1024);
   w.rope_d = c->attn_kind == 0 ? c->head_dim : c->rope_dim;
   w.rope = take(sizeof(float) * 2 * (size_t)c->max_ctx * (size_t)(w.rope_d / 2));
-  w.sync_attn_base = 1 + 5 * c->n_layers + 2;
+  w.sync_attn_base = 1 + PHASES_PER_LAYER * c->n_layers + 2;
   w.n_sync = w.sync_attn_base + c->n_layers + 2;
   w.sync = take(4 * 2 * (size_t)w.n_sync * SP_WORDS_);
   w.err = take(256);
@@ -380,7 +399,8 @@ static md_status fill_params(md_model* m, const int32_t* tokens, const int32_t* 
   p.ws = m->ws; p.ws_bytes = (uint32_t)w.total;
   p.x = (float*)(m->ws + w.x);
   p.off_u = (uint32_t)w.u; p.off_ssq = (uint32_t)w.ssq; p.off_qkv = (uint32_t)w.qkv; p.off_attn = (uint32_t)w.attn; p.off_attn_ml = (uint32_t)w.attn_ml;
-  p.off_ou = (uint32_t)w.ou; p.off_h = (uint32_t)w.h; p.off_cand = (uint32_t)w.cand; p.off_zero = (uint32_t)w.zero;
+  p.off_ou = (uint32_t)w.ou; p.off_h = (uint32_t)w.h;
+  p.off_rl = (uint32_t)w.rl; p.off_hs = (uint32_t)w.hs; p.off_hr = (uint32_t)w.hr; p.hr_stride = (uint32_t)w.hr_stride; p.off_cand = (uint32_t)w.cand; p.off_zero = (uint32_t)w.zero;
   p.rope = (const float*)(m->ws + w.rope); p.rope_d = w.rope_d;
   p.sync = (unsigned*)(m->ws + w.sync);
   p.err = (int*)(m->ws + w.err);
@@ -435,8 +455,9 @@ md_status md_get_device_status(md_model* m) {
     // a failed step leaves its counter bank in an unknown state: clear both
     hipMemset(m->ws + m->lay.sync, 0, (size_t)4 * 2 * m->lay.n_sync * SP_WORDS_);
     hipDeviceSynchronize();
-    return fail(MD_EDEVICE, "device error 0x%x:%s%s%s", err, (err & MDE_WATCHDOG) ? " sync wait exceeded its bound" : "",
-                (err & MDE_TOKEN) ? " token out of range" : "", (err & MDE_POSITION) ? " position out of range" : "");
+    return fail(MD_EDEVICE, "device error 0x%x:%s%s%s%s", err, (err & MDE_WATCHDOG) ? " sync wait exceeded its bound" : "",
+                (err & MDE_TOKEN) ? " token out of range" : "", (err & MDE_POSITION) ? " position out of range" : "",
+                (err & MDE_CAPACITY) ? " a phase's work exceeds the per-workgroup tables (shape too large for this grid)" : "");
   }
   return MD_OK;
 }

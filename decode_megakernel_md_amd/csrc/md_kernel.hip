@@ -119,8 +119,9 @@ __device__ void clear_next_bank(const Params& p) {
 }
 
 // ===================================================================== GEMV
-// Y[r][t] = sum_k W[r][k] * U[t][k] for this workgroup's rows of up to MAXM
-// matrices that share K.
+// Y[r][t] = sum_k W[r][k] * U[t][k] for this workgroup's rows of a list of
+// matrices (up to MAXMAT per phase: q/k/v, the gate and up of every expert a
+// step uses, the down projections of all of them, ...).
 //
 // Weights are in the tiled layout md_pack_weight writes: 16-row tiles, and
 // within a tile one contiguous 1 KB block per 32-column k-step holding the
@@ -129,35 +130,31 @@ __device__ void clear_next_bank(const Params& p) {
 // consecutive, so every wave instruction reads 1 KB contiguous and each tile
 // is one sequential stream.
 //
-// U is the activation in hi/lo form, bf16[2][MAXB][K] (part, token, k): the
+// U is an activation in hi/lo form, bf16[2][MAXB][K] (part, token, k): the
 // B operand (32 k x 16 columns: token t hi at column 2t, lo at 2t+1) is one
 // 16-byte load per lane.
 //
 // Work split: each matrix's rows are cut into 4-row quarters and workgroup w
 // owns quarters [Q*w/G, Q*(w+1)/G), so every workgroup streams the same
-// number of bytes.  Its rows form "slots" (tiles, possibly partial: lanes of
-// other quarters load nothing).  Slots are consumed in pairs; the four waves
-// split the k-steps of a pair and keep DS k-steps of loads in flight in one
-// continuous stream across pairs (no pipeline drain between tiles).
+// number of bytes.  Its quarters are packed four to a "slot" (one
+// matrix-core tile whose lanes may read four different matrices), and slots
+// are consumed in groups of two that share one B operand: a group never
+// mixes inputs, so all its quarters multiply the same U.  The four waves split
+// the k-steps of a group and keep GDS k-steps of loads in flight in one
+// continuous stream across groups (no pipeline drain between tiles).
+//
 // The workgroup's dynamic LDS.  Phases address it through this symbol (not
 // through a pointer argument) so that accesses compile to LDS instructions.
 extern __shared__ __attribute__((aligned(16))) char md_smem[];
 
-constexpr int MAXM = 3;
-constexpr int CMAX_DEV = 256;  // largest chunk count per (sequence, kv head)
-constexpr int TG = 2;          // tiles consumed together (share one B operand load)
-constexpr int GDS = 12;        // k-steps in flight per wave
-constexpr int MAXSLOT = 48;    // slots per workgroup and phase (LM head: <= 41)
-
-struct GemvJob {
-  const uint16_t* W[MAXM];
-  int N[MAXM];
-  int nm;
-  int K;
-  uint32_t u_off;  // byte offset of U in the workspace
-  int B;
-  bool pair;       // slot list interleaves matrices 0 and 1 tile by tile (SwiGLU)
-};
+constexpr int CMAX_DEV = 256;    // largest chunk count per (sequence, kv head)
+constexpr int TG = 2;            // slots per group (share one B operand load)
+constexpr int GDS = 12;          // k-steps in flight per wave
+constexpr int MAXSLOT = 96;      // slots per workgroup and phase
+constexpr int MAXGRP = MAXSLOT / TG;
+constexpr int MAXMAT = 72;       // matrices per phase
+constexpr int STAGE_ROWS = 768;  // epilogue staging rows per workgroup
+constexpr int MIN_KS = NW;       // every wave needs a k-step of every group
 
 struct RowSplit {
   int r0, r1;
@@ -169,93 +166,140 @@ __device__ __forceinline__ RowSplit rows_of(int N, int w, int G) {
   return s;
 }
 
-// One slot = one matrix-core tile of 16 output rows assembled from four
-// 4-row quarters, each from any matrix of the phase (a "virtual tile"): the
-// lanes of quarter position e read matrix m[e], global quarter gq[e]
-// (rows 4*gq .. 4*gq+3), through their own 64-bit addresses.  gq < 0: empty.
+// One slot: the lanes of quarter position e read matrix m[e] (index into the
+// phase's matrix table), global quarter gq[e] (rows 4*gq .. 4*gq+3).
+// gq < 0: an empty quarter (its lanes read the zero block).
 struct Slot {
   int8_t m[4];
   int gq[4];
+};
+struct MatDesc {
+  uint64_t w;        // tiled weights
+  uint64_t tstride;  // bytes per 16-row tile
+  int N;             // rows
+  int tag;           // meaning chosen by the phase (expert slot, ...)
+};
+enum : int { GK_SINGLE = 0, GK_PAIR = 1 };
+// A group: slots 2g and 2g+1.  GK_PAIR: slot 2g holds gate rows and slot
+// 2g+1 the up rows of the same quarters (SwiGLU); GK_SINGLE: two independent
+// slots.
+struct GroupDesc {
+  uint32_t u_off;    // byte offset of U in the workspace
+  int KS;            // k-steps (K / 32); U rows are K elements apart
+  int kind;
+  int pad_;
 };
 
 struct GemvSmem {
   float red[NW][TG][16][16];   // also reused as [NT][MAXB] scratch after the stream
   float y[TG][16][MAXB];
   Slot slots[MAXSLOT];
-  int nslots;
-  // epilogue staging, indexed [slot*16 + row-in-slot][token]: inputs read
-  // before the weight stream starts, outputs written after it ends, so the
-  // stream itself issues no other memory operation
-  float in[MAXSLOT * 16][MAXB];
-  float out[MAXSLOT * 16][MAXB];
-  float gain[MAXSLOT * 16];
+  GroupDesc grp[MAXGRP];
+  MatDesc mats[MAXMAT];
+  int nslots, ngroups, nmats, overflow;
+  // epilogue staging: inputs read before the weight stream starts, outputs
+  // written after it ends, so the stream itself issues no other memory
+  // operation.  Indexed by slot row (slot*16 + row-in-slot) or, in phases
+  // that own residual rows, by row - first owned row.
+  float in[STAGE_ROWS][MAXB];
+  float out[STAGE_ROWS][MAXB];
+  float gain[STAGE_ROWS];
   float inv[MAXB];
 };
-
-// Build this workgroup's slot list (thread 0) into LDS.  Normal mode packs
-// the workgroup's quarters of matrix 0, then 1, then 2, four per slot.  Pair
-// mode (SwiGLU) emits a slot of 4 gate quarters followed by the slot of the
-// same 4 up quarters.
-__device__ void build_slots(const GemvJob& job, GemvSmem& sm) {
-  if (threadIdx.x == 0) {
-    const int G = gridDim.x, w = blockIdx.x;
-    int n = 0, fill = 0;
-    Slot cur;
-    auto reset = [&]() {
-      for (int e = 0; e < 4; ++e) { cur.m[e] = 0; cur.gq[e] = -1; }
-      fill = 0;
-    };
-    reset();
-    if (job.pair) {
-      RowSplit q = rows_of((job.N[0] + 3) >> 2, w, G);
-      for (int g0 = q.r0; g0 < q.r1 && n + 2 <= MAXSLOT; g0 += 4) {
-        Slot a, b;
-        for (int e = 0; e < 4; ++e) {
-          int gq = g0 + e < q.r1 ? g0 + e : -1;
-          a.m[e] = 0; a.gq[e] = gq;
-          b.m[e] = 1; b.gq[e] = gq;
-        }
-        sm.slots[n++] = a;
-        sm.slots[n++] = b;
-      }
-    } else {
-      for (int m = 0; m < job.nm; ++m) {
-        RowSplit q = rows_of((job.N[m] + 3) >> 2, w, G);
-        for (int gq = q.r0; gq < q.r1; ++gq) {
-          cur.m[fill] = (int8_t)m;
-          cur.gq[fill] = gq;
-          if (++fill == 4) {
-            if (n < MAXSLOT) sm.slots[n++] = cur;
-            reset();
-          }
-        }
-      }
-      if (fill > 0 && n < MAXSLOT) sm.slots[n++] = cur;
-    }
-    sm.nslots = n;
-  }
-  __syncthreads();
-}
-
-// Run the GEMV; after each pair of slots epi(sm, slot_index0, count) reads
-// sm.y[i][row-in-slot][token] for slots slot_index0 + i (slot_row maps a row
-// of a slot back to its matrix and row).
-// The GEMV's LDS block, addressed through the LDS symbol itself (never
-// through a pointer held in a closure or passed by value), so that every
-// access compiles to an LDS instruction: a flat or scratch access inside the
-// stream would make the next wait drain the whole prefetch ring.
 #define GSM (*reinterpret_cast<GemvSmem*>(md_smem))
 
-// Per-lane source of one slot of the current group.
-__device__ __forceinline__ void slot_src(int si, int nslots, int lq, uint64_t w0, uint64_t w1, uint64_t w2,
-                                         uint64_t tstride, uint32_t lchunk, int wv, uint64_t zero_addr, uint64_t& pa,
+// Slot-list builder, run by thread 0.  Groups are opened with begin(U, K,
+// kind); quarters are appended with single() or pair() and written straight
+// into the LDS slot table; a group never spans two begin() calls.
+struct SlotBuilder {
+  int ns, fill, pfill;
+  GroupDesc gd;
+  __device__ void empty_slot(int si) {
+    for (int e = 0; e < 4; ++e) { GSM.slots[si].m[e] = 0; GSM.slots[si].gq[e] = -1; }
+  }
+  __device__ void start() {
+    ns = 0; fill = 0; pfill = 0;
+    gd.u_off = 0; gd.KS = MIN_KS; gd.kind = GK_SINGLE; gd.pad_ = 0;
+    GSM.nmats = 0;
+    GSM.overflow = 0;
+  }
+  __device__ int mat(const void* w, int N, int K, int tag) {
+    int i = GSM.nmats;
+    if (i >= MAXMAT) { GSM.overflow = 1; return 0; }
+    MatDesc d;
+    d.w = (uint64_t)w; d.tstride = (uint64_t)(K >> 5) * 1024u; d.N = N; d.tag = tag;
+    GSM.mats[i] = d;
+    GSM.nmats = i + 1;
+    return i;
+  }
+  // open slot ns (and its group when ns is even)
+  __device__ bool open_slot() {
+    if (ns >= MAXSLOT) { GSM.overflow = 1; return false; }
+    empty_slot(ns);
+    if ((ns & 1) == 0) GSM.grp[ns >> 1] = gd;
+    return true;
+  }
+  __device__ void flush() {
+    if (fill) { ++ns; fill = 0; }
+  }
+  __device__ void pflush() {
+    if (pfill) { ns += 2; pfill = 0; }
+  }
+  __device__ void close() {
+    flush();
+    pflush();
+    if (ns & 1) {
+      if (open_slot()) ++ns;
+    }
+  }
+  __device__ void begin(uint32_t u_off, int K, int kind) {
+    close();
+    if (K < 32 * MIN_KS || (K & 31)) GSM.overflow = 1;
+    gd.u_off = u_off; gd.KS = K >> 5; gd.kind = kind; gd.pad_ = 0;
+  }
+  __device__ void single(int m, int gq) {
+    if (fill == 0 && !open_slot()) return;
+    GSM.slots[ns].m[fill] = (int8_t)m;
+    GSM.slots[ns].gq[fill] = gq;
+    if (++fill == 4) flush();
+  }
+  __device__ void pair(int mg, int mu, int gq) {
+    if (pfill == 0) {
+      if (ns + 1 >= MAXSLOT) { GSM.overflow = 1; return; }
+      empty_slot(ns);
+      empty_slot(ns + 1);
+      GSM.grp[ns >> 1] = gd;
+    }
+    GSM.slots[ns].m[pfill] = (int8_t)mg;
+    GSM.slots[ns].gq[pfill] = gq;
+    GSM.slots[ns + 1].m[pfill] = (int8_t)mu;
+    GSM.slots[ns + 1].gq[pfill] = gq;
+    if (++pfill == 4) pflush();
+  }
+  // all of matrix m's quarters this workgroup owns
+  __device__ void singles_of(int m) {
+    RowSplit q = rows_of((GSM.mats[m].N + 3) >> 2, blockIdx.x, gridDim.x);
+    for (int gq = q.r0; gq < q.r1; ++gq) single(m, gq);
+  }
+  __device__ void pairs_of(int mg, int mu) {
+    RowSplit q = rows_of((GSM.mats[mg].N + 3) >> 2, blockIdx.x, gridDim.x);
+    for (int gq = q.r0; gq < q.r1; ++gq) pair(mg, mu, gq);
+  }
+  __device__ void finish() {
+    close();
+    GSM.nslots = ns;
+    GSM.ngroups = ns / TG;
+  }
+};
+
+// Per-lane source of one slot.
+__device__ __forceinline__ void slot_src(int si, int lq, uint32_t lchunk, int wv, uint64_t zero_addr, uint64_t& pa,
                                          uint32_t& pstep) {
-  bool v = si < nslots;
-  int gq = v ? GSM.slots[si].gq[lq] : -1;
-  int m = v ? GSM.slots[si].m[lq] : 0;
-  uint64_t W = m == 0 ? w0 : (m == 1 ? w1 : w2);
+  int gq = GSM.slots[si].gq[lq];
+  int m = GSM.slots[si].m[lq];
   bool lv = gq >= 0;
-  pa = lv ? W + (uint64_t)(gq >> 2) * tstride + (uint64_t)((gq & 3) * 256) + lchunk + (uint64_t)wv * 1024u : zero_addr;
+  uint64_t W = GSM.mats[m].w, ts = GSM.mats[m].tstride;
+  pa = lv ? W + (uint64_t)(gq >> 2) * ts + (uint64_t)((gq & 3) * 256) + lchunk + (uint64_t)wv * 1024u : zero_addr;
   pstep = lv ? (uint32_t)(NW * 1024) : 0u;
 }
 
@@ -276,33 +320,40 @@ __device__ __forceinline__ void gemv_reduce(const f32x4 (&acc)[TG], int wv, int 
   __syncthreads();
 }
 
-// Run the GEMV over GSM's slot list.  After each finished pair of slots,
-// epi(slot_index0, count) reads GSM.y[i][row-in-slot][token] (LDS only).
+__device__ __forceinline__ int group_nks(int g, int wv) {
+  int KS = __builtin_amdgcn_readfirstlane(GSM.grp[g].KS);
+  return (KS - wv + NW - 1) / NW;
+}
+
+// Run the GEMV over GSM's group list.  After each finished group g,
+// epi(g) reads GSM.y[i][row-in-slot][token] for slots 2g + i (LDS only).
 template <class Epi>
-__device__ __forceinline__ void run_gemv(const GemvJob& job, const uint8_t* ws, uint32_t ws_bytes, uint32_t off_zero,
-                                         Epi epi) {
+__device__ __forceinline__ void run_gemv(const uint8_t* ws, uint32_t ws_bytes, uint32_t off_zero, int B, Epi epi) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int K = job.K, KS = K >> 5;
-  const int nslots = __builtin_amdgcn_readfirstlane(GSM.nslots);
-  const int ngroups = (nslots + TG - 1) / TG;
-  const int nks = (KS - wv + NW - 1) / NW;
-  const int total = ngroups * nks;
+  const int ngroups = __builtin_amdgcn_readfirstlane(GSM.ngroups);
+  int total = 0;
+  for (int g = 0; g < ngroups; ++g) total += group_nks(g, wv);
+  total = __builtin_amdgcn_readfirstlane(total);
   const rsrc_t urs = make_rsrc_u(ws, ws_bytes);
   const int lq = (lane & 15) >> 2;
   const uint32_t lchunk = (uint32_t)(((lane >> 4) * 4 + (lane & 3)) * 16);
   const int n16 = lane & 15, tok = n16 >> 1, part = n16 & 1;
-  const uint32_t boff = tok < job.B ? job.u_off + (uint32_t)((part * MAXB + tok) * K) * 2u + (lane >> 4) * 16u : OOB;
-  const uint64_t tstride = (uint64_t)KS * 1024u;
   const uint64_t zero_addr = (uint64_t)(ws + off_zero);
-  const uint64_t w0 = (uint64_t)job.W[0], w1 = job.nm > 1 ? (uint64_t)job.W[1] : w0,
-                 w2 = job.nm > 2 ? (uint64_t)job.W[2] : w0;
-  int ig = 0, is = 0;
-  uint64_t pa0, pa1;
-  uint32_t ps0, ps1;
-  slot_src(0, nslots, lq, w0, w1, w2, tstride, lchunk, wv, zero_addr, pa0, ps0);
-  slot_src(1, nslots, lq, w0, w1, w2, tstride, lchunk, wv, zero_addr, pa1, ps1);
+  int ig = 0, is = 0, nks_i = 0;
+  uint32_t boff = OOB;
+  uint64_t pa0 = zero_addr, pa1 = zero_addr;
+  uint32_t ps0 = 0, ps1 = 0;
   static_assert(TG == 2, "the stream handles slot pairs");
+#define GEMV_GROUP(G_)                                                                                          \
+  {                                                                                                             \
+    const int ks_ = __builtin_amdgcn_readfirstlane(GSM.grp[G_].KS);                                            \
+    const uint32_t uo_ = __builtin_amdgcn_readfirstlane(GSM.grp[G_].u_off);                                    \
+    nks_i = (ks_ - wv + NW - 1) / NW;                                                                           \
+    boff = tok < B ? uo_ + (uint32_t)((part * MAXB + tok) * ks_ * 32) * 2u + (uint32_t)(lane >> 4) * 16u : OOB; \
+    slot_src(2 * (G_), lq, lchunk, wv, zero_addr, pa0, ps0);                                                    \
+    slot_src(2 * (G_) + 1, lq, lchunk, wv, zero_addr, pa1, ps1);                                                \
+  }
 #define GEMV_ISSUE(RA, RB)                                                                                      \
   {                                                                                                             \
     bool ok_ = ig < ngroups;                                                                                    \
@@ -311,15 +362,13 @@ __device__ __forceinline__ void run_gemv(const GemvJob& job, const uint8_t* ws, 
     pa0 += ps0;                                                                                                 \
     pa1 += ps1;                                                                                                 \
     RB = ld_x4<CP_SC1>(urs, ok_ && boff != OOB ? boff + (uint32_t)(is * NW + wv) * 64u : OOB);                  \
-    if (++is == nks) {                                                                                          \
+    if (++is == nks_i) {                                                                                        \
       is = 0;                                                                                                   \
       ++ig;                                                                                                     \
-      if (ig < ngroups) {                                                                                       \
-        slot_src(ig * TG, nslots, lq, w0, w1, w2, tstride, lchunk, wv, zero_addr, pa0, ps0);                   \
-        slot_src(ig * TG + 1, nslots, lq, w0, w1, w2, tstride, lchunk, wv, zero_addr, pa1, ps1);               \
-      }                                                                                                         \
+      if (ig < ngroups) GEMV_GROUP(ig);                                                                         \
     }                                                                                                           \
   }
+  if (ngroups > 0) GEMV_GROUP(0);
   f32x4 acc[TG];
 #pragma unroll
   for (int i = 0; i < TG; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -327,15 +376,7 @@ __device__ __forceinline__ void run_gemv(const GemvJob& job, const uint8_t* ws, 
 #pragma unroll
   for (int d = 0; d < GDS; ++d) GEMV_ISSUE(ra[d], rb[d]);
   int cg = 0, cs = 0;
-  if (nks == 0) {
-    for (; cg < ngroups; ++cg) {
-      gemv_reduce(acc, wv, lane);
-      int n = nslots - cg * TG;
-      epi(cg * TG, n < TG ? n : TG);
-      __syncthreads();
-    }
-    return;
-  }
+  int nks_c = ngroups > 0 ? group_nks(0, wv) : 1;
   // The body is unconditional: steps past the end read the zero block and
   // add nothing.  (A guarded body would make the compiler assume the later
   // loads of the previous round may be missing and wait for all of them.)
@@ -348,30 +389,31 @@ __device__ __forceinline__ void run_gemv(const GemvJob& job, const uint8_t* ws, 
         acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ra[d][i]), bop, acc[i], 0, 0, 0);
       GEMV_ISSUE(ra[d], rb[d]);
       if (j0 + d < total) {
-        if (++cs == nks) {
+        if (++cs == nks_c) {
           cs = 0;
           gemv_reduce(acc, wv, lane);
 #pragma unroll
           for (int i = 0; i < TG; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-          int n = nslots - cg * TG;
-          epi(cg * TG, n < TG ? n : TG);
+          epi(cg);
           __syncthreads();
           ++cg;
+          if (cg < ngroups) nks_c = group_nks(cg, wv);
         }
       }
     }
   }
 #undef GEMV_ISSUE
+#undef GEMV_GROUP
 }
 
 // Row rr (0..15) of a slot: matrix and global row; false for an empty
 // quarter or a row past the matrix end.
-__device__ __forceinline__ bool slot_row(const Slot& sl, int rr, const int* N, int& m, int& row) {
-  int gq = sl.gq[rr >> 2];
+__device__ __forceinline__ bool slot_row(int si, int rr, int& m, int& row) {
+  int gq = GSM.slots[si].gq[rr >> 2];
   if (gq < 0) return false;
-  m = sl.m[rr >> 2];
+  m = GSM.slots[si].m[rr >> 2];
   row = gq * 4 + (rr & 3);
-  return row < N[m];
+  return row < GSM.mats[m].N;
 }
 
 // Rows of an N-row output this workgroup owns: 4-row quarters
@@ -384,6 +426,23 @@ __device__ __forceinline__ RowSplit owned_rows(int N, int w, int G) {
   r.r0 = q.r0 * 4 < N ? q.r0 * 4 : N;
   r.r1 = q.r1 * 4 < N ? q.r1 * 4 : N;
   return r;
+}
+
+// Finish slot building; on overflow (more slots, matrices or staging rows
+// than the LDS tables hold) report it and make the phase compute nothing.
+// stage_rows < 0: the phase stages by slot row (16 per slot).
+__device__ __forceinline__ bool builder_done(const Params& p, SlotBuilder& sb, int stage_rows) {
+  if (threadIdx.x == 0) {
+    sb.finish();
+    if ((stage_rows < 0 ? sb.ns * 16 : stage_rows) > STAGE_ROWS) GSM.overflow = 1;
+    if (GSM.overflow) {
+      set_err(p, MDE_CAPACITY);
+      GSM.nslots = 0;
+      GSM.ngroups = 0;
+    }
+  }
+  __syncthreads();
+  return GSM.ngroups > 0;
 }
 
 
@@ -426,12 +485,16 @@ __device__ __forceinline__ void put_hilo(rsrc_t r, uint32_t u_off, int K, int t,
   st_u16(r, u_off + (uint32_t)((1 * MAXB + t) * K + k) * 2u, lo);
 }
 
-// Residual owner epilogue (shared by the O-projection, the dense down
-// projection and the embedding): x[t][r] += y (or = y), then the next
-// norm's input U = hilo(g[r] * x) and this WG's sum of squares of x.
-struct SsqAcc {
-  float v[MAXB];
-};
+// This workgroup's sum of squares of x per token (partials [NT][MAXB] in
+// the reduction scratch, summed in a fixed order) -> ssq[w][t].
+__device__ __forceinline__ void store_ssq(const Params& p, rsrc_t r, float* part) {
+  __syncthreads();
+  if (threadIdx.x < MAXB) {
+    float a = 0.f;
+    for (int i = 0; i < NT; ++i) a += part[i * MAXB + threadIdx.x];
+    st_f32(r, p.off_ssq + (uint32_t)(blockIdx.x * MAXB + threadIdx.x) * 4u, a);
+  }
+}
 
 // --- embedding: x[t] = E[tok_t] on this WG's hidden rows
 __device__ __noinline__ void phase_embed(const Params& p) {
@@ -452,45 +515,55 @@ __device__ __noinline__ void phase_embed(const Params& p) {
     put_hilo(r, p.off_u, p.H, t, i, bf16_f32(g[i]) * x);
     part[threadIdx.x * MAXB + t] += x * x;
   }
-  __syncthreads();
-  if (threadIdx.x < MAXB) {
-    float a = 0.f;
-    for (int i = 0; i < NT; ++i) a += part[i * MAXB + threadIdx.x];
-    st_f32(r, p.off_ssq + (uint32_t)(blockIdx.x * MAXB + threadIdx.x) * 4u, a);
-  }
+  store_ssq(p, r, part);
 }
+
+// Epilogue of phases whose output is y * inv_rms per slot row.
+#define EPI_SCALED_SINGLE                                                     \
+  [=](int g) {                                                                \
+    for (int e = threadIdx.x; e < TG * 16 * B; e += NT) {                     \
+      int t = e % B, rr = (e / B) % 16, i = e / (B * 16);                     \
+      GSM.out[(2 * g + i) * 16 + rr][t] = GSM.y[i][rr][t] * GSM.inv[t];       \
+    }                                                                         \
+  }
+// SwiGLU epilogue of a pair group: silu(inv*gate) * (inv*up) to the gate
+// slot's rows.
+#define EPI_SWIGLU                                                            \
+  [=](int g) {                                                                \
+    for (int e = threadIdx.x; e < 16 * B; e += NT) {                          \
+      int t = e % B, rr = e / B;                                              \
+      float a = GSM.y[0][rr][t] * GSM.inv[t];                                 \
+      float u = GSM.y[1][rr][t] * GSM.inv[t];                                 \
+      GSM.out[2 * g * 16 + rr][t] = silu(a) * u;                              \
+    }                                                                         \
+  }
 
 // --- QKV projection (GQA): raw q, k, v (RMS-normalised input) -> qkv[t][row]
 __device__ __noinline__ void phase_qkv(const Params& p, const LayerDesc& L) {
-  GemvSmem& sm = *(GemvSmem*)md_smem;
-  GemvJob j;
-  j.nm = 3;
-  j.W[0] = L.wq; j.N[0] = p.nq * p.hd;
-  j.W[1] = L.wk; j.N[1] = p.nkv * p.hd;
-  j.W[2] = L.wv; j.N[2] = p.nkv * p.hd;
-  j.K = p.H;
-  j.u_off = p.off_u;
-  j.B = p.B;
-  j.pair = false;
   const int B = p.B;
-  build_slots(j, sm);
-  load_inv_rms(p, sm.inv, p.H);
+  SlotBuilder sb;
+  if (threadIdx.x == 0) {
+    sb.start();
+    int mq = sb.mat(L.wq, p.nq * p.hd, p.H, 0);
+    int mk = sb.mat(L.wk, p.nkv * p.hd, p.H, p.nq * p.hd);
+    int mv = sb.mat(L.wv, p.nkv * p.hd, p.H, (p.nq + p.nkv) * p.hd);
+    sb.begin(p.off_u, p.H, GK_SINGLE);
+    sb.singles_of(mq);
+    sb.singles_of(mk);
+    sb.singles_of(mv);
+  }
+  builder_done(p, sb, -1);
+  load_inv_rms(p, GSM.inv, p.H);
   sub_stamp(p, 0);
-  run_gemv(j, p.ws, p.ws_bytes, p.off_zero, [=](int slot0, int n) {
-    for (int e = threadIdx.x; e < n * 16 * B; e += NT) {
-      int t = e % B, rr = (e / B) % 16, i = e / (B * 16);
-      GSM.out[(slot0 + i) * 16 + rr][t] = GSM.y[i][rr][t] * GSM.inv[t];
-    }
-  });
+  run_gemv(p.ws, p.ws_bytes, p.off_zero, B, EPI_SCALED_SINGLE);
   sub_stamp(p, 2);
   const int nqkv = (p.nq + 2 * p.nkv) * p.hd;
-  const int col0[3] = {0, p.nq * p.hd, (p.nq + p.nkv) * p.hd};
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-  for (int e = threadIdx.x; e < sm.nslots * 16 * B; e += NT) {
+  for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
     int t = e % B, sr = e / B;
     int m, row;
-    if (!slot_row(sm.slots[sr >> 4], sr & 15, j.N, m, row)) continue;
-    st_f32(r, p.off_qkv + (uint32_t)(t * nqkv + col0[m] + row) * 4u, sm.out[sr][t]);
+    if (!slot_row(sr >> 4, sr & 15, m, row)) continue;
+    st_f32(r, p.off_qkv + (uint32_t)(t * nqkv + GSM.mats[m].tag + row) * 4u, GSM.out[sr][t]);
   }
 }
 
@@ -818,126 +891,279 @@ __device__ __noinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L,
   }
 }
 
-// --- residual-owning projection: x[t][r] += W . U; next norm input + ssq
-__device__ __noinline__ void phase_residual_gemv(const Params& p, const uint16_t* W, int K, uint32_t u_off,
-                                                 const uint16_t* g_next) {
-  GemvSmem& sm = *(GemvSmem*)md_smem;
-  GemvJob j;
-  j.nm = 1;
-  j.W[0] = W;
-  j.N[0] = p.H;
-  j.K = K;
-  j.u_off = u_off;
-  j.B = p.B;
-  j.pair = false;
+// Routing state of the current MoE layer (section "Our Kimi K3 megakernel":
+// router, then shared and routed experts).  It lives in LDS past every
+// phase's own block, so it survives from the routed gate/up phase to the
+// down projections.
+struct RouteSmem {
+  int nu;                 // |U|
+  int u[64];              // U, ascending expert id
+  int pos[64];            // expert id -> index in U, or -1
+  int ids[MAXB][8];       // chosen experts per token, in descending router order
+  float w[MAXB][8];       // their weights
+  float wt[MAXB][64];     // weight of U entry j for token t (0: not chosen)
+};
+constexpr size_t cmax_(size_t a, size_t b) { return a > b ? a : b; }
+constexpr size_t ROUTE_OFF = (cmax_(sizeof(GemvSmem) + (size_t)1024 * MAXB * 4, sizeof(AttnSmem)) + 63) / 64 * 64;
+#define RSM (*reinterpret_cast<RouteSmem*>(md_smem + ROUTE_OFF))
+
+// --- residual-owning projections: x[t][r] += sum over the phase's matrices
+// of W . U (the O-projection; the dense down projection; the shared and
+// routed expert down projections, whose inputs already carry the routing
+// weights), then the next norm's input U = hilo(g_next * x) and this WG's
+// sum of squares of x.
+enum : int { RES_OPROJ = 0, RES_DENSE_DOWN = 1, RES_MOE_DOWN = 2 };
+
+__device__ __noinline__ void phase_residual(const Params& p, const LayerDesc& L, int mode, const uint16_t* g_next) {
   const int B = p.B, H = p.H;
-  build_slots(j, sm);
-  // stage the residual rows and next-norm gains this workgroup owns
-  for (int e = threadIdx.x; e < sm.nslots * 16 * B; e += NT) {
-    int t = e % B, sr = e / B;
-    int m, row;
-    if (!slot_row(sm.slots[sr >> 4], sr & 15, j.N, m, row)) continue;
-    sm.in[sr][t] = p.x[t * H + row];
-    if (t == 0) sm.gain[sr] = bf16_f32(g_next[row]);
+  const RowSplit own = owned_rows(H, blockIdx.x, gridDim.x);
+  const int nrow = own.r1 - own.r0;
+  SlotBuilder sb;
+  if (threadIdx.x == 0) {
+    sb.start();
+    if (mode == RES_OPROJ) {
+      int m = sb.mat(L.wo, H, p.nq * p.hd, 0);
+      sb.begin(p.off_ou, p.nq * p.hd, GK_SINGLE);
+      sb.singles_of(m);
+    } else if (mode == RES_DENSE_DOWN) {
+      int m = sb.mat(L.w_down, H, p.ffn, 0);
+      sb.begin(p.off_h, p.ffn, GK_SINGLE);
+      sb.singles_of(m);
+    } else {
+      if (p.n_shared > 0) {
+        int m = sb.mat(L.sh_down, H, p.shared_ffn, 0);
+        sb.begin(p.off_hs, p.shared_ffn, GK_SINGLE);
+        sb.singles_of(m);
+      }
+      for (int j = 0; j < RSM.nu; ++j) {
+        int m = sb.mat(L.experts[RSM.u[j] * 3 + 2], H, p.expert_ffn, 0);
+        sb.begin(p.off_hr + (uint32_t)j * p.hr_stride, p.expert_ffn, GK_SINGLE);
+        sb.singles_of(m);
+      }
+    }
+  }
+  builder_done(p, sb, nrow);
+  // stage the residual rows this workgroup owns and the next norm's gains
+  for (int e = threadIdx.x; e < nrow * B; e += NT) {
+    int t = e % B, lr = e / B;
+    GSM.out[lr][t] = p.x[t * H + own.r0 + lr];
+    if (t == 0) GSM.gain[lr] = bf16_f32(g_next[own.r0 + lr]);
   }
   __syncthreads();
   sub_stamp(p, 0);
-  run_gemv(j, p.ws, p.ws_bytes, p.off_zero, [=](int slot0, int n) {
-    for (int e = threadIdx.x; e < n * 16 * B; e += NT) {
+  const int r0 = own.r0;
+  run_gemv(p.ws, p.ws_bytes, p.off_zero, B, [=](int g) {
+    for (int e = threadIdx.x; e < TG * 16 * B; e += NT) {
       int t = e % B, rr = (e / B) % 16, i = e / (B * 16);
-      int sr = (slot0 + i) * 16 + rr;
-      GSM.out[sr][t] = GSM.in[sr][t] + GSM.y[i][rr][t];
+      int m, row;
+      if (slot_row(2 * g + i, rr, m, row)) GSM.out[row - r0][t] += GSM.y[i][rr][t];
     }
   });
   sub_stamp(p, 2);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   static_assert(sizeof(GemvSmem::red) >= sizeof(float) * NT * MAXB, "partial sums reuse the reduction scratch");
-  float* part = (float*)sm.red;  // [NT][MAXB], reuses the reduction scratch
+  float* part = (float*)GSM.red;  // [NT][MAXB]
   for (int t = 0; t < MAXB; ++t) part[threadIdx.x * MAXB + t] = 0.f;
-  for (int e = threadIdx.x; e < sm.nslots * 16 * B; e += NT) {
-    int t = e % B, sr = e / B;
-    int m, row;
-    if (!slot_row(sm.slots[sr >> 4], sr & 15, j.N, m, row)) continue;
-    float x = sm.out[sr][t];
-    p.x[t * H + row] = x;
-    put_hilo(r, p.off_u, H, t, row, sm.gain[sr] * x);
+  for (int e = threadIdx.x; e < nrow * B; e += NT) {
+    int t = e % B, lr = e / B;
+    float x = GSM.out[lr][t];
+    p.x[t * H + r0 + lr] = x;
+    put_hilo(r, p.off_u, H, t, r0 + lr, GSM.gain[lr] * x);
     part[threadIdx.x * MAXB + t] += x * x;
   }
-  __syncthreads();
-  if (threadIdx.x < MAXB) {
-    float a = 0.f;
-    for (int i = 0; i < NT; ++i) a += part[i * MAXB + threadIdx.x];
-    st_f32(r, p.off_ssq + (uint32_t)(blockIdx.x * MAXB + threadIdx.x) * 4u, a);
-  }
+  store_ssq(p, r, part);
 }
 
 // --- dense SwiGLU gate/up: h = silu(inv*Wg U) * (inv*Wu U) -> hi/lo
-__device__ __noinline__ void phase_gateup(const Params& p, const uint16_t* Wg, const uint16_t* Wu, int F) {
-  GemvSmem& sm = *(GemvSmem*)md_smem;
-  GemvJob j;
-  j.nm = 2;
-  j.W[0] = Wg; j.N[0] = F;
-  j.W[1] = Wu; j.N[1] = F;
-  j.K = p.H;
-  j.u_off = p.off_u;
-  j.B = p.B;
-  j.pair = true;
-  const int B = p.B;
-  build_slots(j, sm);
-  load_inv_rms(p, sm.inv, p.H);
+__device__ __noinline__ void phase_gateup(const Params& p, const LayerDesc& L) {
+  const int B = p.B, F = p.ffn;
+  SlotBuilder sb;
+  if (threadIdx.x == 0) {
+    sb.start();
+    int mg = sb.mat(L.w_gate, F, p.H, 0);
+    int mu = sb.mat(L.w_up, F, p.H, 0);
+    sb.begin(p.off_u, p.H, GK_PAIR);
+    sb.pairs_of(mg, mu);
+  }
+  builder_done(p, sb, -1);
+  load_inv_rms(p, GSM.inv, p.H);
   sub_stamp(p, 0);
-  // slots come as (gate quarters, the same up quarters); h goes to the gate slot's rows
-  run_gemv(j, p.ws, p.ws_bytes, p.off_zero, [=](int slot0, int n) {
-    for (int e = threadIdx.x; e < 16 * B; e += NT) {
-      int t = e % B, rr = e / B;
-      float a = GSM.y[0][rr][t] * GSM.inv[t];
-      float u = GSM.y[1][rr][t] * GSM.inv[t];
-      GSM.out[slot0 * 16 + rr][t] = silu(a) * u;
+  run_gemv(p.ws, p.ws_bytes, p.off_zero, B, EPI_SWIGLU);
+  sub_stamp(p, 2);
+  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+  for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
+    int t = e % B, sr = e / B;
+    if ((sr >> 4) & 1) continue;  // up slots carry no output
+    int m, row;
+    if (!slot_row(sr >> 4, sr & 15, m, row)) continue;
+    put_hilo(r, p.off_h, F, t, row, GSM.out[sr][t]);
+  }
+}
+
+// ------------------------------------------------------------------ MoE
+// Section "Our Kimi K3 megakernel" of the pages orders a MoE layer as router,
+// shared expert, routed experts.  Phase A streams the router (E rows) and the
+// shared expert's gate/up; after the sync every workgroup derives the
+// routing from the fp32 router logits itself (same data, same fixed order,
+// so every copy is identical and no further sync is needed); phase B streams
+// the gate/up of the experts any token chose (their union U, ascending id),
+// scaling each token's h by its routing weight (0 when it did not choose the
+// expert); the down projections of the shared and the routed experts then
+// run as one residual phase.
+
+
+__device__ __noinline__ void phase_moe_a(const Params& p, const LayerDesc& L) {
+  const int B = p.B;
+  SlotBuilder sb;
+  if (threadIdx.x == 0) {
+    sb.start();
+    if (p.n_shared > 0) {
+      int mg = sb.mat(L.sh_gate, p.shared_ffn, p.H, 0);
+      int mu = sb.mat(L.sh_up, p.shared_ffn, p.H, 0);
+      sb.begin(p.off_u, p.H, GK_PAIR);
+      sb.pairs_of(mg, mu);
+    }
+    int mr = sb.mat(L.router, p.n_experts, p.H, -1);
+    sb.begin(p.off_u, p.H, GK_SINGLE);
+    sb.singles_of(mr);
+  }
+  builder_done(p, sb, -1);
+  load_inv_rms(p, GSM.inv, p.H);
+  sub_stamp(p, 0);
+  run_gemv(p.ws, p.ws_bytes, p.off_zero, B, [=](int g) {
+    if (GSM.grp[g].kind == GK_PAIR) {
+      for (int e = threadIdx.x; e < 16 * B; e += NT) {
+        int t = e % B, rr = e / B;
+        float a = GSM.y[0][rr][t] * GSM.inv[t];
+        float u = GSM.y[1][rr][t] * GSM.inv[t];
+        GSM.out[2 * g * 16 + rr][t] = silu(a) * u;
+      }
+    } else {
+      for (int e = threadIdx.x; e < TG * 16 * B; e += NT) {
+        int t = e % B, rr = (e / B) % 16, i = e / (B * 16);
+        GSM.out[(2 * g + i) * 16 + rr][t] = GSM.y[i][rr][t] * GSM.inv[t];
+      }
     }
   });
   sub_stamp(p, 2);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-  for (int e = threadIdx.x; e < sm.nslots * 16 * B; e += NT) {
+  for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
     int t = e % B, sr = e / B;
-    int slot = sr >> 4;
-    if (slot & 1) continue;  // up slots carry no output
+    int si = sr >> 4;
+    bool pair = GSM.grp[si >> 1].kind == GK_PAIR;
+    if (pair && (si & 1)) continue;  // up slots carry no output
     int m, row;
-    if (!slot_row(sm.slots[slot], sr & 15, j.N, m, row)) continue;
-    put_hilo(r, p.off_h, F, t, row, sm.out[sr][t]);
+    if (!slot_row(si, sr & 15, m, row)) continue;
+    if (pair) put_hilo(r, p.off_hs, p.shared_ffn, t, row, GSM.out[sr][t]);
+    else st_f32(r, p.off_rl + (uint32_t)(t * p.n_experts + row) * 4u, GSM.out[sr][t]);
+  }
+}
+
+// Routing of every token from the router logits (fp32, written by phase A):
+// the top_k experts by logit, larger first and the lower id on ties;
+// weights softmax(logits) over all experts at the chosen ones, renormalised
+// over the chosen ones when norm_topk.  Every workgroup runs this on the same
+// data in the same order.  Workgroup 0 reports the choices.
+__device__ __noinline__ void compute_routes(const Params& p, int layer) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int E = p.n_experts, k = p.top_k, B = p.B;
+  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+  for (int t = wv; t < B; t += NW) {
+    float lg = lane < E ? ld_f32(r, p.off_rl + (uint32_t)(t * E + lane) * 4u) : -INFINITY;
+    float mx0 = wave_max(lg);
+    float pe = lane < E ? __expf(lg - mx0) : 0.f;
+    float all = wave_sum(pe);
+    bool taken = false;
+    float sel = 0.f;
+    for (int j = 0; j < k; ++j) {
+      float key = (taken || lane >= E) ? -INFINITY : lg;
+      float mx = wave_max(key);
+      uint64_t bal = __ballot(!taken && lane < E && key == mx);
+      int e = bal ? (int)__builtin_ctzll(bal) : 0;
+      if (lane == e) taken = true;
+      float pj = __shfl(pe, e, 64);
+      sel += pj;
+      if (lane == 0) { RSM.ids[t][j] = e; RSM.w[t][j] = pj; }
+    }
+    float den = p.norm_topk ? sel : all;
+    __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+    __builtin_amdgcn_wave_barrier();
+    if (lane < k) RSM.w[t][lane] = RSM.w[t][lane] / den;
+  }
+  if (threadIdx.x < 64) RSM.pos[threadIdx.x] = -1;
+  for (int i = threadIdx.x; i < MAXB * 64; i += NT) RSM.wt[i >> 6][i & 63] = 0.f;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t mask = 0;
+    for (int t = 0; t < B; ++t)
+      for (int j = 0; j < k; ++j) mask |= 1ull << RSM.ids[t][j];
+    int n = 0;
+    for (int e = 0; e < E; ++e)
+      if ((mask >> e) & 1ull) { RSM.u[n] = e; RSM.pos[e] = n; ++n; }
+    RSM.nu = n;
+  }
+  __syncthreads();
+  if (threadIdx.x < B * k) {
+    int t = threadIdx.x / k, j = threadIdx.x % k;
+    RSM.wt[t][RSM.pos[RSM.ids[t][j]]] = RSM.w[t][j];
+    if (blockIdx.x == 0 && p.out_ids) p.out_ids[((size_t)layer * B + t) * k + j] = RSM.ids[t][j];
+  }
+  __syncthreads();
+}
+
+__device__ __noinline__ void phase_moe_b(const Params& p, const LayerDesc& L) {
+  const int B = p.B;
+  SlotBuilder sb;
+  if (threadIdx.x == 0) {
+    sb.start();
+    sb.begin(p.off_u, p.H, GK_PAIR);
+    for (int j = 0; j < RSM.nu; ++j) {
+      const uint16_t* const* ex = L.experts + RSM.u[j] * 3;
+      int mg = sb.mat(ex[0], p.expert_ffn, p.H, j);
+      int mu = sb.mat(ex[1], p.expert_ffn, p.H, j);
+      sb.pairs_of(mg, mu);
+    }
+  }
+  builder_done(p, sb, -1);
+  load_inv_rms(p, GSM.inv, p.H);
+  sub_stamp(p, 0);
+  run_gemv(p.ws, p.ws_bytes, p.off_zero, B, EPI_SWIGLU);
+  sub_stamp(p, 2);
+  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+  for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
+    int t = e % B, sr = e / B;
+    if ((sr >> 4) & 1) continue;
+    int m, row;
+    if (!slot_row(sr >> 4, sr & 15, m, row)) continue;
+    int j = GSM.mats[m].tag;
+    put_hilo(r, p.off_hr + (uint32_t)j * p.hr_stride, p.expert_ffn, t, row, GSM.out[sr][t] * RSM.wt[t][j]);
   }
 }
 
 // --- final norm + LM head: logits, per-WG argmax candidates
 __device__ __noinline__ void phase_lmhead(const Params& p) {
-  GemvSmem& sm = *(GemvSmem*)md_smem;
-  GemvJob j;
-  j.nm = 1;
-  j.W[0] = p.lm_head;
-  j.N[0] = p.V;
-  j.K = p.H;
-  j.u_off = p.off_u;
-  j.B = p.B;
-  j.pair = false;
   const int B = p.B;
-  build_slots(j, sm);
-  load_inv_rms(p, sm.inv, p.H);
+  SlotBuilder sb;
+  if (threadIdx.x == 0) {
+    sb.start();
+    int m = sb.mat(p.lm_head, p.V, p.H, 0);
+    sb.begin(p.off_u, p.H, GK_SINGLE);
+    sb.singles_of(m);
+  }
+  builder_done(p, sb, -1);
+  load_inv_rms(p, GSM.inv, p.H);
   sub_stamp(p, 0);
-  run_gemv(j, p.ws, p.ws_bytes, p.off_zero, [=](int slot0, int n) {
-    for (int e = threadIdx.x; e < n * 16 * B; e += NT) {
-      int t = e % B, rr = (e / B) % 16, i = e / (B * 16);
-      GSM.out[(slot0 + i) * 16 + rr][t] = GSM.y[i][rr][t] * GSM.inv[t];
-    }
-  });
+  run_gemv(p.ws, p.ws_bytes, p.off_zero, B, EPI_SCALED_SINGLE);
   sub_stamp(p, 2);
   static_assert(sizeof(GemvSmem::in) >= 2 * sizeof(float) * NT * MAXB, "argmax scratch reuses the input staging");
-  float* bv = &sm.in[0][0];              // [NT][MAXB] best value (the input staging is unused here)
+  float* bv = &GSM.in[0][0];             // [NT][MAXB] best value (the input staging is unused here)
   int* bi = (int*)(bv + NT * MAXB);      // [NT][MAXB] best index
   for (int t = 0; t < MAXB; ++t) { bv[threadIdx.x * MAXB + t] = -INFINITY; bi[threadIdx.x * MAXB + t] = 0x7FFFFFFF; }
-  for (int e = threadIdx.x; e < sm.nslots * 16 * B; e += NT) {
+  for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
     int t = e % B, sr = e / B;
     int m, v;
-    if (!slot_row(sm.slots[sr >> 4], sr & 15, j.N, m, v)) continue;
-    float lg = sm.out[sr][t];
+    if (!slot_row(sr >> 4, sr & 15, m, v)) continue;
+    float lg = GSM.out[sr][t];
     p.logits[(size_t)t * p.V + v] = lg;
     float& cb = bv[threadIdx.x * MAXB + t];
     int& ci = bi[threadIdx.x * MAXB + t];
@@ -999,12 +1225,22 @@ extern "C" __global__ __launch_bounds__(NT) void md_megakernel(Params p) {
     grid_sync(p, sidx);
     phase_attn_gqa(p, L, l);
     grid_sync(p, sidx);
-    phase_residual_gemv(p, L.wo, p.nq * p.hd, p.off_ou, L.ffn_norm);
+    phase_residual(p, L, RES_OPROJ, L.ffn_norm);
     grid_sync(p, sidx);
-    phase_gateup(p, L.w_gate, L.w_up, p.ffn);
-    grid_sync(p, sidx);
-    phase_residual_gemv(p, L.w_down, p.ffn, p.off_h, g_next);
-    grid_sync(p, sidx);
+    if (p.n_experts == 0) {
+      phase_gateup(p, L);
+      grid_sync(p, sidx);
+      phase_residual(p, L, RES_DENSE_DOWN, g_next);
+      grid_sync(p, sidx);
+    } else {
+      phase_moe_a(p, L);
+      grid_sync(p, sidx);
+      compute_routes(p, l);
+      phase_moe_b(p, L);
+      grid_sync(p, sidx);
+      phase_residual(p, L, RES_MOE_DOWN, g_next);
+      grid_sync(p, sidx);
+    }
     if (dev_failed(p)) return;
   }
   phase_lmhead(p);
@@ -1049,11 +1285,9 @@ hipError_t launch_pack(const void* src, void* dst, int64_t rows, int64_t cols, h
   return hipGetLastError();
 }
 
-size_t megakernel_smem_bytes() {
-  size_t gemv = sizeof(GemvSmem) + (size_t)1024 * MAXB * 4 + 64;  // + partial-sum staging of up to 1024 workgroups
-  size_t attn = sizeof(AttnSmem) + 64;
-  return gemv > attn ? gemv : attn;
-}
+// LDS: the larger of the GEMV block (+ partial-sum staging of up to 1024
+// workgroups) and the attention block, then the routing state.
+size_t megakernel_smem_bytes() { return ROUTE_OFF + sizeof(RouteSmem); }
 
 hipError_t launch_megakernel(const Params& p, int grid, hipStream_t stream) {
   void* args[] = {(void*)&p};

@@ -5,7 +5,7 @@
 namespace md {
 
 // device error bits (md_get_device_status)
-enum : int { MDE_WATCHDOG = 1, MDE_TOKEN = 2, MDE_POSITION = 4 };
+enum : int { MDE_WATCHDOG = 1, MDE_TOKEN = 2, MDE_POSITION = 4, MDE_CAPACITY = 8 };
 
 enum LayerKind : int { LK_GQA = 0, LK_MLA = 1, LK_KDA = 2 };
 
@@ -60,7 +60,11 @@ struct Params {
   uint32_t off_attn;  // attention partial outputs fp32[MAXB][nq][C][hd]
   uint32_t off_attn_ml; // attention partial (max, sum) fp32[MAXB][nq][C][2]
   uint32_t off_ou;    // hi/lo bf16[2][MAXB][nq*hd]
-  uint32_t off_h;     // hi/lo bf16[2][MAXB][F]
+  uint32_t off_h;     // hi/lo bf16[2][MAXB][F]           dense FFN hidden
+  uint32_t off_rl;    // fp32[MAXB][n_experts]             router logits
+  uint32_t off_hs;    // hi/lo bf16[2][MAXB][shared_ffn]   shared expert hidden
+  uint32_t off_hr;    // hi/lo bf16[nu][2][MAXB][expert_ffn] routed hidden (x routing weight), U order
+  uint32_t hr_stride; // bytes per routed expert slot
   uint32_t off_cand;  // argmax candidates {f32, i32}[G][MAXB]
   uint32_t off_zero;  // 1 KB that stays zero (target of masked loads)
   const float* rope;  // (cos, sin) fp32[max_ctx][rope_d/2][2]

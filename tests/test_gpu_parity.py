@@ -52,7 +52,9 @@ def test_device_draws_match_host_draws(torch_cuda):
         assert np.array_equal(kv[l], synth.kv_layer_host(w, l))
 
 
-@pytest.mark.parametrize("name,B", [("tiny_dense", 1), ("mini_dense", 1), ("mini_dense", 3), ("mini_dense", 8)])
+@pytest.mark.parametrize("name,B", [("tiny_dense", 1), ("mini_dense", 1), ("mini_dense", 3), ("mini_dense", 8),
+                                    ("mini_moe", 1), ("mini_moe", 3), ("mini_moe", 8),
+                                    ("small_moe", 1), ("small_moe", 8)])
 def test_decode_step_matches_oracle(torch_cuda, name, B):
     w = WL.get(name)
     m = _model(w)
@@ -79,6 +81,22 @@ def test_zero_layer_weights_identity(torch_cuda):
     g = GU.run_gpu_step(m, toks, pos)
     o, _ = GU.run_oracle_step(w, toks, pos, overrides=over)
     GU.compare_step(w, g, o, "zero-weights")
+
+
+def test_zero_router_picks_lowest_ids(torch_cuda):
+    """Zeroed layer matrices in a MoE model: every router logit is 0, all
+    experts tie, and the tie rule picks experts 0..k-1 for every token."""
+    w = WL.mini_moe()
+    over = {t.name: np.zeros((t.rows, t.cols), np.uint16) for t in synth.tensor_inventory(w)
+            if t.kind != "gain" and t.name not in ("embed", "lm_head")}
+    m = _model(w, overrides=over)
+    toks = synth.tokens(w, 3)
+    pos = [3, 40, 7]
+    g = GU.run_gpu_step(m, toks, pos)
+    want = np.broadcast_to(np.arange(w.top_k, dtype=np.int32), g["expert_ids"].shape)
+    assert np.array_equal(g["expert_ids"], want)
+    o, _ = GU.run_oracle_step(w, toks, pos, overrides=over)
+    GU.compare_step(w, g, o, "zero-weights moe")
 
 
 def test_repeated_steps_are_bitwise_deterministic(torch_cuda):

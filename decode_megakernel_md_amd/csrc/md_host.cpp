@@ -38,7 +38,7 @@ constexpr int MAXB_ = 8;
 constexpr int GMAX = 1024;        // largest grid the workspace is sized for
 constexpr int CMAX = 256;         // largest number of KV chunks per (sequence, kv head)
 constexpr int SP_WORDS_ = 9 * 32;
-constexpr int PHASES_PER_LAYER = 8;  // upper bound on sync points per layer
+constexpr int PHASES_PER_LAYER = 10;  // upper bound on sync points per layer
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -119,7 +119,24 @@ md_status validate(const md_config* c) {
     if (c->n_q_heads / c->n_kv_heads > 8) return fail(MD_EUNSUPPORTED, "at most 8 query heads per kv head");
     if (c->head_dim != 64 && c->head_dim != 128) return fail(MD_EUNSUPPORTED, "head_dim must be 64 or 128");
   } else if (c->attn_kind == 1) {
-    return fail(MD_EUNSUPPORTED, "hybrid MLA / delta-rule layers are not built yet");
+    if (c->mla_every < 1) return fail(MD_EINVAL, "mla_every must be >= 1");
+    bool has_mla = c->n_layers >= c->mla_every, has_kda = c->mla_every > 1;
+    if (has_mla) {
+      if (c->mla_heads < 1 || c->mla_heads > 32) return fail(MD_EUNSUPPORTED, "mla_heads must be in [1, 32]");
+      if (c->kv_lora != 512 || c->rope_dim != 64) return fail(MD_EUNSUPPORTED, "MLA needs kv_lora 512 and rope_dim 64");
+      if (c->nope_dim < 16 || c->nope_dim > 128 || c->nope_dim % 16)
+        return fail(MD_EUNSUPPORTED, "nope_dim must be a multiple of 16 in [16, 128]");
+      if (c->v_dim < 32 || c->v_dim % 32) return fail(MD_EUNSUPPORTED, "v_dim must be a positive multiple of 32");
+      if (c->q_lora < 128 || c->q_lora % 32) return fail(MD_EUNSUPPORTED, "q_lora must be a multiple of 32, at least 128");
+      if (c->mla_heads * c->v_dim < 128) return fail(MD_EUNSUPPORTED, "mla_heads * v_dim must be at least 128");
+    }
+    if (has_kda) {
+      if (c->kda_heads < 1) return fail(MD_EINVAL, "kda_heads must be positive");
+      if (c->kda_dk < 1 || c->kda_dk > 128) return fail(MD_EUNSUPPORTED, "kda_dk must be in [1, 128]");
+      if (c->kda_dv < 32 || c->kda_dv % 32) return fail(MD_EUNSUPPORTED, "kda_dv must be a positive multiple of 32");
+      if (c->kda_heads * c->kda_dv < 128) return fail(MD_EUNSUPPORTED, "kda_heads * kda_dv must be at least 128");
+      if (c->kda_qk_l2norm != 0 && c->kda_qk_l2norm != 1) return fail(MD_EINVAL, "kda_qk_l2norm must be 0 or 1");
+    }
   } else {
     return fail(MD_EINVAL, "attn_kind must be 0 or 1");
   }
@@ -145,7 +162,8 @@ md_status validate(const md_config* c) {
 }
 
 struct WsLayout {
-  size_t layers, experts, x, u, ssq, qkv, attn, attn_ml, ou, h, rl, hs, hr, hr_stride, cand, zero, rope, sync, err, total;
+  size_t layers, experts, x, u, ssq, qkv, attn, attn_ml, ou, h, rl, hs, hr, hr_stride, uq, ssq2, ckv, qm, qabs, mz, mml,
+      kda, cand, zero, rope, sync, err, total;
   int rope_d;
   int n_sync, sync_attn_base;
 };
@@ -161,6 +179,12 @@ WsLayout ws_layout(const md_config* c) {
   int64_t H = c->hidden;
   int64_t nqkv = c->attn_kind == 0 ? (int64_t)(c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim : 0;
   int64_t attn_out = c->attn_kind == 0 ? (int64_t)c->n_q_heads * c->head_dim : 0;
+  if (c->attn_kind == 1) {
+    int64_t a = (int64_t)c->mla_heads * c->v_dim, b = (int64_t)c->kda_heads * c->kda_dv;
+    attn_out = a > b ? a : b;
+  }
+  const bool hyb = c->attn_kind == 1;
+  const int64_t mh = hyb ? (c->mla_heads > 0 ? c->mla_heads : 1) : 1;
   int64_t F = c->ffn_dim;
   if (c->expert_ffn > F) F = c->expert_ffn;
   if (c->shared_ffn > F) F = c->shared_ffn;
@@ -179,6 +203,14 @@ WsLayout ws_layout(const md_config* c) {
   int nu = c->n_experts < c->max_batch * c->top_k ? c->n_experts : c->max_batch * c->top_k;
   w.hr_stride = align256(2 * 2 * MAXB_ * (size_t)(c->expert_ffn > 0 ? c->expert_ffn : 1));
   w.hr = take(w.hr_stride * (size_t)(nu > 0 ? nu : 1));
+  w.uq = take(2 * 2 * MAXB_ * (size_t)(hyb ? c->q_lora : 1));
+  w.ssq2 = take(4 * (size_t)GMAX * MAXB_);
+  w.ckv = take(4 * MAXB_ * 576);
+  w.qm = take(4 * MAXB_ * (size_t)mh * (hyb ? c->nope_dim + 64 : 1));
+  w.qabs = take(4 * MAXB_ * (size_t)mh * 576);
+  w.mz = take(hyb ? 4 * (size_t)GMAX * mh * 512 : 256);
+  w.mml = take(8 * (size_t)GMAX * mh);
+  w.kda = take(hyb ? 4 * MAXB_ * (size_t)(2 * c->kda_heads * c->kda_dk + c->kda_heads * c->kda_dv + 2 * c->kda_heads) : 256);
   w.cand = take(8 * (size_t)GMAX * MAXB_);
   w.zero = take(1024);
   w.rope_d = c->attn_kind == 0 ? c->head_dim : c->rope_dim;
@@ -251,7 +283,11 @@ int32_t md_weight_layout(const md_config* cfg, size_t i) {
   if (!cfg) return -1;
   auto T = inventory(cfg);
   if (i >= T.size()) return -1;
-  return (i == 0 || T[i].rows == 1) ? 0 : 1;  // embedding table and norm gains stay row-major
+  // the embedding table, the norm gains and the MLA up-projection (read by
+  // the vector units along both of its axes) stay row-major
+  const std::string& n = T[i].name;
+  bool wkvb = n.size() >= 8 && n.compare(n.size() - 8, 8, "mla_wkvb") == 0;
+  return (i == 0 || T[i].rows == 1 || wkvb) ? 0 : 1;
 }
 
 size_t md_workspace_bytes(const md_config* cfg) {
@@ -400,6 +436,18 @@ static md_status fill_params(md_model* m, const int32_t* tokens, const int32_t* 
   p.x = (float*)(m->ws + w.x);
   p.off_u = (uint32_t)w.u; p.off_ssq = (uint32_t)w.ssq; p.off_qkv = (uint32_t)w.qkv; p.off_attn = (uint32_t)w.attn; p.off_attn_ml = (uint32_t)w.attn_ml;
   p.off_ou = (uint32_t)w.ou; p.off_h = (uint32_t)w.h;
+  p.mla_h = c->mla_heads; p.q_lora = c->q_lora; p.nope = c->nope_dim; p.vdim = c->v_dim;
+  p.kda_h = c->kda_heads; p.kda_dk = c->kda_dk; p.kda_dv = c->kda_dv; p.kda_l2 = c->kda_qk_l2norm;
+  {
+    int cm = m->grid / batch;
+    int by_ctx = (c->max_ctx + 127) / 128;
+    if (cm > by_ctx) cm = by_ctx;
+    if (cm > CMAX) cm = CMAX;
+    if (cm < 1) cm = 1;
+    p.mla_chunks = cm;
+  }
+  p.off_uq = (uint32_t)w.uq; p.off_ssq2 = (uint32_t)w.ssq2; p.off_ckv = (uint32_t)w.ckv; p.off_qm = (uint32_t)w.qm;
+  p.off_qabs = (uint32_t)w.qabs; p.off_mz = (uint32_t)w.mz; p.off_mml = (uint32_t)w.mml; p.off_kda = (uint32_t)w.kda;
   p.off_rl = (uint32_t)w.rl; p.off_hs = (uint32_t)w.hs; p.off_hr = (uint32_t)w.hr; p.hr_stride = (uint32_t)w.hr_stride; p.off_cand = (uint32_t)w.cand; p.off_zero = (uint32_t)w.zero;
   p.rope = (const float*)(m->ws + w.rope); p.rope_d = w.rope_d;
   p.sync = (unsigned*)(m->ws + w.sync);

@@ -450,14 +450,14 @@ __device__ __forceinline__ bool builder_done(const Params& p, SlotBuilder& sb, i
 
 // inv_rms[t] from the per-WG partial sums of squares (fixed order: identical
 // in every workgroup).  ssq: fp32[G][MAXB] at ws offset p.off_ssq.
-__device__ __noinline__ void load_inv_rms(const Params& p, float* inv_rms, int n_feat) {
+__device__ __noinline__ void load_inv_rms(const Params& p, float* inv_rms, int n_feat, uint32_t off_ssq) {
   // every thread fetches one workgroup's partials for all tokens (one round
   // trip), then wave w reduces tokens 2w, 2w+1 in a fixed order
   float* stage = (float*)(md_smem + sizeof(GemvSmem));  // [G][MAXB]
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   for (int g = threadIdx.x; g < (int)gridDim.x; g += NT) {
-    i32x4 a = ld_x4<CP_SC1>(r, p.off_ssq + (uint32_t)(g * MAXB) * 4u);
-    i32x4 b = ld_x4<CP_SC1>(r, p.off_ssq + (uint32_t)(g * MAXB + 4) * 4u);
+    i32x4 a = ld_x4<CP_SC1>(r, off_ssq + (uint32_t)(g * MAXB) * 4u);
+    i32x4 b = ld_x4<CP_SC1>(r, off_ssq + (uint32_t)(g * MAXB + 4) * 4u);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       stage[g * MAXB + k] = __int_as_float(a[k]);
@@ -487,12 +487,12 @@ __device__ __forceinline__ void put_hilo(rsrc_t r, uint32_t u_off, int K, int t,
 
 // This workgroup's sum of squares of x per token (partials [NT][MAXB] in
 // the reduction scratch, summed in a fixed order) -> ssq[w][t].
-__device__ __forceinline__ void store_ssq(const Params& p, rsrc_t r, float* part) {
+__device__ __forceinline__ void store_ssq(const Params& p, rsrc_t r, float* part, uint32_t off_ssq) {
   __syncthreads();
   if (threadIdx.x < MAXB) {
     float a = 0.f;
     for (int i = 0; i < NT; ++i) a += part[i * MAXB + threadIdx.x];
-    st_f32(r, p.off_ssq + (uint32_t)(blockIdx.x * MAXB + threadIdx.x) * 4u, a);
+    st_f32(r, off_ssq + (uint32_t)(blockIdx.x * MAXB + threadIdx.x) * 4u, a);
   }
 }
 
@@ -515,7 +515,7 @@ __device__ __noinline__ void phase_embed(const Params& p) {
     put_hilo(r, p.off_u, p.H, t, i, bf16_f32(g[i]) * x);
     part[threadIdx.x * MAXB + t] += x * x;
   }
-  store_ssq(p, r, part);
+  store_ssq(p, r, part, p.off_ssq);
 }
 
 // Epilogue of phases whose output is y * inv_rms per slot row.
@@ -553,7 +553,7 @@ __device__ __noinline__ void phase_qkv(const Params& p, const LayerDesc& L) {
     sb.singles_of(mv);
   }
   builder_done(p, sb, -1);
-  load_inv_rms(p, GSM.inv, p.H);
+  load_inv_rms(p, GSM.inv, p.H, p.off_ssq);
   sub_stamp(p, 0);
   run_gemv(p.ws, p.ws_bytes, p.off_zero, B, EPI_SCALED_SINGLE);
   sub_stamp(p, 2);
@@ -891,6 +891,576 @@ __device__ __noinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L,
   }
 }
 
+// ------------------------------------------------------------------ gated delta rule
+// Layers that are not MLA in the hybrid model (section "Our Kimi K3
+// megakernel": the attention kind is chosen by layer index).  Per head h,
+// with q and k L2-normalised and alpha, beta the sigmoid gates:
+//   u = S^T k;  S <- alpha S + beta k (v - u)^T;  o = S^T q (updated S).
+// Projection phase: q, k, v and the two gate logits per head, one GEMV
+// over five matrices; kda[t] = [q (nh*dk) | k (nh*dk) | v (nh*dv) | a (nh) | b (nh)].
+__device__ __noinline__ void phase_kda_proj(const Params& p, const LayerDesc& L) {
+  const int B = p.B, nh = p.kda_h, dk = p.kda_dk, dv = p.kda_dv;
+  const int width = 2 * nh * dk + nh * dv + 2 * nh;
+  SlotBuilder sb;
+  if (threadIdx.x == 0) {
+    sb.start();
+    int m0 = sb.mat(L.kda_wq, nh * dk, p.H, 0);
+    int m1 = sb.mat(L.kda_wk, nh * dk, p.H, nh * dk);
+    int m2 = sb.mat(L.kda_wv, nh * dv, p.H, 2 * nh * dk);
+    int m3 = sb.mat(L.kda_wa, nh, p.H, 2 * nh * dk + nh * dv);
+    int m4 = sb.mat(L.kda_wb, nh, p.H, 2 * nh * dk + nh * dv + nh);
+    sb.begin(p.off_u, p.H, GK_SINGLE);
+    sb.singles_of(m0);
+    sb.singles_of(m1);
+    sb.singles_of(m2);
+    sb.singles_of(m3);
+    sb.singles_of(m4);
+  }
+  builder_done(p, sb, -1);
+  load_inv_rms(p, GSM.inv, p.H, p.off_ssq);
+  sub_stamp(p, 0);
+  run_gemv(p.ws, p.ws_bytes, p.off_zero, B, EPI_SCALED_SINGLE);
+  sub_stamp(p, 2);
+  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+  for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
+    int t = e % B, sr = e / B;
+    int m, row;
+    if (!slot_row(sr >> 4, sr & 15, m, row)) continue;
+    st_f32(r, p.off_kda + (uint32_t)(t * width + GSM.mats[m].tag + row) * 4u, GSM.out[sr][t]);
+  }
+}
+
+struct KdaSmem {
+  float q[128], k[128], v[32];
+  float qs, ks, a, b;
+  float red[8][32];
+  float red2[8][32];
+};
+
+// Recurrence phase: task (b, h, 32-column slice of the state).  The slice
+// (dk x 32 fp32) is read once into registers -- thread (rg, j) holds rows
+// rg, rg+8, ... of column j -- updated there and written back in place.
+__device__ __noinline__ void phase_kda_rec(const Params& p, const LayerDesc& L) {
+  KdaSmem& sm = *(KdaSmem*)md_smem;
+  const int B = p.B, nh = p.kda_h, dk = p.kda_dk, dv = p.kda_dv;
+  const int width = 2 * nh * dk + nh * dv + 2 * nh;
+  const int ns = dv / 32;
+  const int ntask = B * nh * ns;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int rg = threadIdx.x >> 5, jj = threadIdx.x & 31;
+  rsrc_t wr = make_rsrc_u(p.ws, p.ws_bytes);
+  for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
+    const int js = task % ns, h = (task / ns) % nh, b = task / (ns * nh);
+    const uint32_t base = p.off_kda + (uint32_t)(b * width) * 4u;
+    float* S = (float*)(p.kv + L.kv_off) + (size_t)(b * nh + h) * dk * dv;
+    rsrc_t srs = make_rsrc_u(S, (uint32_t)(dk * dv * 4));
+    float s[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      int i = rg + 8 * r;
+      s[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          srs, i < dk ? (uint32_t)(i * dv + 32 * js + jj) * 4u : OOB, 0, 0));
+    }
+    if (threadIdx.x < dk) {
+      sm.q[threadIdx.x] = ld_f32(wr, base + (uint32_t)(h * dk + threadIdx.x) * 4u);
+      sm.k[threadIdx.x] = ld_f32(wr, base + (uint32_t)(nh * dk + h * dk + threadIdx.x) * 4u);
+    }
+    if (threadIdx.x < 32) sm.v[threadIdx.x] = ld_f32(wr, base + (uint32_t)(2 * nh * dk + h * dv + 32 * js + threadIdx.x) * 4u);
+    if (threadIdx.x == 0) {
+      sm.a = sigmoid(ld_f32(wr, base + (uint32_t)(2 * nh * dk + nh * dv + h) * 4u));
+      sm.b = sigmoid(ld_f32(wr, base + (uint32_t)(2 * nh * dk + nh * dv + nh + h) * 4u));
+    }
+    __syncthreads();
+    if (wv < 2) {  // wave 0: 1/||q||, wave 1: 1/||k|| (1 without normalisation)
+      const float* vec = wv == 0 ? sm.q : sm.k;
+      float a0 = lane < dk ? vec[lane] : 0.f, a1 = lane + 64 < dk ? vec[lane + 64] : 0.f;
+      float n2 = wave_sum(a0 * a0 + a1 * a1);
+      float sc = p.kda_l2 ? 1.0f / fmaxf(sqrtf(n2), 1e-6f) : 1.0f;
+      if (lane == 0) { if (wv == 0) sm.qs = sc; else sm.ks = sc; }
+    }
+    __syncthreads();
+    const float qs = sm.qs, ks = sm.ks;
+    float up = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      int i = rg + 8 * r;
+      if (i < dk) up += s[r] * (sm.k[i] * ks);
+    }
+    sm.red[rg][jj] = up;
+    __syncthreads();
+    float u = 0.f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) u += sm.red[g][jj];
+    const float delta = sm.b * (sm.v[jj] - u), al = sm.a;
+    float op = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      int i = rg + 8 * r;
+      float kn = sm.k[i < dk ? i : 0] * ks;
+      s[r] = al * s[r] + kn * delta;
+      if (i < dk) op += s[r] * (sm.q[i] * qs);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s[r]), srs,
+                                            i < dk ? (uint32_t)(i * dv + 32 * js + jj) * 4u : OOB, 0, 0);
+    }
+    sm.red2[rg][jj] = op;
+    __syncthreads();
+    if (threadIdx.x < 32) {
+      float o = 0.f;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) o += sm.red2[g][threadIdx.x];
+      put_hilo(wr, p.off_ou, nh * dv, b, h * dv + 32 * js + threadIdx.x, o);
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ MLA
+// Multi-head latent attention (the other layer kind of the hybrid model), in
+// the absorbed form: the cache holds per position the RMS-normalised latent
+// c (kv_lora = 512) and the rotated key part k_pe (64).  Per head h:
+//   q~_h = W_uk,h^T q_nope,h;  s_t = (q~_h . c_t + q_pe,h . kpe_t) / sqrt(nope + rope);
+//   z_h = sum_t softmax(s)_t c_t;  o_h = W_uv,h z_h;  x += W_o o.
+constexpr int MLA_KL = 512, MLA_RD = 64, MLA_QA = MLA_KL + MLA_RD, MLA_KS = MLA_QA / 32;
+
+// M1: c_q0 = W_qa xn (q_lora) and ckv = W_kva xn (kv_lora + rope).  c_q0 goes
+// out as U = hilo(g_q * c_q0) plus its partial sums of squares (the q norm),
+// ckv as fp32.
+__device__ __noinline__ void phase_mla_a(const Params& p, const LayerDesc& L) {
+  const int B = p.B, QL = p.q_lora, KVR = MLA_QA;
+  SlotBuilder sb;
+  if (threadIdx.x == 0) {
+    sb.start();
+    int ma = sb.mat(L.mla_wqa, QL, p.H, 0);
+    int mk = sb.mat(L.mla_wkva, KVR, p.H, 1);
+    sb.begin(p.off_u, p.H, GK_SINGLE);
+    sb.singles_of(ma);
+    sb.singles_of(mk);
+  }
+  builder_done(p, sb, -1);
+  load_inv_rms(p, GSM.inv, p.H, p.off_ssq);
+  sub_stamp(p, 0);
+  run_gemv(p.ws, p.ws_bytes, p.off_zero, B, EPI_SCALED_SINGLE);
+  sub_stamp(p, 2);
+  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+  float* part = (float*)GSM.red;  // [NT][MAXB]
+  for (int t = 0; t < MAXB; ++t) part[threadIdx.x * MAXB + t] = 0.f;
+  for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
+    int t = e % B, sr = e / B;
+    int m, row;
+    if (!slot_row(sr >> 4, sr & 15, m, row)) continue;
+    float v = GSM.out[sr][t];
+    if (GSM.mats[m].tag == 0) {
+      put_hilo(r, p.off_uq, QL, t, row, bf16_f32(L.mla_qnorm[row]) * v);
+      part[threadIdx.x * MAXB + t] += v * v;
+    } else {
+      st_f32(r, p.off_ckv + (uint32_t)(t * KVR + row) * 4u, v);
+    }
+  }
+  store_ssq(p, r, part, p.off_ssq2);
+}
+
+// The new latent cache row of sequence b: RMSNorm(c) * g_kv and the rotated
+// k_pe, rounded to bf16, written device-coherently (another workgroup reads
+// it in this same step).
+__device__ void mla_cache_row(const Params& p, const LayerDesc& L, int b) {
+  float* c = &GSM.in[0][0];  // [576] (the staging area is free before the stream)
+  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+  int pos = p.positions[b];
+  if (pos < 0 || pos >= p.max_ctx) {
+    set_err(p, MDE_POSITION);
+    pos = pos < 0 ? 0 : p.max_ctx - 1;
+  }
+  for (int i = threadIdx.x; i < MLA_QA; i += NT) c[i] = ld_f32(r, p.off_ckv + (uint32_t)(b * MLA_QA + i) * 4u);
+  __syncthreads();
+  float* red = &GSM.in[80][0];  // [NW]
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < MLA_KL; i += NT) ss += c[i] * c[i];
+  ss = wave_sum(ss);
+  if (lane == 0) red[wv] = ss;
+  __syncthreads();
+  float tot = red[0] + red[1] + red[2] + red[3];
+  float inv = 1.0f / sqrtf(tot / (float)MLA_KL + p.eps);
+  uint16_t* row = (uint16_t*)(p.kv + L.kv_off) + ((size_t)b * p.max_ctx + pos) * MLA_QA;
+  rsrc_t cr = make_rsrc_u(row, MLA_QA * 2);
+  for (int i = threadIdx.x; i < MLA_KL; i += NT) st_u16(cr, (uint32_t)i * 2u, bf16_rne(bf16_f32(L.mla_kvnorm[i]) * (c[i] * inv)));
+  for (int i = threadIdx.x; i < MLA_RD / 2; i += NT) {
+    float cs, sn;
+    rope_cs(p, pos, i, cs, sn);
+    float a = c[MLA_KL + i], bb = c[MLA_KL + i + MLA_RD / 2];
+    st_u16(cr, (uint32_t)(MLA_KL + i) * 2u, bf16_rne(a * cs - bb * sn));
+    st_u16(cr, (uint32_t)(MLA_KL + i + MLA_RD / 2) * 2u, bf16_rne(a * sn + bb * cs));
+  }
+  wait_stores();
+  __syncthreads();
+}
+
+// M2: q = W_qb RMSNorm(c_q0) (nh x (nope + rope)), and the new cache rows
+// (workgroup G-1-b writes sequence b's).
+__device__ __noinline__ void phase_mla_b(const Params& p, const LayerDesc& L) {
+  const int B = p.B, nh = p.mla_h, QW = p.nope + MLA_RD;
+  const int cb = (int)gridDim.x - 1 - (int)blockIdx.x;
+  if (cb < B) mla_cache_row(p, L, cb);
+  SlotBuilder sb;
+  if (threadIdx.x == 0) {
+    sb.start();
+    int m = sb.mat(L.mla_wqb, nh * QW, p.q_lora, 0);
+    sb.begin(p.off_uq, p.q_lora, GK_SINGLE);
+    sb.singles_of(m);
+  }
+  builder_done(p, sb, -1);
+  load_inv_rms(p, GSM.inv, p.q_lora, p.off_ssq2);
+  sub_stamp(p, 0);
+  run_gemv(p.ws, p.ws_bytes, p.off_zero, B, EPI_SCALED_SINGLE);
+  sub_stamp(p, 2);
+  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+  for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
+    int t = e % B, sr = e / B;
+    int m, row;
+    if (!slot_row(sr >> 4, sr & 15, m, row)) continue;
+    st_f32(r, p.off_qm + (uint32_t)(t * nh * QW + row) * 4u, GSM.out[sr][t]);
+  }
+}
+
+// M3: absorbed queries qabs[t][h] = [W_uk,h^T q_nope,h | RoPE(q_pe,h)] / sqrt(nope + rope).
+// Task (h, 128-column block of the latent); all tokens at once, so each
+// slice of W_uk is read once.  W_kvb is row-major [nh*(nope+v)][512]: head
+// h's rows are [W_uk,h (nope rows) | W_uv,h (v rows)].
+__device__ __noinline__ void phase_mla_absorb(const Params& p, const LayerDesc& L) {
+  const int B = p.B, nh = p.mla_h, nope = p.nope, QW = nope + MLA_RD, VW = nope + p.vdim;
+  constexpr int NCB = MLA_KL / 128;
+  const int ntask = nh * NCB;
+  const float scale = 1.0f / sqrtf((float)QW);
+  float* qn = &GSM.in[0][0];               // [MAXB][nope <= 128]
+  float* red = &GSM.out[0][0];             // [NW][MAXB][128]
+  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+  rsrc_t wrs = make_rsrc_u(L.mla_wkvb, (uint32_t)((size_t)nh * VW * MLA_KL * 2));
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int cg = lane & 15, rg = wv * 4 + (lane >> 4);  // 16 row groups x 16 column groups of 8
+  for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
+    const int h = task / NCB, cbk = task % NCB;
+    for (int e = threadIdx.x; e < B * nope; e += NT) {
+      int t = e / nope, i = e % nope;
+      qn[t * 128 + i] = ld_f32(r, p.off_qm + (uint32_t)(t * nh * QW + h * QW + i) * 4u);
+    }
+    __syncthreads();
+    float acc[MAXB][8];
+#pragma unroll
+    for (int t = 0; t < MAXB; ++t)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[t][j] = 0.f;
+    for (int i = rg; i < nope; i += 16) {
+      i32x4 w = ld_x4<0>(wrs, (uint32_t)(((h * VW + i) * MLA_KL) + 128 * cbk + 8 * cg) * 2u);
+      float wf[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        wf[2 * j] = __uint_as_float((uint32_t)w[j] << 16);
+        wf[2 * j + 1] = __uint_as_float((uint32_t)w[j] & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int t = 0; t < MAXB; ++t) {
+        float qv = t < B ? qn[t * 128 + i] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[t][j] += wf[j] * qv;
+      }
+    }
+    // sum the 4 row groups of this wave, then the 4 waves
+#pragma unroll
+    for (int t = 0; t < MAXB; ++t)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[t][j] = rows_sum(acc[t][j]);
+    if (lane < 16) {
+#pragma unroll
+      for (int t = 0; t < MAXB; ++t)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) red[(wv * MAXB + t) * 128 + 8 * cg + j] = acc[t][j];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < B * 128; e += NT) {
+      int t = e / 128, c = e % 128;
+      float v = red[(0 * MAXB + t) * 128 + c] + red[(1 * MAXB + t) * 128 + c] + red[(2 * MAXB + t) * 128 + c] +
+                red[(3 * MAXB + t) * 128 + c];
+      st_f32(r, p.off_qabs + (uint32_t)((t * nh + h) * MLA_QA + 128 * cbk + c) * 4u, v * scale);
+    }
+    if (cbk == 0) {
+      for (int e = threadIdx.x; e < B * (MLA_RD / 2); e += NT) {
+        int t = e / (MLA_RD / 2), i = e % (MLA_RD / 2);
+        int pos = p.positions[t];
+        pos = pos < 0 ? 0 : (pos >= p.max_ctx ? p.max_ctx - 1 : pos);
+        float a = ld_f32(r, p.off_qm + (uint32_t)(t * nh * QW + h * QW + nope + i) * 4u);
+        float bb = ld_f32(r, p.off_qm + (uint32_t)(t * nh * QW + h * QW + nope + i + MLA_RD / 2) * 4u);
+        float cs, sn;
+        rope_cs(p, pos, i, cs, sn);
+        st_f32(r, p.off_qabs + (uint32_t)((t * nh + h) * MLA_QA + MLA_KL + i) * 4u, (a * cs - bb * sn) * scale);
+        st_f32(r, p.off_qabs + (uint32_t)((t * nh + h) * MLA_QA + MLA_KL + i + MLA_RD / 2) * 4u, (a * sn + bb * cs) * scale);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// M4: attention over the latent cache.  Task (b, chunk c) covers positions
+// [c*P, (c+1)*P) of 0..pos for every head at once, so each cache row is read
+// once per step.  Blocks of 32 rows are staged in LDS (next block in flight
+// while the current one is used); wave w serves heads 8w..8w+7: scores on
+// the matrix cores (rows as the A operand, the heads' absorbed queries as
+// hi/lo B columns), an online softmax per head, then z_h += p_t c_t with
+// each lane holding 8 latent dims.  Partial (max, sum, z) per head go to the
+// workspace.
+constexpr int MLA_ROWP = MLA_QA + 8;  // LDS row pitch in bf16 (pads rows off the same banks)
+struct MlaSmem {
+  uint16_t rows[2][32][MLA_ROWP];
+  float s[32][32];                    // [position][head] scores, then probabilities
+};
+
+__device__ __forceinline__ void mla_load_block(i32x4 (&pf)[9], rsrc_t crs, int blk, int a1) {
+#pragma unroll
+  for (int k = 0; k < 9; ++k) {
+    int ci = threadIdx.x + NT * k;
+    int rr = ci / (MLA_QA / 8), c16 = ci % (MLA_QA / 8);
+    int t = blk + rr;
+    pf[k] = ld_x4<CP_SC1>(crs, t < a1 ? (uint32_t)(t * MLA_QA + c16 * 8) * 2u : OOB);
+  }
+}
+__device__ __forceinline__ void mla_store_block(const i32x4 (&pf)[9], int buf) {
+  MlaSmem& sm = *(MlaSmem*)md_smem;
+#pragma unroll
+  for (int k = 0; k < 9; ++k) {
+    int ci = threadIdx.x + NT * k;
+    int rr = ci / (MLA_QA / 8), c16 = ci % (MLA_QA / 8);
+    *(i32x4*)&sm.rows[buf][rr][c16 * 8] = pf[k];
+  }
+}
+
+__device__ __noinline__ void phase_mla_attn(const Params& p, const LayerDesc& L) {
+  MlaSmem& sm = *(MlaSmem*)md_smem;
+  const int B = p.B, nh = p.mla_h, C = p.mla_chunks;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int nn = lane & 15, hh = nn >> 1, pp = nn & 1;
+  const int h0 = 8 * wv;
+  rsrc_t wr = make_rsrc_u(p.ws, p.ws_bytes);
+  for (int task = blockIdx.x; task < B * C; task += gridDim.x) {
+    const int c = task % C, b = task / C;
+    int pos = p.positions[b];
+    pos = pos < 0 ? 0 : (pos >= p.max_ctx ? p.max_ctx - 1 : pos);
+    const int n = pos + 1;
+    const int P = (n + C - 1) / C;
+    const int a0 = c * P < n ? c * P : n, a1 = (c + 1) * P < n ? (c + 1) * P : n;
+    const uint16_t* cache = (const uint16_t*)(p.kv + L.kv_off) + (size_t)b * p.max_ctx * MLA_QA;
+    rsrc_t crs = make_rsrc_u(cache, (uint32_t)((size_t)n * MLA_QA * 2));
+    // this wave's heads' absorbed queries as hi/lo B operands
+    bf16x8 qb[MLA_KS];
+    {
+      const int h = h0 + hh;
+#pragma unroll
+      for (int s = 0; s < MLA_KS; ++s) {
+        i32x4 v0 = ld_x4<CP_SC1>(wr, h < nh ? p.off_qabs + (uint32_t)((b * nh + h) * MLA_QA + s * 32 + (lane >> 4) * 8) * 4u : OOB);
+        i32x4 v1 = ld_x4<CP_SC1>(wr, h < nh ? p.off_qabs + (uint32_t)((b * nh + h) * MLA_QA + s * 32 + (lane >> 4) * 8 + 4) * 4u : OOB);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          float v = __int_as_float(k < 4 ? v0[k] : v1[k - 4]);
+          uint16_t hi, lo;
+          split_hilo(v, hi, lo);
+          qb[s][k] = __builtin_bit_cast(__bf16, pp ? lo : hi);
+        }
+      }
+    }
+    float m_run[8], l_run[8], acc[8][8];
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      m_run[h] = -INFINITY;
+      l_run[h] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
+    }
+    i32x4 pf[9];
+    int buf = 0;
+    if (a0 < a1) {
+      mla_load_block(pf, crs, a0, a1);
+      mla_store_block(pf, 0);
+    }
+    __syncthreads();
+    for (int blk = a0; blk < a1; blk += 32) {
+      const bool more = blk + 32 < a1;
+      if (more) mla_load_block(pf, crs, blk + 32, a1);
+      // scores of 32 positions x this wave's 8 heads
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < MLA_KS; ++s) {
+          i32x4 kv = *(const i32x4*)&sm.rows[buf][tt * 16 + (lane & 15)][s * 32 + (lane >> 4) * 8];
+          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qb[s], a, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = a[i] + dpp_f<DPP_QXOR1>(a[i]);
+          int pr = tt * 16 + 4 * (lane >> 4) + i;
+          if (!pp) sm.s[pr][h0 + hh] = (blk + pr < a1) ? v : -INFINITY;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+      __builtin_amdgcn_wave_barrier();
+      float corr[8];
+#pragma unroll
+      for (int h = 0; h < 8; ++h) {
+        float sv = lane < 32 ? sm.s[lane][h0 + h] : -INFINITY;
+        float mb = wave_max(sv);
+        float mn = fmaxf(m_run[h], mb);
+        corr[h] = __expf(m_run[h] - mn);
+        float pv = lane < 32 ? __expf(sv - mn) : 0.f;
+        l_run[h] = l_run[h] * corr[h] + wave_sum(pv);
+        m_run[h] = mn;
+        if (lane < 32) sm.s[lane][h0 + h] = pv;
+      }
+#pragma unroll
+      for (int h = 0; h < 8; ++h)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[h][j] *= corr[h];
+      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+      __builtin_amdgcn_wave_barrier();
+      const int nrow = a1 - blk < 32 ? a1 - blk : 32;
+      for (int t = 0; t < nrow; ++t) {
+        i32x4 cv = *(const i32x4*)&sm.rows[buf][t][lane * 8];
+        f32x4 p0 = *(const f32x4*)&sm.s[t][h0];
+        f32x4 p1 = *(const f32x4*)&sm.s[t][h0 + 4];
+        float cf[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          cf[2 * j] = __uint_as_float((uint32_t)cv[j] << 16);
+          cf[2 * j + 1] = __uint_as_float((uint32_t)cv[j] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          acc[0][j] += p0[0] * cf[j];
+          acc[1][j] += p0[1] * cf[j];
+          acc[2][j] += p0[2] * cf[j];
+          acc[3][j] += p0[3] * cf[j];
+          acc[4][j] += p1[0] * cf[j];
+          acc[5][j] += p1[1] * cf[j];
+          acc[6][j] += p1[2] * cf[j];
+          acc[7][j] += p1[3] * cf[j];
+        }
+      }
+      if (more) mla_store_block(pf, buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    }
+    // partials of this wave's heads
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      const int hg = h0 + h;
+      if (hg >= nh) break;
+      const uint32_t idx = (uint32_t)((b * C + c) * nh + hg);
+      if (lane == 0) {
+        st_f32(wr, p.off_mml + idx * 8u, m_run[h]);
+        st_f32(wr, p.off_mml + idx * 8u + 4u, l_run[h]);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) st_f32(wr, p.off_mz + (idx * MLA_KL + lane * 8 + j) * 4u, acc[h][j]);
+    }
+    __syncthreads();
+  }
+}
+
+// M5: combine the chunks of each head and un-absorb: o_h = W_uv,h z_h.
+// Task (h, 32-row slice of W_uv,h) for all tokens.
+__device__ __noinline__ void phase_mla_out(const Params& p, const LayerDesc& L) {
+  const int B = p.B, nh = p.mla_h, nope = p.nope, vd = p.vdim, VW = nope + vd, C = p.mla_chunks;
+  const int nsl = vd / 32;
+  const int ntask = nh * nsl;
+  float* z = &GSM.in[0][0];      // [MAXB][512]
+  float* cw = &GSM.out[0][0];    // [MAXB][256] combine weights
+  float* cl = cw + MAXB * 256;   // [MAXB] 1 / denominator
+  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+  rsrc_t wrs = make_rsrc_u(L.mla_wkvb, (uint32_t)((size_t)nh * VW * MLA_KL * 2));
+  const int lane = threadIdx.x & 63;
+  for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
+    const int h = task / nsl, sl = task % nsl;
+    for (int e = threadIdx.x; e < B * C; e += NT) {
+      int t = e / C, cc = e % C;
+      cw[t * 256 + cc] = ld_f32(r, p.off_mml + (uint32_t)((t * C + cc) * nh + h) * 8u);
+    }
+    __syncthreads();
+    if (threadIdx.x < B) {
+      int t = threadIdx.x;
+      float M = -INFINITY;
+      for (int cc = 0; cc < C; ++cc) M = fmaxf(M, cw[t * 256 + cc]);
+      float den = 0.f;
+      for (int cc = 0; cc < C; ++cc) {
+        float f = cw[t * 256 + cc] == -INFINITY ? 0.f : __expf(cw[t * 256 + cc] - M);
+        cw[t * 256 + cc] = f;
+        den += f * ld_f32(r, p.off_mml + (uint32_t)((t * C + cc) * nh + h) * 8u + 4u);
+      }
+      cl[t] = 1.0f / den;
+    }
+    __syncthreads();
+    // z[t][d], thread per (token, 4 dims), 8 chunk loads in flight
+    for (int e = threadIdx.x; e < B * (MLA_KL / 4); e += NT) {
+      int t = e / (MLA_KL / 4), d4 = (e % (MLA_KL / 4)) * 4;
+      float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+      for (int c0 = 0; c0 < C; c0 += 8) {
+        i32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          v[u] = ld_x4<CP_SC1>(r, c0 + u < C ? p.off_mz + ((uint32_t)((t * C + c0 + u) * nh + h) * MLA_KL + d4) * 4u : OOB);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          float f = c0 + u < C ? cw[t * 256 + c0 + u] : 0.f;
+          o0 += f * __int_as_float(v[u][0]);
+          o1 += f * __int_as_float(v[u][1]);
+          o2 += f * __int_as_float(v[u][2]);
+          o3 += f * __int_as_float(v[u][3]);
+        }
+      }
+      float il = cl[t];
+      z[t * MLA_KL + d4 + 0] = o0 * il;
+      z[t * MLA_KL + d4 + 1] = o1 * il;
+      z[t * MLA_KL + d4 + 2] = o2 * il;
+      z[t * MLA_KL + d4 + 3] = o3 * il;
+    }
+    __syncthreads();
+    // o[t][row] for the slice's 32 rows: 8 lanes per row, 64 dims each
+    {
+      const int row = sl * 32 + (threadIdx.x >> 3), part = threadIdx.x & 7;
+      float ot[MAXB];
+#pragma unroll
+      for (int t = 0; t < MAXB; ++t) ot[t] = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        int d = part * 64 + k * 8;
+        i32x4 w = ld_x4<0>(wrs, (uint32_t)((h * VW + nope + row) * MLA_KL + d) * 2u);
+        float wf[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          wf[2 * j] = __uint_as_float((uint32_t)w[j] << 16);
+          wf[2 * j + 1] = __uint_as_float((uint32_t)w[j] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int t = 0; t < MAXB; ++t) {
+          if (t < B) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ot[t] += wf[j] * z[t * MLA_KL + d + j];
+          }
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < MAXB; ++t) {
+        float v = ot[t];
+        v += __shfl_xor(v, 1, 64);
+        v += __shfl_xor(v, 2, 64);
+        v += __shfl_xor(v, 4, 64);
+        ot[t] = v;
+      }
+      if (part == 0) {
+        for (int t = 0; t < B; ++t) put_hilo(r, p.off_ou, nh * vd, t, h * vd + row, ot[t]);
+      }
+    }
+    (void)lane;
+    __syncthreads();
+  }
+}
+
 // Routing state of the current MoE layer (section "Our Kimi K3 megakernel":
 // router, then shared and routed experts).  It lives in LDS past every
 // phase's own block, so it survives from the routed gate/up phase to the
@@ -904,7 +1474,9 @@ struct RouteSmem {
   float wt[MAXB][64];     // weight of U entry j for token t (0: not chosen)
 };
 constexpr size_t cmax_(size_t a, size_t b) { return a > b ? a : b; }
-constexpr size_t ROUTE_OFF = (cmax_(sizeof(GemvSmem) + (size_t)1024 * MAXB * 4, sizeof(AttnSmem)) + 63) / 64 * 64;
+constexpr size_t ROUTE_OFF =
+    (cmax_(cmax_(sizeof(GemvSmem) + (size_t)1024 * MAXB * 4, sizeof(AttnSmem)), cmax_(sizeof(MlaSmem), sizeof(KdaSmem))) + 63) /
+    64 * 64;
 #define RSM (*reinterpret_cast<RouteSmem*>(md_smem + ROUTE_OFF))
 
 // --- residual-owning projections: x[t][r] += sum over the phase's matrices
@@ -912,7 +1484,7 @@ constexpr size_t ROUTE_OFF = (cmax_(sizeof(GemvSmem) + (size_t)1024 * MAXB * 4, 
 // routed expert down projections, whose inputs already carry the routing
 // weights), then the next norm's input U = hilo(g_next * x) and this WG's
 // sum of squares of x.
-enum : int { RES_OPROJ = 0, RES_DENSE_DOWN = 1, RES_MOE_DOWN = 2 };
+enum : int { RES_OPROJ = 0, RES_DENSE_DOWN = 1, RES_MOE_DOWN = 2, RES_MLA_O = 3, RES_KDA_O = 4 };
 
 __device__ __noinline__ void phase_residual(const Params& p, const LayerDesc& L, int mode, const uint16_t* g_next) {
   const int B = p.B, H = p.H;
@@ -924,6 +1496,14 @@ __device__ __noinline__ void phase_residual(const Params& p, const LayerDesc& L,
     if (mode == RES_OPROJ) {
       int m = sb.mat(L.wo, H, p.nq * p.hd, 0);
       sb.begin(p.off_ou, p.nq * p.hd, GK_SINGLE);
+      sb.singles_of(m);
+    } else if (mode == RES_MLA_O) {
+      int m = sb.mat(L.mla_wo, H, p.mla_h * p.vdim, 0);
+      sb.begin(p.off_ou, p.mla_h * p.vdim, GK_SINGLE);
+      sb.singles_of(m);
+    } else if (mode == RES_KDA_O) {
+      int m = sb.mat(L.kda_wo, H, p.kda_h * p.kda_dv, 0);
+      sb.begin(p.off_ou, p.kda_h * p.kda_dv, GK_SINGLE);
       sb.singles_of(m);
     } else if (mode == RES_DENSE_DOWN) {
       int m = sb.mat(L.w_down, H, p.ffn, 0);
@@ -971,7 +1551,7 @@ __device__ __noinline__ void phase_residual(const Params& p, const LayerDesc& L,
     put_hilo(r, p.off_u, H, t, r0 + lr, GSM.gain[lr] * x);
     part[threadIdx.x * MAXB + t] += x * x;
   }
-  store_ssq(p, r, part);
+  store_ssq(p, r, part, p.off_ssq);
 }
 
 // --- dense SwiGLU gate/up: h = silu(inv*Wg U) * (inv*Wu U) -> hi/lo
@@ -986,7 +1566,7 @@ __device__ __noinline__ void phase_gateup(const Params& p, const LayerDesc& L) {
     sb.pairs_of(mg, mu);
   }
   builder_done(p, sb, -1);
-  load_inv_rms(p, GSM.inv, p.H);
+  load_inv_rms(p, GSM.inv, p.H, p.off_ssq);
   sub_stamp(p, 0);
   run_gemv(p.ws, p.ws_bytes, p.off_zero, B, EPI_SWIGLU);
   sub_stamp(p, 2);
@@ -1028,7 +1608,7 @@ __device__ __noinline__ void phase_moe_a(const Params& p, const LayerDesc& L) {
     sb.singles_of(mr);
   }
   builder_done(p, sb, -1);
-  load_inv_rms(p, GSM.inv, p.H);
+  load_inv_rms(p, GSM.inv, p.H, p.off_ssq);
   sub_stamp(p, 0);
   run_gemv(p.ws, p.ws_bytes, p.off_zero, B, [=](int g) {
     if (GSM.grp[g].kind == GK_PAIR) {
@@ -1125,7 +1705,7 @@ __device__ __noinline__ void phase_moe_b(const Params& p, const LayerDesc& L) {
     }
   }
   builder_done(p, sb, -1);
-  load_inv_rms(p, GSM.inv, p.H);
+  load_inv_rms(p, GSM.inv, p.H, p.off_ssq);
   sub_stamp(p, 0);
   run_gemv(p.ws, p.ws_bytes, p.off_zero, B, EPI_SWIGLU);
   sub_stamp(p, 2);
@@ -1151,7 +1731,7 @@ __device__ __noinline__ void phase_lmhead(const Params& p) {
     sb.singles_of(m);
   }
   builder_done(p, sb, -1);
-  load_inv_rms(p, GSM.inv, p.H);
+  load_inv_rms(p, GSM.inv, p.H, p.off_ssq);
   sub_stamp(p, 0);
   run_gemv(p.ws, p.ws_bytes, p.off_zero, B, EPI_SCALED_SINGLE);
   sub_stamp(p, 2);
@@ -1221,12 +1801,35 @@ extern "C" __global__ __launch_bounds__(NT) void md_megakernel(Params p) {
   for (int l = 0; l < p.n_layers; ++l) {
     const LayerDesc& L = p.layers[l];
     const uint16_t* g_next = (l + 1 < p.n_layers) ? p.layers[l + 1].attn_norm : p.final_norm;
-    phase_qkv(p, L);
-    grid_sync(p, sidx);
-    phase_attn_gqa(p, L, l);
-    grid_sync(p, sidx);
-    phase_residual(p, L, RES_OPROJ, L.ffn_norm);
-    grid_sync(p, sidx);
+    const int kind = L.kind;
+    if (kind == LK_GQA) {
+      phase_qkv(p, L);
+      grid_sync(p, sidx);
+      phase_attn_gqa(p, L, l);
+      grid_sync(p, sidx);
+      phase_residual(p, L, RES_OPROJ, L.ffn_norm);
+      grid_sync(p, sidx);
+    } else if (kind == LK_KDA) {
+      phase_kda_proj(p, L);
+      grid_sync(p, sidx);
+      phase_kda_rec(p, L);
+      grid_sync(p, sidx);
+      phase_residual(p, L, RES_KDA_O, L.ffn_norm);
+      grid_sync(p, sidx);
+    } else {
+      phase_mla_a(p, L);
+      grid_sync(p, sidx);
+      phase_mla_b(p, L);
+      grid_sync(p, sidx);
+      phase_mla_absorb(p, L);
+      grid_sync(p, sidx);
+      phase_mla_attn(p, L);
+      grid_sync(p, sidx);
+      phase_mla_out(p, L);
+      grid_sync(p, sidx);
+      phase_residual(p, L, RES_MLA_O, L.ffn_norm);
+      grid_sync(p, sidx);
+    }
     if (p.n_experts == 0) {
       phase_gateup(p, L);
       grid_sync(p, sidx);

@@ -41,6 +41,8 @@ struct Params {
   int nq, nkv, hd;
   int ffn;
   int n_experts, top_k, expert_ffn, n_shared, shared_ffn, norm_topk;
+  int mla_h, q_lora, nope, vdim, mla_chunks;   // MLA (kv_lora 512, rope 64)
+  int kda_h, kda_dk, kda_dv, kda_l2;           // gated delta rule
   // step
   int B;
   int attn_chunks;
@@ -65,6 +67,14 @@ struct Params {
   uint32_t off_hs;    // hi/lo bf16[2][MAXB][shared_ffn]   shared expert hidden
   uint32_t off_hr;    // hi/lo bf16[nu][2][MAXB][expert_ffn] routed hidden (x routing weight), U order
   uint32_t hr_stride; // bytes per routed expert slot
+  uint32_t off_uq;    // hi/lo bf16[2][MAXB][q_lora]        g_q * c_q0 (MLA)
+  uint32_t off_ssq2;  // fp32[G][MAXB]                      partial sums of squares of c_q0
+  uint32_t off_ckv;   // fp32[MAXB][576]                    raw latent + key rope part
+  uint32_t off_qm;    // fp32[MAXB][nh][nope + 64]          q (MLA)
+  uint32_t off_qabs;  // fp32[MAXB][nh][576]                absorbed, rotated, scaled q
+  uint32_t off_mz;    // fp32[MAXB][C][nh][512]             attention partial z
+  uint32_t off_mml;   // fp32[MAXB][C][nh][2]               attention partial (max, sum)
+  uint32_t off_kda;   // fp32[MAXB][2 nh dk + nh dv + 2 nh] delta-rule projections
   uint32_t off_cand;  // argmax candidates {f32, i32}[G][MAXB]
   uint32_t off_zero;  // 1 KB that stays zero (target of masked loads)
   const float* rope;  // (cos, sin) fp32[max_ctx][rope_d/2][2]

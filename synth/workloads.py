@@ -268,9 +268,9 @@ def mini_moe() -> Workload:
 
 def mini_hybrid() -> Workload:
     return Workload(name="mini_hybrid", n_layers=4, hidden=384, vocab=1200,
-                    attn_kind=1, mla_every=4, mla_heads=4, q_lora=96, kv_lora=64,
-                    rope_dim=32, nope_dim=32, v_dim=32,
-                    kda_heads=4, kda_dk=32, kda_dv=32, kda_qk_l2norm=1,
+                    attn_kind=1, mla_every=4, mla_heads=4, q_lora=128, kv_lora=512,
+                    rope_dim=64, nope_dim=64, v_dim=64,
+                    kda_heads=3, kda_dk=64, kda_dv=64, kda_qk_l2norm=1,
                     n_experts=8, top_k=4, expert_ffn=160, n_shared=1, shared_ffn=192,
                     gain_sigma=0.1, batches=(1, 8), context=29, max_ctx=48, max_batch=8,
                     steps=2, seed_base=12)

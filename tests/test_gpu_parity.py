@@ -54,7 +54,8 @@ def test_device_draws_match_host_draws(torch_cuda):
 
 @pytest.mark.parametrize("name,B", [("tiny_dense", 1), ("mini_dense", 1), ("mini_dense", 3), ("mini_dense", 8),
                                     ("mini_moe", 1), ("mini_moe", 3), ("mini_moe", 8),
-                                    ("small_moe", 1), ("small_moe", 8)])
+                                    ("small_moe", 1), ("small_moe", 8),
+                                    ("mini_hybrid", 1), ("mini_hybrid", 3), ("mini_hybrid", 8)])
 def test_decode_step_matches_oracle(torch_cuda, name, B):
     w = WL.get(name)
     m = _model(w)

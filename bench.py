@@ -29,22 +29,39 @@ PEAK_GBS = 8000.0
 METRIC = "decode tok/s + step latency at batch 1/8; achieved HBM GB/s vs 8 TB/s peak"
 
 
-def algorithmic_bytes(w, B, positions_per_seq):
-    """Bytes a decode step must read: every weight the step touches (all
-    layer matrices, norm gains, LM head, B embedding rows) plus every cached
-    K/V row attended (positions 0..pos inclusive)."""
+def algorithmic_bytes(w, B, positions_per_seq, expert_ids=None):
+    """Bytes a decode step must read: every weight the step touches (layer
+    matrices and norm gains -- of a MoE layer the router, the shared expert
+    and the experts some token chose, taken from the step's reported expert
+    ids -- the LM head, B embedding rows) plus every cached K/V or latent row
+    attended (positions 0..pos inclusive) and every delta-rule state read."""
+    import re
     from synth.workloads import tensor_inventory
     wb = 0
+    expert = re.compile(r"^L(\d+)\.e(\d+)_")
     for t in tensor_inventory(w):
         if t.name == "embed":
             wb += B * t.cols * 2
-        else:
-            wb += t.numel * 2
+            continue
+        mt = expert.match(t.name)
+        if mt:
+            if expert_ids is None:
+                raise ValueError("MoE byte count needs the step's expert ids")
+            l, e = int(mt.group(1)), int(mt.group(2))
+            if np.any(expert_ids[l, :B] == e):
+                wb += t.numel * 2
+            continue
+        wb += t.numel * 2
     kvb = 0
     for l in range(w.n_layers):
-        if w.layer_kind(l) == "gqa":
-            for p in positions_per_seq:
+        kind = w.layer_kind(l)
+        for p in positions_per_seq:
+            if kind == "gqa":
                 kvb += 2 * w.n_kv_heads * w.head_dim * (int(p) + 1) * 2
+            elif kind == "mla":
+                kvb += (w.kv_lora + w.rope_dim) * (int(p) + 1) * 2
+            else:
+                kvb += w.kda_heads * w.kda_dk * w.kda_dv * 4
     return wb, kvb
 
 
@@ -59,9 +76,12 @@ def time_steps(m, B, steps, warmup, multilaunch=False):
     base = w.context
     pos = torch.tensor([[base + s] * B for s in range(steps + warmup)], dtype=torch.int32, device=dev)
     logits = torch.empty((B, w.vocab), dtype=torch.float32, device=dev)
+    ids = None
+    if w.is_moe:
+        ids = torch.full((steps + warmup, w.n_layers, B, w.top_k), -1, dtype=torch.int32, device=dev)
     # warmup (positions base .. base+warmup-1), then the timed chain restarts at base
     for s in range(warmup):
-        m.decode(toks[s], pos[s], logits, toks[s + 1], multilaunch=multilaunch)
+        m.decode(toks[s], pos[s], logits, toks[s + 1], ids[s] if ids is not None else None, multilaunch=multilaunch)
     torch.cuda.synchronize(dev)
     m.device_status()
     toks[0] = toks[warmup]
@@ -69,13 +89,13 @@ def time_steps(m, B, steps, warmup, multilaunch=False):
     torch.cuda.synchronize(dev)
     ev[0].record(stream)
     for s in range(steps):
-        m.decode(toks[s], pos[s], logits, toks[s + 1], multilaunch=multilaunch)
+        m.decode(toks[s], pos[s], logits, toks[s + 1], ids[s] if ids is not None else None, multilaunch=multilaunch)
         ev[s + 1].record(stream)
     torch.cuda.synchronize(dev)
     m.device_status()
     per = np.array([ev[s].elapsed_time(ev[s + 1]) for s in range(steps)], dtype=np.float64)
     total = ev[0].elapsed_time(ev[steps])
-    return per, total, pos[:steps].cpu().numpy()
+    return per, total, pos[:steps].cpu().numpy(), (ids[:steps].cpu().numpy() if ids is not None else None)
 
 
 def cpu_baseline(w, layers=8, B=1):
@@ -143,10 +163,10 @@ def main():
           flush=True)
     res = {}
     for B in batches:
-        per, total, pos = time_steps(m, B, steps, args.warmup)
+        per, total, pos, ids = time_steps(m, B, steps, args.warmup)
         wb, kvb = [], []
         for s in range(steps):
-            a, b = algorithmic_bytes(w, B, pos[s])
+            a, b = algorithmic_bytes(w, B, pos[s], ids[s] if ids is not None else None)
             wb.append(a)
             kvb.append(b)
         mean_ms = float(per.mean())
@@ -162,13 +182,13 @@ def main():
     if not args.no_multilaunch:
         for B in batches:
             try:
-                per, total, pos = time_steps(m, B, min(steps, 16), 1, multilaunch=True)
+                per, total, pos, _ = time_steps(m, B, min(steps, 16), 1, multilaunch=True)
                 ml[B] = {"ms_per_step": total / min(steps, 16), "tok_s": B * min(steps, 16) / (total * 1e-3)}
             except Exception as e:  # not built for this configuration
                 ml[B] = {"error": str(e)[:120]}
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(w)
+        cpu = cpu_baseline(w, layers=w.mla_every if w.attn_kind == 1 else 8)
         print(f"# cpu oracle: {cpu['value']:.4f} tok/s on {cpu['cores']} threads", file=sys.stderr, flush=True)
     B0 = batches[0]
     r0 = res[B0]

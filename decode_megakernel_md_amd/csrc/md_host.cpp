@@ -155,15 +155,15 @@ md_status validate(const md_config* c) {
     if (c->n_shared == 1 && !width_ok(c->shared_ffn))
       return fail(MD_EUNSUPPORTED, "shared_ffn must be a multiple of 32, at least 128");
     if (c->norm_topk != 0 && c->norm_topk != 1) return fail(MD_EINVAL, "norm_topk must be 0 or 1");
-    int nu = c->n_experts < c->max_batch * c->top_k ? c->n_experts : c->max_batch * c->top_k;
-    if (2 * nu > 72) return fail(MD_EUNSUPPORTED, "too many distinct experts per step (2 * min(n_experts, max_batch * top_k) > 72)");
+    int nu = c->n_experts < MAXB_ * c->top_k ? c->n_experts : MAXB_ * c->top_k;
+    if (2 * nu > 72) return fail(MD_EUNSUPPORTED, "too many distinct experts per step (2 * min(n_experts, 8 * top_k) > 72)");
   }
   return MD_OK;
 }
 
 struct WsLayout {
   size_t layers, experts, x, u, ssq, qkv, attn, attn_ml, ou, h, rl, hs, hr, hr_stride, uq, ssq2, ckv, qm, qabs, mz, mml,
-      kda, cand, zero, rope, sync, err, total;
+      kda, ring, cand, zero, rope, sync, err, total;
   int rope_d;
   int n_sync, sync_attn_base;
 };
@@ -200,7 +200,7 @@ WsLayout ws_layout(const md_config* c) {
   w.h = take(2 * 2 * MAXB_ * (size_t)F);
   w.rl = take(4 * (size_t)MAXB_ * (c->n_experts > 0 ? c->n_experts : 1));
   w.hs = take(2 * 2 * MAXB_ * (size_t)(c->n_shared > 0 ? c->shared_ffn : 1));
-  int nu = c->n_experts < c->max_batch * c->top_k ? c->n_experts : c->max_batch * c->top_k;
+  int nu = c->n_experts < MAXB_ * c->top_k ? c->n_experts : MAXB_ * c->top_k;
   w.hr_stride = align256(2 * 2 * MAXB_ * (size_t)(c->expert_ffn > 0 ? c->expert_ffn : 1));
   w.hr = take(w.hr_stride * (size_t)(nu > 0 ? nu : 1));
   w.uq = take(2 * 2 * MAXB_ * (size_t)(hyb ? c->q_lora : 1));
@@ -211,6 +211,9 @@ WsLayout ws_layout(const md_config* c) {
   w.mz = take(hyb ? 4 * (size_t)GMAX * mh * 512 : 256);
   w.mml = take(8 * (size_t)GMAX * mh);
   w.kda = take(hyb ? 4 * MAXB_ * (size_t)(2 * c->kda_heads * c->kda_dk + c->kda_heads * c->kda_dv + 2 * c->kda_heads) : 256);
+  int n_kda = 0;
+  for (int l = 0; l < c->n_layers; ++l) n_kda += (hyb && !is_mla(c, l)) ? 1 : 0;
+  w.ring = take((size_t)n_kda * MAXB_ * (hyb ? (size_t)c->kda_heads * c->kda_dk * c->kda_dv * 4 : 0));
   w.cand = take(8 * (size_t)GMAX * MAXB_);
   w.zero = take(1024);
   w.rope_d = c->attn_kind == 0 ? c->head_dim : c->rope_dim;
@@ -353,9 +356,11 @@ md_status md_init_model(const md_config* cfg, const void* const* weights, size_t
   std::vector<const void*> ex;
   size_t wi = 1;  // after embed
   auto W = [&]() { return (const uint16_t*)weights[wi++]; };
+  int kda_count = 0;
   for (int l = 0; l < cfg->n_layers; ++l) {
     LayerDesc& d = L[l];
     memset(&d, 0, sizeof d);
+    d.kda_idx = -1;
     d.kv_off = m->kv_off[l];
     d.attn_norm = W();
     if (cfg->attn_kind == 0) {
@@ -367,6 +372,7 @@ md_status md_init_model(const md_config* cfg, const void* const* weights, size_t
       d.mla_wkvb = W(); d.mla_wo = W();
     } else {
       d.kind = LK_KDA;
+      d.kda_idx = kda_count++;
       d.kda_wq = W(); d.kda_wk = W(); d.kda_wv = W(); d.kda_wa = W(); d.kda_wb = W(); d.kda_wo = W();
     }
     d.ffn_norm = W();
@@ -448,6 +454,9 @@ static md_status fill_params(md_model* m, const int32_t* tokens, const int32_t* 
   }
   p.off_uq = (uint32_t)w.uq; p.off_ssq2 = (uint32_t)w.ssq2; p.off_ckv = (uint32_t)w.ckv; p.off_qm = (uint32_t)w.qm;
   p.off_qabs = (uint32_t)w.qabs; p.off_mz = (uint32_t)w.mz; p.off_mml = (uint32_t)w.mml; p.off_kda = (uint32_t)w.kda;
+  p.n_kda = 0;
+  for (int l = 0; l < c->n_layers; ++l) p.n_kda += (c->attn_kind == 1 && !is_mla(c, l)) ? 1 : 0;
+  p.kda_ring = m->ws + w.ring;
   p.off_rl = (uint32_t)w.rl; p.off_hs = (uint32_t)w.hs; p.off_hr = (uint32_t)w.hr; p.hr_stride = (uint32_t)w.hr_stride; p.off_cand = (uint32_t)w.cand; p.off_zero = (uint32_t)w.zero;
   p.rope = (const float*)(m->ws + w.rope); p.rope_d = w.rope_d;
   p.sync = (unsigned*)(m->ws + w.sync);
@@ -485,9 +494,34 @@ md_status md_decode_step_multilaunch(md_model* m, const int32_t* tokens, const i
 md_status md_verify_step(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv_cache,
                          float* out_logits, int32_t* out_accept_len, int32_t* out_next_token, int32_t batch,
                          int32_t n_tok, void* hip_stream) {
-  (void)m; (void)tokens; (void)positions; (void)kv_cache; (void)out_logits; (void)out_accept_len;
-  (void)out_next_token; (void)batch; (void)n_tok; (void)hip_stream;
-  return fail(MD_EUNSUPPORTED, "verify step is not built yet");
+  if (batch != 1) return fail(MD_EUNSUPPORTED, "verify runs one sequence per launch (batch must be 1)");
+  if (n_tok < 2 || n_tok > MAXB_) return fail(MD_EINVAL, "n_tok %d outside [2, %d]", n_tok, MAXB_);
+  if (!out_accept_len || !out_next_token) return fail(MD_EINVAL, "out_accept_len and out_next_token must be non-NULL");
+  if (((uintptr_t)out_accept_len & 3) || ((uintptr_t)out_next_token & 3)) return fail(MD_EINVAL, "misaligned pointer");
+  Params p;
+  // the n_tok rows of the one sequence travel as the step's token rows
+  md_status st = fill_params(m, tokens, positions, kv_cache, out_logits, 1, nullptr, nullptr, p);
+  if (st != MD_OK) return st;
+  const md_config* c = &m->cfg;
+  p.B = n_tok;
+  p.verify = 1;
+  p.out_accept = out_accept_len;
+  p.out_next = out_next_token;
+  {
+    int pairs = n_tok * (c->n_kv_heads > 0 ? c->n_kv_heads : 1);
+    int C = m->grid / pairs;
+    p.attn_chunks = C < 1 ? 1 : (C > CMAX ? CMAX : C);
+    int cm = m->grid / n_tok;
+    int by_ctx = (c->max_ctx + 127) / 128;
+    if (cm > by_ctx) cm = by_ctx;
+    p.mla_chunks = cm < 1 ? 1 : (cm > CMAX ? CMAX : cm);
+  }
+  p.bank = m->bank;
+  hipError_t e = launch_megakernel(p, m->grid, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(MD_EHIP, "megakernel launch: %s", hipGetErrorString(e));
+  m->bank ^= 1;
+  m->last_stream = (hipStream_t)hip_stream;
+  return MD_OK;
 }
 
 md_status md_get_device_status(md_model* m) {

@@ -118,6 +118,20 @@ __device__ void clear_next_bank(const Params& p) {
   for (size_t i = a + threadIdx.x; i < e; i += NT) nb[i] = 0u;
 }
 
+// Row r of a step: its sequence (cache slot) and position.  Decode: row r is
+// sequence r at positions[r].  Verify: every row belongs to sequence 0 and
+// row r is the token at positions[0] + r.  Out-of-range positions set the
+// device error word and are clamped (the step's outputs are then undefined).
+__device__ __forceinline__ int row_seq(const Params& p, int r) { return p.verify ? 0 : r; }
+__device__ __forceinline__ int row_pos(const Params& p, int r) {
+  int pos = p.verify ? p.positions[0] + r : p.positions[r];
+  if (pos < 0 || pos >= p.max_ctx) {
+    set_err(p, MDE_POSITION);
+    pos = pos < 0 ? 0 : p.max_ctx - 1;
+  }
+  return pos;
+}
+
 // ===================================================================== GEMV
 // Y[r][t] = sum_k W[r][k] * U[t][k] for this workgroup's rows of a list of
 // matrices (up to MAXMAT per phase: q/k/v, the gate and up of every expert a
@@ -600,7 +614,7 @@ struct KVBlock {
   i32x4 v[HD / 16];             // 32 positions x HD bf16 = HD/16 loads of 1 KB per wave
 };
 
-template <int HD>
+template <int HD, int CP>
 __device__ __forceinline__ void load_block(KVBlock<HD>& r, rsrc_t krs, rsrc_t vrs, int blk, int w1, int lane) {
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
@@ -608,7 +622,7 @@ __device__ __forceinline__ void load_block(KVBlock<HD>& r, rsrc_t krs, rsrc_t vr
 #pragma unroll
     for (int s = 0; s < HD / 32; ++s) {
       uint32_t off = (prow < w1 && blk < w1) ? (uint32_t)(prow * HD + s * 32 + (lane >> 4) * 8) * 2u : OOB;
-      r.k[tt][s] = ld_x4<0>(krs, off);
+      r.k[tt][s] = ld_x4<CP>(krs, off);
     }
   }
   // V: lanes split a row into HD/8 chunks of 8 dims; one instruction covers 64/(HD/8) rows
@@ -618,13 +632,13 @@ __device__ __forceinline__ void load_block(KVBlock<HD>& r, rsrc_t krs, rsrc_t vr
   for (int q = 0; q < HD / 16; ++q) {
     int t = blk + q * RPI + lane / LPR;
     uint32_t off = (t < w1 && blk < w1) ? (uint32_t)(t * HD + (lane % LPR) * 8) * 2u : OOB;
-    r.v[q] = ld_x4<0>(vrs, off);
+    r.v[q] = ld_x4<CP>(vrs, off);
   }
 }
 
 #define ASM (*reinterpret_cast<AttnSmem*>(md_smem))
 
-template <int HD, int GS>
+template <int HD, int GS, int CP>
 __device__ __noinline__ void attn_task_wave(const uint16_t* kc, const uint16_t* vc, uint32_t nbytes, int w0, int w1) {
   constexpr int gs = GS;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -711,12 +725,12 @@ __device__ __noinline__ void attn_task_wave(const uint16_t* kc, const uint16_t* 
     __builtin_amdgcn_wave_barrier();
   };
   KVBlock<HD> ba, bb;
-  load_block<HD>(ba, krs, vrs, w0, w1, lane);
+  load_block<HD, CP>(ba, krs, vrs, w0, w1, lane);
   for (int blk = w0; blk < w1; blk += 64) {
-    load_block<HD>(bb, krs, vrs, blk + 32, w1, lane);
+    load_block<HD, CP>(bb, krs, vrs, blk + 32, w1, lane);
     block(ba, blk);
     if (blk + 32 >= w1) break;
-    load_block<HD>(ba, krs, vrs, blk + 64, w1, lane);
+    load_block<HD, CP>(ba, krs, vrs, blk + 64, w1, lane);
     block(bb, blk + 32);
   }
   // sum the lane groups that hold the same dims (different rows)
@@ -738,17 +752,45 @@ __device__ __noinline__ void attn_task_wave(const uint16_t* kc, const uint16_t* 
   }
 }
 
-template <int HD>
+template <int HD, int CP>
 __device__ __forceinline__ void attn_dispatch(int gs, const uint16_t* kc, const uint16_t* vc, uint32_t nb, int w0, int w1) {
   switch (gs) {
-    case 1: attn_task_wave<HD, 1>(kc, vc, nb, w0, w1); break;
-    case 2: attn_task_wave<HD, 2>(kc, vc, nb, w0, w1); break;
-    case 3: attn_task_wave<HD, 3>(kc, vc, nb, w0, w1); break;
-    case 4: attn_task_wave<HD, 4>(kc, vc, nb, w0, w1); break;
-    case 5: attn_task_wave<HD, 5>(kc, vc, nb, w0, w1); break;
-    case 6: attn_task_wave<HD, 6>(kc, vc, nb, w0, w1); break;
-    case 7: attn_task_wave<HD, 7>(kc, vc, nb, w0, w1); break;
-    default: attn_task_wave<HD, 8>(kc, vc, nb, w0, w1); break;
+    case 1: attn_task_wave<HD, 1, CP>(kc, vc, nb, w0, w1); break;
+    case 2: attn_task_wave<HD, 2, CP>(kc, vc, nb, w0, w1); break;
+    case 3: attn_task_wave<HD, 3, CP>(kc, vc, nb, w0, w1); break;
+    case 4: attn_task_wave<HD, 4, CP>(kc, vc, nb, w0, w1); break;
+    case 5: attn_task_wave<HD, 5, CP>(kc, vc, nb, w0, w1); break;
+    case 6: attn_task_wave<HD, 6, CP>(kc, vc, nb, w0, w1); break;
+    case 7: attn_task_wave<HD, 7, CP>(kc, vc, nb, w0, w1); break;
+    default: attn_task_wave<HD, 8, CP>(kc, vc, nb, w0, w1); break;
+  }
+}
+
+// Verify: the new K/V rows of all rows (positions p..p+B-1 of sequence 0)
+// go to the cache before attention, device-coherently, because row r
+// attends the rows of the tokens before it, computed by other workgroups.
+__device__ __noinline__ void phase_gqa_kv_write(const Params& p, const LayerDesc& L) {
+  const int hd = p.hd, nqkv = (p.nq + 2 * p.nkv) * hd;
+  rsrc_t wr = make_rsrc_u(p.ws, p.ws_bytes);
+  for (int task = blockIdx.x; task < p.B * p.nkv; task += gridDim.x) {
+    const int g = task % p.nkv, b = task / p.nkv;
+    const int pos = row_pos(p, b);
+    uint16_t* kc = (uint16_t*)(p.kv + L.kv_off) + (size_t)(row_seq(p, b) * p.nkv + g) * p.max_ctx * hd;
+    uint16_t* vc = kc + (size_t)p.max_batch * p.nkv * p.max_ctx * hd;
+    rsrc_t krs = make_rsrc_u(kc + (size_t)pos * hd, hd * 2), vrs = make_rsrc_u(vc + (size_t)pos * hd, hd * 2);
+    for (int i = threadIdx.x; i < hd / 2; i += NT) {
+      int colk = p.nq * hd + g * hd;
+      float a = ld_f32(wr, p.off_qkv + (uint32_t)(b * nqkv + colk + i) * 4u);
+      float bb = ld_f32(wr, p.off_qkv + (uint32_t)(b * nqkv + colk + i + hd / 2) * 4u);
+      float cs, sn;
+      rope_cs(p, pos, i, cs, sn);
+      st_u16(krs, (uint32_t)i * 2u, bf16_rne(a * cs - bb * sn));
+      st_u16(krs, (uint32_t)(i + hd / 2) * 2u, bf16_rne(a * sn + bb * cs));
+    }
+    for (int i = threadIdx.x; i < hd; i += NT) {
+      int colv = (p.nq + p.nkv) * hd + g * hd;
+      st_u16(vrs, (uint32_t)i * 2u, bf16_rne(ld_f32(wr, p.off_qkv + (uint32_t)(b * nqkv + colv + i) * 4u)));
+    }
   }
 }
 
@@ -763,15 +805,11 @@ __device__ __noinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L,
   const float scale = 1.0f / sqrtf((float)hd);
   for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
     const int c = task % C, g = (task / C) % p.nkv, b = task / (C * p.nkv);
-    int pos = p.positions[b];
-    if (pos < 0 || pos >= p.max_ctx) {
-      set_err(p, MDE_POSITION);
-      pos = pos < 0 ? 0 : p.max_ctx - 1;
-    }
+    const int pos = row_pos(p, b);
     const int n = pos + 1;
     const int P = (n + C - 1) / C;
     const int a0 = c * P < n ? c * P : n, a1 = (c + 1) * P < n ? (c + 1) * P : n;
-    uint16_t* kc = (uint16_t*)(p.kv + L.kv_off) + (size_t)(b * p.nkv + g) * p.max_ctx * hd;
+    uint16_t* kc = (uint16_t*)(p.kv + L.kv_off) + (size_t)(row_seq(p, b) * p.nkv + g) * p.max_ctx * hd;
     uint16_t* vc = kc + (size_t)p.max_batch * p.nkv * p.max_ctx * hd;
     for (int e = threadIdx.x; e < gs * (hd / 2); e += NT) {
       int h = e / (hd / 2), i = e % (hd / 2);
@@ -783,7 +821,7 @@ __device__ __noinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L,
       sm.q[h][i] = (a * cs - bb * sn) * scale;
       sm.q[h][i + hd / 2] = (a * sn + bb * cs) * scale;
     }
-    if (a0 <= pos && pos < a1) {
+    if (!p.verify && a0 <= pos && pos < a1) {  // (verify: rows written by phase_gqa_kv_write)
       for (int i = threadIdx.x; i < hd / 2; i += NT) {
         int colk = p.nq * hd + g * hd;
         float a = ld_f32(wr, p.off_qkv + (uint32_t)(b * nqkv + colk + i) * 4u);
@@ -806,8 +844,13 @@ __device__ __noinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L,
     const int w0 = a0 + wv * wq < a1 ? a0 + wv * wq : a1;
     const int w1 = w0 + wq < a1 ? w0 + wq : a1;
     const uint32_t nb = (uint32_t)((size_t)n * hd * 2);
-    if (hd == 128) attn_dispatch<128>(gs, kc, vc, nb, w0, w1);
-    else attn_dispatch<64>(gs, kc, vc, nb, w0, w1);
+    if (p.verify) {
+      if (hd == 128) attn_dispatch<128, CP_SC1>(gs, kc, vc, nb, w0, w1);
+      else attn_dispatch<64, CP_SC1>(gs, kc, vc, nb, w0, w1);
+    } else {
+      if (hd == 128) attn_dispatch<128, 0>(gs, kc, vc, nb, w0, w1);
+      else attn_dispatch<64, 0>(gs, kc, vc, nb, w0, w1);
+    }
     __syncthreads();
     sub_stamp(p, 3);
     // this task's partial: m, l in part_ml[b][head][c]; o in part_o[b][head][c][hd]
@@ -1014,6 +1057,153 @@ __device__ __noinline__ void phase_kda_rec(const Params& p, const LayerDesc& L) 
   }
 }
 
+// ------------------------------------------------------------------ verify
+// Section "DSpark" of the pages: one launch scores an anchor and its proposed
+// continuations.  The rows are the tokens t_0..t_{B-1} of sequence 0 at
+// positions p..p+B-1, each attending the cache up to its own position.  The
+// delta-rule state advances token by token: task (h, 32-column slice) runs
+// the B updates in registers, emits o for every row, and stores the state
+// after every row in the snapshot ring; the state itself is rewritten only
+// once the accepted length is known (verify_finish).
+__device__ __noinline__ void phase_kda_rec_verify(const Params& p, const LayerDesc& L) {
+  KdaSmem& sm = *(KdaSmem*)md_smem;
+  const int B = p.B, nh = p.kda_h, dk = p.kda_dk, dv = p.kda_dv;
+  const int width = 2 * nh * dk + nh * dv + 2 * nh;
+  const int ns = dv / 32;
+  const int ntask = nh * ns;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int rg = threadIdx.x >> 5, jj = threadIdx.x & 31;
+  const size_t sbytes = (size_t)nh * dk * dv * 4;
+  rsrc_t wr = make_rsrc_u(p.ws, p.ws_bytes);
+  for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
+    const int js = task % ns, h = task / ns;
+    const float* S = (const float*)(p.kv + L.kv_off) + (size_t)h * dk * dv;  // sequence 0
+    rsrc_t srs = make_rsrc_u(S, (uint32_t)(dk * dv * 4));
+    float s[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      int i = rg + 8 * r;
+      s[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          srs, i < dk ? (uint32_t)(i * dv + 32 * js + jj) * 4u : OOB, 0, 0));
+    }
+    for (int j = 0; j < B; ++j) {
+      const uint32_t base = p.off_kda + (uint32_t)(j * width) * 4u;
+      if (threadIdx.x < dk) {
+        sm.q[threadIdx.x] = ld_f32(wr, base + (uint32_t)(h * dk + threadIdx.x) * 4u);
+        sm.k[threadIdx.x] = ld_f32(wr, base + (uint32_t)(nh * dk + h * dk + threadIdx.x) * 4u);
+      }
+      if (threadIdx.x < 32) sm.v[threadIdx.x] = ld_f32(wr, base + (uint32_t)(2 * nh * dk + h * dv + 32 * js + threadIdx.x) * 4u);
+      if (threadIdx.x == 0) {
+        sm.a = sigmoid(ld_f32(wr, base + (uint32_t)(2 * nh * dk + nh * dv + h) * 4u));
+        sm.b = sigmoid(ld_f32(wr, base + (uint32_t)(2 * nh * dk + nh * dv + nh + h) * 4u));
+      }
+      __syncthreads();
+      if (wv < 2) {
+        const float* vec = wv == 0 ? sm.q : sm.k;
+        float a0 = lane < dk ? vec[lane] : 0.f, a1 = lane + 64 < dk ? vec[lane + 64] : 0.f;
+        float n2 = wave_sum(a0 * a0 + a1 * a1);
+        float sc = p.kda_l2 ? 1.0f / fmaxf(sqrtf(n2), 1e-6f) : 1.0f;
+        if (lane == 0) { if (wv == 0) sm.qs = sc; else sm.ks = sc; }
+      }
+      __syncthreads();
+      const float qs = sm.qs, ks = sm.ks;
+      float up = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        int i = rg + 8 * r;
+        if (i < dk) up += s[r] * (sm.k[i] * ks);
+      }
+      sm.red[rg][jj] = up;
+      __syncthreads();
+      float u = 0.f;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) u += sm.red[g][jj];
+      const float delta = sm.b * (sm.v[jj] - u), al = sm.a;
+      rsrc_t snap = make_rsrc_u(p.kda_ring + ((size_t)L.kda_idx * MAXB + j) * sbytes + (size_t)h * dk * dv * 4,
+                                (uint32_t)(dk * dv * 4));
+      float op = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        int i = rg + 8 * r;
+        float kn = sm.k[i < dk ? i : 0] * ks;
+        s[r] = al * s[r] + kn * delta;
+        if (i < dk) op += s[r] * (sm.q[i] * qs);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s[r]), snap,
+                                              i < dk ? (uint32_t)(i * dv + 32 * js + jj) * 4u : OOB, 0, CP_SC1);
+      }
+      sm.red2[rg][jj] = op;
+      __syncthreads();
+      if (threadIdx.x < 32) {
+        float o = 0.f;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) o += sm.red2[g][threadIdx.x];
+        put_hilo(wr, p.off_ou, nh * dv, j, h * dv + 32 * js + threadIdx.x, o);
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// After the LM head: every workgroup takes the argmax of every row from the
+// candidates (the same fixed order as the decode path), derives the accepted
+// length a = 1 + m (m: the largest j with t_i == argmax(row i-1) for all
+// 1 <= i <= j), and copies its share of each delta-rule layer's snapshot m
+// into the state.  Workgroup 0 reports a and argmax(row a-1).
+constexpr int MAX_KDA_LAYERS = 512;
+__device__ __noinline__ void verify_finish(const Params& p) {
+  int* arg = (int*)md_smem;                 // [MAXB]
+  int* acc = arg + MAXB;                    // [1]
+  uint64_t* koff = (uint64_t*)(md_smem + 64);  // [MAX_KDA_LAYERS] state offsets of the delta-rule layers
+  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int t = wv; t < p.B; t += NW) {
+    float best = -INFINITY;
+    int idx = 0x7FFFFFFF;
+    for (int g = lane; g < (int)gridDim.x; g += 64) {
+      float v = ld_f32(r, p.off_cand + (uint32_t)(g * MAXB + t) * 8u);
+      int k = (int)ld_u32(r, p.off_cand + (uint32_t)(g * MAXB + t) * 8u + 4u);
+      if (v > best || (v == best && k < idx)) { best = v; idx = k; }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      float ov = __shfl_xor(best, o, 64);
+      int oi = __shfl_xor(idx, o, 64);
+      if (ov > best || (ov == best && oi < idx)) { best = ov; idx = oi; }
+    }
+    if (lane == 0) arg[t] = idx;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int m = 0;
+    for (int j = 1; j < p.B; ++j) {
+      if (p.tokens[j] == arg[j - 1]) m = j;
+      else break;
+    }
+    acc[0] = m + 1;
+    if (blockIdx.x == 0) {
+      p.out_accept[0] = m + 1;
+      p.out_next[0] = arg[m];
+    }
+  }
+  for (int l = threadIdx.x; l < p.n_layers; l += NT) {
+    const LayerDesc& d = p.layers[l];
+    if (d.kind == LK_KDA && d.kda_idx < MAX_KDA_LAYERS) koff[d.kda_idx] = d.kv_off;
+  }
+  __syncthreads();
+  const int m = acc[0] - 1, n = p.n_kda < MAX_KDA_LAYERS ? p.n_kda : MAX_KDA_LAYERS;
+  const size_t sbytes = (size_t)p.kda_h * p.kda_dk * p.kda_dv * 4;
+  const uint32_t units = (uint32_t)(sbytes / 16);
+  const RowSplit my = rows_of((int)units, blockIdx.x, gridDim.x);
+  for (int k = 0; k < n; ++k) {
+    rsrc_t src = make_rsrc_u(p.kda_ring + ((size_t)k * MAXB + m) * sbytes, (uint32_t)sbytes);
+    rsrc_t dst = make_rsrc_u(p.kv + koff[k], (uint32_t)sbytes);
+    for (int u = my.r0 + threadIdx.x; u < my.r1; u += NT) {
+      i32x4 v = ld_x4<CP_SC1>(src, (uint32_t)u * 16u);
+      __builtin_amdgcn_raw_buffer_store_b128(v, dst, (uint32_t)u * 16u, 0, 0);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ MLA
 // Multi-head latent attention (the other layer kind of the hybrid model), in
 // the absorbed form: the cache holds per position the RMS-normalised latent
@@ -1065,11 +1255,7 @@ __device__ __noinline__ void phase_mla_a(const Params& p, const LayerDesc& L) {
 __device__ void mla_cache_row(const Params& p, const LayerDesc& L, int b) {
   float* c = &GSM.in[0][0];  // [576] (the staging area is free before the stream)
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-  int pos = p.positions[b];
-  if (pos < 0 || pos >= p.max_ctx) {
-    set_err(p, MDE_POSITION);
-    pos = pos < 0 ? 0 : p.max_ctx - 1;
-  }
+  const int pos = row_pos(p, b);
   for (int i = threadIdx.x; i < MLA_QA; i += NT) c[i] = ld_f32(r, p.off_ckv + (uint32_t)(b * MLA_QA + i) * 4u);
   __syncthreads();
   float* red = &GSM.in[80][0];  // [NW]
@@ -1081,7 +1267,7 @@ __device__ void mla_cache_row(const Params& p, const LayerDesc& L, int b) {
   __syncthreads();
   float tot = red[0] + red[1] + red[2] + red[3];
   float inv = 1.0f / sqrtf(tot / (float)MLA_KL + p.eps);
-  uint16_t* row = (uint16_t*)(p.kv + L.kv_off) + ((size_t)b * p.max_ctx + pos) * MLA_QA;
+  uint16_t* row = (uint16_t*)(p.kv + L.kv_off) + ((size_t)row_seq(p, b) * p.max_ctx + pos) * MLA_QA;
   rsrc_t cr = make_rsrc_u(row, MLA_QA * 2);
   for (int i = threadIdx.x; i < MLA_KL; i += NT) st_u16(cr, (uint32_t)i * 2u, bf16_rne(bf16_f32(L.mla_kvnorm[i]) * (c[i] * inv)));
   for (int i = threadIdx.x; i < MLA_RD / 2; i += NT) {
@@ -1185,8 +1371,7 @@ __device__ __noinline__ void phase_mla_absorb(const Params& p, const LayerDesc& 
     if (cbk == 0) {
       for (int e = threadIdx.x; e < B * (MLA_RD / 2); e += NT) {
         int t = e / (MLA_RD / 2), i = e % (MLA_RD / 2);
-        int pos = p.positions[t];
-        pos = pos < 0 ? 0 : (pos >= p.max_ctx ? p.max_ctx - 1 : pos);
+        const int pos = row_pos(p, t);
         float a = ld_f32(r, p.off_qm + (uint32_t)(t * nh * QW + h * QW + nope + i) * 4u);
         float bb = ld_f32(r, p.off_qm + (uint32_t)(t * nh * QW + h * QW + nope + i + MLA_RD / 2) * 4u);
         float cs, sn;
@@ -1241,12 +1426,11 @@ __device__ __noinline__ void phase_mla_attn(const Params& p, const LayerDesc& L)
   rsrc_t wr = make_rsrc_u(p.ws, p.ws_bytes);
   for (int task = blockIdx.x; task < B * C; task += gridDim.x) {
     const int c = task % C, b = task / C;
-    int pos = p.positions[b];
-    pos = pos < 0 ? 0 : (pos >= p.max_ctx ? p.max_ctx - 1 : pos);
+    const int pos = row_pos(p, b);
     const int n = pos + 1;
     const int P = (n + C - 1) / C;
     const int a0 = c * P < n ? c * P : n, a1 = (c + 1) * P < n ? (c + 1) * P : n;
-    const uint16_t* cache = (const uint16_t*)(p.kv + L.kv_off) + (size_t)b * p.max_ctx * MLA_QA;
+    const uint16_t* cache = (const uint16_t*)(p.kv + L.kv_off) + (size_t)row_seq(p, b) * p.max_ctx * MLA_QA;
     rsrc_t crs = make_rsrc_u(cache, (uint32_t)((size_t)n * MLA_QA * 2));
     // this wave's heads' absorbed queries as hi/lo B operands
     bf16x8 qb[MLA_KS];
@@ -1805,6 +1989,10 @@ extern "C" __global__ __launch_bounds__(NT) void md_megakernel(Params p) {
     if (kind == LK_GQA) {
       phase_qkv(p, L);
       grid_sync(p, sidx);
+      if (p.verify) {
+        phase_gqa_kv_write(p, L);
+        grid_sync(p, sidx);
+      }
       phase_attn_gqa(p, L, l);
       grid_sync(p, sidx);
       phase_residual(p, L, RES_OPROJ, L.ffn_norm);
@@ -1812,7 +2000,8 @@ extern "C" __global__ __launch_bounds__(NT) void md_megakernel(Params p) {
     } else if (kind == LK_KDA) {
       phase_kda_proj(p, L);
       grid_sync(p, sidx);
-      phase_kda_rec(p, L);
+      if (p.verify) phase_kda_rec_verify(p, L);
+      else phase_kda_rec(p, L);
       grid_sync(p, sidx);
       phase_residual(p, L, RES_KDA_O, L.ffn_norm);
       grid_sync(p, sidx);
@@ -1847,6 +2036,11 @@ extern "C" __global__ __launch_bounds__(NT) void md_megakernel(Params p) {
     if (dev_failed(p)) return;
   }
   phase_lmhead(p);
+  if (p.verify) {
+    grid_sync(p, sidx);
+    verify_finish(p);
+    return;
+  }
   // the last workgroup to arrive reduces the argmax candidates
   bool last = arrive(p, sidx);
   if (threadIdx.x == 0) ((int*)md_smem)[0] = last;

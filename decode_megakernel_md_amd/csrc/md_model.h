@@ -13,7 +13,7 @@ enum LayerKind : int { LK_GQA = 0, LK_MLA = 1, LK_KDA = 2 };
 // caller's bf16 weight tensors; unused ones are null.
 struct LayerDesc {
   int kind;
-  int pad_;
+  int kda_idx;      // index among the delta-rule layers (verify snapshots), else -1
   uint64_t kv_off;  // byte offset of this layer's region in the KV / state buffer
   const uint16_t* attn_norm;
   // GQA
@@ -43,8 +43,13 @@ struct Params {
   int n_experts, top_k, expert_ffn, n_shared, shared_ffn, norm_topk;
   int mla_h, q_lora, nope, vdim, mla_chunks;   // MLA (kv_lora 512, rope 64)
   int kda_h, kda_dk, kda_dv, kda_l2;           // gated delta rule
+  int n_kda;                                   // number of delta-rule layers
   // step
-  int B;
+  int B;              // token rows: sequences (decode) or the verified tokens of one sequence
+  int verify;         // 1: rows are tokens p..p+B-1 of sequence 0
+  uint8_t* kda_ring;  // verify: per delta-rule layer, the state after each row fp32[L_kda][MAXB][nh][dk][dv]
+  int32_t* out_accept;
+  int32_t* out_next;
   int attn_chunks;
   const int32_t* tokens;
   const int32_t* positions;

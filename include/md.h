@@ -149,16 +149,20 @@ md_status md_decode_step_multilaunch(md_model* m, const int32_t* tokens, const i
                                      float* out_logits, int32_t batch, int32_t* out_tokens,
                                      int32_t* out_expert_ids, void* hip_stream);
 
-/* Speculative verify of n_tok (2..8) tokens per sequence (section "DSpark":
- * an anchor plus proposed continuations in one launch).
- *   tokens     dev int32[batch][n_tok]  t_0 (anchor) .. t_{n-1} (drafts)
- *   positions  dev int32[batch]         position of the anchor; rows p..p+n-1 are written
- *   out_logits dev fp32[batch][n_tok][vocab]: row j is the next-token distribution after t_j
+/* Speculative verify of n_tok (2..8) tokens of one sequence in one launch
+ * (section "DSpark": an anchor plus proposed continuations per launch).  The
+ * sequence uses cache / state slot 0.
+ *   tokens     dev int32[batch][n_tok]  t_0 (anchor) .. t_{n-1} (drafts), each in [0, vocab)
+ *   positions  dev int32[batch]         position p of the anchor; cache rows p..p+n-1 are
+ *                                       written, so p + n_tok <= max_ctx is required
+ *   out_logits dev fp32[batch][n_tok][vocab]: row j is the next-token distribution after t_j,
+ *              i.e. what n_tok successive decode steps would produce
  *   out_accept_len dev int32[batch]: a = 1 + m, m the largest j with t_i == argmax(row i-1)
- *              for all 1 <= i <= j
+ *              for all 1 <= i <= j (lowest index on argmax ties)
  *   out_next_token dev int32[batch]: argmax of row a-1
- * Delta-rule states are committed as they stand after token a-1.  batch must
- * be 1 and the model must satisfy max_batch >= n_tok. */
+ * Delta-rule states are committed as they stand after token a-1 (the
+ * per-token states pass through the workspace).  batch must be 1.  Out-of-
+ * range tokens or positions are reported by md_get_device_status. */
 md_status md_verify_step(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv_cache,
                          float* out_logits, int32_t* out_accept_len, int32_t* out_next_token, int32_t batch,
                          int32_t n_tok, void* hip_stream);

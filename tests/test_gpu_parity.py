@@ -110,3 +110,61 @@ def test_repeated_steps_are_bitwise_deterministic(torch_cuda):
     m.reset_kv()
     b = GU.run_gpu_step(m, toks, pos)
     assert np.array_equal(a["logits"], b["logits"])
+
+
+def _greedy_drafts(w, W, kv, p0, accept, n=8):
+    """Tokens t_0..t_{n-1}: the anchor, then the oracle's greedy continuation
+    for accept-1 tokens, then (when accept < n) a token that differs from the
+    greedy one at that point, then arbitrary tokens.  Verifying them must
+    accept exactly `accept` tokens."""
+    from oracle import step as ostep
+    from tests.harness import kv_copy
+    anchor = int(synth.tokens(w, 1)[0])
+    seq = [anchor]
+    kv_g = kv_copy(kv)
+    for j in range(min(accept, n - 1)):
+        o = ostep.decode_step(w, W, [seq[-1]], [p0 + j], kv_g)
+        seq.append(int(o["next"][0]))
+    if accept < n:
+        seq[accept] = (seq[accept] + 1) % w.vocab
+    rng = np.random.default_rng(5000 + accept)
+    while len(seq) < n:
+        seq.append(int(rng.integers(0, w.vocab)))
+    return seq[:n]
+
+
+@pytest.mark.parametrize("name", ["mini_dense", "mini_moe", "mini_hybrid"])
+@pytest.mark.parametrize("accept", [1, 3, 8])
+def test_verify_matches_oracle(torch_cuda, name, accept):
+    torch = torch_cuda
+    from oracle import step as ostep
+    from tests.harness import HostWeights, host_kv, kv_copy
+    w = WL.get(name)
+    n = 8
+    p0 = w.max_ctx - n - 3
+    W = HostWeights(w)
+    kv = host_kv(w)
+    toks = _greedy_drafts(w, W, kv, p0, accept, n)
+    print(f"case {name} accept={accept} p0={p0} toks={toks}", flush=True)
+    kv_ref = kv_copy(kv)
+    v = ostep.verify_step(w, W, np.array([toks]), np.array([p0]), kv_ref)
+    assert int(v["accept_len"][0]) == accept
+    m = _model(w)
+    dev = m.device
+    t = torch.tensor([toks], dtype=torch.int32, device=dev)
+    pp = torch.tensor([p0], dtype=torch.int32, device=dev)
+    logits = torch.full((1, n, w.vocab), float("nan"), dtype=torch.float32, device=dev)
+    acc = torch.full((1,), -7, dtype=torch.int32, device=dev)
+    nxt = torch.full((1,), -7, dtype=torch.int32, device=dev)
+    m.verify(t, pp, logits, acc, nxt)
+    torch.cuda.synchronize(dev)
+    m.device_status()
+    assert int(acc.cpu()[0]) == accept
+    assert int(nxt.cpu()[0]) == int(v["next"][0])
+    g = {"logits": logits.cpu().numpy()[0], "next": v["argmax"][0]}
+    o = {"logits": v["logits"][0], "next": v["argmax"][0]}
+    err = GU.compare_step(w, g, o, f"verify {name} a={accept}")
+    kvg = m.kv_host()
+    for j in range(n):
+        GU.compare_kv_rows(w, kvg, kv_ref, [p0 + j], 1)
+    print(f"  max|dlogit|/rms = {err:.2e}")

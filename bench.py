@@ -133,37 +133,19 @@ def cpu_baseline(w, layers=8, B=1):
                       f"({t_step:.2f} s per step)"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=128)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="dense_27b")
-    ap.add_argument("--batches", default="1,8")
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-multilaunch", action="store_true")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU: the multi-GPU path is designed, not built; "
-                                   "run with --gpus 1"}))
-        sys.exit(2)
-
+def decode_bench(w, batches, steps, warmup, multilaunch=True):
+    """Chained greedy decode steps at each batch size; returns per-batch
+    results (and multi-launch timings when built)."""
     import torch
-    from synth import workloads as WL
     from decode_megakernel_md_amd.model import DeviceModel
-
-    w = WL.get(args.workload)
-    batches = [int(b) for b in args.batches.split(",")]
-    max_steps = w.max_ctx - w.context
-    steps = min(args.steps, max_steps - args.warmup)
     t0 = time.time()
     m = DeviceModel(w)
     torch.cuda.synchronize()
-    print(f"# model ready in {time.time() - t0:.1f} s ({m.weight_bytes / 1e9:.2f} GB weights)", file=sys.stderr,
-          flush=True)
+    print(f"# {w.name}: model ready in {time.time() - t0:.1f} s ({m.weight_bytes / 1e9:.2f} GB weights)",
+          file=sys.stderr, flush=True)
     res = {}
     for B in batches:
-        per, total, pos, ids = time_steps(m, B, steps, args.warmup)
+        per, total, pos, ids = time_steps(m, B, steps, warmup)
         wb, kvb = [], []
         for s in range(steps):
             a, b = algorithmic_bytes(w, B, pos[s], ids[s] if ids is not None else None)
@@ -174,18 +156,138 @@ def main():
         gbs = bytes_step / (mean_ms * 1e-3) / 1e9
         res[B] = {"tok_s": B * steps / (total * 1e-3), "ms_per_step": total / steps,
                   "p50_ms": float(np.percentile(per, 50)), "p90_ms": float(np.percentile(per, 90)),
-                  "bytes_per_step": bytes_step, "weight_bytes": float(np.mean(wb)), "kv_bytes": float(np.mean(kvb)),
-                  "achieved_gbs": gbs, "frac": gbs / PEAK_GBS}
-        print(f"# B={B}: {res[B]['ms_per_step']:.3f} ms/step, {res[B]['tok_s']:.1f} tok/s, {gbs:.0f} GB/s "
+                  "kernel_ms": mean_ms, "bytes_per_step": bytes_step, "weight_bytes": float(np.mean(wb)),
+                  "kv_bytes": float(np.mean(kvb)), "achieved_gbs": gbs, "frac": gbs / PEAK_GBS}
+        print(f"# {w.name} B={B}: {res[B]['ms_per_step']:.3f} ms/step, {res[B]['tok_s']:.1f} tok/s, {gbs:.0f} GB/s "
               f"({100 * gbs / PEAK_GBS:.1f}% of 8 TB/s)", file=sys.stderr, flush=True)
     ml = {}
-    if not args.no_multilaunch:
+    if multilaunch:
         for B in batches:
             try:
-                per, total, pos, _ = time_steps(m, B, min(steps, 16), 1, multilaunch=True)
-                ml[B] = {"ms_per_step": total / min(steps, 16), "tok_s": B * min(steps, 16) / (total * 1e-3)}
+                n = min(steps, 16)
+                per, total, pos, _ = time_steps(m, B, n, 1, multilaunch=True)
+                ml[B] = {"ms_per_step": total / n, "tok_s": B * n / (total * 1e-3)}
+                print(f"# {w.name} B={B} multi-launch: {ml[B]['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
             except Exception as e:  # not built for this configuration
-                ml[B] = {"error": str(e)[:120]}
+                ml[B] = {"error": str(e)[:160]}
+    m.close()
+    del m
+    torch.cuda.empty_cache()
+    return res, ml
+
+
+def verify_bench(w, steps, accepts=(3, 6), n=8):
+    """Speculative verify of 1 anchor + 7 drafts at context w.context.  For
+    acceptance length a the drafts are the greedy continuation of the anchor
+    for a-1 tokens (computed by decode steps on the device, after which the
+    delta-rule states are restored), then a token that differs from the
+    greedy one, then uniform random ids; each timed verify starts from the
+    same state (restored outside the timed region) and must accept a tokens.
+    Reports accepted tokens/s = a / verify latency."""
+    import torch
+    import synth
+    from decode_megakernel_md_amd.model import DeviceModel
+    m = DeviceModel(w)
+    dev = m.device
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    p0 = w.context
+    kda = [l for l in range(w.n_layers) if w.layer_kind(l) == "kda"]
+    saved = {l: m.kv_layer(l)[0].clone() for l in kda}
+
+    def restore():
+        for l in kda:
+            m.kv_layer(l)[0].copy_(saved[l])
+
+    anchor = int(synth.tokens(w, 1)[0])
+    out = {}
+    lg1 = torch.empty((1, w.vocab), dtype=torch.float32, device=dev)
+    nx1 = torch.empty((1,), dtype=torch.int32, device=dev)
+    for a in accepts:
+        restore()
+        toks = [anchor]
+        for j in range(min(a, n - 1)):
+            m.decode(torch.tensor([toks[-1]], dtype=torch.int32, device=dev),
+                     torch.tensor([p0 + j], dtype=torch.int32, device=dev), lg1, nx1)
+            toks.append(int(nx1.cpu()[0]))
+        restore()
+        if a < n:
+            toks[a] = (toks[a] + 1) % w.vocab
+        rng = np.random.default_rng(5000 + a)
+        while len(toks) < n:
+            toks.append(int(rng.integers(0, w.vocab)))
+        tt = torch.tensor([toks[:n]], dtype=torch.int32, device=dev)
+        pp = torch.tensor([p0], dtype=torch.int32, device=dev)
+        lg = torch.empty((1, n, w.vocab), dtype=torch.float32, device=dev)
+        acc = torch.empty((1,), dtype=torch.int32, device=dev)
+        nx = torch.empty((1,), dtype=torch.int32, device=dev)
+        ids = torch.empty((steps, w.n_layers, n, max(w.top_k, 1)), dtype=torch.int32, device=dev)
+        for _ in range(2):
+            restore()
+            m.verify(tt, pp, lg, acc, nx, ids[0])
+        torch.cuda.synchronize()
+        m.device_status()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        accs = []
+        for s_ in range(steps):
+            restore()
+            ev[s_][0].record(stream)
+            m.verify(tt, pp, lg, acc, nx, ids[s_])
+            ev[s_][1].record(stream)
+            accs.append(acc.clone())
+        torch.cuda.synchronize()
+        m.device_status()
+        per = np.array([e0.elapsed_time(e1) for e0, e1 in ev], dtype=np.float64)
+        got = sorted(set(int(x.cpu()[0]) for x in accs))
+        restore()
+        idsn = ids.cpu().numpy()
+        wb = [algorithmic_bytes(w, n, [p0], idsn[s_])[0] for s_ in range(steps)]
+        _, kvb = algorithmic_bytes(w, 1, [p0], idsn[0])
+        mean_ms = float(per.mean())
+        bytes_v = float(np.mean(wb)) + kvb
+        gbs = bytes_v / (mean_ms * 1e-3) / 1e9
+        out[a] = {"accepted": got, "ms_per_verify": mean_ms, "p90_ms": float(np.percentile(per, 90)),
+                  "accepted_tok_s": a / (mean_ms * 1e-3), "bytes_per_verify": bytes_v, "achieved_gbs": gbs,
+                  "frac": gbs / PEAK_GBS}
+        print(f"# {w.name} a={a}: {mean_ms:.3f} ms/verify, accepted {got}, {a / (mean_ms * 1e-3):.1f} accepted tok/s, "
+              f"{gbs:.0f} GB/s", file=sys.stderr, flush=True)
+    m.close()
+    del m
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dense_27b")
+    ap.add_argument("--batches", default="1,2,4,8")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-multilaunch", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the hybrid MoE decode and verify sections")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU: the multi-GPU path is designed, not built; "
+                                   "run with --gpus 1"}))
+        sys.exit(2)
+
+    from synth import workloads as WL
+
+    w = WL.get(args.workload)
+    batches = [int(b) for b in args.batches.split(",")]
+    steps = min(args.steps, w.max_ctx - w.context - args.warmup)
+    res, ml = decode_bench(w, batches, steps, args.warmup, multilaunch=not args.no_multilaunch)
+    extra = {}
+    if not args.no_extra and args.workload == "dense_27b":
+        wh = WL.hybrid_moe()
+        hs = min(16, wh.max_ctx - wh.context - args.warmup)
+        hres, hml = decode_bench(wh, [1, 8], hs, args.warmup, multilaunch=not args.no_multilaunch)
+        extra[wh.name] = {"steps": hs, "batches": {str(B): hres[B] for B in hres},
+                          "multilaunch": {str(B): hml[B] for B in hml}}
+        wv = WL.verify_hybrid()
+        extra[wv.name] = {"steps": 8, "verify": {str(a): r for a, r in verify_bench(wv, 8).items()}}
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(w, layers=w.mla_every if w.attn_kind == 1 else 8)
@@ -212,6 +314,7 @@ def main():
         "cpu_baseline": cpu,
         "batches": {str(B): res[B] for B in batches},
         "multilaunch": {str(B): ml[B] for B in ml},
+        "extra": extra,
     }
     print(json.dumps(line))
 

@@ -72,7 +72,7 @@ def lib():
             f.restype = I32
             f.argtypes = [P, P, P, P, P, I32, P, P, P]
         L.md_verify_step.restype = I32
-        L.md_verify_step.argtypes = [P, P, P, P, P, P, P, I32, I32, P]
+        L.md_verify_step.argtypes = [P, P, P, P, P, P, P, P, I32, I32, P]
         L.md_get_device_status.restype = I32
         L.md_get_device_status.argtypes = [P]
         L.md_last_error.restype = ctypes.c_char_p

@@ -492,15 +492,15 @@ md_status md_decode_step_multilaunch(md_model* m, const int32_t* tokens, const i
 }
 
 md_status md_verify_step(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv_cache,
-                         float* out_logits, int32_t* out_accept_len, int32_t* out_next_token, int32_t batch,
-                         int32_t n_tok, void* hip_stream) {
+                         float* out_logits, int32_t* out_accept_len, int32_t* out_next_token,
+                         int32_t* out_expert_ids, int32_t batch, int32_t n_tok, void* hip_stream) {
   if (batch != 1) return fail(MD_EUNSUPPORTED, "verify runs one sequence per launch (batch must be 1)");
   if (n_tok < 2 || n_tok > MAXB_) return fail(MD_EINVAL, "n_tok %d outside [2, %d]", n_tok, MAXB_);
   if (!out_accept_len || !out_next_token) return fail(MD_EINVAL, "out_accept_len and out_next_token must be non-NULL");
   if (((uintptr_t)out_accept_len & 3) || ((uintptr_t)out_next_token & 3)) return fail(MD_EINVAL, "misaligned pointer");
   Params p;
   // the n_tok rows of the one sequence travel as the step's token rows
-  md_status st = fill_params(m, tokens, positions, kv_cache, out_logits, 1, nullptr, nullptr, p);
+  md_status st = fill_params(m, tokens, positions, kv_cache, out_logits, 1, nullptr, out_expert_ids, p);
   if (st != MD_OK) return st;
   const md_config* c = &m->cfg;
   p.B = n_tok;

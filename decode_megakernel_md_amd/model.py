@@ -131,14 +131,17 @@ class DeviceModel:
                  ctypes.c_void_p(out_ids.data_ptr() if out_ids is not None else 0),
                  ctypes.c_void_p(s.cuda_stream)))
 
-    def verify(self, tokens, positions, logits, accept_len, next_token, stream=None):
+    def verify(self, tokens, positions, logits, accept_len, next_token, out_ids=None, stream=None):
+        """Enqueue one verify of tokens[1, n] (anchor + drafts) at positions[1]."""
         torch = self.torch
         B, n = int(tokens.shape[0]), int(tokens.shape[1])
         s = stream if stream is not None else torch.cuda.current_stream(self.device)
         check(lib().md_verify_step(self.handle, ctypes.c_void_p(tokens.data_ptr()),
                                    ctypes.c_void_p(positions.data_ptr()), ctypes.c_void_p(self.kv.data_ptr()),
                                    ctypes.c_void_p(logits.data_ptr()), ctypes.c_void_p(accept_len.data_ptr()),
-                                   ctypes.c_void_p(next_token.data_ptr()), B, n, ctypes.c_void_p(s.cuda_stream)))
+                                   ctypes.c_void_p(next_token.data_ptr()),
+                                   ctypes.c_void_p(out_ids.data_ptr() if out_ids is not None else 0), B, n,
+                                   ctypes.c_void_p(s.cuda_stream)))
 
     def device_status(self) -> None:
         check(lib().md_get_device_status(self.handle))

@@ -160,12 +160,14 @@ md_status md_decode_step_multilaunch(md_model* m, const int32_t* tokens, const i
  *   out_accept_len dev int32[batch]: a = 1 + m, m the largest j with t_i == argmax(row i-1)
  *              for all 1 <= i <= j (lowest index on argmax ties)
  *   out_next_token dev int32[batch]: argmax of row a-1
+ *   out_expert_ids dev int32[n_layers][n_tok][top_k] or NULL (MoE only): experts chosen
+ *              per layer and row, in descending router order
  * Delta-rule states are committed as they stand after token a-1 (the
  * per-token states pass through the workspace).  batch must be 1.  Out-of-
  * range tokens or positions are reported by md_get_device_status. */
 md_status md_verify_step(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv_cache,
-                         float* out_logits, int32_t* out_accept_len, int32_t* out_next_token, int32_t batch,
-                         int32_t n_tok, void* hip_stream);
+                         float* out_logits, int32_t* out_accept_len, int32_t* out_next_token,
+                         int32_t* out_expert_ids, int32_t batch, int32_t n_tok, void* hip_stream);
 
 /* Synchronises the model's last stream and reports the device error word:
  * MD_OK, or MD_EDEVICE with md_last_error() naming the cause (a sync wait

@@ -16,6 +16,7 @@ size_t megakernel_smem_bytes();
 hipError_t launch_megakernel(const Params& p, int grid, hipStream_t stream);
 hipError_t megakernel_occupancy(int* blocks_per_cu);
 hipError_t launch_pack(const void* src, void* dst, int64_t rows, int64_t cols, hipStream_t stream);
+hipError_t launch_multilaunch(const Params& p, const int* kinds, int grid, hipStream_t stream);
 }  // namespace md
 
 using namespace md;
@@ -256,6 +257,7 @@ struct md_model {
   int grid = 0;
   int bank = 0;
   hipStream_t last_stream = nullptr;
+  std::vector<int> kinds;  // layer kinds (host copy of the layer table's)
   uint64_t* trace = nullptr;
   int trace_n = 0;
 };
@@ -406,6 +408,8 @@ md_status md_init_model(const md_config* cfg, const void* const* weights, size_t
     delete m;
     return fail(MD_EHIP, "uploading the layer table: %s", hipGetErrorString(e));
   }
+  m->kinds.resize(cfg->n_layers);
+  for (int l = 0; l < cfg->n_layers; ++l) m->kinds[l] = L[l].kind;
   *out = m;
   return MD_OK;
 }
@@ -486,9 +490,15 @@ md_status md_decode_step(md_model* m, const int32_t* tokens, const int32_t* posi
 md_status md_decode_step_multilaunch(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv_cache,
                                      float* out_logits, int32_t batch, int32_t* out_tokens, int32_t* out_expert_ids,
                                      void* hip_stream) {
-  (void)m; (void)tokens; (void)positions; (void)kv_cache; (void)out_logits; (void)batch; (void)out_tokens;
-  (void)out_expert_ids; (void)hip_stream;
-  return fail(MD_EUNSUPPORTED, "multi-launch step is not built yet");
+  Params p;
+  md_status st = fill_params(m, tokens, positions, kv_cache, out_logits, batch, out_tokens, out_expert_ids, p);
+  if (st != MD_OK) return st;
+  p.bank = m->bank;
+  hipError_t e = launch_multilaunch(p, m->kinds.data(), m->grid, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(MD_EHIP, "phase launch: %s", hipGetErrorString(e));
+  m->bank ^= 1;
+  m->last_stream = (hipStream_t)hip_stream;
+  return MD_OK;
 }
 
 md_status md_verify_step(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv_cache,

@@ -2048,6 +2048,51 @@ extern "C" __global__ __launch_bounds__(NT) void md_megakernel(Params p) {
   if (((int*)md_smem)[0]) final_argmax(p);
 }
 
+
+// ===================================================================== multi-launch
+// The same step as one kernel launch per phase (the kernel boundary is the
+// barrier): the baseline whose inter-kernel gaps the megakernel removes.
+// Every phase runs the megakernel's own device code on the same grid, so the
+// results are identical.  LDS does not survive a launch, so the routed
+// experts' down projection recomputes the routing (same data, same result).
+enum : int {
+  PH_EMBED = 0, PH_QKV, PH_KV_WRITE, PH_ATTN, PH_OPROJ, PH_GATEUP, PH_DOWN, PH_MOE_A, PH_MOE_B, PH_MOE_C,
+  PH_KDA_PROJ, PH_KDA_REC, PH_KDA_O, PH_MLA_A, PH_MLA_B, PH_MLA_ABS, PH_MLA_ATTN, PH_MLA_OUT, PH_MLA_O,
+  PH_LMHEAD, PH_ARGMAX
+};
+
+extern "C" __global__ __launch_bounds__(NT) void md_phase_kernel(Params p, int layer, int phase) {
+  if (p.B < 1 || p.B > MAXB) return;
+  if (threadIdx.x == 0) md_cur_phase = 0;
+  const int l = layer < 0 ? 0 : layer;
+  const LayerDesc& L = p.layers[l];
+  const uint16_t* g_next = (l + 1 < p.n_layers) ? p.layers[l + 1].attn_norm : p.final_norm;
+  switch (phase) {
+    case PH_EMBED: clear_next_bank(p); phase_embed(p); break;
+    case PH_QKV: phase_qkv(p, L); break;
+    case PH_KV_WRITE: phase_gqa_kv_write(p, L); break;
+    case PH_ATTN: phase_attn_gqa(p, L, l); break;
+    case PH_OPROJ: phase_residual(p, L, RES_OPROJ, L.ffn_norm); break;
+    case PH_GATEUP: phase_gateup(p, L); break;
+    case PH_DOWN: phase_residual(p, L, RES_DENSE_DOWN, g_next); break;
+    case PH_MOE_A: phase_moe_a(p, L); break;
+    case PH_MOE_B: compute_routes(p, l); phase_moe_b(p, L); break;
+    case PH_MOE_C: compute_routes(p, l); phase_residual(p, L, RES_MOE_DOWN, g_next); break;
+    case PH_KDA_PROJ: phase_kda_proj(p, L); break;
+    case PH_KDA_REC: phase_kda_rec(p, L); break;
+    case PH_KDA_O: phase_residual(p, L, RES_KDA_O, L.ffn_norm); break;
+    case PH_MLA_A: phase_mla_a(p, L); break;
+    case PH_MLA_B: phase_mla_b(p, L); break;
+    case PH_MLA_ABS: phase_mla_absorb(p, L); break;
+    case PH_MLA_ATTN: phase_mla_attn(p, L); break;
+    case PH_MLA_OUT: phase_mla_out(p, L); break;
+    case PH_MLA_O: phase_residual(p, L, RES_MLA_O, L.ffn_norm); break;
+    case PH_LMHEAD: phase_lmhead(p); break;
+    case PH_ARGMAX: if (blockIdx.x == 0) final_argmax(p); break;
+    default: break;
+  }
+}
+
 }  // namespace md
 
 // ===================================================================== launch helpers
@@ -2090,6 +2135,46 @@ hipError_t launch_megakernel(const Params& p, int grid, hipStream_t stream) {
   void* args[] = {(void*)&p};
   return hipLaunchCooperativeKernel((const void*)md_megakernel, dim3(grid), dim3(NT), args,
                                     (unsigned)megakernel_smem_bytes(), stream);
+}
+
+// One decode step as a sequence of phase launches on `stream`.
+hipError_t launch_multilaunch(const Params& p, const int* kinds, int grid, hipStream_t stream) {
+  const unsigned smem = (unsigned)megakernel_smem_bytes();
+  hipError_t e = hipFuncSetAttribute((const void*)md_phase_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  auto go = [&](int layer, int phase, int g) {
+    hipLaunchKernelGGL(md_phase_kernel, dim3(g), dim3(NT), smem, stream, p, layer, phase);
+  };
+  go(-1, PH_EMBED, grid);
+  for (int l = 0; l < p.n_layers; ++l) {
+    if (kinds[l] == LK_GQA) {
+      go(l, PH_QKV, grid);
+      go(l, PH_ATTN, grid);
+      go(l, PH_OPROJ, grid);
+    } else if (kinds[l] == LK_KDA) {
+      go(l, PH_KDA_PROJ, grid);
+      go(l, PH_KDA_REC, grid);
+      go(l, PH_KDA_O, grid);
+    } else {
+      go(l, PH_MLA_A, grid);
+      go(l, PH_MLA_B, grid);
+      go(l, PH_MLA_ABS, grid);
+      go(l, PH_MLA_ATTN, grid);
+      go(l, PH_MLA_OUT, grid);
+      go(l, PH_MLA_O, grid);
+    }
+    if (p.n_experts == 0) {
+      go(l, PH_GATEUP, grid);
+      go(l, PH_DOWN, grid);
+    } else {
+      go(l, PH_MOE_A, grid);
+      go(l, PH_MOE_B, grid);
+      go(l, PH_MOE_C, grid);
+    }
+  }
+  go(-1, PH_LMHEAD, grid);
+  go(-1, PH_ARGMAX, grid);  // workgroup 0 reduces all grid candidates
+  return hipGetLastError();
 }
 
 hipError_t megakernel_occupancy(int* blocks_per_cu) {

@@ -168,3 +168,23 @@ def test_verify_matches_oracle(torch_cuda, name, accept):
     for j in range(n):
         GU.compare_kv_rows(w, kvg, kv_ref, [p0 + j], 1)
     print(f"  max|dlogit|/rms = {err:.2e}")
+
+
+@pytest.mark.parametrize("name,B", [("mini_dense", 3), ("mini_moe", 8), ("mini_hybrid", 3)])
+def test_multilaunch_equals_megakernel(torch_cuda, name, B):
+    """The one-launch-per-phase baseline runs the same device code: its
+    logits, tokens and expert ids are bitwise those of the megakernel, and
+    both match the oracle."""
+    w = WL.get(name)
+    m = _model(w)
+    toks = synth.tokens(w, B)
+    pos = [w.context - 3 * b for b in range(B)]
+    a = GU.run_gpu_step(m, toks, pos)
+    m.reset_kv()
+    b = GU.run_gpu_step(m, toks, pos, multilaunch=True)
+    assert np.array_equal(a["logits"], b["logits"])
+    assert np.array_equal(a["next"], b["next"])
+    if "expert_ids" in a:
+        assert np.array_equal(a["expert_ids"], b["expert_ids"])
+    o, _ = GU.run_oracle_step(w, toks, pos)
+    GU.compare_step(w, b, o, f"multilaunch {name}")

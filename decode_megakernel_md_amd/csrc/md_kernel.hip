@@ -639,7 +639,7 @@ __device__ __forceinline__ void load_block(KVBlock<HD>& r, rsrc_t krs, rsrc_t vr
 #define ASM (*reinterpret_cast<AttnSmem*>(md_smem))
 
 template <int HD, int GS, int CP>
-__device__ __noinline__ void attn_task_wave(const uint16_t* kc, const uint16_t* vc, uint32_t nbytes, int w0, int w1) {
+__device__ __forceinline__ void attn_task_wave(const uint16_t* kc, const uint16_t* vc, uint32_t nbytes, int w0, int w1) {
   constexpr int gs = GS;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const rsrc_t krs = make_rsrc_u(kc, nbytes), vrs = make_rsrc_u(vc, nbytes);
@@ -794,7 +794,10 @@ __device__ __noinline__ void phase_gqa_kv_write(const Params& p, const LayerDesc
   }
 }
 
-__device__ __noinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L, int layer) {
+// Inlined into the kernels, as is the per-wave worker above: as a called
+// function it would save and restore the callee-saved registers its
+// hundreds of live values occupy, on every call.
+__device__ __forceinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L, int layer) {
   AttnSmem& sm = *(AttnSmem*)md_smem;
   const int wv = threadIdx.x >> 6;
   const int hd = p.hd, gs = p.nq / p.nkv, B = p.B;

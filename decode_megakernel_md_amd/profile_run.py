@@ -1,0 +1,61 @@
+"""Driver for rocprofv3 counter runs.
+
+    python -m decode_megakernel_md_amd.profile_run [--workload dense_27b] [--batch 1] [--steps 3]
+                                                    [--multilaunch] [--copy-mib 1024]
+
+First a plain device-to-device copy of --copy-mib MiB (its byte count is
+known, so HBM counters read for it calibrate the counters read for the
+decode step), then --steps decode steps of the workload at the given batch
+and context, greedy tokens chained on the device."""
+from __future__ import annotations
+
+import argparse
+import sys
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", default="dense_27b")
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--multilaunch", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=1024)
+    args = ap.parse_args()
+    import torch
+    import synth
+    from synth import workloads as WL
+    from decode_megakernel_md_amd.model import DeviceModel
+
+    dev = torch.device("cuda:0")
+    n = args.copy_mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    print(f"# calibration copy: {n} bytes read, {n} bytes written", flush=True)
+
+    w = WL.get(args.workload)
+    m = DeviceModel(w)
+    B = args.batch
+    toks = torch.empty((args.steps + 1, B), dtype=torch.int32, device=dev)
+    toks[0] = torch.tensor(synth.tokens(w, B), device=dev)
+    logits = torch.empty((B, w.vocab), dtype=torch.float32, device=dev)
+    ids = None
+    if w.is_moe:
+        ids = torch.empty((w.n_layers, B, w.top_k), dtype=torch.int32, device=dev)
+    for s in range(args.steps):
+        pos = torch.full((B,), w.context + s, dtype=torch.int32, device=dev)
+        m.decode(toks[s], pos, logits, toks[s + 1], ids, multilaunch=args.multilaunch)
+    torch.cuda.synchronize()
+    m.device_status()
+    print(f"# {w.name}: {args.steps} steps at batch {B} ({'multi-launch' if args.multilaunch else 'megakernel'})",
+          flush=True)
+    m.close()
+
+
+if __name__ == "__main__":
+    sys.exit(main())

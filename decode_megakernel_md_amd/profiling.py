@@ -1,9 +1,15 @@
 """Profiling helpers: summarise rocprofv3 output.
 
     python -m decode_megakernel_md_amd.profiling <kernel_stats.csv | results.db>
+    python -m decode_megakernel_md_amd.profiling gaps <kernel_trace.csv | results.db> [kernel-name-substring]
+    python -m decode_megakernel_md_amd.profiling pmc <counter_collection.csv>
 
-prints a per-kernel table (calls, total/avg/min/max duration in microseconds)
-from either rocprofv3's --stats CSV or its rocpd SQLite database."""
+The first form prints a per-kernel table (calls, total/avg/min/max duration
+in microseconds) from rocprofv3's --stats CSV or its rocpd SQLite database.
+The second lists the idle time between consecutive dispatches of the named
+kernel (default: the per-phase kernel of the multi-launch step): the
+bubbles a single persistent launch removes.  The third averages each
+counter per dispatch and kernel from a --pmc run."""
 from __future__ import annotations
 
 import csv
@@ -38,7 +44,67 @@ def table(rows: List[Dict]) -> str:
     return "\n".join(lines)
 
 
+def dispatches(path: str, needle: str) -> List[tuple]:
+    """(start_ns, end_ns) of every dispatch whose kernel name contains needle, by start time."""
+    if path.endswith(".db"):
+        db = sqlite3.connect(path)
+        rows = db.execute("select name, start, end from kernels order by start").fetchall()
+        return [(int(r[1]), int(r[2])) for r in rows if needle in r[0]]
+    out = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if needle in r["Kernel_Name"]:
+                out.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    out.sort()
+    return out
+
+
+def gaps(d: List[tuple], break_ns: int = 1_000_000) -> Dict:
+    """Idle time between consecutive dispatches; a gap longer than break_ns is
+    taken as the host pausing between runs and starts a new run."""
+    runs, cur = [], [d[0]] if d else []
+    for a, b in zip(d, d[1:]):
+        if b[0] - a[1] > break_ns:
+            runs.append(cur)
+            cur = [b]
+        else:
+            cur.append(b)
+    if cur:
+        runs.append(cur)
+    busy = sum(e - s for r in runs for s, e in r)
+    span = sum(r[-1][1] - r[0][0] for r in runs)
+    g = [b[0] - a[1] for r in runs for a, b in zip(r, r[1:])]
+    return {"dispatches": len(d), "runs": len(runs), "busy_us": busy / 1e3, "span_us": span / 1e3,
+            "idle_us": (span - busy) / 1e3, "gaps": len(g), "mean_gap_us": (sum(g) / len(g) / 1e3) if g else 0.0,
+            "max_gap_us": (max(g) / 1e3) if g else 0.0}
+
+
+def pmc(path: str) -> List[Dict]:
+    """Per (kernel, counter): dispatches and the mean counter value per dispatch."""
+    acc: Dict[tuple, List[float]] = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            acc.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    return [{"kernel": k[0], "counter": k[1], "dispatches": len(v), "mean": sum(v) / len(v), "min": min(v),
+             "max": max(v)} for k, v in sorted(acc.items(), key=lambda kv: -sum(kv[1]))]
+
+
 if __name__ == "__main__":
-    p = sys.argv[1]
-    rows = stats_from_db(p) if p.endswith(".db") else stats_from_csv(p)
-    print(table(rows))
+    if sys.argv[1] == "pmc":
+        print("| kernel | counter | dispatches | mean per dispatch | min | max |")
+        print("|---|---|---|---|---|---|")
+        for r in pmc(sys.argv[2]):
+            print(f"| {r['kernel'][:70]} | {r['counter']} | {r['dispatches']} | {r['mean']:.1f} | {r['min']:.1f} | "
+                  f"{r['max']:.1f} |")
+    elif sys.argv[1] == "gaps":
+        needle = sys.argv[3] if len(sys.argv) > 3 else "md_phase_kernel"
+        r = gaps(dispatches(sys.argv[2], needle))
+        print("| kernel | dispatches | runs | busy (us) | span (us) | idle between dispatches (us) | gaps | "
+              "mean gap (us) | max gap (us) |")
+        print("|---|---|---|---|---|---|---|---|---|")
+        print(f"| {needle} | {r['dispatches']} | {r['runs']} | {r['busy_us']:.1f} | {r['span_us']:.1f} | "
+              f"{r['idle_us']:.1f} | {r['gaps']} | {r['mean_gap_us']:.2f} | {r['max_gap_us']:.2f} |")
+    else:
+        p = sys.argv[1]
+        rows = stats_from_db(p) if p.endswith(".db") else stats_from_csv(p)
+        print(table(rows))

@@ -1,0 +1,139 @@
+"""CPU tests of the C ABI (no GPU needed): libmd.so loads, exports every
+function include/md.h declares, and rejects bad arguments on the host before
+any device work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_megakernel_md_amd import _lib
+from synth import workloads as WL
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+P = ctypes.c_void_p
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "md.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(md_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert len(names) >= 15
+    so = ctypes.CDLL(_lib.SO)
+    for n in names:
+        assert hasattr(so, n), f"{n} declared in md.h but not exported"
+    assert sorted(_lib.EXPORTS) == names
+
+
+def _cfg(name="mini_dense", **kw):
+    c = _lib.config_from(WL.get(name))
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def _err():
+    return _lib.lib().md_last_error().decode()
+
+
+def test_inventory_matches_the_workload_tensor_list():
+    for name in ("tiny_dense", "mini_moe", "mini_hybrid", "hybrid_moe"):
+        w = WL.get(name)
+        inv = _lib.weight_inventory(_lib.config_from(w))
+        assert inv == [(t.name, t.rows, t.cols) for t in WL.tensor_inventory(w)]
+
+
+def test_weight_layouts():
+    L = _lib.lib()
+    w = WL.mini_hybrid()
+    c = _lib.config_from(w)
+    for i, t in enumerate(WL.tensor_inventory(w)):
+        want = 0 if (i == 0 or t.rows == 1 or t.name.endswith("mla_wkvb")) else 1
+        assert L.md_weight_layout(ctypes.byref(c), i) == want, t.name
+    assert L.md_weight_layout(ctypes.byref(c), 10 ** 6) == -1
+
+
+def test_packed_bytes():
+    L = _lib.lib()
+    assert L.md_packed_bytes(16, 32) == 1024
+    assert L.md_packed_bytes(17, 64) == 2 * 2 * 1024
+    assert L.md_packed_bytes(5, 31) == 0
+    assert L.md_packed_bytes(0, 32) == 0
+
+
+def test_kv_bytes_match_the_documented_layout():
+    L = _lib.lib()
+    for name in ("mini_dense", "mini_moe", "mini_hybrid", "dense_27b", "hybrid_moe"):
+        w = WL.get(name)
+        _, total = WL.kv_layout(w)
+        assert L.md_kv_bytes(ctypes.byref(_lib.config_from(w))) == total, name
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("max_batch", 9, _lib.MD_EINVAL),
+    ("max_batch", 0, _lib.MD_EINVAL),
+    ("hidden", 330, _lib.MD_EUNSUPPORTED),
+    ("head_dim", 96, _lib.MD_EUNSUPPORTED),
+    ("n_kv_heads", 4, _lib.MD_EINVAL),       # 6 q heads are not a multiple of 4
+    ("ffn_dim", 100, _lib.MD_EUNSUPPORTED),
+    ("attn_kind", 2, _lib.MD_EINVAL),
+    ("flags", 1, _lib.MD_EINVAL),
+])
+def test_invalid_configs_are_rejected(field, value, status):
+    L = _lib.lib()
+    c = _cfg(**{field: value})
+    assert L.md_workspace_bytes(ctypes.byref(c)) == 0
+    h = P()
+    assert L.md_init_model(ctypes.byref(c), None, 0, None, 0, None, ctypes.byref(h)) == status
+    assert _err()
+    assert not h.value
+
+
+def test_moe_and_hybrid_limits():
+    L = _lib.lib()
+    h = P()
+    c = _cfg("mini_moe", n_experts=65)
+    assert L.md_init_model(ctypes.byref(c), None, 0, None, 0, None, ctypes.byref(h)) == _lib.MD_EUNSUPPORTED
+    c = _cfg("mini_moe", top_k=9)
+    assert L.md_init_model(ctypes.byref(c), None, 0, None, 0, None, ctypes.byref(h)) == _lib.MD_EINVAL
+    c = _cfg("mini_hybrid", kv_lora=256)
+    assert L.md_init_model(ctypes.byref(c), None, 0, None, 0, None, ctypes.byref(h)) == _lib.MD_EUNSUPPORTED
+    c = _cfg("mini_hybrid", kda_dv=48)
+    assert L.md_init_model(ctypes.byref(c), None, 0, None, 0, None, ctypes.byref(h)) == _lib.MD_EUNSUPPORTED
+
+
+def test_init_argument_checks_before_any_device_call():
+    L = _lib.lib()
+    c = _cfg()
+    h = P()
+    assert L.md_init_model(ctypes.byref(c), None, 0, None, 0, None, None) == _lib.MD_EINVAL
+    assert L.md_init_model(ctypes.byref(c), None, 0, None, 0, None, ctypes.byref(h)) == _lib.MD_EINVAL
+    assert "weight pointers" in _err()
+    n = L.md_weight_count(ctypes.byref(c))
+    ptrs = (P * n)(*([0] * n))
+    assert L.md_init_model(ctypes.byref(c), ptrs, n, None, 0, None, ctypes.byref(h)) == _lib.MD_EINVAL
+    assert "NULL" in _err()
+
+
+def test_null_model_and_bad_step_arguments():
+    L = _lib.lib()
+    assert L.md_decode_step(None, None, None, None, None, 1, None, None, None) == _lib.MD_EINVAL
+    assert L.md_decode_step_multilaunch(None, None, None, None, None, 1, None, None, None) == _lib.MD_EINVAL
+    assert L.md_verify_step(None, None, None, None, None, None, None, None, 2, 8, None) == _lib.MD_EUNSUPPORTED
+    assert L.md_verify_step(None, None, None, None, None, None, None, None, 1, 9, None) == _lib.MD_EINVAL
+    assert L.md_verify_step(None, None, None, None, None, None, None, None, 1, 1, None) == _lib.MD_EINVAL
+    assert L.md_get_device_status(None) == _lib.MD_EINVAL
+    assert L.md_set_trace(None, None, 0) == _lib.MD_EINVAL
+    assert L.md_grid_size(None) == 0
+    L.md_free_model(None)
+
+
+def test_pack_argument_checks():
+    L = _lib.lib()
+    assert L.md_pack_weight(None, None, 16, 32, None) == _lib.MD_EINVAL
+    assert L.md_pack_weight(P(16), P(32), 16, 33, None) == _lib.MD_EINVAL
+    assert L.md_pack_weight(P(8), P(32), 16, 32, None) == _lib.MD_EINVAL

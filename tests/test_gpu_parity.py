@@ -188,3 +188,23 @@ def test_multilaunch_equals_megakernel(torch_cuda, name, B):
         assert np.array_equal(a["expert_ids"], b["expert_ids"])
     o, _ = GU.run_oracle_step(w, toks, pos)
     GU.compare_step(w, b, o, f"multilaunch {name}")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,B", [("dense_27b", 1), ("dense_27b", 8), ("hybrid_moe", 1), ("hybrid_moe", 8)])
+def test_full_shape_layers_match_oracle(torch_cuda, name, B):
+    """The two large models at their full layer shapes, vocabulary and
+    context, in the launch configuration bench.py times (grid = CU count,
+    same batch), reduced to 4 layers so that the fp64 oracle finishes in
+    seconds (the hybrid model's 4 layers are 3 delta-rule layers and 1 MLA
+    layer, each with the 16-expert MoE)."""
+    w = WL.get(name).replace(n_layers=4)
+    toks = synth.tokens(w, B)
+    pos = [w.context - 97 * b for b in range(B)]
+    print(f"case {name} 4 layers B={B} pos={pos}", flush=True)
+    m = _model(w)
+    g = GU.run_gpu_step(m, toks, pos)
+    o, kv_ref = GU.run_oracle_step(w, toks, pos)
+    err = GU.compare_step(w, g, o, f"{name} B={B}")
+    GU.compare_kv_rows(w, m.kv_host(), kv_ref, pos, B)
+    print(f"  max|dlogit|/rms = {err:.2e}")

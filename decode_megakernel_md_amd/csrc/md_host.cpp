@@ -423,6 +423,7 @@ static md_status fill_params(md_model* m, const int32_t* tokens, const int32_t* 
   if (((uintptr_t)kv & 255) || ((uintptr_t)out_logits & 3) || ((uintptr_t)tokens & 3) || ((uintptr_t)positions & 3))
     return fail(MD_EINVAL, "misaligned pointer (kv_cache needs 256-byte alignment)");
   memset(&p, 0, sizeof p);
+  p.ml_phase = -1;
   const WsLayout& w = m->lay;
   p.layers = (const LayerDesc*)(m->ws + w.layers);
   p.embed = (const uint16_t*)m->weights.front();

@@ -109,6 +109,21 @@ __device__ __forceinline__ void grid_sync(const Params& p, int& sidx) {
   if (threadIdx.x == 0) md_cur_phase = sidx;
 }
 
+// Split form of a sync point: grid_arrive when this workgroup's work for it is
+// done; wait_point once the next phase has issued what it may issue before
+// the other workgroups are done (its first weight loads).  idx < 0: no wait
+// (the multi-launch step, where the kernel boundary is the barrier).
+__device__ __forceinline__ void grid_arrive(const Params& p, int sidx) {
+  stamp(p, 2 * sidx);
+  arrive(p, sidx);
+}
+__device__ __forceinline__ void wait_point(const Params& p, int idx) {
+  if (idx < 0) return;
+  wait_all(p, idx);
+  stamp(p, 2 * idx + 1);
+  if (threadIdx.x == 0) md_cur_phase = idx + 1;
+}
+
 // clear this WG's share of the other bank (used by the next step)
 __device__ void clear_next_bank(const Params& p) {
   unsigned* nb = p.sync + (size_t)(p.bank ^ 1) * p.n_sync * SP_WORDS;
@@ -157,9 +172,12 @@ __device__ __forceinline__ int row_pos(const Params& p, int r) {
 // the k-steps of a group and keep GDS k-steps of loads in flight in one
 // continuous stream across groups (no pipeline drain between tiles).
 //
-// The workgroup's dynamic LDS.  Phases address it through this symbol (not
-// through a pointer argument) so that accesses compile to LDS instructions.
-extern __shared__ __attribute__((aligned(16))) char md_smem[];
+// The workgroup's LDS.  Phases address it through this symbol (not through a
+// pointer argument) so that accesses compile to LDS instructions.  It is a
+// static array: functions reach it at a fixed address (dynamic LDS would be
+// found through a per-kernel offset table in memory, a load in the stream).
+constexpr size_t MD_SMEM_BYTES = 112 * 1024;
+__shared__ __attribute__((aligned(16))) char md_smem[MD_SMEM_BYTES];
 
 constexpr int CMAX_DEV = 256;    // largest chunk count per (sequence, kv head)
 constexpr int TG = 2;            // slots per group (share one B operand load)
@@ -205,8 +223,8 @@ struct GroupDesc {
 };
 
 struct GemvSmem {
-  float red[NW][TG][16][16];   // also reused as [NT][MAXB] scratch after the stream
-  float y[TG][16][MAXB];
+  float red[2][NW][TG][16][16];  // per-wave partial tiles of a group, two buffers alternating by group;
+                                 // also reused as [NT][MAXB] scratch after the stream
   Slot slots[MAXSLOT];
   GroupDesc grp[MAXGRP];
   MatDesc mats[MAXMAT];
@@ -317,21 +335,13 @@ __device__ __forceinline__ void slot_src(int si, int lq, uint32_t lchunk, int wv
   pstep = lv ? (uint32_t)(NW * 1024) : 0u;
 }
 
-// Reduce the four waves' partial tiles of a finished group into GSM.y.
-__device__ __forceinline__ void gemv_reduce(const f32x4 (&acc)[TG], int wv, int lane) {
+// Output (token t, row rr of slot 2g + i) of a finished group: the four
+// waves' partials, hi and lo columns, summed in a fixed order.
+__device__ __forceinline__ float gy(int rb, int i, int rr, int t) {
+  float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < TG; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) GSM.red[wv][i][4 * (lane >> 4) + r][lane & 15] = acc[i][r];
-  __syncthreads();
-  for (int e = threadIdx.x; e < TG * 16 * MAXB; e += NT) {
-    int i = e / (16 * MAXB), r = (e / MAXB) % 16, k = e % MAXB;
-    float s = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) s += GSM.red[w][i][r][2 * k] + GSM.red[w][i][r][2 * k + 1];
-    GSM.y[i][r][k] = s;
-  }
-  __syncthreads();
+  for (int w = 0; w < NW; ++w) s += GSM.red[rb][w][i][rr][2 * t] + GSM.red[rb][w][i][rr][2 * t + 1];
+  return s;
 }
 
 __device__ __forceinline__ int group_nks(int g, int wv) {
@@ -339,85 +349,185 @@ __device__ __forceinline__ int group_nks(int g, int wv) {
   return (KS - wv + NW - 1) / NW;
 }
 
-// Run the GEMV over GSM's group list.  After each finished group g,
-// epi(g) reads GSM.y[i][row-in-slot][token] for slots 2g + i (LDS only).
-template <class Epi>
-__device__ __forceinline__ void run_gemv(const uint8_t* ws, uint32_t ws_bytes, uint32_t off_zero, int B, Epi epi) {
+// 1/rms per token from the partial sums of squares of every workgroup (this
+// thread holds those of workgroups tid and tid + NT), summed in a fixed
+// order: identical in every workgroup.
+__device__ __forceinline__ void inv_finish(const Params& p, float* inv, int n_feat, i32x4 a0, i32x4 b0, i32x4 a1,
+                                           i32x4 b1) {
+  float* stage = (float*)(md_smem + sizeof(GemvSmem));  // [2*NT][MAXB]
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    stage[threadIdx.x * MAXB + k] = __int_as_float(a0[k]);
+    stage[threadIdx.x * MAXB + 4 + k] = __int_as_float(b0[k]);
+    stage[(threadIdx.x + NT) * MAXB + k] = __int_as_float(a1[k]);
+    stage[(threadIdx.x + NT) * MAXB + 4 + k] = __int_as_float(b1[k]);
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    int t = 2 * wv + k;
+    float sum = 0.f;
+    for (int g = lane; g < (int)gridDim.x; g += 64) sum += stage[g * MAXB + t];
+    sum = wave_sum(sum);
+    if (lane == 0) inv[t] = 1.0f / sqrtf(sum / (float)n_feat + p.eps);
+  }
+  __syncthreads();
+}
+
+// The per-wave weight stream over GSM's group list.  gemv_begin issues the
+// weight loads of the first GDS k-steps (they depend on no other workgroup,
+// so a phase issues them before it waits at its sync point); gemv_run then
+// issues the matching activation (B operand) loads and streams the rest,
+// GDS k-steps ahead of the matrix cores, continuously across groups.
+struct GemvStream {
+  int wv, lq, tok, part, B, ngroups, total;
+  uint32_t lchunk, lane16;
+  uint64_t zero_addr;
+  rsrc_t urs;
+  int ig, is, nks_i;
+  uint32_t boff;
+  uint64_t pa0, pa1;
+  uint32_t ps0, ps1;
+  i32x4 ra[GDS][TG];
+  i32x4 rb[GDS];
+  uint32_t bo[GDS];
+};
+
+__device__ __forceinline__ void gs_group(GemvStream& s, int g) {
+  const int ks = __builtin_amdgcn_readfirstlane(GSM.grp[g].KS);
+  const uint32_t uo = __builtin_amdgcn_readfirstlane(GSM.grp[g].u_off);
+  s.nks_i = (ks - s.wv + NW - 1) / NW;
+  s.boff = s.tok < s.B ? uo + (uint32_t)((s.part * MAXB + s.tok) * ks * 32) * 2u + s.lane16 : OOB;
+  slot_src(2 * g, s.lq, s.lchunk, s.wv, s.zero_addr, s.pa0, s.ps0);
+  slot_src(2 * g + 1, s.lq, s.lchunk, s.wv, s.zero_addr, s.pa1, s.ps1);
+}
+
+// Weight loads of one k-step (ring entry d); past the last group they read
+// the zero block.  Records the k-step's B-operand offset.
+__device__ __forceinline__ void gs_issue_a(GemvStream& s, int d) {
+  const bool ok = s.ig < s.ngroups;
+  s.ra[d][0] = __builtin_nontemporal_load((const __attribute__((address_space(1))) i32x4*)(ok ? s.pa0 : s.zero_addr));
+  s.ra[d][1] = __builtin_nontemporal_load((const __attribute__((address_space(1))) i32x4*)(ok ? s.pa1 : s.zero_addr));
+  s.pa0 += s.ps0;
+  s.pa1 += s.ps1;
+  s.bo[d] = (ok && s.boff != OOB) ? s.boff + (uint32_t)(s.is * NW + s.wv) * 64u : OOB;
+  if (++s.is == s.nks_i) {
+    s.is = 0;
+    ++s.ig;
+    if (s.ig < s.ngroups) gs_group(s, s.ig);
+  }
+}
+__device__ __forceinline__ void gs_issue_b(GemvStream& s, int d) { s.rb[d] = ld_x4<CP_SC1>(s.urs, s.bo[d]); }
+
+// Steady state: weight and activation loads of one k-step, then the group
+// switch (loads before the branch, so the compiler sees one load sequence).
+__device__ __forceinline__ void gs_issue(GemvStream& s, int d) {
+  const bool ok = s.ig < s.ngroups;
+  s.ra[d][0] = __builtin_nontemporal_load((const __attribute__((address_space(1))) i32x4*)(ok ? s.pa0 : s.zero_addr));
+  s.ra[d][1] = __builtin_nontemporal_load((const __attribute__((address_space(1))) i32x4*)(ok ? s.pa1 : s.zero_addr));
+  s.pa0 += s.ps0;
+  s.pa1 += s.ps1;
+  s.rb[d] = ld_x4<CP_SC1>(s.urs, (ok && s.boff != OOB) ? s.boff + (uint32_t)(s.is * NW + s.wv) * 64u : OOB);
+  if (++s.is == s.nks_i) {
+    s.is = 0;
+    ++s.ig;
+    if (s.ig < s.ngroups) gs_group(s, s.ig);
+  }
+}
+
+__device__ __forceinline__ void gemv_begin(GemvStream& s, const uint8_t* ws, uint32_t ws_bytes, uint32_t off_zero,
+                                           int B) {
   const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ngroups = __builtin_amdgcn_readfirstlane(GSM.ngroups);
+  s.wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  s.ngroups = __builtin_amdgcn_readfirstlane(GSM.ngroups);
   int total = 0;
-  for (int g = 0; g < ngroups; ++g) total += group_nks(g, wv);
-  total = __builtin_amdgcn_readfirstlane(total);
-  const rsrc_t urs = make_rsrc_u(ws, ws_bytes);
-  const int lq = (lane & 15) >> 2;
-  const uint32_t lchunk = (uint32_t)(((lane >> 4) * 4 + (lane & 3)) * 16);
-  const int n16 = lane & 15, tok = n16 >> 1, part = n16 & 1;
-  const uint64_t zero_addr = (uint64_t)(ws + off_zero);
-  int ig = 0, is = 0, nks_i = 0;
-  uint32_t boff = OOB;
-  uint64_t pa0 = zero_addr, pa1 = zero_addr;
-  uint32_t ps0 = 0, ps1 = 0;
+  for (int g = 0; g < s.ngroups; ++g) total += group_nks(g, s.wv);
+  s.total = __builtin_amdgcn_readfirstlane(total);
+  s.urs = make_rsrc_u(ws, ws_bytes);
+  s.lq = (lane & 15) >> 2;
+  s.lchunk = (uint32_t)(((lane >> 4) * 4 + (lane & 3)) * 16);
+  s.lane16 = (uint32_t)(lane >> 4) * 16u;
+  s.tok = (lane & 15) >> 1;
+  s.part = lane & 1;
+  s.B = B;
+  s.zero_addr = (uint64_t)(ws + off_zero);
+  s.ig = 0;
+  s.is = 0;
+  s.nks_i = 1;
+  s.boff = OOB;
+  s.pa0 = s.pa1 = s.zero_addr;
+  s.ps0 = s.ps1 = 0;
+  if (s.ngroups > 0) gs_group(s, 0);
+#pragma unroll
+  for (int d = 0; d < GDS; ++d) gs_issue_a(s, d);
+}
+
+// Stream everything.  After each finished group g, epi(g, rb) reads its
+// outputs with gy(rb, i, row-in-slot, token) (LDS only).  One barrier per
+// group: the partials of consecutive groups go to alternating buffers.
+// inv_n > 0: first fill GSM.inv with 1/rms over inv_n features from the
+// per-workgroup partial sums of squares at inv_off.  Those loads are issued
+// before the ring's activation loads, so waiting for them never waits for
+// the ring.
+template <class Epi>
+__device__ __forceinline__ void gemv_run(GemvStream& s, const Params& p, int inv_n, uint32_t inv_off, Epi epi) {
   static_assert(TG == 2, "the stream handles slot pairs");
-#define GEMV_GROUP(G_)                                                                                          \
-  {                                                                                                             \
-    const int ks_ = __builtin_amdgcn_readfirstlane(GSM.grp[G_].KS);                                            \
-    const uint32_t uo_ = __builtin_amdgcn_readfirstlane(GSM.grp[G_].u_off);                                    \
-    nks_i = (ks_ - wv + NW - 1) / NW;                                                                           \
-    boff = tok < B ? uo_ + (uint32_t)((part * MAXB + tok) * ks_ * 32) * 2u + (uint32_t)(lane >> 4) * 16u : OOB; \
-    slot_src(2 * (G_), lq, lchunk, wv, zero_addr, pa0, ps0);                                                    \
-    slot_src(2 * (G_) + 1, lq, lchunk, wv, zero_addr, pa1, ps1);                                                \
+  const int lane = threadIdx.x & 63;
+  i32x4 ia0, ib0, ia1, ib1;
+  if (inv_n > 0) {
+    const rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+    const int g0 = threadIdx.x, g1 = threadIdx.x + NT;
+    const int G = gridDim.x;
+    ia0 = ld_x4<CP_SC1>(r, g0 < G ? inv_off + (uint32_t)(g0 * MAXB) * 4u : OOB);
+    ib0 = ld_x4<CP_SC1>(r, g0 < G ? inv_off + (uint32_t)(g0 * MAXB + 4) * 4u : OOB);
+    ia1 = ld_x4<CP_SC1>(r, g1 < G ? inv_off + (uint32_t)(g1 * MAXB) * 4u : OOB);
+    ib1 = ld_x4<CP_SC1>(r, g1 < G ? inv_off + (uint32_t)(g1 * MAXB + 4) * 4u : OOB);
   }
-#define GEMV_ISSUE(RA, RB)                                                                                      \
-  {                                                                                                             \
-    bool ok_ = ig < ngroups;                                                                                    \
-    RA[0] = __builtin_nontemporal_load((const __attribute__((address_space(1))) i32x4*)(ok_ ? pa0 : zero_addr)); \
-    RA[1] = __builtin_nontemporal_load((const __attribute__((address_space(1))) i32x4*)(ok_ ? pa1 : zero_addr)); \
-    pa0 += ps0;                                                                                                 \
-    pa1 += ps1;                                                                                                 \
-    RB = ld_x4<CP_SC1>(urs, ok_ && boff != OOB ? boff + (uint32_t)(is * NW + wv) * 64u : OOB);                  \
-    if (++is == nks_i) {                                                                                        \
-      is = 0;                                                                                                   \
-      ++ig;                                                                                                     \
-      if (ig < ngroups) GEMV_GROUP(ig);                                                                         \
-    }                                                                                                           \
-  }
-  if (ngroups > 0) GEMV_GROUP(0);
+#pragma unroll
+  for (int d = 0; d < GDS; ++d) gs_issue_b(s, d);
+  if (inv_n > 0) inv_finish(p, GSM.inv, inv_n, ia0, ib0, ia1, ib1);
   f32x4 acc[TG];
 #pragma unroll
   for (int i = 0; i < TG; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  i32x4 ra[GDS][TG], rb[GDS];
-#pragma unroll
-  for (int d = 0; d < GDS; ++d) GEMV_ISSUE(ra[d], rb[d]);
-  int cg = 0, cs = 0;
-  int nks_c = ngroups > 0 ? group_nks(0, wv) : 1;
-  // The body is unconditional: steps past the end read the zero block and
+  int cg = 0, cs = 0, rbuf = 0;
+  int nks_c = s.ngroups > 0 ? group_nks(0, s.wv) : 1;
+  // One k-step: matrix-core work on ring entry d, its refill, and at the end
+  // of a group the partials to LDS, one barrier, and the epilogue.
+#define GEMV_STEP(J0, D)                                                                                        \
+  {                                                                                                             \
+    bf16x8 bop = __builtin_bit_cast(bf16x8, s.rb[D]);                                                           \
+    _Pragma("unroll") for (int i = 0; i < TG; ++i) acc[i] =                                                     \
+        __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, s.ra[D][i]), bop, acc[i], 0, 0, 0);  \
+    gs_issue(s, D);                                                                                             \
+    if ((J0) + (D) < s.total) {                                                                                 \
+      if (++cs == nks_c) {                                                                                      \
+        cs = 0;                                                                                                 \
+        _Pragma("unroll") for (int i = 0; i < TG; ++i) _Pragma("unroll") for (int r = 0; r < 4; ++r)            \
+            GSM.red[rbuf][s.wv][i][4 * (lane >> 4) + r][lane & 15] = acc[i][r];                                 \
+        __syncthreads();                                                                                        \
+        _Pragma("unroll") for (int i = 0; i < TG; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};                      \
+        epi(cg, rbuf);                                                                                          \
+        rbuf ^= 1;                                                                                              \
+        ++cg;                                                                                                   \
+        if (cg < s.ngroups) nks_c = group_nks(cg, s.wv);                                                        \
+      }                                                                                                         \
+    }                                                                                                           \
+  }
+  // The first round is peeled: its ring was filled in two parts (weights
+  // before the sync point, activations after), and a loop entered from that
+  // state would get the first round's conservative load waits in every round.
+  // The bodies are unconditional: steps past the end read the zero block and
   // add nothing.  (A guarded body would make the compiler assume the later
   // loads of the previous round may be missing and wait for all of them.)
-  for (int j0 = 0; j0 < total; j0 += GDS) {
 #pragma unroll
-    for (int d = 0; d < GDS; ++d) {
-      bf16x8 bop = __builtin_bit_cast(bf16x8, rb[d]);
+  for (int d = 0; d < GDS; ++d) GEMV_STEP(0, d)
+  for (int j0 = GDS; j0 < s.total; j0 += GDS) {
 #pragma unroll
-      for (int i = 0; i < TG; ++i)
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ra[d][i]), bop, acc[i], 0, 0, 0);
-      GEMV_ISSUE(ra[d], rb[d]);
-      if (j0 + d < total) {
-        if (++cs == nks_c) {
-          cs = 0;
-          gemv_reduce(acc, wv, lane);
-#pragma unroll
-          for (int i = 0; i < TG; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-          epi(cg);
-          __syncthreads();
-          ++cg;
-          if (cg < ngroups) nks_c = group_nks(cg, wv);
-        }
-      }
-    }
+    for (int d = 0; d < GDS; ++d) GEMV_STEP(j0, d)
   }
-#undef GEMV_ISSUE
-#undef GEMV_GROUP
+#undef GEMV_STEP
+  __syncthreads();
 }
 
 // Row rr (0..15) of a slot: matrix and global row; false for an empty
@@ -462,35 +572,6 @@ __device__ __forceinline__ bool builder_done(const Params& p, SlotBuilder& sb, i
 
 // ===================================================================== phases
 
-// inv_rms[t] from the per-WG partial sums of squares (fixed order: identical
-// in every workgroup).  ssq: fp32[G][MAXB] at ws offset p.off_ssq.
-__device__ __noinline__ void load_inv_rms(const Params& p, float* inv_rms, int n_feat, uint32_t off_ssq) {
-  // every thread fetches one workgroup's partials for all tokens (one round
-  // trip), then wave w reduces tokens 2w, 2w+1 in a fixed order
-  float* stage = (float*)(md_smem + sizeof(GemvSmem));  // [G][MAXB]
-  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-  for (int g = threadIdx.x; g < (int)gridDim.x; g += NT) {
-    i32x4 a = ld_x4<CP_SC1>(r, off_ssq + (uint32_t)(g * MAXB) * 4u);
-    i32x4 b = ld_x4<CP_SC1>(r, off_ssq + (uint32_t)(g * MAXB + 4) * 4u);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      stage[g * MAXB + k] = __int_as_float(a[k]);
-      stage[g * MAXB + 4 + k] = __int_as_float(b[k]);
-    }
-  }
-  __syncthreads();
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    int t = 2 * wv + k;
-    float s = 0.f;
-    for (int g = lane; g < (int)gridDim.x; g += 64) s += stage[g * MAXB + t];
-    s = wave_sum(s);
-    if (lane == 0) inv_rms[t] = 1.0f / sqrtf(s / (float)n_feat + p.eps);
-  }
-  __syncthreads();
-}
-
 // Write U[part][t][k] = hilo(v) for one element.
 __device__ __forceinline__ void put_hilo(rsrc_t r, uint32_t u_off, int K, int t, int k, float v) {
   uint16_t hi, lo;
@@ -534,26 +615,26 @@ __device__ __noinline__ void phase_embed(const Params& p) {
 
 // Epilogue of phases whose output is y * inv_rms per slot row.
 #define EPI_SCALED_SINGLE                                                     \
-  [=](int g) {                                                                \
+  [=](int g, int rb) {                                                                \
     for (int e = threadIdx.x; e < TG * 16 * B; e += NT) {                     \
       int t = e % B, rr = (e / B) % 16, i = e / (B * 16);                     \
-      GSM.out[(2 * g + i) * 16 + rr][t] = GSM.y[i][rr][t] * GSM.inv[t];       \
+      GSM.out[(2 * g + i) * 16 + rr][t] = gy(rb, i, rr, t) * GSM.inv[t];       \
     }                                                                         \
   }
 // SwiGLU epilogue of a pair group: silu(inv*gate) * (inv*up) to the gate
 // slot's rows.
 #define EPI_SWIGLU                                                            \
-  [=](int g) {                                                                \
+  [=](int g, int rb) {                                                                \
     for (int e = threadIdx.x; e < 16 * B; e += NT) {                          \
       int t = e % B, rr = e / B;                                              \
-      float a = GSM.y[0][rr][t] * GSM.inv[t];                                 \
-      float u = GSM.y[1][rr][t] * GSM.inv[t];                                 \
+      float a = gy(rb, 0, rr, t) * GSM.inv[t];                                 \
+      float u = gy(rb, 1, rr, t) * GSM.inv[t];                                 \
       GSM.out[2 * g * 16 + rr][t] = silu(a) * u;                              \
     }                                                                         \
   }
 
 // --- QKV projection (GQA): raw q, k, v (RMS-normalised input) -> qkv[t][row]
-__device__ __noinline__ void phase_qkv(const Params& p, const LayerDesc& L) {
+__device__ __noinline__ void phase_qkv(const Params& p, const LayerDesc& L, int wait_idx) {
   const int B = p.B;
   SlotBuilder sb;
   if (threadIdx.x == 0) {
@@ -567,9 +648,11 @@ __device__ __noinline__ void phase_qkv(const Params& p, const LayerDesc& L) {
     sb.singles_of(mv);
   }
   builder_done(p, sb, -1);
-  load_inv_rms(p, GSM.inv, p.H, p.off_ssq);
+  GemvStream gs;
+  gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
+  wait_point(p, wait_idx);
   sub_stamp(p, 0);
-  run_gemv(p.ws, p.ws_bytes, p.off_zero, B, EPI_SCALED_SINGLE);
+  gemv_run(gs, p, p.H, p.off_ssq, EPI_SCALED_SINGLE);
   sub_stamp(p, 2);
   const int nqkv = (p.nq + 2 * p.nkv) * p.hd;
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
@@ -944,7 +1027,7 @@ __device__ __forceinline__ void phase_attn_gqa(const Params& p, const LayerDesc&
 //   u = S^T k;  S <- alpha S + beta k (v - u)^T;  o = S^T q (updated S).
 // Projection phase: q, k, v and the two gate logits per head, one GEMV
 // over five matrices; kda[t] = [q (nh*dk) | k (nh*dk) | v (nh*dv) | a (nh) | b (nh)].
-__device__ __noinline__ void phase_kda_proj(const Params& p, const LayerDesc& L) {
+__device__ __noinline__ void phase_kda_proj(const Params& p, const LayerDesc& L, int wait_idx) {
   const int B = p.B, nh = p.kda_h, dk = p.kda_dk, dv = p.kda_dv;
   const int width = 2 * nh * dk + nh * dv + 2 * nh;
   SlotBuilder sb;
@@ -963,9 +1046,11 @@ __device__ __noinline__ void phase_kda_proj(const Params& p, const LayerDesc& L)
     sb.singles_of(m4);
   }
   builder_done(p, sb, -1);
-  load_inv_rms(p, GSM.inv, p.H, p.off_ssq);
+  GemvStream gs;
+  gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
+  wait_point(p, wait_idx);
   sub_stamp(p, 0);
-  run_gemv(p.ws, p.ws_bytes, p.off_zero, B, EPI_SCALED_SINGLE);
+  gemv_run(gs, p, p.H, p.off_ssq, EPI_SCALED_SINGLE);
   sub_stamp(p, 2);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
@@ -1218,7 +1303,7 @@ constexpr int MLA_KL = 512, MLA_RD = 64, MLA_QA = MLA_KL + MLA_RD, MLA_KS = MLA_
 // M1: c_q0 = W_qa xn (q_lora) and ckv = W_kva xn (kv_lora + rope).  c_q0 goes
 // out as U = hilo(g_q * c_q0) plus its partial sums of squares (the q norm),
 // ckv as fp32.
-__device__ __noinline__ void phase_mla_a(const Params& p, const LayerDesc& L) {
+__device__ __noinline__ void phase_mla_a(const Params& p, const LayerDesc& L, int wait_idx) {
   const int B = p.B, QL = p.q_lora, KVR = MLA_QA;
   SlotBuilder sb;
   if (threadIdx.x == 0) {
@@ -1230,9 +1315,11 @@ __device__ __noinline__ void phase_mla_a(const Params& p, const LayerDesc& L) {
     sb.singles_of(mk);
   }
   builder_done(p, sb, -1);
-  load_inv_rms(p, GSM.inv, p.H, p.off_ssq);
+  GemvStream gs;
+  gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
+  wait_point(p, wait_idx);
   sub_stamp(p, 0);
-  run_gemv(p.ws, p.ws_bytes, p.off_zero, B, EPI_SCALED_SINGLE);
+  gemv_run(gs, p, p.H, p.off_ssq, EPI_SCALED_SINGLE);
   sub_stamp(p, 2);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   float* part = (float*)GSM.red;  // [NT][MAXB]
@@ -1286,10 +1373,9 @@ __device__ void mla_cache_row(const Params& p, const LayerDesc& L, int b) {
 
 // M2: q = W_qb RMSNorm(c_q0) (nh x (nope + rope)), and the new cache rows
 // (workgroup G-1-b writes sequence b's).
-__device__ __noinline__ void phase_mla_b(const Params& p, const LayerDesc& L) {
+__device__ __noinline__ void phase_mla_b(const Params& p, const LayerDesc& L, int wait_idx) {
   const int B = p.B, nh = p.mla_h, QW = p.nope + MLA_RD;
   const int cb = (int)gridDim.x - 1 - (int)blockIdx.x;
-  if (cb < B) mla_cache_row(p, L, cb);
   SlotBuilder sb;
   if (threadIdx.x == 0) {
     sb.start();
@@ -1298,9 +1384,12 @@ __device__ __noinline__ void phase_mla_b(const Params& p, const LayerDesc& L) {
     sb.singles_of(m);
   }
   builder_done(p, sb, -1);
-  load_inv_rms(p, GSM.inv, p.q_lora, p.off_ssq2);
+  GemvStream gs;
+  gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
+  wait_point(p, wait_idx);
+  if (cb < B) mla_cache_row(p, L, cb);
   sub_stamp(p, 0);
-  run_gemv(p.ws, p.ws_bytes, p.off_zero, B, EPI_SCALED_SINGLE);
+  gemv_run(gs, p, p.q_lora, p.off_ssq2, EPI_SCALED_SINGLE);
   sub_stamp(p, 2);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
@@ -1665,6 +1754,7 @@ constexpr size_t ROUTE_OFF =
     (cmax_(cmax_(sizeof(GemvSmem) + (size_t)1024 * MAXB * 4, sizeof(AttnSmem)), cmax_(sizeof(MlaSmem), sizeof(KdaSmem))) + 63) /
     64 * 64;
 #define RSM (*reinterpret_cast<RouteSmem*>(md_smem + ROUTE_OFF))
+static_assert(ROUTE_OFF + sizeof(RouteSmem) <= MD_SMEM_BYTES, "LDS layout exceeds the static LDS block");
 
 // --- residual-owning projections: x[t][r] += sum over the phase's matrices
 // of W . U (the O-projection; the dense down projection; the shared and
@@ -1673,7 +1763,7 @@ constexpr size_t ROUTE_OFF =
 // sum of squares of x.
 enum : int { RES_OPROJ = 0, RES_DENSE_DOWN = 1, RES_MOE_DOWN = 2, RES_MLA_O = 3, RES_KDA_O = 4 };
 
-__device__ __noinline__ void phase_residual(const Params& p, const LayerDesc& L, int mode, const uint16_t* g_next) {
+__device__ __noinline__ void phase_residual(const Params& p, const LayerDesc& L, int mode, const uint16_t* g_next, int wait_idx) {
   const int B = p.B, H = p.H;
   const RowSplit own = owned_rows(H, blockIdx.x, gridDim.x);
   const int nrow = own.r1 - own.r0;
@@ -1717,13 +1807,16 @@ __device__ __noinline__ void phase_residual(const Params& p, const LayerDesc& L,
     if (t == 0) GSM.gain[lr] = bf16_f32(g_next[own.r0 + lr]);
   }
   __syncthreads();
+  GemvStream gs;
+  gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
+  wait_point(p, wait_idx);
   sub_stamp(p, 0);
   const int r0 = own.r0;
-  run_gemv(p.ws, p.ws_bytes, p.off_zero, B, [=](int g) {
+  gemv_run(gs, p, 0, 0u, [=](int g, int rb) {
     for (int e = threadIdx.x; e < TG * 16 * B; e += NT) {
       int t = e % B, rr = (e / B) % 16, i = e / (B * 16);
       int m, row;
-      if (slot_row(2 * g + i, rr, m, row)) GSM.out[row - r0][t] += GSM.y[i][rr][t];
+      if (slot_row(2 * g + i, rr, m, row)) GSM.out[row - r0][t] += gy(rb, i, rr, t);
     }
   });
   sub_stamp(p, 2);
@@ -1742,7 +1835,7 @@ __device__ __noinline__ void phase_residual(const Params& p, const LayerDesc& L,
 }
 
 // --- dense SwiGLU gate/up: h = silu(inv*Wg U) * (inv*Wu U) -> hi/lo
-__device__ __noinline__ void phase_gateup(const Params& p, const LayerDesc& L) {
+__device__ __noinline__ void phase_gateup(const Params& p, const LayerDesc& L, int wait_idx) {
   const int B = p.B, F = p.ffn;
   SlotBuilder sb;
   if (threadIdx.x == 0) {
@@ -1753,9 +1846,11 @@ __device__ __noinline__ void phase_gateup(const Params& p, const LayerDesc& L) {
     sb.pairs_of(mg, mu);
   }
   builder_done(p, sb, -1);
-  load_inv_rms(p, GSM.inv, p.H, p.off_ssq);
+  GemvStream gs;
+  gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
+  wait_point(p, wait_idx);
   sub_stamp(p, 0);
-  run_gemv(p.ws, p.ws_bytes, p.off_zero, B, EPI_SWIGLU);
+  gemv_run(gs, p, p.H, p.off_ssq, EPI_SWIGLU);
   sub_stamp(p, 2);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
@@ -1779,7 +1874,7 @@ __device__ __noinline__ void phase_gateup(const Params& p, const LayerDesc& L) {
 // run as one residual phase.
 
 
-__device__ __noinline__ void phase_moe_a(const Params& p, const LayerDesc& L) {
+__device__ __noinline__ void phase_moe_a(const Params& p, const LayerDesc& L, int wait_idx) {
   const int B = p.B;
   SlotBuilder sb;
   if (threadIdx.x == 0) {
@@ -1795,20 +1890,22 @@ __device__ __noinline__ void phase_moe_a(const Params& p, const LayerDesc& L) {
     sb.singles_of(mr);
   }
   builder_done(p, sb, -1);
-  load_inv_rms(p, GSM.inv, p.H, p.off_ssq);
+  GemvStream gs;
+  gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
+  wait_point(p, wait_idx);
   sub_stamp(p, 0);
-  run_gemv(p.ws, p.ws_bytes, p.off_zero, B, [=](int g) {
+  gemv_run(gs, p, p.H, p.off_ssq, [=](int g, int rb) {
     if (GSM.grp[g].kind == GK_PAIR) {
       for (int e = threadIdx.x; e < 16 * B; e += NT) {
         int t = e % B, rr = e / B;
-        float a = GSM.y[0][rr][t] * GSM.inv[t];
-        float u = GSM.y[1][rr][t] * GSM.inv[t];
+        float a = gy(rb, 0, rr, t) * GSM.inv[t];
+        float u = gy(rb, 1, rr, t) * GSM.inv[t];
         GSM.out[2 * g * 16 + rr][t] = silu(a) * u;
       }
     } else {
       for (int e = threadIdx.x; e < TG * 16 * B; e += NT) {
         int t = e % B, rr = (e / B) % 16, i = e / (B * 16);
-        GSM.out[(2 * g + i) * 16 + rr][t] = GSM.y[i][rr][t] * GSM.inv[t];
+        GSM.out[(2 * g + i) * 16 + rr][t] = gy(rb, i, rr, t) * GSM.inv[t];
       }
     }
   });
@@ -1878,7 +1975,7 @@ __device__ __noinline__ void compute_routes(const Params& p, int layer) {
   __syncthreads();
 }
 
-__device__ __noinline__ void phase_moe_b(const Params& p, const LayerDesc& L) {
+__device__ __noinline__ void phase_moe_b(const Params& p, const LayerDesc& L, int wait_idx) {
   const int B = p.B;
   SlotBuilder sb;
   if (threadIdx.x == 0) {
@@ -1892,9 +1989,11 @@ __device__ __noinline__ void phase_moe_b(const Params& p, const LayerDesc& L) {
     }
   }
   builder_done(p, sb, -1);
-  load_inv_rms(p, GSM.inv, p.H, p.off_ssq);
+  GemvStream gs;
+  gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
+  wait_point(p, wait_idx);
   sub_stamp(p, 0);
-  run_gemv(p.ws, p.ws_bytes, p.off_zero, B, EPI_SWIGLU);
+  gemv_run(gs, p, p.H, p.off_ssq, EPI_SWIGLU);
   sub_stamp(p, 2);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
@@ -1908,7 +2007,7 @@ __device__ __noinline__ void phase_moe_b(const Params& p, const LayerDesc& L) {
 }
 
 // --- final norm + LM head: logits, per-WG argmax candidates
-__device__ __noinline__ void phase_lmhead(const Params& p) {
+__device__ __noinline__ void phase_lmhead(const Params& p, int wait_idx) {
   const int B = p.B;
   SlotBuilder sb;
   if (threadIdx.x == 0) {
@@ -1918,9 +2017,11 @@ __device__ __noinline__ void phase_lmhead(const Params& p) {
     sb.singles_of(m);
   }
   builder_done(p, sb, -1);
-  load_inv_rms(p, GSM.inv, p.H, p.off_ssq);
+  GemvStream gs;
+  gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
+  wait_point(p, wait_idx);
   sub_stamp(p, 0);
-  run_gemv(p.ws, p.ws_bytes, p.off_zero, B, EPI_SCALED_SINGLE);
+  gemv_run(gs, p, p.H, p.off_ssq, EPI_SCALED_SINGLE);
   sub_stamp(p, 2);
   static_assert(sizeof(GemvSmem::in) >= 2 * sizeof(float) * NT * MAXB, "argmax scratch reuses the input staging");
   float* bv = &GSM.in[0][0];             // [NT][MAXB] best value (the input staging is unused here)
@@ -1976,86 +2077,12 @@ __device__ __noinline__ void final_argmax(const Params& p) {
   }
 }
 
-// ===================================================================== kernel
-extern "C" __global__ __launch_bounds__(NT) void md_megakernel(Params p) {
-  if (p.B < 1 || p.B > MAXB) return;
-  if (p.trace && threadIdx.x == 0 && p.trace_n > 0) p.trace[(size_t)blockIdx.x * p.trace_n + p.trace_n - 1] = wall_clock64();
-  clear_next_bank(p);
-  int sidx = 0;
-  if (threadIdx.x == 0) md_cur_phase = 0;
-  phase_embed(p);
-  grid_sync(p, sidx);
-  for (int l = 0; l < p.n_layers; ++l) {
-    const LayerDesc& L = p.layers[l];
-    const uint16_t* g_next = (l + 1 < p.n_layers) ? p.layers[l + 1].attn_norm : p.final_norm;
-    const int kind = L.kind;
-    if (kind == LK_GQA) {
-      phase_qkv(p, L);
-      grid_sync(p, sidx);
-      if (p.verify) {
-        phase_gqa_kv_write(p, L);
-        grid_sync(p, sidx);
-      }
-      phase_attn_gqa(p, L, l);
-      grid_sync(p, sidx);
-      phase_residual(p, L, RES_OPROJ, L.ffn_norm);
-      grid_sync(p, sidx);
-    } else if (kind == LK_KDA) {
-      phase_kda_proj(p, L);
-      grid_sync(p, sidx);
-      if (p.verify) phase_kda_rec_verify(p, L);
-      else phase_kda_rec(p, L);
-      grid_sync(p, sidx);
-      phase_residual(p, L, RES_KDA_O, L.ffn_norm);
-      grid_sync(p, sidx);
-    } else {
-      phase_mla_a(p, L);
-      grid_sync(p, sidx);
-      phase_mla_b(p, L);
-      grid_sync(p, sidx);
-      phase_mla_absorb(p, L);
-      grid_sync(p, sidx);
-      phase_mla_attn(p, L);
-      grid_sync(p, sidx);
-      phase_mla_out(p, L);
-      grid_sync(p, sidx);
-      phase_residual(p, L, RES_MLA_O, L.ffn_norm);
-      grid_sync(p, sidx);
-    }
-    if (p.n_experts == 0) {
-      phase_gateup(p, L);
-      grid_sync(p, sidx);
-      phase_residual(p, L, RES_DENSE_DOWN, g_next);
-      grid_sync(p, sidx);
-    } else {
-      phase_moe_a(p, L);
-      grid_sync(p, sidx);
-      compute_routes(p, l);
-      phase_moe_b(p, L);
-      grid_sync(p, sidx);
-      phase_residual(p, L, RES_MOE_DOWN, g_next);
-      grid_sync(p, sidx);
-    }
-    if (dev_failed(p)) return;
-  }
-  phase_lmhead(p);
-  if (p.verify) {
-    grid_sync(p, sidx);
-    verify_finish(p);
-    return;
-  }
-  // the last workgroup to arrive reduces the argmax candidates
-  bool last = arrive(p, sidx);
-  if (threadIdx.x == 0) ((int*)md_smem)[0] = last;
-  __syncthreads();
-  if (((int*)md_smem)[0]) final_argmax(p);
-}
-
-
 // ===================================================================== multi-launch
 // The same step as one kernel launch per phase (the kernel boundary is the
 // barrier): the baseline whose inter-kernel gaps the megakernel removes.
-// Every phase runs the megakernel's own device code on the same grid, so the
+// Every launch is md_megakernel itself in its one-phase mode (a second kernel
+// calling the same phase functions would make every LDS access in them go
+// through a per-kernel address table in memory), on the same grid, so the
 // results are identical.  LDS does not survive a launch, so the routed
 // experts' down projection recomputes the routing (same data, same result).
 enum : int {
@@ -2064,36 +2091,130 @@ enum : int {
   PH_LMHEAD, PH_ARGMAX
 };
 
-extern "C" __global__ __launch_bounds__(NT) void md_phase_kernel(Params p, int layer, int phase) {
-  if (p.B < 1 || p.B > MAXB) return;
-  if (threadIdx.x == 0) md_cur_phase = 0;
+__device__ __forceinline__ void run_one_phase(const Params& p, int layer, int phase) {
   const int l = layer < 0 ? 0 : layer;
   const LayerDesc& L = p.layers[l];
   const uint16_t* g_next = (l + 1 < p.n_layers) ? p.layers[l + 1].attn_norm : p.final_norm;
   switch (phase) {
     case PH_EMBED: clear_next_bank(p); phase_embed(p); break;
-    case PH_QKV: phase_qkv(p, L); break;
+    case PH_QKV: phase_qkv(p, L, -1); break;
     case PH_KV_WRITE: phase_gqa_kv_write(p, L); break;
     case PH_ATTN: phase_attn_gqa(p, L, l); break;
-    case PH_OPROJ: phase_residual(p, L, RES_OPROJ, L.ffn_norm); break;
-    case PH_GATEUP: phase_gateup(p, L); break;
-    case PH_DOWN: phase_residual(p, L, RES_DENSE_DOWN, g_next); break;
-    case PH_MOE_A: phase_moe_a(p, L); break;
-    case PH_MOE_B: compute_routes(p, l); phase_moe_b(p, L); break;
-    case PH_MOE_C: compute_routes(p, l); phase_residual(p, L, RES_MOE_DOWN, g_next); break;
-    case PH_KDA_PROJ: phase_kda_proj(p, L); break;
+    case PH_OPROJ: phase_residual(p, L, RES_OPROJ, L.ffn_norm, -1); break;
+    case PH_GATEUP: phase_gateup(p, L, -1); break;
+    case PH_DOWN: phase_residual(p, L, RES_DENSE_DOWN, g_next, -1); break;
+    case PH_MOE_A: phase_moe_a(p, L, -1); break;
+    case PH_MOE_B: compute_routes(p, l); phase_moe_b(p, L, -1); break;
+    case PH_MOE_C: compute_routes(p, l); phase_residual(p, L, RES_MOE_DOWN, g_next, -1); break;
+    case PH_KDA_PROJ: phase_kda_proj(p, L, -1); break;
     case PH_KDA_REC: phase_kda_rec(p, L); break;
-    case PH_KDA_O: phase_residual(p, L, RES_KDA_O, L.ffn_norm); break;
-    case PH_MLA_A: phase_mla_a(p, L); break;
-    case PH_MLA_B: phase_mla_b(p, L); break;
+    case PH_KDA_O: phase_residual(p, L, RES_KDA_O, L.ffn_norm, -1); break;
+    case PH_MLA_A: phase_mla_a(p, L, -1); break;
+    case PH_MLA_B: phase_mla_b(p, L, -1); break;
     case PH_MLA_ABS: phase_mla_absorb(p, L); break;
     case PH_MLA_ATTN: phase_mla_attn(p, L); break;
     case PH_MLA_OUT: phase_mla_out(p, L); break;
-    case PH_MLA_O: phase_residual(p, L, RES_MLA_O, L.ffn_norm); break;
-    case PH_LMHEAD: phase_lmhead(p); break;
+    case PH_MLA_O: phase_residual(p, L, RES_MLA_O, L.ffn_norm, -1); break;
+    case PH_LMHEAD: phase_lmhead(p, -1); break;
     case PH_ARGMAX: if (blockIdx.x == 0) final_argmax(p); break;
     default: break;
   }
+}
+
+// ===================================================================== kernel
+extern "C" __global__ __launch_bounds__(NT) void md_megakernel(Params p) {
+  if (p.B < 1 || p.B > MAXB) return;
+  if (p.ml_phase >= 0) {  // one phase of the multi-launch step
+    if (threadIdx.x == 0) md_cur_phase = 0;
+    run_one_phase(p, p.ml_layer, p.ml_phase);
+    return;
+  }
+  if (p.trace && threadIdx.x == 0 && p.trace_n > 0) p.trace[(size_t)blockIdx.x * p.trace_n + p.trace_n - 1] = wall_clock64();
+  clear_next_bank(p);
+  int sidx = 0;
+  if (threadIdx.x == 0) md_cur_phase = 0;
+  // Every sync point s is split: grid_arrive(s) when this workgroup's share
+  // is done; the next phase waits for s itself -- a weight-streaming phase
+  // after issuing its first weight loads (they depend on nobody), any other
+  // phase first thing (WAIT).
+#define WAIT() wait_point(p, sidx++)
+#define ARRIVE() grid_arrive(p, sidx)
+  phase_embed(p);
+  ARRIVE();
+  for (int l = 0; l < p.n_layers; ++l) {
+    const LayerDesc& L = p.layers[l];
+    const uint16_t* g_next = (l + 1 < p.n_layers) ? p.layers[l + 1].attn_norm : p.final_norm;
+    const int kind = L.kind;
+    if (kind == LK_GQA) {
+      phase_qkv(p, L, sidx++);
+      ARRIVE();
+      if (p.verify) {
+        WAIT();
+        phase_gqa_kv_write(p, L);
+        ARRIVE();
+      }
+      WAIT();
+      phase_attn_gqa(p, L, l);
+      ARRIVE();
+      phase_residual(p, L, RES_OPROJ, L.ffn_norm, sidx++);
+      ARRIVE();
+    } else if (kind == LK_KDA) {
+      phase_kda_proj(p, L, sidx++);
+      ARRIVE();
+      WAIT();
+      if (p.verify) phase_kda_rec_verify(p, L);
+      else phase_kda_rec(p, L);
+      ARRIVE();
+      phase_residual(p, L, RES_KDA_O, L.ffn_norm, sidx++);
+      ARRIVE();
+    } else {
+      phase_mla_a(p, L, sidx++);
+      ARRIVE();
+      phase_mla_b(p, L, sidx++);
+      ARRIVE();
+      WAIT();
+      phase_mla_absorb(p, L);
+      ARRIVE();
+      WAIT();
+      phase_mla_attn(p, L);
+      ARRIVE();
+      WAIT();
+      phase_mla_out(p, L);
+      ARRIVE();
+      phase_residual(p, L, RES_MLA_O, L.ffn_norm, sidx++);
+      ARRIVE();
+    }
+    if (p.n_experts == 0) {
+      phase_gateup(p, L, sidx++);
+      ARRIVE();
+      phase_residual(p, L, RES_DENSE_DOWN, g_next, sidx++);
+      ARRIVE();
+    } else {
+      phase_moe_a(p, L, sidx++);
+      ARRIVE();
+      WAIT();
+      compute_routes(p, l);
+      phase_moe_b(p, L, -1);
+      ARRIVE();
+      phase_residual(p, L, RES_MOE_DOWN, g_next, sidx++);
+      ARRIVE();
+    }
+    if (dev_failed(p)) return;
+  }
+  phase_lmhead(p, sidx++);
+  if (p.verify) {
+    ARRIVE();
+    WAIT();
+    verify_finish(p);
+    return;
+  }
+#undef WAIT
+#undef ARRIVE
+  // the last workgroup to arrive reduces the argmax candidates
+  bool last = arrive(p, sidx);
+  if (threadIdx.x == 0) ((int*)md_smem)[0] = last;
+  __syncthreads();
+  if (((int*)md_smem)[0]) final_argmax(p);
 }
 
 }  // namespace md
@@ -2132,7 +2253,7 @@ hipError_t launch_pack(const void* src, void* dst, int64_t rows, int64_t cols, h
 
 // LDS: the larger of the GEMV block (+ partial-sum staging of up to 1024
 // workgroups) and the attention block, then the routing state.
-size_t megakernel_smem_bytes() { return ROUTE_OFF + sizeof(RouteSmem); }
+size_t megakernel_smem_bytes() { return 0; }  // all LDS is static (md_smem)
 
 hipError_t launch_megakernel(const Params& p, int grid, hipStream_t stream) {
   void* args[] = {(void*)&p};
@@ -2143,10 +2264,11 @@ hipError_t launch_megakernel(const Params& p, int grid, hipStream_t stream) {
 // One decode step as a sequence of phase launches on `stream`.
 hipError_t launch_multilaunch(const Params& p, const int* kinds, int grid, hipStream_t stream) {
   const unsigned smem = (unsigned)megakernel_smem_bytes();
-  hipError_t e = hipFuncSetAttribute((const void*)md_phase_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  if (e != hipSuccess) return e;
+  Params q = p;
   auto go = [&](int layer, int phase, int g) {
-    hipLaunchKernelGGL(md_phase_kernel, dim3(g), dim3(NT), smem, stream, p, layer, phase);
+    q.ml_layer = layer;
+    q.ml_phase = phase;
+    hipLaunchKernelGGL(md_megakernel, dim3(g), dim3(NT), smem, stream, q);
   };
   go(-1, PH_EMBED, grid);
   for (int l = 0; l < p.n_layers; ++l) {

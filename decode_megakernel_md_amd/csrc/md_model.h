@@ -47,6 +47,8 @@ struct Params {
   // step
   int B;              // token rows: sequences (decode) or the verified tokens of one sequence
   int verify;         // 1: rows are tokens p..p+B-1 of sequence 0
+  int ml_phase;       // >= 0: run only this phase (multi-launch step), of layer ml_layer
+  int ml_layer;
   uint8_t* kda_ring;  // verify: per delta-rule layer, the state after each row fp32[L_kda][MAXB][nh][dk][dv]
   int32_t* out_accept;
   int32_t* out_next;

@@ -181,7 +181,7 @@ __shared__ __attribute__((aligned(16))) char md_smem[MD_SMEM_BYTES];
 
 constexpr int CMAX_DEV = 256;    // largest chunk count per (sequence, kv head)
 constexpr int TG = 2;            // slots per group (share one B operand load)
-constexpr int GDS = 12;          // k-steps in flight per wave
+constexpr int GDS = 8;          // k-steps in flight per wave
 constexpr int MAXSLOT = 96;      // slots per workgroup and phase
 constexpr int MAXGRP = MAXSLOT / TG;
 constexpr int MAXMAT = 72;       // matrices per phase
@@ -684,10 +684,9 @@ __device__ __forceinline__ void rope_cs(const Params& p, int pos, int i, float& 
 struct AttnSmem {
   float q[MAXB][128];           // rotated, scaled q of the group's heads
   float s[NW][32][MAXB];        // per-wave scores / probabilities of a block
-  float wm[NW][MAXB], wl[NW][MAXB];
+  float wm[NW + 1][MAXB], wl[NW + 1][MAXB];  // entry NW: the new row (decode, last chunk)
   float wo[NW][MAXB][128];
-  float cw[MAXB][CMAX_DEV];     // combine weights
-  float cl[MAXB];
+  float knew[128], vnew[128];   // the new row, as the cache stores it
   int last;
 };
 
@@ -721,11 +720,12 @@ __device__ __forceinline__ void load_block(KVBlock<HD>& r, rsrc_t krs, rsrc_t vr
 
 #define ASM (*reinterpret_cast<AttnSmem*>(md_smem))
 
+// The wave's blocks ba (positions w0..) and bb (w0 + 32..) are already in
+// flight when it is called; each block used is refilled two blocks ahead.
 template <int HD, int GS, int CP>
-__device__ __forceinline__ void attn_task_wave(const uint16_t* kc, const uint16_t* vc, uint32_t nbytes, int w0, int w1) {
+__device__ __forceinline__ void attn_task_wave(rsrc_t krs, rsrc_t vrs, int w0, int w1) {
   constexpr int gs = GS;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const rsrc_t krs = make_rsrc_u(kc, nbytes), vrs = make_rsrc_u(vc, nbytes);
   w0 = __builtin_amdgcn_readfirstlane(w0);
   w1 = __builtin_amdgcn_readfirstlane(w1);
   const int nn = lane & 15, hh = nn >> 1, pp = nn & 1;
@@ -809,12 +809,14 @@ __device__ __forceinline__ void attn_task_wave(const uint16_t* kc, const uint16_
   };
   KVBlock<HD> ba, bb;
   load_block<HD, CP>(ba, krs, vrs, w0, w1, lane);
+  load_block<HD, CP>(bb, krs, vrs, w0 + 32, w1, lane);
   for (int blk = w0; blk < w1; blk += 64) {
-    load_block<HD, CP>(bb, krs, vrs, blk + 32, w1, lane);
     block(ba, blk);
     if (blk + 32 >= w1) break;
     load_block<HD, CP>(ba, krs, vrs, blk + 64, w1, lane);
     block(bb, blk + 32);
+    if (blk + 64 >= w1) break;
+    load_block<HD, CP>(bb, krs, vrs, blk + 96, w1, lane);
   }
   // sum the lane groups that hold the same dims (different rows)
 #pragma unroll
@@ -836,16 +838,16 @@ __device__ __forceinline__ void attn_task_wave(const uint16_t* kc, const uint16_
 }
 
 template <int HD, int CP>
-__device__ __forceinline__ void attn_dispatch(int gs, const uint16_t* kc, const uint16_t* vc, uint32_t nb, int w0, int w1) {
+__device__ __forceinline__ void attn_dispatch(int gs, rsrc_t krs, rsrc_t vrs, int w0, int w1) {
   switch (gs) {
-    case 1: attn_task_wave<HD, 1, CP>(kc, vc, nb, w0, w1); break;
-    case 2: attn_task_wave<HD, 2, CP>(kc, vc, nb, w0, w1); break;
-    case 3: attn_task_wave<HD, 3, CP>(kc, vc, nb, w0, w1); break;
-    case 4: attn_task_wave<HD, 4, CP>(kc, vc, nb, w0, w1); break;
-    case 5: attn_task_wave<HD, 5, CP>(kc, vc, nb, w0, w1); break;
-    case 6: attn_task_wave<HD, 6, CP>(kc, vc, nb, w0, w1); break;
-    case 7: attn_task_wave<HD, 7, CP>(kc, vc, nb, w0, w1); break;
-    default: attn_task_wave<HD, 8, CP>(kc, vc, nb, w0, w1); break;
+    case 1: attn_task_wave<HD, 1, CP>(krs, vrs, w0, w1); break;
+    case 2: attn_task_wave<HD, 2, CP>(krs, vrs, w0, w1); break;
+    case 3: attn_task_wave<HD, 3, CP>(krs, vrs, w0, w1); break;
+    case 4: attn_task_wave<HD, 4, CP>(krs, vrs, w0, w1); break;
+    case 5: attn_task_wave<HD, 5, CP>(krs, vrs, w0, w1); break;
+    case 6: attn_task_wave<HD, 6, CP>(krs, vrs, w0, w1); break;
+    case 7: attn_task_wave<HD, 7, CP>(krs, vrs, w0, w1); break;
+    default: attn_task_wave<HD, 8, CP>(krs, vrs, w0, w1); break;
   }
 }
 
@@ -877,85 +879,130 @@ __device__ __noinline__ void phase_gqa_kv_write(const Params& p, const LayerDesc
   }
 }
 
-// Inlined into the kernels, as is the per-wave worker above: as a called
-// function it would save and restore the callee-saved registers its
-// hundreds of live values occupy, on every call.
-__device__ __forceinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L, int layer) {
+// One task of the GQA attention phase: (sequence b, kv head g, chunk c) of
+// the cached rows, and this wave's share [w0, w1) of the chunk.  Decode: the
+// cached rows are 0..pos-1 (the new row is folded in by the combine); verify:
+// 0..pos (the new rows were written by phase_gqa_kv_write).
+struct AttnTask {
+  int b, g, c, pos, n, a0, a1, w0, w1;
+  const uint16_t* kc;
+  const uint16_t* vc;
+};
+__device__ __forceinline__ AttnTask attn_task(const Params& p, const LayerDesc& L, int task) {
+  AttnTask t;
+  const int C = p.attn_chunks, hd = p.hd;
+  t.c = task % C;
+  t.g = (task / C) % p.nkv;
+  t.b = task / (C * p.nkv);
+  t.pos = row_pos(p, t.b);
+  t.n = p.verify ? t.pos + 1 : t.pos;
+  const int P = (t.n + C - 1) / C;
+  t.a0 = t.c * P < t.n ? t.c * P : t.n;
+  t.a1 = (t.c + 1) * P < t.n ? (t.c + 1) * P : t.n;
+  const int wv = threadIdx.x >> 6, len = t.a1 - t.a0;
+  t.w0 = t.a0 + len * wv / NW;
+  t.w1 = t.a0 + len * (wv + 1) / NW;
+  t.kc = (const uint16_t*)(p.kv + L.kv_off) + (size_t)(row_seq(p, t.b) * p.nkv + t.g) * p.max_ctx * hd;
+  t.vc = t.kc + (size_t)p.max_batch * p.nkv * p.max_ctx * hd;
+  return t;
+}
+
+// GQA decode attention.  Each task's partial (max, sum, o) per head goes to
+// the workspace; when decoding, the task of the last chunk also folds in the
+// new row, computed in place (q . k_new, v_new) rather than read back from
+// the cache it writes.  The last workgroup to finish a (b, g) combines the
+// chunks with one round of loads (a running max over the chunks).  Inlined
+// into the kernel, as is the per-wave worker: as a called function it would
+// save and restore the callee-saved registers its live values occupy.
+template <int HD>
+__device__ __forceinline__ void attn_phase(const Params& p, const LayerDesc& L, int layer, int wait_idx) {
   AttnSmem& sm = *(AttnSmem*)md_smem;
-  const int wv = threadIdx.x >> 6;
-  const int hd = p.hd, gs = p.nq / p.nkv, B = p.B;
+  const int lane = threadIdx.x & 63;
+  const int gs = p.nq / p.nkv, B = p.B;
   const int C = p.attn_chunks;
   const int ntask = B * p.nkv * C;
-  const int nqkv = (p.nq + 2 * p.nkv) * hd;
+  const int nqkv = (p.nq + 2 * p.nkv) * HD;
   rsrc_t wr = make_rsrc_u(p.ws, p.ws_bytes);
-  const float scale = 1.0f / sqrtf((float)hd);
+  const float scale = 1.0f / sqrtf((float)HD);
+  wait_point(p, wait_idx);
   for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
-    const int c = task % C, g = (task / C) % p.nkv, b = task / (C * p.nkv);
-    const int pos = row_pos(p, b);
-    const int n = pos + 1;
-    const int P = (n + C - 1) / C;
-    const int a0 = c * P < n ? c * P : n, a1 = (c + 1) * P < n ? (c + 1) * P : n;
-    uint16_t* kc = (uint16_t*)(p.kv + L.kv_off) + (size_t)(row_seq(p, b) * p.nkv + g) * p.max_ctx * hd;
-    uint16_t* vc = kc + (size_t)p.max_batch * p.nkv * p.max_ctx * hd;
-    for (int e = threadIdx.x; e < gs * (hd / 2); e += NT) {
-      int h = e / (hd / 2), i = e % (hd / 2);
-      int col = (g * gs + h) * hd;
+    const AttnTask t = attn_task(p, L, task);
+    const int b = t.b, g = t.g, c = t.c, pos = t.pos;
+    const uint32_t nb = (uint32_t)((size_t)t.n * HD * 2);
+    rsrc_t krs = make_rsrc_u(t.kc, nb), vrs = make_rsrc_u(t.vc, nb);
+    for (int e = threadIdx.x; e < gs * (HD / 2); e += NT) {
+      int h = e / (HD / 2), i = e % (HD / 2);
+      int col = (g * gs + h) * HD;
       float a = ld_f32(wr, p.off_qkv + (uint32_t)(b * nqkv + col + i) * 4u);
-      float bb = ld_f32(wr, p.off_qkv + (uint32_t)(b * nqkv + col + i + hd / 2) * 4u);
+      float bq = ld_f32(wr, p.off_qkv + (uint32_t)(b * nqkv + col + i + HD / 2) * 4u);
       float cs, sn;
       rope_cs(p, pos, i, cs, sn);
-      sm.q[h][i] = (a * cs - bb * sn) * scale;
-      sm.q[h][i + hd / 2] = (a * sn + bb * cs) * scale;
+      sm.q[h][i] = (a * cs - bq * sn) * scale;
+      sm.q[h][i + HD / 2] = (a * sn + bq * cs) * scale;
     }
-    if (!p.verify && a0 <= pos && pos < a1) {  // (verify: rows written by phase_gqa_kv_write)
-      for (int i = threadIdx.x; i < hd / 2; i += NT) {
-        int colk = p.nq * hd + g * hd;
+    // decode: the task of the last chunk folds the new row into its partial
+    // (and writes it to the cache; nothing reads it back in this step)
+    const bool newrow = !p.verify && c == C - 1;
+    if (newrow) {
+      uint16_t* kc = const_cast<uint16_t*>(t.kc);
+      uint16_t* vc = const_cast<uint16_t*>(t.vc);
+      for (int i = threadIdx.x; i < HD / 2; i += NT) {
+        int colk = p.nq * HD + g * HD;
         float a = ld_f32(wr, p.off_qkv + (uint32_t)(b * nqkv + colk + i) * 4u);
-        float bb = ld_f32(wr, p.off_qkv + (uint32_t)(b * nqkv + colk + i + hd / 2) * 4u);
+        float bk = ld_f32(wr, p.off_qkv + (uint32_t)(b * nqkv + colk + i + HD / 2) * 4u);
         float cs, sn;
         rope_cs(p, pos, i, cs, sn);
-        kc[(size_t)pos * hd + i] = bf16_rne(a * cs - bb * sn);
-        kc[(size_t)pos * hd + i + hd / 2] = bf16_rne(a * sn + bb * cs);
+        uint16_t k0 = bf16_rne(a * cs - bk * sn), k1 = bf16_rne(a * sn + bk * cs);
+        kc[(size_t)pos * HD + i] = k0;
+        kc[(size_t)pos * HD + i + HD / 2] = k1;
+        sm.knew[i] = bf16_f32(k0);
+        sm.knew[i + HD / 2] = bf16_f32(k1);
       }
-      for (int i = threadIdx.x; i < hd; i += NT) {
-        int colv = (p.nq + p.nkv) * hd + g * hd;
-        vc[(size_t)pos * hd + i] = bf16_rne(ld_f32(wr, p.off_qkv + (uint32_t)(b * nqkv + colv + i) * 4u));
+      for (int i = threadIdx.x; i < HD; i += NT) {
+        int colv = (p.nq + p.nkv) * HD + g * HD;
+        uint16_t v0 = bf16_rne(ld_f32(wr, p.off_qkv + (uint32_t)(b * nqkv + colv + i) * 4u));
+        vc[(size_t)pos * HD + i] = v0;
+        sm.vnew[i] = bf16_f32(v0);
       }
-      wait_stores();
     }
     __syncthreads();
-    sub_stamp(p, 0);
-    const int len = a1 - a0;
-    const int wq = ((len + NW - 1) / NW + 31) / 32 * 32;
-    const int w0 = a0 + wv * wq < a1 ? a0 + wv * wq : a1;
-    const int w1 = w0 + wq < a1 ? w0 + wq : a1;
-    const uint32_t nb = (uint32_t)((size_t)n * hd * 2);
-    if (p.verify) {
-      if (hd == 128) attn_dispatch<128, CP_SC1>(gs, kc, vc, nb, w0, w1);
-      else attn_dispatch<64, CP_SC1>(gs, kc, vc, nb, w0, w1);
-    } else {
-      if (hd == 128) attn_dispatch<128, 0>(gs, kc, vc, nb, w0, w1);
-      else attn_dispatch<64, 0>(gs, kc, vc, nb, w0, w1);
+    if (newrow) {  // q_h . k_new, one head per wave at a time
+      const int ln = threadIdx.x & 63;
+      for (int h = threadIdx.x >> 6; h < gs; h += NW) {
+        float sp = 0.f;
+        for (int d = ln; d < HD; d += 64) sp += sm.q[h][d] * sm.knew[d];
+        sp = wave_sum(sp);
+        if (ln == 0) { sm.wm[NW][h] = sp; sm.wl[NW][h] = 1.f; }
+      }
     }
+    sub_stamp(p, 0);
+    if (p.verify) attn_dispatch<HD, CP_SC1>(gs, krs, vrs, t.w0, t.w1);
+    else attn_dispatch<HD, 0>(gs, krs, vrs, t.w0, t.w1);
     __syncthreads();
     sub_stamp(p, 3);
-    // this task's partial: m, l in part_ml[b][head][c]; o in part_o[b][head][c][hd]
-    for (int e = threadIdx.x; e < gs * hd; e += NT) {
-      int h = e / hd, d = e % hd;
+    // this task's partial: (m, l) in part_ml[b][head][c]; o in part_o[b][head][c][hd]
+    for (int e = threadIdx.x; e < gs * HD; e += NT) {
+      int h = e / HD, d = e % HD;
       float M = -INFINITY;
       for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.wm[w][h]);
+      if (newrow) M = fmaxf(M, sm.wm[NW][h]);
       float o = 0.f, l = 0.f;
       for (int w = 0; w < NW; ++w) {
         float f = sm.wm[w][h] == -INFINITY ? 0.f : __expf(sm.wm[w][h] - M);
         o += f * sm.wo[w][h][d];
         l += f * sm.wl[w][h];
       }
+      if (newrow) {
+        float f = __expf(sm.wm[NW][h] - M);
+        o += f * sm.vnew[d];
+        l += f;
+      }
       uint32_t head = (uint32_t)((b * p.nq + g * gs + h) * C + c);
       if (d == 0) {
         st_f32(wr, p.off_attn_ml + head * 8u, M);
         st_f32(wr, p.off_attn_ml + head * 8u + 4u, l);
       }
-      st_f32(wr, p.off_attn + (head * (uint32_t)hd + d) * 4u, o);
+      st_f32(wr, p.off_attn + (head * (uint32_t)HD + d) * 4u, o);
     }
     wait_stores();
     __syncthreads();
@@ -967,57 +1014,51 @@ __device__ __forceinline__ void phase_attn_gqa(const Params& p, const LayerDesc&
     }
     __syncthreads();
     if (sm.last) {
-      // combine weights per head: w_c = exp(m_c - M), 1 / sum_c w_c l_c
-      for (int e = threadIdx.x; e < gs * C; e += NT) {
-        int h = e / C, cc = e % C;
-        uint32_t hb = (uint32_t)((b * p.nq + g * gs + h) * C);
-        sm.cw[h][cc] = ld_f32(wr, p.off_attn_ml + (hb + cc) * 8u);
-      }
-      __syncthreads();
-      if (threadIdx.x < gs) {
-        int h = threadIdx.x;
-        uint32_t hb = (uint32_t)((b * p.nq + g * gs + h) * C);
-        float M = -INFINITY;
-        for (int cc = 0; cc < C; ++cc) M = fmaxf(M, sm.cw[h][cc]);
-        float den = 0.f;
-        for (int cc = 0; cc < C; ++cc) {
-          float f = sm.cw[h][cc] == -INFINITY ? 0.f : __expf(sm.cw[h][cc] - M);
-          sm.cw[h][cc] = f;
-          den += f * ld_f32(wr, p.off_attn_ml + (hb + cc) * 8u + 4u);
-        }
-        sm.cl[h] = 1.0f / den;
-      }
-      __syncthreads();
-      // o = sum_c w_c o_c: thread per (head, 4 dims), 16 chunk loads in flight
-      for (int e = threadIdx.x; e < gs * (hd / 4); e += NT) {
-        int h = e / (hd / 4), d4 = (e % (hd / 4)) * 4;
-        uint32_t hb = (uint32_t)((b * p.nq + g * gs + h) * C);
-        float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-        for (int c0 = 0; c0 < C; c0 += 16) {
-          i32x4 v[16];
+      // thread per (head, 4 dims): running-max combine over the chunks, 8 in flight
+      constexpr int TPH = HD / 4;  // threads per head
+      for (int e = threadIdx.x; e < gs * TPH; e += NT) {
+        const int h = e / TPH, d4 = (e % TPH) * 4;
+        const uint32_t hb = (uint32_t)((b * p.nq + g * gs + h) * C);
+        float M = -INFINITY, den = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+        for (int c0 = 0; c0 < C; c0 += 8) {
+          float mc[8], lc[8];
+          i32x4 v[8];
 #pragma unroll
-          for (int u = 0; u < 16; ++u)
-            v[u] = ld_x4<CP_SC1>(wr, c0 + u < C ? p.off_attn + ((hb + c0 + u) * (uint32_t)hd + d4) * 4u : OOB);
+          for (int u = 0; u < 8; ++u) {
+            const bool ok = c0 + u < C;
+            mc[u] = ok ? ld_f32(wr, p.off_attn_ml + (hb + c0 + u) * 8u) : -INFINITY;
+            lc[u] = ok ? ld_f32(wr, p.off_attn_ml + (hb + c0 + u) * 8u + 4u) : 0.f;
+            v[u] = ld_x4<CP_SC1>(wr, ok ? p.off_attn + ((hb + c0 + u) * (uint32_t)HD + d4) * 4u : OOB);
+          }
 #pragma unroll
-          for (int u = 0; u < 16; ++u) {
-            float f = c0 + u < C ? sm.cw[h][c0 + u] : 0.f;
-            o0 += f * __int_as_float(v[u][0]);
-            o1 += f * __int_as_float(v[u][1]);
-            o2 += f * __int_as_float(v[u][2]);
-            o3 += f * __int_as_float(v[u][3]);
+          for (int u = 0; u < 8; ++u) {
+            if (mc[u] == -INFINITY) continue;
+            const float mn = fmaxf(M, mc[u]);
+            const float fo = M == -INFINITY ? 0.f : __expf(M - mn), fc = __expf(mc[u] - mn);
+            den = den * fo + lc[u] * fc;
+            o0 = o0 * fo + __int_as_float(v[u][0]) * fc;
+            o1 = o1 * fo + __int_as_float(v[u][1]) * fc;
+            o2 = o2 * fo + __int_as_float(v[u][2]) * fc;
+            o3 = o3 * fo + __int_as_float(v[u][3]) * fc;
+            M = mn;
           }
         }
-        float il = sm.cl[h];
-        int col = (g * gs + h) * hd + d4;
-        put_hilo(wr, p.off_ou, p.nq * hd, b, col + 0, o0 * il);
-        put_hilo(wr, p.off_ou, p.nq * hd, b, col + 1, o1 * il);
-        put_hilo(wr, p.off_ou, p.nq * hd, b, col + 2, o2 * il);
-        put_hilo(wr, p.off_ou, p.nq * hd, b, col + 3, o3 * il);
+        const float il = 1.0f / den;
+        const int col = (g * gs + h) * HD + d4;
+        put_hilo(wr, p.off_ou, p.nq * HD, b, col + 0, o0 * il);
+        put_hilo(wr, p.off_ou, p.nq * HD, b, col + 1, o1 * il);
+        put_hilo(wr, p.off_ou, p.nq * HD, b, col + 2, o2 * il);
+        put_hilo(wr, p.off_ou, p.nq * HD, b, col + 3, o3 * il);
       }
     }
     __syncthreads();
     sub_stamp(p, 2);
   }
+}
+
+__device__ __forceinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L, int layer, int wait_idx) {
+  if (p.hd == 128) attn_phase<128>(p, L, layer, wait_idx);
+  else attn_phase<64>(p, L, layer, wait_idx);
 }
 
 // ------------------------------------------------------------------ gated delta rule
@@ -2099,7 +2140,7 @@ __device__ __forceinline__ void run_one_phase(const Params& p, int layer, int ph
     case PH_EMBED: clear_next_bank(p); phase_embed(p); break;
     case PH_QKV: phase_qkv(p, L, -1); break;
     case PH_KV_WRITE: phase_gqa_kv_write(p, L); break;
-    case PH_ATTN: phase_attn_gqa(p, L, l); break;
+    case PH_ATTN: phase_attn_gqa(p, L, l, -1); break;
     case PH_OPROJ: phase_residual(p, L, RES_OPROJ, L.ffn_norm, -1); break;
     case PH_GATEUP: phase_gateup(p, L, -1); break;
     case PH_DOWN: phase_residual(p, L, RES_DENSE_DOWN, g_next, -1); break;
@@ -2153,8 +2194,7 @@ extern "C" __global__ __launch_bounds__(NT) void md_megakernel(Params p) {
         phase_gqa_kv_write(p, L);
         ARRIVE();
       }
-      WAIT();
-      phase_attn_gqa(p, L, l);
+      phase_attn_gqa(p, L, l, sidx++);
       ARRIVE();
       phase_residual(p, L, RES_OPROJ, L.ffn_norm, sidx++);
       ARRIVE();

@@ -1,5 +1,12 @@
 """In-kernel phase trace: record per-workgroup wall-clock stamps around every
-sync point of a step (md_set_trace) and summarise phase and wait times."""
+sync point of a step (md_set_trace) and summarise phase and wait times.
+
+    python -m decode_megakernel_md_amd.trace [--workload dense_27b] [--batches 1,8]
+
+prints, per phase kind, the median and slowest workgroup's time per layer,
+the release latency of its sync point (last arrival to median wait end) and,
+for weight-streaming phases, the time from the end of the wait to the start
+of the stream and the stream itself."""
 from __future__ import annotations
 
 import ctypes
@@ -9,10 +16,18 @@ import numpy as np
 from ._lib import check, lib
 
 
-def dense_phase_names(n_layers):
+def phase_names(w, verify=False):
+    """Names of the phases of one step, in sync-point order."""
     names = ["embed"]
-    for l in range(n_layers):
-        names += ["qkv", "attn", "oproj", "gateup", "down"]
+    for l in range(w.n_layers):
+        kind = w.layer_kind(l)
+        if kind == "gqa":
+            names += ["qkv"] + (["kv_write"] if verify else []) + ["attn", "oproj"]
+        elif kind == "kda":
+            names += ["kda_proj", "kda_rec", "kda_o"]
+        else:
+            names += ["mla_a", "mla_b", "mla_absorb", "mla_attn", "mla_out", "mla_o"]
+        names += ["moe_a", "moe_b", "moe_down"] if w.is_moe else ["gateup", "down"]
     names += ["lmhead"]
     return names
 
@@ -64,3 +79,49 @@ class Tracer:
                 if np.all(sub[:, s, 3] > 0):
                     d["k3"] += float(np.median(sub[:, s, 3] - sub[:, s, 0]))
         return out, total
+
+
+def main():
+    import argparse
+    import sys
+
+    import torch
+
+    import synth
+    from synth import workloads as WL
+
+    from .model import DeviceModel
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", default="dense_27b")
+    ap.add_argument("--batches", default="1,8")
+    args = ap.parse_args()
+    w = WL.get(args.workload)
+    m = DeviceModel(w)
+    for B in [int(b) for b in args.batches.split(",")]:
+        toks = torch.tensor(synth.tokens(w, B), device=m.device)
+        pos = torch.full((B,), w.context, dtype=torch.int32, device=m.device)
+        logits = torch.empty((B, w.vocab), device=m.device)
+        nxt = torch.empty((B,), dtype=torch.int32, device=m.device)
+        ids = torch.empty((w.n_layers, B, max(w.top_k, 1)), dtype=torch.int32, device=m.device)
+        for _ in range(2):
+            m.decode(toks, pos, logits, nxt, ids if w.is_moe else None)
+        tr = Tracer(m)
+        m.decode(toks, pos, logits, nxt, ids if w.is_moe else None)
+        torch.cuda.synchronize()
+        m.device_status()
+        tr.stop()
+        out, total = tr.summary(phase_names(w))
+        print(f"{w.name} B={B}: step {total:.1f} us (per layer below, us)")
+        print("| phase | layers | work (median WG) | work (slowest WG) | release | wait end -> stream | stream |")
+        print("|---|---|---|---|---|---|---|")
+        for k, d in out.items():
+            n = d["n"]
+            print(f"| {k} | {n} | {d['med'] / n:.1f} | {d['max'] / n:.1f} | {d['release'] / n:.1f} | "
+                  f"{d['to_slots'] / n:.1f} | {d['to_sweep_end'] / n:.1f} |")
+        sys.stdout.flush()
+        del tr
+    m.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -581,13 +581,22 @@ __device__ __forceinline__ void put_hilo(rsrc_t r, uint32_t u_off, int K, int t,
 }
 
 // This workgroup's sum of squares of x per token (partials [NT][MAXB] in
-// the reduction scratch, summed in a fixed order) -> ssq[w][t].
+// the reduction scratch, one per thread) -> ssq[w][t]: wave sums, then the
+// four waves in order (a fixed order: deterministic).
 __device__ __forceinline__ void store_ssq(const Params& p, rsrc_t r, float* part, uint32_t off_ssq) {
   __syncthreads();
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  float* wsum = part + NT * MAXB;  // [NW][MAXB]
+#pragma unroll
+  for (int t = 0; t < MAXB; ++t) {
+    float v = wave_sum(part[threadIdx.x * MAXB + t]);
+    if (lane == 0) wsum[wv * MAXB + t] = v;
+  }
+  __syncthreads();
   if (threadIdx.x < MAXB) {
-    float a = 0.f;
-    for (int i = 0; i < NT; ++i) a += part[i * MAXB + threadIdx.x];
-    st_f32(r, off_ssq + (uint32_t)(blockIdx.x * MAXB + threadIdx.x) * 4u, a);
+    const int t = threadIdx.x;
+    float a = wsum[t] + wsum[MAXB + t] + wsum[2 * MAXB + t] + wsum[3 * MAXB + t];
+    st_f32(r, off_ssq + (uint32_t)(blockIdx.x * MAXB + t) * 4u, a);
   }
 }
 
@@ -1841,16 +1850,36 @@ __device__ __noinline__ void phase_residual(const Params& p, const LayerDesc& L,
     }
   }
   builder_done(p, sb, nrow);
-  // stage the residual rows this workgroup owns and the next norm's gains
-  for (int e = threadIdx.x; e < nrow * B; e += NT) {
+  GemvStream gs;
+  gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
+  // the residual rows this workgroup owns (its own earlier output) and the
+  // next norm's gains, requested behind the first weight loads and staged
+  // once the wait (which waits for every earlier load) is over
+  float xv[4], gv[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int e = threadIdx.x + k * NT;
+    const bool in = e < nrow * B;
+    const int t = in ? e % B : 0, lr = in ? e / B : 0;
+    xv[k] = in ? p.x[t * H + own.r0 + lr] : 0.f;
+    gv[k] = (in && t == 0) ? bf16_f32(g_next[own.r0 + lr]) : 0.f;
+  }
+  wait_point(p, wait_idx);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int e = threadIdx.x + k * NT;
+    if (e < nrow * B) {
+      const int t = e % B, lr = e / B;
+      GSM.out[lr][t] = xv[k];
+      if (t == 0) GSM.gain[lr] = gv[k];
+    }
+  }
+  for (int e = threadIdx.x + 4 * NT; e < nrow * B; e += NT) {  // more rows than 4 per thread
     int t = e % B, lr = e / B;
     GSM.out[lr][t] = p.x[t * H + own.r0 + lr];
     if (t == 0) GSM.gain[lr] = bf16_f32(g_next[own.r0 + lr]);
   }
   __syncthreads();
-  GemvStream gs;
-  gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
-  wait_point(p, wait_idx);
   sub_stamp(p, 0);
   const int r0 = own.r0;
   gemv_run(gs, p, 0, 0u, [=](int g, int rb) {
@@ -1862,7 +1891,7 @@ __device__ __noinline__ void phase_residual(const Params& p, const LayerDesc& L,
   });
   sub_stamp(p, 2);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-  static_assert(sizeof(GemvSmem::red) >= sizeof(float) * NT * MAXB, "partial sums reuse the reduction scratch");
+  static_assert(sizeof(GemvSmem::red) >= sizeof(float) * (NT + NW) * MAXB, "partial sums reuse the reduction scratch");
   float* part = (float*)GSM.red;  // [NT][MAXB]
   for (int t = 0; t < MAXB; ++t) part[threadIdx.x * MAXB + t] = 0.f;
   for (int e = threadIdx.x; e < nrow * B; e += NT) {

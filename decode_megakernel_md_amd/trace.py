@@ -4,9 +4,11 @@ sync point of a step (md_set_trace) and summarise phase and wait times.
     python -m decode_megakernel_md_amd.trace [--workload dense_27b] [--batches 1,8]
 
 prints, per phase kind, the median and slowest workgroup's time per layer,
-the release latency of its sync point (last arrival to median wait end) and,
-for weight-streaming phases, the time from the end of the wait to the start
-of the stream and the stream itself."""
+the release latency of its sync point (last arrival to median wait end) and
+the medians of the phase's own sub-stamps: the end of the wait to stamp 0
+(weight-streaming phases: the stream starts; attention: q is ready), and
+stamp 0 to stamps 1, 2, 3 (streams: 2 = stream done; attention: 3 = this
+workgroup's blocks done, 1 = its partial stored, 2 = combine done)."""
 from __future__ import annotations
 
 import ctypes
@@ -112,12 +114,14 @@ def main():
         tr.stop()
         out, total = tr.summary(phase_names(w))
         print(f"{w.name} B={B}: step {total:.1f} us (per layer below, us)")
-        print("| phase | layers | work (median WG) | work (slowest WG) | release | wait end -> stream | stream |")
-        print("|---|---|---|---|---|---|---|")
+        print("| phase | layers | work (median WG) | work (slowest WG) | release | wait end -> stamp 0 | "
+              "stamp 0 -> 1 | stamp 0 -> 2 | stamp 0 -> 3 |")
+        print("|---|---|---|---|---|---|---|---|---|")
         for k, d in out.items():
             n = d["n"]
             print(f"| {k} | {n} | {d['med'] / n:.1f} | {d['max'] / n:.1f} | {d['release'] / n:.1f} | "
-                  f"{d['to_slots'] / n:.1f} | {d['to_sweep_end'] / n:.1f} |")
+                  f"{d['to_slots'] / n:.1f} | {d['to_first'] / n:.1f} | {d['to_sweep_end'] / n:.1f} | "
+                  f"{d['k3'] / n:.1f} |")
         sys.stdout.flush()
         del tr
     m.close()

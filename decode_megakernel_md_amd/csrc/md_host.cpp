@@ -451,7 +451,7 @@ static md_status fill_params(md_model* m, const int32_t* tokens, const int32_t* 
   p.kda_h = c->kda_heads; p.kda_dk = c->kda_dk; p.kda_dv = c->kda_dv; p.kda_l2 = c->kda_qk_l2norm;
   {
     int cm = m->grid / batch;
-    int by_ctx = (c->max_ctx + 127) / 128;
+    int by_ctx = (c->max_ctx + 31) / 32;
     if (cm > by_ctx) cm = by_ctx;
     if (cm > CMAX) cm = CMAX;
     if (cm < 1) cm = 1;
@@ -523,7 +523,7 @@ md_status md_verify_step(md_model* m, const int32_t* tokens, const int32_t* posi
     int C = m->grid / pairs;
     p.attn_chunks = C < 1 ? 1 : (C > CMAX ? CMAX : C);
     int cm = m->grid / n_tok;
-    int by_ctx = (c->max_ctx + 127) / 128;
+    int by_ctx = (c->max_ctx + 31) / 32;
     if (cm > by_ctx) cm = by_ctx;
     p.mla_chunks = cm < 1 ? 1 : (cm > CMAX ? CMAX : cm);
   }

@@ -244,29 +244,29 @@ struct GemvSmem {
 // kind); quarters are appended with single() or pair() and written straight
 // into the LDS slot table; a group never spans two begin() calls.
 struct SlotBuilder {
-  int ns, fill, pfill;
+  int ns, fill, pfill, nm;  // slots, quarters in the open slot, pending pairs, matrices (all in registers:
+                            // the builder only writes LDS, so its stores pipeline)
   GroupDesc gd;
   __device__ void empty_slot(int si) {
     for (int e = 0; e < 4; ++e) { GSM.slots[si].m[e] = 0; GSM.slots[si].gq[e] = -1; }
   }
+  bool ovf;
   __device__ void start() {
-    ns = 0; fill = 0; pfill = 0;
+    ns = 0; fill = 0; pfill = 0; nm = 0; ovf = false;
     gd.u_off = 0; gd.KS = MIN_KS; gd.kind = GK_SINGLE; gd.pad_ = 0;
-    GSM.nmats = 0;
-    GSM.overflow = 0;
   }
   __device__ int mat(const void* w, int N, int K, int tag) {
-    int i = GSM.nmats;
-    if (i >= MAXMAT) { GSM.overflow = 1; return 0; }
+    int i = nm;
+    if (i >= MAXMAT) { ovf = true; return 0; }
     MatDesc d;
     d.w = (uint64_t)w; d.tstride = (uint64_t)(K >> 5) * 1024u; d.N = N; d.tag = tag;
     GSM.mats[i] = d;
-    GSM.nmats = i + 1;
+    nm = i + 1;
     return i;
   }
   // open slot ns (and its group when ns is even)
   __device__ bool open_slot() {
-    if (ns >= MAXSLOT) { GSM.overflow = 1; return false; }
+    if (ns >= MAXSLOT) { ovf = true; return false; }
     empty_slot(ns);
     if ((ns & 1) == 0) GSM.grp[ns >> 1] = gd;
     return true;
@@ -286,7 +286,7 @@ struct SlotBuilder {
   }
   __device__ void begin(uint32_t u_off, int K, int kind) {
     close();
-    if (K < 32 * MIN_KS || (K & 31)) GSM.overflow = 1;
+    if (K < 32 * MIN_KS || (K & 31)) ovf = true;
     gd.u_off = u_off; gd.KS = K >> 5; gd.kind = kind; gd.pad_ = 0;
   }
   __device__ void single(int m, int gq) {
@@ -297,7 +297,7 @@ struct SlotBuilder {
   }
   __device__ void pair(int mg, int mu, int gq) {
     if (pfill == 0) {
-      if (ns + 1 >= MAXSLOT) { GSM.overflow = 1; return; }
+      if (ns + 1 >= MAXSLOT) { ovf = true; return; }
       empty_slot(ns);
       empty_slot(ns + 1);
       GSM.grp[ns >> 1] = gd;
@@ -308,19 +308,21 @@ struct SlotBuilder {
     GSM.slots[ns + 1].gq[pfill] = gq;
     if (++pfill == 4) pflush();
   }
-  // all of matrix m's quarters this workgroup owns
-  __device__ void singles_of(int m) {
-    RowSplit q = rows_of((GSM.mats[m].N + 3) >> 2, blockIdx.x, gridDim.x);
+  // all of an N-row matrix m's quarters this workgroup owns
+  __device__ void singles_of(int m, int N) {
+    RowSplit q = rows_of((N + 3) >> 2, blockIdx.x, gridDim.x);
     for (int gq = q.r0; gq < q.r1; ++gq) single(m, gq);
   }
-  __device__ void pairs_of(int mg, int mu) {
-    RowSplit q = rows_of((GSM.mats[mg].N + 3) >> 2, blockIdx.x, gridDim.x);
+  __device__ void pairs_of(int mg, int mu, int N) {
+    RowSplit q = rows_of((N + 3) >> 2, blockIdx.x, gridDim.x);
     for (int gq = q.r0; gq < q.r1; ++gq) pair(mg, mu, gq);
   }
   __device__ void finish() {
     close();
     GSM.nslots = ns;
     GSM.ngroups = ns / TG;
+    GSM.nmats = nm;
+    GSM.overflow = ovf ? 1 : 0;
   }
 };
 
@@ -652,9 +654,9 @@ __device__ __noinline__ void phase_qkv(const Params& p, const LayerDesc& L, int 
     int mk = sb.mat(L.wk, p.nkv * p.hd, p.H, p.nq * p.hd);
     int mv = sb.mat(L.wv, p.nkv * p.hd, p.H, (p.nq + p.nkv) * p.hd);
     sb.begin(p.off_u, p.H, GK_SINGLE);
-    sb.singles_of(mq);
-    sb.singles_of(mk);
-    sb.singles_of(mv);
+    sb.singles_of(mq, p.nq * p.hd);
+    sb.singles_of(mk, p.nkv * p.hd);
+    sb.singles_of(mv, p.nkv * p.hd);
   }
   builder_done(p, sb, -1);
   GemvStream gs;
@@ -1089,11 +1091,11 @@ __device__ __noinline__ void phase_kda_proj(const Params& p, const LayerDesc& L,
     int m3 = sb.mat(L.kda_wa, nh, p.H, 2 * nh * dk + nh * dv);
     int m4 = sb.mat(L.kda_wb, nh, p.H, 2 * nh * dk + nh * dv + nh);
     sb.begin(p.off_u, p.H, GK_SINGLE);
-    sb.singles_of(m0);
-    sb.singles_of(m1);
-    sb.singles_of(m2);
-    sb.singles_of(m3);
-    sb.singles_of(m4);
+    sb.singles_of(m0, nh * dk);
+    sb.singles_of(m1, nh * dk);
+    sb.singles_of(m2, nh * dv);
+    sb.singles_of(m3, nh);
+    sb.singles_of(m4, nh);
   }
   builder_done(p, sb, -1);
   GemvStream gs;
@@ -1361,8 +1363,8 @@ __device__ __noinline__ void phase_mla_a(const Params& p, const LayerDesc& L, in
     int ma = sb.mat(L.mla_wqa, QL, p.H, 0);
     int mk = sb.mat(L.mla_wkva, KVR, p.H, 1);
     sb.begin(p.off_u, p.H, GK_SINGLE);
-    sb.singles_of(ma);
-    sb.singles_of(mk);
+    sb.singles_of(ma, QL);
+    sb.singles_of(mk, KVR);
   }
   builder_done(p, sb, -1);
   GemvStream gs;
@@ -1431,7 +1433,7 @@ __device__ __noinline__ void phase_mla_b(const Params& p, const LayerDesc& L, in
     sb.start();
     int m = sb.mat(L.mla_wqb, nh * QW, p.q_lora, 0);
     sb.begin(p.off_uq, p.q_lora, GK_SINGLE);
-    sb.singles_of(m);
+    sb.singles_of(m, nh * QW);
   }
   builder_done(p, sb, -1);
   GemvStream gs;
@@ -1682,8 +1684,9 @@ __device__ __noinline__ void phase_mla_attn(const Params& p, const LayerDesc& L)
         st_f32(wr, p.off_mml + idx * 8u, m_run[h]);
         st_f32(wr, p.off_mml + idx * 8u + 4u, l_run[h]);
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) st_f32(wr, p.off_mz + (idx * MLA_KL + lane * 8 + j) * 4u, acc[h][j]);
+      const f32x4 z0 = {acc[h][0], acc[h][1], acc[h][2], acc[h][3]}, z1 = {acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, z0), wr, p.off_mz + (idx * MLA_KL + lane * 8) * 4u, 0, CP_SC1);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, z1), wr, p.off_mz + (idx * MLA_KL + lane * 8 + 4) * 4u, 0, CP_SC1);
     }
     __syncthreads();
   }
@@ -1703,22 +1706,26 @@ __device__ __noinline__ void phase_mla_out(const Params& p, const LayerDesc& L) 
   const int lane = threadIdx.x & 63;
   for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
     const int h = task / nsl, sl = task % nsl;
+    float* cs = cl + MAXB;         // [MAXB][256] chunk sums
     for (int e = threadIdx.x; e < B * C; e += NT) {
       int t = e / C, cc = e % C;
       cw[t * 256 + cc] = ld_f32(r, p.off_mml + (uint32_t)((t * C + cc) * nh + h) * 8u);
+      cs[t * 256 + cc] = ld_f32(r, p.off_mml + (uint32_t)((t * C + cc) * nh + h) * 8u + 4u);
     }
     __syncthreads();
-    if (threadIdx.x < B) {
-      int t = threadIdx.x;
+    for (int t = threadIdx.x >> 6; t < B; t += NW) {  // one wave per token: max, weights, denominator
+      const int ln = threadIdx.x & 63;
       float M = -INFINITY;
-      for (int cc = 0; cc < C; ++cc) M = fmaxf(M, cw[t * 256 + cc]);
+      for (int cc = ln; cc < C; cc += 64) M = fmaxf(M, cw[t * 256 + cc]);
+      M = wave_max(M);
       float den = 0.f;
-      for (int cc = 0; cc < C; ++cc) {
+      for (int cc = ln; cc < C; cc += 64) {
         float f = cw[t * 256 + cc] == -INFINITY ? 0.f : __expf(cw[t * 256 + cc] - M);
         cw[t * 256 + cc] = f;
-        den += f * ld_f32(r, p.off_mml + (uint32_t)((t * C + cc) * nh + h) * 8u + 4u);
+        den += f * cs[t * 256 + cc];
       }
-      cl[t] = 1.0f / den;
+      den = wave_sum(den);
+      if (ln == 0) cl[t] = 1.0f / den;
     }
     __syncthreads();
     // z[t][d], thread per (token, 4 dims), 8 chunk loads in flight
@@ -1798,6 +1805,8 @@ struct RouteSmem {
   int ids[MAXB][8];       // chosen experts per token, in descending router order
   float w[MAXB][8];       // their weights
   float wt[MAXB][64];     // weight of U entry j for token t (0: not chosen)
+  const uint16_t* ex[64][3];  // gate, up, down weights of U entry j
+  uint64_t mask[MAXB];    // experts each token chose
 };
 constexpr size_t cmax_(size_t a, size_t b) { return a > b ? a : b; }
 constexpr size_t ROUTE_OFF =
@@ -1823,29 +1832,29 @@ __device__ __noinline__ void phase_residual(const Params& p, const LayerDesc& L,
     if (mode == RES_OPROJ) {
       int m = sb.mat(L.wo, H, p.nq * p.hd, 0);
       sb.begin(p.off_ou, p.nq * p.hd, GK_SINGLE);
-      sb.singles_of(m);
+      sb.singles_of(m, H);
     } else if (mode == RES_MLA_O) {
       int m = sb.mat(L.mla_wo, H, p.mla_h * p.vdim, 0);
       sb.begin(p.off_ou, p.mla_h * p.vdim, GK_SINGLE);
-      sb.singles_of(m);
+      sb.singles_of(m, H);
     } else if (mode == RES_KDA_O) {
       int m = sb.mat(L.kda_wo, H, p.kda_h * p.kda_dv, 0);
       sb.begin(p.off_ou, p.kda_h * p.kda_dv, GK_SINGLE);
-      sb.singles_of(m);
+      sb.singles_of(m, H);
     } else if (mode == RES_DENSE_DOWN) {
       int m = sb.mat(L.w_down, H, p.ffn, 0);
       sb.begin(p.off_h, p.ffn, GK_SINGLE);
-      sb.singles_of(m);
+      sb.singles_of(m, H);
     } else {
       if (p.n_shared > 0) {
         int m = sb.mat(L.sh_down, H, p.shared_ffn, 0);
         sb.begin(p.off_hs, p.shared_ffn, GK_SINGLE);
-        sb.singles_of(m);
+        sb.singles_of(m, H);
       }
       for (int j = 0; j < RSM.nu; ++j) {
-        int m = sb.mat(L.experts[RSM.u[j] * 3 + 2], H, p.expert_ffn, 0);
+        int m = sb.mat(RSM.ex[j][2], H, p.expert_ffn, 0);
         sb.begin(p.off_hr + (uint32_t)j * p.hr_stride, p.expert_ffn, GK_SINGLE);
-        sb.singles_of(m);
+        sb.singles_of(m, H);
       }
     }
   }
@@ -1913,7 +1922,7 @@ __device__ __noinline__ void phase_gateup(const Params& p, const LayerDesc& L, i
     int mg = sb.mat(L.w_gate, F, p.H, 0);
     int mu = sb.mat(L.w_up, F, p.H, 0);
     sb.begin(p.off_u, p.H, GK_PAIR);
-    sb.pairs_of(mg, mu);
+    sb.pairs_of(mg, mu, F);
   }
   builder_done(p, sb, -1);
   GemvStream gs;
@@ -1953,11 +1962,11 @@ __device__ __noinline__ void phase_moe_a(const Params& p, const LayerDesc& L, in
       int mg = sb.mat(L.sh_gate, p.shared_ffn, p.H, 0);
       int mu = sb.mat(L.sh_up, p.shared_ffn, p.H, 0);
       sb.begin(p.off_u, p.H, GK_PAIR);
-      sb.pairs_of(mg, mu);
+      sb.pairs_of(mg, mu, p.shared_ffn);
     }
     int mr = sb.mat(L.router, p.n_experts, p.H, -1);
     sb.begin(p.off_u, p.H, GK_SINGLE);
-    sb.singles_of(mr);
+    sb.singles_of(mr, p.n_experts);
   }
   builder_done(p, sb, -1);
   GemvStream gs;
@@ -2020,23 +2029,28 @@ __device__ __noinline__ void compute_routes(const Params& p, int layer) {
       if (lane == 0) { RSM.ids[t][j] = e; RSM.w[t][j] = pj; }
     }
     float den = p.norm_topk ? sel : all;
+    const uint64_t chosen = __ballot(taken);
     __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
     __builtin_amdgcn_wave_barrier();
     if (lane < k) RSM.w[t][lane] = RSM.w[t][lane] / den;
+    if (lane == 0) RSM.mask[t] = chosen;
   }
   if (threadIdx.x < 64) RSM.pos[threadIdx.x] = -1;
   for (int i = threadIdx.x; i < MAXB * 64; i += NT) RSM.wt[i >> 6][i & 63] = 0.f;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint64_t mask = 0;
-    for (int t = 0; t < B; ++t)
-      for (int j = 0; j < k; ++j) mask |= 1ull << RSM.ids[t][j];
+    for (int t = 0; t < B; ++t) mask |= RSM.mask[t];
     int n = 0;
     for (int e = 0; e < E; ++e)
       if ((mask >> e) & 1ull) { RSM.u[n] = e; RSM.pos[e] = n; ++n; }
     RSM.nu = n;
   }
   __syncthreads();
+  // the chosen experts' weight pointers, fetched in parallel (the slot
+  // builders read them from LDS)
+  const LayerDesc& L = p.layers[layer];
+  for (int i = threadIdx.x; i < RSM.nu * 3; i += NT) RSM.ex[i / 3][i % 3] = L.experts[RSM.u[i / 3] * 3 + i % 3];
   if (threadIdx.x < B * k) {
     int t = threadIdx.x / k, j = threadIdx.x % k;
     RSM.wt[t][RSM.pos[RSM.ids[t][j]]] = RSM.w[t][j];
@@ -2052,10 +2066,9 @@ __device__ __noinline__ void phase_moe_b(const Params& p, const LayerDesc& L, in
     sb.start();
     sb.begin(p.off_u, p.H, GK_PAIR);
     for (int j = 0; j < RSM.nu; ++j) {
-      const uint16_t* const* ex = L.experts + RSM.u[j] * 3;
-      int mg = sb.mat(ex[0], p.expert_ffn, p.H, j);
-      int mu = sb.mat(ex[1], p.expert_ffn, p.H, j);
-      sb.pairs_of(mg, mu);
+      int mg = sb.mat(RSM.ex[j][0], p.expert_ffn, p.H, j);
+      int mu = sb.mat(RSM.ex[j][1], p.expert_ffn, p.H, j);
+      sb.pairs_of(mg, mu, p.expert_ffn);
     }
   }
   builder_done(p, sb, -1);
@@ -2084,7 +2097,7 @@ __device__ __noinline__ void phase_lmhead(const Params& p, int wait_idx) {
     sb.start();
     int m = sb.mat(p.lm_head, p.V, p.H, 0);
     sb.begin(p.off_u, p.H, GK_SINGLE);
-    sb.singles_of(m);
+    sb.singles_of(m, p.V);
   }
   builder_done(p, sb, -1);
   GemvStream gs;

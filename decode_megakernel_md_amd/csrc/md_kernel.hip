@@ -29,6 +29,27 @@
 
 namespace md {
 
+// The step's parameter block is read where the launch placed it, in the
+// kernel-argument segment: the kernel passes that pointer to every device
+// function, which makes it wave-uniform, so the loads are scalar (no copy in
+// scratch memory, no wait on the vector-memory counter that the weight
+// streams use).  The kernel-argument intrinsic itself is only meaningful in
+// the kernel's own body, hence the explicit argument.  The layer table is
+// read the same way (it does not change during a step).
+typedef const __attribute__((address_space(4))) Params KParams;
+typedef const __attribute__((address_space(4))) LayerDesc KLayer;
+__device__ __forceinline__ KParams& kp_uniform(KParams& r) {
+  const uint64_t a = (uint64_t)&r;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return *(KParams*)(((uint64_t)hi << 32) | lo);
+}
+#define PARAMS KParams& p = kp_uniform(pk)
+__device__ __forceinline__ KLayer& layer_ref(KParams& pk, int l) {
+  PARAMS;
+  return ((KLayer*)p.layers)[__builtin_amdgcn_readfirstlane(l)];
+}
+
 // ===================================================================== sync
 // One sync point = 8 sub-counters (one per workgroup class blockIdx % 8,
 // which on this part is the XCD the workgroup runs on) and one top counter,
@@ -39,21 +60,25 @@ namespace md {
 constexpr int SP_WORDS = 9 * 32;          // 9 lines of 128 B
 constexpr int NGRP = 8;
 
-__device__ __forceinline__ unsigned* sync_pt(const Params& p, int idx) {
+__device__ __forceinline__ unsigned* sync_pt(KParams& pk, int idx) {
+  PARAMS;
   return p.sync + (size_t)p.bank * p.n_sync * SP_WORDS + (size_t)idx * SP_WORDS;
 }
 
-__device__ __forceinline__ bool dev_failed(const Params& p) {
+__device__ __forceinline__ bool dev_failed(KParams& pk) {
+  PARAMS;
   return __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
 }
 
-__device__ __forceinline__ void set_err(const Params& p, int code) {
+__device__ __forceinline__ void set_err(KParams& pk, int code) {
+  PARAMS;
   __hip_atomic_fetch_or(p.err, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // every wave: make this wave's stores complete, then the workgroup arrives
 // once.  Returns (in thread 0) whether this workgroup was the last to arrive.
-__device__ bool arrive(const Params& p, int idx) {
+__device__ bool arrive(KParams& pk, int idx) {
+  PARAMS;
   wait_stores();
   __builtin_amdgcn_s_barrier();
   bool last = false;
@@ -70,7 +95,8 @@ __device__ bool arrive(const Params& p, int idx) {
 }
 
 // wait until every group has fully arrived at sync point idx
-__device__ void wait_all(const Params& p, int idx) {
+__device__ void wait_all(KParams& pk, int idx) {
+  PARAMS;
   if (threadIdx.x == 0) {
     unsigned* top = sync_pt(p, idx) + 32 * NGRP;
     unsigned ngrp = gridDim.x < NGRP ? gridDim.x : NGRP;
@@ -86,13 +112,15 @@ __device__ void wait_all(const Params& p, int idx) {
   __builtin_amdgcn_s_barrier();
 }
 
-__device__ __forceinline__ void stamp(const Params& p, int slot) {
+__device__ __forceinline__ void stamp(KParams& pk, int slot) {
+  PARAMS;
   if (p.trace && threadIdx.x == 0 && slot < p.trace_n) p.trace[(size_t)blockIdx.x * p.trace_n + slot] = wall_clock64();
 }
 
 // Sub-phase stamps: slot trace_n/2 + 4*(phase index) + k, k < 4.
 __shared__ int md_cur_phase;
-__device__ __forceinline__ void sub_stamp(const Params& p, int k) {
+__device__ __forceinline__ void sub_stamp(KParams& pk, int k) {
+  PARAMS;
   if (p.trace && threadIdx.x == 0) {
     int slot = p.trace_n / 2 + 4 * md_cur_phase + k;
     if (slot < p.trace_n - 1) p.trace[(size_t)blockIdx.x * p.trace_n + slot] = wall_clock64();
@@ -100,7 +128,8 @@ __device__ __forceinline__ void sub_stamp(const Params& p, int k) {
 }
 
 // Sync point sidx: stamps 2*sidx (work done) and 2*sidx+1 (wait over).
-__device__ __forceinline__ void grid_sync(const Params& p, int& sidx) {
+__device__ __forceinline__ void grid_sync(KParams& pk, int& sidx) {
+  PARAMS;
   stamp(p, 2 * sidx);
   arrive(p, sidx);
   wait_all(p, sidx);
@@ -113,11 +142,13 @@ __device__ __forceinline__ void grid_sync(const Params& p, int& sidx) {
 // done; wait_point once the next phase has issued what it may issue before
 // the other workgroups are done (its first weight loads).  idx < 0: no wait
 // (the multi-launch step, where the kernel boundary is the barrier).
-__device__ __forceinline__ void grid_arrive(const Params& p, int sidx) {
+__device__ __forceinline__ void grid_arrive(KParams& pk, int sidx) {
+  PARAMS;
   stamp(p, 2 * sidx);
   arrive(p, sidx);
 }
-__device__ __forceinline__ void wait_point(const Params& p, int idx) {
+__device__ __forceinline__ void wait_point(KParams& pk, int idx) {
+  PARAMS;
   if (idx < 0) return;
   wait_all(p, idx);
   stamp(p, 2 * idx + 1);
@@ -125,7 +156,8 @@ __device__ __forceinline__ void wait_point(const Params& p, int idx) {
 }
 
 // clear this WG's share of the other bank (used by the next step)
-__device__ void clear_next_bank(const Params& p) {
+__device__ void clear_next_bank(KParams& pk) {
+  PARAMS;
   unsigned* nb = p.sync + (size_t)(p.bank ^ 1) * p.n_sync * SP_WORDS;
   size_t n = (size_t)p.n_sync * SP_WORDS;
   size_t per = (n + gridDim.x - 1) / gridDim.x;
@@ -137,8 +169,10 @@ __device__ void clear_next_bank(const Params& p) {
 // sequence r at positions[r].  Verify: every row belongs to sequence 0 and
 // row r is the token at positions[0] + r.  Out-of-range positions set the
 // device error word and are clamped (the step's outputs are then undefined).
-__device__ __forceinline__ int row_seq(const Params& p, int r) { return p.verify ? 0 : r; }
-__device__ __forceinline__ int row_pos(const Params& p, int r) {
+__device__ __forceinline__ int row_seq(KParams& pk, int r) {
+  PARAMS; return p.verify ? 0 : r; }
+__device__ __forceinline__ int row_pos(KParams& pk, int r) {
+  PARAMS;
   int pos = p.verify ? p.positions[0] + r : p.positions[r];
   if (pos < 0 || pos >= p.max_ctx) {
     set_err(p, MDE_POSITION);
@@ -191,10 +225,12 @@ constexpr int MIN_KS = NW;       // every wave needs a k-step of every group
 struct RowSplit {
   int r0, r1;
 };
+// (N * w fits in 32 bits for every split made here: N <= 2^22 quarters or
+// units, w <= G <= 1024.)
 __device__ __forceinline__ RowSplit rows_of(int N, int w, int G) {
   RowSplit s;
-  s.r0 = (int)((int64_t)N * w / G);
-  s.r1 = (int)((int64_t)N * (w + 1) / G);
+  s.r0 = (int)((uint32_t)N * (uint32_t)w / (uint32_t)G);
+  s.r1 = (int)((uint32_t)N * (uint32_t)(w + 1) / (uint32_t)G);
   return s;
 }
 
@@ -308,13 +344,19 @@ struct SlotBuilder {
     GSM.slots[ns + 1].gq[pfill] = gq;
     if (++pfill == 4) pflush();
   }
-  // all of an N-row matrix m's quarters this workgroup owns
+  // this workgroup's quarters of an N-row matrix (the split of the last N is kept)
+  int lastN = -1;
+  RowSplit lastq;
+  __device__ RowSplit quarters(int N) {
+    if (N != lastN) { lastq = rows_of((N + 3) >> 2, blockIdx.x, gridDim.x); lastN = N; }
+    return lastq;
+  }
   __device__ void singles_of(int m, int N) {
-    RowSplit q = rows_of((N + 3) >> 2, blockIdx.x, gridDim.x);
+    RowSplit q = quarters(N);
     for (int gq = q.r0; gq < q.r1; ++gq) single(m, gq);
   }
   __device__ void pairs_of(int mg, int mu, int N) {
-    RowSplit q = rows_of((N + 3) >> 2, blockIdx.x, gridDim.x);
+    RowSplit q = quarters(N);
     for (int gq = q.r0; gq < q.r1; ++gq) pair(mg, mu, gq);
   }
   __device__ void finish() {
@@ -354,8 +396,8 @@ __device__ __forceinline__ int group_nks(int g, int wv) {
 // 1/rms per token from the partial sums of squares of every workgroup (this
 // thread holds those of workgroups tid and tid + NT), summed in a fixed
 // order: identical in every workgroup.
-__device__ __forceinline__ void inv_finish(const Params& p, float* inv, int n_feat, i32x4 a0, i32x4 b0, i32x4 a1,
-                                           i32x4 b1) {
+__device__ __forceinline__ void inv_finish(KParams& pk, float* inv, int n_feat, i32x4 a0, i32x4 b0, i32x4 a1, i32x4 b1) {
+  PARAMS;
   float* stage = (float*)(md_smem + sizeof(GemvSmem));  // [2*NT][MAXB]
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -473,7 +515,8 @@ __device__ __forceinline__ void gemv_begin(GemvStream& s, const uint8_t* ws, uin
 // before the ring's activation loads, so waiting for them never waits for
 // the ring.
 template <class Epi>
-__device__ __forceinline__ void gemv_run(GemvStream& s, const Params& p, int inv_n, uint32_t inv_off, Epi epi) {
+__device__ __forceinline__ void gemv_run(KParams& pk, GemvStream& s, int inv_n, uint32_t inv_off, Epi epi) {
+  PARAMS;
   static_assert(TG == 2, "the stream handles slot pairs");
   const int lane = threadIdx.x & 63;
   i32x4 ia0, ib0, ia1, ib1;
@@ -557,7 +600,8 @@ __device__ __forceinline__ RowSplit owned_rows(int N, int w, int G) {
 // Finish slot building; on overflow (more slots, matrices or staging rows
 // than the LDS tables hold) report it and make the phase compute nothing.
 // stage_rows < 0: the phase stages by slot row (16 per slot).
-__device__ __forceinline__ bool builder_done(const Params& p, SlotBuilder& sb, int stage_rows) {
+__device__ __forceinline__ bool builder_done(KParams& pk, SlotBuilder& sb, int stage_rows) {
+  PARAMS;
   if (threadIdx.x == 0) {
     sb.finish();
     if ((stage_rows < 0 ? sb.ns * 16 : stage_rows) > STAGE_ROWS) GSM.overflow = 1;
@@ -585,7 +629,8 @@ __device__ __forceinline__ void put_hilo(rsrc_t r, uint32_t u_off, int K, int t,
 // This workgroup's sum of squares of x per token (partials [NT][MAXB] in
 // the reduction scratch, one per thread) -> ssq[w][t]: wave sums, then the
 // four waves in order (a fixed order: deterministic).
-__device__ __forceinline__ void store_ssq(const Params& p, rsrc_t r, float* part, uint32_t off_ssq) {
+__device__ __forceinline__ void store_ssq(KParams& pk, rsrc_t r, float* part, uint32_t off_ssq) {
+  PARAMS;
   __syncthreads();
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   float* wsum = part + NT * MAXB;  // [NW][MAXB]
@@ -603,7 +648,8 @@ __device__ __forceinline__ void store_ssq(const Params& p, rsrc_t r, float* part
 }
 
 // --- embedding: x[t] = E[tok_t] on this WG's hidden rows
-__device__ __noinline__ void phase_embed(const Params& p) {
+__device__ __noinline__ void phase_embed(KParams& pk) {
+  PARAMS;
   RowSplit s = owned_rows(p.H, blockIdx.x, gridDim.x);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   const uint16_t* g = p.layers[0].attn_norm;
@@ -645,7 +691,9 @@ __device__ __noinline__ void phase_embed(const Params& p) {
   }
 
 // --- QKV projection (GQA): raw q, k, v (RMS-normalised input) -> qkv[t][row]
-__device__ __noinline__ void phase_qkv(const Params& p, const LayerDesc& L, int wait_idx) {
+__device__ __noinline__ void phase_qkv(KParams& pk, int l_layer, int wait_idx) {
+  PARAMS;
+  KLayer& L = layer_ref(p, l_layer);
   const int B = p.B;
   SlotBuilder sb;
   if (threadIdx.x == 0) {
@@ -663,7 +711,7 @@ __device__ __noinline__ void phase_qkv(const Params& p, const LayerDesc& L, int 
   gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
   wait_point(p, wait_idx);
   sub_stamp(p, 0);
-  gemv_run(gs, p, p.H, p.off_ssq, EPI_SCALED_SINGLE);
+  gemv_run(p, gs, p.H, p.off_ssq, EPI_SCALED_SINGLE);
   sub_stamp(p, 2);
   const int nqkv = (p.nq + 2 * p.nkv) * p.hd;
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
@@ -678,7 +726,8 @@ __device__ __noinline__ void phase_qkv(const Params& p, const LayerDesc& L, int 
 // RoPE rotation of pair i at position pos: (cos, sin) from the table the
 // host fills at init (angles pos * theta^(-2i/d) evaluated in fp64, rounded
 // to fp32), fp32[max_ctx][d/2][2].
-__device__ __forceinline__ void rope_cs(const Params& p, int pos, int i, float& c, float& s) {
+__device__ __forceinline__ void rope_cs(KParams& pk, int pos, int i, float& c, float& s) {
+  PARAMS;
   const float* t = p.rope + ((size_t)pos * (p.rope_d / 2) + i) * 2;
   c = t[0];
   s = t[1];
@@ -865,7 +914,9 @@ __device__ __forceinline__ void attn_dispatch(int gs, rsrc_t krs, rsrc_t vrs, in
 // Verify: the new K/V rows of all rows (positions p..p+B-1 of sequence 0)
 // go to the cache before attention, device-coherently, because row r
 // attends the rows of the tokens before it, computed by other workgroups.
-__device__ __noinline__ void phase_gqa_kv_write(const Params& p, const LayerDesc& L) {
+__device__ __noinline__ void phase_gqa_kv_write(KParams& pk, int l_layer) {
+  PARAMS;
+  KLayer& L = layer_ref(p, l_layer);
   const int hd = p.hd, nqkv = (p.nq + 2 * p.nkv) * hd;
   rsrc_t wr = make_rsrc_u(p.ws, p.ws_bytes);
   for (int task = blockIdx.x; task < p.B * p.nkv; task += gridDim.x) {
@@ -899,7 +950,9 @@ struct AttnTask {
   const uint16_t* kc;
   const uint16_t* vc;
 };
-__device__ __forceinline__ AttnTask attn_task(const Params& p, const LayerDesc& L, int task) {
+__device__ __forceinline__ AttnTask attn_task(KParams& pk, int l_layer, int task) {
+  PARAMS;
+  KLayer& L = layer_ref(p, l_layer);
   AttnTask t;
   const int C = p.attn_chunks, hd = p.hd;
   t.c = task % C;
@@ -926,7 +979,9 @@ __device__ __forceinline__ AttnTask attn_task(const Params& p, const LayerDesc& 
 // into the kernel, as is the per-wave worker: as a called function it would
 // save and restore the callee-saved registers its live values occupy.
 template <int HD>
-__device__ __forceinline__ void attn_phase(const Params& p, const LayerDesc& L, int layer, int wait_idx) {
+__device__ __forceinline__ void attn_phase(KParams& pk, int l_layer, int layer, int wait_idx) {
+  PARAMS;
+  KLayer& L = layer_ref(p, l_layer);
   AttnSmem& sm = *(AttnSmem*)md_smem;
   const int lane = threadIdx.x & 63;
   const int gs = p.nq / p.nkv, B = p.B;
@@ -937,7 +992,7 @@ __device__ __forceinline__ void attn_phase(const Params& p, const LayerDesc& L, 
   const float scale = 1.0f / sqrtf((float)HD);
   wait_point(p, wait_idx);
   for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
-    const AttnTask t = attn_task(p, L, task);
+    const AttnTask t = attn_task(p, l_layer, task);
     const int b = t.b, g = t.g, c = t.c, pos = t.pos;
     const uint32_t nb = (uint32_t)((size_t)t.n * HD * 2);
     rsrc_t krs = make_rsrc_u(t.kc, nb), vrs = make_rsrc_u(t.vc, nb);
@@ -1067,9 +1122,11 @@ __device__ __forceinline__ void attn_phase(const Params& p, const LayerDesc& L, 
   }
 }
 
-__device__ __forceinline__ void phase_attn_gqa(const Params& p, const LayerDesc& L, int layer, int wait_idx) {
-  if (p.hd == 128) attn_phase<128>(p, L, layer, wait_idx);
-  else attn_phase<64>(p, L, layer, wait_idx);
+__device__ __forceinline__ void phase_attn_gqa(KParams& pk, int l_layer, int layer, int wait_idx) {
+  PARAMS;
+  KLayer& L = layer_ref(p, l_layer);
+  if (p.hd == 128) attn_phase<128>(p, l_layer, layer, wait_idx);
+  else attn_phase<64>(p, l_layer, layer, wait_idx);
 }
 
 // ------------------------------------------------------------------ gated delta rule
@@ -1079,7 +1136,9 @@ __device__ __forceinline__ void phase_attn_gqa(const Params& p, const LayerDesc&
 //   u = S^T k;  S <- alpha S + beta k (v - u)^T;  o = S^T q (updated S).
 // Projection phase: q, k, v and the two gate logits per head, one GEMV
 // over five matrices; kda[t] = [q (nh*dk) | k (nh*dk) | v (nh*dv) | a (nh) | b (nh)].
-__device__ __noinline__ void phase_kda_proj(const Params& p, const LayerDesc& L, int wait_idx) {
+__device__ __noinline__ void phase_kda_proj(KParams& pk, int l_layer, int wait_idx) {
+  PARAMS;
+  KLayer& L = layer_ref(p, l_layer);
   const int B = p.B, nh = p.kda_h, dk = p.kda_dk, dv = p.kda_dv;
   const int width = 2 * nh * dk + nh * dv + 2 * nh;
   SlotBuilder sb;
@@ -1102,7 +1161,7 @@ __device__ __noinline__ void phase_kda_proj(const Params& p, const LayerDesc& L,
   gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
   wait_point(p, wait_idx);
   sub_stamp(p, 0);
-  gemv_run(gs, p, p.H, p.off_ssq, EPI_SCALED_SINGLE);
+  gemv_run(p, gs, p.H, p.off_ssq, EPI_SCALED_SINGLE);
   sub_stamp(p, 2);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
@@ -1123,7 +1182,9 @@ struct KdaSmem {
 // Recurrence phase: task (b, h, 32-column slice of the state).  The slice
 // (dk x 32 fp32) is read once into registers -- thread (rg, j) holds rows
 // rg, rg+8, ... of column j -- updated there and written back in place.
-__device__ __noinline__ void phase_kda_rec(const Params& p, const LayerDesc& L) {
+__device__ __noinline__ void phase_kda_rec(KParams& pk, int l_layer) {
+  PARAMS;
+  KLayer& L = layer_ref(p, l_layer);
   KdaSmem& sm = *(KdaSmem*)md_smem;
   const int B = p.B, nh = p.kda_h, dk = p.kda_dk, dv = p.kda_dv;
   const int width = 2 * nh * dk + nh * dv + 2 * nh;
@@ -1205,7 +1266,9 @@ __device__ __noinline__ void phase_kda_rec(const Params& p, const LayerDesc& L) 
 // the B updates in registers, emits o for every row, and stores the state
 // after every row in the snapshot ring; the state itself is rewritten only
 // once the accepted length is known (verify_finish).
-__device__ __noinline__ void phase_kda_rec_verify(const Params& p, const LayerDesc& L) {
+__device__ __noinline__ void phase_kda_rec_verify(KParams& pk, int l_layer) {
+  PARAMS;
+  KLayer& L = layer_ref(p, l_layer);
   KdaSmem& sm = *(KdaSmem*)md_smem;
   const int B = p.B, nh = p.kda_h, dk = p.kda_dk, dv = p.kda_dv;
   const int width = 2 * nh * dk + nh * dv + 2 * nh;
@@ -1290,7 +1353,8 @@ __device__ __noinline__ void phase_kda_rec_verify(const Params& p, const LayerDe
 // 1 <= i <= j), and copies its share of each delta-rule layer's snapshot m
 // into the state.  Workgroup 0 reports a and argmax(row a-1).
 constexpr int MAX_KDA_LAYERS = 512;
-__device__ __noinline__ void verify_finish(const Params& p) {
+__device__ __noinline__ void verify_finish(KParams& pk) {
+  PARAMS;
   int* arg = (int*)md_smem;                 // [MAXB]
   int* acc = arg + MAXB;                    // [1]
   uint64_t* koff = (uint64_t*)(md_smem + 64);  // [MAX_KDA_LAYERS] state offsets of the delta-rule layers
@@ -1355,7 +1419,9 @@ constexpr int MLA_KL = 512, MLA_RD = 64, MLA_QA = MLA_KL + MLA_RD, MLA_KS = MLA_
 // M1: c_q0 = W_qa xn (q_lora) and ckv = W_kva xn (kv_lora + rope).  c_q0 goes
 // out as U = hilo(g_q * c_q0) plus its partial sums of squares (the q norm),
 // ckv as fp32.
-__device__ __noinline__ void phase_mla_a(const Params& p, const LayerDesc& L, int wait_idx) {
+__device__ __noinline__ void phase_mla_a(KParams& pk, int l_layer, int wait_idx) {
+  PARAMS;
+  KLayer& L = layer_ref(p, l_layer);
   const int B = p.B, QL = p.q_lora, KVR = MLA_QA;
   SlotBuilder sb;
   if (threadIdx.x == 0) {
@@ -1371,7 +1437,7 @@ __device__ __noinline__ void phase_mla_a(const Params& p, const LayerDesc& L, in
   gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
   wait_point(p, wait_idx);
   sub_stamp(p, 0);
-  gemv_run(gs, p, p.H, p.off_ssq, EPI_SCALED_SINGLE);
+  gemv_run(p, gs, p.H, p.off_ssq, EPI_SCALED_SINGLE);
   sub_stamp(p, 2);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   float* part = (float*)GSM.red;  // [NT][MAXB]
@@ -1394,7 +1460,9 @@ __device__ __noinline__ void phase_mla_a(const Params& p, const LayerDesc& L, in
 // The new latent cache row of sequence b: RMSNorm(c) * g_kv and the rotated
 // k_pe, rounded to bf16, written device-coherently (another workgroup reads
 // it in this same step).
-__device__ void mla_cache_row(const Params& p, const LayerDesc& L, int b) {
+__device__ void mla_cache_row(KParams& pk, int l_layer, int b) {
+  PARAMS;
+  KLayer& L = layer_ref(p, l_layer);
   float* c = &GSM.in[0][0];  // [576] (the staging area is free before the stream)
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   const int pos = row_pos(p, b);
@@ -1425,7 +1493,9 @@ __device__ void mla_cache_row(const Params& p, const LayerDesc& L, int b) {
 
 // M2: q = W_qb RMSNorm(c_q0) (nh x (nope + rope)), and the new cache rows
 // (workgroup G-1-b writes sequence b's).
-__device__ __noinline__ void phase_mla_b(const Params& p, const LayerDesc& L, int wait_idx) {
+__device__ __noinline__ void phase_mla_b(KParams& pk, int l_layer, int wait_idx) {
+  PARAMS;
+  KLayer& L = layer_ref(p, l_layer);
   const int B = p.B, nh = p.mla_h, QW = p.nope + MLA_RD;
   const int cb = (int)gridDim.x - 1 - (int)blockIdx.x;
   SlotBuilder sb;
@@ -1439,9 +1509,9 @@ __device__ __noinline__ void phase_mla_b(const Params& p, const LayerDesc& L, in
   GemvStream gs;
   gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
   wait_point(p, wait_idx);
-  if (cb < B) mla_cache_row(p, L, cb);
+  if (cb < B) mla_cache_row(p, l_layer, cb);
   sub_stamp(p, 0);
-  gemv_run(gs, p, p.q_lora, p.off_ssq2, EPI_SCALED_SINGLE);
+  gemv_run(p, gs, p.q_lora, p.off_ssq2, EPI_SCALED_SINGLE);
   sub_stamp(p, 2);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
@@ -1456,7 +1526,9 @@ __device__ __noinline__ void phase_mla_b(const Params& p, const LayerDesc& L, in
 // Task (h, 128-column block of the latent); all tokens at once, so each
 // slice of W_uk is read once.  W_kvb is row-major [nh*(nope+v)][512]: head
 // h's rows are [W_uk,h (nope rows) | W_uv,h (v rows)].
-__device__ __noinline__ void phase_mla_absorb(const Params& p, const LayerDesc& L) {
+__device__ __noinline__ void phase_mla_absorb(KParams& pk, int l_layer) {
+  PARAMS;
+  KLayer& L = layer_ref(p, l_layer);
   const int B = p.B, nh = p.mla_h, nope = p.nope, QW = nope + MLA_RD, VW = nope + p.vdim;
   constexpr int NCB = MLA_KL / 128;
   const int ntask = nh * NCB;
@@ -1561,7 +1633,9 @@ __device__ __forceinline__ void mla_store_block(const i32x4 (&pf)[9], int buf) {
   }
 }
 
-__device__ __noinline__ void phase_mla_attn(const Params& p, const LayerDesc& L) {
+__device__ __noinline__ void phase_mla_attn(KParams& pk, int l_layer) {
+  PARAMS;
+  KLayer& L = layer_ref(p, l_layer);
   MlaSmem& sm = *(MlaSmem*)md_smem;
   const int B = p.B, nh = p.mla_h, C = p.mla_chunks;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -1694,7 +1768,9 @@ __device__ __noinline__ void phase_mla_attn(const Params& p, const LayerDesc& L)
 
 // M5: combine the chunks of each head and un-absorb: o_h = W_uv,h z_h.
 // Task (h, 32-row slice of W_uv,h) for all tokens.
-__device__ __noinline__ void phase_mla_out(const Params& p, const LayerDesc& L) {
+__device__ __noinline__ void phase_mla_out(KParams& pk, int l_layer) {
+  PARAMS;
+  KLayer& L = layer_ref(p, l_layer);
   const int B = p.B, nh = p.mla_h, nope = p.nope, vd = p.vdim, VW = nope + vd, C = p.mla_chunks;
   const int nsl = vd / 32;
   const int ntask = nh * nsl;
@@ -1822,7 +1898,9 @@ static_assert(ROUTE_OFF + sizeof(RouteSmem) <= MD_SMEM_BYTES, "LDS layout exceed
 // sum of squares of x.
 enum : int { RES_OPROJ = 0, RES_DENSE_DOWN = 1, RES_MOE_DOWN = 2, RES_MLA_O = 3, RES_KDA_O = 4 };
 
-__device__ __noinline__ void phase_residual(const Params& p, const LayerDesc& L, int mode, const uint16_t* g_next, int wait_idx) {
+__device__ __noinline__ void phase_residual(KParams& pk, int l_layer, int mode, const uint16_t* g_next, int wait_idx) {
+  PARAMS;
+  KLayer& L = layer_ref(p, l_layer);
   const int B = p.B, H = p.H;
   const RowSplit own = owned_rows(H, blockIdx.x, gridDim.x);
   const int nrow = own.r1 - own.r0;
@@ -1891,7 +1969,7 @@ __device__ __noinline__ void phase_residual(const Params& p, const LayerDesc& L,
   __syncthreads();
   sub_stamp(p, 0);
   const int r0 = own.r0;
-  gemv_run(gs, p, 0, 0u, [=](int g, int rb) {
+  gemv_run(p, gs, 0, 0u, [=](int g, int rb) {
     for (int e = threadIdx.x; e < TG * 16 * B; e += NT) {
       int t = e % B, rr = (e / B) % 16, i = e / (B * 16);
       int m, row;
@@ -1914,7 +1992,9 @@ __device__ __noinline__ void phase_residual(const Params& p, const LayerDesc& L,
 }
 
 // --- dense SwiGLU gate/up: h = silu(inv*Wg U) * (inv*Wu U) -> hi/lo
-__device__ __noinline__ void phase_gateup(const Params& p, const LayerDesc& L, int wait_idx) {
+__device__ __noinline__ void phase_gateup(KParams& pk, int l_layer, int wait_idx) {
+  PARAMS;
+  KLayer& L = layer_ref(p, l_layer);
   const int B = p.B, F = p.ffn;
   SlotBuilder sb;
   if (threadIdx.x == 0) {
@@ -1929,7 +2009,7 @@ __device__ __noinline__ void phase_gateup(const Params& p, const LayerDesc& L, i
   gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
   wait_point(p, wait_idx);
   sub_stamp(p, 0);
-  gemv_run(gs, p, p.H, p.off_ssq, EPI_SWIGLU);
+  gemv_run(p, gs, p.H, p.off_ssq, EPI_SWIGLU);
   sub_stamp(p, 2);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
@@ -1953,7 +2033,9 @@ __device__ __noinline__ void phase_gateup(const Params& p, const LayerDesc& L, i
 // run as one residual phase.
 
 
-__device__ __noinline__ void phase_moe_a(const Params& p, const LayerDesc& L, int wait_idx) {
+__device__ __noinline__ void phase_moe_a(KParams& pk, int l_layer, int wait_idx) {
+  PARAMS;
+  KLayer& L = layer_ref(p, l_layer);
   const int B = p.B;
   SlotBuilder sb;
   if (threadIdx.x == 0) {
@@ -1973,7 +2055,7 @@ __device__ __noinline__ void phase_moe_a(const Params& p, const LayerDesc& L, in
   gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
   wait_point(p, wait_idx);
   sub_stamp(p, 0);
-  gemv_run(gs, p, p.H, p.off_ssq, [=](int g, int rb) {
+  gemv_run(p, gs, p.H, p.off_ssq, [=](int g, int rb) {
     if (GSM.grp[g].kind == GK_PAIR) {
       for (int e = threadIdx.x; e < 16 * B; e += NT) {
         int t = e % B, rr = e / B;
@@ -2007,7 +2089,8 @@ __device__ __noinline__ void phase_moe_a(const Params& p, const LayerDesc& L, in
 // weights softmax(logits) over all experts at the chosen ones, renormalised
 // over the chosen ones when norm_topk.  Every workgroup runs this on the same
 // data in the same order.  Workgroup 0 reports the choices.
-__device__ __noinline__ void compute_routes(const Params& p, int layer) {
+__device__ __noinline__ void compute_routes(KParams& pk, int layer) {
+  PARAMS;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int E = p.n_experts, k = p.top_k, B = p.B;
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
@@ -2059,7 +2142,9 @@ __device__ __noinline__ void compute_routes(const Params& p, int layer) {
   __syncthreads();
 }
 
-__device__ __noinline__ void phase_moe_b(const Params& p, const LayerDesc& L, int wait_idx) {
+__device__ __noinline__ void phase_moe_b(KParams& pk, int l_layer, int wait_idx) {
+  PARAMS;
+  KLayer& L = layer_ref(p, l_layer);
   const int B = p.B;
   SlotBuilder sb;
   if (threadIdx.x == 0) {
@@ -2076,7 +2161,7 @@ __device__ __noinline__ void phase_moe_b(const Params& p, const LayerDesc& L, in
   gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
   wait_point(p, wait_idx);
   sub_stamp(p, 0);
-  gemv_run(gs, p, p.H, p.off_ssq, EPI_SWIGLU);
+  gemv_run(p, gs, p.H, p.off_ssq, EPI_SWIGLU);
   sub_stamp(p, 2);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
@@ -2090,7 +2175,8 @@ __device__ __noinline__ void phase_moe_b(const Params& p, const LayerDesc& L, in
 }
 
 // --- final norm + LM head: logits, per-WG argmax candidates
-__device__ __noinline__ void phase_lmhead(const Params& p, int wait_idx) {
+__device__ __noinline__ void phase_lmhead(KParams& pk, int wait_idx) {
+  PARAMS;
   const int B = p.B;
   SlotBuilder sb;
   if (threadIdx.x == 0) {
@@ -2104,7 +2190,7 @@ __device__ __noinline__ void phase_lmhead(const Params& p, int wait_idx) {
   gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
   wait_point(p, wait_idx);
   sub_stamp(p, 0);
-  gemv_run(gs, p, p.H, p.off_ssq, EPI_SCALED_SINGLE);
+  gemv_run(p, gs, p.H, p.off_ssq, EPI_SCALED_SINGLE);
   sub_stamp(p, 2);
   static_assert(sizeof(GemvSmem::in) >= 2 * sizeof(float) * NT * MAXB, "argmax scratch reuses the input staging");
   float* bv = &GSM.in[0][0];             // [NT][MAXB] best value (the input staging is unused here)
@@ -2137,7 +2223,8 @@ __device__ __noinline__ void phase_lmhead(const Params& p, int wait_idx) {
 }
 
 // final argmax over the WG candidates (one workgroup)
-__device__ __noinline__ void final_argmax(const Params& p) {
+__device__ __noinline__ void final_argmax(KParams& pk) {
+  PARAMS;
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
@@ -2174,30 +2261,32 @@ enum : int {
   PH_LMHEAD, PH_ARGMAX
 };
 
-__device__ __forceinline__ void run_one_phase(const Params& p, int layer, int phase) {
+__device__ __forceinline__ void run_one_phase(KParams& pk, int layer, int phase) {
+  PARAMS;
   const int l = layer < 0 ? 0 : layer;
-  const LayerDesc& L = p.layers[l];
-  const uint16_t* g_next = (l + 1 < p.n_layers) ? p.layers[l + 1].attn_norm : p.final_norm;
+  const int l_layer = l;
+  KLayer& L = layer_ref(p, l);
+  const uint16_t* g_next = (l + 1 < p.n_layers) ? layer_ref(p, l + 1).attn_norm : p.final_norm;
   switch (phase) {
     case PH_EMBED: clear_next_bank(p); phase_embed(p); break;
-    case PH_QKV: phase_qkv(p, L, -1); break;
-    case PH_KV_WRITE: phase_gqa_kv_write(p, L); break;
-    case PH_ATTN: phase_attn_gqa(p, L, l, -1); break;
-    case PH_OPROJ: phase_residual(p, L, RES_OPROJ, L.ffn_norm, -1); break;
-    case PH_GATEUP: phase_gateup(p, L, -1); break;
-    case PH_DOWN: phase_residual(p, L, RES_DENSE_DOWN, g_next, -1); break;
-    case PH_MOE_A: phase_moe_a(p, L, -1); break;
-    case PH_MOE_B: compute_routes(p, l); phase_moe_b(p, L, -1); break;
-    case PH_MOE_C: compute_routes(p, l); phase_residual(p, L, RES_MOE_DOWN, g_next, -1); break;
-    case PH_KDA_PROJ: phase_kda_proj(p, L, -1); break;
-    case PH_KDA_REC: phase_kda_rec(p, L); break;
-    case PH_KDA_O: phase_residual(p, L, RES_KDA_O, L.ffn_norm, -1); break;
-    case PH_MLA_A: phase_mla_a(p, L, -1); break;
-    case PH_MLA_B: phase_mla_b(p, L, -1); break;
-    case PH_MLA_ABS: phase_mla_absorb(p, L); break;
-    case PH_MLA_ATTN: phase_mla_attn(p, L); break;
-    case PH_MLA_OUT: phase_mla_out(p, L); break;
-    case PH_MLA_O: phase_residual(p, L, RES_MLA_O, L.ffn_norm, -1); break;
+    case PH_QKV: phase_qkv(p, l_layer, -1); break;
+    case PH_KV_WRITE: phase_gqa_kv_write(p, l_layer); break;
+    case PH_ATTN: phase_attn_gqa(p, l_layer, l, -1); break;
+    case PH_OPROJ: phase_residual(p, l_layer, RES_OPROJ, L.ffn_norm, -1); break;
+    case PH_GATEUP: phase_gateup(p, l_layer, -1); break;
+    case PH_DOWN: phase_residual(p, l_layer, RES_DENSE_DOWN, g_next, -1); break;
+    case PH_MOE_A: phase_moe_a(p, l_layer, -1); break;
+    case PH_MOE_B: compute_routes(p, l); phase_moe_b(p, l_layer, -1); break;
+    case PH_MOE_C: compute_routes(p, l); phase_residual(p, l_layer, RES_MOE_DOWN, g_next, -1); break;
+    case PH_KDA_PROJ: phase_kda_proj(p, l_layer, -1); break;
+    case PH_KDA_REC: phase_kda_rec(p, l_layer); break;
+    case PH_KDA_O: phase_residual(p, l_layer, RES_KDA_O, L.ffn_norm, -1); break;
+    case PH_MLA_A: phase_mla_a(p, l_layer, -1); break;
+    case PH_MLA_B: phase_mla_b(p, l_layer, -1); break;
+    case PH_MLA_ABS: phase_mla_absorb(p, l_layer); break;
+    case PH_MLA_ATTN: phase_mla_attn(p, l_layer); break;
+    case PH_MLA_OUT: phase_mla_out(p, l_layer); break;
+    case PH_MLA_O: phase_residual(p, l_layer, RES_MLA_O, L.ffn_norm, -1); break;
     case PH_LMHEAD: phase_lmhead(p, -1); break;
     case PH_ARGMAX: if (blockIdx.x == 0) final_argmax(p); break;
     default: break;
@@ -2205,7 +2294,9 @@ __device__ __forceinline__ void run_one_phase(const Params& p, int layer, int ph
 }
 
 // ===================================================================== kernel
-extern "C" __global__ __launch_bounds__(NT) void md_megakernel(Params p) {
+extern "C" __global__ __launch_bounds__(NT) void md_megakernel(Params p_arg) {
+  KParams& p = *(KParams*)__builtin_amdgcn_kernarg_segment_ptr();
+  (void)p_arg;
   if (p.B < 1 || p.B > MAXB) return;
   if (p.ml_phase >= 0) {  // one phase of the multi-launch step
     if (threadIdx.x == 0) md_cur_phase = 0;
@@ -2216,7 +2307,7 @@ extern "C" __global__ __launch_bounds__(NT) void md_megakernel(Params p) {
   clear_next_bank(p);
   int sidx = 0;
   if (threadIdx.x == 0) md_cur_phase = 0;
-  // Every sync point s is split: grid_arrive(s) when this workgroup's share
+  // Every sync point s is split: grid_arrive(p, s) when this workgroup's share
   // is done; the next phase waits for s itself -- a weight-streaming phase
   // after issuing its first weight loads (they depend on nobody), any other
   // phase first thing (WAIT).
@@ -2225,60 +2316,61 @@ extern "C" __global__ __launch_bounds__(NT) void md_megakernel(Params p) {
   phase_embed(p);
   ARRIVE();
   for (int l = 0; l < p.n_layers; ++l) {
-    const LayerDesc& L = p.layers[l];
-    const uint16_t* g_next = (l + 1 < p.n_layers) ? p.layers[l + 1].attn_norm : p.final_norm;
+    const int l_layer = l;
+    KLayer& L = layer_ref(p, l);
+    const uint16_t* g_next = (l + 1 < p.n_layers) ? layer_ref(p, l + 1).attn_norm : p.final_norm;
     const int kind = L.kind;
     if (kind == LK_GQA) {
-      phase_qkv(p, L, sidx++);
+      phase_qkv(p, l_layer, sidx++);
       ARRIVE();
       if (p.verify) {
         WAIT();
-        phase_gqa_kv_write(p, L);
+        phase_gqa_kv_write(p, l_layer);
         ARRIVE();
       }
-      phase_attn_gqa(p, L, l, sidx++);
+      phase_attn_gqa(p, l_layer, l, sidx++);
       ARRIVE();
-      phase_residual(p, L, RES_OPROJ, L.ffn_norm, sidx++);
+      phase_residual(p, l_layer, RES_OPROJ, L.ffn_norm, sidx++);
       ARRIVE();
     } else if (kind == LK_KDA) {
-      phase_kda_proj(p, L, sidx++);
+      phase_kda_proj(p, l_layer, sidx++);
       ARRIVE();
       WAIT();
-      if (p.verify) phase_kda_rec_verify(p, L);
-      else phase_kda_rec(p, L);
+      if (p.verify) phase_kda_rec_verify(p, l_layer);
+      else phase_kda_rec(p, l_layer);
       ARRIVE();
-      phase_residual(p, L, RES_KDA_O, L.ffn_norm, sidx++);
+      phase_residual(p, l_layer, RES_KDA_O, L.ffn_norm, sidx++);
       ARRIVE();
     } else {
-      phase_mla_a(p, L, sidx++);
+      phase_mla_a(p, l_layer, sidx++);
       ARRIVE();
-      phase_mla_b(p, L, sidx++);
-      ARRIVE();
-      WAIT();
-      phase_mla_absorb(p, L);
+      phase_mla_b(p, l_layer, sidx++);
       ARRIVE();
       WAIT();
-      phase_mla_attn(p, L);
+      phase_mla_absorb(p, l_layer);
       ARRIVE();
       WAIT();
-      phase_mla_out(p, L);
+      phase_mla_attn(p, l_layer);
       ARRIVE();
-      phase_residual(p, L, RES_MLA_O, L.ffn_norm, sidx++);
+      WAIT();
+      phase_mla_out(p, l_layer);
+      ARRIVE();
+      phase_residual(p, l_layer, RES_MLA_O, L.ffn_norm, sidx++);
       ARRIVE();
     }
     if (p.n_experts == 0) {
-      phase_gateup(p, L, sidx++);
+      phase_gateup(p, l_layer, sidx++);
       ARRIVE();
-      phase_residual(p, L, RES_DENSE_DOWN, g_next, sidx++);
+      phase_residual(p, l_layer, RES_DENSE_DOWN, g_next, sidx++);
       ARRIVE();
     } else {
-      phase_moe_a(p, L, sidx++);
+      phase_moe_a(p, l_layer, sidx++);
       ARRIVE();
       WAIT();
       compute_routes(p, l);
-      phase_moe_b(p, L, -1);
+      phase_moe_b(p, l_layer, -1);
       ARRIVE();
-      phase_residual(p, L, RES_MOE_DOWN, g_next, sidx++);
+      phase_residual(p, l_layer, RES_MOE_DOWN, g_next, sidx++);
       ARRIVE();
     }
     if (dev_failed(p)) return;

@@ -119,6 +119,7 @@ md_status validate(const md_config* c) {
       return fail(MD_EINVAL, "n_q_heads must be a positive multiple of n_kv_heads");
     if (c->n_q_heads / c->n_kv_heads > 8) return fail(MD_EUNSUPPORTED, "at most 8 query heads per kv head");
     if (c->head_dim != 64 && c->head_dim != 128) return fail(MD_EUNSUPPORTED, "head_dim must be 64 or 128");
+    if (c->max_ctx % 32) return fail(MD_EUNSUPPORTED, "max_ctx must be a multiple of 32 (V cache tiles)");
   } else if (c->attn_kind == 1) {
     if (c->mla_every < 1) return fail(MD_EINVAL, "mla_every must be >= 1");
     bool has_mla = c->n_layers >= c->mla_every, has_kda = c->mla_every > 1;
@@ -168,6 +169,17 @@ struct WsLayout {
   int rope_d;
   int n_sync, sync_attn_base;
 };
+
+// GQA key/value chunks per (row, kv head): enough tasks to cover the grid,
+// at most one per 32-position tile of the cache.
+int attn_chunks(const md_config* c, int grid, int rows) {
+  const int pairs = rows * (c->n_kv_heads > 0 ? c->n_kv_heads : 1);
+  int C = grid / pairs;
+  const int tiles = (c->max_ctx + 31) / 32;
+  if (C > tiles) C = tiles;
+  if (C > CMAX) C = CMAX;
+  return C < 1 ? 1 : C;
+}
 
 WsLayout ws_layout(const md_config* c) {
   WsLayout w{};
@@ -436,11 +448,7 @@ static md_status fill_params(md_model* m, const int32_t* tokens, const int32_t* 
   p.n_experts = c->n_experts; p.top_k = c->top_k; p.expert_ffn = c->expert_ffn; p.n_shared = c->n_shared;
   p.shared_ffn = c->shared_ffn; p.norm_topk = c->norm_topk;
   p.B = batch;
-  int pairs = batch * (c->n_kv_heads > 0 ? c->n_kv_heads : 1);
-  int C = m->grid / pairs;
-  if (C < 1) C = 1;
-  if (C > CMAX) C = CMAX;
-  p.attn_chunks = C;
+  p.attn_chunks = attn_chunks(c, m->grid, batch);
   p.tokens = tokens; p.positions = positions; p.kv = (uint8_t*)kv; p.logits = out_logits;
   p.out_tokens = out_tokens; p.out_ids = out_ids;
   p.ws = m->ws; p.ws_bytes = (uint32_t)w.total;
@@ -519,9 +527,7 @@ md_status md_verify_step(md_model* m, const int32_t* tokens, const int32_t* posi
   p.out_accept = out_accept_len;
   p.out_next = out_next_token;
   {
-    int pairs = n_tok * (c->n_kv_heads > 0 ? c->n_kv_heads : 1);
-    int C = m->grid / pairs;
-    p.attn_chunks = C < 1 ? 1 : (C > CMAX ? CMAX : C);
+    p.attn_chunks = attn_chunks(c, m->grid, n_tok);
     int cm = m->grid / n_tok;
     int by_ctx = (c->max_ctx + 31) / 32;
     if (cm > by_ctx) cm = by_ctx;

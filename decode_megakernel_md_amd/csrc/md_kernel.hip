@@ -734,18 +734,25 @@ __device__ __forceinline__ void rope_cs(KParams& pk, int pos, int i, float& c, f
 }
 
 // --- GQA decode attention.  Task (b, kv head g, chunk c) covers cached
-// positions [c*P, (c+1)*P) of sequence b (positions 0..pos inclusive, the new
-// row included).  Each wave takes a quarter of the chunk in 32-position
-// blocks, with the next block's K and V rows in flight while the current one
-// is used: scores on the matrix cores (K rows as the A operand, the group's
-// rotated q heads as hi/lo B columns), an online softmax per head, and P.V on
-// the vector ALUs.  The chunk's partial (max, sum, o) per head goes to the
-// workspace; the last workgroup to finish a (b, g) combines the chunks.
+// positions [a0, a1) of sequence b, chunk boundaries on 32-position tiles.
+// Each wave takes a quarter of the chunk's tiles, one 32-position block per
+// tile, with the next block's K and V in flight while the current one is
+// used.  Both products run on the matrix cores:
+//   scores S^T = K . Q: K rows are the A operand, the group's rotated q heads
+//     the B columns (head h: column 2h its bf16 high part, 2h+1 the rest);
+//   output O^T = V^T . P: the V tile (stored dimension-major) is the A
+//     operand, the probabilities the B columns (column 2h the high bf16 part
+//     of head h's, 2h+1 the rest).
+// The score tile's rows are permuted (row 4i+j of K tile tt is position
+// 8i+4tt+j of the block) so that each lane's scores are exactly the eight
+// positions its B column of P needs: the online softmax runs in registers,
+// per column, with cross-row swaps only.  The task's partial (max, sum, o)
+// per head goes to the workspace; the last workgroup to finish a (b, g)
+// combines the chunks.
 struct AttnSmem {
   float q[MAXB][128];           // rotated, scaled q of the group's heads
-  float s[NW][32][MAXB];        // per-wave scores / probabilities of a block
   float wm[NW + 1][MAXB], wl[NW + 1][MAXB];  // entry NW: the new row (decode, last chunk)
-  float wo[NW][MAXB][128];
+  alignas(16) float wo[NW][MAXB][128];
   float knew[128], vnew[128];   // the new row, as the cache stores it
   int last;
 };
@@ -753,65 +760,70 @@ struct AttnSmem {
 template <int HD>
 struct KVBlock {
   i32x4 k[2][HD / 32];          // 2 tiles of 16 positions x HD/32 k-steps
-  i32x4 v[HD / 16];             // 32 positions x HD bf16 = HD/16 loads of 1 KB per wave
+  i32x4 v[HD / 16];             // the V tile: HD/16 slices of 16 dims x 32 positions
 };
 
+// Block at blk (a multiple of 32) of a wave share ending at w1.  K is
+// row-major [pos][HD]; V is the tile (blk/32) of [tile][HD][32].
 template <int HD, int CP>
 __device__ __forceinline__ void load_block(KVBlock<HD>& r, rsrc_t krs, rsrc_t vrs, int blk, int w1, int lane) {
+  const int m = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    int prow = blk + tt * 16 + (lane & 15);
+    const int prow = blk + 8 * (m >> 2) + 4 * tt + (m & 3);
 #pragma unroll
     for (int s = 0; s < HD / 32; ++s) {
-      uint32_t off = (prow < w1 && blk < w1) ? (uint32_t)(prow * HD + s * 32 + (lane >> 4) * 8) * 2u : OOB;
+      uint32_t off = (prow < w1) ? (uint32_t)(prow * HD + s * 32 + g * 8) * 2u : OOB;
       r.k[tt][s] = ld_x4<CP>(krs, off);
     }
   }
-  // V: lanes split a row into HD/8 chunks of 8 dims; one instruction covers 64/(HD/8) rows
-  constexpr int LPR = HD / 8;
-  constexpr int RPI = 64 / LPR;
 #pragma unroll
   for (int q = 0; q < HD / 16; ++q) {
-    int t = blk + q * RPI + lane / LPR;
-    uint32_t off = (t < w1 && blk < w1) ? (uint32_t)(t * HD + (lane % LPR) * 8) * 2u : OOB;
+    uint32_t off = blk < w1 ? (uint32_t)(blk * HD + (q * 16 + m) * 32 + g * 8) * 2u : OOB;
     r.v[q] = ld_x4<CP>(vrs, off);
   }
 }
 
 #define ASM (*reinterpret_cast<AttnSmem*>(md_smem))
 
-// The wave's blocks ba (positions w0..) and bb (w0 + 32..) are already in
-// flight when it is called; each block used is refilled two blocks ahead.
-template <int HD, int GS, int CP>
-__device__ __forceinline__ void attn_task_wave(rsrc_t krs, rsrc_t vrs, int w0, int w1) {
-  constexpr int gs = GS;
+// bf16 pairs of (x0, x1) as one 32-bit word (round to nearest even)
+__device__ __forceinline__ uint32_t cvt_bf16x2(float x0, float x1) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  f32x2 v = {x0, x1};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// One wave's share [w0, w1) of a task.  Its first two blocks (w0, w0 + 32)
+// are in flight in ba, bb on entry; each block used is refilled two blocks
+// ahead.  Leaves the wave's (max, sum, o) per head in ASM.wm/wl/wo[wv].
+template <int HD, int CP>
+__device__ __forceinline__ void attn_wave(KVBlock<HD>& ba, KVBlock<HD>& bb, rsrc_t krs, rsrc_t vrs, int w0, int w1,
+                                          int gs) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  w0 = __builtin_amdgcn_readfirstlane(w0);
-  w1 = __builtin_amdgcn_readfirstlane(w1);
-  const int nn = lane & 15, hh = nn >> 1, pp = nn & 1;
-  constexpr int LPR = HD / 8, RPI = 64 / LPR;
+  const int nn = lane & 15, hh = nn >> 1, pp = nn & 1, g = lane >> 4;
   bf16x8 qb[HD / 32];
 #pragma unroll
   for (int s = 0; s < HD / 32; ++s) {
+    uint32_t u[4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      int d = s * 32 + (lane >> 4) * 8 + k;
-      float v = hh < gs ? ASM.q[hh][d] : 0.f;
-      uint16_t hi, lo;
-      split_hilo(v, hi, lo);
-      qb[s][k] = __builtin_bit_cast(__bf16, pp ? lo : hi);
+    for (int k = 0; k < 4; ++k) {
+      const int d = s * 32 + g * 8 + 2 * k;
+      const float v0 = hh < gs ? ASM.q[hh][d] : 0.f, v1 = hh < gs ? ASM.q[hh][d + 1] : 0.f;
+      const uint32_t hi = cvt_bf16x2(v0, v1);
+      // column 2h+1 carries q minus its bf16 high part
+      const float r0 = v0 - __uint_as_float(hi << 16), r1 = v1 - __uint_as_float(hi & 0xFFFF0000u);
+      u[k] = pp ? cvt_bf16x2(r0, r1) : hi;
     }
+    qb[s] = __builtin_bit_cast(bf16x8, u);
   }
-  float m_run[GS], l_run[GS], acc[GS][8];
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 acc[HD / 16];
 #pragma unroll
-  for (int h = 0; h < GS; ++h) {
-    m_run[h] = -INFINITY;
-    l_run[h] = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
-  }
+  for (int q = 0; q < HD / 16; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto block = [&](const KVBlock<HD>& cur, int blk) __attribute__((always_inline)) {
-    // scores of the 32 positions
+    // scores: lane holds positions blk + 8g + j (j < 8) of column nn
+    float sc[8];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       f32x4 a = {0.f, 0.f, 0.f, 0.f};
@@ -819,57 +831,59 @@ __device__ __forceinline__ void attn_task_wave(rsrc_t krs, rsrc_t vrs, int w0, i
       for (int s = 0; s < HD / 32; ++s)
         a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[tt][s]), qb[s], a, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = a[i] + dpp_f<DPP_QXOR1>(a[i]);
-        int pr = tt * 16 + 4 * (lane >> 4) + i;
-        if (!pp && hh < gs) ASM.s[wv][pr][hh] = (blk + pr < w1) ? v : -INFINITY;
-      }
+      for (int i = 0; i < 4; ++i) sc[4 * tt + i] = a[i] + dpp_f<DPP_QXOR1>(a[i]);
     }
-    __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
-    __builtin_amdgcn_wave_barrier();
-    // online softmax per head over this block; probabilities replace scores
+    if (blk + 32 > w1) {  // the share's last, partial block
 #pragma unroll
-    for (int h = 0; h < GS; ++h) {
-      {
-        float sv = lane < 32 ? ASM.s[wv][lane][h] : -INFINITY;
-        float mb = wave_max(sv);
-        float mn = fmaxf(m_run[h], mb);
-        float corr = __expf(m_run[h] - mn);
-        float pv = lane < 32 ? __expf(sv - mn) : 0.f;
-        l_run[h] = l_run[h] * corr + wave_sum(pv);
-        m_run[h] = mn;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[h][j] *= corr;
-        if (lane < 32) ASM.s[wv][lane][h] = pv;
-      }
+      for (int j = 0; j < 8; ++j)
+        if (blk + 8 * g + j >= w1) sc[j] = -INFINITY;
     }
-    __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
-    __builtin_amdgcn_wave_barrier();
-    // P.V: this lane holds 8 dims of the rows q*RPI + lane/LPR
+    float mb = sc[0];
 #pragma unroll
-    for (int q = 0; q < HD / 16; ++q) {
-      int t = q * RPI + lane / LPR;
-      uint32_t u[4] = {(uint32_t)cur.v[q][0], (uint32_t)cur.v[q][1], (uint32_t)cur.v[q][2], (uint32_t)cur.v[q][3]};
-      float vv[8];
+    for (int j = 1; j < 8; ++j) mb = fmaxf(mb, sc[j]);
+    mb = rows_max(mb);
+    const float mn = fmaxf(m_run, mb);  // finite: position blk is always valid
+    const float corr = __expf(m_run - mn);
+    float pr[8], ps = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        vv[2 * j] = __uint_as_float(u[j] << 16);
-        vv[2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
-      }
+    for (int j = 0; j < 8; ++j) {
+      pr[j] = __expf(sc[j] - mn);
+      ps += pr[j];
+    }
+    l_run = l_run * corr + rows_sum(ps);
+    m_run = mn;
+    uint32_t u[4];
 #pragma unroll
-      for (int h = 0; h < GS; ++h) {
-        {
-          float pw = ASM.s[wv][t][h];
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t hi = cvt_bf16x2(pr[2 * k], pr[2 * k + 1]);
+      const float r0 = pr[2 * k] - __uint_as_float(hi << 16);
+      const float r1 = pr[2 * k + 1] - __uint_as_float(hi & 0xFFFF0000u);
+      u[k] = pp ? cvt_bf16x2(r0, r1) : hi;
+    }
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, u);
+    if (blk + 32 > w1) {
+      // V rows past the share may hold anything (even non-finite values):
+      // zero this lane's positions >= w1 so that 0 * V cannot poison O
+      const int nv = w1 - blk - 8 * g;  // valid positions of this lane's eight
 #pragma unroll
-          for (int j = 0; j < 8; ++j) acc[h][j] += pw * vv[j];
+      for (int q = 0; q < HD / 16; ++q) {
+        i32x4 v = cur.v[q];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t keep = (2 * k + 1 < nv) ? 0xFFFFFFFFu : (2 * k < nv ? 0x0000FFFFu : 0u);
+          v[k] = (int)((uint32_t)v[k] & keep);
         }
+        acc[q] *= corr;
+        acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), pb, acc[q], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < HD / 16; ++q) {
+        acc[q] *= corr;
+        acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.v[q]), pb, acc[q], 0, 0, 0);
       }
     }
-    __builtin_amdgcn_wave_barrier();
   };
-  KVBlock<HD> ba, bb;
-  load_block<HD, CP>(ba, krs, vrs, w0, w1, lane);
-  load_block<HD, CP>(bb, krs, vrs, w0 + 32, w1, lane);
   for (int blk = w0; blk < w1; blk += 64) {
     block(ba, blk);
     if (blk + 32 >= w1) break;
@@ -878,36 +892,19 @@ __device__ __forceinline__ void attn_task_wave(rsrc_t krs, rsrc_t vrs, int w0, i
     if (blk + 64 >= w1) break;
     load_block<HD, CP>(bb, krs, vrs, blk + 96, w1, lane);
   }
-  // sum the lane groups that hold the same dims (different rows)
+  // head hh's output = column 2hh + column 2hh+1; lane holds dims 16q + 4g + i
+  if (hh < gs) {
 #pragma unroll
-  for (int h = 0; h < GS; ++h) {
-    {
+    for (int q = 0; q < HD / 16; ++q) {
+      f32x4 o;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float v = acc[h][j];
-        if (LPR == 8) v += dpp_f<DPP_ROR8>(v);  // lanes i and i^8 hold the same dims
-        acc[h][j] = rows_sum(v);
-      }
-      if (lane == 0) { ASM.wm[wv][h] = m_run[h]; ASM.wl[wv][h] = l_run[h]; }
-      if (lane < LPR) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ASM.wo[wv][h][lane * 8 + j] = acc[h][j];
-      }
+      for (int i = 0; i < 4; ++i) o[i] = acc[q][i] + dpp_f<DPP_QXOR1>(acc[q][i]);
+      if (!pp) *(f32x4*)&ASM.wo[wv][hh][16 * q + 4 * g] = o;
     }
-  }
-}
-
-template <int HD, int CP>
-__device__ __forceinline__ void attn_dispatch(int gs, rsrc_t krs, rsrc_t vrs, int w0, int w1) {
-  switch (gs) {
-    case 1: attn_task_wave<HD, 1, CP>(krs, vrs, w0, w1); break;
-    case 2: attn_task_wave<HD, 2, CP>(krs, vrs, w0, w1); break;
-    case 3: attn_task_wave<HD, 3, CP>(krs, vrs, w0, w1); break;
-    case 4: attn_task_wave<HD, 4, CP>(krs, vrs, w0, w1); break;
-    case 5: attn_task_wave<HD, 5, CP>(krs, vrs, w0, w1); break;
-    case 6: attn_task_wave<HD, 6, CP>(krs, vrs, w0, w1); break;
-    case 7: attn_task_wave<HD, 7, CP>(krs, vrs, w0, w1); break;
-    default: attn_task_wave<HD, 8, CP>(krs, vrs, w0, w1); break;
+    if (g == 0 && !pp) {
+      ASM.wm[wv][hh] = m_run;
+      ASM.wl[wv][hh] = l_run;
+    }
   }
 }
 
@@ -924,7 +921,8 @@ __device__ __noinline__ void phase_gqa_kv_write(KParams& pk, int l_layer) {
     const int pos = row_pos(p, b);
     uint16_t* kc = (uint16_t*)(p.kv + L.kv_off) + (size_t)(row_seq(p, b) * p.nkv + g) * p.max_ctx * hd;
     uint16_t* vc = kc + (size_t)p.max_batch * p.nkv * p.max_ctx * hd;
-    rsrc_t krs = make_rsrc_u(kc + (size_t)pos * hd, hd * 2), vrs = make_rsrc_u(vc + (size_t)pos * hd, hd * 2);
+    rsrc_t krs = make_rsrc_u(kc + (size_t)pos * hd, hd * 2);
+    rsrc_t vrs = make_rsrc_u(vc + (size_t)(pos & ~31) * hd, hd * 64);  // the V tile holding pos
     for (int i = threadIdx.x; i < hd / 2; i += NT) {
       int colk = p.nq * hd + g * hd;
       float a = ld_f32(wr, p.off_qkv + (uint32_t)(b * nqkv + colk + i) * 4u);
@@ -936,7 +934,8 @@ __device__ __noinline__ void phase_gqa_kv_write(KParams& pk, int l_layer) {
     }
     for (int i = threadIdx.x; i < hd; i += NT) {
       int colv = (p.nq + p.nkv) * hd + g * hd;
-      st_u16(vrs, (uint32_t)i * 2u, bf16_rne(ld_f32(wr, p.off_qkv + (uint32_t)(b * nqkv + colv + i) * 4u)));
+      st_u16(vrs, (uint32_t)(i * 32 + (pos & 31)) * 2u,
+             bf16_rne(ld_f32(wr, p.off_qkv + (uint32_t)(b * nqkv + colv + i) * 4u)));
     }
   }
 }
@@ -944,7 +943,8 @@ __device__ __noinline__ void phase_gqa_kv_write(KParams& pk, int l_layer) {
 // One task of the GQA attention phase: (sequence b, kv head g, chunk c) of
 // the cached rows, and this wave's share [w0, w1) of the chunk.  Decode: the
 // cached rows are 0..pos-1 (the new row is folded in by the combine); verify:
-// 0..pos (the new rows were written by phase_gqa_kv_write).
+// 0..pos (the new rows were written by phase_gqa_kv_write).  Chunks are
+// whole 32-position tiles (the last one ragged); waves split a chunk's tiles.
 struct AttnTask {
   int b, g, c, pos, n, a0, a1, w0, w1;
   const uint16_t* kc;
@@ -960,12 +960,13 @@ __device__ __forceinline__ AttnTask attn_task(KParams& pk, int l_layer, int task
   t.b = task / (C * p.nkv);
   t.pos = row_pos(p, t.b);
   t.n = p.verify ? t.pos + 1 : t.pos;
-  const int P = (t.n + C - 1) / C;
+  const int P = ((t.n + C - 1) / C + 31) & ~31;
   t.a0 = t.c * P < t.n ? t.c * P : t.n;
   t.a1 = (t.c + 1) * P < t.n ? (t.c + 1) * P : t.n;
-  const int wv = threadIdx.x >> 6, len = t.a1 - t.a0;
-  t.w0 = t.a0 + len * wv / NW;
-  t.w1 = t.a0 + len * (wv + 1) / NW;
+  const int wv = threadIdx.x >> 6, nt = (t.a1 - t.a0 + 31) >> 5;
+  t.w0 = t.a0 + 32 * (nt * wv / NW);
+  const int e = t.a0 + 32 * (nt * (wv + 1) / NW);
+  t.w1 = e < t.a1 ? e : t.a1;
   t.kc = (const uint16_t*)(p.kv + L.kv_off) + (size_t)(row_seq(p, t.b) * p.nkv + t.g) * p.max_ctx * hd;
   t.vc = t.kc + (size_t)p.max_batch * p.nkv * p.max_ctx * hd;
   return t;
@@ -975,13 +976,15 @@ __device__ __forceinline__ AttnTask attn_task(KParams& pk, int l_layer, int task
 // the workspace; when decoding, the task of the last chunk also folds in the
 // new row, computed in place (q . k_new, v_new) rather than read back from
 // the cache it writes.  The last workgroup to finish a (b, g) combines the
-// chunks with one round of loads (a running max over the chunks).  Inlined
-// into the kernel, as is the per-wave worker: as a called function it would
-// save and restore the callee-saved registers its live values occupy.
-template <int HD>
+// chunks with one round of loads (a running max over the chunks).  When
+// decoding, the first task's first K/V blocks are requested before the wait
+// for the q/k/v projections (the cached rows do not depend on them).
+// Inlined into the kernel: as a called function it would save and restore
+// the callee-saved registers its live values occupy.
+template <int HD, bool VERIFY>
 __device__ __forceinline__ void attn_phase(KParams& pk, int l_layer, int layer, int wait_idx) {
   PARAMS;
-  KLayer& L = layer_ref(p, l_layer);
+  constexpr int CP = VERIFY ? CP_SC1 : 0;
   AttnSmem& sm = *(AttnSmem*)md_smem;
   const int lane = threadIdx.x & 63;
   const int gs = p.nq / p.nkv, B = p.B;
@@ -990,12 +993,22 @@ __device__ __forceinline__ void attn_phase(KParams& pk, int l_layer, int layer, 
   const int nqkv = (p.nq + 2 * p.nkv) * HD;
   rsrc_t wr = make_rsrc_u(p.ws, p.ws_bytes);
   const float scale = 1.0f / sqrtf((float)HD);
+  KVBlock<HD> ba, bb;
+  AttnTask t;
+  rsrc_t krs, vrs;
+  auto start = [&](int task) __attribute__((always_inline)) {
+    t = attn_task(p, l_layer, task);
+    const int nt = (t.n + 31) >> 5;
+    krs = make_rsrc_u(t.kc, (uint32_t)((size_t)t.n * HD * 2));
+    vrs = make_rsrc_u(t.vc, (uint32_t)((size_t)nt * 32 * HD * 2));
+    load_block<HD, CP>(ba, krs, vrs, t.w0, t.w1, lane);
+    load_block<HD, CP>(bb, krs, vrs, t.w0 + 32, t.w1, lane);
+  };
+  if (!VERIFY && (int)blockIdx.x < ntask) start(blockIdx.x);
   wait_point(p, wait_idx);
   for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
-    const AttnTask t = attn_task(p, l_layer, task);
+    if (VERIFY || task != (int)blockIdx.x) start(task);
     const int b = t.b, g = t.g, c = t.c, pos = t.pos;
-    const uint32_t nb = (uint32_t)((size_t)t.n * HD * 2);
-    rsrc_t krs = make_rsrc_u(t.kc, nb), vrs = make_rsrc_u(t.vc, nb);
     for (int e = threadIdx.x; e < gs * (HD / 2); e += NT) {
       int h = e / (HD / 2), i = e % (HD / 2);
       int col = (g * gs + h) * HD;
@@ -1008,10 +1021,10 @@ __device__ __forceinline__ void attn_phase(KParams& pk, int l_layer, int layer, 
     }
     // decode: the task of the last chunk folds the new row into its partial
     // (and writes it to the cache; nothing reads it back in this step)
-    const bool newrow = !p.verify && c == C - 1;
+    const bool newrow = !VERIFY && c == C - 1;
     if (newrow) {
       uint16_t* kc = const_cast<uint16_t*>(t.kc);
-      uint16_t* vc = const_cast<uint16_t*>(t.vc);
+      uint16_t* vt = const_cast<uint16_t*>(t.vc) + (size_t)(pos & ~31) * HD + (pos & 31);  // V tile of pos
       for (int i = threadIdx.x; i < HD / 2; i += NT) {
         int colk = p.nq * HD + g * HD;
         float a = ld_f32(wr, p.off_qkv + (uint32_t)(b * nqkv + colk + i) * 4u);
@@ -1027,7 +1040,7 @@ __device__ __forceinline__ void attn_phase(KParams& pk, int l_layer, int layer, 
       for (int i = threadIdx.x; i < HD; i += NT) {
         int colv = (p.nq + p.nkv) * HD + g * HD;
         uint16_t v0 = bf16_rne(ld_f32(wr, p.off_qkv + (uint32_t)(b * nqkv + colv + i) * 4u));
-        vc[(size_t)pos * HD + i] = v0;
+        vt[i * 32] = v0;
         sm.vnew[i] = bf16_f32(v0);
       }
     }
@@ -1042,8 +1055,7 @@ __device__ __forceinline__ void attn_phase(KParams& pk, int l_layer, int layer, 
       }
     }
     sub_stamp(p, 0);
-    if (p.verify) attn_dispatch<HD, CP_SC1>(gs, krs, vrs, t.w0, t.w1);
-    else attn_dispatch<HD, 0>(gs, krs, vrs, t.w0, t.w1);
+    attn_wave<HD, CP>(ba, bb, krs, vrs, t.w0, t.w1, gs);
     __syncthreads();
     sub_stamp(p, 3);
     // this task's partial: (m, l) in part_ml[b][head][c]; o in part_o[b][head][c][hd]
@@ -1125,8 +1137,13 @@ __device__ __forceinline__ void attn_phase(KParams& pk, int l_layer, int layer, 
 __device__ __forceinline__ void phase_attn_gqa(KParams& pk, int l_layer, int layer, int wait_idx) {
   PARAMS;
   KLayer& L = layer_ref(p, l_layer);
-  if (p.hd == 128) attn_phase<128>(p, l_layer, layer, wait_idx);
-  else attn_phase<64>(p, l_layer, layer, wait_idx);
+  if (p.verify) {
+    if (p.hd == 128) attn_phase<128, true>(p, l_layer, layer, wait_idx);
+    else attn_phase<64, true>(p, l_layer, layer, wait_idx);
+  } else {
+    if (p.hd == 128) attn_phase<128, false>(p, l_layer, layer, wait_idx);
+    else attn_phase<64, false>(p, l_layer, layer, wait_idx);
+  }
 }
 
 // ------------------------------------------------------------------ gated delta rule
@@ -2385,6 +2402,7 @@ extern "C" __global__ __launch_bounds__(NT) void md_megakernel(Params p_arg) {
 #undef WAIT
 #undef ARRIVE
   // the last workgroup to arrive reduces the argmax candidates
+  stamp(p, 2 * sidx);
   bool last = arrive(p, sidx);
   if (threadIdx.x == 0) ((int*)md_smem)[0] = last;
   __syncthreads();

@@ -11,10 +11,18 @@ from typing import Dict, Optional
 import numpy as np
 
 import synth
-from synth.workloads import Workload, kv_layout, tensor_inventory
+from synth.workloads import V_TILE, Workload, kv_layout, tensor_inventory
 
 from . import _lib
 from ._lib import check, config_from, lib
+
+
+def v_logical(v: np.ndarray) -> np.ndarray:
+    """A GQA V cache [.., max_ctx, head_dim] as stored (V_TILE-position tiles,
+    dim-major within a tile) -> the same values in row order."""
+    *lead, C, D = v.shape
+    t = v.reshape(*lead, C // V_TILE, D, V_TILE)
+    return np.swapaxes(t, -1, -2).reshape(*lead, C, D)
 
 
 def _align(x: int, a: int = 256) -> int:
@@ -98,7 +106,9 @@ class DeviceModel:
             synth.kv_layer_device(self.w, l, base + off, sptr)
 
     def kv_layer(self, l: int):
-        """Device tensor view of layer l's cache / state (shape per synth.kv_layout)."""
+        """Device tensor view of layer l's cache / state as stored (shape per
+        synth.kv_layout; for a GQA layer, index 1 is V in its stored tile
+        order: view it with v_logical)."""
         torch = self.torch
         kind, off, nbytes, shape, dt = self.kv_layout[l]
         raw = self.kv[off:off + nbytes]
@@ -109,12 +119,15 @@ class DeviceModel:
         return raw.view(torch.int16).view(*shape)
 
     def kv_host(self):
-        """Host copies of every layer's cache / state in the oracle's layout."""
+        """Host copies of every layer's cache / state in the oracle's layout
+        (GQA V converted from its tiles to [max_batch][n_kv][max_ctx][head_dim])."""
         out = []
         for l in range(self.w.n_layers):
             t = self.kv_layer(l).cpu().numpy()
             if t.dtype == np.int16:
                 t = t.view(np.uint16)
+            if self.kv_layout[l][0] == "gqa":
+                t = np.stack([t[0], v_logical(t[1])])
             out.append(np.ascontiguousarray(t))
         return out
 

@@ -39,8 +39,7 @@ class Tracer:
         import torch
         self.m = model
         self.G = lib().md_grid_size(model.handle)
-        self.n = 2 * n_sync_max + 1
-        self.n = 16384
+        self.n = max(2 * n_sync_max + 1, 16384)
         self.buf = torch.zeros((self.G, self.n), dtype=torch.int64, device=model.device)
         check(lib().md_set_trace(model.handle, ctypes.c_void_p(self.buf.data_ptr()), self.n))
 
@@ -60,7 +59,9 @@ class Tracer:
             end = t[:, 2 * s]
             work[:, s] = end - prev
             wait_end = t[:, 2 * s + 1]
-            release[s] = np.median(wait_end) - end.max()
+            # the last sync point of a decode step has no wait (its last
+            # arrival reduces the argmax)
+            release[s] = np.median(wait_end) - end.max() if np.all(wait_end > 0) else 0.0
             prev = wait_end
         total = t[:, 2 * (ns - 1)].max() - start.min()
         # sub-phase stamps (GEMV phases): 0 slots built, 1 first group flushed, 2 sweep done

@@ -111,7 +111,11 @@ size_t md_workspace_bytes(const md_config* cfg);
 
 /* Bytes of the KV / state buffer.  Per layer, in layer order, each region
  * starting on a 256-byte boundary:
- *   GQA layer: K bf16[max_batch][n_kv_heads][max_ctx][head_dim], then V (same shape)
+ *   GQA layer: K bf16[max_batch][n_kv_heads][max_ctx][head_dim], then
+ *              V bf16[max_batch][n_kv_heads][max_ctx / 32][head_dim][32]:
+ *              32-position tiles, dimension-major within a tile, so that
+ *              V[b][h][t][d] sits at ((b*n_kv_heads + h)*max_ctx + t/32*32)*head_dim
+ *              + d*32 + t%32 (max_ctx must be a multiple of 32)
  *   MLA layer: latent rows bf16[max_batch][max_ctx][kv_lora + rope_dim]
  *              (RMS-normalised latent, then the rotated key part)
  *   KDA layer: state fp32[max_batch][kda_heads][kda_dk][kda_dv]

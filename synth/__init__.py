@@ -16,7 +16,7 @@ from typing import Optional
 import numpy as np
 
 from . import workloads  # noqa: F401
-from .workloads import KV_SIGMA, TensorSpec, Workload, kv_layout, tensor_inventory  # noqa: F401
+from .workloads import KV_SIGMA, V_TILE, TensorSpec, Workload, kv_layout, tensor_inventory  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 HOST_SO = os.path.join(_HERE, "libsynth_host.so")
@@ -72,6 +72,9 @@ def _dev_lib():
             f = getattr(lib, fn)
             f.restype = ctypes.c_int
             f.argtypes = [ctypes.c_uint64, extra, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+        lib.synth_dev_normal_bf16_tiles.restype = ctypes.c_int
+        lib.synth_dev_normal_bf16_tiles.argtypes = [ctypes.c_uint64, ctypes.c_float, ctypes.c_void_p, ctypes.c_int64,
+                                                    ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
         lib.synth_dev_fill_u16.restype = ctypes.c_int
         lib.synth_dev_fill_u16.argtypes = [ctypes.c_uint16, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         _dev = lib
@@ -187,8 +190,10 @@ def kv_layer_device(w: Workload, layer: int, ptr: int, stream: int = 0) -> None:
     elif kind == "gqa":
         _dev_check(lib.synth_dev_normal_bf16(key(w.seed("kv"), f"L{layer}.k_cache"), scale_for(KV_SIGMA),
                                              ptr, n, 0, stream), "k")
-        _dev_check(lib.synth_dev_normal_bf16(key(w.seed("kv"), f"L{layer}.v_cache"), scale_for(KV_SIGMA),
-                                             ptr + n * 2, n, 0, stream), "v")
+        # V is stored in V_TILE-position tiles, dim-major within a tile
+        rows = n // w.head_dim
+        _dev_check(lib.synth_dev_normal_bf16_tiles(key(w.seed("kv"), f"L{layer}.v_cache"), scale_for(KV_SIGMA),
+                                                   ptr + n * 2, rows, w.head_dim, V_TILE, stream), "v")
     else:
         _dev_check(lib.synth_dev_normal_bf16(key(w.seed("kv"), f"L{layer}.mla_cache"), scale_for(KV_SIGMA),
                                              ptr, n, 0, stream), "mla")

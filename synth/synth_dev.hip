@@ -33,6 +33,19 @@ __global__ void k_normal_bf16(uint64_t key, float scale, uint16_t* out, int64_t 
     out[i] = f32_to_bf16_rne(irwin_hall4(sm64(key, (uint64_t)(offset + i)), scale));
 }
 
+// A rows x cols matrix whose logical element (r, c) is draw r*cols + c,
+// stored in tiles of tr consecutive rows, column-major within a tile:
+// element (r, c) sits at ((r / tr) * cols + c) * tr + r % tr.
+__global__ void k_normal_bf16_tiles(uint64_t key, float scale, uint16_t* out, int64_t rows, int64_t cols, int64_t tr) {
+  const int64_t n = rows * cols, tile = tr * cols;
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n; q += stride) {
+    const int64_t t = q / tile, w = q % tile;
+    const int64_t r = t * tr + w % tr, c = w / tr;
+    out[q] = f32_to_bf16_rne(irwin_hall4(sm64(key, (uint64_t)(r * cols + c)), scale));
+  }
+}
+
 __global__ void k_normal_f32(uint64_t key, float scale, float* out, int64_t n, int64_t offset) {
   int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
@@ -62,6 +75,14 @@ static unsigned grid_for(int64_t n) {
 extern "C" int synth_dev_normal_bf16(uint64_t key, float scale, void* out, int64_t n, int64_t offset, void* stream) {
   if (n <= 0) return 0;
   hipLaunchKernelGGL(k_normal_bf16, dim3(grid_for(n)), dim3(256), 0, (hipStream_t)stream, key, scale, (uint16_t*)out, n, offset);
+  return (int)hipGetLastError();
+}
+extern "C" int synth_dev_normal_bf16_tiles(uint64_t key, float scale, void* out, int64_t rows, int64_t cols,
+                                           int64_t tile_rows, void* stream) {
+  if (rows <= 0 || cols <= 0) return 0;
+  if (tile_rows <= 0 || rows % tile_rows) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_normal_bf16_tiles, dim3(grid_for(rows * cols)), dim3(256), 0, (hipStream_t)stream, key, scale,
+                     (uint16_t*)out, rows, cols, tile_rows);
   return (int)hipGetLastError();
 }
 extern "C" int synth_dev_normal_f32(uint64_t key, float scale, void* out, int64_t n, int64_t offset, void* stream) {

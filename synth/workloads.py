@@ -21,6 +21,7 @@ from typing import List, Optional, Tuple
 # Draw standard deviations.
 W_SIGMA = 0.02          # every weight matrix
 KV_SIGMA = 1.0          # cached K/V rows, MLA latent rows, KDA state
+V_TILE = 32             # positions per tile of the GQA V cache
 
 
 @dataclass
@@ -175,7 +176,10 @@ def weight_bytes(w: Workload) -> int:
 # --------------------------------------------------------------------------
 # Cache / state layout of the single caller-owned KV buffer.  Per layer, in
 # layer order:
-#   GQA: K bf16[max_batch][n_kv][max_ctx][head_dim], then V with the same shape
+#   GQA: K bf16[max_batch][n_kv][max_ctx][head_dim], then V with the same
+#        logical shape stored in V_TILE-position tiles, dim-major within a
+#        tile: bf16[max_batch][n_kv][max_ctx / V_TILE][head_dim][V_TILE]
+#        (max_ctx a multiple of V_TILE).  kv_layout gives the logical shape.
 #   MLA: latent rows bf16[max_batch][max_ctx][kv_lora + rope_dim]
 #   KDA: state fp32[max_batch][kda_heads][kda_dk][kda_dv]
 # Each layer's region starts on a 256-byte boundary.
@@ -263,7 +267,7 @@ def mini_moe() -> Workload:
                     n_q_heads=4, n_kv_heads=2, head_dim=64,
                     n_experts=12, top_k=3, expert_ffn=192, n_shared=1, shared_ffn=256,
                     router_sigma=0.1, gain_sigma=0.1,
-                    batches=(1, 5, 8), context=45, max_ctx=80, max_batch=8, steps=2, seed_base=11)
+                    batches=(1, 5, 8), context=45, max_ctx=96, max_batch=8, steps=2, seed_base=11)
 
 
 def mini_hybrid() -> Workload:

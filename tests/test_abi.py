@@ -80,6 +80,7 @@ def test_kv_bytes_match_the_documented_layout():
     ("head_dim", 96, _lib.MD_EUNSUPPORTED),
     ("n_kv_heads", 4, _lib.MD_EINVAL),       # 6 q heads are not a multiple of 4
     ("ffn_dim", 100, _lib.MD_EUNSUPPORTED),
+    ("max_ctx", 80, _lib.MD_EUNSUPPORTED),    # the V cache is stored in 32-position tiles
     ("attn_kind", 2, _lib.MD_EINVAL),
     ("flags", 1, _lib.MD_EINVAL),
 ])

@@ -51,12 +51,15 @@ __device__ __forceinline__ KLayer& layer_ref(KParams& pk, int l) {
 }
 
 // ===================================================================== sync
-// One sync point = 8 sub-counters (one per workgroup class blockIdx % 8,
-// which on this part is the XCD the workgroup runs on) and one top counter,
-// each on its own 128-byte line.  A workgroup increments its sub-counter;
-// the last arrival of a class increments the top counter; waiters poll the
-// top counter.  Counters live in two banks used by alternate steps; every
-// step clears the bank of the next step (nobody touches it during this step).
+// One sync point = 8 class counters (one per workgroup class blockIdx % 8,
+// which on this part is the XCD the workgroup runs on) and one extra line,
+// each on its own 128-byte line.  A workgroup arrives by incrementing its
+// class counter without waiting for the result; a waiter polls the 8 class
+// counters at once (one lane each) until every class has fully arrived.  The
+// last sync point of a decode step instead reports which workgroup arrived
+// last (its class counter's last arrival increments the extra line).
+// Counters live in two banks used by alternate steps; every step clears the
+// bank of the next step (nobody touches it during this step).
 constexpr int SP_WORDS = 9 * 32;          // 9 lines of 128 B
 constexpr int NGRP = 8;
 
@@ -75,36 +78,56 @@ __device__ __forceinline__ void set_err(KParams& pk, int code) {
   __hip_atomic_fetch_or(p.err, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ __forceinline__ unsigned class_members(int grp) { return (gridDim.x - grp + NGRP - 1) / NGRP; }
+
 // every wave: make this wave's stores complete, then the workgroup arrives
-// once.  Returns (in thread 0) whether this workgroup was the last to arrive.
-__device__ bool arrive(KParams& pk, int idx) {
+// once.  The increment returns nothing, so nobody waits for it here.
+__device__ void arrive(KParams& pk, int idx) {
+  PARAMS;
+  wait_stores();
+  __builtin_amdgcn_s_barrier();
+  if (threadIdx.x == 0) {
+    unsigned* sp = sync_pt(p, idx);
+    const int grp = blockIdx.x & (NGRP - 1);
+    (void)__hip_atomic_fetch_add(sp + 32 * grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Arrival at the step's last sync point; returns (in thread 0) whether this
+// workgroup was the last of the grid to arrive.
+__device__ bool arrive_last(KParams& pk, int idx) {
   PARAMS;
   wait_stores();
   __builtin_amdgcn_s_barrier();
   bool last = false;
   if (threadIdx.x == 0) {
     unsigned* sp = sync_pt(p, idx);
-    int grp = blockIdx.x & (NGRP - 1);
-    int members = (gridDim.x - grp + NGRP - 1) / NGRP;
-    unsigned ngrp = gridDim.x < NGRP ? gridDim.x : NGRP;
+    const int grp = blockIdx.x & (NGRP - 1);
+    const unsigned ngrp = gridDim.x < NGRP ? gridDim.x : NGRP;
     unsigned old = __hip_atomic_fetch_add(sp + 32 * grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old + 1 == (unsigned)members)
+    if (old + 1 == class_members(grp))
       last = __hip_atomic_fetch_add(sp + 32 * NGRP, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 == ngrp;
   }
   return last;
 }
 
-// wait until every group has fully arrived at sync point idx
+// wait until every class has fully arrived at sync point idx (wave 0 polls,
+// lane g the counter of class g)
 __device__ void wait_all(KParams& pk, int idx) {
   PARAMS;
-  if (threadIdx.x == 0) {
-    unsigned* top = sync_pt(p, idx) + 32 * NGRP;
-    unsigned ngrp = gridDim.x < NGRP ? gridDim.x : NGRP;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int ngrp = gridDim.x < NGRP ? gridDim.x : NGRP;
+    const bool mine = lane < ngrp;
+    const unsigned need = mine ? class_members(lane) : 0u;
+    unsigned* c = sync_pt(p, idx) + 32 * (mine ? lane : 0);
     unsigned spins = 0;
-    while (__hip_atomic_load(top, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < ngrp) {
+    while (true) {
+      const unsigned v = mine ? __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+      if (__all(v >= need)) break;
       __builtin_amdgcn_s_sleep(1);
       if (((++spins) & 1023u) == 0 && (spins > p.spin_limit || dev_failed(p))) {
-        set_err(p, MDE_WATCHDOG);
+        if (lane == 0) set_err(p, MDE_WATCHDOG);
         break;
       }
     }
@@ -117,12 +140,22 @@ __device__ __forceinline__ void stamp(KParams& pk, int slot) {
   if (p.trace && threadIdx.x == 0 && slot < p.trace_n) p.trace[(size_t)blockIdx.x * p.trace_n + slot] = wall_clock64();
 }
 
-// Sub-phase stamps: slot trace_n/2 + 4*(phase index) + k, k < 4.
+// Sub-phase stamps: slot trace_n/2 + 8*(phase index) + k, k < 8.  k < 4:
+// the phase's own, after its wait; k = 4: its slot tables are built, k = 5:
+// it starts waiting (both before the wait, while md_cur_phase still holds
+// the previous phase's index).
 __shared__ int md_cur_phase;
 __device__ __forceinline__ void sub_stamp(KParams& pk, int k) {
   PARAMS;
   if (p.trace && threadIdx.x == 0) {
-    int slot = p.trace_n / 2 + 4 * md_cur_phase + k;
+    int slot = p.trace_n / 2 + 8 * md_cur_phase + k;
+    if (slot < p.trace_n - 1) p.trace[(size_t)blockIdx.x * p.trace_n + slot] = wall_clock64();
+  }
+}
+__device__ __forceinline__ void pre_stamp(KParams& pk, int k) {
+  PARAMS;
+  if (p.trace && threadIdx.x == 0) {
+    int slot = p.trace_n / 2 + 8 * (md_cur_phase + 1) + k;
     if (slot < p.trace_n - 1) p.trace[(size_t)blockIdx.x * p.trace_n + slot] = wall_clock64();
   }
 }
@@ -150,6 +183,7 @@ __device__ __forceinline__ void grid_arrive(KParams& pk, int sidx) {
 __device__ __forceinline__ void wait_point(KParams& pk, int idx) {
   PARAMS;
   if (idx < 0) return;
+  pre_stamp(p, 5);
   wait_all(p, idx);
   stamp(p, 2 * idx + 1);
   if (threadIdx.x == 0) md_cur_phase = idx + 1;
@@ -210,12 +244,12 @@ __device__ __forceinline__ int row_pos(KParams& pk, int r) {
 // pointer argument) so that accesses compile to LDS instructions.  It is a
 // static array: functions reach it at a fixed address (dynamic LDS would be
 // found through a per-kernel offset table in memory, a load in the stream).
-constexpr size_t MD_SMEM_BYTES = 112 * 1024;
+constexpr size_t MD_SMEM_BYTES = 130 * 1024;
 __shared__ __attribute__((aligned(16))) char md_smem[MD_SMEM_BYTES];
 
 constexpr int CMAX_DEV = 256;    // largest chunk count per (sequence, kv head)
-constexpr int TG = 2;            // slots per group (share one B operand load)
-constexpr int GDS = 8;          // k-steps in flight per wave
+constexpr int TG = 2;            // slots per group (share one B operand load); even: SwiGLU pairs
+constexpr int GDS = 8;           // k-steps in flight per wave
 constexpr int MAXSLOT = 96;      // slots per workgroup and phase
 constexpr int MAXGRP = MAXSLOT / TG;
 constexpr int MAXMAT = 72;       // matrices per phase
@@ -248,9 +282,9 @@ struct MatDesc {
   int tag;           // meaning chosen by the phase (expert slot, ...)
 };
 enum : int { GK_SINGLE = 0, GK_PAIR = 1 };
-// A group: slots 2g and 2g+1.  GK_PAIR: slot 2g holds gate rows and slot
-// 2g+1 the up rows of the same quarters (SwiGLU); GK_SINGLE: two independent
-// slots.
+// A group: slots TG*g .. TG*g + TG-1, which share every B operand load.
+// GK_PAIR: slots TG*g + 2j hold gate rows and TG*g + 2j+1 the up rows of the
+// same quarters (SwiGLU); GK_SINGLE: independent slots.
 struct GroupDesc {
   uint32_t u_off;    // byte offset of U in the workspace
   int KS;            // k-steps (K / 32); U rows are K elements apart
@@ -265,6 +299,7 @@ struct GemvSmem {
   GroupDesc grp[MAXGRP];
   MatDesc mats[MAXMAT];
   int nslots, ngroups, nmats, overflow;
+  int wtot[NW];                  // k-steps of every group, per wave
   // epilogue staging: inputs read before the weight stream starts, outputs
   // written after it ends, so the stream itself issues no other memory
   // operation.  Indexed by slot row (slot*16 + row-in-slot) or, in phases
@@ -276,19 +311,58 @@ struct GemvSmem {
 };
 #define GSM (*reinterpret_cast<GemvSmem*>(md_smem))
 
-// Slot-list builder, run by thread 0.  Groups are opened with begin(U, K,
-// kind); quarters are appended with single() or pair() and written straight
-// into the LDS slot table; a group never spans two begin() calls.
+// Slot tables of a phase whose work split does not depend on the step's data
+// (everything but the routed experts' phases) are the same in every layer:
+// the first layer of a launch builds them, later layers copy them back and
+// only re-enter the per-layer weight pointers.  They live at the end of the
+// static LDS block.
+enum : int {
+  PL_QKV = 0, PL_OPROJ, PL_GATEUP, PL_DDOWN, PL_LMHEAD, PL_KDA_PROJ, PL_KDA_O, PL_MLA_A, PL_MLA_B, PL_MLA_O, PL_MOE_A,
+  NPLAN
+};
+constexpr int PLAN_SLOTS = 48;
+struct SlotPlan {
+  int valid, nslots, overflow, pad_;
+  int wtot[NW];
+  Slot slots[PLAN_SLOTS];
+  GroupDesc grp[PLAN_SLOTS / TG];
+};
+constexpr size_t PLAN_OFF = MD_SMEM_BYTES - NPLAN * sizeof(SlotPlan);
+#define PLANS (reinterpret_cast<SlotPlan*>(md_smem + PLAN_OFF))
+static_assert(sizeof(Slot) % 4 == 0 && sizeof(GroupDesc) % 4 == 0 && PLAN_OFF % 16 == 0, "plans are copied as words");
+
+// wave-parallel copy of n 32-bit words (wave 0 calls it)
+__device__ __forceinline__ void copy_words(void* dst, const void* src, int n) {
+  for (int i = __lane_id(); i < n; i += 64) ((int*)dst)[i] = ((const int*)src)[i];
+}
+
+// Slot-list builder, run by wave 0 on wave-uniform values (scalar
+// arithmetic; every lane writes the same table entries).  Groups are opened
+// with begin(U, K, kind); quarters are appended with single() or pair() and
+// written straight into the LDS slot table; a group never spans two begin()
+// calls.
 struct SlotBuilder {
   int ns, fill, pfill, nm;  // slots, quarters in the open slot, pending pairs, matrices (all in registers:
                             // the builder only writes LDS, so its stores pipeline)
+  int tot[NW];              // k-steps of the groups so far, per wave
   GroupDesc gd;
+  __device__ void new_group() {
+    GSM.grp[ns / TG] = gd;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot[w] += (gd.KS - w + NW - 1) / NW;
+  }
   __device__ void empty_slot(int si) {
     for (int e = 0; e < 4; ++e) { GSM.slots[si].m[e] = 0; GSM.slots[si].gq[e] = -1; }
   }
   bool ovf;
-  __device__ void start() {
+  int plan;     // cached plan of this phase (built or replayed), or -1
+  bool replay;  // the plan is valid: only matrices are entered
+  __device__ void start(int plan_id = -1) {
+    plan = plan_id;
+    replay = plan_id >= 0 && __builtin_amdgcn_readfirstlane(PLANS[plan_id].valid) != 0;
     ns = 0; fill = 0; pfill = 0; nm = 0; ovf = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot[w] = 0;
     gd.u_off = 0; gd.KS = MIN_KS; gd.kind = GK_SINGLE; gd.pad_ = 0;
   }
   __device__ int mat(const void* w, int N, int K, int tag) {
@@ -304,7 +378,7 @@ struct SlotBuilder {
   __device__ bool open_slot() {
     if (ns >= MAXSLOT) { ovf = true; return false; }
     empty_slot(ns);
-    if ((ns & 1) == 0) GSM.grp[ns >> 1] = gd;
+    if (ns % TG == 0) new_group();
     return true;
   }
   __device__ void flush() {
@@ -316,11 +390,13 @@ struct SlotBuilder {
   __device__ void close() {
     flush();
     pflush();
-    if (ns & 1) {
-      if (open_slot()) ++ns;
+    while (ns % TG) {
+      if (!open_slot()) break;
+      ++ns;
     }
   }
   __device__ void begin(uint32_t u_off, int K, int kind) {
+    if (replay) return;
     close();
     if (K < 32 * MIN_KS || (K & 31)) ovf = true;
     gd.u_off = u_off; gd.KS = K >> 5; gd.kind = kind; gd.pad_ = 0;
@@ -336,7 +412,7 @@ struct SlotBuilder {
       if (ns + 1 >= MAXSLOT) { ovf = true; return; }
       empty_slot(ns);
       empty_slot(ns + 1);
-      GSM.grp[ns >> 1] = gd;
+      if (ns % TG == 0) new_group();
     }
     GSM.slots[ns].m[pfill] = (int8_t)mg;
     GSM.slots[ns].gq[pfill] = gq;
@@ -352,19 +428,43 @@ struct SlotBuilder {
     return lastq;
   }
   __device__ void singles_of(int m, int N) {
+    if (replay) return;
     RowSplit q = quarters(N);
     for (int gq = q.r0; gq < q.r1; ++gq) single(m, gq);
   }
   __device__ void pairs_of(int mg, int mu, int N) {
+    if (replay) return;
     RowSplit q = quarters(N);
     for (int gq = q.r0; gq < q.r1; ++gq) pair(mg, mu, gq);
   }
   __device__ void finish() {
-    close();
+    if (replay) {
+      SlotPlan& P = PLANS[plan];
+      ns = __builtin_amdgcn_readfirstlane(P.nslots);
+      ovf = ovf || __builtin_amdgcn_readfirstlane(P.overflow) != 0;
+      copy_words(GSM.slots, P.slots, ns * (int)(sizeof(Slot) / 4));
+      copy_words(GSM.grp, P.grp, (ns / TG) * (int)(sizeof(GroupDesc) / 4));
+#pragma unroll
+      for (int w = 0; w < NW; ++w) tot[w] = __builtin_amdgcn_readfirstlane(P.wtot[w]);
+    } else {
+      close();
+    }
     GSM.nslots = ns;
     GSM.ngroups = ns / TG;
     GSM.nmats = nm;
     GSM.overflow = ovf ? 1 : 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) GSM.wtot[w] = tot[w];
+    if (!replay && plan >= 0 && !ovf && ns <= PLAN_SLOTS) {
+      SlotPlan& P = PLANS[plan];
+      copy_words(P.slots, GSM.slots, ns * (int)(sizeof(Slot) / 4));
+      copy_words(P.grp, GSM.grp, (ns / TG) * (int)(sizeof(GroupDesc) / 4));
+      P.nslots = ns;
+      P.overflow = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) P.wtot[w] = tot[w];
+      P.valid = 1;
+    }
   }
 };
 
@@ -379,7 +479,7 @@ __device__ __forceinline__ void slot_src(int si, int lq, uint32_t lchunk, int wv
   pstep = lv ? (uint32_t)(NW * 1024) : 0u;
 }
 
-// Output (token t, row rr of slot 2g + i) of a finished group: the four
+// Output (token t, row rr of slot TG*g + i) of a finished group: the four
 // waves' partials, hi and lo columns, summed in a fixed order.
 __device__ __forceinline__ float gy(int rb, int i, int rr, int t) {
   float s = 0.f;
@@ -431,8 +531,8 @@ struct GemvStream {
   rsrc_t urs;
   int ig, is, nks_i;
   uint32_t boff;
-  uint64_t pa0, pa1;
-  uint32_t ps0, ps1;
+  uint64_t pa[TG];
+  uint32_t ps[TG];
   i32x4 ra[GDS][TG];
   i32x4 rb[GDS];
   uint32_t bo[GDS];
@@ -443,18 +543,19 @@ __device__ __forceinline__ void gs_group(GemvStream& s, int g) {
   const uint32_t uo = __builtin_amdgcn_readfirstlane(GSM.grp[g].u_off);
   s.nks_i = (ks - s.wv + NW - 1) / NW;
   s.boff = s.tok < s.B ? uo + (uint32_t)((s.part * MAXB + s.tok) * ks * 32) * 2u + s.lane16 : OOB;
-  slot_src(2 * g, s.lq, s.lchunk, s.wv, s.zero_addr, s.pa0, s.ps0);
-  slot_src(2 * g + 1, s.lq, s.lchunk, s.wv, s.zero_addr, s.pa1, s.ps1);
+#pragma unroll
+  for (int i = 0; i < TG; ++i) slot_src(TG * g + i, s.lq, s.lchunk, s.wv, s.zero_addr, s.pa[i], s.ps[i]);
 }
 
 // Weight loads of one k-step (ring entry d); past the last group they read
 // the zero block.  Records the k-step's B-operand offset.
 __device__ __forceinline__ void gs_issue_a(GemvStream& s, int d) {
   const bool ok = s.ig < s.ngroups;
-  s.ra[d][0] = __builtin_nontemporal_load((const __attribute__((address_space(1))) i32x4*)(ok ? s.pa0 : s.zero_addr));
-  s.ra[d][1] = __builtin_nontemporal_load((const __attribute__((address_space(1))) i32x4*)(ok ? s.pa1 : s.zero_addr));
-  s.pa0 += s.ps0;
-  s.pa1 += s.ps1;
+#pragma unroll
+  for (int i = 0; i < TG; ++i) {
+    s.ra[d][i] = __builtin_nontemporal_load((const __attribute__((address_space(1))) i32x4*)(ok ? s.pa[i] : s.zero_addr));
+    s.pa[i] += s.ps[i];
+  }
   s.bo[d] = (ok && s.boff != OOB) ? s.boff + (uint32_t)(s.is * NW + s.wv) * 64u : OOB;
   if (++s.is == s.nks_i) {
     s.is = 0;
@@ -468,10 +569,11 @@ __device__ __forceinline__ void gs_issue_b(GemvStream& s, int d) { s.rb[d] = ld_
 // switch (loads before the branch, so the compiler sees one load sequence).
 __device__ __forceinline__ void gs_issue(GemvStream& s, int d) {
   const bool ok = s.ig < s.ngroups;
-  s.ra[d][0] = __builtin_nontemporal_load((const __attribute__((address_space(1))) i32x4*)(ok ? s.pa0 : s.zero_addr));
-  s.ra[d][1] = __builtin_nontemporal_load((const __attribute__((address_space(1))) i32x4*)(ok ? s.pa1 : s.zero_addr));
-  s.pa0 += s.ps0;
-  s.pa1 += s.ps1;
+#pragma unroll
+  for (int i = 0; i < TG; ++i) {
+    s.ra[d][i] = __builtin_nontemporal_load((const __attribute__((address_space(1))) i32x4*)(ok ? s.pa[i] : s.zero_addr));
+    s.pa[i] += s.ps[i];
+  }
   s.rb[d] = ld_x4<CP_SC1>(s.urs, (ok && s.boff != OOB) ? s.boff + (uint32_t)(s.is * NW + s.wv) * 64u : OOB);
   if (++s.is == s.nks_i) {
     s.is = 0;
@@ -485,9 +587,7 @@ __device__ __forceinline__ void gemv_begin(GemvStream& s, const uint8_t* ws, uin
   const int lane = threadIdx.x & 63;
   s.wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   s.ngroups = __builtin_amdgcn_readfirstlane(GSM.ngroups);
-  int total = 0;
-  for (int g = 0; g < s.ngroups; ++g) total += group_nks(g, s.wv);
-  s.total = __builtin_amdgcn_readfirstlane(total);
+  s.total = __builtin_amdgcn_readfirstlane(GSM.wtot[s.wv]);
   s.urs = make_rsrc_u(ws, ws_bytes);
   s.lq = (lane & 15) >> 2;
   s.lchunk = (uint32_t)(((lane >> 4) * 4 + (lane & 3)) * 16);
@@ -500,8 +600,11 @@ __device__ __forceinline__ void gemv_begin(GemvStream& s, const uint8_t* ws, uin
   s.is = 0;
   s.nks_i = 1;
   s.boff = OOB;
-  s.pa0 = s.pa1 = s.zero_addr;
-  s.ps0 = s.ps1 = 0;
+#pragma unroll
+  for (int i = 0; i < TG; ++i) {
+    s.pa[i] = s.zero_addr;
+    s.ps[i] = 0;
+  }
   if (s.ngroups > 0) gs_group(s, 0);
 #pragma unroll
   for (int d = 0; d < GDS; ++d) gs_issue_a(s, d);
@@ -517,7 +620,7 @@ __device__ __forceinline__ void gemv_begin(GemvStream& s, const uint8_t* ws, uin
 template <class Epi>
 __device__ __forceinline__ void gemv_run(KParams& pk, GemvStream& s, int inv_n, uint32_t inv_off, Epi epi) {
   PARAMS;
-  static_assert(TG == 2, "the stream handles slot pairs");
+  static_assert(TG % 2 == 0, "SwiGLU groups hold gate/up slot pairs");
   const int lane = threadIdx.x & 63;
   i32x4 ia0, ib0, ia1, ib1;
   if (inv_n > 0) {
@@ -602,16 +705,20 @@ __device__ __forceinline__ RowSplit owned_rows(int N, int w, int G) {
 // stage_rows < 0: the phase stages by slot row (16 per slot).
 __device__ __forceinline__ bool builder_done(KParams& pk, SlotBuilder& sb, int stage_rows) {
   PARAMS;
-  if (threadIdx.x == 0) {
+  if (threadIdx.x < 64) {
     sb.finish();
-    if ((stage_rows < 0 ? sb.ns * 16 : stage_rows) > STAGE_ROWS) GSM.overflow = 1;
-    if (GSM.overflow) {
-      set_err(p, MDE_CAPACITY);
+    const bool ovf = sb.ovf || (stage_rows < 0 ? sb.ns * 16 : stage_rows) > STAGE_ROWS;
+    if (ovf) {
+      if (threadIdx.x == 0) set_err(p, MDE_CAPACITY);
+      GSM.overflow = 1;
       GSM.nslots = 0;
       GSM.ngroups = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) GSM.wtot[w] = 0;
     }
   }
   __syncthreads();
+  pre_stamp(p, 4);
   return GSM.ngroups > 0;
 }
 
@@ -670,25 +777,89 @@ __device__ __noinline__ void phase_embed(KParams& pk) {
   store_ssq(p, r, part, p.off_ssq);
 }
 
-// Epilogue of phases whose output is y * inv_rms per slot row.
-#define EPI_SCALED_SINGLE                                                     \
-  [=](int g, int rb) {                                                                \
-    for (int e = threadIdx.x; e < TG * 16 * B; e += NT) {                     \
-      int t = e % B, rr = (e / B) % 16, i = e / (B * 16);                     \
-      GSM.out[(2 * g + i) * 16 + rr][t] = gy(rb, i, rr, t) * GSM.inv[t];       \
-    }                                                                         \
+// ------------------------------------------------------------ shared stream
+// Every weight-streaming phase runs through gemv_phase: one copy of the
+// stream loop and of the group epilogue, shared by all of them, so that the
+// code stays in the instruction cache from phase to phase and layer to layer.
+enum : int { EPI_BY_KIND = 0, EPI_RESIDUAL = 1 };
+
+// Epilogue of finished group g (the waves' partials in GSM.red[rb]).
+// EPI_BY_KIND: a GK_SINGLE group stores y * inv_rms per slot row, a GK_PAIR
+// group silu(inv*gate) * (inv*up) at the gate slots' rows; EPI_RESIDUAL adds
+// y to the owned residual rows staged at GSM.out[row - r0].
+__device__ __forceinline__ void gemv_epi(int g, int rb, int kind, int B, int r0) {
+  if (kind == EPI_RESIDUAL) {
+    for (int e = threadIdx.x; e < TG * 16 * B; e += NT) {
+      int t = e % B, rr = (e / B) % 16, i = e / (B * 16);
+      int m, row;
+      if (slot_row(TG * g + i, rr, m, row)) GSM.out[row - r0][t] += gy(rb, i, rr, t);
+    }
+  } else if (GSM.grp[g].kind == GK_PAIR) {
+    for (int e = threadIdx.x; e < (TG / 2) * 16 * B; e += NT) {
+      int t = e % B, rr = (e / B) % 16, j = e / (B * 16);
+      float a = gy(rb, 2 * j, rr, t) * GSM.inv[t];
+      float u = gy(rb, 2 * j + 1, rr, t) * GSM.inv[t];
+      GSM.out[(TG * g + 2 * j) * 16 + rr][t] = silu(a) * u;
+    }
+  } else {
+    for (int e = threadIdx.x; e < TG * 16 * B; e += NT) {
+      int t = e % B, rr = (e / B) % 16, i = e / (B * 16);
+      GSM.out[(TG * g + i) * 16 + rr][t] = gy(rb, i, rr, t) * GSM.inv[t];
+    }
   }
-// SwiGLU epilogue of a pair group: silu(inv*gate) * (inv*up) to the gate
-// slot's rows.
-#define EPI_SWIGLU                                                            \
-  [=](int g, int rb) {                                                                \
-    for (int e = threadIdx.x; e < 16 * B; e += NT) {                          \
-      int t = e % B, rr = e / B;                                              \
-      float a = gy(rb, 0, rr, t) * GSM.inv[t];                                 \
-      float u = gy(rb, 1, rr, t) * GSM.inv[t];                                 \
-      GSM.out[2 * g * 16 + rr][t] = silu(a) * u;                              \
-    }                                                                         \
+}
+
+// The weight stream of a phase whose slot tables are built: its first
+// k-steps are requested, then the phase waits at sync point wait_idx, then
+// everything streams.  inv_n > 0: outputs are scaled by 1/rms over inv_n
+// features (partial sums of squares at inv_off).  EPI_RESIDUAL: the owned
+// residual rows [r0, r0 + nrow) of x and the gains g_next of the next norm
+// are staged in GSM.out / GSM.gain (requested behind the first weight loads,
+// written once the wait is over).
+__device__ __noinline__ void gemv_phase(KParams& pk, int wait_idx, int inv_n, uint32_t inv_off, int kind, int r0,
+                                        int nrow, const uint16_t* g_next) {
+  PARAMS;
+  const int B = p.B, H = p.H;
+  GemvStream gs;
+  gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
+  float xv[4], gv[4];
+  if (kind == EPI_RESIDUAL) {
+    // buffer loads: an offset past the resource reads 0, so no load is
+    // conditional (a conditional load would be waited for on its own, and
+    // with it the weight loads above)
+    const rsrc_t xr = make_rsrc_u(p.x, (uint32_t)(MAXB * H * 4));
+    const rsrc_t gr = make_rsrc_u(g_next, (uint32_t)(H * 2));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = threadIdx.x + k * NT;
+      const bool in = e < nrow * B;
+      const int t = e % B, lr = e / B;
+      xv[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, in ? (uint32_t)(t * H + r0 + lr) * 4u : OOB, 0, 0));
+      gv[k] = bf16_f32(__builtin_amdgcn_raw_buffer_load_b16(gr, (in && t == 0) ? (uint32_t)(r0 + lr) * 2u : OOB, 0, 0));
+    }
   }
+  wait_point(p, wait_idx);
+  if (kind == EPI_RESIDUAL) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = threadIdx.x + k * NT;
+      if (e < nrow * B) {
+        const int t = e % B, lr = e / B;
+        GSM.out[lr][t] = xv[k];
+        if (t == 0) GSM.gain[lr] = gv[k];
+      }
+    }
+    for (int e = threadIdx.x + 4 * NT; e < nrow * B; e += NT) {  // more rows than 4 per thread
+      int t = e % B, lr = e / B;
+      GSM.out[lr][t] = p.x[t * H + r0 + lr];
+      if (t == 0) GSM.gain[lr] = bf16_f32(g_next[r0 + lr]);
+    }
+    __syncthreads();
+  }
+  sub_stamp(p, 0);
+  gemv_run(p, gs, inv_n, inv_off, [=](int g, int rb) { gemv_epi(g, rb, kind, B, r0); });
+  sub_stamp(p, 2);
+}
 
 // --- QKV projection (GQA): raw q, k, v (RMS-normalised input) -> qkv[t][row]
 __device__ __noinline__ void phase_qkv(KParams& pk, int l_layer, int wait_idx) {
@@ -696,8 +867,8 @@ __device__ __noinline__ void phase_qkv(KParams& pk, int l_layer, int wait_idx) {
   KLayer& L = layer_ref(p, l_layer);
   const int B = p.B;
   SlotBuilder sb;
-  if (threadIdx.x == 0) {
-    sb.start();
+  if (threadIdx.x < 64) {
+    sb.start(PL_QKV);
     int mq = sb.mat(L.wq, p.nq * p.hd, p.H, 0);
     int mk = sb.mat(L.wk, p.nkv * p.hd, p.H, p.nq * p.hd);
     int mv = sb.mat(L.wv, p.nkv * p.hd, p.H, (p.nq + p.nkv) * p.hd);
@@ -707,12 +878,7 @@ __device__ __noinline__ void phase_qkv(KParams& pk, int l_layer, int wait_idx) {
     sb.singles_of(mv, p.nkv * p.hd);
   }
   builder_done(p, sb, -1);
-  GemvStream gs;
-  gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
-  wait_point(p, wait_idx);
-  sub_stamp(p, 0);
-  gemv_run(p, gs, p.H, p.off_ssq, EPI_SCALED_SINGLE);
-  sub_stamp(p, 2);
+  gemv_phase(p, wait_idx, p.H, p.off_ssq, EPI_BY_KIND, 0, 0, nullptr);
   const int nqkv = (p.nq + 2 * p.nkv) * p.hd;
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
@@ -1159,8 +1325,8 @@ __device__ __noinline__ void phase_kda_proj(KParams& pk, int l_layer, int wait_i
   const int B = p.B, nh = p.kda_h, dk = p.kda_dk, dv = p.kda_dv;
   const int width = 2 * nh * dk + nh * dv + 2 * nh;
   SlotBuilder sb;
-  if (threadIdx.x == 0) {
-    sb.start();
+  if (threadIdx.x < 64) {
+    sb.start(PL_KDA_PROJ);
     int m0 = sb.mat(L.kda_wq, nh * dk, p.H, 0);
     int m1 = sb.mat(L.kda_wk, nh * dk, p.H, nh * dk);
     int m2 = sb.mat(L.kda_wv, nh * dv, p.H, 2 * nh * dk);
@@ -1174,12 +1340,7 @@ __device__ __noinline__ void phase_kda_proj(KParams& pk, int l_layer, int wait_i
     sb.singles_of(m4, nh);
   }
   builder_done(p, sb, -1);
-  GemvStream gs;
-  gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
-  wait_point(p, wait_idx);
-  sub_stamp(p, 0);
-  gemv_run(p, gs, p.H, p.off_ssq, EPI_SCALED_SINGLE);
-  sub_stamp(p, 2);
+  gemv_phase(p, wait_idx, p.H, p.off_ssq, EPI_BY_KIND, 0, 0, nullptr);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
     int t = e % B, sr = e / B;
@@ -1441,8 +1602,8 @@ __device__ __noinline__ void phase_mla_a(KParams& pk, int l_layer, int wait_idx)
   KLayer& L = layer_ref(p, l_layer);
   const int B = p.B, QL = p.q_lora, KVR = MLA_QA;
   SlotBuilder sb;
-  if (threadIdx.x == 0) {
-    sb.start();
+  if (threadIdx.x < 64) {
+    sb.start(PL_MLA_A);
     int ma = sb.mat(L.mla_wqa, QL, p.H, 0);
     int mk = sb.mat(L.mla_wkva, KVR, p.H, 1);
     sb.begin(p.off_u, p.H, GK_SINGLE);
@@ -1450,12 +1611,7 @@ __device__ __noinline__ void phase_mla_a(KParams& pk, int l_layer, int wait_idx)
     sb.singles_of(mk, KVR);
   }
   builder_done(p, sb, -1);
-  GemvStream gs;
-  gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
-  wait_point(p, wait_idx);
-  sub_stamp(p, 0);
-  gemv_run(p, gs, p.H, p.off_ssq, EPI_SCALED_SINGLE);
-  sub_stamp(p, 2);
+  gemv_phase(p, wait_idx, p.H, p.off_ssq, EPI_BY_KIND, 0, 0, nullptr);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   float* part = (float*)GSM.red;  // [NT][MAXB]
   for (int t = 0; t < MAXB; ++t) part[threadIdx.x * MAXB + t] = 0.f;
@@ -1516,20 +1672,15 @@ __device__ __noinline__ void phase_mla_b(KParams& pk, int l_layer, int wait_idx)
   const int B = p.B, nh = p.mla_h, QW = p.nope + MLA_RD;
   const int cb = (int)gridDim.x - 1 - (int)blockIdx.x;
   SlotBuilder sb;
-  if (threadIdx.x == 0) {
-    sb.start();
+  if (threadIdx.x < 64) {
+    sb.start(PL_MLA_B);
     int m = sb.mat(L.mla_wqb, nh * QW, p.q_lora, 0);
     sb.begin(p.off_uq, p.q_lora, GK_SINGLE);
     sb.singles_of(m, nh * QW);
   }
   builder_done(p, sb, -1);
-  GemvStream gs;
-  gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
-  wait_point(p, wait_idx);
+  gemv_phase(p, wait_idx, p.q_lora, p.off_ssq2, EPI_BY_KIND, 0, 0, nullptr);
   if (cb < B) mla_cache_row(p, l_layer, cb);
-  sub_stamp(p, 0);
-  gemv_run(p, gs, p.q_lora, p.off_ssq2, EPI_SCALED_SINGLE);
-  sub_stamp(p, 2);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
     int t = e % B, sr = e / B;
@@ -1906,7 +2057,7 @@ constexpr size_t ROUTE_OFF =
     (cmax_(cmax_(sizeof(GemvSmem) + (size_t)1024 * MAXB * 4, sizeof(AttnSmem)), cmax_(sizeof(MlaSmem), sizeof(KdaSmem))) + 63) /
     64 * 64;
 #define RSM (*reinterpret_cast<RouteSmem*>(md_smem + ROUTE_OFF))
-static_assert(ROUTE_OFF + sizeof(RouteSmem) <= MD_SMEM_BYTES, "LDS layout exceeds the static LDS block");
+static_assert(ROUTE_OFF + sizeof(RouteSmem) <= PLAN_OFF, "LDS layout exceeds the static LDS block");
 
 // --- residual-owning projections: x[t][r] += sum over the phase's matrices
 // of W . U (the O-projection; the dense down projection; the shared and
@@ -1922,8 +2073,8 @@ __device__ __noinline__ void phase_residual(KParams& pk, int l_layer, int mode, 
   const RowSplit own = owned_rows(H, blockIdx.x, gridDim.x);
   const int nrow = own.r1 - own.r0;
   SlotBuilder sb;
-  if (threadIdx.x == 0) {
-    sb.start();
+  if (threadIdx.x < 64) {
+    sb.start(mode == RES_OPROJ ? PL_OPROJ : mode == RES_DENSE_DOWN ? PL_DDOWN : mode == RES_MLA_O ? PL_MLA_O : mode == RES_KDA_O ? PL_KDA_O : -1);
     if (mode == RES_OPROJ) {
       int m = sb.mat(L.wo, H, p.nq * p.hd, 0);
       sb.begin(p.off_ou, p.nq * p.hd, GK_SINGLE);
@@ -1946,7 +2097,8 @@ __device__ __noinline__ void phase_residual(KParams& pk, int l_layer, int mode, 
         sb.begin(p.off_hs, p.shared_ffn, GK_SINGLE);
         sb.singles_of(m, H);
       }
-      for (int j = 0; j < RSM.nu; ++j) {
+      const int nu = __builtin_amdgcn_readfirstlane(RSM.nu);
+      for (int j = 0; j < nu; ++j) {
         int m = sb.mat(RSM.ex[j][2], H, p.expert_ffn, 0);
         sb.begin(p.off_hr + (uint32_t)j * p.hr_stride, p.expert_ffn, GK_SINGLE);
         sb.singles_of(m, H);
@@ -1954,46 +2106,8 @@ __device__ __noinline__ void phase_residual(KParams& pk, int l_layer, int mode, 
     }
   }
   builder_done(p, sb, nrow);
-  GemvStream gs;
-  gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
-  // the residual rows this workgroup owns (its own earlier output) and the
-  // next norm's gains, requested behind the first weight loads and staged
-  // once the wait (which waits for every earlier load) is over
-  float xv[4], gv[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int e = threadIdx.x + k * NT;
-    const bool in = e < nrow * B;
-    const int t = in ? e % B : 0, lr = in ? e / B : 0;
-    xv[k] = in ? p.x[t * H + own.r0 + lr] : 0.f;
-    gv[k] = (in && t == 0) ? bf16_f32(g_next[own.r0 + lr]) : 0.f;
-  }
-  wait_point(p, wait_idx);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int e = threadIdx.x + k * NT;
-    if (e < nrow * B) {
-      const int t = e % B, lr = e / B;
-      GSM.out[lr][t] = xv[k];
-      if (t == 0) GSM.gain[lr] = gv[k];
-    }
-  }
-  for (int e = threadIdx.x + 4 * NT; e < nrow * B; e += NT) {  // more rows than 4 per thread
-    int t = e % B, lr = e / B;
-    GSM.out[lr][t] = p.x[t * H + own.r0 + lr];
-    if (t == 0) GSM.gain[lr] = bf16_f32(g_next[own.r0 + lr]);
-  }
-  __syncthreads();
-  sub_stamp(p, 0);
   const int r0 = own.r0;
-  gemv_run(p, gs, 0, 0u, [=](int g, int rb) {
-    for (int e = threadIdx.x; e < TG * 16 * B; e += NT) {
-      int t = e % B, rr = (e / B) % 16, i = e / (B * 16);
-      int m, row;
-      if (slot_row(2 * g + i, rr, m, row)) GSM.out[row - r0][t] += gy(rb, i, rr, t);
-    }
-  });
-  sub_stamp(p, 2);
+  gemv_phase(p, wait_idx, 0, 0u, EPI_RESIDUAL, r0, nrow, g_next);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   static_assert(sizeof(GemvSmem::red) >= sizeof(float) * (NT + NW) * MAXB, "partial sums reuse the reduction scratch");
   float* part = (float*)GSM.red;  // [NT][MAXB]
@@ -2014,20 +2128,15 @@ __device__ __noinline__ void phase_gateup(KParams& pk, int l_layer, int wait_idx
   KLayer& L = layer_ref(p, l_layer);
   const int B = p.B, F = p.ffn;
   SlotBuilder sb;
-  if (threadIdx.x == 0) {
-    sb.start();
+  if (threadIdx.x < 64) {
+    sb.start(PL_GATEUP);
     int mg = sb.mat(L.w_gate, F, p.H, 0);
     int mu = sb.mat(L.w_up, F, p.H, 0);
     sb.begin(p.off_u, p.H, GK_PAIR);
     sb.pairs_of(mg, mu, F);
   }
   builder_done(p, sb, -1);
-  GemvStream gs;
-  gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
-  wait_point(p, wait_idx);
-  sub_stamp(p, 0);
-  gemv_run(p, gs, p.H, p.off_ssq, EPI_SWIGLU);
-  sub_stamp(p, 2);
+  gemv_phase(p, wait_idx, p.H, p.off_ssq, EPI_BY_KIND, 0, 0, nullptr);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
     int t = e % B, sr = e / B;
@@ -2055,8 +2164,8 @@ __device__ __noinline__ void phase_moe_a(KParams& pk, int l_layer, int wait_idx)
   KLayer& L = layer_ref(p, l_layer);
   const int B = p.B;
   SlotBuilder sb;
-  if (threadIdx.x == 0) {
-    sb.start();
+  if (threadIdx.x < 64) {
+    sb.start(PL_MOE_A);
     if (p.n_shared > 0) {
       int mg = sb.mat(L.sh_gate, p.shared_ffn, p.H, 0);
       int mu = sb.mat(L.sh_up, p.shared_ffn, p.H, 0);
@@ -2068,31 +2177,12 @@ __device__ __noinline__ void phase_moe_a(KParams& pk, int l_layer, int wait_idx)
     sb.singles_of(mr, p.n_experts);
   }
   builder_done(p, sb, -1);
-  GemvStream gs;
-  gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
-  wait_point(p, wait_idx);
-  sub_stamp(p, 0);
-  gemv_run(p, gs, p.H, p.off_ssq, [=](int g, int rb) {
-    if (GSM.grp[g].kind == GK_PAIR) {
-      for (int e = threadIdx.x; e < 16 * B; e += NT) {
-        int t = e % B, rr = e / B;
-        float a = gy(rb, 0, rr, t) * GSM.inv[t];
-        float u = gy(rb, 1, rr, t) * GSM.inv[t];
-        GSM.out[2 * g * 16 + rr][t] = silu(a) * u;
-      }
-    } else {
-      for (int e = threadIdx.x; e < TG * 16 * B; e += NT) {
-        int t = e % B, rr = (e / B) % 16, i = e / (B * 16);
-        GSM.out[(2 * g + i) * 16 + rr][t] = gy(rb, i, rr, t) * GSM.inv[t];
-      }
-    }
-  });
-  sub_stamp(p, 2);
+  gemv_phase(p, wait_idx, p.H, p.off_ssq, EPI_BY_KIND, 0, 0, nullptr);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
     int t = e % B, sr = e / B;
     int si = sr >> 4;
-    bool pair = GSM.grp[si >> 1].kind == GK_PAIR;
+    bool pair = GSM.grp[si / TG].kind == GK_PAIR;
     if (pair && (si & 1)) continue;  // up slots carry no output
     int m, row;
     if (!slot_row(si, sr & 15, m, row)) continue;
@@ -2164,22 +2254,18 @@ __device__ __noinline__ void phase_moe_b(KParams& pk, int l_layer, int wait_idx)
   KLayer& L = layer_ref(p, l_layer);
   const int B = p.B;
   SlotBuilder sb;
-  if (threadIdx.x == 0) {
+  if (threadIdx.x < 64) {
     sb.start();
     sb.begin(p.off_u, p.H, GK_PAIR);
-    for (int j = 0; j < RSM.nu; ++j) {
+    const int nu = __builtin_amdgcn_readfirstlane(RSM.nu);
+    for (int j = 0; j < nu; ++j) {
       int mg = sb.mat(RSM.ex[j][0], p.expert_ffn, p.H, j);
       int mu = sb.mat(RSM.ex[j][1], p.expert_ffn, p.H, j);
       sb.pairs_of(mg, mu, p.expert_ffn);
     }
   }
   builder_done(p, sb, -1);
-  GemvStream gs;
-  gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
-  wait_point(p, wait_idx);
-  sub_stamp(p, 0);
-  gemv_run(p, gs, p.H, p.off_ssq, EPI_SWIGLU);
-  sub_stamp(p, 2);
+  gemv_phase(p, wait_idx, p.H, p.off_ssq, EPI_BY_KIND, 0, 0, nullptr);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
     int t = e % B, sr = e / B;
@@ -2196,19 +2282,14 @@ __device__ __noinline__ void phase_lmhead(KParams& pk, int wait_idx) {
   PARAMS;
   const int B = p.B;
   SlotBuilder sb;
-  if (threadIdx.x == 0) {
-    sb.start();
+  if (threadIdx.x < 64) {
+    sb.start(PL_LMHEAD);
     int m = sb.mat(p.lm_head, p.V, p.H, 0);
     sb.begin(p.off_u, p.H, GK_SINGLE);
     sb.singles_of(m, p.V);
   }
   builder_done(p, sb, -1);
-  GemvStream gs;
-  gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
-  wait_point(p, wait_idx);
-  sub_stamp(p, 0);
-  gemv_run(p, gs, p.H, p.off_ssq, EPI_SCALED_SINGLE);
-  sub_stamp(p, 2);
+  gemv_phase(p, wait_idx, p.H, p.off_ssq, EPI_BY_KIND, 0, 0, nullptr);
   static_assert(sizeof(GemvSmem::in) >= 2 * sizeof(float) * NT * MAXB, "argmax scratch reuses the input staging");
   float* bv = &GSM.in[0][0];             // [NT][MAXB] best value (the input staging is unused here)
   int* bi = (int*)(bv + NT * MAXB);      // [NT][MAXB] best index
@@ -2315,6 +2396,8 @@ extern "C" __global__ __launch_bounds__(NT) void md_megakernel(Params p_arg) {
   KParams& p = *(KParams*)__builtin_amdgcn_kernarg_segment_ptr();
   (void)p_arg;
   if (p.B < 1 || p.B > MAXB) return;
+  if (threadIdx.x < NPLAN) PLANS[threadIdx.x].valid = 0;
+  __syncthreads();
   if (p.ml_phase >= 0) {  // one phase of the multi-launch step
     if (threadIdx.x == 0) md_cur_phase = 0;
     run_one_phase(p, p.ml_layer, p.ml_phase);
@@ -2403,7 +2486,7 @@ extern "C" __global__ __launch_bounds__(NT) void md_megakernel(Params p_arg) {
 #undef ARRIVE
   // the last workgroup to arrive reduces the argmax candidates
   stamp(p, 2 * sidx);
-  bool last = arrive(p, sidx);
+  bool last = arrive_last(p, sidx);
   if (threadIdx.x == 0) ((int*)md_smem)[0] = last;
   __syncthreads();
   if (((int*)md_smem)[0]) final_argmax(p);

@@ -8,7 +8,9 @@ the release latency of its sync point (last arrival to median wait end) and
 the medians of the phase's own sub-stamps: the end of the wait to stamp 0
 (weight-streaming phases: the stream starts; attention: q is ready), and
 stamp 0 to stamps 1, 2, 3 (streams: 2 = stream done; attention: 3 = this
-workgroup's blocks done, 1 = its partial stored, 2 = combine done)."""
+workgroup's blocks done, 1 = its partial stored, 2 = combine done); and,
+measured from the workgroup's arrival at the previous sync point, when its
+slot tables were built and when it started to wait (after the prefetch)."""
 from __future__ import annotations
 
 import ctypes
@@ -47,9 +49,11 @@ class Tracer:
         check(lib().md_set_trace(self.m.handle, None, 0))
 
     def summary(self, names, rate_hz=100e6):
-        """Per phase kind: median/max work time across WGs and the release
-        latency (last arrival -> median wait end), in microseconds."""
+        """Per phase kind (summed over its layers, microseconds): median and
+        slowest workgroup's work time, the release latency of its sync point
+        (last arrival -> median wait end), and medians of its sub-stamps."""
         t = self.buf.cpu().numpy().astype(np.float64) / rate_hz * 1e6
+        raw = self.buf.cpu().numpy()
         start = t[:, -1]
         ns = len(names)
         work = np.empty((self.G, ns))
@@ -61,26 +65,34 @@ class Tracer:
             wait_end = t[:, 2 * s + 1]
             # the last sync point of a decode step has no wait (its last
             # arrival reduces the argmax)
-            release[s] = np.median(wait_end) - end.max() if np.all(wait_end > 0) else 0.0
+            release[s] = np.median(wait_end) - end.max() if np.all(raw[:, 2 * s + 1] > 0) else 0.0
             prev = wait_end
         total = t[:, 2 * (ns - 1)].max() - start.min()
-        # sub-phase stamps (GEMV phases): 0 slots built, 1 first group flushed, 2 sweep done
-        sub = t[:, self.n // 2: self.n // 2 + 4 * ns].reshape(self.G, ns, 4)
+        h = self.n // 2
+        sub = t[:, h: h + 8 * ns].reshape(self.G, ns, 8)
+        subraw = raw[:, h: h + 8 * ns].reshape(self.G, ns, 8)
         out = {}
-        prevs = [start] + [t[:, 2 * s + 1] for s in range(ns - 1)]
+        # phase s waits on sync point s-1: its wait ends at t[2(s-1)+1]; the
+        # previous phase's work ends at t[2(s-1)]
+        wait_ends = [start] + [t[:, 2 * s + 1] for s in range(ns - 1)]
+        prev_ends = [start] + [t[:, 2 * s] for s in range(ns - 1)]
+        keys = ("med", "max", "release", "to_s0", "s0_s1", "s0_s2", "s0_s3", "arr_built", "arr_wait")
         for s, nm in enumerate(names):
-            d = out.setdefault(nm, {"n": 0, "med": 0.0, "max": 0.0, "release": 0.0, "to_slots": 0.0,
-                                    "to_first": 0.0, "to_sweep_end": 0.0, "k3": 0.0})
+            d = out.setdefault(nm, dict({"n": 0}, **{k: 0.0 for k in keys}))
             d["n"] += 1
             d["med"] += float(np.median(work[:, s]))
             d["max"] += float(work[:, s].max())
             d["release"] += float(release[s])
-            if np.all(sub[:, s, 0] > 0):
-                d["to_slots"] += float(np.median(sub[:, s, 0] - prevs[s]))
-                d["to_first"] += float(np.median(sub[:, s, 1] - sub[:, s, 0]))
-                d["to_sweep_end"] += float(np.median(sub[:, s, 2] - sub[:, s, 0]))
-                if np.all(sub[:, s, 3] > 0):
-                    d["k3"] += float(np.median(sub[:, s, 3] - sub[:, s, 0]))
+            ok = lambda k: bool(np.all(subraw[:, s, k] > 0))  # noqa: E731
+            if ok(0):
+                d["to_s0"] += float(np.median(sub[:, s, 0] - wait_ends[s]))
+                for k, key in ((1, "s0_s1"), (2, "s0_s2"), (3, "s0_s3")):
+                    if ok(k):
+                        d[key] += float(np.median(sub[:, s, k] - sub[:, s, 0]))
+            if ok(4):
+                d["arr_built"] += float(np.median(sub[:, s, 4] - prev_ends[s]))
+            if ok(5):
+                d["arr_wait"] += float(np.median(sub[:, s, 5] - prev_ends[s]))
         return out, total
 
 
@@ -116,13 +128,13 @@ def main():
         out, total = tr.summary(phase_names(w))
         print(f"{w.name} B={B}: step {total:.1f} us (per layer below, us)")
         print("| phase | layers | work (median WG) | work (slowest WG) | release | wait end -> stamp 0 | "
-              "stamp 0 -> 1 | stamp 0 -> 2 | stamp 0 -> 3 |")
-        print("|---|---|---|---|---|---|---|---|---|")
+              "stamp 0 -> 1 | stamp 0 -> 2 | stamp 0 -> 3 | prev arrival -> tables built | prev arrival -> wait |")
+        print("|---|---|---|---|---|---|---|---|---|---|---|")
         for k, d in out.items():
             n = d["n"]
             print(f"| {k} | {n} | {d['med'] / n:.1f} | {d['max'] / n:.1f} | {d['release'] / n:.1f} | "
-                  f"{d['to_slots'] / n:.1f} | {d['to_first'] / n:.1f} | {d['to_sweep_end'] / n:.1f} | "
-                  f"{d['k3'] / n:.1f} |")
+                  f"{d['to_s0'] / n:.1f} | {d['s0_s1'] / n:.1f} | {d['s0_s2'] / n:.1f} | {d['s0_s3'] / n:.1f} | "
+                  f"{d['arr_built'] / n:.1f} | {d['arr_wait'] / n:.1f} |")
         sys.stdout.flush()
         del tr
     m.close()

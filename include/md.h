@@ -182,8 +182,10 @@ md_status md_get_device_status(md_model* m);
  * wall-clock stamps (hipDeviceAttributeWallClockRate ticks) into
  * dev_buf[wg * n_per_wg + i]: slot 2s is when workgroup wg finished the work
  * before sync point s, slot 2s+1 when its wait there ended, and the last
- * slot when the workgroup started.  dev_buf holds md_grid_size(m) * n_per_wg
- * uint64 values; NULL turns recording off. */
+ * slot when the workgroup started; slots n_per_wg/2 + 8p + k hold phase p's
+ * own stamps (k < 4, after its wait; k = 4 its work tables built, k = 5 its
+ * wait started).  Stamps that do not fit are dropped.  dev_buf holds
+ * md_grid_size(m) * n_per_wg uint64 values; NULL turns recording off. */
 md_status md_set_trace(md_model* m, uint64_t* dev_buf, int32_t n_per_wg);
 
 /* Number of workgroups (one per CU) a step launches. */

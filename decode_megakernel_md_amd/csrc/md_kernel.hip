@@ -427,15 +427,116 @@ struct SlotBuilder {
     if (N != lastN) { lastq = rows_of((N + 3) >> 2, blockIdx.x, gridDim.x); lastN = N; }
     return lastq;
   }
-  __device__ void singles_of(int m, int N) {
-    if (replay) return;
-    RowSplit q = quarters(N);
-    for (int gq = q.r0; gq < q.r1; ++gq) single(m, gq);
+  // Whole slots of a run, one lane per slot: slots ns .. ns+n-1 hold
+  // quarters gq0 + 4k .. +3 of matrix m (and, for pairs, slots ns+2k /
+  // ns+2k+1 the gate / up quarters of the same rows).  Opens their groups.
+  __device__ void bulk(int m, int mu, int gq0, int n, bool pairs) {
+    const int per = pairs ? 2 : 1;
+    if (ns + per * n > MAXSLOT) { ovf = true; return; }
+    for (int k = __lane_id(); k < n; k += 64) {
+      const int si = ns + per * k;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        GSM.slots[si].m[e] = (int8_t)m;
+        GSM.slots[si].gq[e] = gq0 + 4 * k + e;
+        if (pairs) {
+          GSM.slots[si + 1].m[e] = (int8_t)mu;
+          GSM.slots[si + 1].gq[e] = gq0 + 4 * k + e;
+        }
+      }
+      if (si % TG == 0) GSM.grp[si / TG] = gd;
+    }
+    // groups opened: slot indices in [ns, ns + per*n) that are multiples of TG
+    const int first = (ns + TG - 1) / TG, last = (ns + per * n - 1) / TG;
+    const int ng = last - first + 1;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot[w] += ng * ((gd.KS - w + NW - 1) / NW);
+    ns += per * n;
   }
-  __device__ void pairs_of(int mg, int mu, int N) {
+  __device__ void singles_of(int m, int N) { singles_in(m, quarters(N)); }
+  __device__ void pairs_of(int mg, int mu, int N) { pairs_in(mg, mu, quarters(N)); }
+  // quarters q.r0 .. q.r1-1 of matrix m (of gate/up matrices mg, mu)
+  __device__ void singles_in(int m, RowSplit q) {
     if (replay) return;
+    int gq = q.r0;
+    while (fill != 0 && gq < q.r1) single(m, gq++);
+    if (fill == 0 && q.r1 - gq >= 4) {
+      const int n = (q.r1 - gq) >> 2;
+      bulk(m, 0, gq, n, false);
+      gq += 4 * n;
+    }
+    for (; gq < q.r1; ++gq) single(m, gq);
+  }
+  __device__ void pairs_in(int mg, int mu, RowSplit q) {
+    if (replay) return;
+    int gq = q.r0;
+    while (pfill != 0 && gq < q.r1) pair(mg, mu, gq++);
+    if (pfill == 0 && q.r1 - gq >= 4) {
+      const int n = (q.r1 - gq) >> 2;
+      bulk(mg, mu, gq, n, true);
+      gq += 4 * n;
+    }
+    for (; gq < q.r1; ++gq) pair(mg, mu, gq);
+  }
+  // Gate/up pairs of nu experts entered as matrices m0 + 2j (gate) and
+  // m0 + 2j + 1 (up), all N rows: this workgroup's quarters of each, expert
+  // after expert, four to a pair of slots (one lane per quarter); the last
+  // pair of slots is closed.  Same tables as pairs_of expert by expert.
+  __device__ void expert_pairs(int m0, int nu, int N) {
+    if (replay) return;
+    pflush();
     RowSplit q = quarters(N);
-    for (int gq = q.r0; gq < q.r1; ++gq) pair(mg, mu, gq);
+    const int npq = q.r1 - q.r0, E = nu * npq, P = (E + 3) >> 2;
+    if (ns + 2 * P > MAXSLOT) { ovf = true; return; }
+    for (int i = __lane_id(); i < 4 * P; i += 64) {
+      const int ps = i >> 2, e = i & 3, si = ns + 2 * ps;
+      const bool v = i < E;
+      const int j = v ? i / npq : 0;
+      const int gq = v ? q.r0 + (i - j * npq) : -1;
+      GSM.slots[si].m[e] = (int8_t)(v ? m0 + 2 * j : 0);
+      GSM.slots[si].gq[e] = gq;
+      GSM.slots[si + 1].m[e] = (int8_t)(v ? m0 + 2 * j + 1 : 0);
+      GSM.slots[si + 1].gq[e] = gq;
+      if (e == 0 && si % TG == 0) GSM.grp[si / TG] = gd;
+    }
+    if (P > 0) {
+      const int ng = (ns + 2 * P - 1) / TG - (ns + TG - 1) / TG + 1;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) tot[w] += ng * ((gd.KS - w + NW - 1) / NW);
+    }
+    ns += 2 * P;
+  }
+  // Singles of nu experts entered as matrices m0 + j, all N rows, expert j
+  // reading U at u0 + j * ustride (K columns): each expert's quarters fill
+  // whole groups of their own (one lane per slot).  Same tables as begin()
+  // plus singles_of expert by expert.
+  __device__ void expert_singles(int m0, int nu, int N, uint32_t u0, uint32_t ustride, int K) {
+    if (replay) return;
+    close();
+    if (K < 32 * MIN_KS || (K & 31)) ovf = true;
+    RowSplit q = quarters(N);
+    const int nq = q.r1 - q.r0;
+    if (nq <= 0 || nu <= 0) return;
+    const int S = ((nq + 3) / 4 + TG - 1) / TG * TG;  // slots per expert
+    if (ns + nu * S > MAXSLOT) { ovf = true; return; }
+    for (int i = __lane_id(); i < nu * S; i += 64) {
+      const int j = i / S, k = i - j * S, si = ns + i;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int qi = 4 * k + e;
+        const bool v = qi < nq;
+        GSM.slots[si].m[e] = (int8_t)(v ? m0 + j : 0);
+        GSM.slots[si].gq[e] = v ? q.r0 + qi : -1;
+      }
+      if (k % TG == 0) {
+        GroupDesc g;
+        g.u_off = u0 + (uint32_t)j * ustride; g.KS = K >> 5; g.kind = GK_SINGLE; g.pad_ = 0;
+        GSM.grp[si / TG] = g;
+      }
+    }
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot[w] += nu * (S / TG) * (((K >> 5) - w + NW - 1) / NW);
+    ns += nu * S;
   }
   __device__ void finish() {
     if (replay) {
@@ -2050,6 +2151,7 @@ struct RouteSmem {
   float w[MAXB][8];       // their weights
   float wt[MAXB][64];     // weight of U entry j for token t (0: not chosen)
   const uint16_t* ex[64][3];  // gate, up, down weights of U entry j
+  const uint16_t* exall[64][3];  // every expert's (fetched before the routing is known)
   uint64_t mask[MAXB];    // experts each token chose
 };
 constexpr size_t cmax_(size_t a, size_t b) { return a > b ? a : b; }
@@ -2098,11 +2200,9 @@ __device__ __noinline__ void phase_residual(KParams& pk, int l_layer, int mode, 
         sb.singles_of(m, H);
       }
       const int nu = __builtin_amdgcn_readfirstlane(RSM.nu);
-      for (int j = 0; j < nu; ++j) {
-        int m = sb.mat(RSM.ex[j][2], H, p.expert_ffn, 0);
-        sb.begin(p.off_hr + (uint32_t)j * p.hr_stride, p.expert_ffn, GK_SINGLE);
-        sb.singles_of(m, H);
-      }
+      const int m0 = sb.nm;
+      for (int j = 0; j < nu; ++j) sb.mat(RSM.ex[j][2], H, p.expert_ffn, 0);
+      sb.expert_singles(m0, nu, H, p.off_hr, p.hr_stride, p.expert_ffn);
     }
   }
   builder_done(p, sb, nrow);
@@ -2166,15 +2266,29 @@ __device__ __noinline__ void phase_moe_a(KParams& pk, int l_layer, int wait_idx)
   SlotBuilder sb;
   if (threadIdx.x < 64) {
     sb.start(PL_MOE_A);
+    // The router's few quarters go to workgroups of their own (the last
+    // ones): a router quarter is a whole group of k-steps, which on top of
+    // a shared-expert group would double that workgroup's stream.
+    const int G = gridDim.x, w = blockIdx.x, rq = (p.n_experts + 3) >> 2;
+    const bool apart = p.n_shared > 0 && G > 2 * rq;
     if (p.n_shared > 0) {
       int mg = sb.mat(L.sh_gate, p.shared_ffn, p.H, 0);
       int mu = sb.mat(L.sh_up, p.shared_ffn, p.H, 0);
       sb.begin(p.off_u, p.H, GK_PAIR);
-      sb.pairs_of(mg, mu, p.shared_ffn);
+      const int nq = (p.shared_ffn + 3) >> 2;
+      if (!apart) sb.pairs_of(mg, mu, p.shared_ffn);
+      else if (w < G - rq) sb.pairs_in(mg, mu, rows_of(nq, w, G - rq));
     }
     int mr = sb.mat(L.router, p.n_experts, p.H, -1);
     sb.begin(p.off_u, p.H, GK_SINGLE);
-    sb.singles_of(mr, p.n_experts);
+    if (!apart) {
+      sb.singles_of(mr, p.n_experts);
+    } else if (w >= G - rq) {
+      RowSplit q;
+      q.r0 = w - (G - rq);
+      q.r1 = q.r0 + 1;
+      sb.singles_in(mr, q);
+    }
   }
   builder_done(p, sb, -1);
   gemv_phase(p, wait_idx, p.H, p.off_ssq, EPI_BY_KIND, 0, 0, nullptr);
@@ -2196,6 +2310,14 @@ __device__ __noinline__ void phase_moe_a(KParams& pk, int l_layer, int wait_idx)
 // weights softmax(logits) over all experts at the chosen ones, renormalised
 // over the chosen ones when norm_topk.  Every workgroup runs this on the same
 // data in the same order.  Workgroup 0 reports the choices.
+// Every expert's weight pointers of the layer into LDS.  They do not depend
+// on the routing, so this runs before the wait for the router logits.
+__device__ __forceinline__ void prefetch_experts(KParams& pk, int layer) {
+  PARAMS;
+  KLayer& L = layer_ref(p, layer);
+  for (int i = threadIdx.x; i < p.n_experts * 3; i += NT) RSM.exall[i / 3][i % 3] = L.experts[i];
+}
+
 __device__ __noinline__ void compute_routes(KParams& pk, int layer) {
   PARAMS;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -2237,10 +2359,8 @@ __device__ __noinline__ void compute_routes(KParams& pk, int layer) {
     RSM.nu = n;
   }
   __syncthreads();
-  // the chosen experts' weight pointers, fetched in parallel (the slot
-  // builders read them from LDS)
-  const LayerDesc& L = p.layers[layer];
-  for (int i = threadIdx.x; i < RSM.nu * 3; i += NT) RSM.ex[i / 3][i % 3] = L.experts[RSM.u[i / 3] * 3 + i % 3];
+  // the chosen experts' weight pointers (the slot builders read them here)
+  for (int i = threadIdx.x; i < RSM.nu * 3; i += NT) RSM.ex[i / 3][i % 3] = RSM.exall[RSM.u[i / 3]][i % 3];
   if (threadIdx.x < B * k) {
     int t = threadIdx.x / k, j = threadIdx.x % k;
     RSM.wt[t][RSM.pos[RSM.ids[t][j]]] = RSM.w[t][j];
@@ -2258,11 +2378,12 @@ __device__ __noinline__ void phase_moe_b(KParams& pk, int l_layer, int wait_idx)
     sb.start();
     sb.begin(p.off_u, p.H, GK_PAIR);
     const int nu = __builtin_amdgcn_readfirstlane(RSM.nu);
+    const int m0 = sb.nm;
     for (int j = 0; j < nu; ++j) {
-      int mg = sb.mat(RSM.ex[j][0], p.expert_ffn, p.H, j);
-      int mu = sb.mat(RSM.ex[j][1], p.expert_ffn, p.H, j);
-      sb.pairs_of(mg, mu, p.expert_ffn);
+      sb.mat(RSM.ex[j][0], p.expert_ffn, p.H, j);
+      sb.mat(RSM.ex[j][1], p.expert_ffn, p.H, j);
     }
+    sb.expert_pairs(m0, nu, p.expert_ffn);
   }
   builder_done(p, sb, -1);
   gemv_phase(p, wait_idx, p.H, p.off_ssq, EPI_BY_KIND, 0, 0, nullptr);
@@ -2374,8 +2495,8 @@ __device__ __forceinline__ void run_one_phase(KParams& pk, int layer, int phase)
     case PH_GATEUP: phase_gateup(p, l_layer, -1); break;
     case PH_DOWN: phase_residual(p, l_layer, RES_DENSE_DOWN, g_next, -1); break;
     case PH_MOE_A: phase_moe_a(p, l_layer, -1); break;
-    case PH_MOE_B: compute_routes(p, l); phase_moe_b(p, l_layer, -1); break;
-    case PH_MOE_C: compute_routes(p, l); phase_residual(p, l_layer, RES_MOE_DOWN, g_next, -1); break;
+    case PH_MOE_B: prefetch_experts(p, l); compute_routes(p, l); phase_moe_b(p, l_layer, -1); break;
+    case PH_MOE_C: prefetch_experts(p, l); compute_routes(p, l); phase_residual(p, l_layer, RES_MOE_DOWN, g_next, -1); break;
     case PH_KDA_PROJ: phase_kda_proj(p, l_layer, -1); break;
     case PH_KDA_REC: phase_kda_rec(p, l_layer); break;
     case PH_KDA_O: phase_residual(p, l_layer, RES_KDA_O, L.ffn_norm, -1); break;
@@ -2466,6 +2587,7 @@ extern "C" __global__ __launch_bounds__(NT) void md_megakernel(Params p_arg) {
     } else {
       phase_moe_a(p, l_layer, sidx++);
       ARRIVE();
+      prefetch_experts(p, l);
       WAIT();
       compute_routes(p, l);
       phase_moe_b(p, l_layer, -1);

@@ -365,6 +365,22 @@ struct SlotBuilder {
     for (int w = 0; w < NW; ++w) tot[w] = 0;
     gd.u_off = 0; gd.KS = MIN_KS; gd.kind = GK_SINGLE; gd.pad_ = 0;
   }
+  // Matrices of the chosen experts, one lane per matrix: for expert j of
+  // U, its weights RSM.ex[j][c0 .. c0+nc-1] (N x K), entered at m0 + nc*j + c;
+  // tag j when tag_j, else 0.  Returns m0.
+  template <int NC>
+  __device__ int expert_mats(const uint16_t* const (*ex)[3], int nu, int c0, int N, int K, bool tag_j) {
+    const int m0 = nm;
+    if (m0 + NC * nu > MAXMAT) { ovf = true; return 0; }
+    for (int i = __lane_id(); i < NC * nu; i += 64) {
+      const int j = i / NC, c = i - j * NC;
+      MatDesc d;
+      d.w = (uint64_t)ex[j][c0 + c]; d.tstride = (uint64_t)(K >> 5) * 1024u; d.N = N; d.tag = tag_j ? j : 0;
+      GSM.mats[m0 + i] = d;
+    }
+    nm = m0 + NC * nu;
+    return m0;
+  }
   __device__ int mat(const void* w, int N, int K, int tag) {
     int i = nm;
     if (i >= MAXMAT) { ovf = true; return 0; }
@@ -2200,8 +2216,7 @@ __device__ __noinline__ void phase_residual(KParams& pk, int l_layer, int mode, 
         sb.singles_of(m, H);
       }
       const int nu = __builtin_amdgcn_readfirstlane(RSM.nu);
-      const int m0 = sb.nm;
-      for (int j = 0; j < nu; ++j) sb.mat(RSM.ex[j][2], H, p.expert_ffn, 0);
+      const int m0 = sb.expert_mats<1>(RSM.ex, nu, 2, H, p.expert_ffn, false);
       sb.expert_singles(m0, nu, H, p.off_hr, p.hr_stride, p.expert_ffn);
     }
   }
@@ -2347,16 +2362,16 @@ __device__ __noinline__ void compute_routes(KParams& pk, int layer) {
     if (lane < k) RSM.w[t][lane] = RSM.w[t][lane] / den;
     if (lane == 0) RSM.mask[t] = chosen;
   }
-  if (threadIdx.x < 64) RSM.pos[threadIdx.x] = -1;
   for (int i = threadIdx.x; i < MAXB * 64; i += NT) RSM.wt[i >> 6][i & 63] = 0.f;
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x < 64) {  // U = the union, ascending; expert e (lane e) sits at popcount of the ids below it
     uint64_t mask = 0;
     for (int t = 0; t < B; ++t) mask |= RSM.mask[t];
-    int n = 0;
-    for (int e = 0; e < E; ++e)
-      if ((mask >> e) & 1ull) { RSM.u[n] = e; RSM.pos[e] = n; ++n; }
-    RSM.nu = n;
+    const bool in = (mask >> lane) & 1ull;
+    const int at = __popcll(mask & ((1ull << lane) - 1ull));
+    if (in) RSM.u[at] = lane;
+    RSM.pos[lane] = in ? at : -1;
+    if (lane == 0) RSM.nu = __popcll(mask);
   }
   __syncthreads();
   // the chosen experts' weight pointers (the slot builders read them here)
@@ -2378,11 +2393,7 @@ __device__ __noinline__ void phase_moe_b(KParams& pk, int l_layer, int wait_idx)
     sb.start();
     sb.begin(p.off_u, p.H, GK_PAIR);
     const int nu = __builtin_amdgcn_readfirstlane(RSM.nu);
-    const int m0 = sb.nm;
-    for (int j = 0; j < nu; ++j) {
-      sb.mat(RSM.ex[j][0], p.expert_ffn, p.H, j);
-      sb.mat(RSM.ex[j][1], p.expert_ffn, p.H, j);
-    }
+    const int m0 = sb.expert_mats<2>(RSM.ex, nu, 0, p.expert_ffn, p.H, true);
     sb.expert_pairs(m0, nu, p.expert_ffn);
   }
   builder_done(p, sb, -1);

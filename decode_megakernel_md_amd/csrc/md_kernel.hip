@@ -1892,7 +1892,9 @@ __device__ __noinline__ void phase_mla_absorb(KParams& pk, int l_layer) {
 // the matrix cores (rows as the A operand, the heads' absorbed queries as
 // hi/lo B columns), an online softmax per head, then z_h += p_t c_t with
 // each lane holding 8 latent dims.  Partial (max, sum, z) per head go to the
-// workspace.
+// workspace.  Inlined into the kernel: as a called function it would save
+// and restore the callee-saved registers its live values occupy (about 116
+// per lane, through scratch memory, on every call).
 constexpr int MLA_ROWP = MLA_QA + 8;  // LDS row pitch in bf16 (pads rows off the same banks)
 struct MlaSmem {
   uint16_t rows[2][32][MLA_ROWP];
@@ -1918,7 +1920,7 @@ __device__ __forceinline__ void mla_store_block(const i32x4 (&pf)[9], int buf) {
   }
 }
 
-__device__ __noinline__ void phase_mla_attn(KParams& pk, int l_layer) {
+__device__ __forceinline__ void phase_mla_attn(KParams& pk, int l_layer) {
   PARAMS;
   KLayer& L = layer_ref(p, l_layer);
   MlaSmem& sm = *(MlaSmem*)md_smem;

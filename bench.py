@@ -65,6 +65,16 @@ def algorithmic_bytes(w, B, positions_per_seq, expert_ids=None):
     return wb, kvb
 
 
+def traffic_bytes(workload, B):
+    """HBM bytes (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter
+    reads for a plain device copy) per megakernel launch, as recorded by
+    `profiling traffic` from rocprofv3 counter runs; None when there is no
+    record for this workload and batch or the kernel has changed since."""
+    from decode_megakernel_md_amd.profiling import traffic_for
+    rec = traffic_for(workload, B)
+    return None if rec is None else rec["bytes"]
+
+
 def time_steps(m, B, steps, warmup, multilaunch=False):
     import torch
     w = m.w
@@ -310,7 +320,7 @@ def main():
         "config": {"workload": w.name, "batch": B0, "context": w.context, "layers": w.n_layers,
                    "hidden": w.hidden, "chained_greedy_steps": steps},
         "roofline": {"bound": "hbm", "achieved": r0["achieved_gbs"], "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": r0["frac"], "traffic": None},
+                     "frac": r0["frac"], "traffic": traffic_bytes(args.workload, B0)},
         "cpu_baseline": cpu,
         "batches": {str(B): res[B] for B in batches},
         "multilaunch": {str(B): ml[B] for B in ml},

@@ -3,19 +3,34 @@
     python -m decode_megakernel_md_amd.profiling <kernel_stats.csv | results.db>
     python -m decode_megakernel_md_amd.profiling gaps <kernel_trace.csv | results.db> [kernel-name-substring]
     python -m decode_megakernel_md_amd.profiling pmc <counter_collection.csv>
+    python -m decode_megakernel_md_amd.profiling traffic <fetch.csv> <write.csv> [workload] [batch]
 
 The first form prints a per-kernel table (calls, total/avg/min/max duration
 in microseconds) from rocprofv3's --stats CSV or its rocpd SQLite database.
 The second lists the idle time between consecutive dispatches of the named
 kernel (default: the per-phase kernel of the multi-launch step): the
 bubbles a single persistent launch removes.  The third averages each
-counter per dispatch and kernel from a --pmc run."""
+counter per dispatch and kernel from a --pmc run.  The fourth turns a
+FETCH_SIZE run and a WRITE_SIZE run of profile_run.py (a 1 GiB device copy,
+then decode steps) into HBM bytes per megakernel launch, each counter scaled
+by what it reads for the copy, and records them in traffic.json together
+with a hash of the kernel sources they were measured on (bench.py reports
+them only while the sources still hash the same)."""
 from __future__ import annotations
 
 import csv
+import hashlib
+import json
+import os
 import sqlite3
 import sys
 from typing import Dict, List
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_JSON = os.path.join(HERE, "traffic.json")
+KERNEL_SOURCES = ("md_kernel.hip", "md_device.h", "md_model.h")
+COPY_BYTES = 1 << 30       # profile_run.py's calibration copy
+COPY_KERNEL = "copyBuffer"
 
 
 def stats_from_db(path: str) -> List[Dict]:
@@ -89,6 +104,49 @@ def pmc(path: str) -> List[Dict]:
              "max": max(v)} for k, v in sorted(acc.items(), key=lambda kv: -sum(kv[1]))]
 
 
+def kernel_source_hash() -> str:
+    """SHA-256 over the device sources of the megakernel."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(HERE, "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_record(fetch_csv: str, write_csv: str, workload: str, batch: int) -> Dict:
+    """HBM bytes per md_megakernel launch from a FETCH_SIZE and a WRITE_SIZE
+    run.  Both counters are in KiB per dispatch; the calibration copy of
+    COPY_BYTES read and written gives each counter's bytes-per-unit factor."""
+    out = {"workload": workload, "batch": batch, "kernel_sha256": kernel_source_hash()}
+    for name, path in (("fetch", fetch_csv), ("write", write_csv)):
+        rows = list(csv.DictReader(open(path)))
+        copy = sum(float(r["Counter_Value"]) for r in rows if COPY_KERNEL in r["Kernel_Name"])
+        mk = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"] == "md_megakernel"]
+        if copy <= 0 or not mk:
+            raise ValueError(f"{path}: no calibration copy or no md_megakernel dispatch")
+        factor = COPY_BYTES / (copy * 1024.0)
+        out[name + "_kib_per_dispatch"] = sum(mk) / len(mk)
+        out[name + "_factor"] = factor
+        out[name + "_bytes"] = sum(mk) / len(mk) * 1024.0 * factor
+    out["bytes"] = out["fetch_bytes"] + out["write_bytes"]
+    return out
+
+
+def traffic_for(workload: str, batch: int):
+    """The recorded HBM bytes per launch for this workload and batch, or None
+    when there is no record or the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("batch") != batch:
+        return None
+    if rec.get("kernel_sha256") != kernel_source_hash():
+        return None
+    return rec
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "pmc":
         print("| kernel | counter | dispatches | mean per dispatch | min | max |")
@@ -96,6 +154,13 @@ if __name__ == "__main__":
         for r in pmc(sys.argv[2]):
             print(f"| {r['kernel'][:70]} | {r['counter']} | {r['dispatches']} | {r['mean']:.1f} | {r['min']:.1f} | "
                   f"{r['max']:.1f} |")
+    elif sys.argv[1] == "traffic":
+        wl = sys.argv[4] if len(sys.argv) > 4 else "dense_27b"
+        b = int(sys.argv[5]) if len(sys.argv) > 5 else 1
+        rec = traffic_record(sys.argv[2], sys.argv[3], wl, b)
+        with open(TRAFFIC_JSON, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec, indent=1))
     elif sys.argv[1] == "gaps":
         needle = sys.argv[3] if len(sys.argv) > 3 else "md_phase_kernel"
         r = gaps(dispatches(sys.argv[2], needle))

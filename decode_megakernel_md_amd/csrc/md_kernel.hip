@@ -1887,36 +1887,64 @@ __device__ __noinline__ void phase_mla_absorb(KParams& pk, int l_layer) {
 
 // M4: attention over the latent cache.  Task (b, chunk c) covers positions
 // [c*P, (c+1)*P) of 0..pos for every head at once, so each cache row is read
-// once per step.  Blocks of 32 rows are staged in LDS (next block in flight
-// while the current one is used); wave w serves heads 8w..8w+7: scores on
-// the matrix cores (rows as the A operand, the heads' absorbed queries as
-// hi/lo B columns), an online softmax per head, then z_h += p_t c_t with
-// each lane holding 8 latent dims.  Partial (max, sum, z) per head go to the
-// workspace.  Inlined into the kernel: as a called function it would save
-// and restore the callee-saved registers its live values occupy (about 116
-// per lane, through scratch memory, on every call).
+// once per step.  Blocks of 32 rows are staged in LDS twice: row-major (the A
+// operand of the scores) and transposed, latent dims by positions (the A
+// operand of P.C); the next block is in flight while the current one is
+// used.  Scores: wave w serves heads 8w..8w+7 on the matrix cores (rows as
+// the A operand, the heads' absorbed queries as hi/lo B columns), then an
+// online softmax per head; the probabilities go to LDS as hi/lo bf16 (about
+// 16 bits).  z_h += sum_t p_t c_t on the matrix cores too: wave w serves
+// heads 16(w%2)..+15 and latent dims 256(w/2)..+255, the hi and lo halves
+// of P accumulating into the same 16 dims x 16 heads tiles.  Partial
+// (max, sum, z) per head go to the workspace.  Inlined into the kernel: as a
+// called function it would save and restore the callee-saved registers its
+// live values occupy (about 116 per lane, through scratch memory, on every
+// call).
 constexpr int MLA_ROWP = MLA_QA + 8;  // LDS row pitch in bf16 (pads rows off the same banks)
+constexpr int MLA_TP = 32 + 8;        // pitch of the transposed block and of P, in bf16 (20 dwords:
+                                      // conflict-free transposed writes and operand reads)
 struct MlaSmem {
-  uint16_t rows[2][32][MLA_ROWP];
-  float s[32][32];                    // [position][head] scores, then probabilities
+  uint16_t rows[32][MLA_ROWP];        // the block, row-major: [position][latent | rope]
+  uint16_t ct[MLA_KL][MLA_TP];        // its latent part transposed: [dim][position]
+  uint16_t pb[2][32][MLA_TP];         // probabilities [hi, lo][head][position]
+  float s[32][32];                    // [position][head] scores
+  float corr[32];                     // per head: rescale of z for this block
 };
 
+// Thread tid loads chunk c16 = tid/32 + 8k (16 bytes) of row tid%32, k < 9;
+// rows past the chunk end are loaded as zeros.
 __device__ __forceinline__ void mla_load_block(i32x4 (&pf)[9], rsrc_t crs, int blk, int a1) {
+  const int rr = threadIdx.x & 31, t = blk + rr;
 #pragma unroll
   for (int k = 0; k < 9; ++k) {
-    int ci = threadIdx.x + NT * k;
-    int rr = ci / (MLA_QA / 8), c16 = ci % (MLA_QA / 8);
-    int t = blk + rr;
+    const int c16 = (threadIdx.x >> 5) + 8 * k;
     pf[k] = ld_x4<CP_SC1>(crs, t < a1 ? (uint32_t)(t * MLA_QA + c16 * 8) * 2u : OOB);
   }
 }
-__device__ __forceinline__ void mla_store_block(const i32x4 (&pf)[9], int buf) {
+// Row-major copy, and the transposed copy of the latent chunks (k < 8): the
+// lanes of rows 2i and 2i+1 (adjacent lanes) swap halves so that each writes
+// whole dwords (two positions) of four dims, even lane dims 0..3, odd lane 4..7.
+__device__ __forceinline__ void mla_store_block(const i32x4 (&pf)[9]) {
   MlaSmem& sm = *(MlaSmem*)md_smem;
+  const int rr = threadIdx.x & 31, odd = rr & 1, r0 = rr & ~1;
 #pragma unroll
   for (int k = 0; k < 9; ++k) {
-    int ci = threadIdx.x + NT * k;
-    int rr = ci / (MLA_QA / 8), c16 = ci % (MLA_QA / 8);
-    *(i32x4*)&sm.rows[buf][rr][c16 * 8] = pf[k];
+    const int c16 = (threadIdx.x >> 5) + 8 * k;
+    *(i32x4*)&sm.rows[rr][c16 * 8] = pf[k];
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int c16 = (threadIdx.x >> 5) + 8 * k;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int q = t + 2 * odd;  // this lane's dword of the chunk: dims 2q, 2q+1
+      const uint32_t send = (uint32_t)(odd ? pf[k][t] : pf[k][t + 2]);
+      const uint32_t par = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, DPP_QXOR1, 0xF, 0xF, false);
+      const uint32_t own = (uint32_t)pf[k][q];
+      const uint32_t lo = odd ? par : own, hi = odd ? own : par;  // position r0 in the low half
+      *(uint32_t*)&sm.ct[c16 * 8 + 2 * q][r0] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+      *(uint32_t*)&sm.ct[c16 * 8 + 2 * q + 1][r0] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+    }
   }
 }
 
@@ -1927,7 +1955,8 @@ __device__ __forceinline__ void phase_mla_attn(KParams& pk, int l_layer) {
   const int B = p.B, nh = p.mla_h, C = p.mla_chunks;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int nn = lane & 15, hh = nn >> 1, pp = nn & 1;
-  const int h0 = 8 * wv;
+  const int h0 = 8 * wv;                      // scores and softmax: heads h0..h0+7
+  const int hb = 16 * (wv & 1), db = 256 * (wv >> 1);  // P.C: heads hb..hb+15, dims db..db+255
   rsrc_t wr = make_rsrc_u(p.ws, p.ws_bytes);
   for (int task = blockIdx.x; task < B * C; task += gridDim.x) {
     const int c = task % C, b = task / C;
@@ -1937,6 +1966,8 @@ __device__ __forceinline__ void phase_mla_attn(KParams& pk, int l_layer) {
     const int a0 = c * P < n ? c * P : n, a1 = (c + 1) * P < n ? (c + 1) * P : n;
     const uint16_t* cache = (const uint16_t*)(p.kv + L.kv_off) + (size_t)row_seq(p, b) * p.max_ctx * MLA_QA;
     rsrc_t crs = make_rsrc_u(cache, (uint32_t)((size_t)n * MLA_QA * 2));
+    i32x4 pf[9];
+    if (a0 < a1) mla_load_block(pf, crs, a0, a1);
     // this wave's heads' absorbed queries as hi/lo B operands
     bf16x8 qb[MLA_KS];
     {
@@ -1954,20 +1985,16 @@ __device__ __forceinline__ void phase_mla_attn(KParams& pk, int l_layer) {
         }
       }
     }
-    float m_run[8], l_run[8], acc[8][8];
+    float m_run[8], l_run[8];
+    f32x4 z[16];  // tile j: dims db + 16j + 4*(lane/16) + i, head hb + nn
 #pragma unroll
     for (int h = 0; h < 8; ++h) {
       m_run[h] = -INFINITY;
       l_run[h] = 0.f;
+    }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
-    }
-    i32x4 pf[9];
-    int buf = 0;
-    if (a0 < a1) {
-      mla_load_block(pf, crs, a0, a1);
-      mla_store_block(pf, 0);
-    }
+    for (int j = 0; j < 16; ++j) z[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (a0 < a1) mla_store_block(pf);
     __syncthreads();
     for (int blk = a0; blk < a1; blk += 32) {
       const bool more = blk + 32 < a1;
@@ -1978,7 +2005,7 @@ __device__ __forceinline__ void phase_mla_attn(KParams& pk, int l_layer) {
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < MLA_KS; ++s) {
-          i32x4 kv = *(const i32x4*)&sm.rows[buf][tt * 16 + (lane & 15)][s * 32 + (lane >> 4) * 8];
+          i32x4 kv = *(const i32x4*)&sm.rows[tt * 16 + (lane & 15)][s * 32 + (lane >> 4) * 8];
           a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qb[s], a, 0, 0, 0);
         }
 #pragma unroll
@@ -1990,52 +2017,45 @@ __device__ __forceinline__ void phase_mla_attn(KParams& pk, int l_layer) {
       }
       __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
       __builtin_amdgcn_wave_barrier();
-      float corr[8];
+      // online softmax per head (positions past the chunk end have p = 0)
 #pragma unroll
       for (int h = 0; h < 8; ++h) {
         float sv = lane < 32 ? sm.s[lane][h0 + h] : -INFINITY;
         float mb = wave_max(sv);
         float mn = fmaxf(m_run[h], mb);
-        corr[h] = __expf(m_run[h] - mn);
+        const float corr = __expf(m_run[h] - mn);
         float pv = lane < 32 ? __expf(sv - mn) : 0.f;
-        l_run[h] = l_run[h] * corr[h] + wave_sum(pv);
+        l_run[h] = l_run[h] * corr + wave_sum(pv);
         m_run[h] = mn;
-        if (lane < 32) sm.s[lane][h0 + h] = pv;
-      }
-#pragma unroll
-      for (int h = 0; h < 8; ++h)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[h][j] *= corr[h];
-      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
-      __builtin_amdgcn_wave_barrier();
-      const int nrow = a1 - blk < 32 ? a1 - blk : 32;
-      for (int t = 0; t < nrow; ++t) {
-        i32x4 cv = *(const i32x4*)&sm.rows[buf][t][lane * 8];
-        f32x4 p0 = *(const f32x4*)&sm.s[t][h0];
-        f32x4 p1 = *(const f32x4*)&sm.s[t][h0 + 4];
-        float cf[8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          cf[2 * j] = __uint_as_float((uint32_t)cv[j] << 16);
-          cf[2 * j + 1] = __uint_as_float((uint32_t)cv[j] & 0xFFFF0000u);
+        if (lane < 32) {
+          uint16_t hi, lo;
+          split_hilo(pv, hi, lo);
+          sm.pb[0][h0 + h][lane] = hi;
+          sm.pb[1][h0 + h][lane] = lo;
         }
+        if (lane == 0) sm.corr[h0 + h] = corr;
+      }
+      __syncthreads();  // P and the rescales of every head
+      // z += P.C for heads hb..hb+15, dims db..db+255
+      {
+        const float cr = sm.corr[hb + nn];
+        const bf16x8 ph = *(const bf16x8*)&sm.pb[0][hb + nn][8 * (lane >> 4)];
+        const bf16x8 pl = *(const bf16x8*)&sm.pb[1][hb + nn][8 * (lane >> 4)];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          acc[0][j] += p0[0] * cf[j];
-          acc[1][j] += p0[1] * cf[j];
-          acc[2][j] += p0[2] * cf[j];
-          acc[3][j] += p0[3] * cf[j];
-          acc[4][j] += p1[0] * cf[j];
-          acc[5][j] += p1[1] * cf[j];
-          acc[6][j] += p1[2] * cf[j];
-          acc[7][j] += p1[3] * cf[j];
+        for (int j = 0; j < 16; ++j) {
+          const i32x4 cv = *(const i32x4*)&sm.ct[db + 16 * j + (lane & 15)][8 * (lane >> 4)];
+          f32x4 acc = z[j] * cr;
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cv), ph, acc, 0, 0, 0);
+          z[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cv), pl, acc, 0, 0, 0);
         }
       }
-      if (more) mla_store_block(pf, buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
+      __syncthreads();  // every wave is done with this block's rows, transposed copy and P
+      if (more) {
+        mla_store_block(pf);
+        __syncthreads();
+      }
     }
-    // partials of this wave's heads
+    // partials: (m, l) of the softmax heads by lane 0; z of the P.C heads, 4 dims per tile
 #pragma unroll
     for (int h = 0; h < 8; ++h) {
       const int hg = h0 + h;
@@ -2045,9 +2065,15 @@ __device__ __forceinline__ void phase_mla_attn(KParams& pk, int l_layer) {
         st_f32(wr, p.off_mml + idx * 8u, m_run[h]);
         st_f32(wr, p.off_mml + idx * 8u + 4u, l_run[h]);
       }
-      const f32x4 z0 = {acc[h][0], acc[h][1], acc[h][2], acc[h][3]}, z1 = {acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, z0), wr, p.off_mz + (idx * MLA_KL + lane * 8) * 4u, 0, CP_SC1);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, z1), wr, p.off_mz + (idx * MLA_KL + lane * 8 + 4) * 4u, 0, CP_SC1);
+    }
+    {
+      const int hg = hb + nn;
+      const uint32_t idx = (uint32_t)((b * C + c) * nh + (hg < nh ? hg : 0));
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, z[j]), wr,
+                                               hg < nh ? p.off_mz + (idx * MLA_KL + db + 16 * j + 4 * (lane >> 4)) * 4u : OOB,
+                                               0, CP_SC1);
     }
     __syncthreads();
   }

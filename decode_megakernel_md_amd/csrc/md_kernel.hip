@@ -2080,8 +2080,11 @@ __device__ __forceinline__ void phase_mla_attn(KParams& pk, int l_layer) {
 }
 
 // M5: combine the chunks of each head and un-absorb: o_h = W_uv,h z_h.
-// Task (h, 32-row slice of W_uv,h) for all tokens.
-__device__ __noinline__ void phase_mla_out(KParams& pk, int l_layer) {
+// Task (h, 32-row slice of W_uv,h) for all tokens.  The chunk partials are
+// read 32 at a time (the combine is latency-bound: one round trip per
+// round); inlined into the kernel, as the attention phases are, so that
+// those registers are not saved and restored through scratch.
+__device__ __forceinline__ void phase_mla_out(KParams& pk, int l_layer) {
   PARAMS;
   KLayer& L = layer_ref(p, l_layer);
   const int B = p.B, nh = p.mla_h, nope = p.nope, vd = p.vdim, VW = nope + vd, C = p.mla_chunks;
@@ -2117,17 +2120,18 @@ __device__ __noinline__ void phase_mla_out(KParams& pk, int l_layer) {
       if (ln == 0) cl[t] = 1.0f / den;
     }
     __syncthreads();
-    // z[t][d], thread per (token, 4 dims), 8 chunk loads in flight
+    // z[t][d], thread per (token, 4 dims), MZU chunk loads in flight
+    constexpr int MZU = 32;
     for (int e = threadIdx.x; e < B * (MLA_KL / 4); e += NT) {
       int t = e / (MLA_KL / 4), d4 = (e % (MLA_KL / 4)) * 4;
       float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-      for (int c0 = 0; c0 < C; c0 += 8) {
-        i32x4 v[8];
+      for (int c0 = 0; c0 < C; c0 += MZU) {
+        i32x4 v[MZU];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < MZU; ++u)
           v[u] = ld_x4<CP_SC1>(r, c0 + u < C ? p.off_mz + ((uint32_t)((t * C + c0 + u) * nh + h) * MLA_KL + d4) * 4u : OOB);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < MZU; ++u) {
           float f = c0 + u < C ? cw[t * 256 + c0 + u] : 0.f;
           o0 += f * __int_as_float(v[u][0]);
           o1 += f * __int_as_float(v[u][1]);

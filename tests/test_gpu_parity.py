@@ -191,7 +191,8 @@ def test_multilaunch_equals_megakernel(torch_cuda, name, B):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name,B", [("dense_27b", 1), ("dense_27b", 8), ("hybrid_moe", 1), ("hybrid_moe", 8)])
+@pytest.mark.parametrize("name,B", [("dense_27b", 1), ("dense_27b", 2), ("dense_27b", 4), ("dense_27b", 8),
+                                    ("hybrid_moe", 1), ("hybrid_moe", 8)])
 def test_full_shape_layers_match_oracle(torch_cuda, name, B):
     """The two large models at their full layer shapes, vocabulary and
     context, in the launch configuration bench.py times (grid = CU count,
@@ -207,4 +208,51 @@ def test_full_shape_layers_match_oracle(torch_cuda, name, B):
     o, kv_ref = GU.run_oracle_step(w, toks, pos)
     err = GU.compare_step(w, g, o, f"{name} B={B}")
     GU.compare_kv_rows(w, m.kv_host(), kv_ref, pos, B)
+    print(f"  max|dlogit|/rms = {err:.2e}")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("accept", [3, 6])
+def test_full_shape_verify_matches_oracle(torch_cuda, accept):
+    """Verify of 1 anchor + 7 drafts on the hybrid model at its full layer
+    shapes and vocabulary, in bench.py's launch configuration (4 layers: 3
+    delta-rule and 1 MLA, each with the 16-expert MoE; context 1024 rather
+    than 8192 so that the a-1 greedy steps and the 8 sequential verify rows
+    of the fp64 oracle finish in under a minute -- the 8192-position MLA
+    cache is covered by the decode test above), at the acceptance lengths
+    bench.py times: drafts are the oracle's greedy continuation for a-1
+    tokens, then a token that differs from the greedy one.  The acceptance
+    length, the next token, all 8 logit rows, the new cache rows and the
+    committed delta-rule states must match the oracle."""
+    torch = torch_cuda
+    from oracle import step as ostep
+    from tests.harness import HostWeights, host_kv, kv_copy
+    w = WL.get("verify_hybrid").replace(n_layers=4, context=1024, max_ctx=1024 + 32)
+    n = 8
+    p0 = w.context
+    W = HostWeights(w)
+    kv = host_kv(w)
+    toks = _greedy_drafts(w, W, kv, p0, accept, n)
+    print(f"case verify_hybrid 4 layers accept={accept} p0={p0} toks={toks}", flush=True)
+    kv_ref = kv_copy(kv)
+    v = ostep.verify_step(w, W, np.array([toks]), np.array([p0]), kv_ref)
+    assert int(v["accept_len"][0]) == accept
+    m = _model(w)
+    dev = m.device
+    t = torch.tensor([toks], dtype=torch.int32, device=dev)
+    pp = torch.tensor([p0], dtype=torch.int32, device=dev)
+    logits = torch.full((1, n, w.vocab), float("nan"), dtype=torch.float32, device=dev)
+    acc = torch.full((1,), -7, dtype=torch.int32, device=dev)
+    nxt = torch.full((1,), -7, dtype=torch.int32, device=dev)
+    m.verify(t, pp, logits, acc, nxt)
+    torch.cuda.synchronize(dev)
+    m.device_status()
+    assert int(acc.cpu()[0]) == accept
+    assert int(nxt.cpu()[0]) == int(v["next"][0])
+    g = {"logits": logits.cpu().numpy()[0], "next": v["argmax"][0]}
+    o = {"logits": v["logits"][0], "next": v["argmax"][0]}
+    err = GU.compare_step(w, g, o, f"verify_hybrid 4 layers a={accept}")
+    kvg = m.kv_host()
+    for j in range(n):
+        GU.compare_kv_rows(w, kvg, kv_ref, [p0 + j], 1)
     print(f"  max|dlogit|/rms = {err:.2e}")

@@ -112,6 +112,34 @@ def test_repeated_steps_are_bitwise_deterministic(torch_cuda):
     assert np.array_equal(a["logits"], b["logits"])
 
 
+@pytest.mark.parametrize("name,B", [("mini_dense", 3), ("mini_moe", 3), ("mini_hybrid", 3)])
+def test_chained_steps_match_oracle(torch_cuda, name, B):
+    """Several greedy decode steps in a row, each a launch of its own: the
+    GPU's cache rows and delta-rule states advance in place and its sync
+    counters alternate between their two banks, while the oracle advances its
+    own copy of the cache; every step's logits, tokens and expert ids must
+    match, and so must the caches and states at the end."""
+    from tests.harness import HostWeights, host_kv
+    from oracle import step as ostep
+    w = WL.get(name)
+    m = _model(w)
+    W = HostWeights(w)
+    kv_ref = host_kv(w)
+    toks = list(synth.tokens(w, B))
+    pos0 = [w.context - 4 * b for b in range(B)]
+    steps = 5
+    for s in range(steps):
+        pos = [p + s for p in pos0]
+        print(f"case {name} B={B} step {s} pos={pos} toks={toks}", flush=True)
+        g = GU.run_gpu_step(m, toks, pos)
+        o = ostep.decode_step(w, W, np.asarray(toks), np.asarray(pos), kv_ref)
+        GU.compare_step(w, g, o, f"{name} step {s}")
+        toks = [int(t) for t in o["next"]]
+    kvg = m.kv_host()
+    for s in range(steps):
+        GU.compare_kv_rows(w, kvg, kv_ref, [p + s for p in pos0], B)
+
+
 def _greedy_drafts(w, W, kv, p0, accept, n=8):
     """Tokens t_0..t_{n-1}: the anchor, then the oracle's greedy continuation
     for accept-1 tokens, then (when accept < n) a token that differs from the

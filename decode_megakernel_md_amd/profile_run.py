@@ -1,16 +1,19 @@
 """Driver for rocprofv3 counter runs.
 
     python -m decode_megakernel_md_amd.profile_run [--workload dense_27b] [--batch 1] [--steps 3]
-                                                    [--multilaunch] [--copy-mib 1024]
+                                                    [--multilaunch | --compare] [--copy-mib 1024]
 
 First a plain device-to-device copy of --copy-mib MiB (its byte count is
 known, so HBM counters read for it calibrate the counters read for the
 decode step), then --steps decode steps of the workload at the given batch
-and context, greedy tokens chained on the device."""
+and context, greedy tokens chained on the device.  --compare runs the steps
+once as the megakernel and, after a pause of 20 ms, once as the multi-launch
+baseline (one launch per phase), so that one kernel trace holds both."""
 from __future__ import annotations
 
 import argparse
 import sys
+import time
 
 
 def main():
@@ -19,6 +22,7 @@ def main():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--multilaunch", action="store_true")
+    ap.add_argument("--compare", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
     import torch
@@ -47,13 +51,15 @@ def main():
     ids = None
     if w.is_moe:
         ids = torch.empty((w.n_layers, B, w.top_k), dtype=torch.int32, device=dev)
-    for s in range(args.steps):
-        pos = torch.full((B,), w.context + s, dtype=torch.int32, device=dev)
-        m.decode(toks[s], pos, logits, toks[s + 1], ids, multilaunch=args.multilaunch)
-    torch.cuda.synchronize()
-    m.device_status()
-    print(f"# {w.name}: {args.steps} steps at batch {B} ({'multi-launch' if args.multilaunch else 'megakernel'})",
-          flush=True)
+    modes = [False, True] if args.compare else [args.multilaunch]
+    for ml in modes:
+        for s in range(args.steps):
+            pos = torch.full((B,), w.context + s, dtype=torch.int32, device=dev)
+            m.decode(toks[s], pos, logits, toks[s + 1], ids, multilaunch=ml)
+        torch.cuda.synchronize()
+        m.device_status()
+        print(f"# {w.name}: {args.steps} steps at batch {B} ({'multi-launch' if ml else 'megakernel'})", flush=True)
+        time.sleep(0.02)
     m.close()
 
 

@@ -7,9 +7,10 @@
 
 The first form prints a per-kernel table (calls, total/avg/min/max duration
 in microseconds) from rocprofv3's --stats CSV or its rocpd SQLite database.
-The second lists the idle time between consecutive dispatches of the named
-kernel (default: the per-phase kernel of the multi-launch step): the
-bubbles a single persistent launch removes.  The third averages each
+The second lists, per run of back-to-back dispatches of the named kernel
+(default md_megakernel, which also serves the multi-launch baseline's
+per-phase launches), the busy time and the idle time between consecutive
+dispatches: the bubbles a single persistent launch removes.  The third averages each
 counter per dispatch and kernel from a --pmc run.  The fourth turns a
 FETCH_SIZE run and a WRITE_SIZE run of profile_run.py (a 1 GiB device copy,
 then decode steps) into HBM bytes per megakernel launch, each counter scaled
@@ -162,13 +163,26 @@ if __name__ == "__main__":
             json.dump(rec, f, indent=1)
         print(json.dumps(rec, indent=1))
     elif sys.argv[1] == "gaps":
-        needle = sys.argv[3] if len(sys.argv) > 3 else "md_phase_kernel"
-        r = gaps(dispatches(sys.argv[2], needle))
-        print("| kernel | dispatches | runs | busy (us) | span (us) | idle between dispatches (us) | gaps | "
+        needle = sys.argv[3] if len(sys.argv) > 3 else "md_megakernel"
+        d = dispatches(sys.argv[2], needle)
+        print("| run | dispatches | busy (us) | span (us) | idle between dispatches (us) | gaps | "
               "mean gap (us) | max gap (us) |")
-        print("|---|---|---|---|---|---|---|---|---|")
-        print(f"| {needle} | {r['dispatches']} | {r['runs']} | {r['busy_us']:.1f} | {r['span_us']:.1f} | "
-              f"{r['idle_us']:.1f} | {r['gaps']} | {r['mean_gap_us']:.2f} | {r['max_gap_us']:.2f} |")
+        print("|---|---|---|---|---|---|---|---|")
+        # one row per run (dispatches separated by less than 1 ms), then all of them
+        runs, cur = [], d[:1]
+        for a, b in zip(d, d[1:]):
+            if b[0] - a[1] > 1_000_000:
+                runs.append(cur)
+                cur = [b]
+            else:
+                cur.append(b)
+        if cur:
+            runs.append(cur)
+        for i, run in enumerate(runs + [d]):
+            r = gaps(run)
+            name = f"{i + 1}" if i < len(runs) else "all"
+            print(f"| {name} | {r['dispatches']} | {r['busy_us']:.1f} | {r['span_us']:.1f} | "
+                  f"{r['idle_us']:.1f} | {r['gaps']} | {r['mean_gap_us']:.2f} | {r['max_gap_us']:.2f} |")
     else:
         p = sys.argv[1]
         rows = stats_from_db(p) if p.endswith(".db") else stats_from_csv(p)

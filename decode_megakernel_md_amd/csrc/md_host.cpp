@@ -550,10 +550,14 @@ md_status md_get_device_status(md_model* m) {
   if (e != hipSuccess) return fail(MD_EHIP, "reading the device error word: %s", hipGetErrorString(e));
   if (err) {
     int zero = 0;
-    hipMemcpy(m->ws + m->lay.err, &zero, sizeof zero, hipMemcpyHostToDevice);
     // a failed step leaves its counter bank in an unknown state: clear both
-    hipMemset(m->ws + m->lay.sync, 0, (size_t)4 * 2 * m->lay.n_sync * SP_WORDS_);
-    hipDeviceSynchronize();
+    // (and the error word), so that the handle can run again
+    hipError_t c = hipMemcpy(m->ws + m->lay.err, &zero, sizeof zero, hipMemcpyHostToDevice);
+    if (c == hipSuccess) c = hipMemset(m->ws + m->lay.sync, 0, (size_t)4 * 2 * m->lay.n_sync * SP_WORDS_);
+    if (c == hipSuccess) c = hipDeviceSynchronize();
+    if (c != hipSuccess)
+      return fail(MD_EHIP, "device error 0x%x, and resetting the error word and counters failed: %s", err,
+                  hipGetErrorString(c));
     return fail(MD_EDEVICE, "device error 0x%x:%s%s%s%s", err, (err & MDE_WATCHDOG) ? " sync wait exceeded its bound" : "",
                 (err & MDE_TOKEN) ? " token out of range" : "", (err & MDE_POSITION) ? " position out of range" : "",
                 (err & MDE_CAPACITY) ? " a phase's work exceeds the per-workgroup tables (shape too large for this grid)" : "");

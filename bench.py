@@ -279,7 +279,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the hybrid MoE decode and verify sections")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU: the multi-GPU path is designed, not built; "
+        print(json.dumps({"error": "this library runs on one GPU: the multi-GPU path is designed, not built; "
                                    "run with --gpus 1"}))
         sys.exit(2)
 

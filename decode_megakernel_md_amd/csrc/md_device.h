@@ -15,6 +15,12 @@
 // a consumer reads the data only after it has observed the counter.  Because
 // no cross-workgroup value ever sits dirty in an L2, no L2 write-back or
 // invalidate (the costly part of an agent-scope fence on this part) is needed.
+// One exception: the weight stream's activations (the B operands of its
+// matrix-core tiles) are read with cache policy sc0, served by the XCD's L2.
+// That is safe because each activation buffer is written and read once per
+// launch (one buffer per use) and the L2s start every launch without copies
+// of the workspace: an XCD's first read misses and fetches the written-through
+// data, later reads of the same lines hit.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -32,6 +38,7 @@ constexpr int MAXB = 8;      // token rows per step (batch, or verify tokens)
 constexpr unsigned OOB = 0xFFFFFFF0u;  // buffer offset beyond any resource: loads return 0
 
 // cache-policy bits of buffer instructions on gfx950
+constexpr int CP_SC0 = 1;    // not kept in the CU's L1
 constexpr int CP_NT = 2;     // streaming (non-temporal)
 constexpr int CP_SC1 = 16;   // device scope: coherent across XCDs
 

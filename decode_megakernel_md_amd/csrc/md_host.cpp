@@ -166,6 +166,7 @@ md_status validate(const md_config* c) {
 struct WsLayout {
   size_t layers, experts, x, u, ssq, qkv, attn, attn_ml, ou, h, rl, hs, hr, hr_stride, uq, ssq2, ckv, qm, qabs, mz, mml,
       kda, ring, cand, zero, rope, sync, err, total;
+  size_t u_stride, ou_stride, h_stride, hs_stride, hr_lstride, uq_stride;  // one GEMV input buffer per use
   int rope_d;
   int n_sync, sync_attn_base;
 };
@@ -204,19 +205,26 @@ WsLayout ws_layout(const md_config* c) {
   w.layers = take(sizeof(LayerDesc) * (size_t)c->n_layers);
   w.experts = take(sizeof(void*) * 3 * (size_t)c->n_layers * (size_t)(c->n_experts > 0 ? c->n_experts : 1));
   w.x = take(4 * MAXB_ * H);
-  w.u = take(2 * 2 * MAXB_ * H);
+  const size_t L = (size_t)c->n_layers;
+  w.u_stride = align256(2 * 2 * MAXB_ * H);
+  w.u = take(w.u_stride * (2 * L + 1));
   w.ssq = take(4 * (size_t)GMAX * MAXB_);
   w.qkv = take(4 * MAXB_ * (size_t)nqkv);
   w.attn = take(4 * (size_t)MAXB_ * (c->n_q_heads > 0 ? c->n_q_heads : 1) * CMAX * (size_t)c->head_dim);
   w.attn_ml = take(8 * (size_t)MAXB_ * (c->n_q_heads > 0 ? c->n_q_heads : 1) * CMAX);
-  w.ou = take(2 * 2 * MAXB_ * (size_t)attn_out);
-  w.h = take(2 * 2 * MAXB_ * (size_t)F);
+  w.ou_stride = align256(2 * 2 * MAXB_ * (size_t)attn_out);
+  w.ou = take(w.ou_stride * L);
+  w.h_stride = align256(2 * 2 * MAXB_ * (size_t)F);
+  w.h = take(w.h_stride * L);
   w.rl = take(4 * (size_t)MAXB_ * (c->n_experts > 0 ? c->n_experts : 1));
-  w.hs = take(2 * 2 * MAXB_ * (size_t)(c->n_shared > 0 ? c->shared_ffn : 1));
+  w.hs_stride = align256(2 * 2 * MAXB_ * (size_t)(c->n_shared > 0 ? c->shared_ffn : 1));
+  w.hs = take(w.hs_stride * L);
   int nu = c->n_experts < MAXB_ * c->top_k ? c->n_experts : MAXB_ * c->top_k;
   w.hr_stride = align256(2 * 2 * MAXB_ * (size_t)(c->expert_ffn > 0 ? c->expert_ffn : 1));
-  w.hr = take(w.hr_stride * (size_t)(nu > 0 ? nu : 1));
-  w.uq = take(2 * 2 * MAXB_ * (size_t)(hyb ? c->q_lora : 1));
+  w.hr_lstride = w.hr_stride * (size_t)(nu > 0 ? nu : 1);
+  w.hr = take(w.hr_lstride * L);
+  w.uq_stride = align256(2 * 2 * MAXB_ * (size_t)(hyb ? c->q_lora : 1));
+  w.uq = take(w.uq_stride * L);
   w.ssq2 = take(4 * (size_t)GMAX * MAXB_);
   w.ckv = take(4 * MAXB_ * 576);
   w.qm = take(4 * MAXB_ * (size_t)mh * (hyb ? c->nope_dim + 64 : 1));
@@ -453,6 +461,8 @@ static md_status fill_params(md_model* m, const int32_t* tokens, const int32_t* 
   p.out_tokens = out_tokens; p.out_ids = out_ids;
   p.ws = m->ws; p.ws_bytes = (uint32_t)w.total;
   p.x = (float*)(m->ws + w.x);
+  p.u_stride = (uint32_t)w.u_stride; p.ou_stride = (uint32_t)w.ou_stride; p.h_stride = (uint32_t)w.h_stride;
+  p.hs_stride = (uint32_t)w.hs_stride; p.hr_lstride = (uint32_t)w.hr_lstride; p.uq_stride = (uint32_t)w.uq_stride;
   p.off_u = (uint32_t)w.u; p.off_ssq = (uint32_t)w.ssq; p.off_qkv = (uint32_t)w.qkv; p.off_attn = (uint32_t)w.attn; p.off_attn_ml = (uint32_t)w.attn_ml;
   p.off_ou = (uint32_t)w.ou; p.off_h = (uint32_t)w.h;
   p.mla_h = c->mla_heads; p.q_lora = c->q_lora; p.nope = c->nope_dim; p.vdim = c->v_dim;

@@ -50,6 +50,17 @@ __device__ __forceinline__ KLayer& layer_ref(KParams& pk, int l) {
   return ((KLayer*)p.layers)[__builtin_amdgcn_readfirstlane(l)];
 }
 
+// GEMV inputs: one buffer per use within a step (u: 2l = attention input
+// of layer l, 2l+1 = its FFN input, 2L = the final norm's input; the others
+// one per layer), so that no such address is read before it is written in
+// the same launch and their loads may be served by the local L2.
+__device__ __forceinline__ uint32_t u_at(KParams& pk, int i) { PARAMS; return p.off_u + (uint32_t)i * p.u_stride; }
+__device__ __forceinline__ uint32_t ou_at(KParams& pk, int l) { PARAMS; return p.off_ou + (uint32_t)l * p.ou_stride; }
+__device__ __forceinline__ uint32_t h_at(KParams& pk, int l) { PARAMS; return p.off_h + (uint32_t)l * p.h_stride; }
+__device__ __forceinline__ uint32_t hs_at(KParams& pk, int l) { PARAMS; return p.off_hs + (uint32_t)l * p.hs_stride; }
+__device__ __forceinline__ uint32_t hr_at(KParams& pk, int l) { PARAMS; return p.off_hr + (uint32_t)l * p.hr_lstride; }
+__device__ __forceinline__ uint32_t uq_at(KParams& pk, int l) { PARAMS; return p.off_uq + (uint32_t)l * p.uq_stride; }
+
 // ===================================================================== sync
 // One sync point = 8 class counters (one per workgroup class blockIdx % 8,
 // which on this part is the XCD the workgroup runs on) and one extra line,
@@ -360,6 +371,12 @@ struct SlotBuilder {
   __device__ void start(int plan_id = -1) {
     plan = plan_id;
     replay = plan_id >= 0 && __builtin_amdgcn_readfirstlane(PLANS[plan_id].valid) != 0;
+    if (replay) {  // the cached tables; begin() enters this use's input
+      SlotPlan& P = PLANS[plan_id];
+      const int pns = __builtin_amdgcn_readfirstlane(P.nslots);
+      copy_words(GSM.slots, P.slots, pns * (int)(sizeof(Slot) / 4));
+      copy_words(GSM.grp, P.grp, (pns / TG) * (int)(sizeof(GroupDesc) / 4));
+    }
     ns = 0; fill = 0; pfill = 0; nm = 0; ovf = false;
 #pragma unroll
     for (int w = 0; w < NW; ++w) tot[w] = 0;
@@ -412,7 +429,11 @@ struct SlotBuilder {
     }
   }
   __device__ void begin(uint32_t u_off, int K, int kind) {
-    if (replay) return;
+    if (replay) {  // a replayed plan's groups all take this use's input
+      const int ng = __builtin_amdgcn_readfirstlane(PLANS[plan].nslots) / TG;
+      for (int i = __lane_id(); i < ng; i += 64) GSM.grp[i].u_off = u_off;
+      return;
+    }
     close();
     if (K < 32 * MIN_KS || (K & 31)) ovf = true;
     gd.u_off = u_off; gd.KS = K >> 5; gd.kind = kind; gd.pad_ = 0;
@@ -559,8 +580,6 @@ struct SlotBuilder {
       SlotPlan& P = PLANS[plan];
       ns = __builtin_amdgcn_readfirstlane(P.nslots);
       ovf = ovf || __builtin_amdgcn_readfirstlane(P.overflow) != 0;
-      copy_words(GSM.slots, P.slots, ns * (int)(sizeof(Slot) / 4));
-      copy_words(GSM.grp, P.grp, (ns / TG) * (int)(sizeof(GroupDesc) / 4));
 #pragma unroll
       for (int w = 0; w < NW; ++w) tot[w] = __builtin_amdgcn_readfirstlane(P.wtot[w]);
     } else {
@@ -572,7 +591,12 @@ struct SlotBuilder {
     GSM.overflow = ovf ? 1 : 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) GSM.wtot[w] = tot[w];
-    if (!replay && plan >= 0 && !ovf && ns <= PLAN_SLOTS) {
+    // a plan is kept only when all its groups read one input (replays give
+    // them this use's input, which differs from layer to layer)
+    bool one_u = true;
+    for (int i = __lane_id(); i < ns / TG; i += 64) one_u = one_u && GSM.grp[i].u_off == GSM.grp[0].u_off;
+    one_u = __all(one_u);
+    if (!replay && plan >= 0 && !ovf && ns <= PLAN_SLOTS && one_u) {
       SlotPlan& P = PLANS[plan];
       copy_words(P.slots, GSM.slots, ns * (int)(sizeof(Slot) / 4));
       copy_words(P.grp, GSM.grp, (ns / TG) * (int)(sizeof(GroupDesc) / 4));
@@ -680,7 +704,13 @@ __device__ __forceinline__ void gs_issue_a(GemvStream& s, int d) {
     if (s.ig < s.ngroups) gs_group(s, s.ig);
   }
 }
-__device__ __forceinline__ void gs_issue_b(GemvStream& s, int d) { s.rb[d] = ld_x4<CP_SC1>(s.urs, s.bo[d]); }
+// Activation (B operand) loads: cache policy sc0 (not kept in the CU's L1,
+// served by the XCD's L2).  Every activation buffer is used once per launch
+// (one buffer per use, see u_at), so the L2 never holds an older copy of it:
+// the first read in an XCD fetches what the producers wrote through to
+// memory before the sync point, later reads in that XCD hit.  (On a buffer
+// reused within a launch such loads would return stale lines: measured.)
+__device__ __forceinline__ void gs_issue_b(GemvStream& s, int d) { s.rb[d] = ld_x4<CP_SC0>(s.urs, s.bo[d]); }
 
 // Steady state: weight and activation loads of one k-step, then the group
 // switch (loads before the branch, so the compiler sees one load sequence).
@@ -691,7 +721,7 @@ __device__ __forceinline__ void gs_issue(GemvStream& s, int d) {
     s.ra[d][i] = __builtin_nontemporal_load((const __attribute__((address_space(1))) i32x4*)(ok ? s.pa[i] : s.zero_addr));
     s.pa[i] += s.ps[i];
   }
-  s.rb[d] = ld_x4<CP_SC1>(s.urs, (ok && s.boff != OOB) ? s.boff + (uint32_t)(s.is * NW + s.wv) * 64u : OOB);
+  s.rb[d] = ld_x4<CP_SC0>(s.urs, (ok && s.boff != OOB) ? s.boff + (uint32_t)(s.is * NW + s.wv) * 64u : OOB);
   if (++s.is == s.nks_i) {
     s.is = 0;
     ++s.ig;
@@ -888,7 +918,7 @@ __device__ __noinline__ void phase_embed(KParams& pk) {
     }
     float x = bf16_f32(p.embed[(size_t)tok * p.H + i]);
     p.x[t * p.H + i] = x;
-    put_hilo(r, p.off_u, p.H, t, i, bf16_f32(g[i]) * x);
+    put_hilo(r, u_at(p, 0), p.H, t, i, bf16_f32(g[i]) * x);
     part[threadIdx.x * MAXB + t] += x * x;
   }
   store_ssq(p, r, part, p.off_ssq);
@@ -989,7 +1019,7 @@ __device__ __noinline__ void phase_qkv(KParams& pk, int l_layer, int wait_idx) {
     int mq = sb.mat(L.wq, p.nq * p.hd, p.H, 0);
     int mk = sb.mat(L.wk, p.nkv * p.hd, p.H, p.nq * p.hd);
     int mv = sb.mat(L.wv, p.nkv * p.hd, p.H, (p.nq + p.nkv) * p.hd);
-    sb.begin(p.off_u, p.H, GK_SINGLE);
+    sb.begin(u_at(p, 2 * l_layer), p.H, GK_SINGLE);
     sb.singles_of(mq, p.nq * p.hd);
     sb.singles_of(mk, p.nkv * p.hd);
     sb.singles_of(mv, p.nkv * p.hd);
@@ -1406,10 +1436,10 @@ __device__ __forceinline__ void attn_phase(KParams& pk, int l_layer, int layer, 
         }
         const float il = 1.0f / den;
         const int col = (g * gs + h) * HD + d4;
-        put_hilo(wr, p.off_ou, p.nq * HD, b, col + 0, o0 * il);
-        put_hilo(wr, p.off_ou, p.nq * HD, b, col + 1, o1 * il);
-        put_hilo(wr, p.off_ou, p.nq * HD, b, col + 2, o2 * il);
-        put_hilo(wr, p.off_ou, p.nq * HD, b, col + 3, o3 * il);
+        put_hilo(wr, ou_at(p, l_layer), p.nq * HD, b, col + 0, o0 * il);
+        put_hilo(wr, ou_at(p, l_layer), p.nq * HD, b, col + 1, o1 * il);
+        put_hilo(wr, ou_at(p, l_layer), p.nq * HD, b, col + 2, o2 * il);
+        put_hilo(wr, ou_at(p, l_layer), p.nq * HD, b, col + 3, o3 * il);
       }
     }
     __syncthreads();
@@ -1449,7 +1479,7 @@ __device__ __noinline__ void phase_kda_proj(KParams& pk, int l_layer, int wait_i
     int m2 = sb.mat(L.kda_wv, nh * dv, p.H, 2 * nh * dk);
     int m3 = sb.mat(L.kda_wa, nh, p.H, 2 * nh * dk + nh * dv);
     int m4 = sb.mat(L.kda_wb, nh, p.H, 2 * nh * dk + nh * dv + nh);
-    sb.begin(p.off_u, p.H, GK_SINGLE);
+    sb.begin(u_at(p, 2 * l_layer), p.H, GK_SINGLE);
     sb.singles_of(m0, nh * dk);
     sb.singles_of(m1, nh * dk);
     sb.singles_of(m2, nh * dv);
@@ -1547,7 +1577,7 @@ __device__ __noinline__ void phase_kda_rec(KParams& pk, int l_layer) {
       float o = 0.f;
 #pragma unroll
       for (int g = 0; g < 8; ++g) o += sm.red2[g][threadIdx.x];
-      put_hilo(wr, p.off_ou, nh * dv, b, h * dv + 32 * js + threadIdx.x, o);
+      put_hilo(wr, ou_at(p, l_layer), nh * dv, b, h * dv + 32 * js + threadIdx.x, o);
     }
     __syncthreads();
   }
@@ -1635,7 +1665,7 @@ __device__ __noinline__ void phase_kda_rec_verify(KParams& pk, int l_layer) {
         float o = 0.f;
 #pragma unroll
         for (int g = 0; g < 8; ++g) o += sm.red2[g][threadIdx.x];
-        put_hilo(wr, p.off_ou, nh * dv, j, h * dv + 32 * js + threadIdx.x, o);
+        put_hilo(wr, ou_at(p, l_layer), nh * dv, j, h * dv + 32 * js + threadIdx.x, o);
       }
       __syncthreads();
     }
@@ -1723,7 +1753,7 @@ __device__ __noinline__ void phase_mla_a(KParams& pk, int l_layer, int wait_idx)
     sb.start(PL_MLA_A);
     int ma = sb.mat(L.mla_wqa, QL, p.H, 0);
     int mk = sb.mat(L.mla_wkva, KVR, p.H, 1);
-    sb.begin(p.off_u, p.H, GK_SINGLE);
+    sb.begin(u_at(p, 2 * l_layer), p.H, GK_SINGLE);
     sb.singles_of(ma, QL);
     sb.singles_of(mk, KVR);
   }
@@ -1738,7 +1768,7 @@ __device__ __noinline__ void phase_mla_a(KParams& pk, int l_layer, int wait_idx)
     if (!slot_row(sr >> 4, sr & 15, m, row)) continue;
     float v = GSM.out[sr][t];
     if (GSM.mats[m].tag == 0) {
-      put_hilo(r, p.off_uq, QL, t, row, bf16_f32(L.mla_qnorm[row]) * v);
+      put_hilo(r, uq_at(p, l_layer), QL, t, row, bf16_f32(L.mla_qnorm[row]) * v);
       part[threadIdx.x * MAXB + t] += v * v;
     } else {
       st_f32(r, p.off_ckv + (uint32_t)(t * KVR + row) * 4u, v);
@@ -1792,7 +1822,7 @@ __device__ __noinline__ void phase_mla_b(KParams& pk, int l_layer, int wait_idx)
   if (threadIdx.x < 64) {
     sb.start(PL_MLA_B);
     int m = sb.mat(L.mla_wqb, nh * QW, p.q_lora, 0);
-    sb.begin(p.off_uq, p.q_lora, GK_SINGLE);
+    sb.begin(uq_at(p, l_layer), p.q_lora, GK_SINGLE);
     sb.singles_of(m, nh * QW);
   }
   builder_done(p, sb, -1);
@@ -2179,7 +2209,7 @@ __device__ __forceinline__ void phase_mla_out(KParams& pk, int l_layer) {
         ot[t] = v;
       }
       if (part == 0) {
-        for (int t = 0; t < B; ++t) put_hilo(r, p.off_ou, nh * vd, t, h * vd + row, ot[t]);
+        for (int t = 0; t < B; ++t) put_hilo(r, ou_at(p, l_layer), nh * vd, t, h * vd + row, ot[t]);
       }
     }
     (void)lane;
@@ -2227,33 +2257,37 @@ __device__ __noinline__ void phase_residual(KParams& pk, int l_layer, int mode, 
     sb.start(mode == RES_OPROJ ? PL_OPROJ : mode == RES_DENSE_DOWN ? PL_DDOWN : mode == RES_MLA_O ? PL_MLA_O : mode == RES_KDA_O ? PL_KDA_O : -1);
     if (mode == RES_OPROJ) {
       int m = sb.mat(L.wo, H, p.nq * p.hd, 0);
-      sb.begin(p.off_ou, p.nq * p.hd, GK_SINGLE);
+      sb.begin(ou_at(p, l_layer), p.nq * p.hd, GK_SINGLE);
       sb.singles_of(m, H);
     } else if (mode == RES_MLA_O) {
       int m = sb.mat(L.mla_wo, H, p.mla_h * p.vdim, 0);
-      sb.begin(p.off_ou, p.mla_h * p.vdim, GK_SINGLE);
+      sb.begin(ou_at(p, l_layer), p.mla_h * p.vdim, GK_SINGLE);
       sb.singles_of(m, H);
     } else if (mode == RES_KDA_O) {
       int m = sb.mat(L.kda_wo, H, p.kda_h * p.kda_dv, 0);
-      sb.begin(p.off_ou, p.kda_h * p.kda_dv, GK_SINGLE);
+      sb.begin(ou_at(p, l_layer), p.kda_h * p.kda_dv, GK_SINGLE);
       sb.singles_of(m, H);
     } else if (mode == RES_DENSE_DOWN) {
       int m = sb.mat(L.w_down, H, p.ffn, 0);
-      sb.begin(p.off_h, p.ffn, GK_SINGLE);
+      sb.begin(h_at(p, l_layer), p.ffn, GK_SINGLE);
       sb.singles_of(m, H);
     } else {
       if (p.n_shared > 0) {
         int m = sb.mat(L.sh_down, H, p.shared_ffn, 0);
-        sb.begin(p.off_hs, p.shared_ffn, GK_SINGLE);
+        sb.begin(hs_at(p, l_layer), p.shared_ffn, GK_SINGLE);
         sb.singles_of(m, H);
       }
       const int nu = __builtin_amdgcn_readfirstlane(RSM.nu);
       const int m0 = sb.expert_mats<1>(RSM.ex, nu, 2, H, p.expert_ffn, false);
-      sb.expert_singles(m0, nu, H, p.off_hr, p.hr_stride, p.expert_ffn);
+      sb.expert_singles(m0, nu, H, hr_at(p, l_layer), p.hr_stride, p.expert_ffn);
     }
   }
   builder_done(p, sb, nrow);
   const int r0 = own.r0;
+  // the next norm's input: this layer's FFN input after an attention block,
+  // the next layer's attention input (or the final norm's) after the FFN
+  const bool attn_block = mode == RES_OPROJ || mode == RES_MLA_O || mode == RES_KDA_O;
+  const uint32_t u_next = u_at(p, 2 * l_layer + (attn_block ? 1 : 2));
   gemv_phase(p, wait_idx, 0, 0u, EPI_RESIDUAL, r0, nrow, g_next);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   static_assert(sizeof(GemvSmem::red) >= sizeof(float) * (NT + NW) * MAXB, "partial sums reuse the reduction scratch");
@@ -2263,7 +2297,7 @@ __device__ __noinline__ void phase_residual(KParams& pk, int l_layer, int mode, 
     int t = e % B, lr = e / B;
     float x = GSM.out[lr][t];
     p.x[t * H + r0 + lr] = x;
-    put_hilo(r, p.off_u, H, t, r0 + lr, GSM.gain[lr] * x);
+    put_hilo(r, u_next, H, t, r0 + lr, GSM.gain[lr] * x);
     part[threadIdx.x * MAXB + t] += x * x;
   }
   store_ssq(p, r, part, p.off_ssq);
@@ -2279,7 +2313,7 @@ __device__ __noinline__ void phase_gateup(KParams& pk, int l_layer, int wait_idx
     sb.start(PL_GATEUP);
     int mg = sb.mat(L.w_gate, F, p.H, 0);
     int mu = sb.mat(L.w_up, F, p.H, 0);
-    sb.begin(p.off_u, p.H, GK_PAIR);
+    sb.begin(u_at(p, 2 * l_layer + 1), p.H, GK_PAIR);
     sb.pairs_of(mg, mu, F);
   }
   builder_done(p, sb, -1);
@@ -2290,7 +2324,7 @@ __device__ __noinline__ void phase_gateup(KParams& pk, int l_layer, int wait_idx
     if ((sr >> 4) & 1) continue;  // up slots carry no output
     int m, row;
     if (!slot_row(sr >> 4, sr & 15, m, row)) continue;
-    put_hilo(r, p.off_h, F, t, row, GSM.out[sr][t]);
+    put_hilo(r, h_at(p, l_layer), F, t, row, GSM.out[sr][t]);
   }
 }
 
@@ -2321,13 +2355,13 @@ __device__ __noinline__ void phase_moe_a(KParams& pk, int l_layer, int wait_idx)
     if (p.n_shared > 0) {
       int mg = sb.mat(L.sh_gate, p.shared_ffn, p.H, 0);
       int mu = sb.mat(L.sh_up, p.shared_ffn, p.H, 0);
-      sb.begin(p.off_u, p.H, GK_PAIR);
+      sb.begin(u_at(p, 2 * l_layer + 1), p.H, GK_PAIR);
       const int nq = (p.shared_ffn + 3) >> 2;
       if (!apart) sb.pairs_of(mg, mu, p.shared_ffn);
       else if (w < G - rq) sb.pairs_in(mg, mu, rows_of(nq, w, G - rq));
     }
     int mr = sb.mat(L.router, p.n_experts, p.H, -1);
-    sb.begin(p.off_u, p.H, GK_SINGLE);
+    sb.begin(u_at(p, 2 * l_layer + 1), p.H, GK_SINGLE);
     if (!apart) {
       sb.singles_of(mr, p.n_experts);
     } else if (w >= G - rq) {
@@ -2347,7 +2381,7 @@ __device__ __noinline__ void phase_moe_a(KParams& pk, int l_layer, int wait_idx)
     if (pair && (si & 1)) continue;  // up slots carry no output
     int m, row;
     if (!slot_row(si, sr & 15, m, row)) continue;
-    if (pair) put_hilo(r, p.off_hs, p.shared_ffn, t, row, GSM.out[sr][t]);
+    if (pair) put_hilo(r, hs_at(p, l_layer), p.shared_ffn, t, row, GSM.out[sr][t]);
     else st_f32(r, p.off_rl + (uint32_t)(t * p.n_experts + row) * 4u, GSM.out[sr][t]);
   }
 }
@@ -2423,7 +2457,7 @@ __device__ __noinline__ void phase_moe_b(KParams& pk, int l_layer, int wait_idx)
   SlotBuilder sb;
   if (threadIdx.x < 64) {
     sb.start();
-    sb.begin(p.off_u, p.H, GK_PAIR);
+    sb.begin(u_at(p, 2 * l_layer + 1), p.H, GK_PAIR);
     const int nu = __builtin_amdgcn_readfirstlane(RSM.nu);
     const int m0 = sb.expert_mats<2>(RSM.ex, nu, 0, p.expert_ffn, p.H, true);
     sb.expert_pairs(m0, nu, p.expert_ffn);
@@ -2437,7 +2471,7 @@ __device__ __noinline__ void phase_moe_b(KParams& pk, int l_layer, int wait_idx)
     int m, row;
     if (!slot_row(sr >> 4, sr & 15, m, row)) continue;
     int j = GSM.mats[m].tag;
-    put_hilo(r, p.off_hr + (uint32_t)j * p.hr_stride, p.expert_ffn, t, row, GSM.out[sr][t] * RSM.wt[t][j]);
+    put_hilo(r, hr_at(p, l_layer) + (uint32_t)j * p.hr_stride, p.expert_ffn, t, row, GSM.out[sr][t] * RSM.wt[t][j]);
   }
 }
 
@@ -2449,7 +2483,7 @@ __device__ __noinline__ void phase_lmhead(KParams& pk, int wait_idx) {
   if (threadIdx.x < 64) {
     sb.start(PL_LMHEAD);
     int m = sb.mat(p.lm_head, p.V, p.H, 0);
-    sb.begin(p.off_u, p.H, GK_SINGLE);
+    sb.begin(u_at(p, p.n_layers * 2), p.H, GK_SINGLE);
     sb.singles_of(m, p.V);
   }
   builder_done(p, sb, -1);

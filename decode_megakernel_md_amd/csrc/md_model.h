@@ -63,18 +63,24 @@ struct Params {
   uint8_t* ws;
   uint32_t ws_bytes;
   float* x;           // residual fp32[MAXB][H] (rows owned by their workgroup)
-  uint32_t off_u;     // hi/lo bf16[2][MAXB][H]  next norm input (gain folded, not yet scaled)
+  // The GEMV inputs (hi/lo activations) have one buffer per use within a
+  // step, so that no address is read before it is written in the same launch
+  // (their loads may then hit a copy in the local L2, see md_device.h):
+  // index 2l = attention input of layer l, 2l+1 = its FFN input, 2L = the
+  // final norm's input; the others one per layer.
+  uint32_t off_u;     // hi/lo bf16[2][MAXB][H] x (2L+1), u_stride apart: norm input (gain folded, not yet scaled)
+  uint32_t u_stride, ou_stride, h_stride, hs_stride, hr_lstride, uq_stride;  // bytes per use
   uint32_t off_ssq;   // fp32[G][MAXB] partial sums of squares of x
   uint32_t off_qkv;   // fp32[MAXB][nq+2nkv][hd]
   uint32_t off_attn;  // attention partial outputs fp32[MAXB][nq][C][hd]
   uint32_t off_attn_ml; // attention partial (max, sum) fp32[MAXB][nq][C][2]
-  uint32_t off_ou;    // hi/lo bf16[2][MAXB][nq*hd]
-  uint32_t off_h;     // hi/lo bf16[2][MAXB][F]           dense FFN hidden
+  uint32_t off_ou;    // hi/lo bf16[2][MAXB][nq*hd] per layer
+  uint32_t off_h;     // hi/lo bf16[2][MAXB][F]           dense FFN hidden, per layer
   uint32_t off_rl;    // fp32[MAXB][n_experts]             router logits
-  uint32_t off_hs;    // hi/lo bf16[2][MAXB][shared_ffn]   shared expert hidden
-  uint32_t off_hr;    // hi/lo bf16[nu][2][MAXB][expert_ffn] routed hidden (x routing weight), U order
+  uint32_t off_hs;    // hi/lo bf16[2][MAXB][shared_ffn]   shared expert hidden, per layer
+  uint32_t off_hr;    // hi/lo bf16[nu][2][MAXB][expert_ffn] routed hidden (x routing weight), U order, per layer
   uint32_t hr_stride; // bytes per routed expert slot
-  uint32_t off_uq;    // hi/lo bf16[2][MAXB][q_lora]        g_q * c_q0 (MLA)
+  uint32_t off_uq;    // hi/lo bf16[2][MAXB][q_lora]        g_q * c_q0 (MLA), per layer
   uint32_t off_ssq2;  // fp32[G][MAXB]                      partial sums of squares of c_q0
   uint32_t off_ckv;   // fp32[MAXB][576]                    raw latent + key rope part
   uint32_t off_qm;    // fp32[MAXB][nh][nope + 64]          q (MLA)

@@ -167,6 +167,7 @@ struct WsLayout {
   size_t layers, experts, x, u, ssq, qkv, attn, attn_ml, ou, h, rl, hs, hr, hr_stride, uq, ssq2, ckv, qm, qabs, mz, mml,
       kda, ring, cand, zero, rope, sync, err, total;
   size_t u_stride, ou_stride, h_stride, hs_stride, hr_lstride, uq_stride;  // one GEMV input buffer per use
+  size_t ssq_stride, ssq2_stride;
   int rope_d;
   int n_sync, sync_attn_base;
 };
@@ -208,7 +209,8 @@ WsLayout ws_layout(const md_config* c) {
   const size_t L = (size_t)c->n_layers;
   w.u_stride = align256(2 * 2 * MAXB_ * H);
   w.u = take(w.u_stride * (2 * L + 1));
-  w.ssq = take(4 * (size_t)GMAX * MAXB_);
+  w.ssq_stride = align256(4 * (size_t)GMAX * MAXB_);
+  w.ssq = take(w.ssq_stride * (2 * L + 1));
   w.qkv = take(4 * MAXB_ * (size_t)nqkv);
   w.attn = take(4 * (size_t)MAXB_ * (c->n_q_heads > 0 ? c->n_q_heads : 1) * CMAX * (size_t)c->head_dim);
   w.attn_ml = take(8 * (size_t)MAXB_ * (c->n_q_heads > 0 ? c->n_q_heads : 1) * CMAX);
@@ -225,7 +227,8 @@ WsLayout ws_layout(const md_config* c) {
   w.hr = take(w.hr_lstride * L);
   w.uq_stride = align256(2 * 2 * MAXB_ * (size_t)(hyb ? c->q_lora : 1));
   w.uq = take(w.uq_stride * L);
-  w.ssq2 = take(4 * (size_t)GMAX * MAXB_);
+  w.ssq2_stride = align256(4 * (size_t)GMAX * MAXB_);
+  w.ssq2 = take(w.ssq2_stride * L);
   w.ckv = take(4 * MAXB_ * 576);
   w.qm = take(4 * MAXB_ * (size_t)mh * (hyb ? c->nope_dim + 64 : 1));
   w.qabs = take(4 * MAXB_ * (size_t)mh * 576);
@@ -463,6 +466,7 @@ static md_status fill_params(md_model* m, const int32_t* tokens, const int32_t* 
   p.x = (float*)(m->ws + w.x);
   p.u_stride = (uint32_t)w.u_stride; p.ou_stride = (uint32_t)w.ou_stride; p.h_stride = (uint32_t)w.h_stride;
   p.hs_stride = (uint32_t)w.hs_stride; p.hr_lstride = (uint32_t)w.hr_lstride; p.uq_stride = (uint32_t)w.uq_stride;
+  p.ssq_stride = (uint32_t)w.ssq_stride; p.ssq2_stride = (uint32_t)w.ssq2_stride;
   p.off_u = (uint32_t)w.u; p.off_ssq = (uint32_t)w.ssq; p.off_qkv = (uint32_t)w.qkv; p.off_attn = (uint32_t)w.attn; p.off_attn_ml = (uint32_t)w.attn_ml;
   p.off_ou = (uint32_t)w.ou; p.off_h = (uint32_t)w.h;
   p.mla_h = c->mla_heads; p.q_lora = c->q_lora; p.nope = c->nope_dim; p.vdim = c->v_dim;

@@ -60,6 +60,9 @@ __device__ __forceinline__ uint32_t h_at(KParams& pk, int l) { PARAMS; return p.
 __device__ __forceinline__ uint32_t hs_at(KParams& pk, int l) { PARAMS; return p.off_hs + (uint32_t)l * p.hs_stride; }
 __device__ __forceinline__ uint32_t hr_at(KParams& pk, int l) { PARAMS; return p.off_hr + (uint32_t)l * p.hr_lstride; }
 __device__ __forceinline__ uint32_t uq_at(KParams& pk, int l) { PARAMS; return p.off_uq + (uint32_t)l * p.uq_stride; }
+// the partial sums of squares that scale u(i) (indexed as u) and uq(l)
+__device__ __forceinline__ uint32_t ssq_at(KParams& pk, int i) { PARAMS; return p.off_ssq + (uint32_t)i * p.ssq_stride; }
+__device__ __forceinline__ uint32_t ssq2_at(KParams& pk, int l) { PARAMS; return p.off_ssq2 + (uint32_t)l * p.ssq2_stride; }
 
 // ===================================================================== sync
 // One sync point = 8 class counters (one per workgroup class blockIdx % 8,
@@ -774,10 +777,10 @@ __device__ __forceinline__ void gemv_run(KParams& pk, GemvStream& s, int inv_n, 
     const rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
     const int g0 = threadIdx.x, g1 = threadIdx.x + NT;
     const int G = gridDim.x;
-    ia0 = ld_x4<CP_SC1>(r, g0 < G ? inv_off + (uint32_t)(g0 * MAXB) * 4u : OOB);
-    ib0 = ld_x4<CP_SC1>(r, g0 < G ? inv_off + (uint32_t)(g0 * MAXB + 4) * 4u : OOB);
-    ia1 = ld_x4<CP_SC1>(r, g1 < G ? inv_off + (uint32_t)(g1 * MAXB) * 4u : OOB);
-    ib1 = ld_x4<CP_SC1>(r, g1 < G ? inv_off + (uint32_t)(g1 * MAXB + 4) * 4u : OOB);
+    ia0 = ld_x4<CP_SC0>(r, g0 < G ? inv_off + (uint32_t)(g0 * MAXB) * 4u : OOB);
+    ib0 = ld_x4<CP_SC0>(r, g0 < G ? inv_off + (uint32_t)(g0 * MAXB + 4) * 4u : OOB);
+    ia1 = ld_x4<CP_SC0>(r, g1 < G ? inv_off + (uint32_t)(g1 * MAXB) * 4u : OOB);
+    ib1 = ld_x4<CP_SC0>(r, g1 < G ? inv_off + (uint32_t)(g1 * MAXB + 4) * 4u : OOB);
   }
 #pragma unroll
   for (int d = 0; d < GDS; ++d) gs_issue_b(s, d);
@@ -921,7 +924,7 @@ __device__ __noinline__ void phase_embed(KParams& pk) {
     put_hilo(r, u_at(p, 0), p.H, t, i, bf16_f32(g[i]) * x);
     part[threadIdx.x * MAXB + t] += x * x;
   }
-  store_ssq(p, r, part, p.off_ssq);
+  store_ssq(p, r, part, ssq_at(p, 0));
 }
 
 // ------------------------------------------------------------ shared stream
@@ -1025,7 +1028,7 @@ __device__ __noinline__ void phase_qkv(KParams& pk, int l_layer, int wait_idx) {
     sb.singles_of(mv, p.nkv * p.hd);
   }
   builder_done(p, sb, -1);
-  gemv_phase(p, wait_idx, p.H, p.off_ssq, EPI_BY_KIND, 0, 0, nullptr);
+  gemv_phase(p, wait_idx, p.H, ssq_at(p, 2 * l_layer), EPI_BY_KIND, 0, 0, nullptr);
   const int nqkv = (p.nq + 2 * p.nkv) * p.hd;
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
@@ -1487,7 +1490,7 @@ __device__ __noinline__ void phase_kda_proj(KParams& pk, int l_layer, int wait_i
     sb.singles_of(m4, nh);
   }
   builder_done(p, sb, -1);
-  gemv_phase(p, wait_idx, p.H, p.off_ssq, EPI_BY_KIND, 0, 0, nullptr);
+  gemv_phase(p, wait_idx, p.H, ssq_at(p, 2 * l_layer), EPI_BY_KIND, 0, 0, nullptr);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
     int t = e % B, sr = e / B;
@@ -1758,7 +1761,7 @@ __device__ __noinline__ void phase_mla_a(KParams& pk, int l_layer, int wait_idx)
     sb.singles_of(mk, KVR);
   }
   builder_done(p, sb, -1);
-  gemv_phase(p, wait_idx, p.H, p.off_ssq, EPI_BY_KIND, 0, 0, nullptr);
+  gemv_phase(p, wait_idx, p.H, ssq_at(p, 2 * l_layer), EPI_BY_KIND, 0, 0, nullptr);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   float* part = (float*)GSM.red;  // [NT][MAXB]
   for (int t = 0; t < MAXB; ++t) part[threadIdx.x * MAXB + t] = 0.f;
@@ -1774,7 +1777,7 @@ __device__ __noinline__ void phase_mla_a(KParams& pk, int l_layer, int wait_idx)
       st_f32(r, p.off_ckv + (uint32_t)(t * KVR + row) * 4u, v);
     }
   }
-  store_ssq(p, r, part, p.off_ssq2);
+  store_ssq(p, r, part, ssq2_at(p, l_layer));
 }
 
 // The new latent cache row of sequence b: RMSNorm(c) * g_kv and the rotated
@@ -1826,7 +1829,7 @@ __device__ __noinline__ void phase_mla_b(KParams& pk, int l_layer, int wait_idx)
     sb.singles_of(m, nh * QW);
   }
   builder_done(p, sb, -1);
-  gemv_phase(p, wait_idx, p.q_lora, p.off_ssq2, EPI_BY_KIND, 0, 0, nullptr);
+  gemv_phase(p, wait_idx, p.q_lora, ssq2_at(p, l_layer), EPI_BY_KIND, 0, 0, nullptr);
   if (cb < B) mla_cache_row(p, l_layer, cb);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
@@ -2287,7 +2290,8 @@ __device__ __noinline__ void phase_residual(KParams& pk, int l_layer, int mode, 
   // the next norm's input: this layer's FFN input after an attention block,
   // the next layer's attention input (or the final norm's) after the FFN
   const bool attn_block = mode == RES_OPROJ || mode == RES_MLA_O || mode == RES_KDA_O;
-  const uint32_t u_next = u_at(p, 2 * l_layer + (attn_block ? 1 : 2));
+  const int nxt = 2 * l_layer + (attn_block ? 1 : 2);
+  const uint32_t u_next = u_at(p, nxt);
   gemv_phase(p, wait_idx, 0, 0u, EPI_RESIDUAL, r0, nrow, g_next);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   static_assert(sizeof(GemvSmem::red) >= sizeof(float) * (NT + NW) * MAXB, "partial sums reuse the reduction scratch");
@@ -2300,7 +2304,7 @@ __device__ __noinline__ void phase_residual(KParams& pk, int l_layer, int mode, 
     put_hilo(r, u_next, H, t, r0 + lr, GSM.gain[lr] * x);
     part[threadIdx.x * MAXB + t] += x * x;
   }
-  store_ssq(p, r, part, p.off_ssq);
+  store_ssq(p, r, part, ssq_at(p, nxt));
 }
 
 // --- dense SwiGLU gate/up: h = silu(inv*Wg U) * (inv*Wu U) -> hi/lo
@@ -2317,7 +2321,7 @@ __device__ __noinline__ void phase_gateup(KParams& pk, int l_layer, int wait_idx
     sb.pairs_of(mg, mu, F);
   }
   builder_done(p, sb, -1);
-  gemv_phase(p, wait_idx, p.H, p.off_ssq, EPI_BY_KIND, 0, 0, nullptr);
+  gemv_phase(p, wait_idx, p.H, ssq_at(p, 2 * l_layer + 1), EPI_BY_KIND, 0, 0, nullptr);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
     int t = e % B, sr = e / B;
@@ -2372,7 +2376,7 @@ __device__ __noinline__ void phase_moe_a(KParams& pk, int l_layer, int wait_idx)
     }
   }
   builder_done(p, sb, -1);
-  gemv_phase(p, wait_idx, p.H, p.off_ssq, EPI_BY_KIND, 0, 0, nullptr);
+  gemv_phase(p, wait_idx, p.H, ssq_at(p, 2 * l_layer + 1), EPI_BY_KIND, 0, 0, nullptr);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
     int t = e % B, sr = e / B;
@@ -2463,7 +2467,7 @@ __device__ __noinline__ void phase_moe_b(KParams& pk, int l_layer, int wait_idx)
     sb.expert_pairs(m0, nu, p.expert_ffn);
   }
   builder_done(p, sb, -1);
-  gemv_phase(p, wait_idx, p.H, p.off_ssq, EPI_BY_KIND, 0, 0, nullptr);
+  gemv_phase(p, wait_idx, p.H, ssq_at(p, 2 * l_layer + 1), EPI_BY_KIND, 0, 0, nullptr);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
     int t = e % B, sr = e / B;
@@ -2487,7 +2491,7 @@ __device__ __noinline__ void phase_lmhead(KParams& pk, int wait_idx) {
     sb.singles_of(m, p.V);
   }
   builder_done(p, sb, -1);
-  gemv_phase(p, wait_idx, p.H, p.off_ssq, EPI_BY_KIND, 0, 0, nullptr);
+  gemv_phase(p, wait_idx, p.H, ssq_at(p, 2 * p.n_layers), EPI_BY_KIND, 0, 0, nullptr);
   static_assert(sizeof(GemvSmem::in) >= 2 * sizeof(float) * NT * MAXB, "argmax scratch reuses the input staging");
   float* bv = &GSM.in[0][0];             // [NT][MAXB] best value (the input staging is unused here)
   int* bi = (int*)(bv + NT * MAXB);      // [NT][MAXB] best index

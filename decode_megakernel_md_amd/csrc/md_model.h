@@ -70,7 +70,8 @@ struct Params {
   // final norm's input; the others one per layer.
   uint32_t off_u;     // hi/lo bf16[2][MAXB][H] x (2L+1), u_stride apart: norm input (gain folded, not yet scaled)
   uint32_t u_stride, ou_stride, h_stride, hs_stride, hr_lstride, uq_stride;  // bytes per use
-  uint32_t off_ssq;   // fp32[G][MAXB] partial sums of squares of x
+  uint32_t ssq_stride, ssq2_stride;  // the partial sums of squares that scale them, one buffer per use too
+  uint32_t off_ssq;   // fp32[G][MAXB] x (2L+1), ssq_stride apart: partial sums of squares of x (indexed as u)
   uint32_t off_qkv;   // fp32[MAXB][nq+2nkv][hd]
   uint32_t off_attn;  // attention partial outputs fp32[MAXB][nq][C][hd]
   uint32_t off_attn_ml; // attention partial (max, sum) fp32[MAXB][nq][C][2]
@@ -81,7 +82,7 @@ struct Params {
   uint32_t off_hr;    // hi/lo bf16[nu][2][MAXB][expert_ffn] routed hidden (x routing weight), U order, per layer
   uint32_t hr_stride; // bytes per routed expert slot
   uint32_t off_uq;    // hi/lo bf16[2][MAXB][q_lora]        g_q * c_q0 (MLA), per layer
-  uint32_t off_ssq2;  // fp32[G][MAXB]                      partial sums of squares of c_q0
+  uint32_t off_ssq2;  // fp32[G][MAXB]                      partial sums of squares of c_q0, per layer
   uint32_t off_ckv;   // fp32[MAXB][576]                    raw latent + key rope part
   uint32_t off_qm;    // fp32[MAXB][nh][nope + 64]          q (MLA)
   uint32_t off_qabs;  // fp32[MAXB][nh][576]                absorbed, rotated, scaled q

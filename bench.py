@@ -108,9 +108,11 @@ def time_steps(m, B, steps, warmup, multilaunch=False):
     return per, total, pos[:steps].cpu().numpy(), (ids[:steps].cpu().numpy() if ids is not None else None)
 
 
-def cpu_baseline(w, layers=8, B=1):
+def cpu_baseline(w, layers=8, B=1, min_seconds=10.0, max_rounds=16):
     """Time the oracle on layers 0..layers-1 plus the final norm and LM head
-    for one token at the workload's context; extrapolate to all layers."""
+    for one token at the workload's context, repeated until at least
+    min_seconds of CPU work are timed (a bounded sample), and extrapolate the
+    mean per-layer time to all layers."""
     import synth
     from oracle import lib as olib, ptr
     from oracle import step as ostep
@@ -123,24 +125,31 @@ def cpu_baseline(w, layers=8, B=1):
     kv = [synth.kv_layer_host(wsub, l) for l in range(layers)]
     toks = synth.tokens(w, B)
     pos = np.array([w.context] * B)
-    t0 = time.perf_counter()
-    xs = np.empty((B, w.hidden))
-    for b in range(B):
-        olib().orc_embed(w.hidden, ptr(W("embed")), int(toks[b]), ptr(xs[b]))
-    for l in range(layers):
-        ostep._layer(wsub, W, l, xs, pos, kv[l], B, None, None)
-    t1 = time.perf_counter()
-    logits = np.empty((B, w.vocab), dtype=np.float32)
-    for b in range(B):
-        olib().orc_head(w.hidden, w.vocab, w.rms_eps, ptr(W("final_norm")), ptr(W("lm_head")), ptr(xs[b]),
-                        ptr(logits[b]))
-    t2 = time.perf_counter()
-    t_step = (t1 - t0) / layers * w.n_layers + (t2 - t1)
+    t_layers = t_head = 0.0
+    rounds = 0
+    while rounds < max_rounds and (t_layers + t_head) < min_seconds:
+        t0 = time.perf_counter()
+        xs = np.empty((B, w.hidden))
+        for b in range(B):
+            olib().orc_embed(w.hidden, ptr(W("embed")), int(toks[b]), ptr(xs[b]))
+        for l in range(layers):  # rewrites the same cache rows every round
+            ostep._layer(wsub, W, l, xs, pos, kv[l], B, None, None)
+        t1 = time.perf_counter()
+        logits = np.empty((B, w.vocab), dtype=np.float32)
+        for b in range(B):
+            olib().orc_head(w.hidden, w.vocab, w.rms_eps, ptr(W("final_norm")), ptr(W("lm_head")), ptr(xs[b]),
+                            ptr(logits[b]))
+        t2 = time.perf_counter()
+        t_layers += t1 - t0
+        t_head += t2 - t1
+        rounds += 1
+    t_step = t_layers / rounds / layers * w.n_layers + t_head / rounds
     cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     return {"value": B / t_step, "unit": "tok/s", "cores": cores, "kind": "oracle",
-            "sample": f"fp64 oracle, batch {B}, context {w.context}: layers 0-{layers - 1} ({t1 - t0:.2f} s) plus "
-                      f"final norm and LM head ({t2 - t1:.2f} s), extrapolated to {w.n_layers} layers "
-                      f"({t_step:.2f} s per step)"}
+            "sample": f"fp64 oracle, batch {B}, context {w.context}: layers 0-{layers - 1} plus final norm and LM head, "
+                      f"{rounds} rounds ({t_layers + t_head:.1f} s of CPU work timed), mean per layer "
+                      f"{t_layers / rounds / layers * 1e3:.1f} ms and head {t_head / rounds * 1e3:.1f} ms, "
+                      f"extrapolated to {w.n_layers} layers ({t_step:.2f} s per step)"}
 
 
 def decode_bench(w, batches, steps, warmup, multilaunch=True):

@@ -138,3 +138,20 @@ def test_pack_argument_checks():
     assert L.md_pack_weight(None, None, 16, 32, None) == _lib.MD_EINVAL
     assert L.md_pack_weight(P(16), P(32), 16, 33, None) == _lib.MD_EINVAL
     assert L.md_pack_weight(P(8), P(32), 16, 32, None) == _lib.MD_EINVAL
+
+
+def test_workspace_sizes():
+    """The workspace holds one activation buffer per use within a step (two
+    norm inputs per layer plus the final one, and per layer the attention
+    output and FFN hidden): it grows with the layer count by at least those
+    buffers, and the benchmark models stay within the 32-bit offsets the
+    kernels use."""
+    L = _lib.lib()
+    for name in ("dense_27b", "hybrid_moe", "verify_hybrid", "small_moe"):
+        c = _cfg(name)
+        assert L.md_workspace_bytes(ctypes.byref(c)) < 0xFFFFFF00, name
+    w = WL.get("mini_dense")
+    c1, c2 = _cfg("mini_dense", n_layers=3), _cfg("mini_dense", n_layers=6)
+    grow = L.md_workspace_bytes(ctypes.byref(c2)) - L.md_workspace_bytes(ctypes.byref(c1))
+    per_layer = 2 * (2 * 2 * 8 * w.hidden) + 2 * 2 * 8 * w.n_q_heads * w.head_dim + 2 * 2 * 8 * w.ffn_dim
+    assert grow >= 3 * per_layer

@@ -528,11 +528,19 @@ struct SlotBuilder {
     RowSplit q = quarters(N);
     const int npq = q.r1 - q.r0, E = nu * npq, P = (E + 3) >> 2;
     if (ns + 2 * P > MAXSLOT) { ovf = true; return; }
+    // When every workgroup owns the same number of quarters, workgroups 2k
+    // and 2k+1 trade places on every other expert: the two halves of a tile's
+    // blocks then alternate between them instead of one of them always
+    // reading the first half (measured: with a fixed order, the workgroups
+    // of one parity streamed the routed experts up to 20% slower at batch 8).
+    const int Q = (N + 3) >> 2, G = gridDim.x, wx = blockIdx.x ^ 1;
+    const bool trade = Q % G == 0 && wx < G;
+    const int r0x = trade ? rows_of(Q, wx, G).r0 : q.r0;
     for (int i = __lane_id(); i < 4 * P; i += 64) {
       const int ps = i >> 2, e = i & 3, si = ns + 2 * ps;
       const bool v = i < E;
       const int j = v ? i / npq : 0;
-      const int gq = v ? q.r0 + (i - j * npq) : -1;
+      const int gq = v ? ((j & 1) ? r0x : q.r0) + (i - j * npq) : -1;
       GSM.slots[si].m[e] = (int8_t)(v ? m0 + 2 * j : 0);
       GSM.slots[si].gq[e] = gq;
       GSM.slots[si + 1].m[e] = (int8_t)(v ? m0 + 2 * j + 1 : 0);

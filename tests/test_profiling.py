@@ -42,3 +42,14 @@ def test_traffic_for_rejects_other_sources_and_workloads(tmp_path, monkeypatch):
     assert P.traffic_for("hybrid_moe", 1) is None
     path.write_text(json.dumps(dict(rec, kernel_sha256="0" * 64)))
     assert P.traffic_for("dense_27b", 1) is None
+
+
+def test_dispatch_gaps():
+    """Idle time between back-to-back dispatches; a pause longer than 1 ms
+    starts a new run and is not counted as a gap."""
+    d = [(0, 100_000), (110_000, 200_000), (5_000_000, 5_000_100), (5_000_150, 5_000_300)]
+    r = P.gaps(d)
+    assert r["dispatches"] == 4 and r["runs"] == 2 and r["gaps"] == 2
+    assert abs(r["busy_us"] - 190.25) < 1e-9
+    assert abs(r["idle_us"] - 10.05) < 1e-9
+    assert abs(r["max_gap_us"] - 10.0) < 1e-9

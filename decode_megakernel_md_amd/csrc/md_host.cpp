@@ -164,7 +164,7 @@ md_status validate(const md_config* c) {
 }
 
 struct WsLayout {
-  size_t layers, experts, x, u, ssq, qkv, attn, attn_ml, ou, h, rl, hs, hr, hr_stride, uq, ssq2, ckv, qm, qabs, mz, mml,
+  size_t layers, experts, x, u, ssq, qkv, attn, attn_ml, ou, h, rl, hs, hr, hr_stride, uq, ssq2, ckv, qm, qabs, mz, mml, mzc,
       kda, ring, cand, zero, rope, sync, err, total;
   size_t u_stride, ou_stride, h_stride, hs_stride, hr_lstride, uq_stride;  // one GEMV input buffer per use
   size_t ssq_stride, ssq2_stride;
@@ -246,6 +246,7 @@ WsLayout ws_layout(const md_config* c) {
   w.n_sync = w.sync_attn_base + c->n_layers + 2;
   w.sync = take(4 * 2 * (size_t)w.n_sync * SP_WORDS_);
   w.err = take(256);
+  w.mzc = take(hyb ? 4 * MAXB_ * (size_t)mh * 512 : 256);
   w.total = o;
   return w;
 }
@@ -480,7 +481,7 @@ static md_status fill_params(md_model* m, const int32_t* tokens, const int32_t* 
     p.mla_chunks = cm;
   }
   p.off_uq = (uint32_t)w.uq; p.off_ssq2 = (uint32_t)w.ssq2; p.off_ckv = (uint32_t)w.ckv; p.off_qm = (uint32_t)w.qm;
-  p.off_qabs = (uint32_t)w.qabs; p.off_mz = (uint32_t)w.mz; p.off_mml = (uint32_t)w.mml; p.off_kda = (uint32_t)w.kda;
+  p.off_qabs = (uint32_t)w.qabs; p.off_mz = (uint32_t)w.mz; p.off_mml = (uint32_t)w.mml; p.off_mzc = (uint32_t)w.mzc; p.off_kda = (uint32_t)w.kda;
   p.n_kda = 0;
   for (int l = 0; l < c->n_layers; ++l) p.n_kda += (c->attn_kind == 1 && !is_mla(c, l)) ? 1 : 0;
   p.kda_ring = m->ws + w.ring;

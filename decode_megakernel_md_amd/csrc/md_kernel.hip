@@ -2121,11 +2121,16 @@ __device__ __forceinline__ void phase_mla_attn(KParams& pk, int l_layer) {
 }
 
 // M5: combine the chunks of each head and un-absorb: o_h = W_uv,h z_h.
-// Task (h, 32-row slice of W_uv,h) for all tokens.  The chunk partials are
-// read 32 at a time (the combine is latency-bound: one round trip per
-// round); inlined into the kernel, as the attention phases are, so that
-// those registers are not saved and restored through scratch.
-__device__ __forceinline__ void phase_mla_out(KParams& pk, int l_layer) {
+// The nsl = v_dim/32 tasks of a head first split its 512 latent dims for the
+// combine (each reads a quarter of the chunk partials when nsl = 4, with the
+// chunks shared out over all threads so that one round of loads covers them),
+// publish the combined z to the workspace and count themselves in a per-head
+// word; then task (h, sl) waits for that count and multiplies the whole z by
+// its 32-row slice of W_uv,h, whose loads were issued before the wait.
+// parts: 1 = the combine, 2 = the rows, 3 = both (the multi-launch step runs
+// them as two launches).  Inlined into the kernel, as the attention phases
+// are, so that those registers are not saved and restored through scratch.
+__device__ __forceinline__ void phase_mla_out(KParams& pk, int l_layer, int parts) {
   PARAMS;
   KLayer& L = layer_ref(p, l_layer);
   const int B = p.B, nh = p.mla_h, nope = p.nope, vd = p.vdim, VW = nope + vd, C = p.mla_chunks;
@@ -2134,12 +2139,16 @@ __device__ __forceinline__ void phase_mla_out(KParams& pk, int l_layer) {
   float* z = &GSM.in[0][0];      // [MAXB][512]
   float* cw = &GSM.out[0][0];    // [MAXB][256] combine weights
   float* cl = cw + MAXB * 256;   // [MAXB] 1 / denominator
+  float* cs = cl + MAXB;         // [MAXB][256] chunk sums
+  float* zp = &GSM.red[0][0][0][0][0];  // [NT][4] sums over a share of the chunks
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   rsrc_t wrs = make_rsrc_u(L.mla_wkvb, (uint32_t)((size_t)nh * VW * MLA_KL * 2));
-  const int lane = threadIdx.x & 63;
-  for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
-    const int h = task / nsl, sl = task % nsl;
-    float* cs = cl + MAXB;         // [MAXB][256] chunk sums
+  unsigned* ready = sync_pt(p, p.sync_attn_base + l_layer);  // per head: parts of z published
+  // Part 1: task (h, q) combines dims [d0, d1) of head h's z over the chunks
+  // and publishes them; the nsl tasks of a head split the 512 dims.
+  for (int task = blockIdx.x; (parts & 1) && task < ntask; task += gridDim.x) {
+    const int h = task / nsl, q = task % nsl;
+    const int d0 = 4 * ((q * (MLA_KL / 4)) / nsl), nd4 = ((q + 1) * (MLA_KL / 4)) / nsl - d0 / 4;
     for (int e = threadIdx.x; e < B * C; e += NT) {
       int t = e / C, cc = e % C;
       cw[t * 256 + cc] = ld_f32(r, p.off_mml + (uint32_t)((t * C + cc) * nh + h) * 8u);
@@ -2161,47 +2170,112 @@ __device__ __forceinline__ void phase_mla_out(KParams& pk, int l_layer) {
       if (ln == 0) cl[t] = 1.0f / den;
     }
     __syncthreads();
-    // z[t][d], thread per (token, 4 dims), MZU chunk loads in flight
+    // thread per (share s of the chunks, token, 4 dims), MZU chunk loads in flight
     constexpr int MZU = 32;
-    for (int e = threadIdx.x; e < B * (MLA_KL / 4); e += NT) {
-      int t = e / (MLA_KL / 4), d4 = (e % (MLA_KL / 4)) * 4;
+    const int items = B * nd4;
+    const int S = items < NT ? NT / items : 1;
+    const int per = (C + S - 1) / S;
+    for (int e = threadIdx.x; e < items * S; e += NT) {
+      const int sh = e / items, it = e % items;
+      const int t = it / nd4, d4 = d0 + (it % nd4) * 4;
+      const int ca = sh * per, cb = ca + per < C ? ca + per : C;
       float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-      for (int c0 = 0; c0 < C; c0 += MZU) {
+      for (int c0 = ca; c0 < cb; c0 += MZU) {
         i32x4 v[MZU];
 #pragma unroll
         for (int u = 0; u < MZU; ++u)
-          v[u] = ld_x4<CP_SC1>(r, c0 + u < C ? p.off_mz + ((uint32_t)((t * C + c0 + u) * nh + h) * MLA_KL + d4) * 4u : OOB);
+          v[u] = ld_x4<CP_SC1>(r, c0 + u < cb ? p.off_mz + ((uint32_t)((t * C + c0 + u) * nh + h) * MLA_KL + d4) * 4u : OOB);
 #pragma unroll
         for (int u = 0; u < MZU; ++u) {
-          float f = c0 + u < C ? cw[t * 256 + c0 + u] : 0.f;
+          float f = c0 + u < cb ? cw[t * 256 + c0 + u] : 0.f;
           o0 += f * __int_as_float(v[u][0]);
           o1 += f * __int_as_float(v[u][1]);
           o2 += f * __int_as_float(v[u][2]);
           o3 += f * __int_as_float(v[u][3]);
         }
       }
-      float il = cl[t];
-      z[t * MLA_KL + d4 + 0] = o0 * il;
-      z[t * MLA_KL + d4 + 1] = o1 * il;
-      z[t * MLA_KL + d4 + 2] = o2 * il;
-      z[t * MLA_KL + d4 + 3] = o3 * il;
+      if (S == 1) {
+        const float il = cl[t];
+        const uint32_t at = p.off_mzc + ((uint32_t)(t * nh + h) * MLA_KL + d4) * 4u;
+        st_f32(r, at, o0 * il);
+        st_f32(r, at + 4u, o1 * il);
+        st_f32(r, at + 8u, o2 * il);
+        st_f32(r, at + 12u, o3 * il);
+      } else {
+        zp[e * 4 + 0] = o0;
+        zp[e * 4 + 1] = o1;
+        zp[e * 4 + 2] = o2;
+        zp[e * 4 + 3] = o3;
+      }
+    }
+    if (S > 1) {  // add the shares (e < items * S <= NT above)
+      __syncthreads();
+      for (int it = threadIdx.x; it < items; it += NT) {
+        const int t = it / nd4, d4 = d0 + (it % nd4) * 4;
+        float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+        for (int sh = 0; sh < S; ++sh) {
+          o0 += zp[(sh * items + it) * 4 + 0];
+          o1 += zp[(sh * items + it) * 4 + 1];
+          o2 += zp[(sh * items + it) * 4 + 2];
+          o3 += zp[(sh * items + it) * 4 + 3];
+        }
+        const float il = cl[t];
+        const uint32_t at = p.off_mzc + ((uint32_t)(t * nh + h) * MLA_KL + d4) * 4u;
+        st_f32(r, at, o0 * il);
+        st_f32(r, at + 4u, o1 * il);
+        st_f32(r, at + 8u, o2 * il);
+        st_f32(r, at + 12u, o3 * il);
+      }
+    }
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0) (void)__hip_atomic_fetch_add(ready + h, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // Part 2: task (h, sl) computes o rows sl*32 .. sl*32+31 of head h from
+  // the whole combined z, once the nsl parts of it are published.  Every
+  // workgroup publishes all of its parts before it waits for any, so the
+  // wait ends whatever the grid size.
+  for (int task = blockIdx.x; (parts & 2) && task < ntask; task += gridDim.x) {
+    const int h = task / nsl, sl = task % nsl;
+    const int row = sl * 32 + (threadIdx.x >> 3), part = threadIdx.x & 7;
+    i32x4 wv[8];  // this lane's 64 dims of its row, requested before the wait
+#pragma unroll
+    for (int k = 0; k < 8; ++k) wv[k] = ld_x4<0>(wrs, (uint32_t)((h * VW + nope + row) * MLA_KL + part * 64 + k * 8) * 2u);
+    if (threadIdx.x < 64) {
+      unsigned spins = 0;
+      while (true) {
+        const unsigned v = __hip_atomic_load(ready + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (v >= (unsigned)nsl) break;
+        __builtin_amdgcn_s_sleep(1);
+        if (((++spins) & 1023u) == 0 && (spins > p.spin_limit || dev_failed(p))) {
+          if (threadIdx.x == 0) set_err(p, MDE_WATCHDOG);
+          break;
+        }
+      }
     }
     __syncthreads();
-    // o[t][row] for the slice's 32 rows: 8 lanes per row, 64 dims each
+    for (int e = threadIdx.x; e < B * (MLA_KL / 4); e += NT) {
+      const int t = e / (MLA_KL / 4), d4 = (e % (MLA_KL / 4)) * 4;
+      const i32x4 v = ld_x4<CP_SC1>(r, p.off_mzc + ((uint32_t)(t * nh + h) * MLA_KL + d4) * 4u);
+      z[t * MLA_KL + d4 + 0] = __int_as_float(v[0]);
+      z[t * MLA_KL + d4 + 1] = __int_as_float(v[1]);
+      z[t * MLA_KL + d4 + 2] = __int_as_float(v[2]);
+      z[t * MLA_KL + d4 + 3] = __int_as_float(v[3]);
+    }
+    __syncthreads();
+    // o[t][row]: 8 lanes per row, 64 dims each
     {
-      const int row = sl * 32 + (threadIdx.x >> 3), part = threadIdx.x & 7;
       float ot[MAXB];
 #pragma unroll
       for (int t = 0; t < MAXB; ++t) ot[t] = 0.f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         int d = part * 64 + k * 8;
-        i32x4 w = ld_x4<0>(wrs, (uint32_t)((h * VW + nope + row) * MLA_KL + d) * 2u);
         float wf[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          wf[2 * j] = __uint_as_float((uint32_t)w[j] << 16);
-          wf[2 * j + 1] = __uint_as_float((uint32_t)w[j] & 0xFFFF0000u);
+          wf[2 * j] = __uint_as_float((uint32_t)wv[k][j] << 16);
+          wf[2 * j + 1] = __uint_as_float((uint32_t)wv[k][j] & 0xFFFF0000u);
         }
 #pragma unroll
         for (int t = 0; t < MAXB; ++t) {
@@ -2223,7 +2297,6 @@ __device__ __forceinline__ void phase_mla_out(KParams& pk, int l_layer) {
         for (int t = 0; t < B; ++t) put_hilo(r, ou_at(p, l_layer), nh * vd, t, h * vd + row, ot[t]);
       }
     }
-    (void)lane;
     __syncthreads();
   }
 }
@@ -2566,7 +2639,7 @@ __device__ __noinline__ void final_argmax(KParams& pk) {
 enum : int {
   PH_EMBED = 0, PH_QKV, PH_KV_WRITE, PH_ATTN, PH_OPROJ, PH_GATEUP, PH_DOWN, PH_MOE_A, PH_MOE_B, PH_MOE_C,
   PH_KDA_PROJ, PH_KDA_REC, PH_KDA_O, PH_MLA_A, PH_MLA_B, PH_MLA_ABS, PH_MLA_ATTN, PH_MLA_OUT, PH_MLA_O,
-  PH_LMHEAD, PH_ARGMAX
+  PH_LMHEAD, PH_ARGMAX, PH_MLA_OUT2
 };
 
 __device__ __forceinline__ void run_one_phase(KParams& pk, int layer, int phase) {
@@ -2593,7 +2666,8 @@ __device__ __forceinline__ void run_one_phase(KParams& pk, int layer, int phase)
     case PH_MLA_B: phase_mla_b(p, l_layer, -1); break;
     case PH_MLA_ABS: phase_mla_absorb(p, l_layer); break;
     case PH_MLA_ATTN: phase_mla_attn(p, l_layer); break;
-    case PH_MLA_OUT: phase_mla_out(p, l_layer); break;
+    case PH_MLA_OUT: phase_mla_out(p, l_layer, 1); break;
+    case PH_MLA_OUT2: phase_mla_out(p, l_layer, 2); break;
     case PH_MLA_O: phase_residual(p, l_layer, RES_MLA_O, L.ffn_norm, -1); break;
     case PH_LMHEAD: phase_lmhead(p, -1); break;
     case PH_ARGMAX: if (blockIdx.x == 0) final_argmax(p); break;
@@ -2663,7 +2737,7 @@ extern "C" __global__ __launch_bounds__(NT) void md_megakernel(Params p_arg) {
       phase_mla_attn(p, l_layer);
       ARRIVE();
       WAIT();
-      phase_mla_out(p, l_layer);
+      phase_mla_out(p, l_layer, 3);
       ARRIVE();
       phase_residual(p, l_layer, RES_MLA_O, L.ffn_norm, sidx++);
       ARRIVE();
@@ -2772,6 +2846,7 @@ hipError_t launch_multilaunch(const Params& p, const int* kinds, int grid, hipSt
       go(l, PH_MLA_ABS, grid);
       go(l, PH_MLA_ATTN, grid);
       go(l, PH_MLA_OUT, grid);
+      go(l, PH_MLA_OUT2, grid);
       go(l, PH_MLA_O, grid);
     }
     if (p.n_experts == 0) {

@@ -88,6 +88,7 @@ struct Params {
   uint32_t off_qabs;  // fp32[MAXB][nh][576]                absorbed, rotated, scaled q
   uint32_t off_mz;    // fp32[MAXB][C][nh][512]             attention partial z
   uint32_t off_mml;   // fp32[MAXB][C][nh][2]               attention partial (max, sum)
+  uint32_t off_mzc;   // fp32[MAXB][nh][512]                z combined over the chunks
   uint32_t off_kda;   // fp32[MAXB][2 nh dk + nh dv + 2 nh] delta-rule projections
   uint32_t off_cand;  // argmax candidates {f32, i32}[G][MAXB]
   uint32_t off_zero;  // 1 KB that stays zero (target of masked loads)

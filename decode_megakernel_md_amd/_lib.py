@@ -64,7 +64,7 @@ def lib():
         L.md_workspace_bytes.restype = ctypes.c_size_t
         L.md_workspace_bytes.argtypes = [CFG]
         L.md_kv_bytes.restype = ctypes.c_size_t
-        L.md_kv_bytes.argtypes = [CFG]
+        L.md_kv_bytes.argtypes = [CFG, I32, I32]
         L.md_init_model.restype = I32
         L.md_init_model.argtypes = [CFG, ctypes.POINTER(P), ctypes.c_size_t, P, ctypes.c_size_t, P, ctypes.POINTER(P)]
         for fn in ("md_decode_step", "md_decode_step_multilaunch"):

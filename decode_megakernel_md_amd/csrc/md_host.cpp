@@ -12,7 +12,6 @@
 #include "md_model.h"
 
 namespace md {
-size_t megakernel_smem_bytes();
 hipError_t launch_megakernel(const Params& p, int grid, hipStream_t stream);
 hipError_t megakernel_occupancy(int* blocks_per_cu);
 hipError_t launch_pack(const void* src, void* dst, int64_t rows, int64_t cols, hipStream_t stream);
@@ -120,6 +119,11 @@ md_status validate(const md_config* c) {
     if (c->n_q_heads / c->n_kv_heads > 8) return fail(MD_EUNSUPPORTED, "at most 8 query heads per kv head");
     if (c->head_dim != 64 && c->head_dim != 128) return fail(MD_EUNSUPPORTED, "head_dim must be 64 or 128");
     if (c->max_ctx % 32) return fail(MD_EUNSUPPORTED, "max_ctx must be a multiple of 32 (V cache tiles)");
+    // the attention phase counts the finished chunks of every (row, kv head)
+    // in one word of a layer's sync point
+    if (MAXB_ * c->n_kv_heads > SP_WORDS_)
+      return fail(MD_EUNSUPPORTED, "at most %d kv heads (%d rows x kv heads must fit a sync point's %d words)",
+                  SP_WORDS_ / MAXB_, MAXB_, SP_WORDS_);
   } else if (c->attn_kind == 1) {
     if (c->mla_every < 1) return fail(MD_EINVAL, "mla_every must be >= 1");
     bool has_mla = c->n_layers >= c->mla_every, has_kda = c->mla_every > 1;
@@ -324,10 +328,18 @@ size_t md_workspace_bytes(const md_config* cfg) {
   return ws_layout(cfg).total;
 }
 
-size_t md_kv_bytes(const md_config* cfg) {
+size_t md_kv_bytes(const md_config* cfg, int32_t batch, int32_t ctx_cap) {
   if (validate(cfg) != MD_OK) return 0;
+  if (batch < 1 || batch > MAXB_ || ctx_cap < 1) {
+    fail(MD_EINVAL, "batch must be in [1, %d] and ctx_cap positive", MAXB_);
+    return 0;
+  }
+  md_config c = *cfg;
+  c.max_batch = batch;
+  c.max_ctx = ctx_cap;
+  if (validate(&c) != MD_OK) return 0;
   size_t t = 0;
-  kv_offsets(cfg, &t);
+  kv_offsets(&c, &t);
   return t;
 }
 

@@ -2,7 +2,7 @@
 //
 // One persistent cooperative launch runs a whole decode step: one workgroup
 // per CU, each walking the same phase list; phases are separated by
-// device-wide sync points (hierarchical counters, see md_sync.h).  This is the
+// device-wide sync points (hierarchical counters, see the sync section below).  This is the
 // megakernel of Inferact, "700 TPS on Kimi K3: A Case for TPU Megakernels",
 // section "Why megakernels?" (the decoder step inside one program, so no
 // kernel boundary leaves the HBM interface idle) and section "Our Kimi K3
@@ -2811,19 +2811,15 @@ hipError_t launch_pack(const void* src, void* dst, int64_t rows, int64_t cols, h
   return hipGetLastError();
 }
 
-// LDS: the larger of the GEMV block (+ partial-sum staging of up to 1024
-// workgroups) and the attention block, then the routing state.
-size_t megakernel_smem_bytes() { return 0; }  // all LDS is static (md_smem)
-
+// All of the kernel's LDS is static (md_smem): launches ask for no dynamic LDS.
 hipError_t launch_megakernel(const Params& p, int grid, hipStream_t stream) {
   void* args[] = {(void*)&p};
-  return hipLaunchCooperativeKernel((const void*)md_megakernel, dim3(grid), dim3(NT), args,
-                                    (unsigned)megakernel_smem_bytes(), stream);
+  return hipLaunchCooperativeKernel((const void*)md_megakernel, dim3(grid), dim3(NT), args, 0u, stream);
 }
 
 // One decode step as a sequence of phase launches on `stream`.
 hipError_t launch_multilaunch(const Params& p, const int* kinds, int grid, hipStream_t stream) {
-  const unsigned smem = (unsigned)megakernel_smem_bytes();
+  const unsigned smem = 0u;
   Params q = p;
   auto go = [&](int layer, int phase, int g) {
     q.ml_layer = layer;
@@ -2864,11 +2860,7 @@ hipError_t launch_multilaunch(const Params& p, const int* kinds, int grid, hipSt
 }
 
 hipError_t megakernel_occupancy(int* blocks_per_cu) {
-  hipError_t e = hipFuncSetAttribute((const void*)md_megakernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)megakernel_smem_bytes());
-  if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, (const void*)md_megakernel, NT,
-                                                      megakernel_smem_bytes());
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, (const void*)md_megakernel, NT, 0);
 }
 
 }  // namespace md

@@ -83,7 +83,7 @@ class DeviceModel:
         if self.ws_bytes == 0:  # the configuration was rejected: surface the library's reason
             check(L.md_init_model(ctypes.byref(self.cfg), None, 0, None, 0, None, ctypes.byref(ctypes.c_void_p())))
         self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=self.device)
-        self.kv_bytes = L.md_kv_bytes(ctypes.byref(self.cfg))
+        self.kv_bytes = L.md_kv_bytes(ctypes.byref(self.cfg), self.cfg.max_batch, self.cfg.max_ctx)
         lay, total = kv_layout(w)
         if total != self.kv_bytes:
             raise RuntimeError(f"KV layout mismatch: library {self.kv_bytes} vs workload {total}")
@@ -160,9 +160,16 @@ class DeviceModel:
         check(lib().md_get_device_status(self.handle))
 
     def close(self) -> None:
+        """Free the library handle and every device buffer of the model (after
+        the device has finished with them), so that nothing of it is left for
+        the runtime's own teardown at interpreter exit."""
         if getattr(self, "handle", None):
+            self.torch.cuda.synchronize(self.device)
             lib().md_free_model(self.handle)
             self.handle = None
+        for name in ("wbuf", "ws", "kv"):
+            if getattr(self, name, None) is not None:
+                setattr(self, name, None)
 
     def __del__(self):
         try:

@@ -12,8 +12,23 @@ baseline (one launch per phase), so that one kernel trace holds both."""
 from __future__ import annotations
 
 import argparse
+import os
 import sys
 import time
+
+
+def print_code_maps() -> None:
+    """The executable mappings of this process (address range and file), so
+    that the frames of any fault after this point can be attributed."""
+    try:
+        with open(f"/proc/{os.getpid()}/maps") as f:
+            for line in f:
+                parts = line.split()
+                if len(parts) >= 6 and "x" in parts[1]:
+                    print(f"# map {parts[0]} {parts[5]}", file=sys.stderr)
+    except OSError as e:
+        print(f"# maps unavailable: {e}", file=sys.stderr)
+    sys.stderr.flush()
 
 
 def main():
@@ -60,7 +75,15 @@ def main():
         m.device_status()
         print(f"# {w.name}: {args.steps} steps at batch {B} ({'multi-launch' if ml else 'megakernel'})", flush=True)
         time.sleep(0.02)
+    # release every device object before returning, so that the runtime's
+    # teardown at exit (which runs after the profiler has finalised) has
+    # nothing of ours left to free
     m.close()
+    del m, toks, logits, ids
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    print_code_maps()
+    print("# released", flush=True)
 
 
 if __name__ == "__main__":

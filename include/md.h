@@ -109,18 +109,24 @@ md_status md_pack_weight(const void* src, void* dst, int64_t rows, int64_t cols,
  * by the caller. */
 size_t md_workspace_bytes(const md_config* cfg);
 
-/* Bytes of the KV / state buffer.  Per layer, in layer order, each region
- * starting on a 256-byte boundary:
- *   GQA layer: K bf16[max_batch][n_kv_heads][max_ctx][head_dim], then
- *              V bf16[max_batch][n_kv_heads][max_ctx / 32][head_dim][32]:
+/* Bytes of a KV / state buffer for `batch` sequence slots of `ctx_cap`
+ * positions each, for a model of shape cfg (cfg's own max_batch and max_ctx
+ * are replaced by batch and ctx_cap).  The buffer a model's steps take must
+ * be sized and laid out for that model's own slots and capacity:
+ * md_kv_bytes(cfg, cfg->max_batch, cfg->max_ctx).  Per layer, in layer
+ * order, each region starting on a 256-byte boundary (Bm = slots, C =
+ * capacity):
+ *   GQA layer: K bf16[Bm][n_kv_heads][C][head_dim], then
+ *              V bf16[Bm][n_kv_heads][C / 32][head_dim][32]:
  *              32-position tiles, dimension-major within a tile, so that
- *              V[b][h][t][d] sits at ((b*n_kv_heads + h)*max_ctx + t/32*32)*head_dim
- *              + d*32 + t%32 (max_ctx must be a multiple of 32)
- *   MLA layer: latent rows bf16[max_batch][max_ctx][kv_lora + rope_dim]
+ *              V[b][h][t][d] sits at ((b*n_kv_heads + h)*C + t/32*32)*head_dim
+ *              + d*32 + t%32 (C must be a multiple of 32)
+ *   MLA layer: latent rows bf16[Bm][C][kv_lora + rope_dim]
  *              (RMS-normalised latent, then the rotated key part)
- *   KDA layer: state fp32[max_batch][kda_heads][kda_dk][kda_dv]
- * Sequence b of a batch uses slot b. */
-size_t md_kv_bytes(const md_config* cfg);
+ *   KDA layer: state fp32[Bm][kda_heads][kda_dk][kda_dv]
+ * Sequence b of a batch uses slot b.  Returns 0 (md_last_error says why) for
+ * an invalid cfg, batch outside [1, 8] or a capacity the cfg does not allow. */
+size_t md_kv_bytes(const md_config* cfg, int32_t batch, int32_t ctx_cap);
 
 /* Validate cfg, check the device (gfx950, cooperative launch, LDS), record
  * the weight pointers (dev, n_weights of them) and build the layer table in

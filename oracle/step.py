@@ -29,7 +29,8 @@ def _w(get_weight: GetW, name: str) -> np.ndarray:
 
 
 def _layer(w, get_weight: GetW, l: int, xs: np.ndarray, positions, kv_l, B: int,
-           ids_out: Optional[np.ndarray], wts_out: Optional[np.ndarray]) -> None:
+           ids_out: Optional[np.ndarray], wts_out: Optional[np.ndarray],
+           rlog_out: Optional[np.ndarray] = None) -> None:
     """Apply layer l to the residuals xs[B, H] (fp64, in place)."""
     L = lib()
     H = w.hidden
@@ -85,9 +86,12 @@ def _layer(w, get_weight: GetW, l: int, xs: np.ndarray, positions, kv_l, B: int,
     xns = np.empty((B, H), dtype=np.float64)
     ids = np.empty((B, k), dtype=np.int32)
     wts = np.empty((B, k), dtype=np.float64)
+    rlog = np.empty((B, w.n_experts), dtype=np.float32)
     for b in range(B):
         L.orc_rmsnorm(H, ptr(xs[b]), ptr(g_ffn), w.rms_eps, ptr(xns[b]))
-        L.orc_router(H, w.n_experts, k, w.norm_topk, ptr(wr), ptr(xns[b]), ptr(ids[b]), ptr(wts[b]), None)
+        L.orc_router(H, w.n_experts, k, w.norm_topk, ptr(wr), ptr(xns[b]), ptr(ids[b]), ptr(wts[b]), ptr(rlog[b]))
+    if rlog_out is not None:
+        rlog_out[:] = rlog
     if ids_out is not None:
         ids_out[:] = ids
     if wts_out is not None:
@@ -116,8 +120,9 @@ def decode_step(w, get_weight: GetW, tokens, positions, kv: List[np.ndarray],
     """One decode step for a batch.  kv[l] is updated in place.
 
     Returns logits fp32[B, V], next int32[B] (greedy argmax, lowest index on
-    ties), expert_ids int32[n_layers, B, top_k] and expert_w fp64[...] (MoE
-    only), and the final residual fp64[B, H]."""
+    ties), expert_ids int32[n_layers, B, top_k], expert_w fp64[...] and the
+    fp32 router logits router_logits[n_layers, B, n_experts] on which the
+    choice was made (MoE only), and the final residual fp64[B, H]."""
     L = lib()
     tokens = np.asarray(tokens, dtype=np.int32)
     positions = np.asarray(positions, dtype=np.int64)
@@ -131,9 +136,10 @@ def decode_step(w, get_weight: GetW, tokens, positions, kv: List[np.ndarray],
     k = max(w.top_k, 1)
     ids = np.full((w.n_layers, B, k), -1, dtype=np.int32)
     wts = np.zeros((w.n_layers, B, k), dtype=np.float64)
+    rlog = np.zeros((w.n_layers, B, max(w.n_experts, 1)), dtype=np.float32)
     for l in range(w.n_layers):
         _layer(w, get_weight, l, xs, positions, kv[l], B,
-               ids[l] if w.is_moe else None, wts[l] if w.is_moe else None)
+               ids[l] if w.is_moe else None, wts[l] if w.is_moe else None, rlog[l] if w.is_moe else None)
         if layer_dump is not None:
             layer_dump.append(xs.copy())
     g_final = _w(get_weight, "final_norm")
@@ -146,6 +152,7 @@ def decode_step(w, get_weight: GetW, tokens, positions, kv: List[np.ndarray],
     if w.is_moe:
         out["expert_ids"] = ids
         out["expert_w"] = wts
+        out["router_logits"] = rlog
     return out
 
 
@@ -169,7 +176,9 @@ def verify_step(w, get_weight: GetW, tokens, positions, kv: List[np.ndarray]) ->
     Row j of the logits is the decode-step output after t_0..t_j.  The
     delta-rule states are committed as they stand after token m (accepted
     length a = m + 1); cache rows p..p+n-1 are all written.  kv is updated
-    in place accordingly."""
+    in place accordingly.  MoE models also return, per sequence, the experts
+    every row chose, expert_ids int32[B, n_layers, n, top_k], and the router
+    logits behind them, router_logits fp32[B, n_layers, n, n_experts]."""
     tokens = np.asarray(tokens, dtype=np.int32)
     positions = np.asarray(positions, dtype=np.int64)
     B, n = tokens.shape
@@ -178,10 +187,16 @@ def verify_step(w, get_weight: GetW, tokens, positions, kv: List[np.ndarray]) ->
     arg = np.empty((B, n), dtype=np.int32)
     kda_layers = [l for l in range(w.n_layers) if w.layer_kind(l) == "kda"]
     snaps = []  # per token j: copies of the KDA states after token j
+    k = max(w.top_k, 1)
+    ids = np.full((B, w.n_layers, n, k), -1, dtype=np.int32)
+    rlog = np.zeros((B, w.n_layers, n, max(w.n_experts, 1)), dtype=np.float32)
     for j in range(n):
         o = decode_step(w, get_weight, tokens[:, j], positions + j, kv)
         logits[:, j] = o["logits"]
         arg[:, j] = o["next"]
+        if w.is_moe:
+            ids[:, :, j] = np.swapaxes(o["expert_ids"], 0, 1)
+            rlog[:, :, j] = np.swapaxes(o["router_logits"], 0, 1)
         snaps.append({l: kv[l].copy() for l in kda_layers})
     acc = np.array([acceptance(tokens[b], arg[b]) for b in range(B)], dtype=np.int32)
     for b in range(B):
@@ -189,4 +204,8 @@ def verify_step(w, get_weight: GetW, tokens, positions, kv: List[np.ndarray]) ->
         for l in kda_layers:
             kv[l][b] = snaps[m][l][b]
     nxt = np.array([arg[b, int(acc[b]) - 1] for b in range(B)], dtype=np.int32)
-    return {"logits": logits, "argmax": arg, "accept_len": acc, "next": nxt}
+    out = {"logits": logits, "argmax": arg, "accept_len": acc, "next": nxt}
+    if w.is_moe:
+        out["expert_ids"] = ids
+        out["router_logits"] = rlog
+    return out

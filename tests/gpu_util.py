@@ -40,10 +40,46 @@ def run_oracle_step(w, toks, pos, overrides=None, kv=None):
     return o, kv
 
 
+def lm_margin(ref_row: np.ndarray) -> float:
+    """Oracle's top-1 minus top-2 logit, relative to the row's RMS."""
+    r = ref_row.astype(np.float64)
+    top2 = np.sort(r)[-2:]
+    return float(top2[1] - top2[0]) / float(np.sqrt(np.mean(r ** 2)))
+
+
+def router_margins(router_logits: np.ndarray, k: int) -> np.ndarray:
+    """Per (layer, token): the oracle's k-th largest router logit minus the
+    (k+1)-th (the gap that decides the selection), relative to the logits'
+    spread; +inf when every expert is chosen."""
+    lg = np.sort(router_logits.astype(np.float64), axis=-1)[..., ::-1]
+    if lg.shape[-1] <= k:
+        return np.full(lg.shape[:-1], np.inf)
+    sd = np.std(lg, axis=-1)
+    sd = np.where(sd > 0, sd, 1.0)
+    return (lg[..., k - 1] - lg[..., k]) / sd
+
+
+def log_margins(w, o, label=""):
+    """Print the oracle's decision margins of a step: the smallest LM-head
+    top-2 gap and, for MoE models, the smallest router k-th vs (k+1)-th gap,
+    so that a mismatch can be told from a near-tie.  Returns them."""
+    lm = min(lm_margin(o["logits"].reshape(-1, o["logits"].shape[-1])[i])
+             for i in range(o["logits"].reshape(-1, o["logits"].shape[-1]).shape[0]))
+    msg = f"  margins {label}: LM-head top-2 >= {lm:.3e} x rms"
+    rm = None
+    if "router_logits" in o:
+        rm = float(np.min(router_margins(o["router_logits"], w.top_k)))
+        msg += f"; router k-th vs (k+1)-th >= {rm:.3e} x sd"
+    print(msg, flush=True)
+    return lm, rm
+
+
 def compare_step(w, g, o, label=""):
-    """Assert GPU outputs g match oracle outputs o; returns the worst rel err."""
+    """Assert GPU outputs g match oracle outputs o; returns the worst rel err.
+    Prints the oracle's decision margins first (every case, pass or fail)."""
     B = o["logits"].shape[0]
     worst = 0.0
+    log_margins(w, o, label)
     for b in range(B):
         ref = o["logits"][b].astype(np.float64)
         got = g["logits"][b].astype(np.float64)
@@ -51,13 +87,40 @@ def compare_step(w, g, o, label=""):
         rms = float(np.sqrt(np.mean(ref ** 2)))
         err = float(np.max(np.abs(got - ref))) / rms
         worst = max(worst, err)
-        top2 = np.sort(ref)[-2:]
         assert err <= LOGIT_TOL, f"{label} b={b}: max|dlogit|/rms = {err:.3e} > {LOGIT_TOL}"
         assert int(g["next"][b]) == int(o["next"][b]), \
-            f"{label} b={b}: argmax {g['next'][b]} != oracle {o['next'][b]} (oracle top-2 margin {top2[1]-top2[0]:.3e})"
+            f"{label} b={b}: argmax {g['next'][b]} != oracle {o['next'][b]} (oracle top-2 margin {lm_margin(ref):.3e} x rms)"
     if "expert_ids" in o:
-        assert np.array_equal(g["expert_ids"], o["expert_ids"]), f"{label}: expert selection differs"
+        same = g["expert_ids"] == o["expert_ids"]
+        if not same.all():
+            l, b = [int(i) for i in np.argwhere(~same.all(axis=-1))[0]]
+            m = router_margins(o["router_logits"][l, b], w.top_k)
+            raise AssertionError(f"{label}: expert selection differs at layer {l} token {b}: gpu "
+                                 f"{g['expert_ids'][l, b].tolist()} oracle {o['expert_ids'][l, b].tolist()} "
+                                 f"(oracle router margin {float(m):.3e} x sd)")
     return worst
+
+
+def gpu_argmax_rows(logits: np.ndarray) -> np.ndarray:
+    """Greedy token of every row of the GPU's logits (lowest index on ties)."""
+    return np.argmax(logits, axis=-1).astype(np.int32)
+
+
+def compare_verify(w, logits, ids, acc, nxt, v, label=""):
+    """Verify outputs of the GPU (logits [n][V], expert ids [L][n][k] or None,
+    accepted length, next token) against the oracle's verify_step of one
+    sequence: every row's argmax and, for MoE models, every row's experts
+    bit-exact; logits within the tolerance; acceptance and next token equal."""
+    o = {"logits": v["logits"][0], "next": v["argmax"][0]}
+    g = {"logits": logits, "next": gpu_argmax_rows(logits)}
+    if ids is not None:
+        o["expert_ids"] = v["expert_ids"][0]          # [L][n][k]: row j plays the part of token j
+        o["router_logits"] = v["router_logits"][0]
+        g["expert_ids"] = ids
+    err = compare_step(w, g, o, label)
+    assert int(acc) == int(v["accept_len"][0]), f"{label}: accepted {acc} != oracle {v['accept_len'][0]}"
+    assert int(nxt) == int(v["next"][0]), f"{label}: next token {nxt} != oracle {v['next'][0]}"
+    return err
 
 
 def compare_kv_rows(w, kv_gpu, kv_ref, positions, B):

@@ -70,7 +70,16 @@ def test_kv_bytes_match_the_documented_layout():
     for name in ("mini_dense", "mini_moe", "mini_hybrid", "dense_27b", "hybrid_moe"):
         w = WL.get(name)
         _, total = WL.kv_layout(w)
-        assert L.md_kv_bytes(ctypes.byref(_lib.config_from(w))) == total, name
+        c = _lib.config_from(w)
+        assert L.md_kv_bytes(ctypes.byref(c), w.max_batch, w.max_ctx) == total, name
+        # other slot counts and capacities: the same layout with those sizes
+        for B, C in ((1, w.max_ctx), (3, w.max_ctx + 32), (8, 64)):
+            _, t2 = WL.kv_layout(w.replace(max_batch=B, max_ctx=C))
+            assert L.md_kv_bytes(ctypes.byref(c), B, C) == t2, (name, B, C)
+    c = _lib.config_from(WL.mini_dense())
+    assert L.md_kv_bytes(ctypes.byref(c), 0, 64) == 0 and "batch" in _err()
+    assert L.md_kv_bytes(ctypes.byref(c), 9, 64) == 0
+    assert L.md_kv_bytes(ctypes.byref(c), 2, 80) == 0     # not a multiple of the 32-position V tiles
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -105,6 +114,20 @@ def test_moe_and_hybrid_limits():
     assert L.md_init_model(ctypes.byref(c), None, 0, None, 0, None, ctypes.byref(h)) == _lib.MD_EUNSUPPORTED
     c = _cfg("mini_hybrid", kda_dv=48)
     assert L.md_init_model(ctypes.byref(c), None, 0, None, 0, None, ctypes.byref(h)) == _lib.MD_EUNSUPPORTED
+
+
+def test_kv_head_count_fits_the_attention_counters():
+    """The GQA attention phase counts each (row, kv head)'s finished chunks in
+    one word of a 288-word sync point: 8 rows x 36 kv heads fit, 37 do not
+    (they would spill into the next layer's counters)."""
+    L = _lib.lib()
+    h = P()
+    ok = _cfg("mini_dense", n_q_heads=36, n_kv_heads=36, head_dim=64)
+    assert L.md_workspace_bytes(ctypes.byref(ok)) > 0
+    bad = _cfg("mini_dense", n_q_heads=37, n_kv_heads=37, head_dim=64)
+    assert L.md_workspace_bytes(ctypes.byref(bad)) == 0
+    assert L.md_init_model(ctypes.byref(bad), None, 0, None, 0, None, ctypes.byref(h)) == _lib.MD_EUNSUPPORTED
+    assert "kv heads" in _err()
 
 
 def test_init_argument_checks_before_any_device_call():

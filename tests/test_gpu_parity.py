@@ -161,6 +161,24 @@ def _greedy_drafts(w, W, kv, p0, accept, n=8):
     return seq[:n]
 
 
+def _gpu_verify(m, toks, p0):
+    """One verify launch through the C ABI: logits [n][V], expert ids
+    [L][n][k] (MoE models; else None), accepted length, next token."""
+    import torch
+    w, dev, n = m.w, m.device, len(toks)
+    t = torch.tensor([toks], dtype=torch.int32, device=dev)
+    pp = torch.tensor([p0], dtype=torch.int32, device=dev)
+    logits = torch.full((1, n, w.vocab), float("nan"), dtype=torch.float32, device=dev)
+    acc = torch.full((1,), -7, dtype=torch.int32, device=dev)
+    nxt = torch.full((1,), -7, dtype=torch.int32, device=dev)
+    ids = torch.full((w.n_layers, n, w.top_k), -7, dtype=torch.int32, device=dev) if w.is_moe else None
+    m.verify(t, pp, logits, acc, nxt, ids)
+    torch.cuda.synchronize(dev)
+    m.device_status()
+    return (logits.cpu().numpy()[0], ids.cpu().numpy() if ids is not None else None, int(acc.cpu()[0]),
+            int(nxt.cpu()[0]))
+
+
 @pytest.mark.parametrize("name", ["mini_dense", "mini_moe", "mini_hybrid"])
 @pytest.mark.parametrize("accept", [1, 3, 8])
 def test_verify_matches_oracle(torch_cuda, name, accept):
@@ -178,20 +196,9 @@ def test_verify_matches_oracle(torch_cuda, name, accept):
     v = ostep.verify_step(w, W, np.array([toks]), np.array([p0]), kv_ref)
     assert int(v["accept_len"][0]) == accept
     m = _model(w)
-    dev = m.device
-    t = torch.tensor([toks], dtype=torch.int32, device=dev)
-    pp = torch.tensor([p0], dtype=torch.int32, device=dev)
-    logits = torch.full((1, n, w.vocab), float("nan"), dtype=torch.float32, device=dev)
-    acc = torch.full((1,), -7, dtype=torch.int32, device=dev)
-    nxt = torch.full((1,), -7, dtype=torch.int32, device=dev)
-    m.verify(t, pp, logits, acc, nxt)
-    torch.cuda.synchronize(dev)
-    m.device_status()
-    assert int(acc.cpu()[0]) == accept
-    assert int(nxt.cpu()[0]) == int(v["next"][0])
-    g = {"logits": logits.cpu().numpy()[0], "next": v["argmax"][0]}
-    o = {"logits": v["logits"][0], "next": v["argmax"][0]}
-    err = GU.compare_step(w, g, o, f"verify {name} a={accept}")
+    logits, ids, acc, nxt = _gpu_verify(m, toks, p0)
+    assert acc == accept
+    err = GU.compare_verify(w, logits, ids, acc, nxt, v, f"verify {name} a={accept}")
     kvg = m.kv_host()
     for j in range(n):
         GU.compare_kv_rows(w, kvg, kv_ref, [p0 + j], 1)
@@ -266,20 +273,9 @@ def test_full_shape_verify_matches_oracle(torch_cuda, accept):
     v = ostep.verify_step(w, W, np.array([toks]), np.array([p0]), kv_ref)
     assert int(v["accept_len"][0]) == accept
     m = _model(w)
-    dev = m.device
-    t = torch.tensor([toks], dtype=torch.int32, device=dev)
-    pp = torch.tensor([p0], dtype=torch.int32, device=dev)
-    logits = torch.full((1, n, w.vocab), float("nan"), dtype=torch.float32, device=dev)
-    acc = torch.full((1,), -7, dtype=torch.int32, device=dev)
-    nxt = torch.full((1,), -7, dtype=torch.int32, device=dev)
-    m.verify(t, pp, logits, acc, nxt)
-    torch.cuda.synchronize(dev)
-    m.device_status()
-    assert int(acc.cpu()[0]) == accept
-    assert int(nxt.cpu()[0]) == int(v["next"][0])
-    g = {"logits": logits.cpu().numpy()[0], "next": v["argmax"][0]}
-    o = {"logits": v["logits"][0], "next": v["argmax"][0]}
-    err = GU.compare_step(w, g, o, f"verify_hybrid 4 layers a={accept}")
+    logits, ids, acc, nxt = _gpu_verify(m, toks, p0)
+    assert acc == accept
+    err = GU.compare_verify(w, logits, ids, acc, nxt, v, f"verify_hybrid 4 layers a={accept}")
     kvg = m.kv_host()
     for j in range(n):
         GU.compare_kv_rows(w, kvg, kv_ref, [p0 + j], 1)

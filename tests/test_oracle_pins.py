@@ -589,3 +589,54 @@ def test_head_argmax_ties_pick_lowest_index():
     lm[:] = 0
     out = ostep.decode_step(w, W, np.array([0]), np.array([3]), host_kv(w))
     assert int(out["next"][0]) == 0
+
+
+def test_moe_routed_weights_reach_their_own_experts():
+    """Each routed expert writes a one-hot pattern of its own: its gate and up
+    matrices have one nonzero row (the same vector a for every expert), so its
+    hidden state is s = silu(a.xn) * (a.xn) in unit 0 only, and its down
+    projection maps unit 0 to residual row e.  With attention and the shared
+    expert zeroed, the block adds w_e * s to row e for every chosen expert e
+    and nothing elsewhere, so each expert's weight is read off the residual.
+    The expected ids and weights come from a brute-force sort of a NumPy
+    softmax of the router logits.  Catches a weight given to the wrong expert
+    (a permutation of the chosen ones), a missing or wrong renormalisation, a
+    weight applied to the wrong token, and an expert added twice or never."""
+    w = WL.mini_moe().replace(n_layers=1)
+    assert w.hidden >= w.n_experts
+    W = HostWeights(w)
+    rng = np.random.default_rng(7)
+    for n in ("wq", "wk", "wv", "wo"):
+        W.overrides["L0." + n] = np.zeros_like(W("L0." + n))
+    for n in ("gate", "up", "down"):
+        W.overrides[f"L0.sh0_{n}"] = np.zeros_like(W(f"L0.sh0_{n}"))
+    a_bits = rand_bits(rng, (w.hidden,), 0.05)
+    for e in range(w.n_experts):
+        g = np.zeros((w.expert_ffn, w.hidden), np.uint16)
+        g[0] = a_bits
+        d = np.zeros((w.hidden, w.expert_ffn), np.uint16)
+        d[e, 0] = BF1
+        W.overrides[f"L0.e{e}_gate"] = g
+        W.overrides[f"L0.e{e}_up"] = g.copy()
+        W.overrides[f"L0.e{e}_down"] = d
+    kv = host_kv(w)
+    B = 4
+    toks = synth.tokens(w, B)
+    out = ostep.decode_step(w, W, toks, np.array([3, 9, 17, 30]), kv)
+    x0 = R.widen(W("embed"))[toks]
+    xn = R.rms_norm(x0, W("L0.ffn_norm").reshape(-1), w.rms_eps)
+    lg = (xn @ R.widen(W("L0.router")).T).astype(np.float32).astype(np.float64)
+    for b in range(B):
+        order = sorted(range(w.n_experts), key=lambda e: (-lg[b, e], e))[: w.top_k]
+        p = np.exp(lg[b] - lg[b].max())
+        p /= p.sum()
+        wts = p[order] / p[order].sum()
+        assert list(out["expert_ids"][0, b]) == order
+        av = float(xn[b] @ R.widen(a_bits))
+        s = R.silu(av) * av
+        want = np.zeros(w.hidden)
+        want[order] = wts * s
+        got = out["x_final"][b] - x0[b]
+        assert np.allclose(got, want, rtol=1e-9, atol=1e-12 * abs(s)), f"token {b}"
+        # the weights differ from expert to expert, so a permutation would show
+        assert len(set(np.round(wts, 12))) == w.top_k

@@ -195,27 +195,35 @@ int orc_mla_block(int H, int nh, int q_lora, int kv_lora, int rope, int nope, in
   for (int i = 0; i < rope; ++i) cache[pos * row + kv_lora + i] = orc_to_bf16(ckv[kv_lora + i]);
   double scale = 1.0 / sqrt((double)qk);
   /* heads are independent: one head per OpenMP iteration, each with its own
-   * scratch; the per-head arithmetic is the serial loop nest below. */
+   * scratch.  Per head, W_uk,h and W_uv,h are widened once and stored
+   * column-major (wt[c][r]) so that all rows of k_t and v_t accumulate side
+   * by side; every element is still the plain sum over c in ascending order. */
 #pragma omp parallel for schedule(dynamic)
   for (int h = 0; h < nh; ++h) {
     double* ct = malloc(sizeof(double) * kv_lora);
     double* kt = malloc(sizeof(double) * nope);
     double* s = malloc(sizeof(double) * (pos + 1));
     double* vall = malloc(sizeof(double) * (pos + 1) * vdim);
+    double* wukt = malloc(sizeof(double) * kv_lora * nope);
+    double* wuvt = malloc(sizeof(double) * kv_lora * vdim);
     const uint16_t* wuk = wkvb + (int64_t)h * (nope + vdim) * kv_lora;
     const uint16_t* wuv = wuk + (int64_t)nope * kv_lora;
+    for (int r = 0; r < nope; ++r)
+      for (int c = 0; c < kv_lora; ++c) wukt[(int64_t)c * nope + r] = orc_bf16(wuk[(int64_t)r * kv_lora + c]);
+    for (int r = 0; r < vdim; ++r)
+      for (int c = 0; c < kv_lora; ++c) wuvt[(int64_t)c * vdim + r] = orc_bf16(wuv[(int64_t)r * kv_lora + c]);
     const double* qh = q + h * qk;
     for (int64_t t = 0; t <= pos; ++t) {
       for (int i = 0; i < kv_lora; ++i) ct[i] = orc_bf16(cache[t * row + i]);
-      for (int r = 0; r < nope; ++r) {            /* k_nope = W_uk,h c_t */
-        double acc = 0.0;
-        for (int c = 0; c < kv_lora; ++c) acc += orc_bf16(wuk[(int64_t)r * kv_lora + c]) * ct[c];
-        kt[r] = acc;
-      }
-      for (int r = 0; r < vdim; ++r) {            /* v = W_uv,h c_t */
-        double acc = 0.0;
-        for (int c = 0; c < kv_lora; ++c) acc += orc_bf16(wuv[(int64_t)r * kv_lora + c]) * ct[c];
-        vall[t * vdim + r] = acc;
+      double* vt = vall + t * vdim;
+      for (int r = 0; r < nope; ++r) kt[r] = 0.0;      /* k_nope = W_uk,h c_t */
+      for (int r = 0; r < vdim; ++r) vt[r] = 0.0;      /* v = W_uv,h c_t */
+      for (int c = 0; c < kv_lora; ++c) {
+        const double cc = ct[c];
+        const double* wk = wukt + (int64_t)c * nope;
+        const double* wv = wuvt + (int64_t)c * vdim;
+        for (int r = 0; r < nope; ++r) kt[r] += wk[r] * cc;
+        for (int r = 0; r < vdim; ++r) vt[r] += wv[r] * cc;
       }
       double d = 0.0;
       for (int i = 0; i < nope; ++i) d += qh[i] * kt[i];
@@ -228,7 +236,7 @@ int orc_mla_block(int H, int nh, int q_lora, int kv_lora, int rope, int nope, in
       for (int64_t t = 0; t <= pos; ++t) acc += s[t] * vall[t * vdim + i];
       o[h * vdim + i] = acc;
     }
-    free(ct); free(kt); free(s); free(vall);
+    free(ct); free(kt); free(s); free(vall); free(wukt); free(wuvt);
   }
   orc_matvec(H, (int64_t)nh * vdim, wo, o, a);
   for (int i = 0; i < H; ++i) x[i] += a[i];

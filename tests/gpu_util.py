@@ -123,12 +123,56 @@ def compare_verify(w, logits, ids, acc, nxt, v, label=""):
     return err
 
 
+def kv_rows(w, kv, positions, B):
+    """From full host caches (the oracle's layout), the entries a step wrote:
+    per layer, GQA [2][B][n_kv][head_dim] at each sequence's position, MLA
+    [B][row] likewise, delta-rule states [B][heads][dk][dv] whole."""
+    out = []
+    for l in range(w.n_layers):
+        kind = w.layer_kind(l)
+        if kind == "kda":
+            out.append(np.ascontiguousarray(kv[l][:B]))
+        elif kind == "mla":
+            out.append(np.stack([kv[l][b, int(positions[b])] for b in range(B)]))
+        else:
+            out.append(np.stack([kv[l][:, b, :, int(positions[b]), :] for b in range(B)], axis=1))
+    return out
+
+
+def kv_rows_dev(m, positions, B):
+    """The same entries read from the GPU's cache (only those rows are copied
+    to the host; GQA V rows are taken from their 32-position tiles)."""
+    from synth.workloads import V_TILE
+    out = []
+    for l in range(m.w.n_layers):
+        kind = m.w.layer_kind(l)
+        t = m.kv_layer(l)
+        if kind == "kda":
+            out.append(t[:B].cpu().numpy())
+        elif kind == "mla":
+            out.append(np.stack([t[b, int(positions[b])].cpu().numpy().view(np.uint16) for b in range(B)]))
+        else:
+            rows = []
+            for b in range(B):
+                p = int(positions[b])
+                k = t[0, b, :, p, :]
+                vt = t[1, b].reshape(t.shape[2], t.shape[3] // V_TILE, t.shape[4], V_TILE)  # [nkv][tile][hd][32]
+                v = vt[:, p // V_TILE, :, p % V_TILE]
+                rows.append(np.stack([k.cpu().numpy(), v.cpu().numpy()]).view(np.uint16))
+            out.append(np.stack(rows, axis=1))
+    return out
+
+
 def compare_kv_rows(w, kv_gpu, kv_ref, positions, B):
     """New cache rows.  Layer 0's row depends only on the embedding and the
     layer's weights, so GPU (fp32) and oracle (fp64) values round to the same
     bf16 or to neighbours: at most 1 ulp apart.  Deeper rows inherit the
-    residual's fp32-vs-fp64 difference: 1 ulp plus 1e-3 of the row's RMS."""
+    residual's fp32-vs-fp64 difference: 1 ulp plus 1e-3 of the row's RMS.
+    kv_gpu: full host caches (DeviceModel.kv_host) or kv_rows_dev's rows."""
     from tests.ref_numpy import widen
+    if len(kv_gpu) and kv_gpu[0].ndim == kv_ref[0].ndim and kv_gpu[0].shape == kv_ref[0].shape:
+        kv_gpu = kv_rows(w, kv_gpu, positions, B)
+    ref = kv_rows(w, kv_ref, positions, B)
     n_off = 0
     for l in range(w.n_layers):
         kind = w.layer_kind(l)
@@ -136,15 +180,14 @@ def compare_kv_rows(w, kv_gpu, kv_ref, positions, B):
             # delta-rule state, rewritten in place: max |diff| <= 1e-3 of the state's RMS
             for b in range(B):
                 a = kv_gpu[l][b].astype(np.float64)
-                r = kv_ref[l][b].astype(np.float64)
+                r = ref[l][b].astype(np.float64)
                 rms = float(np.sqrt(np.mean(r ** 2)))
                 err = float(np.max(np.abs(a - r)))
                 assert err <= 1e-3 * rms, f"layer {l} b={b}: delta-rule state max|diff| {err:.3e} > 1e-3 * rms {rms:.3e}"
             continue
         if kind == "mla":
             for b in range(B):
-                p = int(positions[b])
-                a, r = kv_gpu[l][b, p], kv_ref[l][b, p]
+                a, r = kv_gpu[l][b], ref[l][b]
                 af, rf = widen(a), widen(r)
                 rms = np.sqrt(np.mean(rf ** 2))
                 bad = np.abs(af - rf) > np.abs(rf) * 2.0 ** -7 + 1e-3 * rms
@@ -152,9 +195,8 @@ def compare_kv_rows(w, kv_gpu, kv_ref, positions, B):
                 n_off += int((a != r).sum())
             continue
         for b in range(B):
-            p = int(positions[b])
-            a = kv_gpu[l][:, b, :, p, :]
-            r = kv_ref[l][:, b, :, p, :]
+            a = kv_gpu[l][:, b]
+            r = ref[l][:, b]
             d_ulp = np.abs(a.astype(np.int32) - r.astype(np.int32))
             if l == 0:
                 assert d_ulp.max() <= 1, f"layer 0 b={b}: cache row differs by {d_ulp.max()} ulp"

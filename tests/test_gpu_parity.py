@@ -1,5 +1,7 @@
 """GPU parity: the megakernel step against the oracle on identical seeded
 inputs (the oracle never sees anything the GPU produced)."""
+import os
+
 import numpy as np
 import pytest
 
@@ -247,22 +249,55 @@ def test_full_shape_layers_match_oracle(torch_cuda, name, B):
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("name,B", [("dense_27b", 1), ("dense_27b", 8), ("hybrid_moe", 1)])
+def test_full_depth_step_matches_oracle(torch_cuda, name, B):
+    """A whole decode step of the 64-layer dense model (batches 1 and 8) and
+    of the 92-layer hybrid MoE (batch 1) at full context, in bench.py's
+    launch configuration, against the oracle's unfused layer-by-layer step:
+    greedy tokens and every layer's expert ids bit-exact, logits within
+    2e-2 x row RMS, every new cache row and delta-rule state within its
+    tolerance.  The GPU model is freed before the oracle runs (its weights are
+    drawn again on the host, layer by layer, from the same seeded generator)."""
+    torch = torch_cuda
+    w = WL.get(name)
+    toks = synth.tokens(w, B)
+    pos = [w.context - 97 * b for b in range(B)]
+    print(f"case {name} full depth ({w.n_layers} layers) B={B} pos={pos}", flush=True)
+    m = _model(w)
+    g = GU.run_gpu_step(m, toks, pos)
+    rows = GU.kv_rows_dev(m, pos, B)
+    m.close()
+    del m
+    torch.cuda.empty_cache()
+    o, kv_ref = GU.run_oracle_step(w, toks, pos)
+    err = GU.compare_step(w, g, o, f"{name} full depth B={B}")
+    GU.compare_kv_rows(w, rows, kv_ref, pos, B)
+    print(f"  max|dlogit|/rms = {err:.2e}", flush=True)
+
+
+@pytest.mark.slow
+@pytest.mark.skipif(not os.environ.get("MD_FULL_DEPTH_B8"), reason="hybrid 92 layers at batch 8: about 6 minutes of "
+                    "fp64 oracle (8 x 23 MLA layers over 8192 positions); run with MD_FULL_DEPTH_B8=1")
+def test_full_depth_hybrid_batch8_matches_oracle(torch_cuda):
+    test_full_depth_step_matches_oracle(torch_cuda, "hybrid_moe", 8)
+
+
+@pytest.mark.slow
 @pytest.mark.parametrize("accept", [3, 6])
 def test_full_shape_verify_matches_oracle(torch_cuda, accept):
     """Verify of 1 anchor + 7 drafts on the hybrid model at its full layer
-    shapes and vocabulary, in bench.py's launch configuration (4 layers: 3
-    delta-rule and 1 MLA, each with the 16-expert MoE; context 1024 rather
-    than 8192 so that the a-1 greedy steps and the 8 sequential verify rows
-    of the fp64 oracle finish in under a minute -- the 8192-position MLA
-    cache is covered by the decode test above), at the acceptance lengths
-    bench.py times: drafts are the oracle's greedy continuation for a-1
-    tokens, then a token that differs from the greedy one.  The acceptance
-    length, the next token, all 8 logit rows, the new cache rows and the
-    committed delta-rule states must match the oracle."""
+    shapes, vocabulary and context (8192), in bench.py's launch configuration
+    (4 layers: 3 delta-rule and 1 MLA, each with the 16-expert MoE, so that
+    the a-1 greedy steps and the 8 sequential verify rows of the fp64 oracle
+    finish in under a minute), at the acceptance lengths bench.py times:
+    drafts are the oracle's greedy continuation for a-1 tokens, then a token
+    that differs from the greedy one.  The acceptance length, the next token,
+    every row's greedy token and expert ids, all 8 logit rows, the new cache
+    rows and the committed delta-rule states must match the oracle."""
     torch = torch_cuda
     from oracle import step as ostep
     from tests.harness import HostWeights, host_kv, kv_copy
-    w = WL.get("verify_hybrid").replace(n_layers=4, context=1024, max_ctx=1024 + 32)
+    w = WL.get("verify_hybrid").replace(n_layers=4)
     n = 8
     p0 = w.context
     W = HostWeights(w)
@@ -280,3 +315,38 @@ def test_full_shape_verify_matches_oracle(torch_cuda, accept):
     for j in range(n):
         GU.compare_kv_rows(w, kvg, kv_ref, [p0 + j], 1)
     print(f"  max|dlogit|/rms = {err:.2e}")
+
+
+@pytest.mark.slow
+@pytest.mark.skipif(not os.environ.get("MD_LONG_CHAIN"), reason="256 chained full-width steps: about 2-3 minutes of "
+                    "fp64 oracle; run with MD_LONG_CHAIN=1")
+@pytest.mark.parametrize("B,steps,sampled", [(1, 256, (0, 1, 127, 255)), (8, 64, (0, 1, 31, 63))])
+def test_long_chain_full_width(torch_cuda, B, steps, sampled):
+    """Chained greedy decode steps of the 27B-shaped dense model at its full
+    width, vocabulary and context 4096 (2 layers, so that the fp64 oracle can
+    run every step): 256 steps at batch 1, 64 at batch 8, each step one
+    launch in bench.py's launch configuration.  The GPU and the oracle each
+    advance their own caches (the oracle never sees a value the GPU
+    produced); every step's greedy tokens must agree (the next step's input),
+    and at the sampled steps the logits and that step's new cache rows are
+    compared."""
+    from tests.harness import HostWeights, host_kv
+    from oracle import step as ostep
+    torch = torch_cuda
+    w = WL.get("dense_27b").replace(n_layers=2)
+    m = _model(w)
+    W = HostWeights(w)
+    kv_ref = host_kv(w)
+    toks = [int(t) for t in synth.tokens(w, B)]
+    pos0 = [w.context - 13 * b for b in range(B)]
+    for s in range(steps):
+        pos = [p + s for p in pos0]
+        if s in sampled:
+            print(f"case long chain B={B} step {s} pos={pos} toks={toks}", flush=True)
+        g = GU.run_gpu_step(m, toks, pos)
+        o = ostep.decode_step(w, W, np.asarray(toks), np.asarray(pos), kv_ref)
+        assert np.array_equal(g["next"], o["next"]), f"step {s}: greedy tokens {g['next']} != oracle {o['next']}"
+        if s in sampled:
+            GU.compare_step(w, g, o, f"long chain B={B} step {s}")
+            GU.compare_kv_rows(w, GU.kv_rows_dev(m, pos, B), kv_ref, pos, B)
+        toks = [int(t) for t in o["next"]]

@@ -40,7 +40,7 @@ class MdError(RuntimeError):
 
 EXPORTS = [
     "md_weight_count", "md_weight_info", "md_workspace_bytes", "md_kv_bytes", "md_init_model",
-    "md_decode_step", "md_decode_step_multilaunch", "md_verify_step", "md_get_device_status",
+    "md_decode_step", "md_decode_step_multilaunch", "md_decode_step_noalloc", "md_verify_step", "md_get_device_status",
     "md_last_error", "md_free_model", "md_set_trace", "md_grid_size", "md_packed_bytes", "md_pack_weight",
     "md_weight_layout",
 ]
@@ -67,7 +67,7 @@ def lib():
         L.md_kv_bytes.argtypes = [CFG, I32, I32]
         L.md_init_model.restype = I32
         L.md_init_model.argtypes = [CFG, ctypes.POINTER(P), ctypes.c_size_t, P, ctypes.c_size_t, P, ctypes.POINTER(P)]
-        for fn in ("md_decode_step", "md_decode_step_multilaunch"):
+        for fn in ("md_decode_step", "md_decode_step_multilaunch", "md_decode_step_noalloc"):
             f = getattr(L, fn)
             f.restype = I32
             f.argtypes = [P, P, P, P, P, I32, P, P, P]

@@ -16,6 +16,9 @@ hipError_t launch_megakernel(const Params& p, int grid, hipStream_t stream);
 hipError_t megakernel_occupancy(int* blocks_per_cu);
 hipError_t launch_pack(const void* src, void* dst, int64_t rows, int64_t cols, hipStream_t stream);
 hipError_t launch_multilaunch(const Params& p, const int* kinds, int grid, hipStream_t stream);
+size_t scratch_bytes();
+hipError_t scratch_address(int dev, void** out);
+hipError_t launch_fill_u32(void* dst, uint32_t v, uint32_t n_words, hipStream_t stream);
 }  // namespace md
 
 using namespace md;
@@ -288,6 +291,10 @@ struct md_model {
   std::vector<int> kinds;  // layer kinds (host copy of the layer table's)
   uint64_t* trace = nullptr;
   int trace_n = 0;
+  int dev = 0;                  // the device the model lives on
+  uint8_t* scratch = nullptr;   // that device's static scratch (md_decode_step_noalloc)
+  hipError_t scratch_err = hipSuccess;
+  int* last_err_word = nullptr; // error word of the last step (workspace or static scratch)
 };
 
 extern "C" {
@@ -446,6 +453,13 @@ md_status md_init_model(const md_config* cfg, const void* const* weights, size_t
   }
   m->kinds.resize(cfg->n_layers);
   for (int l = 0; l < cfg->n_layers; ++l) m->kinds[l] = L[l].kind;
+  // the static scratch of the allocation-free step: its address on this
+  // device, taken here at set-up with the device current
+  m->dev = dev;
+  void* sp = nullptr;
+  m->scratch_err = scratch_address(dev, &sp);
+  m->scratch = (uint8_t*)sp;
+  m->last_err_word = (int*)(m->ws + lay.err);
   *out = m;
   return MD_OK;
 }
@@ -520,6 +534,43 @@ md_status md_decode_step(md_model* m, const int32_t* tokens, const int32_t* posi
   if (e != hipSuccess) return fail(MD_EHIP, "megakernel launch: %s", hipGetErrorString(e));
   m->bank ^= 1;
   m->last_stream = (hipStream_t)hip_stream;
+  m->last_err_word = p.err;
+  return MD_OK;
+}
+
+md_status md_decode_step_noalloc(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv_cache,
+                                 float* out_logits, int32_t batch, int32_t* out_tokens, int32_t* out_expert_ids,
+                                 void* hip_stream) {
+  Params p;
+  md_status st = fill_params(m, tokens, positions, kv_cache, out_logits, batch, out_tokens, out_expert_ids, p);
+  if (st != MD_OK) return st;
+  if (m->scratch_err != hipSuccess || !m->scratch)
+    return fail(MD_EHIP, "the static scratch's device address is unavailable: %s", hipGetErrorString(m->scratch_err));
+  const WsLayout& w = m->lay;
+  if (w.total > scratch_bytes())
+    return fail(MD_ENOMEM, "this model's step needs %zu bytes of scratch; the static scratch holds %zu "
+                "(use md_decode_step with the model's workspace)", w.total, scratch_bytes());
+  // Per-step buffers from the static scratch, at the workspace layout's own
+  // offsets; the layer table, expert pointers and rotary table stay in the
+  // model's workspace (written once at md_init_model).
+  uint8_t* s = m->scratch;
+  p.ws = s;
+  p.x = (float*)(s + w.x);
+  p.sync = (unsigned*)(s + w.sync);
+  p.err = (int*)(s + w.err);
+  p.kda_ring = s + w.ring;
+  p.bank = 0;
+  // The scratch keeps whatever the last call on this device left: clear the
+  // counters this step uses, its error word and the zero line.
+  hipStream_t stream = (hipStream_t)hip_stream;
+  hipError_t e = launch_fill_u32(s + w.sync, 0u, (uint32_t)((size_t)w.n_sync * SP_WORDS_), stream);
+  if (e == hipSuccess) e = launch_fill_u32(s + w.err, 0u, 1u, stream);
+  if (e == hipSuccess) e = launch_fill_u32(s + w.zero, 0u, 1024u / 4u, stream);
+  if (e != hipSuccess) return fail(MD_EHIP, "clearing the static scratch: %s", hipGetErrorString(e));
+  e = launch_megakernel(p, m->grid, stream);
+  if (e != hipSuccess) return fail(MD_EHIP, "megakernel launch: %s", hipGetErrorString(e));
+  m->last_stream = stream;
+  m->last_err_word = p.err;
   return MD_OK;
 }
 
@@ -534,6 +585,7 @@ md_status md_decode_step_multilaunch(md_model* m, const int32_t* tokens, const i
   if (e != hipSuccess) return fail(MD_EHIP, "phase launch: %s", hipGetErrorString(e));
   m->bank ^= 1;
   m->last_stream = (hipStream_t)hip_stream;
+  m->last_err_word = p.err;
   return MD_OK;
 }
 
@@ -565,6 +617,7 @@ md_status md_verify_step(md_model* m, const int32_t* tokens, const int32_t* posi
   if (e != hipSuccess) return fail(MD_EHIP, "megakernel launch: %s", hipGetErrorString(e));
   m->bank ^= 1;
   m->last_stream = (hipStream_t)hip_stream;
+  m->last_err_word = p.err;
   return MD_OK;
 }
 
@@ -573,13 +626,15 @@ md_status md_get_device_status(md_model* m) {
   hipError_t e = m->last_stream ? hipStreamSynchronize(m->last_stream) : hipDeviceSynchronize();
   if (e != hipSuccess) return fail(MD_EHIP, "synchronise: %s", hipGetErrorString(e));
   int err = 0;
-  e = hipMemcpy(&err, m->ws + m->lay.err, sizeof err, hipMemcpyDeviceToHost);
+  int* word = m->last_err_word ? m->last_err_word : (int*)(m->ws + m->lay.err);
+  e = hipMemcpy(&err, word, sizeof err, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return fail(MD_EHIP, "reading the device error word: %s", hipGetErrorString(e));
   if (err) {
     int zero = 0;
     // a failed step leaves its counter bank in an unknown state: clear both
-    // (and the error word), so that the handle can run again
-    hipError_t c = hipMemcpy(m->ws + m->lay.err, &zero, sizeof zero, hipMemcpyHostToDevice);
+    // (and the error word), so that the handle can run again (the static
+    // scratch's counters are cleared by every allocation-free step itself)
+    hipError_t c = hipMemcpy(word, &zero, sizeof zero, hipMemcpyHostToDevice);
     if (c == hipSuccess) c = hipMemset(m->ws + m->lay.sync, 0, (size_t)4 * 2 * m->lay.n_sync * SP_WORDS_);
     if (c == hipSuccess) c = hipDeviceSynchronize();
     if (c != hipSuccess)

@@ -20,6 +20,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -2856,6 +2857,52 @@ hipError_t launch_multilaunch(const Params& p, const int* kinds, int grid, hipSt
   }
   go(-1, PH_LMHEAD, grid);
   go(-1, PH_ARGMAX, grid);  // workgroup 0 reduces all grid candidates
+  return hipGetLastError();
+}
+
+// ===================================================================== static scratch
+// The allocation-free decode step (md_decode_step_noalloc) takes its per-step
+// buffers from this file-scope array instead of the model's workspace: one
+// copy per device, held from the library's load until the process ends.  In
+// host code its name is only a stand-in; the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current and
+// kept per device.
+constexpr size_t MD_SCRATCH_BYTES = (size_t)128 << 20;
+static __device__ __align__(256) uint8_t scratch[MD_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+static void* g_scratch_addr[MAX_DEVICES];
+static std::mutex g_scratch_mu;
+
+size_t scratch_bytes() { return MD_SCRATCH_BYTES; }
+
+// Device address of `scratch` on device dev, which must be the current device.
+hipError_t scratch_address(int dev, void** out) {
+  *out = nullptr;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = ptr;
+  }
+  *out = g_scratch_addr[dev];
+  return hipSuccess;
+}
+
+// n 32-bit words at dst set to v (a kernel, not a memset, so that the fill is
+// an ordinary kernel node where the call is captured into a graph).
+__global__ void k_fill_u32(uint32_t* __restrict__ dst, uint32_t v, uint32_t n) {
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) dst[i] = v;
+}
+
+hipError_t launch_fill_u32(void* dst, uint32_t v, uint32_t n_words, hipStream_t stream) {
+  uint32_t g = (n_words + 255) / 256;
+  if (g > 1024) g = 1024;
+  if (g < 1) g = 1;
+  hipLaunchKernelGGL(k_fill_u32, dim3(g), dim3(256), 0, stream, (uint32_t*)dst, v, n_words);
   return hipGetLastError();
 }
 

@@ -132,12 +132,16 @@ class DeviceModel:
         return out
 
     # ------------------------------------------------------------------ steps
-    def decode(self, tokens, positions, logits, out_tokens=None, out_ids=None, multilaunch=False, stream=None):
-        """Enqueue one decode step.  All tensors are device tensors."""
+    def decode(self, tokens, positions, logits, out_tokens=None, out_ids=None, multilaunch=False, stream=None,
+               noalloc=False):
+        """Enqueue one decode step.  All tensors are device tensors.
+        multilaunch: one launch per phase; noalloc: the allocation-free step
+        (scratch from the library's static array)."""
         torch = self.torch
         B = int(tokens.shape[0])
         s = stream if stream is not None else torch.cuda.current_stream(self.device)
-        fn = lib().md_decode_step_multilaunch if multilaunch else lib().md_decode_step
+        fn = (lib().md_decode_step_multilaunch if multilaunch else
+              lib().md_decode_step_noalloc if noalloc else lib().md_decode_step)
         check(fn(self.handle, ctypes.c_void_p(tokens.data_ptr()), ctypes.c_void_p(positions.data_ptr()),
                  ctypes.c_void_p(self.kv.data_ptr()), ctypes.c_void_p(logits.data_ptr()), B,
                  ctypes.c_void_p(out_tokens.data_ptr() if out_tokens is not None else 0),

@@ -152,6 +152,26 @@ md_status md_decode_step(md_model* m, const int32_t* tokens, const int32_t* posi
                          float* out_logits, int32_t batch, int32_t* out_tokens, int32_t* out_expert_ids,
                          void* hip_stream);
 
+/* md_decode_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments, kernels and results, but the step's scratch buffers
+ * (activations, partial results, sync counters, error word) come from a
+ * static device array of the library, 128 MiB per device, held from the
+ * library's load until the process ends, instead of the model's workspace
+ * (which still holds the layer table, expert pointers and rotary table
+ * written by md_init_model).  The call allocates nothing and frees nothing;
+ * it enqueues three small fill kernels (clearing the counters, error word and
+ * zero line the step relies on: the array keeps whatever the last call on
+ * this device left) and the megakernel.  Returns MD_ENOMEM, enqueuing
+ * nothing, when the model's step needs more scratch than the array holds
+ * (md_workspace_bytes(cfg) > 128 MiB).  Every call on a device shares that
+ * device's array: calls that overlap on one device (other streams, other
+ * models, other threads) race and their results are undefined.
+ * md_get_device_status reports this call's device errors like any step's. */
+md_status md_decode_step_noalloc(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv_cache,
+                                 float* out_logits, int32_t batch, int32_t* out_tokens, int32_t* out_expert_ids,
+                                 void* hip_stream);
+
 /* The same step as md_decode_step executed as one kernel launch per
  * operation (no megakernel): the baseline that exposes the inter-kernel
  * bubbles.  Same arguments and results. */

@@ -147,6 +147,7 @@ def test_null_model_and_bad_step_arguments():
     L = _lib.lib()
     assert L.md_decode_step(None, None, None, None, None, 1, None, None, None) == _lib.MD_EINVAL
     assert L.md_decode_step_multilaunch(None, None, None, None, None, 1, None, None, None) == _lib.MD_EINVAL
+    assert L.md_decode_step_noalloc(None, None, None, None, None, 1, None, None, None) == _lib.MD_EINVAL
     assert L.md_verify_step(None, None, None, None, None, None, None, None, 2, 8, None) == _lib.MD_EUNSUPPORTED
     assert L.md_verify_step(None, None, None, None, None, None, None, None, 1, 9, None) == _lib.MD_EINVAL
     assert L.md_verify_step(None, None, None, None, None, None, None, None, 1, 1, None) == _lib.MD_EINVAL

@@ -133,19 +133,32 @@ def traffic_record(fetch_csv: str, write_csv: str, workload: str, batch: int) ->
     return out
 
 
-def traffic_for(workload: str, batch: int):
-    """The recorded HBM bytes per launch for this workload and batch, or None
-    when there is no record or the kernel sources changed since."""
+def _traffic_records() -> List[Dict]:
     try:
         with open(TRAFFIC_JSON) as f:
             rec = json.load(f)
     except (OSError, ValueError):
-        return None
-    if rec.get("workload") != workload or rec.get("batch") != batch:
-        return None
-    if rec.get("kernel_sha256") != kernel_source_hash():
-        return None
-    return rec
+        return []
+    return rec.get("records", []) if isinstance(rec, dict) and "records" in rec else ([rec] if rec else [])
+
+
+def store_traffic(rec: Dict) -> None:
+    """Keep rec in traffic.json, replacing any record of its workload and batch."""
+    recs = [r for r in _traffic_records() if (r.get("workload"), r.get("batch")) != (rec["workload"], rec["batch"])]
+    recs.append(rec)
+    recs.sort(key=lambda r: (r["workload"], r["batch"]))
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump({"records": recs}, f, indent=1)
+
+
+def traffic_for(workload: str, batch: int):
+    """The recorded HBM bytes per launch for this workload and batch, or None
+    when there is no record or the kernel sources changed since."""
+    h = kernel_source_hash()
+    for rec in _traffic_records():
+        if rec.get("workload") == workload and rec.get("batch") == batch and rec.get("kernel_sha256") == h:
+            return rec
+    return None
 
 
 if __name__ == "__main__":
@@ -159,8 +172,7 @@ if __name__ == "__main__":
         wl = sys.argv[4] if len(sys.argv) > 4 else "dense_27b"
         b = int(sys.argv[5]) if len(sys.argv) > 5 else 1
         rec = traffic_record(sys.argv[2], sys.argv[3], wl, b)
-        with open(TRAFFIC_JSON, "w") as f:
-            json.dump(rec, f, indent=1)
+        store_traffic(rec)
         print(json.dumps(rec, indent=1))
     elif sys.argv[1] == "gaps":
         needle = sys.argv[3] if len(sys.argv) > 3 else "md_megakernel"

@@ -350,3 +350,18 @@ def test_long_chain_full_width(torch_cuda, B, steps, sampled):
             GU.compare_step(w, g, o, f"long chain B={B} step {s}")
             GU.compare_kv_rows(w, GU.kv_rows_dev(m, pos, B), kv_ref, pos, B)
         toks = [int(t) for t in o["next"]]
+
+
+@pytest.mark.parametrize("name,B", [("mini_moe", 3), ("mini_hybrid", 2)])
+def test_multilaunch_graph_replays_match_eager(torch_cuda, name, B):
+    """The multi-launch baseline captured in a HIP graph (two steps per
+    graph, one per counter bank): three replays, each with eager steps
+    between them, and the timed replays after them must all give the eager
+    multi-launch step's logits bitwise."""
+    import bench
+    w = WL.get(name)
+    m = _model(w)
+    print(f"case graph {name} B={B}", flush=True)
+    ms, ok = bench.time_multilaunch_graph(m, B, reps=4)
+    assert ok, f"{name}: a graph replay differs from the eager multi-launch step"
+    m.close()

@@ -53,3 +53,18 @@ def test_dispatch_gaps():
     assert abs(r["busy_us"] - 190.25) < 1e-9
     assert abs(r["idle_us"] - 10.05) < 1e-9
     assert abs(r["max_gap_us"] - 10.0) < 1e-9
+
+
+def test_traffic_records_per_workload_and_batch(tmp_path, monkeypatch):
+    """Records of several (workload, batch) pairs live side by side; storing
+    one replaces only the record of its own pair."""
+    path = tmp_path / "traffic.json"
+    monkeypatch.setattr(P, "TRAFFIC_JSON", str(path))
+    h = P.kernel_source_hash()
+    P.store_traffic({"workload": "dense_27b", "batch": 1, "kernel_sha256": h, "bytes": 1.0})
+    P.store_traffic({"workload": "hybrid_moe", "batch": 8, "kernel_sha256": h, "bytes": 2.0})
+    P.store_traffic({"workload": "dense_27b", "batch": 1, "kernel_sha256": h, "bytes": 3.0})
+    assert P.traffic_for("dense_27b", 1)["bytes"] == 3.0
+    assert P.traffic_for("hybrid_moe", 8)["bytes"] == 2.0
+    assert P.traffic_for("hybrid_moe", 1) is None
+    assert len(json.loads(path.read_text())["records"]) == 2

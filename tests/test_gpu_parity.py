@@ -72,6 +72,24 @@ def test_decode_step_matches_oracle(torch_cuda, name, B):
     print(f"  max|dlogit|/rms = {err:.2e}; cache entries 1 ulp apart: {n_ulp}")
 
 
+@pytest.mark.parametrize("B", [1, 5])
+def test_moe_without_shared_expert_matches_oracle(torch_cuda, B):
+    """A MoE model with no shared expert: every workgroup streams router rows
+    and every workgroup publishes them (the other layout of the router's
+    sync point), then the routed experts as usual."""
+    w = WL.mini_moe().replace(name="mini_moe_noshared", n_shared=0)
+    m = _model(w)
+    toks = synth.tokens(w, B)
+    pos = [max(w.context - 9 * b, 0) for b in range(B)]
+    print(f"case {w.name} B={B} pos={pos}", flush=True)
+    g = GU.run_gpu_step(m, toks, pos)
+    o, kv_ref = GU.run_oracle_step(w, toks, pos)
+    err = GU.compare_step(w, g, o, f"{w.name} B={B}")
+    GU.compare_kv_rows(w, m.kv_host(), kv_ref, pos, B)
+    print(f"  max|dlogit|/rms = {err:.2e}")
+    m.close()
+
+
 def test_zero_layer_weights_identity(torch_cuda):
     """Zeroed layer matrices: the residual stays the embedding row, so the
     logits equal the LM head applied to the normalised embedding."""

@@ -29,6 +29,7 @@ class MdConfig(ctypes.Structure):
         ("n_experts", I32), ("top_k", I32), ("expert_ffn", I32), ("n_shared", I32), ("shared_ffn", I32),
         ("norm_topk", I32),
         ("flags", I32),
+        ("kv_page", I32), ("kv_pages", I32),
     ]
 
 
@@ -42,7 +43,7 @@ EXPORTS = [
     "md_weight_count", "md_weight_info", "md_workspace_bytes", "md_kv_bytes", "md_init_model",
     "md_decode_step", "md_decode_step_multilaunch", "md_decode_step_noalloc", "md_verify_step", "md_get_device_status",
     "md_last_error", "md_free_model", "md_set_trace", "md_grid_size", "md_packed_bytes", "md_pack_weight",
-    "md_weight_layout",
+    "md_weight_layout", "md_decode_step_paged", "md_verify_step_paged", "md_kv_copy_pages", "md_kv_copy_slot",
 ]
 
 _lib = None
@@ -87,6 +88,14 @@ def lib():
         L.md_packed_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
         L.md_pack_weight.restype = I32
         L.md_pack_weight.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, P]
+        L.md_decode_step_paged.restype = I32
+        L.md_decode_step_paged.argtypes = [P, P, P, P, P, P, I32, P, P, P]
+        L.md_verify_step_paged.restype = I32
+        L.md_verify_step_paged.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, P]
+        L.md_kv_copy_pages.restype = I32
+        L.md_kv_copy_pages.argtypes = [P, P, P, P, I32, P]
+        L.md_kv_copy_slot.restype = I32
+        L.md_kv_copy_slot.argtypes = [P, P, I32, I32, P]
         L.md_free_model.restype = None
         L.md_free_model.argtypes = [P]
         _lib = L

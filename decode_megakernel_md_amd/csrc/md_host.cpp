@@ -19,6 +19,8 @@ hipError_t launch_multilaunch(const Params& p, const int* kinds, int grid, hipSt
 size_t scratch_bytes();
 hipError_t scratch_address(int dev, void** out);
 hipError_t launch_fill_u32(void* dst, uint32_t v, uint32_t n_words, hipStream_t stream);
+hipError_t launch_kv_copy(const Params& p, const int32_t* src, const int32_t* dst, int n, int src_slot, int dst_slot,
+                          hipStream_t stream);
 }  // namespace md
 
 using namespace md;
@@ -149,6 +151,20 @@ md_status validate(const md_config* c) {
   } else {
     return fail(MD_EINVAL, "attn_kind must be 0 or 1");
   }
+  if (c->kv_page != 0) {
+    if (c->kv_page < 32 || (c->kv_page & (c->kv_page - 1)))
+      return fail(MD_EINVAL, "kv_page must be 0 (contiguous caches) or a power of two >= 32");
+    if (c->max_ctx % c->kv_page) return fail(MD_EINVAL, "max_ctx must be a multiple of kv_page");
+    if (c->kv_pages < 1) return fail(MD_EINVAL, "a paged cache needs kv_pages >= 1");
+  } else if (c->kv_pages != 0) {
+    return fail(MD_EINVAL, "kv_pages must be 0 when kv_page is 0");
+  }
+  {
+    // an MLA layer's cache is read through one buffer resource (32-bit range)
+    const int64_t rows = c->kv_page ? (int64_t)c->kv_pages * c->kv_page : (int64_t)c->max_batch * c->max_ctx;
+    if (c->attn_kind == 1 && rows * (c->kv_lora + c->rope_dim) * 2 >= ((int64_t)1 << 32))
+      return fail(MD_EUNSUPPORTED, "an MLA layer's cache must stay below 4 GiB");
+  }
   if (c->hidden < 128) return fail(MD_EUNSUPPORTED, "hidden must be at least 128");
   if (c->attn_kind == 0 && c->n_q_heads * c->head_dim < 128)
     return fail(MD_EUNSUPPORTED, "n_q_heads * head_dim must be at least 128");
@@ -258,16 +274,22 @@ WsLayout ws_layout(const md_config* c) {
   return w;
 }
 
+// Attention caches are n_pages pages of cap positions: one page per sequence
+// slot (contiguous) or the configured pool (paged).
+size_t kv_n_pages(const md_config* c) { return c->kv_page ? (size_t)c->kv_pages : (size_t)c->max_batch; }
+size_t kv_page_cap(const md_config* c) { return c->kv_page ? (size_t)c->kv_page : (size_t)c->max_ctx; }
+
 std::vector<size_t> kv_offsets(const md_config* c, size_t* total) {
   std::vector<size_t> off;
   size_t o = 0;
+  const size_t np = kv_n_pages(c), cap = kv_page_cap(c);
   for (int l = 0; l < c->n_layers; ++l) {
     off.push_back(o);
     size_t n;
     if (c->attn_kind == 0)
-      n = 2 * 2 * (size_t)c->max_batch * c->n_kv_heads * c->max_ctx * c->head_dim;
+      n = 2 * 2 * np * c->n_kv_heads * cap * c->head_dim;
     else if (is_mla(c, l))
-      n = 2 * (size_t)c->max_batch * c->max_ctx * (c->kv_lora + c->rope_dim);
+      n = 2 * np * cap * (c->kv_lora + c->rope_dim);
     else
       n = 4 * (size_t)c->max_batch * c->kda_heads * c->kda_dk * c->kda_dv;
     o = align256(o + n);
@@ -464,15 +486,28 @@ md_status md_init_model(const md_config* cfg, const void* const* weights, size_t
   return MD_OK;
 }
 
+// The kernel parameters of one step.  block_table: the step's page map (paged
+// caches only: a paged model needs one, a contiguous model takes none).
 static md_status fill_params(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv,
-                             float* out_logits, int32_t batch, int32_t* out_tokens, int32_t* out_ids, Params& p) {
+                             float* out_logits, int32_t batch, int32_t* out_tokens, int32_t* out_ids, Params& p,
+                             const int32_t* block_table = nullptr) {
   if (!m) return fail(MD_EINVAL, "model is NULL");
   const md_config* c = &m->cfg;
   if (batch < 1 || batch > c->max_batch) return fail(MD_EINVAL, "batch %d outside [1, %d]", batch, c->max_batch);
   if (!tokens || !positions || !kv || !out_logits) return fail(MD_EINVAL, "tokens, positions, kv_cache and out_logits must be non-NULL");
   if (((uintptr_t)kv & 255) || ((uintptr_t)out_logits & 3) || ((uintptr_t)tokens & 3) || ((uintptr_t)positions & 3))
     return fail(MD_EINVAL, "misaligned pointer (kv_cache needs 256-byte alignment)");
+  if (c->kv_page && !block_table)
+    return fail(MD_EINVAL, "the model's caches are paged (kv_page %d): use the _paged step with a block table", c->kv_page);
+  if (!c->kv_page && block_table) return fail(MD_EINVAL, "a block table needs a paged model (kv_page > 0)");
+  if ((uintptr_t)block_table & 3) return fail(MD_EINVAL, "misaligned block table");
   memset(&p, 0, sizeof p);
+  p.bt = block_table;
+  p.n_pages = (int)kv_n_pages(c);
+  p.pg_cap = (int)kv_page_cap(c);
+  p.bt_stride = c->kv_page ? c->max_ctx / c->kv_page : 0;
+  p.pg_shift = 0;
+  while (c->kv_page && (1 << p.pg_shift) < c->kv_page) ++p.pg_shift;
   p.ml_phase = -1;
   const WsLayout& w = m->lay;
   p.layers = (const LayerDesc*)(m->ws + w.layers);
@@ -589,16 +624,17 @@ md_status md_decode_step_multilaunch(md_model* m, const int32_t* tokens, const i
   return MD_OK;
 }
 
-md_status md_verify_step(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv_cache,
-                         float* out_logits, int32_t* out_accept_len, int32_t* out_next_token,
-                         int32_t* out_expert_ids, int32_t batch, int32_t n_tok, void* hip_stream) {
+static md_status verify_step(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv_cache,
+                             const int32_t* block_table, float* out_logits, int32_t* out_accept_len,
+                             int32_t* out_next_token, int32_t* out_expert_ids, int32_t batch, int32_t n_tok,
+                             void* hip_stream) {
   if (batch != 1) return fail(MD_EUNSUPPORTED, "verify runs one sequence per launch (batch must be 1)");
   if (n_tok < 2 || n_tok > MAXB_) return fail(MD_EINVAL, "n_tok %d outside [2, %d]", n_tok, MAXB_);
   if (!out_accept_len || !out_next_token) return fail(MD_EINVAL, "out_accept_len and out_next_token must be non-NULL");
   if (((uintptr_t)out_accept_len & 3) || ((uintptr_t)out_next_token & 3)) return fail(MD_EINVAL, "misaligned pointer");
   Params p;
   // the n_tok rows of the one sequence travel as the step's token rows
-  md_status st = fill_params(m, tokens, positions, kv_cache, out_logits, 1, nullptr, out_expert_ids, p);
+  md_status st = fill_params(m, tokens, positions, kv_cache, out_logits, 1, nullptr, out_expert_ids, p, block_table);
   if (st != MD_OK) return st;
   const md_config* c = &m->cfg;
   p.B = n_tok;
@@ -616,6 +652,91 @@ md_status md_verify_step(md_model* m, const int32_t* tokens, const int32_t* posi
   hipError_t e = launch_megakernel(p, m->grid, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(MD_EHIP, "megakernel launch: %s", hipGetErrorString(e));
   m->bank ^= 1;
+  m->last_stream = (hipStream_t)hip_stream;
+  m->last_err_word = p.err;
+  return MD_OK;
+}
+
+md_status md_verify_step(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv_cache,
+                         float* out_logits, int32_t* out_accept_len, int32_t* out_next_token,
+                         int32_t* out_expert_ids, int32_t batch, int32_t n_tok, void* hip_stream) {
+  return verify_step(m, tokens, positions, kv_cache, nullptr, out_logits, out_accept_len, out_next_token,
+                     out_expert_ids, batch, n_tok, hip_stream);
+}
+
+md_status md_decode_step_paged(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv_pool,
+                               const int32_t* block_table, float* out_logits, int32_t batch, int32_t* out_tokens,
+                               int32_t* out_expert_ids, void* hip_stream) {
+  if (!block_table) return fail(MD_EINVAL, "block_table must be non-NULL");
+  Params p;
+  md_status st = fill_params(m, tokens, positions, kv_pool, out_logits, batch, out_tokens, out_expert_ids, p,
+                             block_table);
+  if (st != MD_OK) return st;
+  p.bank = m->bank;
+  hipError_t e = launch_megakernel(p, m->grid, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(MD_EHIP, "megakernel launch: %s", hipGetErrorString(e));
+  m->bank ^= 1;
+  m->last_stream = (hipStream_t)hip_stream;
+  m->last_err_word = p.err;
+  return MD_OK;
+}
+
+md_status md_verify_step_paged(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv_pool,
+                               const int32_t* block_table, float* out_logits, int32_t* out_accept_len,
+                               int32_t* out_next_token, int32_t* out_expert_ids, int32_t batch, int32_t n_tok,
+                               void* hip_stream) {
+  if (!block_table) return fail(MD_EINVAL, "block_table must be non-NULL");
+  return verify_step(m, tokens, positions, kv_pool, block_table, out_logits, out_accept_len, out_next_token,
+                     out_expert_ids, batch, n_tok, hip_stream);
+}
+
+// Parameters of a copy: the model's layer table and cache geometry only.
+static md_status copy_params(md_model* m, void* kv, Params& p) {
+  if (!m) return fail(MD_EINVAL, "model is NULL");
+  if (!kv || ((uintptr_t)kv & 255)) return fail(MD_EINVAL, "kv must be non-NULL and 256-byte aligned");
+  const md_config* c = &m->cfg;
+  memset(&p, 0, sizeof p);
+  p.layers = (const LayerDesc*)(m->ws + m->lay.layers);
+  p.n_layers = c->n_layers;
+  p.kv = (uint8_t*)kv;
+  p.nkv = c->n_kv_heads;
+  p.hd = c->head_dim;
+  p.kda_h = c->kda_heads;
+  p.kda_dk = c->kda_dk;
+  p.kda_dv = c->kda_dv;
+  p.n_pages = (int)kv_n_pages(c);
+  p.pg_cap = (int)kv_page_cap(c);
+  p.bt_stride = c->kv_page ? c->max_ctx / c->kv_page : 0;  // > 0: the caches are paged
+  p.err = (int*)(m->ws + m->lay.err);
+  return MD_OK;
+}
+
+md_status md_kv_copy_pages(md_model* m, void* kv_pool, const int32_t* src_pages, const int32_t* dst_pages,
+                           int32_t n, void* hip_stream) {
+  Params p;
+  md_status st = copy_params(m, kv_pool, p);
+  if (st != MD_OK) return st;
+  if (!m->cfg.kv_page) return fail(MD_EINVAL, "page copies need a paged model (kv_page > 0)");
+  if (n < 0) return fail(MD_EINVAL, "n must be >= 0");
+  if (n > 0 && (!src_pages || !dst_pages)) return fail(MD_EINVAL, "src_pages and dst_pages must be non-NULL");
+  if (((uintptr_t)src_pages & 3) || ((uintptr_t)dst_pages & 3)) return fail(MD_EINVAL, "misaligned page list");
+  hipError_t e = launch_kv_copy(p, src_pages, dst_pages, n, 0, 0, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(MD_EHIP, "page copy launch: %s", hipGetErrorString(e));
+  m->last_stream = (hipStream_t)hip_stream;
+  m->last_err_word = p.err;
+  return MD_OK;
+}
+
+md_status md_kv_copy_slot(md_model* m, void* kv, int32_t src_slot, int32_t dst_slot, void* hip_stream) {
+  Params p;
+  md_status st = copy_params(m, kv, p);
+  if (st != MD_OK) return st;
+  const int bm = m->cfg.max_batch;
+  if (src_slot < 0 || src_slot >= bm || dst_slot < 0 || dst_slot >= bm)
+    return fail(MD_EINVAL, "slots must be in [0, %d)", bm);
+  if (src_slot == dst_slot) return MD_OK;
+  hipError_t e = launch_kv_copy(p, nullptr, nullptr, 1, src_slot, dst_slot, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(MD_EHIP, "slot copy launch: %s", hipGetErrorString(e));
   m->last_stream = (hipStream_t)hip_stream;
   m->last_err_word = p.err;
   return MD_OK;
@@ -640,9 +761,10 @@ md_status md_get_device_status(md_model* m) {
     if (c != hipSuccess)
       return fail(MD_EHIP, "device error 0x%x, and resetting the error word and counters failed: %s", err,
                   hipGetErrorString(c));
-    return fail(MD_EDEVICE, "device error 0x%x:%s%s%s%s", err, (err & MDE_WATCHDOG) ? " sync wait exceeded its bound" : "",
+    return fail(MD_EDEVICE, "device error 0x%x:%s%s%s%s%s", err, (err & MDE_WATCHDOG) ? " sync wait exceeded its bound" : "",
                 (err & MDE_TOKEN) ? " token out of range" : "", (err & MDE_POSITION) ? " position out of range" : "",
-                (err & MDE_CAPACITY) ? " a phase's work exceeds the per-workgroup tables (shape too large for this grid)" : "");
+                (err & MDE_CAPACITY) ? " a phase's work exceeds the per-workgroup tables (shape too large for this grid)" : "",
+                (err & MDE_PAGE) ? " page id out of range" : "");
   }
   return MD_OK;
 }

@@ -230,6 +230,34 @@ __device__ __forceinline__ int row_pos(KParams& pk, int r) {
   return pos;
 }
 
+// Where position pos of sequence slot s sits in a layer's attention cache:
+// its page and the row within the page.  A contiguous cache has one page per
+// slot; a paged one looks the page up in the block table (s and pos uniform
+// across the wave: one scalar load).  A page id outside the pool sets the
+// device error word and reads page 0 instead (the step's outputs are then
+// undefined, but no access leaves the cache).
+struct KvLoc {
+  int page, r;
+};
+__device__ __forceinline__ KvLoc kv_loc(KParams& pk, int s, int pos) {
+  PARAMS;
+  KvLoc l;
+  if (p.bt == nullptr) {
+    l.page = s;
+    l.r = pos;
+    return l;
+  }
+  const int idx = __builtin_amdgcn_readfirstlane(s * p.bt_stride + (pos >> p.pg_shift));
+  int pg = ((const __attribute__((address_space(4))) int32_t*)(uintptr_t)p.bt)[idx];
+  if ((unsigned)pg >= (unsigned)p.n_pages) {
+    set_err(p, MDE_PAGE);
+    pg = 0;
+  }
+  l.page = pg;
+  l.r = pos & (p.pg_cap - 1);
+  return l;
+}
+
 // ===================================================================== GEMV
 // Y[r][t] = sum_k W[r][k] * U[t][k] for this workgroup's rows of a list of
 // matrices (up to MAXMAT per phase: q/k/v, the gate and up of every expert a
@@ -1088,23 +1116,25 @@ struct KVBlock {
   i32x4 v[HD / 16];             // the V tile: HD/16 slices of 16 dims x 32 positions
 };
 
-// Block at blk (a multiple of 32) of a wave share ending at w1.  K is
-// row-major [pos][HD]; V is the tile (blk/32) of [tile][HD][32].
+// Block at blk (a multiple of 32) of a wave share ending at w1: its 32 K
+// rows (row-major [32][HD]) at kb and its V tile ([HD][32]) at vb.
 template <int HD, int CP>
-__device__ __forceinline__ void load_block(KVBlock<HD>& r, rsrc_t krs, rsrc_t vrs, int blk, int w1, int lane) {
+__device__ __forceinline__ void load_block(KVBlock<HD>& r, const uint16_t* kb, const uint16_t* vb, int blk, int w1,
+                                           int lane) {
   const int m = lane & 15, g = lane >> 4;
+  const rsrc_t krs = make_rsrc_u(kb, 32 * HD * 2), vrs = make_rsrc_u(vb, 32 * HD * 2);
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
     const int prow = blk + 8 * (m >> 2) + 4 * tt + (m & 3);
 #pragma unroll
     for (int s = 0; s < HD / 32; ++s) {
-      uint32_t off = (prow < w1) ? (uint32_t)(prow * HD + s * 32 + g * 8) * 2u : OOB;
+      uint32_t off = (prow < w1) ? (uint32_t)((prow - blk) * HD + s * 32 + g * 8) * 2u : OOB;
       r.k[tt][s] = ld_x4<CP>(krs, off);
     }
   }
 #pragma unroll
   for (int q = 0; q < HD / 16; ++q) {
-    uint32_t off = blk < w1 ? (uint32_t)(blk * HD + (q * 16 + m) * 32 + g * 8) * 2u : OOB;
+    uint32_t off = blk < w1 ? (uint32_t)((q * 16 + m) * 32 + g * 8) * 2u : OOB;
     r.v[q] = ld_x4<CP>(vrs, off);
   }
 }
@@ -1122,9 +1152,12 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float x0, float x1) {
 // One wave's share [w0, w1) of a task.  Its first two blocks (w0, w0 + 32)
 // are in flight in ba, bb on entry; each block used is refilled two blocks
 // ahead.  Leaves the wave's (max, sum, o) per head in ASM.wm/wl/wo[wv].
+struct AttnTask;
 template <int HD, int CP>
-__device__ __forceinline__ void attn_wave(KVBlock<HD>& ba, KVBlock<HD>& bb, rsrc_t krs, rsrc_t vrs, int w0, int w1,
-                                          int gs) {
+__device__ __forceinline__ void load_kv_block(KParams& pk, KVBlock<HD>& r, const AttnTask& t, int blk, int lane);
+template <int HD, int CP>
+__device__ __forceinline__ void attn_wave(KParams& pk, KVBlock<HD>& ba, KVBlock<HD>& bb, const AttnTask& t, int w0,
+                                          int w1, int gs) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int nn = lane & 15, hh = nn >> 1, pp = nn & 1, g = lane >> 4;
   bf16x8 qb[HD / 32];
@@ -1212,10 +1245,10 @@ __device__ __forceinline__ void attn_wave(KVBlock<HD>& ba, KVBlock<HD>& bb, rsrc
   for (int blk = w0; blk < w1; blk += 64) {
     block(ba, blk);
     if (blk + 32 >= w1) break;
-    load_block<HD, CP>(ba, krs, vrs, blk + 64, w1, lane);
+    load_kv_block<HD, CP>(pk, ba, t, blk + 64, lane);
     block(bb, blk + 32);
     if (blk + 64 >= w1) break;
-    load_block<HD, CP>(bb, krs, vrs, blk + 96, w1, lane);
+    load_kv_block<HD, CP>(pk, bb, t, blk + 96, lane);
   }
   // head hh's output = column 2hh + column 2hh+1; lane holds dims 16q + 4g + i
   if (hh < gs) {
@@ -1244,10 +1277,12 @@ __device__ __noinline__ void phase_gqa_kv_write(KParams& pk, int l_layer) {
   for (int task = blockIdx.x; task < p.B * p.nkv; task += gridDim.x) {
     const int g = task % p.nkv, b = task / p.nkv;
     const int pos = row_pos(p, b);
-    uint16_t* kc = (uint16_t*)(p.kv + L.kv_off) + (size_t)(row_seq(p, b) * p.nkv + g) * p.max_ctx * hd;
-    uint16_t* vc = kc + (size_t)p.max_batch * p.nkv * p.max_ctx * hd;
-    rsrc_t krs = make_rsrc_u(kc + (size_t)pos * hd, hd * 2);
-    rsrc_t vrs = make_rsrc_u(vc + (size_t)(pos & ~31) * hd, hd * 64);  // the V tile holding pos
+    const KvLoc l = kv_loc(p, row_seq(p, b), pos);
+    const size_t pstride = (size_t)p.nkv * p.pg_cap * hd;
+    uint16_t* kc = (uint16_t*)(p.kv + L.kv_off) + (size_t)l.page * pstride + (size_t)g * p.pg_cap * hd;
+    uint16_t* vc = kc + (size_t)p.n_pages * pstride;
+    rsrc_t krs = make_rsrc_u(kc + (size_t)l.r * hd, hd * 2);
+    rsrc_t vrs = make_rsrc_u(vc + (size_t)(l.r & ~31) * hd, hd * 64);  // the V tile holding pos
     for (int i = threadIdx.x; i < hd / 2; i += NT) {
       int colk = p.nq * hd + g * hd;
       float a = ld_f32(wr, p.off_qkv + (uint32_t)(b * nqkv + colk + i) * 4u);
@@ -1259,7 +1294,7 @@ __device__ __noinline__ void phase_gqa_kv_write(KParams& pk, int l_layer) {
     }
     for (int i = threadIdx.x; i < hd; i += NT) {
       int colv = (p.nq + p.nkv) * hd + g * hd;
-      st_u16(vrs, (uint32_t)(i * 32 + (pos & 31)) * 2u,
+      st_u16(vrs, (uint32_t)(i * 32 + (l.r & 31)) * 2u,
              bf16_rne(ld_f32(wr, p.off_qkv + (uint32_t)(b * nqkv + colv + i) * 4u)));
     }
   }
@@ -1272,8 +1307,10 @@ __device__ __noinline__ void phase_gqa_kv_write(KParams& pk, int l_layer) {
 // whole 32-position tiles (the last one ragged); waves split a chunk's tiles.
 struct AttnTask {
   int b, g, c, pos, n, a0, a1, w0, w1;
-  const uint16_t* kc;
-  const uint16_t* vc;
+  int s;                // the sequence's cache slot
+  const uint16_t* kh;   // K rows of kv head g in page 0 (page q: + q * pstride)
+  const uint16_t* vh;   // V tiles of kv head g in page 0
+  size_t pstride;       // elements per page (all kv heads)
 };
 __device__ __forceinline__ AttnTask attn_task(KParams& pk, int l_layer, int task) {
   PARAMS;
@@ -1292,9 +1329,33 @@ __device__ __forceinline__ AttnTask attn_task(KParams& pk, int l_layer, int task
   t.w0 = t.a0 + 32 * (nt * wv / NW);
   const int e = t.a0 + 32 * (nt * (wv + 1) / NW);
   t.w1 = e < t.a1 ? e : t.a1;
-  t.kc = (const uint16_t*)(p.kv + L.kv_off) + (size_t)(row_seq(p, t.b) * p.nkv + t.g) * p.max_ctx * hd;
-  t.vc = t.kc + (size_t)p.max_batch * p.nkv * p.max_ctx * hd;
+  t.s = row_seq(p, t.b);
+  t.pstride = (size_t)p.nkv * p.pg_cap * hd;
+  t.kh = (const uint16_t*)(p.kv + L.kv_off) + (size_t)t.g * p.pg_cap * hd;
+  t.vh = t.kh + (size_t)p.n_pages * t.pstride;
   return t;
+}
+
+// K rows and V tile of block blk (a multiple of 32) of a task's sequence:
+// one page holds the whole block.  Blocks past the wave's share load nothing
+// (every offset is out of range) and look nothing up.
+template <int HD>
+__device__ __forceinline__ void kv_block_ptrs(KParams& pk, const AttnTask& t, int blk, const uint16_t*& kb,
+                                              const uint16_t*& vb) {
+  kb = t.kh;
+  vb = t.vh;
+  if (blk < t.w1) {
+    const KvLoc l = kv_loc(pk, t.s, blk);
+    const size_t o = (size_t)l.page * t.pstride + (size_t)l.r * HD;
+    kb += o;
+    vb += o;
+  }
+}
+template <int HD, int CP>
+__device__ __forceinline__ void load_kv_block(KParams& pk, KVBlock<HD>& r, const AttnTask& t, int blk, int lane) {
+  const uint16_t *kb, *vb;
+  kv_block_ptrs<HD>(pk, t, blk, kb, vb);
+  load_block<HD, CP>(r, kb, vb, blk, t.w1, lane);
 }
 
 // GQA decode attention.  Each task's partial (max, sum, o) per head goes to
@@ -1320,14 +1381,10 @@ __device__ __forceinline__ void attn_phase(KParams& pk, int l_layer, int layer, 
   const float scale = 1.0f / sqrtf((float)HD);
   KVBlock<HD> ba, bb;
   AttnTask t;
-  rsrc_t krs, vrs;
   auto start = [&](int task) __attribute__((always_inline)) {
     t = attn_task(p, l_layer, task);
-    const int nt = (t.n + 31) >> 5;
-    krs = make_rsrc_u(t.kc, (uint32_t)((size_t)t.n * HD * 2));
-    vrs = make_rsrc_u(t.vc, (uint32_t)((size_t)nt * 32 * HD * 2));
-    load_block<HD, CP>(ba, krs, vrs, t.w0, t.w1, lane);
-    load_block<HD, CP>(bb, krs, vrs, t.w0 + 32, t.w1, lane);
+    load_kv_block<HD, CP>(p, ba, t, t.w0, lane);
+    load_kv_block<HD, CP>(p, bb, t, t.w0 + 32, lane);
   };
   if (!VERIFY && (int)blockIdx.x < ntask) start(blockIdx.x);
   wait_point(p, wait_idx);
@@ -1348,8 +1405,10 @@ __device__ __forceinline__ void attn_phase(KParams& pk, int l_layer, int layer, 
     // (and writes it to the cache; nothing reads it back in this step)
     const bool newrow = !VERIFY && c == C - 1;
     if (newrow) {
-      uint16_t* kc = const_cast<uint16_t*>(t.kc);
-      uint16_t* vt = const_cast<uint16_t*>(t.vc) + (size_t)(pos & ~31) * HD + (pos & 31);  // V tile of pos
+      const KvLoc nl = kv_loc(p, t.s, pos);
+      const size_t po = (size_t)nl.page * t.pstride;
+      uint16_t* kc = const_cast<uint16_t*>(t.kh) + po + (size_t)nl.r * HD;                          // K row of pos
+      uint16_t* vt = const_cast<uint16_t*>(t.vh) + po + (size_t)(nl.r & ~31) * HD + (nl.r & 31);  // V tile of pos
       for (int i = threadIdx.x; i < HD / 2; i += NT) {
         int colk = p.nq * HD + g * HD;
         float a = ld_f32(wr, p.off_qkv + (uint32_t)(b * nqkv + colk + i) * 4u);
@@ -1357,8 +1416,8 @@ __device__ __forceinline__ void attn_phase(KParams& pk, int l_layer, int layer, 
         float cs, sn;
         rope_cs(p, pos, i, cs, sn);
         uint16_t k0 = bf16_rne(a * cs - bk * sn), k1 = bf16_rne(a * sn + bk * cs);
-        kc[(size_t)pos * HD + i] = k0;
-        kc[(size_t)pos * HD + i + HD / 2] = k1;
+        kc[i] = k0;
+        kc[i + HD / 2] = k1;
         sm.knew[i] = bf16_f32(k0);
         sm.knew[i + HD / 2] = bf16_f32(k1);
       }
@@ -1380,7 +1439,7 @@ __device__ __forceinline__ void attn_phase(KParams& pk, int l_layer, int layer, 
       }
     }
     sub_stamp(p, 0);
-    attn_wave<HD, CP>(ba, bb, krs, vrs, t.w0, t.w1, gs);
+    attn_wave<HD, CP>(p, ba, bb, t, t.w0, t.w1, gs);
     __syncthreads();
     sub_stamp(p, 3);
     // this task's partial: (m, l) in part_ml[b][head][c]; o in part_o[b][head][c][hd]
@@ -1809,7 +1868,8 @@ __device__ void mla_cache_row(KParams& pk, int l_layer, int b) {
   __syncthreads();
   float tot = red[0] + red[1] + red[2] + red[3];
   float inv = 1.0f / sqrtf(tot / (float)MLA_KL + p.eps);
-  uint16_t* row = (uint16_t*)(p.kv + L.kv_off) + ((size_t)row_seq(p, b) * p.max_ctx + pos) * MLA_QA;
+  const KvLoc l = kv_loc(p, row_seq(p, b), pos);
+  uint16_t* row = (uint16_t*)(p.kv + L.kv_off) + ((size_t)l.page * p.pg_cap + l.r) * MLA_QA;
   rsrc_t cr = make_rsrc_u(row, MLA_QA * 2);
   for (int i = threadIdx.x; i < MLA_KL; i += NT) st_u16(cr, (uint32_t)i * 2u, bf16_rne(bf16_f32(L.mla_kvnorm[i]) * (c[i] * inv)));
   for (int i = threadIdx.x; i < MLA_RD / 2; i += NT) {
@@ -1954,13 +2014,25 @@ struct MlaSmem {
 };
 
 // Thread tid loads chunk c16 = tid/32 + 8k (16 bytes) of row tid%32, k < 9;
-// rows past the chunk end are loaded as zeros.
-__device__ __forceinline__ void mla_load_block(i32x4 (&pf)[9], rsrc_t crs, int blk, int a1) {
+// rows past the chunk end are loaded as zeros.  crs covers the layer's whole
+// cache; the block's 32 rows of sequence slot sq lie in at most two pages.
+__device__ __forceinline__ void mla_load_block(KParams& pk, i32x4 (&pf)[9], rsrc_t crs, int sq, int blk, int a1) {
+  PARAMS;
   const int rr = threadIdx.x & 31, t = blk + rr;
+  const KvLoc l0 = kv_loc(p, sq, blk);
+  KvLoc l1 = l0;
+  const int last = blk + 31 < a1 ? blk + 31 : a1 - 1;  // the block's last row in the chunk (a partial block too)
+  if (p.bt != nullptr && (last >> p.pg_shift) != (blk >> p.pg_shift)) l1 = kv_loc(p, sq, last);
+  // this thread's row: contiguous, row t of page sq; paged, row t % pg_cap of
+  // the first page or, past its end, of the second
+  const bool second = p.bt != nullptr && (t >> p.pg_shift) != (blk >> p.pg_shift);
+  const int pg = second ? l1.page : l0.page;
+  const int r = p.bt != nullptr ? (t & (p.pg_cap - 1)) : t;
+  const uint32_t row = (uint32_t)pg * (uint32_t)p.pg_cap + (uint32_t)r;
 #pragma unroll
   for (int k = 0; k < 9; ++k) {
     const int c16 = (threadIdx.x >> 5) + 8 * k;
-    pf[k] = ld_x4<CP_SC1>(crs, t < a1 ? (uint32_t)(t * MLA_QA + c16 * 8) * 2u : OOB);
+    pf[k] = ld_x4<CP_SC1>(crs, t < a1 ? (row * MLA_QA + c16 * 8) * 2u : OOB);
   }
 }
 // Row-major copy, and the transposed copy of the latent chunks (k < 8): the
@@ -2006,10 +2078,10 @@ __device__ __forceinline__ void phase_mla_attn(KParams& pk, int l_layer) {
     const int n = pos + 1;
     const int P = (n + C - 1) / C;
     const int a0 = c * P < n ? c * P : n, a1 = (c + 1) * P < n ? (c + 1) * P : n;
-    const uint16_t* cache = (const uint16_t*)(p.kv + L.kv_off) + (size_t)row_seq(p, b) * p.max_ctx * MLA_QA;
-    rsrc_t crs = make_rsrc_u(cache, (uint32_t)((size_t)n * MLA_QA * 2));
+    const int sq = row_seq(p, b);
+    rsrc_t crs = make_rsrc_u(p.kv + L.kv_off, (uint32_t)((size_t)p.n_pages * p.pg_cap * MLA_QA * 2));
     i32x4 pf[9];
-    if (a0 < a1) mla_load_block(pf, crs, a0, a1);
+    if (a0 < a1) mla_load_block(p, pf, crs, sq, a0, a1);
     // this wave's heads' absorbed queries as hi/lo B operands
     bf16x8 qb[MLA_KS];
     {
@@ -2040,7 +2112,7 @@ __device__ __forceinline__ void phase_mla_attn(KParams& pk, int l_layer) {
     __syncthreads();
     for (int blk = a0; blk < a1; blk += 32) {
       const bool more = blk + 32 < a1;
-      if (more) mla_load_block(pf, crs, blk + 32, a1);
+      if (more) mla_load_block(p, pf, crs, sq, blk + 32, a1);
       // scores of 32 positions x this wave's 8 heads
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -2857,6 +2929,59 @@ hipError_t launch_multilaunch(const Params& p, const int* kinds, int grid, hipSt
   }
   go(-1, PH_LMHEAD, grid);
   go(-1, PH_ARGMAX, grid);  // workgroup 0 reduces all grid candidates
+  return hipGetLastError();
+}
+
+// ===================================================================== KV movement
+// Copies between attention-cache pages and between sequence slots, for
+// callers that fork a sequence or move its cache (copy-on-write of a shared
+// last page, prefix reuse).  Block (i, l) copies item i of layer l with
+// 16-byte loads and stores.
+//   pages (src, dst non-null): page src[i] -> dst[i] of every GQA layer (its
+//     K page and its V page) and every MLA layer; ids outside the pool set
+//     the error word and are skipped;
+//   slot (src, dst null): slot src_slot -> dst_slot of every delta-rule
+//     layer's state and, where the attention caches are contiguous (one page
+//     per slot; bt_stride == 0), of every GQA and MLA layer too.
+__device__ __forceinline__ void copy_bytes(uint8_t* dst, const uint8_t* src, size_t n) {
+  for (size_t i = (size_t)threadIdx.x * 16; i < n; i += (size_t)blockDim.x * 16)
+    *(i32x4*)(dst + i) = *(const i32x4*)(src + i);
+}
+
+__global__ void k_kv_copy(Params p, const int32_t* __restrict__ src, const int32_t* __restrict__ dst, int src_slot,
+                          int dst_slot) {
+  const int i = blockIdx.x, l = blockIdx.y;
+  const LayerDesc& L = p.layers[l];
+  uint8_t* base = p.kv + L.kv_off;
+  const bool pages = src != nullptr;
+  if (L.kind == LK_KDA) {
+    if (pages) return;
+    const size_t sb = (size_t)p.kda_h * p.kda_dk * p.kda_dv * 4;
+    copy_bytes(base + (size_t)dst_slot * sb, base + (size_t)src_slot * sb, sb);
+    return;
+  }
+  if (!pages && p.bt_stride > 0) return;  // paged: the block table maps the slot's pages
+  const int a = pages ? src[i] : src_slot, b = pages ? dst[i] : dst_slot;
+  if ((unsigned)a >= (unsigned)p.n_pages || (unsigned)b >= (unsigned)p.n_pages) {
+    if (threadIdx.x == 0) __hip_atomic_fetch_or(p.err, (int)MDE_PAGE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (a == b) return;
+  if (L.kind == LK_GQA) {
+    const size_t pb = (size_t)p.nkv * p.pg_cap * p.hd * 2;
+    uint8_t* vbase = base + (size_t)p.n_pages * pb;
+    copy_bytes(base + (size_t)b * pb, base + (size_t)a * pb, pb);
+    copy_bytes(vbase + (size_t)b * pb, vbase + (size_t)a * pb, pb);
+  } else {
+    const size_t pb = (size_t)p.pg_cap * 576 * 2;
+    copy_bytes(base + (size_t)b * pb, base + (size_t)a * pb, pb);
+  }
+}
+
+hipError_t launch_kv_copy(const Params& p, const int32_t* src, const int32_t* dst, int n, int src_slot, int dst_slot,
+                          hipStream_t stream) {
+  if (n <= 0 || p.n_layers <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_kv_copy, dim3(n, p.n_layers), dim3(256), 0, stream, p, src, dst, src_slot, dst_slot);
   return hipGetLastError();
 }
 

@@ -5,7 +5,7 @@
 namespace md {
 
 // device error bits (md_get_device_status)
-enum : int { MDE_WATCHDOG = 1, MDE_TOKEN = 2, MDE_POSITION = 4, MDE_CAPACITY = 8 };
+enum : int { MDE_WATCHDOG = 1, MDE_TOKEN = 2, MDE_POSITION = 4, MDE_CAPACITY = 8, MDE_PAGE = 16 };
 
 enum LayerKind : int { LK_GQA = 0, LK_MLA = 1, LK_KDA = 2 };
 
@@ -56,6 +56,13 @@ struct Params {
   const int32_t* tokens;
   const int32_t* positions;
   uint8_t* kv;
+  // Attention-cache addressing.  A GQA or MLA layer's cache is n_pages pages
+  // of pg_cap positions.  Contiguous caches have one page per sequence slot
+  // (n_pages = max_batch, pg_cap = max_ctx, bt = null); paged caches
+  // (pg_cap = 1 << pg_shift) find position pos of sequence s in page
+  // bt[s * bt_stride + (pos >> pg_shift)], row pos & (pg_cap - 1).
+  const int32_t* bt;
+  int bt_stride, pg_cap, pg_shift, n_pages;
   float* logits;
   int32_t* out_tokens;
   int32_t* out_ids;

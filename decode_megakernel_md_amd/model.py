@@ -11,7 +11,7 @@ from typing import Dict, Optional
 import numpy as np
 
 import synth
-from synth.workloads import V_TILE, Workload, kv_layout, tensor_inventory
+from synth.workloads import V_TILE, Workload, kv_layout, kv_pool_layout, tensor_inventory
 
 from . import _lib
 from ._lib import check, config_from, lib
@@ -33,9 +33,17 @@ class DeviceModel:
     """One model instance on one GPU.
 
     overrides: optional {tensor name: uint16 host array} replacing drawn
-    weights (used by tests that pin special cases)."""
+    weights (used by tests that pin special cases).
 
-    def __init__(self, w: Workload, device: str = "cuda:0", overrides: Optional[Dict[str, np.ndarray]] = None):
+    Paged caches (w.kv_page > 0): self.kv is the page pool and self.bt the
+    block table (int32 [max_batch][max_ctx / kv_page], device); block_table
+    gives its initial contents (default: slot s, page j -> s * (max_ctx /
+    kv_page) + j).  The seeded synthetic cache of every slot is drawn in the
+    contiguous layout and scattered into the pages the table names; pages
+    no slot maps are filled with NaN, so that a read of a wrong page shows."""
+
+    def __init__(self, w: Workload, device: str = "cuda:0", overrides: Optional[Dict[str, np.ndarray]] = None,
+                 block_table: Optional[np.ndarray] = None):
         import torch
 
         self.torch = torch
@@ -84,11 +92,18 @@ class DeviceModel:
             check(L.md_init_model(ctypes.byref(self.cfg), None, 0, None, 0, None, ctypes.byref(ctypes.c_void_p())))
         self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=self.device)
         self.kv_bytes = L.md_kv_bytes(ctypes.byref(self.cfg), self.cfg.max_batch, self.cfg.max_ctx)
-        lay, total = kv_layout(w)
+        self.paged = w.kv_page > 0
+        lay, total = kv_pool_layout(w) if self.paged else kv_layout(w)
         if total != self.kv_bytes:
             raise RuntimeError(f"KV layout mismatch: library {self.kv_bytes} vs workload {total}")
         self.kv_layout = lay
         self.kv = torch.empty(self.kv_bytes, dtype=torch.uint8, device=self.device)
+        self.bt = None
+        if self.paged:
+            npp = w.max_ctx // w.kv_page
+            if block_table is None:
+                block_table = np.arange(w.max_batch * npp, dtype=np.int32).reshape(w.max_batch, npp)
+            self.set_block_table(block_table)
         self.reset_kv()
         ptrs = (ctypes.c_void_p * len(specs))(*[base + o for o in self.offsets])
         h = ctypes.c_void_p()
@@ -98,12 +113,52 @@ class DeviceModel:
         self.handle = h
 
     # ------------------------------------------------------------------ state
+    def set_block_table(self, bt: np.ndarray) -> None:
+        """Block table of a paged model (host int32 [max_batch][max_ctx / kv_page]), copied to the device."""
+        w = self.w
+        bt = np.ascontiguousarray(bt, dtype=np.int32)
+        assert bt.shape == (w.max_batch, w.max_ctx // w.kv_page), bt.shape
+        self.bt_host = bt
+        self.bt = self.torch.from_numpy(bt).to(self.device)
+
     def reset_kv(self) -> None:
-        """Redraw every layer's cache / state from the seeded generator."""
-        sptr = self.torch.cuda.current_stream(self.device).cuda_stream
+        """Redraw every layer's cache / state from the seeded generator (paged:
+        each slot's contiguous draw scattered into the pages of the block table)."""
+        torch = self.torch
+        sptr = torch.cuda.current_stream(self.device).cuda_stream
         base = self.kv.data_ptr()
+        if not self.paged:
+            for l, (kind, off, nbytes, shape, dt) in enumerate(self.kv_layout):
+                synth.kv_layer_device(self.w, l, base + off, sptr)
+            return
+        w = self.w
+        clay, _ = kv_layout(w)
+        P, N, Bm, C = w.kv_page, w.kv_pages, w.max_batch, w.max_ctx
+        idx = torch.from_numpy(self.bt_host.reshape(-1).astype(np.int64)).to(self.device)
         for l, (kind, off, nbytes, shape, dt) in enumerate(self.kv_layout):
-            synth.kv_layer_device(self.w, l, base + off, sptr)
+            if kind == "kda":
+                synth.kv_layer_device(w, l, base + off, sptr)
+                continue
+            tmp = torch.empty(clay[l][2], dtype=torch.uint8, device=self.device)
+            synth.kv_layer_device(w, l, tmp.data_ptr(), sptr)
+            pool = self.kv[off:off + nbytes].view(torch.int16)
+            pool.fill_(0x7FC0)  # NaN: pages no slot maps
+            src = tmp.view(torch.int16)
+            if kind == "gqa":
+                nkv, hd = w.n_kv_heads, w.head_dim
+                half = Bm * nkv * C * hd
+                k = src[:half].view(Bm, nkv, C // P, P, hd).permute(0, 2, 1, 3, 4).reshape(Bm * (C // P), nkv, P, hd)
+                v = src[half:].view(Bm, nkv, C // P, P // V_TILE, hd, V_TILE).permute(0, 2, 1, 3, 4, 5)
+                v = v.reshape(Bm * (C // P), nkv, P // V_TILE, hd, V_TILE)
+                pk = pool[:N * nkv * P * hd].view(N, nkv, P, hd)
+                pv = pool[N * nkv * P * hd:].view(N, nkv, P // V_TILE, hd, V_TILE)
+                pk[idx] = k
+                pv[idx] = v
+            else:
+                rows = src.view(Bm, C // P, P, w.mla_row).reshape(Bm * (C // P), P, w.mla_row)
+                pool.view(N, P, w.mla_row)[idx] = rows
+            del tmp
+        torch.cuda.synchronize(self.device)
 
     def kv_layer(self, l: int):
         """Device tensor view of layer l's cache / state as stored (shape per
@@ -120,7 +175,10 @@ class DeviceModel:
 
     def kv_host(self):
         """Host copies of every layer's cache / state in the oracle's layout
-        (GQA V converted from its tiles to [max_batch][n_kv][max_ctx][head_dim])."""
+        (GQA V converted from its tiles to [max_batch][n_kv][max_ctx][head_dim];
+        a paged model's pages gathered through its block table)."""
+        if self.paged:
+            return self._kv_host_paged()
         out = []
         for l in range(self.w.n_layers):
             t = self.kv_layer(l).cpu().numpy()
@@ -129,6 +187,31 @@ class DeviceModel:
             if self.kv_layout[l][0] == "gqa":
                 t = np.stack([t[0], v_logical(t[1])])
             out.append(np.ascontiguousarray(t))
+        return out
+
+    def _kv_host_paged(self):
+        w = self.w
+        P, N, Bm, C = w.kv_page, w.kv_pages, w.max_batch, w.max_ctx
+        bt = self.bt_host.reshape(-1)
+        out = []
+        for l, (kind, off, nbytes, shape, dt) in enumerate(self.kv_layout):
+            raw = self.kv[off:off + nbytes].cpu().numpy()
+            if kind == "kda":
+                out.append(np.ascontiguousarray(raw.view(np.float32).reshape(shape)))
+                continue
+            a = raw.view(np.uint16)
+            if kind == "gqa":
+                nkv, hd = w.n_kv_heads, w.head_dim
+                pk = a[:N * nkv * P * hd].reshape(N, nkv, P, hd)[bt].reshape(Bm, C // P, nkv, P, hd)
+                pv = a[N * nkv * P * hd:].reshape(N, nkv, P // V_TILE, hd, V_TILE)[bt]
+                pv = pv.reshape(Bm, C // P, nkv, P // V_TILE, hd, V_TILE)
+                k = pk.transpose(0, 2, 1, 3, 4).reshape(Bm, nkv, C, hd)
+                vt = pv.transpose(0, 2, 1, 3, 4, 5).reshape(Bm, nkv, C // V_TILE, hd, V_TILE)
+                v = np.swapaxes(vt, -1, -2).reshape(Bm, nkv, C, hd)
+                out.append(np.ascontiguousarray(np.stack([k, v])))
+            else:
+                rows = a.reshape(N, P, w.mla_row)[bt].reshape(Bm, C, w.mla_row)
+                out.append(np.ascontiguousarray(rows))
         return out
 
     # ------------------------------------------------------------------ steps
@@ -140,6 +223,16 @@ class DeviceModel:
         torch = self.torch
         B = int(tokens.shape[0])
         s = stream if stream is not None else torch.cuda.current_stream(self.device)
+        if self.paged:
+            if multilaunch or noalloc:
+                raise ValueError("a paged model runs the megakernel step (md_decode_step_paged) only")
+            check(lib().md_decode_step_paged(self.handle, ctypes.c_void_p(tokens.data_ptr()),
+                                             ctypes.c_void_p(positions.data_ptr()), ctypes.c_void_p(self.kv.data_ptr()),
+                                             ctypes.c_void_p(self.bt.data_ptr()), ctypes.c_void_p(logits.data_ptr()), B,
+                                             ctypes.c_void_p(out_tokens.data_ptr() if out_tokens is not None else 0),
+                                             ctypes.c_void_p(out_ids.data_ptr() if out_ids is not None else 0),
+                                             ctypes.c_void_p(s.cuda_stream)))
+            return
         fn = (lib().md_decode_step_multilaunch if multilaunch else
               lib().md_decode_step_noalloc if noalloc else lib().md_decode_step)
         check(fn(self.handle, ctypes.c_void_p(tokens.data_ptr()), ctypes.c_void_p(positions.data_ptr()),
@@ -153,12 +246,38 @@ class DeviceModel:
         torch = self.torch
         B, n = int(tokens.shape[0]), int(tokens.shape[1])
         s = stream if stream is not None else torch.cuda.current_stream(self.device)
+        if self.paged:
+            check(lib().md_verify_step_paged(self.handle, ctypes.c_void_p(tokens.data_ptr()),
+                                             ctypes.c_void_p(positions.data_ptr()), ctypes.c_void_p(self.kv.data_ptr()),
+                                             ctypes.c_void_p(self.bt.data_ptr()), ctypes.c_void_p(logits.data_ptr()),
+                                             ctypes.c_void_p(accept_len.data_ptr()),
+                                             ctypes.c_void_p(next_token.data_ptr()),
+                                             ctypes.c_void_p(out_ids.data_ptr() if out_ids is not None else 0), B, n,
+                                             ctypes.c_void_p(s.cuda_stream)))
+            return
         check(lib().md_verify_step(self.handle, ctypes.c_void_p(tokens.data_ptr()),
                                    ctypes.c_void_p(positions.data_ptr()), ctypes.c_void_p(self.kv.data_ptr()),
                                    ctypes.c_void_p(logits.data_ptr()), ctypes.c_void_p(accept_len.data_ptr()),
                                    ctypes.c_void_p(next_token.data_ptr()),
                                    ctypes.c_void_p(out_ids.data_ptr() if out_ids is not None else 0), B, n,
                                    ctypes.c_void_p(s.cuda_stream)))
+
+    def copy_pages(self, src, dst, stream=None) -> None:
+        """md_kv_copy_pages: page src[i] -> dst[i] of every GQA / MLA layer (int sequences)."""
+        torch = self.torch
+        s = stream if stream is not None else torch.cuda.current_stream(self.device)
+        a = torch.tensor(list(src), dtype=torch.int32, device=self.device)
+        b = torch.tensor(list(dst), dtype=torch.int32, device=self.device)
+        check(lib().md_kv_copy_pages(self.handle, ctypes.c_void_p(self.kv.data_ptr()), ctypes.c_void_p(a.data_ptr()),
+                                     ctypes.c_void_p(b.data_ptr()), len(a), ctypes.c_void_p(s.cuda_stream)))
+        torch.cuda.synchronize(self.device)
+
+    def copy_slot(self, src: int, dst: int, stream=None) -> None:
+        """md_kv_copy_slot: sequence slot src -> dst (delta-rule states; contiguous caches' rows too)."""
+        torch = self.torch
+        s = stream if stream is not None else torch.cuda.current_stream(self.device)
+        check(lib().md_kv_copy_slot(self.handle, ctypes.c_void_p(self.kv.data_ptr()), src, dst,
+                                    ctypes.c_void_p(s.cuda_stream)))
 
     def device_status(self) -> None:
         check(lib().md_get_device_status(self.handle))
@@ -171,7 +290,7 @@ class DeviceModel:
             self.torch.cuda.synchronize(self.device)
             lib().md_free_model(self.handle)
             self.handle = None
-        for name in ("wbuf", "ws", "kv"):
+        for name in ("wbuf", "ws", "kv", "bt"):
             if getattr(self, name, None) is not None:
                 setattr(self, name, None)
 

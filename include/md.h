@@ -72,6 +72,13 @@ typedef struct md_config {
   int32_t ffn_dim;
   int32_t n_experts, top_k, expert_ffn, n_shared, shared_ffn, norm_topk;
   int32_t flags; /* reserved, must be 0 */
+  /* Paged attention caches (GQA and MLA layers).  kv_page = 0: contiguous,
+   * one region of max_ctx positions per sequence slot (md_kv_bytes).
+   * kv_page > 0 (a power of two, >= 32, dividing max_ctx): every GQA / MLA
+   * layer's cache is a pool of kv_pages pages of kv_page positions, and the
+   * _paged steps map each sequence's positions to pages through a block
+   * table (see md_decode_step_paged).  Delta-rule states stay one per slot. */
+  int32_t kv_page, kv_pages;
 } md_config;
 
 /* Number of weight tensors the model expects. */
@@ -125,7 +132,18 @@ size_t md_workspace_bytes(const md_config* cfg);
  *              (RMS-normalised latent, then the rotated key part)
  *   KDA layer: state fp32[Bm][kda_heads][kda_dk][kda_dv]
  * Sequence b of a batch uses slot b.  Returns 0 (md_last_error says why) for
- * an invalid cfg, batch outside [1, 8] or a capacity the cfg does not allow. */
+ * an invalid cfg, batch outside [1, 8] or a capacity the cfg does not allow.
+ *
+ * Paged configurations (cfg->kv_page = P > 0, cfg->kv_pages = N) give the
+ * size of a page pool instead: the GQA and MLA regions hold N pages of P
+ * positions each (ctx_cap must still be a multiple of P; it only bounds
+ * positions), laid out as above with one page in place of one slot:
+ *   GQA layer: K bf16[N][n_kv_heads][P][head_dim], then
+ *              V bf16[N][n_kv_heads][P / 32][head_dim][32]
+ *   MLA layer: latent rows bf16[N][P][kv_lora + rope_dim]
+ *   KDA layer: state fp32[batch][kda_heads][kda_dk][kda_dv] (one per slot)
+ * Page q of every layer belongs to the same owner: one block table serves
+ * all layers. */
 size_t md_kv_bytes(const md_config* cfg, int32_t batch, int32_t ctx_cap);
 
 /* Validate cfg, check the device (gfx950, cooperative launch, LDS), record
@@ -172,6 +190,50 @@ md_status md_decode_step_noalloc(md_model* m, const int32_t* tokens, const int32
                                  float* out_logits, int32_t batch, int32_t* out_tokens, int32_t* out_expert_ids,
                                  void* hip_stream);
 
+/* Paged attention caches (the agentic / serving workloads of the Kimi K3
+ * post's section "Future work": KV cache movement and management).  The
+ * model must be configured with kv_page = P > 0 and kv_pages = N, and kv_pool
+ * is the pool md_kv_bytes(cfg, cfg->max_batch, cfg->max_ctx) describes.
+ *   block_table  dev int32[batch][max_ctx / P]  row b maps sequence b's
+ *                positions: positions j*P .. j*P + P-1 live in page
+ *                block_table[b][j] (in [0, N)) of every GQA / MLA layer.
+ *                Only the entries covering positions 0 .. positions[b] (for
+ *                verify: positions[0] + n_tok - 1) are read.
+ * Everything else is md_decode_step's (md_verify_step's): same arguments,
+ * same results; the delta-rule states of sequence b stay in slot b.  Pages
+ * may be shared between sequences for positions that are only read (a
+ * common prefix); the page that receives a sequence's new row must be its
+ * own for the step (two rows of one step writing one page position race).
+ * A page id outside [0, N) sets the device error (md_get_device_status:
+ * MD_EDEVICE) and page 0 is read in its place.  A contiguous model
+ * (kv_page = 0) rejects these calls with MD_EINVAL, and a paged model
+ * rejects md_decode_step / md_verify_step / md_decode_step_noalloc /
+ * md_decode_step_multilaunch. */
+md_status md_decode_step_paged(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv_pool,
+                               const int32_t* block_table, float* out_logits, int32_t batch, int32_t* out_tokens,
+                               int32_t* out_expert_ids, void* hip_stream);
+md_status md_verify_step_paged(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv_pool,
+                               const int32_t* block_table, float* out_logits, int32_t* out_accept_len,
+                               int32_t* out_next_token, int32_t* out_expert_ids, int32_t batch, int32_t n_tok,
+                               void* hip_stream);
+
+/* KV movement on the device, enqueued on hip_stream (ordered with the steps
+ * of that stream).
+ * md_kv_copy_pages: page src_pages[i] -> dst_pages[i] (dev int32[n] each,
+ *   n >= 0) of every GQA layer (K and V) and every MLA layer of a paged
+ *   model: the copy-on-write of a shared page before a sequence writes into
+ *   it, or a move.  A destination must not also be a source of the same
+ *   call.  Ids outside [0, kv_pages) set the device error and are skipped.
+ * md_kv_copy_slot: sequence slot src_slot -> dst_slot (both in
+ *   [0, max_batch)): every delta-rule state and, for a contiguous model, the
+ *   slot's GQA / MLA cache rows too (a paged model's rows are shared or
+ *   copied through the block table and md_kv_copy_pages).  Forking a
+ *   sequence = copy its slot (and, paged, point the new row of the block
+ *   table at the same pages, copying the last partly-filled one). */
+md_status md_kv_copy_pages(md_model* m, void* kv_pool, const int32_t* src_pages, const int32_t* dst_pages,
+                           int32_t n, void* hip_stream);
+md_status md_kv_copy_slot(md_model* m, void* kv, int32_t src_slot, int32_t dst_slot, void* hip_stream);
+
 /* The same step as md_decode_step executed as one kernel launch per
  * operation (no megakernel): the baseline that exposes the inter-kernel
  * bubbles.  Same arguments and results. */
@@ -201,7 +263,8 @@ md_status md_verify_step(md_model* m, const int32_t* tokens, const int32_t* posi
 
 /* Synchronises the model's last stream and reports the device error word:
  * MD_OK, or MD_EDEVICE with md_last_error() naming the cause (a sync wait
- * that exceeded its bound, an out-of-range token or position).  Clears it. */
+ * that exceeded its bound, an out-of-range token, position or page id).
+ * Clears it. */
 md_status md_get_device_status(md_model* m);
 
 /* Profiling aid.  When dev_buf is non-NULL, every later step records

@@ -66,6 +66,9 @@ class Workload:
     context: int = 16               # prior cached positions per sequence
     max_ctx: int = 32               # cache capacity in positions
     max_batch: int = 8
+    # paged attention caches: positions per page (0: contiguous) and pool pages per layer
+    kv_page: int = 0
+    kv_pages: int = 0
     steps: int = 1
     seed_base: int = 0              # seeds: weights 1000+s, kv 2000+s, state 3000+s, tokens 4000+s, drafts 5000+s
 
@@ -207,6 +210,30 @@ def kv_layout(w: Workload):
             shape = (Bm, w.kda_heads, w.kda_dk, w.kda_dv)
             n = Bm * w.kda_heads * w.kda_dk * w.kda_dv * 4
             out.append(("kda", off, n, shape, "f32"))
+        off = _align(off + n)
+    return out, off
+
+
+def kv_pool_layout(w: Workload):
+    """Paged form of kv_layout (w.kv_page > 0): per layer (kind, offset_bytes,
+    nbytes, shape, dtype) with N = w.kv_pages pages of P = w.kv_page positions
+    in place of the slots of a GQA or MLA layer; delta-rule states stay one
+    per slot.  Returns the list and the total."""
+    out = []
+    off = 0
+    N, P = w.kv_pages, w.kv_page
+    for l in range(w.n_layers):
+        kind = w.layer_kind(l)
+        if kind == "gqa":
+            shape = (N, w.n_kv_heads, P, w.head_dim)
+            n = 2 * N * w.n_kv_heads * P * w.head_dim * 2
+        elif kind == "mla":
+            shape = (N, P, w.mla_row)
+            n = N * P * w.mla_row * 2
+        else:
+            shape = (w.max_batch, w.kda_heads, w.kda_dk, w.kda_dv)
+            n = w.max_batch * w.kda_heads * w.kda_dk * w.kda_dv * 4
+        out.append((kind, off, n, shape, "f32" if kind == "kda" else "bf16"))
         off = _align(off + n)
     return out, off
 

@@ -82,6 +82,46 @@ def test_kv_bytes_match_the_documented_layout():
     assert L.md_kv_bytes(ctypes.byref(c), 2, 80) == 0     # not a multiple of the 32-position V tiles
 
 
+def test_paged_kv_bytes_match_the_pool_layout():
+    """Paged configurations: md_kv_bytes is the page pool (pages in place of
+    slots for GQA and MLA layers, one state per slot for delta-rule layers)."""
+    L = _lib.lib()
+    for name, page, pages in (("mini_dense", 32, 7), ("mini_hybrid", 32, 5), ("dense_27b", 128, 300),
+                              ("hybrid_moe", 256, 40), ("mini_moe", 64, 3)):
+        w = WL.get(name)
+        w = w.replace(max_ctx=(w.max_ctx + page - 1) // page * page, kv_page=page, kv_pages=pages)
+        _, total = WL.kv_pool_layout(w)
+        c = _lib.config_from(w)
+        assert L.md_kv_bytes(ctypes.byref(c), w.max_batch, w.max_ctx) == total, name
+        assert L.md_workspace_bytes(ctypes.byref(c)) > 0, name
+
+
+@pytest.mark.parametrize("page,pages,max_ctx,msg", [
+    (48, 4, 96, "power of two"),
+    (16, 4, 64, "power of two"),
+    (64, 4, 96, "multiple of kv_page"),
+    (32, 0, 64, "kv_pages"),
+    (0, 4, 64, "kv_pages must be 0"),
+])
+def test_invalid_paged_configs_are_rejected(page, pages, max_ctx, msg):
+    L = _lib.lib()
+    c = _cfg(kv_page=page, kv_pages=pages, max_ctx=max_ctx)
+    assert L.md_workspace_bytes(ctypes.byref(c)) == 0
+    h = P()
+    assert L.md_init_model(ctypes.byref(c), None, 0, None, 0, None, ctypes.byref(h)) == _lib.MD_EINVAL
+    assert msg in _err()
+
+
+def test_paged_entry_point_argument_checks():
+    L = _lib.lib()
+    assert L.md_decode_step_paged(None, None, None, None, None, None, 1, None, None, None) == _lib.MD_EINVAL
+    assert "block_table" in _err()
+    assert L.md_verify_step_paged(None, None, None, None, None, None, None, None, None, 1, 4, None) == _lib.MD_EINVAL
+    assert L.md_kv_copy_pages(None, None, None, None, 0, None) == _lib.MD_EINVAL
+    assert L.md_kv_copy_slot(None, None, 0, 1, None) == _lib.MD_EINVAL
+    assert "model is NULL" in _err()
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("max_batch", 9, _lib.MD_EINVAL),
     ("max_batch", 0, _lib.MD_EINVAL),

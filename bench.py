@@ -226,13 +226,14 @@ def cpu_baseline(w, layers=8, B=1, min_seconds=10.0, max_rounds=16):
                       f"extrapolated to {w.n_layers} layers ({t_step:.2f} s per step)"}
 
 
-def decode_bench(w, batches, steps, warmup, multilaunch=True):
+def decode_bench(w, batches, steps, warmup, multilaunch=True, block_table=None):
     """Chained greedy decode steps at each batch size; returns per-batch
-    results (and multi-launch timings when built)."""
+    results (and multi-launch timings when built).  block_table: the page
+    map of a paged workload (w.kv_page > 0)."""
     import torch
     from decode_megakernel_md_amd.model import DeviceModel
     t0 = time.time()
-    m = DeviceModel(w)
+    m = DeviceModel(w, block_table=block_table)
     torch.cuda.synchronize()
     print(f"# {w.name}: model ready in {time.time() - t0:.1f} s ({m.weight_bytes / 1e9:.2f} GB weights)",
           file=sys.stderr, flush=True)
@@ -388,6 +389,16 @@ def main():
                                                 "traffic": traffic_bytes("hybrid_moe", B)} for B in hres}}
         wv = WL.verify_hybrid()
         extra[wv.name] = {"steps": 8, "verify": {str(a): r for a, r in verify_bench(wv, 8).items()}}
+        # paged attention caches: every sequence's pages scattered over a pool
+        # in random order (the same bytes per step as the contiguous runs)
+        for base, page in ((WL.dense_27b(), 128), (WL.hybrid_moe(), 32)):
+            npp = base.max_ctx // page
+            wp = base.replace(name=base.name + f"_paged{page}", kv_page=page, kv_pages=base.max_batch * npp + 64)
+            bt = np.random.default_rng(1).permutation(wp.kv_pages)[:wp.max_batch * npp].reshape(wp.max_batch, npp)
+            ps = min(16, wp.max_ctx - wp.context - args.warmup)
+            pres, _ = decode_bench(wp, [1, 8], ps, args.warmup, multilaunch=False, block_table=bt.astype(np.int32))
+            extra[wp.name] = {"steps": ps, "kv_page": page, "kv_pages": wp.kv_pages,
+                              "batches": {str(B): pres[B] for B in pres}}
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(w, layers=w.mla_every if w.attn_kind == 1 else 8)

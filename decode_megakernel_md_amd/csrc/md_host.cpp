@@ -794,6 +794,11 @@ md_status md_pack_weight(const void* src, void* dst, int64_t rows, int64_t cols,
   return MD_OK;
 }
 
-void md_free_model(md_model* m) { delete m; }
+void md_free_model(md_model* m) {
+  if (!m) return;
+  // nothing of this handle may still run on the device once it is gone
+  if (m->last_stream) (void)hipStreamSynchronize(m->last_stream);
+  delete m;
+}
 
 }  // extern "C"

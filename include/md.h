@@ -283,6 +283,10 @@ int32_t md_grid_size(const md_model* m);
 /* Text of the calling thread's last error; valid until its next md_* call. */
 const char* md_last_error(void);
 
+/* Release a model handle (NULL: nothing).  Waits for the last stream a call
+ * of this handle enqueued work on, so that every step, verify or copy of the
+ * handle has finished when it returns and the caller may free the weights,
+ * workspace and caches.  The caller's buffers are not freed. */
 void md_free_model(md_model* m);
 
 #ifdef __cplusplus

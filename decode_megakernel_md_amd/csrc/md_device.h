@@ -25,6 +25,18 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#ifndef MD_MAXB
+#define MD_MAXB 8
+#endif
+// Names of the two builds' kernel and launch functions
+#if MD_MAXB == 8
+#define MD_KERNEL md_megakernel
+#define MD_BUILD_NAME(x) x
+#else
+#define MD_KERNEL md_megakernel_w64
+#define MD_BUILD_NAME(x) x##_w64
+#endif
+
 namespace md {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -34,7 +46,23 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr int NT = 256;      // threads per workgroup (4 waves of 64)
 constexpr int NW = 4;        // waves per workgroup
-constexpr int MAXB = 8;      // token rows per step (batch, or verify tokens)
+// Token rows a step can carry: the library builds this file twice, with 8
+// (batches up to 8 and the verify step) and with 64 (wide batches, up to 64
+// sequences).  Activation buffers are laid out [..][MAXB][..].
+constexpr int MAXB = MD_MAXB;
+static_assert(MAXB == 8 || MAXB == 64, "the two builds: 8 and 64 rows");
+constexpr bool WIDE = MAXB > 8;       // the 64-row build (decode only)
+// The matrix cores' B operand is 16 columns.  8-row build: a tile is 8
+// tokens, token t's bf16 high part in column 2t and the rest in 2t+1 (one
+// operand, one instruction per tile).  64-row build: a tile is 16 tokens,
+// one per column, with the high parts and the rests as two operands whose
+// products go to the same accumulators (half the accumulator registers per
+// token).
+constexpr int TTILE = WIDE ? 16 : 8;  // tokens per B tile
+constexpr int NPART = WIDE ? 2 : 1;   // B operands per tile
+constexpr int NBT = MAXB / TTILE;     // B tiles of a full step
+constexpr int VMAX = 8;               // rows of a verify step (anchor + 7 drafts)
+constexpr int GSMAX = 8;              // query heads per kv head
 constexpr unsigned OOB = 0xFFFFFFF0u;  // buffer offset beyond any resource: loads return 0
 
 // cache-policy bits of buffer instructions on gfx950

@@ -12,10 +12,15 @@
 #include "md_model.h"
 
 namespace md {
+// the two builds of the kernel: up to 8 token rows (decode and verify) and
+// up to 64 (decode)
 hipError_t launch_megakernel(const Params& p, int grid, hipStream_t stream);
 hipError_t megakernel_occupancy(int* blocks_per_cu);
-hipError_t launch_pack(const void* src, void* dst, int64_t rows, int64_t cols, hipStream_t stream);
 hipError_t launch_multilaunch(const Params& p, const int* kinds, int grid, hipStream_t stream);
+hipError_t launch_megakernel_w64(const Params& p, int grid, hipStream_t stream);
+hipError_t megakernel_occupancy_w64(int* blocks_per_cu);
+hipError_t launch_multilaunch_w64(const Params& p, const int* kinds, int grid, hipStream_t stream);
+hipError_t launch_pack(const void* src, void* dst, int64_t rows, int64_t cols, hipStream_t stream);
 size_t scratch_bytes();
 hipError_t scratch_address(int dev, void** out);
 hipError_t launch_fill_u32(void* dst, uint32_t v, uint32_t n_words, hipStream_t stream);
@@ -39,11 +44,19 @@ md_status fail(md_status s, const char* fmt, ...) {
   return s;
 }
 
-constexpr int MAXB_ = 8;
+constexpr int MAXB_ = 8;          // token rows of the 8-row build (verify: n_tok)
+constexpr int MAXB_W = 64;        // sequences of the 64-row build
 constexpr int GMAX = 1024;        // largest grid the workspace is sized for
 constexpr int CMAX = 256;         // largest number of KV chunks per (sequence, kv head)
-constexpr int SP_WORDS_ = 9 * 32;
 constexpr int PHASES_PER_LAYER = 10;  // upper bound on sync points per layer
+
+// The kernel build a model runs on, by its max_batch, and what follows from
+// it: the token-row stride of the workspace's activation buffers and the
+// words per sync point (the 64-row build's attention phase counts up to
+// 64 x 8 (row, kv head) pairs in one).
+bool wide_model(const md_config* c) { return c->max_batch > MAXB_; }
+int row_stride(const md_config* c) { return wide_model(c) ? MAXB_W : MAXB_; }
+int sp_words(const md_config* c) { return wide_model(c) ? 17 * 32 : 9 * 32; }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -115,7 +128,7 @@ md_status validate(const md_config* c) {
   if (c->flags != 0) return fail(MD_EINVAL, "flags must be 0");
   if (c->n_layers < 1 || c->hidden < 32 || c->vocab < 1 || c->max_ctx < 1)
     return fail(MD_EINVAL, "n_layers, hidden, vocab and max_ctx must be positive");
-  if (c->max_batch < 1 || c->max_batch > MAXB_) return fail(MD_EINVAL, "max_batch must be in [1, 8]");
+  if (c->max_batch < 1 || c->max_batch > MAXB_W) return fail(MD_EINVAL, "max_batch must be in [1, %d]", MAXB_W);
   if (c->hidden % 32) return fail(MD_EUNSUPPORTED, "hidden must be a multiple of 32");
   if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f)) return fail(MD_EINVAL, "rms_eps and rope_theta must be > 0");
   if (c->attn_kind == 0) {
@@ -126,9 +139,10 @@ md_status validate(const md_config* c) {
     if (c->max_ctx % 32) return fail(MD_EUNSUPPORTED, "max_ctx must be a multiple of 32 (V cache tiles)");
     // the attention phase counts the finished chunks of every (row, kv head)
     // in one word of a layer's sync point
-    if (MAXB_ * c->n_kv_heads > SP_WORDS_)
+    const int rs = row_stride(c), spw = sp_words(c);
+    if (rs * c->n_kv_heads > spw)
       return fail(MD_EUNSUPPORTED, "at most %d kv heads (%d rows x kv heads must fit a sync point's %d words)",
-                  SP_WORDS_ / MAXB_, MAXB_, SP_WORDS_);
+                  spw / rs, rs, spw);
   } else if (c->attn_kind == 1) {
     if (c->mla_every < 1) return fail(MD_EINVAL, "mla_every must be >= 1");
     bool has_mla = c->n_layers >= c->mla_every, has_kda = c->mla_every > 1;
@@ -180,8 +194,10 @@ md_status validate(const md_config* c) {
     if (c->n_shared == 1 && !width_ok(c->shared_ffn))
       return fail(MD_EUNSUPPORTED, "shared_ffn must be a multiple of 32, at least 128");
     if (c->norm_topk != 0 && c->norm_topk != 1) return fail(MD_EINVAL, "norm_topk must be 0 or 1");
-    int nu = c->n_experts < MAXB_ * c->top_k ? c->n_experts : MAXB_ * c->top_k;
-    if (2 * nu > 72) return fail(MD_EUNSUPPORTED, "too many distinct experts per step (2 * min(n_experts, 8 * top_k) > 72)");
+    const int rs = row_stride(c);
+    int nu = c->n_experts < rs * c->top_k ? c->n_experts : rs * c->top_k;
+    if (2 * nu > 72)
+      return fail(MD_EUNSUPPORTED, "too many distinct experts per step (2 * min(n_experts, %d * top_k) > 72)", rs);
   }
   return MD_OK;
 }
@@ -209,6 +225,7 @@ int attn_chunks(const md_config* c, int grid, int rows) {
 WsLayout ws_layout(const md_config* c) {
   WsLayout w{};
   size_t o = 0;
+  const int64_t RS = row_stride(c);  // token rows of the activation buffers
   auto take = [&](size_t bytes) {
     size_t at = o;
     o = align256(o + bytes);
@@ -228,48 +245,49 @@ WsLayout ws_layout(const md_config* c) {
   if (c->shared_ffn > F) F = c->shared_ffn;
   w.layers = take(sizeof(LayerDesc) * (size_t)c->n_layers);
   w.experts = take(sizeof(void*) * 3 * (size_t)c->n_layers * (size_t)(c->n_experts > 0 ? c->n_experts : 1));
-  w.x = take(4 * MAXB_ * H);
+  w.x = take(4 * RS * H);
   const size_t L = (size_t)c->n_layers;
-  w.u_stride = align256(2 * 2 * MAXB_ * H);
+  w.u_stride = align256(2 * 2 * RS * H);
   w.u = take(w.u_stride * (2 * L + 1));
-  w.ssq_stride = align256(4 * (size_t)GMAX * MAXB_);
+  w.ssq_stride = align256(4 * (size_t)GMAX * RS);
   w.ssq = take(w.ssq_stride * (2 * L + 1));
-  w.qkv = take(4 * MAXB_ * (size_t)nqkv);
-  w.attn = take(4 * (size_t)MAXB_ * (c->n_q_heads > 0 ? c->n_q_heads : 1) * CMAX * (size_t)c->head_dim);
-  w.attn_ml = take(8 * (size_t)MAXB_ * (c->n_q_heads > 0 ? c->n_q_heads : 1) * CMAX);
-  w.ou_stride = align256(2 * 2 * MAXB_ * (size_t)attn_out);
+  w.qkv = take(4 * RS * (size_t)nqkv);
+  w.attn = take(4 * (size_t)RS * (c->n_q_heads > 0 ? c->n_q_heads : 1) * CMAX * (size_t)c->head_dim);
+  w.attn_ml = take(8 * (size_t)RS * (c->n_q_heads > 0 ? c->n_q_heads : 1) * CMAX);
+  w.ou_stride = align256(2 * 2 * RS * (size_t)attn_out);
   w.ou = take(w.ou_stride * L);
-  w.h_stride = align256(2 * 2 * MAXB_ * (size_t)F);
+  w.h_stride = align256(2 * 2 * RS * (size_t)F);
   w.h = take(w.h_stride * L);
-  w.rl = take(4 * (size_t)MAXB_ * (c->n_experts > 0 ? c->n_experts : 1));
-  w.hs_stride = align256(2 * 2 * MAXB_ * (size_t)(c->n_shared > 0 ? c->shared_ffn : 1));
+  w.rl = take(4 * (size_t)RS * (c->n_experts > 0 ? c->n_experts : 1));
+  w.hs_stride = align256(2 * 2 * RS * (size_t)(c->n_shared > 0 ? c->shared_ffn : 1));
   w.hs = take(w.hs_stride * L);
-  int nu = c->n_experts < MAXB_ * c->top_k ? c->n_experts : MAXB_ * c->top_k;
-  w.hr_stride = align256(2 * 2 * MAXB_ * (size_t)(c->expert_ffn > 0 ? c->expert_ffn : 1));
+  int nu = c->n_experts < RS * c->top_k ? c->n_experts : RS * c->top_k;
+  w.hr_stride = align256(2 * 2 * RS * (size_t)(c->expert_ffn > 0 ? c->expert_ffn : 1));
   w.hr_lstride = w.hr_stride * (size_t)(nu > 0 ? nu : 1);
   w.hr = take(w.hr_lstride * L);
-  w.uq_stride = align256(2 * 2 * MAXB_ * (size_t)(hyb ? c->q_lora : 1));
+  w.uq_stride = align256(2 * 2 * RS * (size_t)(hyb ? c->q_lora : 1));
   w.uq = take(w.uq_stride * L);
-  w.ssq2_stride = align256(4 * (size_t)GMAX * MAXB_);
+  w.ssq2_stride = align256(4 * (size_t)GMAX * RS);
   w.ssq2 = take(w.ssq2_stride * L);
-  w.ckv = take(4 * MAXB_ * 576);
-  w.qm = take(4 * MAXB_ * (size_t)mh * (hyb ? c->nope_dim + 64 : 1));
-  w.qabs = take(4 * MAXB_ * (size_t)mh * 576);
+  w.ckv = take(4 * RS * 576);
+  w.qm = take(4 * RS * (size_t)mh * (hyb ? c->nope_dim + 64 : 1));
+  w.qabs = take(4 * RS * (size_t)mh * 576);
   w.mz = take(hyb ? 4 * (size_t)GMAX * mh * 512 : 256);
   w.mml = take(8 * (size_t)GMAX * mh);
-  w.kda = take(hyb ? 4 * MAXB_ * (size_t)(2 * c->kda_heads * c->kda_dk + c->kda_heads * c->kda_dv + 2 * c->kda_heads) : 256);
+  w.kda = take(hyb ? 4 * RS * (size_t)(2 * c->kda_heads * c->kda_dk + c->kda_heads * c->kda_dv + 2 * c->kda_heads) : 256);
   int n_kda = 0;
   for (int l = 0; l < c->n_layers; ++l) n_kda += (hyb && !is_mla(c, l)) ? 1 : 0;
-  w.ring = take((size_t)n_kda * MAXB_ * (hyb ? (size_t)c->kda_heads * c->kda_dk * c->kda_dv * 4 : 0));
-  w.cand = take(8 * (size_t)GMAX * MAXB_);
+  // delta-rule snapshots of the verify step (8-row build only)
+  w.ring = take((size_t)n_kda * (RS > 8 ? 0 : RS) * (hyb ? (size_t)c->kda_heads * c->kda_dk * c->kda_dv * 4 : 0));
+  w.cand = take(8 * (size_t)GMAX * RS);
   w.zero = take(1024);
   w.rope_d = c->attn_kind == 0 ? c->head_dim : c->rope_dim;
   w.rope = take(sizeof(float) * 2 * (size_t)c->max_ctx * (size_t)(w.rope_d / 2));
   w.sync_attn_base = 1 + PHASES_PER_LAYER * c->n_layers + 2;
   w.n_sync = w.sync_attn_base + c->n_layers + 2;
-  w.sync = take(4 * 2 * (size_t)w.n_sync * SP_WORDS_);
+  w.sync = take(4 * 2 * (size_t)w.n_sync * sp_words(c));
   w.err = take(256);
-  w.mzc = take(hyb ? 4 * MAXB_ * (size_t)mh * 512 : 256);
+  w.mzc = take(hyb ? 4 * RS * (size_t)mh * 512 : 256);
   w.total = o;
   return w;
 }
@@ -317,7 +335,13 @@ struct md_model {
   uint8_t* scratch = nullptr;   // that device's static scratch (md_decode_step_noalloc)
   hipError_t scratch_err = hipSuccess;
   int* last_err_word = nullptr; // error word of the last step (workspace or static scratch)
+  bool wide = false;            // runs on the 64-row build (max_batch > 8)
 };
+
+// One decode or verify step on the model's kernel build.
+static hipError_t launch_step(const md_model* m, const Params& p, hipStream_t stream) {
+  return m->wide ? launch_megakernel_w64(p, m->grid, stream) : launch_megakernel(p, m->grid, stream);
+}
 
 extern "C" {
 
@@ -359,8 +383,8 @@ size_t md_workspace_bytes(const md_config* cfg) {
 
 size_t md_kv_bytes(const md_config* cfg, int32_t batch, int32_t ctx_cap) {
   if (validate(cfg) != MD_OK) return 0;
-  if (batch < 1 || batch > MAXB_ || ctx_cap < 1) {
-    fail(MD_EINVAL, "batch must be in [1, %d] and ctx_cap positive", MAXB_);
+  if (batch < 1 || batch > MAXB_W || ctx_cap < 1) {
+    fail(MD_EINVAL, "batch must be in [1, %d] and ctx_cap positive", MAXB_W);
     return 0;
   }
   md_config c = *cfg;
@@ -403,7 +427,7 @@ md_status md_init_model(const md_config* cfg, const void* const* weights, size_t
     return fail(MD_EUNSUPPORTED, "device is %s; the kernels are built for gfx950", prop.gcnArchName);
   if (!prop.cooperativeLaunch) return fail(MD_EUNSUPPORTED, "device lacks cooperative launch");
   int per_cu = 0;
-  e = megakernel_occupancy(&per_cu);
+  e = wide_model(cfg) ? megakernel_occupancy_w64(&per_cu) : megakernel_occupancy(&per_cu);
   if (e != hipSuccess) return fail(MD_EHIP, "occupancy query: %s", hipGetErrorString(e));
   if (per_cu < 1) return fail(MD_EUNSUPPORTED, "megakernel does not fit on a CU");
   int grid = prop.multiProcessorCount;
@@ -417,6 +441,7 @@ md_status md_init_model(const md_config* cfg, const void* const* weights, size_t
   m->ws = (uint8_t*)workspace;
   m->ws_bytes = workspace_bytes;
   m->grid = grid;
+  m->wide = wide_model(cfg);
 
   // layer table
   std::vector<LayerDesc> L(cfg->n_layers);
@@ -565,7 +590,7 @@ md_status md_decode_step(md_model* m, const int32_t* tokens, const int32_t* posi
   md_status st = fill_params(m, tokens, positions, kv_cache, out_logits, batch, out_tokens, out_expert_ids, p);
   if (st != MD_OK) return st;
   p.bank = m->bank;
-  hipError_t e = launch_megakernel(p, m->grid, (hipStream_t)hip_stream);
+  hipError_t e = launch_step(m, p, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(MD_EHIP, "megakernel launch: %s", hipGetErrorString(e));
   m->bank ^= 1;
   m->last_stream = (hipStream_t)hip_stream;
@@ -598,11 +623,11 @@ md_status md_decode_step_noalloc(md_model* m, const int32_t* tokens, const int32
   // The scratch keeps whatever the last call on this device left: clear the
   // counters this step uses, its error word and the zero line.
   hipStream_t stream = (hipStream_t)hip_stream;
-  hipError_t e = launch_fill_u32(s + w.sync, 0u, (uint32_t)((size_t)w.n_sync * SP_WORDS_), stream);
+  hipError_t e = launch_fill_u32(s + w.sync, 0u, (uint32_t)((size_t)w.n_sync * sp_words(&m->cfg)), stream);
   if (e == hipSuccess) e = launch_fill_u32(s + w.err, 0u, 1u, stream);
   if (e == hipSuccess) e = launch_fill_u32(s + w.zero, 0u, 1024u / 4u, stream);
   if (e != hipSuccess) return fail(MD_EHIP, "clearing the static scratch: %s", hipGetErrorString(e));
-  e = launch_megakernel(p, m->grid, stream);
+  e = launch_step(m, p, stream);
   if (e != hipSuccess) return fail(MD_EHIP, "megakernel launch: %s", hipGetErrorString(e));
   m->last_stream = stream;
   m->last_err_word = p.err;
@@ -616,7 +641,8 @@ md_status md_decode_step_multilaunch(md_model* m, const int32_t* tokens, const i
   md_status st = fill_params(m, tokens, positions, kv_cache, out_logits, batch, out_tokens, out_expert_ids, p);
   if (st != MD_OK) return st;
   p.bank = m->bank;
-  hipError_t e = launch_multilaunch(p, m->kinds.data(), m->grid, (hipStream_t)hip_stream);
+  hipError_t e = m->wide ? launch_multilaunch_w64(p, m->kinds.data(), m->grid, (hipStream_t)hip_stream)
+                          : launch_multilaunch(p, m->kinds.data(), m->grid, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(MD_EHIP, "phase launch: %s", hipGetErrorString(e));
   m->bank ^= 1;
   m->last_stream = (hipStream_t)hip_stream;
@@ -628,6 +654,8 @@ static md_status verify_step(md_model* m, const int32_t* tokens, const int32_t* 
                              const int32_t* block_table, float* out_logits, int32_t* out_accept_len,
                              int32_t* out_next_token, int32_t* out_expert_ids, int32_t batch, int32_t n_tok,
                              void* hip_stream) {
+  if (m && m->wide)
+    return fail(MD_EUNSUPPORTED, "verify runs on models with max_batch <= %d (this one has %d)", MAXB_, m->cfg.max_batch);
   if (batch != 1) return fail(MD_EUNSUPPORTED, "verify runs one sequence per launch (batch must be 1)");
   if (n_tok < 2 || n_tok > MAXB_) return fail(MD_EINVAL, "n_tok %d outside [2, %d]", n_tok, MAXB_);
   if (!out_accept_len || !out_next_token) return fail(MD_EINVAL, "out_accept_len and out_next_token must be non-NULL");
@@ -649,7 +677,7 @@ static md_status verify_step(md_model* m, const int32_t* tokens, const int32_t* 
     p.mla_chunks = cm < 1 ? 1 : (cm > CMAX ? CMAX : cm);
   }
   p.bank = m->bank;
-  hipError_t e = launch_megakernel(p, m->grid, (hipStream_t)hip_stream);
+  hipError_t e = launch_step(m, p, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(MD_EHIP, "megakernel launch: %s", hipGetErrorString(e));
   m->bank ^= 1;
   m->last_stream = (hipStream_t)hip_stream;
@@ -673,7 +701,7 @@ md_status md_decode_step_paged(md_model* m, const int32_t* tokens, const int32_t
                              block_table);
   if (st != MD_OK) return st;
   p.bank = m->bank;
-  hipError_t e = launch_megakernel(p, m->grid, (hipStream_t)hip_stream);
+  hipError_t e = launch_step(m, p, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(MD_EHIP, "megakernel launch: %s", hipGetErrorString(e));
   m->bank ^= 1;
   m->last_stream = (hipStream_t)hip_stream;
@@ -756,7 +784,7 @@ md_status md_get_device_status(md_model* m) {
     // (and the error word), so that the handle can run again (the static
     // scratch's counters are cleared by every allocation-free step itself)
     hipError_t c = hipMemcpy(word, &zero, sizeof zero, hipMemcpyHostToDevice);
-    if (c == hipSuccess) c = hipMemset(m->ws + m->lay.sync, 0, (size_t)4 * 2 * m->lay.n_sync * SP_WORDS_);
+    if (c == hipSuccess) c = hipMemset(m->ws + m->lay.sync, 0, (size_t)4 * 2 * m->lay.n_sync * sp_words(&m->cfg));
     if (c == hipSuccess) c = hipDeviceSynchronize();
     if (c != hipSuccess)
       return fail(MD_EHIP, "device error 0x%x, and resetting the error word and counters failed: %s", err,

@@ -75,7 +75,9 @@ __device__ __forceinline__ uint32_t ssq2_at(KParams& pk, int l) { PARAMS; return
 // last (its class counter's last arrival increments the extra line).
 // Counters live in two banks used by alternate steps; every step clears the
 // bank of the next step (nobody touches it during this step).
-constexpr int SP_WORDS = 9 * 32;          // 9 lines of 128 B
+// 9 lines of 128 B; 17 in the 64-row build, whose attention phase counts
+// the finished chunks of up to 64 x 8 (row, kv head) pairs in one sync point
+constexpr int SP_WORDS = WIDE ? 17 * 32 : 9 * 32;
 constexpr int NGRP = 8;
 
 __device__ __forceinline__ unsigned* sync_pt(KParams& pk, int idx) {
@@ -292,11 +294,14 @@ __shared__ __attribute__((aligned(16))) char md_smem[MD_SMEM_BYTES];
 
 constexpr int CMAX_DEV = 256;    // largest chunk count per (sequence, kv head)
 constexpr int TG = 2;            // slots per group (share one B operand load); even: SwiGLU pairs
-constexpr int GDS = 8;           // k-steps in flight per wave
+// k-steps in flight per wave: 8 (measured: 4 and 8 stream equally fast,
+// deeper is slower); fewer in the 64-row build, whose ring holds 8 B
+// operands per k-step
+constexpr int GDS = WIDE ? 2 : 8;
 constexpr int MAXSLOT = 96;      // slots per workgroup and phase
 constexpr int MAXGRP = MAXSLOT / TG;
 constexpr int MAXMAT = 72;       // matrices per phase
-constexpr int STAGE_ROWS = 768;  // epilogue staging rows per workgroup
+constexpr int STAGE_ROWS = 768 * 8 / MAXB;  // epilogue staging rows per workgroup (of MAXB tokens)
 constexpr int MIN_KS = NW;       // every wave needs a k-step of every group
 
 struct RowSplit {
@@ -336,8 +341,8 @@ struct GroupDesc {
 };
 
 struct GemvSmem {
-  float red[2][NW][TG][16][16];  // per-wave partial tiles of a group, two buffers alternating by group;
-                                 // also reused as [NT][MAXB] scratch after the stream
+  float red[2][NW][TG][16][16];  // per-wave partial tiles of a group (one B tile of it), two buffers
+                                 // alternating; also reused as [NT][MAXB] scratch after the stream (8-row build)
   Slot slots[MAXSLOT];
   GroupDesc grp[MAXGRP];
   MatDesc mats[MAXMAT];
@@ -660,12 +665,16 @@ __device__ __forceinline__ void slot_src(int si, int lq, uint32_t lchunk, int wv
   pstep = lv ? (uint32_t)(NW * 1024) : 0u;
 }
 
-// Output (token t, row rr of slot TG*g + i) of a finished group: the four
-// waves' partials, hi and lo columns, summed in a fixed order.
+// Output (token t of the tile, row rr of slot TG*g + i) of a finished
+// group: the four waves' partials (8-row build: hi and lo columns) summed in
+// a fixed order.
 __device__ __forceinline__ float gy(int rb, int i, int rr, int t) {
   float s = 0.f;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) s += GSM.red[rb][w][i][rr][2 * t] + GSM.red[rb][w][i][rr][2 * t + 1];
+  for (int w = 0; w < NW; ++w) {
+    if constexpr (WIDE) s += GSM.red[rb][w][i][rr][t];
+    else s += GSM.red[rb][w][i][rr][2 * t] + GSM.red[rb][w][i][rr][2 * t + 1];
+  }
   return s;
 }
 
@@ -700,68 +709,94 @@ __device__ __forceinline__ void inv_finish(KParams& pk, float* inv, int n_feat, 
   __syncthreads();
 }
 
-// The per-wave weight stream over GSM's group list.  gemv_begin issues the
-// weight loads of the first GDS k-steps (they depend on no other workgroup,
-// so a phase issues them before it waits at its sync point); gemv_run then
-// issues the matching activation (B operand) loads and streams the rest,
-// GDS k-steps ahead of the matrix cores, continuously across groups.
+// The per-wave weight stream over a range of GSM's group list.  gemv_begin
+// issues the weight loads of the first GDS k-steps (they depend on no other
+// workgroup, so a phase issues them before it waits at its sync point);
+// gemv_run then issues the matching activation (B operand) loads and streams
+// the rest, GDS k-steps ahead of the matrix cores, continuously across
+// groups.  Each weight block is multiplied by every B tile of the step (NB
+// tiles, NPART operands each), so a step's weights are read once whatever
+// the batch.
+template <int NB>
 struct GemvStream {
   int wv, lq, tok, part, B, ngroups, total;
+  int gfirst;           // the range's first group (ig runs ahead of the matrix cores)
   uint32_t lchunk, lane16;
   uint64_t zero_addr;
   rsrc_t urs;
   int ig, is, nks_i;
-  uint32_t boff;
+  uint32_t boff;        // B operand offset of this lane's row in tile 0 (OOB: a token past B)
+  uint32_t btile;       // bytes between the B tiles of the group
+  uint32_t bpart;       // bytes between a tile's operands (the high parts and the rests)
+  uint32_t bmask;       // bit j: this lane's token of tile j is a row of the step
   uint64_t pa[TG];
   uint32_t ps[TG];
   i32x4 ra[GDS][TG];
-  i32x4 rb[GDS];
+  i32x4 rb[GDS][NB * NPART];
   uint32_t bo[GDS];
+  uint32_t btd[GDS], bpd[GDS];  // btile and bpart of the k-step's group (the first GDS k-steps may span groups)
 };
 
-__device__ __forceinline__ void gs_group(GemvStream& s, int g) {
+template <int NB>
+__device__ __forceinline__ void gs_group(GemvStream<NB>& s, int g) {
   const int ks = __builtin_amdgcn_readfirstlane(GSM.grp[g].KS);
   const uint32_t uo = __builtin_amdgcn_readfirstlane(GSM.grp[g].u_off);
   s.nks_i = (ks - s.wv + NW - 1) / NW;
-  s.boff = s.tok < s.B ? uo + (uint32_t)((s.part * MAXB + s.tok) * ks * 32) * 2u + s.lane16 : OOB;
+  s.boff = uo + (uint32_t)((s.part * MAXB + s.tok) * ks * 32) * 2u + s.lane16;
+  s.btile = (uint32_t)(TTILE * ks * 32) * 2u;
+  s.bpart = (uint32_t)(MAXB * ks * 32) * 2u;
 #pragma unroll
   for (int i = 0; i < TG; ++i) slot_src(TG * g + i, s.lq, s.lchunk, s.wv, s.zero_addr, s.pa[i], s.ps[i]);
 }
 
 // Weight loads of one k-step (ring entry d); past the last group they read
-// the zero block.  Records the k-step's B-operand offset.
-__device__ __forceinline__ void gs_issue_a(GemvStream& s, int d) {
+// the zero block.  Records the k-step's B-operand offset (tile 0).
+template <int NB>
+__device__ __forceinline__ void gs_issue_a(GemvStream<NB>& s, int d) {
   const bool ok = s.ig < s.ngroups;
 #pragma unroll
   for (int i = 0; i < TG; ++i) {
     s.ra[d][i] = __builtin_nontemporal_load((const __attribute__((address_space(1))) i32x4*)(ok ? s.pa[i] : s.zero_addr));
     s.pa[i] += s.ps[i];
   }
-  s.bo[d] = (ok && s.boff != OOB) ? s.boff + (uint32_t)(s.is * NW + s.wv) * 64u : OOB;
+  s.bo[d] = ok ? s.boff + (uint32_t)(s.is * NW + s.wv) * 64u : OOB;
+  s.btd[d] = s.btile;
+  s.bpd[d] = s.bpart;
   if (++s.is == s.nks_i) {
     s.is = 0;
     ++s.ig;
     if (s.ig < s.ngroups) gs_group(s, s.ig);
   }
 }
-// Activation (B operand) loads: cache policy sc0 (not kept in the CU's L1,
-// served by the XCD's L2).  Every activation buffer is used once per launch
-// (one buffer per use, see u_at), so the L2 never holds an older copy of it:
-// the first read in an XCD fetches what the producers wrote through to
-// memory before the sync point, later reads in that XCD hit.  (On a buffer
-// reused within a launch such loads would return stale lines: measured.)
-__device__ __forceinline__ void gs_issue_b(GemvStream& s, int d) { s.rb[d] = ld_x4<CP_SC0>(s.urs, s.bo[d]); }
+// Activation (B operand) loads of one k-step, every tile: cache policy sc0
+// (not kept in the CU's L1, served by the XCD's L2).  Every activation buffer
+// is used once per launch (one buffer per use, see u_at), so the L2 never
+// holds an older copy of it: the first read in an XCD fetches what the
+// producers wrote through to memory before the sync point, later reads in
+// that XCD hit.  (On a buffer reused within a launch such loads would return
+// stale lines: measured.)  Lanes whose token of a tile is past the step's
+// rows read nothing (offset past the resource: zeros).
+template <int NB>
+__device__ __forceinline__ void gs_issue_b(GemvStream<NB>& s, int d, uint32_t bo, uint32_t btile, uint32_t bpart) {
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const uint32_t o = (bo != OOB && ((s.bmask >> j) & 1u)) ? bo + (uint32_t)j * btile : OOB;
+#pragma unroll
+    for (int q = 0; q < NPART; ++q) s.rb[d][j * NPART + q] = ld_x4<CP_SC0>(s.urs, o == OOB ? OOB : o + (uint32_t)q * bpart);
+  }
+}
 
 // Steady state: weight and activation loads of one k-step, then the group
 // switch (loads before the branch, so the compiler sees one load sequence).
-__device__ __forceinline__ void gs_issue(GemvStream& s, int d) {
+template <int NB>
+__device__ __forceinline__ void gs_issue(GemvStream<NB>& s, int d) {
   const bool ok = s.ig < s.ngroups;
 #pragma unroll
   for (int i = 0; i < TG; ++i) {
     s.ra[d][i] = __builtin_nontemporal_load((const __attribute__((address_space(1))) i32x4*)(ok ? s.pa[i] : s.zero_addr));
     s.pa[i] += s.ps[i];
   }
-  s.rb[d] = ld_x4<CP_SC0>(s.urs, (ok && s.boff != OOB) ? s.boff + (uint32_t)(s.is * NW + s.wv) * 64u : OOB);
+  gs_issue_b(s, d, ok ? s.boff + (uint32_t)(s.is * NW + s.wv) * 64u : OOB, s.btile, s.bpart);
   if (++s.is == s.nks_i) {
     s.is = 0;
     ++s.ig;
@@ -769,81 +804,141 @@ __device__ __forceinline__ void gs_issue(GemvStream& s, int d) {
   }
 }
 
-__device__ __forceinline__ void gemv_begin(GemvStream& s, const uint8_t* ws, uint32_t ws_bytes, uint32_t off_zero,
-                                           int B) {
+// Groups [g0, g1) of the tables (one staging pass).
+template <int NB>
+__device__ __forceinline__ void gemv_begin(GemvStream<NB>& s, const uint8_t* ws, uint32_t ws_bytes, uint32_t off_zero,
+                                           int B, int g0, int g1) {
   const int lane = threadIdx.x & 63;
   s.wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  s.ngroups = __builtin_amdgcn_readfirstlane(GSM.ngroups);
-  s.total = __builtin_amdgcn_readfirstlane(GSM.wtot[s.wv]);
+  s.ngroups = g1;
+  if (g0 == 0 && g1 == __builtin_amdgcn_readfirstlane(GSM.ngroups)) {
+    s.total = __builtin_amdgcn_readfirstlane(GSM.wtot[s.wv]);
+  } else {
+    int t = 0;
+    for (int g = g0; g < g1; ++g) t += group_nks(g, s.wv);
+    s.total = t;
+  }
   s.urs = make_rsrc_u(ws, ws_bytes);
   s.lq = (lane & 15) >> 2;
   s.lchunk = (uint32_t)(((lane >> 4) * 4 + (lane & 3)) * 16);
   s.lane16 = (uint32_t)(lane >> 4) * 16u;
-  s.tok = (lane & 15) >> 1;
-  s.part = lane & 1;
+  // B column lane & 15: 8-row build token (lane & 15) / 2, hi or lo by the
+  // lane's parity; 64-row build token lane & 15 of the tile (hi and lo are
+  // separate operands)
+  s.tok = WIDE ? (lane & 15) : (lane & 15) >> 1;
+  s.part = WIDE ? 0 : lane & 1;
   s.B = B;
+  s.bmask = 0;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) s.bmask |= (TTILE * j + s.tok < B) ? (1u << j) : 0u;
   s.zero_addr = (uint64_t)(ws + off_zero);
-  s.ig = 0;
+  s.ig = g0;
+  s.gfirst = g0;
   s.is = 0;
   s.nks_i = 1;
   s.boff = OOB;
+  s.btile = 0;
+  s.bpart = 0;
 #pragma unroll
   for (int i = 0; i < TG; ++i) {
     s.pa[i] = s.zero_addr;
     s.ps[i] = 0;
   }
-  if (s.ngroups > 0) gs_group(s, 0);
+  if (g0 < g1) gs_group(s, g0);
 #pragma unroll
   for (int d = 0; d < GDS; ++d) gs_issue_a(s, d);
 }
 
-// Stream everything.  After each finished group g, epi(g, rb) reads its
-// outputs with gy(rb, i, row-in-slot, token) (LDS only).  One barrier per
-// group: the partials of consecutive groups go to alternating buffers.
-// inv_n > 0: first fill GSM.inv with 1/rms over inv_n features from the
-// per-workgroup partial sums of squares at inv_off.  Those loads are issued
-// before the ring's activation loads, so waiting for them never waits for
-// the ring.
-template <class Epi>
-__device__ __forceinline__ void gemv_run(KParams& pk, GemvStream& s, int inv_n, uint32_t inv_off, Epi epi) {
+// 1/rms of every token of a 64-row step (the wide build): wave w sums
+// tokens 16w .. 16w+15 over all workgroups' partials, lane l taking
+// workgroups l, l + 64, ... in order, then a fixed-order wave reduction (the
+// same order as inv_finish).
+__device__ __forceinline__ void inv_finish_wide(KParams& pk, float* inv, int n_feat, uint32_t inv_off, int B) {
+  PARAMS;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+  const int G = gridDim.x;
+  constexpr int TPW = MAXB / NW;  // tokens per wave
+  float acc[TPW];
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) acc[k] = 0.f;
+  for (int g = lane; g < G; g += 64) {
+    float v[TPW];
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) v[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+        r, (TPW * wv + k < B) ? inv_off + (uint32_t)(g * MAXB + TPW * wv + k) * 4u : OOB, 0, CP_SC0));
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) acc[k] += v[k];
+  }
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) {
+    const float sum = wave_sum(acc[k]);
+    if (lane == 0) inv[TPW * wv + k] = 1.0f / sqrtf(sum / (float)n_feat + p.eps);
+  }
+  __syncthreads();
+}
+
+// Stream everything.  After each finished group g, epi(g, rb, j) reads the
+// outputs of its B tile j with gy(rb, i, row-in-slot, token) (LDS only).
+// One barrier per tile of a group: the partials of consecutive tiles go to
+// alternating buffers.  inv_n > 0: first fill GSM.inv with 1/rms over inv_n
+// features from the per-workgroup partial sums of squares at inv_off.  Those
+// loads are issued before the ring's activation loads, so waiting for them
+// never waits for the ring.
+template <int NB, class Epi>
+__device__ __forceinline__ void gemv_run(KParams& pk, GemvStream<NB>& s, int inv_n, uint32_t inv_off, Epi epi) {
   PARAMS;
   static_assert(TG % 2 == 0, "SwiGLU groups hold gate/up slot pairs");
   const int lane = threadIdx.x & 63;
-  i32x4 ia0, ib0, ia1, ib1;
-  if (inv_n > 0) {
-    const rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-    const int g0 = threadIdx.x, g1 = threadIdx.x + NT;
-    const int G = gridDim.x;
-    ia0 = ld_x4<CP_SC0>(r, g0 < G ? inv_off + (uint32_t)(g0 * MAXB) * 4u : OOB);
-    ib0 = ld_x4<CP_SC0>(r, g0 < G ? inv_off + (uint32_t)(g0 * MAXB + 4) * 4u : OOB);
-    ia1 = ld_x4<CP_SC0>(r, g1 < G ? inv_off + (uint32_t)(g1 * MAXB) * 4u : OOB);
-    ib1 = ld_x4<CP_SC0>(r, g1 < G ? inv_off + (uint32_t)(g1 * MAXB + 4) * 4u : OOB);
+  if constexpr (!WIDE) {
+    i32x4 ia0, ib0, ia1, ib1;
+    if (inv_n > 0) {
+      const rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+      const int g0 = threadIdx.x, g1 = threadIdx.x + NT;
+      const int G = gridDim.x;
+      ia0 = ld_x4<CP_SC0>(r, g0 < G ? inv_off + (uint32_t)(g0 * MAXB) * 4u : OOB);
+      ib0 = ld_x4<CP_SC0>(r, g0 < G ? inv_off + (uint32_t)(g0 * MAXB + 4) * 4u : OOB);
+      ia1 = ld_x4<CP_SC0>(r, g1 < G ? inv_off + (uint32_t)(g1 * MAXB) * 4u : OOB);
+      ib1 = ld_x4<CP_SC0>(r, g1 < G ? inv_off + (uint32_t)(g1 * MAXB + 4) * 4u : OOB);
+    }
+#pragma unroll
+    for (int d = 0; d < GDS; ++d) gs_issue_b(s, d, s.bo[d], s.btd[d], s.bpd[d]);
+    if (inv_n > 0) inv_finish(p, GSM.inv, inv_n, ia0, ib0, ia1, ib1);
+  } else {
+    if (inv_n > 0) inv_finish_wide(p, GSM.inv, inv_n, inv_off, s.B);
+#pragma unroll
+    for (int d = 0; d < GDS; ++d) gs_issue_b(s, d, s.bo[d], s.btd[d], s.bpd[d]);
   }
+  f32x4 acc[TG][NB];
 #pragma unroll
-  for (int d = 0; d < GDS; ++d) gs_issue_b(s, d);
-  if (inv_n > 0) inv_finish(p, GSM.inv, inv_n, ia0, ib0, ia1, ib1);
-  f32x4 acc[TG];
+  for (int i = 0; i < TG; ++i)
 #pragma unroll
-  for (int i = 0; i < TG; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  int cg = 0, cs = 0, rbuf = 0;
-  int nks_c = s.ngroups > 0 ? group_nks(0, s.wv) : 1;
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int cg = s.gfirst, cs = 0, rbuf = 0;
+  int nks_c = cg < s.ngroups ? group_nks(cg, s.wv) : 1;
   // One k-step: matrix-core work on ring entry d, its refill, and at the end
-  // of a group the partials to LDS, one barrier, and the epilogue.
+  // of a group its tiles' partials to LDS, one barrier each, and the epilogue.
 #define GEMV_STEP(J0, D)                                                                                        \
   {                                                                                                             \
-    bf16x8 bop = __builtin_bit_cast(bf16x8, s.rb[D]);                                                           \
-    _Pragma("unroll") for (int i = 0; i < TG; ++i) acc[i] =                                                     \
-        __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, s.ra[D][i]), bop, acc[i], 0, 0, 0);  \
+    _Pragma("unroll") for (int j = 0; j < NB; ++j) _Pragma("unroll") for (int q = 0; q < NPART; ++q) {          \
+      bf16x8 bop = __builtin_bit_cast(bf16x8, s.rb[D][j * NPART + q]);                                          \
+      _Pragma("unroll") for (int i = 0; i < TG; ++i) acc[i][j] =                                                \
+          __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, s.ra[D][i]), bop, acc[i][j], 0, 0, 0); \
+    }                                                                                                           \
     gs_issue(s, D);                                                                                             \
     if ((J0) + (D) < s.total) {                                                                                 \
       if (++cs == nks_c) {                                                                                      \
         cs = 0;                                                                                                 \
-        _Pragma("unroll") for (int i = 0; i < TG; ++i) _Pragma("unroll") for (int r = 0; r < 4; ++r)            \
-            GSM.red[rbuf][s.wv][i][4 * (lane >> 4) + r][lane & 15] = acc[i][r];                                 \
-        __syncthreads();                                                                                        \
-        _Pragma("unroll") for (int i = 0; i < TG; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};                      \
-        epi(cg, rbuf);                                                                                          \
-        rbuf ^= 1;                                                                                              \
+        _Pragma("unroll") for (int j = 0; j < NB; ++j) {                                                        \
+          if (TTILE * j < s.B) {                                                                                \
+            _Pragma("unroll") for (int i = 0; i < TG; ++i) _Pragma("unroll") for (int r = 0; r < 4; ++r)        \
+                GSM.red[rbuf][s.wv][i][4 * (lane >> 4) + r][lane & 15] = acc[i][j][r];                          \
+            __syncthreads();                                                                                    \
+            _Pragma("unroll") for (int i = 0; i < TG; ++i) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};               \
+            epi(cg, rbuf, j);                                                                                   \
+            rbuf ^= 1;                                                                                          \
+          }                                                                                                     \
+        }                                                                                                       \
         ++cg;                                                                                                   \
         if (cg < s.ngroups) nks_c = group_nks(cg, s.wv);                                                        \
       }                                                                                                         \
@@ -894,7 +989,8 @@ __device__ __forceinline__ bool builder_done(KParams& pk, SlotBuilder& sb, int s
   PARAMS;
   if (threadIdx.x < 64) {
     sb.finish();
-    const bool ovf = sb.ovf || (stage_rows < 0 ? sb.ns * 16 : stage_rows) > STAGE_ROWS;
+    // (slot-staged phases of the 64-row build run in staging passes)
+    const bool ovf = sb.ovf || (stage_rows < 0 ? (WIDE ? 0 : sb.ns * 16) : stage_rows) > STAGE_ROWS;
     if (ovf) {
       if (threadIdx.x == 0) set_err(p, MDE_CAPACITY);
       GSM.overflow = 1;
@@ -941,16 +1037,27 @@ __device__ __forceinline__ void store_ssq(KParams& pk, rsrc_t r, float* part, ui
   }
 }
 
+// The same for the 64-row build: thread tid holds the partial of token
+// tid % 64 over its rows (acc); the four waves' partials are added in order.
+__device__ __forceinline__ void store_ssq_wide(KParams& pk, rsrc_t r, float acc, uint32_t off_ssq) {
+  float* part = (float*)GSM.red;  // [NT]
+  __syncthreads();
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x < MAXB) {
+    const int t = threadIdx.x;
+    const float a = part[t] + part[64 + t] + part[128 + t] + part[192 + t];
+    st_f32(r, off_ssq + (uint32_t)(blockIdx.x * MAXB + t) * 4u, a);
+  }
+}
+
 // --- embedding: x[t] = E[tok_t] on this WG's hidden rows
 __device__ __noinline__ void phase_embed(KParams& pk) {
   PARAMS;
   RowSplit s = owned_rows(p.H, blockIdx.x, gridDim.x);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   const uint16_t* g = p.layers[0].attn_norm;
-  float* part = (float*)md_smem;  // [NT][MAXB]
-  for (int t = 0; t < MAXB; ++t) part[threadIdx.x * MAXB + t] = 0.f;
-  for (int e = threadIdx.x; e < (s.r1 - s.r0) * p.B; e += NT) {
-    int t = e / (s.r1 - s.r0), i = s.r0 + e % (s.r1 - s.r0);
+  auto elem = [&](int t, int i) -> float {
     int tok = p.tokens[t];
     if (tok < 0 || tok >= p.V) {
       set_err(p, MDE_TOKEN);
@@ -959,9 +1066,23 @@ __device__ __noinline__ void phase_embed(KParams& pk) {
     float x = bf16_f32(p.embed[(size_t)tok * p.H + i]);
     p.x[t * p.H + i] = x;
     put_hilo(r, u_at(p, 0), p.H, t, i, bf16_f32(g[i]) * x);
-    part[threadIdx.x * MAXB + t] += x * x;
+    return x * x;
+  };
+  if constexpr (WIDE) {
+    float acc = 0.f;
+    const int t = threadIdx.x & 63;
+    if (t < p.B)
+      for (int i = s.r0 + (threadIdx.x >> 6); i < s.r1; i += NT / 64) acc += elem(t, i);
+    store_ssq_wide(p, r, acc, ssq_at(p, 0));
+  } else {
+    float* part = (float*)md_smem;  // [NT][MAXB]
+    for (int t = 0; t < MAXB; ++t) part[threadIdx.x * MAXB + t] = 0.f;
+    for (int e = threadIdx.x; e < (s.r1 - s.r0) * p.B; e += NT) {
+      int t = e / (s.r1 - s.r0), i = s.r0 + e % (s.r1 - s.r0);
+      part[threadIdx.x * MAXB + t] += elem(t, i);
+    }
+    store_ssq(p, r, part, ssq_at(p, 0));
   }
-  store_ssq(p, r, part, ssq_at(p, 0));
 }
 
 // ------------------------------------------------------------ shared stream
@@ -974,24 +1095,28 @@ enum : int { EPI_BY_KIND = 0, EPI_RESIDUAL = 1 };
 // EPI_BY_KIND: a GK_SINGLE group stores y * inv_rms per slot row, a GK_PAIR
 // group silu(inv*gate) * (inv*up) at the gate slots' rows; EPI_RESIDUAL adds
 // y to the owned residual rows staged at GSM.out[row - r0].
-__device__ __forceinline__ void gemv_epi(int g, int rb, int kind, int B, int r0) {
+// (B tile j of the group: tokens TTILE*j .. TTILE*(j+1) - 1, those below B; slot
+// rows are staged relative to s0, the first slot of the staging pass.)
+__device__ __forceinline__ void gemv_epi(int g, int rb, int j, int kind, int B, int r0, int s0) {
+  const int t0 = TTILE * j;
+  const int Bt = B - t0 < TTILE ? B - t0 : TTILE;
   if (kind == EPI_RESIDUAL) {
-    for (int e = threadIdx.x; e < TG * 16 * B; e += NT) {
-      int t = e % B, rr = (e / B) % 16, i = e / (B * 16);
+    for (int e = threadIdx.x; e < TG * 16 * Bt; e += NT) {
+      int t = e % Bt, rr = (e / Bt) % 16, i = e / (Bt * 16);
       int m, row;
-      if (slot_row(TG * g + i, rr, m, row)) GSM.out[row - r0][t] += gy(rb, i, rr, t);
+      if (slot_row(TG * g + i, rr, m, row)) GSM.out[row - r0][t0 + t] += gy(rb, i, rr, t);
     }
   } else if (GSM.grp[g].kind == GK_PAIR) {
-    for (int e = threadIdx.x; e < (TG / 2) * 16 * B; e += NT) {
-      int t = e % B, rr = (e / B) % 16, j = e / (B * 16);
-      float a = gy(rb, 2 * j, rr, t) * GSM.inv[t];
-      float u = gy(rb, 2 * j + 1, rr, t) * GSM.inv[t];
-      GSM.out[(TG * g + 2 * j) * 16 + rr][t] = silu(a) * u;
+    for (int e = threadIdx.x; e < (TG / 2) * 16 * Bt; e += NT) {
+      int t = e % Bt, rr = (e / Bt) % 16, jj = e / (Bt * 16);
+      float a = gy(rb, 2 * jj, rr, t) * GSM.inv[t0 + t];
+      float u = gy(rb, 2 * jj + 1, rr, t) * GSM.inv[t0 + t];
+      GSM.out[(TG * g + 2 * jj - s0) * 16 + rr][t0 + t] = silu(a) * u;
     }
   } else {
-    for (int e = threadIdx.x; e < TG * 16 * B; e += NT) {
-      int t = e % B, rr = (e / B) % 16, i = e / (B * 16);
-      GSM.out[(TG * g + i) * 16 + rr][t] = gy(rb, i, rr, t) * GSM.inv[t];
+    for (int e = threadIdx.x; e < TG * 16 * Bt; e += NT) {
+      int t = e % Bt, rr = (e / Bt) % 16, i = e / (Bt * 16);
+      GSM.out[(TG * g + i - s0) * 16 + rr][t0 + t] = gy(rb, i, rr, t) * GSM.inv[t0 + t];
     }
   }
 }
@@ -1003,12 +1128,16 @@ __device__ __forceinline__ void gemv_epi(int g, int rb, int kind, int B, int r0)
 // residual rows [r0, r0 + nrow) of x and the gains g_next of the next norm
 // are staged in GSM.out / GSM.gain (requested behind the first weight loads,
 // written once the wait is over).
+// Groups [g0, g1) only (g1 < 0: to the end): one pass of a phase whose
+// slot rows do not all fit the staging at once (64-row steps).
 __device__ __noinline__ void gemv_phase(KParams& pk, int wait_idx, int inv_n, uint32_t inv_off, int kind, int r0,
-                                        int nrow, const uint16_t* g_next) {
+                                        int nrow, const uint16_t* g_next, int g0 = 0, int g1 = -1) {
   PARAMS;
   const int B = p.B, H = p.H;
-  GemvStream gs;
-  gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B);
+  if (g1 < 0) g1 = __builtin_amdgcn_readfirstlane(GSM.ngroups);
+  const int s0 = TG * g0;
+  GemvStream<NBT> gs;
+  gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B, g0, g1);
   float xv[4], gv[4];
   if (kind == EPI_RESIDUAL) {
     // buffer loads: an offset past the resource reads 0, so no load is
@@ -1044,8 +1173,30 @@ __device__ __noinline__ void gemv_phase(KParams& pk, int wait_idx, int inv_n, ui
     __syncthreads();
   }
   sub_stamp(p, 0);
-  gemv_run(p, gs, inv_n, inv_off, [=](int g, int rb) { gemv_epi(g, rb, kind, B, r0); });
+  gemv_run(p, gs, inv_n, inv_off, [=](int g, int rb, int j) { gemv_epi(g, rb, j, kind, B, r0, s0); });
   sub_stamp(p, 2);
+}
+
+// A slot-staged phase in staging passes: groups [g0, g1) per pass (one pass
+// unless the slot rows of MAXB tokens exceed the staging), every pass after
+// the first without a wait; post(s0, s1) writes out the staged outputs of
+// slots [s0, s1) (staging row (si - s0) * 16 + row-in-slot).
+template <class Post>
+__device__ __forceinline__ void gemv_passes(KParams& pk, int wait_idx, int inv_n, uint32_t inv_off, Post post) {
+  if constexpr (!WIDE) {  // the slot tables' rows always fit: one pass
+    gemv_phase(pk, wait_idx, inv_n, inv_off, EPI_BY_KIND, 0, 0, nullptr);
+    post(0, __builtin_amdgcn_readfirstlane(GSM.nslots));
+  } else {
+    constexpr int PER = STAGE_ROWS / (16 * TG);
+    const int ng = __builtin_amdgcn_readfirstlane(GSM.ngroups);
+    int g0 = 0;
+    do {
+      const int g1 = ng - g0 < PER ? ng : g0 + PER;
+      gemv_phase(pk, g0 == 0 ? wait_idx : -1, inv_n, inv_off, EPI_BY_KIND, 0, 0, nullptr, g0, g1);
+      post(TG * g0, TG * g1);
+      g0 = g1;
+    } while (g0 < ng);
+  }
 }
 
 // --- QKV projection (GQA): raw q, k, v (RMS-normalised input) -> qkv[t][row]
@@ -1065,15 +1216,16 @@ __device__ __noinline__ void phase_qkv(KParams& pk, int l_layer, int wait_idx) {
     sb.singles_of(mv, p.nkv * p.hd);
   }
   builder_done(p, sb, -1);
-  gemv_phase(p, wait_idx, p.H, ssq_at(p, 2 * l_layer), EPI_BY_KIND, 0, 0, nullptr);
   const int nqkv = (p.nq + 2 * p.nkv) * p.hd;
-  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-  for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
-    int t = e % B, sr = e / B;
-    int m, row;
-    if (!slot_row(sr >> 4, sr & 15, m, row)) continue;
-    st_f32(r, p.off_qkv + (uint32_t)(t * nqkv + GSM.mats[m].tag + row) * 4u, GSM.out[sr][t]);
-  }
+  gemv_passes(p, wait_idx, p.H, ssq_at(p, 2 * l_layer), [&](int s0, int s1) {
+    rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+    for (int e = threadIdx.x; e < (s1 - s0) * 16 * B; e += NT) {
+      int t = e % B, sr = e / B;
+      int m, row;
+      if (!slot_row(s0 + (sr >> 4), sr & 15, m, row)) continue;
+      st_f32(r, p.off_qkv + (uint32_t)(t * nqkv + GSM.mats[m].tag + row) * 4u, GSM.out[sr][t]);
+    }
+  });
 }
 
 // RoPE rotation of pair i at position pos: (cos, sin) from the table the
@@ -1103,9 +1255,9 @@ __device__ __forceinline__ void rope_cs(KParams& pk, int pos, int i, float& c, f
 // per head goes to the workspace; the last workgroup to finish a (b, g)
 // combines the chunks.
 struct AttnSmem {
-  float q[MAXB][128];           // rotated, scaled q of the group's heads
-  float wm[NW + 1][MAXB], wl[NW + 1][MAXB];  // entry NW: the new row (decode, last chunk)
-  alignas(16) float wo[NW][MAXB][128];
+  float q[GSMAX][128];          // rotated, scaled q of the group's heads
+  float wm[NW + 1][GSMAX], wl[NW + 1][GSMAX];  // entry NW: the new row (decode, last chunk)
+  alignas(16) float wo[NW][GSMAX][128];
   float knew[128], vnew[128];   // the new row, as the cache stores it
   int last;
 };
@@ -1558,14 +1710,15 @@ __device__ __noinline__ void phase_kda_proj(KParams& pk, int l_layer, int wait_i
     sb.singles_of(m4, nh);
   }
   builder_done(p, sb, -1);
-  gemv_phase(p, wait_idx, p.H, ssq_at(p, 2 * l_layer), EPI_BY_KIND, 0, 0, nullptr);
-  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-  for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
-    int t = e % B, sr = e / B;
-    int m, row;
-    if (!slot_row(sr >> 4, sr & 15, m, row)) continue;
-    st_f32(r, p.off_kda + (uint32_t)(t * width + GSM.mats[m].tag + row) * 4u, GSM.out[sr][t]);
-  }
+  gemv_passes(p, wait_idx, p.H, ssq_at(p, 2 * l_layer), [&](int s0, int s1) {
+    rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+    for (int e = threadIdx.x; e < (s1 - s0) * 16 * B; e += NT) {
+      int t = e % B, sr = e / B;
+      int m, row;
+      if (!slot_row(s0 + (sr >> 4), sr & 15, m, row)) continue;
+      st_f32(r, p.off_kda + (uint32_t)(t * width + GSM.mats[m].tag + row) * 4u, GSM.out[sr][t]);
+    }
+  });
 }
 
 struct KdaSmem {
@@ -1829,23 +1982,38 @@ __device__ __noinline__ void phase_mla_a(KParams& pk, int l_layer, int wait_idx)
     sb.singles_of(mk, KVR);
   }
   builder_done(p, sb, -1);
-  gemv_phase(p, wait_idx, p.H, ssq_at(p, 2 * l_layer), EPI_BY_KIND, 0, 0, nullptr);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-  float* part = (float*)GSM.red;  // [NT][MAXB]
-  for (int t = 0; t < MAXB; ++t) part[threadIdx.x * MAXB + t] = 0.f;
-  for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
-    int t = e % B, sr = e / B;
+  // staged output (token t, staging row sr of a pass from slot s0); returns
+  // its square for c_q0's norm, 0 for the latent part
+  auto elem = [&](int t, int sr, int s0) -> float {
     int m, row;
-    if (!slot_row(sr >> 4, sr & 15, m, row)) continue;
+    if (!slot_row(s0 + (sr >> 4), sr & 15, m, row)) return 0.f;
     float v = GSM.out[sr][t];
     if (GSM.mats[m].tag == 0) {
       put_hilo(r, uq_at(p, l_layer), QL, t, row, bf16_f32(L.mla_qnorm[row]) * v);
-      part[threadIdx.x * MAXB + t] += v * v;
-    } else {
-      st_f32(r, p.off_ckv + (uint32_t)(t * KVR + row) * 4u, v);
+      return v * v;
     }
+    st_f32(r, p.off_ckv + (uint32_t)(t * KVR + row) * 4u, v);
+    return 0.f;
+  };
+  if constexpr (WIDE) {
+    float acc = 0.f;
+    const int t = threadIdx.x & 63;
+    gemv_passes(p, wait_idx, p.H, ssq_at(p, 2 * l_layer), [&](int s0, int s1) {
+      if (t < B)
+        for (int sr = threadIdx.x >> 6; sr < (s1 - s0) * 16; sr += NT / 64) acc += elem(t, sr, s0);
+    });
+    store_ssq_wide(p, r, acc, ssq2_at(p, l_layer));
+  } else {
+    gemv_phase(p, wait_idx, p.H, ssq_at(p, 2 * l_layer), EPI_BY_KIND, 0, 0, nullptr);
+    float* part = (float*)GSM.red;  // [NT][MAXB]
+    for (int t = 0; t < MAXB; ++t) part[threadIdx.x * MAXB + t] = 0.f;
+    for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
+      int t = e % B, sr = e / B;
+      part[threadIdx.x * MAXB + t] += elem(t, sr, 0);
+    }
+    store_ssq(p, r, part, ssq2_at(p, l_layer));
   }
-  store_ssq(p, r, part, ssq2_at(p, l_layer));
 }
 
 // The new latent cache row of sequence b: RMSNorm(c) * g_kv and the rotated
@@ -1898,20 +2066,23 @@ __device__ __noinline__ void phase_mla_b(KParams& pk, int l_layer, int wait_idx)
     sb.singles_of(m, nh * QW);
   }
   builder_done(p, sb, -1);
-  gemv_phase(p, wait_idx, p.q_lora, ssq2_at(p, l_layer), EPI_BY_KIND, 0, 0, nullptr);
-  if (cb < B) mla_cache_row(p, l_layer, cb);
-  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-  for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
-    int t = e % B, sr = e / B;
-    int m, row;
-    if (!slot_row(sr >> 4, sr & 15, m, row)) continue;
-    st_f32(r, p.off_qm + (uint32_t)(t * nh * QW + row) * 4u, GSM.out[sr][t]);
-  }
+  bool row_done = false;
+  gemv_passes(p, wait_idx, p.q_lora, ssq2_at(p, l_layer), [&](int s0, int s1) {
+    if (!row_done && cb < B) mla_cache_row(p, l_layer, cb);  // (in the input staging, which the stream leaves alone)
+    row_done = true;
+    rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+    for (int e = threadIdx.x; e < (s1 - s0) * 16 * B; e += NT) {
+      int t = e % B, sr = e / B;
+      int m, row;
+      if (!slot_row(s0 + (sr >> 4), sr & 15, m, row)) continue;
+      st_f32(r, p.off_qm + (uint32_t)(t * nh * QW + row) * 4u, GSM.out[sr][t]);
+    }
+  });
 }
 
 // M3: absorbed queries qabs[t][h] = [W_uk,h^T q_nope,h | RoPE(q_pe,h)] / sqrt(nope + rope).
-// Task (h, 128-column block of the latent); all tokens at once, so each
-// slice of W_uk is read once.  W_kvb is row-major [nh*(nope+v)][512]: head
+// Task (h, 128-column block of the latent); the tokens in tiles of 8 (one
+// tile up to 8 rows), so each slice of W_uk is read from memory once.  W_kvb is row-major [nh*(nope+v)][512]: head
 // h's rows are [W_uk,h (nope rows) | W_uv,h (v rows)].
 __device__ __noinline__ void phase_mla_absorb(KParams& pk, int l_layer) {
   PARAMS;
@@ -1920,22 +2091,26 @@ __device__ __noinline__ void phase_mla_absorb(KParams& pk, int l_layer) {
   constexpr int NCB = MLA_KL / 128;
   const int ntask = nh * NCB;
   const float scale = 1.0f / sqrtf((float)QW);
-  float* qn = &GSM.in[0][0];               // [MAXB][nope <= 128]
-  float* red = &GSM.out[0][0];             // [NW][MAXB][128]
+  constexpr int AT = 8;                    // tokens per tile
+  float* qn = &GSM.in[0][0];               // [AT][nope <= 128]
+  float* red = &GSM.out[0][0];             // [NW][AT][128]
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   rsrc_t wrs = make_rsrc_u(L.mla_wkvb, (uint32_t)((size_t)nh * VW * MLA_KL * 2));
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int cg = lane & 15, rg = wv * 4 + (lane >> 4);  // 16 row groups x 16 column groups of 8
   for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
     const int h = task / NCB, cbk = task % NCB;
-    for (int e = threadIdx.x; e < B * nope; e += NT) {
+    for (int t0 = 0; t0 < B; t0 += AT) {
+    const int Bt = B - t0 < AT ? B - t0 : AT;
+    if (t0 > 0) __syncthreads();  // the previous tile's reads of qn and red are done
+    for (int e = threadIdx.x; e < Bt * nope; e += NT) {
       int t = e / nope, i = e % nope;
-      qn[t * 128 + i] = ld_f32(r, p.off_qm + (uint32_t)(t * nh * QW + h * QW + i) * 4u);
+      qn[t * 128 + i] = ld_f32(r, p.off_qm + (uint32_t)((t0 + t) * nh * QW + h * QW + i) * 4u);
     }
     __syncthreads();
-    float acc[MAXB][8];
+    float acc[AT][8];
 #pragma unroll
-    for (int t = 0; t < MAXB; ++t)
+    for (int t = 0; t < AT; ++t)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[t][j] = 0.f;
     for (int i = rg; i < nope; i += 16) {
@@ -1947,29 +2122,30 @@ __device__ __noinline__ void phase_mla_absorb(KParams& pk, int l_layer) {
         wf[2 * j + 1] = __uint_as_float((uint32_t)w[j] & 0xFFFF0000u);
       }
 #pragma unroll
-      for (int t = 0; t < MAXB; ++t) {
-        float qv = t < B ? qn[t * 128 + i] : 0.f;
+      for (int t = 0; t < AT; ++t) {
+        float qv = t < Bt ? qn[t * 128 + i] : 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[t][j] += wf[j] * qv;
       }
     }
     // sum the 4 row groups of this wave, then the 4 waves
 #pragma unroll
-    for (int t = 0; t < MAXB; ++t)
+    for (int t = 0; t < AT; ++t)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[t][j] = rows_sum(acc[t][j]);
     if (lane < 16) {
 #pragma unroll
-      for (int t = 0; t < MAXB; ++t)
+      for (int t = 0; t < AT; ++t)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) red[(wv * MAXB + t) * 128 + 8 * cg + j] = acc[t][j];
+        for (int j = 0; j < 8; ++j) red[(wv * AT + t) * 128 + 8 * cg + j] = acc[t][j];
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < B * 128; e += NT) {
+    for (int e = threadIdx.x; e < Bt * 128; e += NT) {
       int t = e / 128, c = e % 128;
-      float v = red[(0 * MAXB + t) * 128 + c] + red[(1 * MAXB + t) * 128 + c] + red[(2 * MAXB + t) * 128 + c] +
-                red[(3 * MAXB + t) * 128 + c];
-      st_f32(r, p.off_qabs + (uint32_t)((t * nh + h) * MLA_QA + 128 * cbk + c) * 4u, v * scale);
+      float v = red[(0 * AT + t) * 128 + c] + red[(1 * AT + t) * 128 + c] + red[(2 * AT + t) * 128 + c] +
+                red[(3 * AT + t) * 128 + c];
+      st_f32(r, p.off_qabs + (uint32_t)(((t0 + t) * nh + h) * MLA_QA + 128 * cbk + c) * 4u, v * scale);
+    }
     }
     if (cbk == 0) {
       for (int e = threadIdx.x; e < B * (MLA_RD / 2); e += NT) {
@@ -2209,10 +2385,11 @@ __device__ __forceinline__ void phase_mla_out(KParams& pk, int l_layer, int part
   const int B = p.B, nh = p.mla_h, nope = p.nope, vd = p.vdim, VW = nope + vd, C = p.mla_chunks;
   const int nsl = vd / 32;
   const int ntask = nh * nsl;
-  float* z = &GSM.in[0][0];      // [MAXB][512]
-  float* cw = &GSM.out[0][0];    // [MAXB][256] combine weights
-  float* cl = cw + MAXB * 256;   // [MAXB] 1 / denominator
-  float* cs = cl + MAXB;         // [MAXB][256] chunk sums
+  constexpr int OT = 8;          // tokens per tile (one tile up to 8 rows)
+  float* z = &GSM.in[0][0];      // [OT][512]
+  float* cw = &GSM.out[0][0];    // [OT][256] combine weights
+  float* cl = cw + OT * 256;     // [OT] 1 / denominator
+  float* cs = cl + OT;           // [OT][256] chunk sums
   float* zp = &GSM.red[0][0][0][0][0];  // [NT][4] sums over a share of the chunks
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
   rsrc_t wrs = make_rsrc_u(L.mla_wkvb, (uint32_t)((size_t)nh * VW * MLA_KL * 2));
@@ -2222,13 +2399,16 @@ __device__ __forceinline__ void phase_mla_out(KParams& pk, int l_layer, int part
   for (int task = blockIdx.x; (parts & 1) && task < ntask; task += gridDim.x) {
     const int h = task / nsl, q = task % nsl;
     const int d0 = 4 * ((q * (MLA_KL / 4)) / nsl), nd4 = ((q + 1) * (MLA_KL / 4)) / nsl - d0 / 4;
-    for (int e = threadIdx.x; e < B * C; e += NT) {
+    for (int t0 = 0; t0 < B; t0 += OT) {
+    const int Bt = B - t0 < OT ? B - t0 : OT;
+    if (t0 > 0) __syncthreads();  // the previous tile is done with cw, cs, cl and zp
+    for (int e = threadIdx.x; e < Bt * C; e += NT) {
       int t = e / C, cc = e % C;
-      cw[t * 256 + cc] = ld_f32(r, p.off_mml + (uint32_t)((t * C + cc) * nh + h) * 8u);
-      cs[t * 256 + cc] = ld_f32(r, p.off_mml + (uint32_t)((t * C + cc) * nh + h) * 8u + 4u);
+      cw[t * 256 + cc] = ld_f32(r, p.off_mml + (uint32_t)(((t0 + t) * C + cc) * nh + h) * 8u);
+      cs[t * 256 + cc] = ld_f32(r, p.off_mml + (uint32_t)(((t0 + t) * C + cc) * nh + h) * 8u + 4u);
     }
     __syncthreads();
-    for (int t = threadIdx.x >> 6; t < B; t += NW) {  // one wave per token: max, weights, denominator
+    for (int t = threadIdx.x >> 6; t < Bt; t += NW) {  // one wave per token: max, weights, denominator
       const int ln = threadIdx.x & 63;
       float M = -INFINITY;
       for (int cc = ln; cc < C; cc += 64) M = fmaxf(M, cw[t * 256 + cc]);
@@ -2245,7 +2425,7 @@ __device__ __forceinline__ void phase_mla_out(KParams& pk, int l_layer, int part
     __syncthreads();
     // thread per (share s of the chunks, token, 4 dims), MZU chunk loads in flight
     constexpr int MZU = 32;
-    const int items = B * nd4;
+    const int items = Bt * nd4;
     const int S = items < NT ? NT / items : 1;
     const int per = (C + S - 1) / S;
     for (int e = threadIdx.x; e < items * S; e += NT) {
@@ -2257,7 +2437,7 @@ __device__ __forceinline__ void phase_mla_out(KParams& pk, int l_layer, int part
         i32x4 v[MZU];
 #pragma unroll
         for (int u = 0; u < MZU; ++u)
-          v[u] = ld_x4<CP_SC1>(r, c0 + u < cb ? p.off_mz + ((uint32_t)((t * C + c0 + u) * nh + h) * MLA_KL + d4) * 4u : OOB);
+          v[u] = ld_x4<CP_SC1>(r, c0 + u < cb ? p.off_mz + ((uint32_t)(((t0 + t) * C + c0 + u) * nh + h) * MLA_KL + d4) * 4u : OOB);
 #pragma unroll
         for (int u = 0; u < MZU; ++u) {
           float f = c0 + u < cb ? cw[t * 256 + c0 + u] : 0.f;
@@ -2269,7 +2449,7 @@ __device__ __forceinline__ void phase_mla_out(KParams& pk, int l_layer, int part
       }
       if (S == 1) {
         const float il = cl[t];
-        const uint32_t at = p.off_mzc + ((uint32_t)(t * nh + h) * MLA_KL + d4) * 4u;
+        const uint32_t at = p.off_mzc + ((uint32_t)((t0 + t) * nh + h) * MLA_KL + d4) * 4u;
         st_f32(r, at, o0 * il);
         st_f32(r, at + 4u, o1 * il);
         st_f32(r, at + 8u, o2 * il);
@@ -2293,12 +2473,13 @@ __device__ __forceinline__ void phase_mla_out(KParams& pk, int l_layer, int part
           o3 += zp[(sh * items + it) * 4 + 3];
         }
         const float il = cl[t];
-        const uint32_t at = p.off_mzc + ((uint32_t)(t * nh + h) * MLA_KL + d4) * 4u;
+        const uint32_t at = p.off_mzc + ((uint32_t)((t0 + t) * nh + h) * MLA_KL + d4) * 4u;
         st_f32(r, at, o0 * il);
         st_f32(r, at + 4u, o1 * il);
         st_f32(r, at + 8u, o2 * il);
         st_f32(r, at + 12u, o3 * il);
       }
+    }
     }
     wait_stores();
     __syncthreads();
@@ -2327,9 +2508,12 @@ __device__ __forceinline__ void phase_mla_out(KParams& pk, int l_layer, int part
       }
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < B * (MLA_KL / 4); e += NT) {
+    for (int t0 = 0; t0 < B; t0 += OT) {
+    const int Bt = B - t0 < OT ? B - t0 : OT;
+    if (t0 > 0) __syncthreads();  // the previous tile is done with z
+    for (int e = threadIdx.x; e < Bt * (MLA_KL / 4); e += NT) {
       const int t = e / (MLA_KL / 4), d4 = (e % (MLA_KL / 4)) * 4;
-      const i32x4 v = ld_x4<CP_SC1>(r, p.off_mzc + ((uint32_t)(t * nh + h) * MLA_KL + d4) * 4u);
+      const i32x4 v = ld_x4<CP_SC1>(r, p.off_mzc + ((uint32_t)((t0 + t) * nh + h) * MLA_KL + d4) * 4u);
       z[t * MLA_KL + d4 + 0] = __int_as_float(v[0]);
       z[t * MLA_KL + d4 + 1] = __int_as_float(v[1]);
       z[t * MLA_KL + d4 + 2] = __int_as_float(v[2]);
@@ -2338,9 +2522,9 @@ __device__ __forceinline__ void phase_mla_out(KParams& pk, int l_layer, int part
     __syncthreads();
     // o[t][row]: 8 lanes per row, 64 dims each
     {
-      float ot[MAXB];
+      float ot[OT];
 #pragma unroll
-      for (int t = 0; t < MAXB; ++t) ot[t] = 0.f;
+      for (int t = 0; t < OT; ++t) ot[t] = 0.f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         int d = part * 64 + k * 8;
@@ -2351,15 +2535,15 @@ __device__ __forceinline__ void phase_mla_out(KParams& pk, int l_layer, int part
           wf[2 * j + 1] = __uint_as_float((uint32_t)wv[k][j] & 0xFFFF0000u);
         }
 #pragma unroll
-        for (int t = 0; t < MAXB; ++t) {
-          if (t < B) {
+        for (int t = 0; t < OT; ++t) {
+          if (t < Bt) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) ot[t] += wf[j] * z[t * MLA_KL + d + j];
           }
         }
       }
 #pragma unroll
-      for (int t = 0; t < MAXB; ++t) {
+      for (int t = 0; t < OT; ++t) {
         float v = ot[t];
         v += __shfl_xor(v, 1, 64);
         v += __shfl_xor(v, 2, 64);
@@ -2367,8 +2551,9 @@ __device__ __forceinline__ void phase_mla_out(KParams& pk, int l_layer, int part
         ot[t] = v;
       }
       if (part == 0) {
-        for (int t = 0; t < B; ++t) put_hilo(r, ou_at(p, l_layer), nh * vd, t, h * vd + row, ot[t]);
+        for (int t = 0; t < Bt; ++t) put_hilo(r, ou_at(p, l_layer), nh * vd, t0 + t, h * vd + row, ot[t]);
       }
+    }
     }
     __syncthreads();
   }
@@ -2391,7 +2576,7 @@ struct RouteSmem {
 };
 constexpr size_t cmax_(size_t a, size_t b) { return a > b ? a : b; }
 constexpr size_t ROUTE_OFF =
-    (cmax_(cmax_(sizeof(GemvSmem) + (size_t)1024 * MAXB * 4, sizeof(AttnSmem)), cmax_(sizeof(MlaSmem), sizeof(KdaSmem))) + 63) /
+    (cmax_(cmax_(sizeof(GemvSmem) + (WIDE ? 0 : (size_t)1024 * MAXB * 4), sizeof(AttnSmem)), cmax_(sizeof(MlaSmem), sizeof(KdaSmem))) + 63) /
     64 * 64;
 #define RSM (*reinterpret_cast<RouteSmem*>(md_smem + ROUTE_OFF))
 static_assert(ROUTE_OFF + sizeof(RouteSmem) <= PLAN_OFF, "LDS layout exceeds the static LDS block");
@@ -2448,17 +2633,28 @@ __device__ __noinline__ void phase_residual(KParams& pk, int l_layer, int mode, 
   const uint32_t u_next = u_at(p, nxt);
   gemv_phase(p, wait_idx, 0, 0u, EPI_RESIDUAL, r0, nrow, g_next);
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-  static_assert(sizeof(GemvSmem::red) >= sizeof(float) * (NT + NW) * MAXB, "partial sums reuse the reduction scratch");
-  float* part = (float*)GSM.red;  // [NT][MAXB]
-  for (int t = 0; t < MAXB; ++t) part[threadIdx.x * MAXB + t] = 0.f;
-  for (int e = threadIdx.x; e < nrow * B; e += NT) {
-    int t = e % B, lr = e / B;
+  auto elem = [&](int t, int lr) -> float {
     float x = GSM.out[lr][t];
     p.x[t * H + r0 + lr] = x;
     put_hilo(r, u_next, H, t, r0 + lr, GSM.gain[lr] * x);
-    part[threadIdx.x * MAXB + t] += x * x;
+    return x * x;
+  };
+  if constexpr (WIDE) {
+    float acc = 0.f;
+    const int t = threadIdx.x & 63;
+    if (t < B)
+      for (int lr = threadIdx.x >> 6; lr < nrow; lr += NT / 64) acc += elem(t, lr);
+    store_ssq_wide(p, r, acc, ssq_at(p, nxt));
+  } else {
+    static_assert(WIDE || sizeof(GemvSmem::red) >= sizeof(float) * (NT + NW) * MAXB, "partial sums reuse the reduction scratch");
+    float* part = (float*)GSM.red;  // [NT][MAXB]
+    for (int t = 0; t < MAXB; ++t) part[threadIdx.x * MAXB + t] = 0.f;
+    for (int e = threadIdx.x; e < nrow * B; e += NT) {
+      int t = e % B, lr = e / B;
+      part[threadIdx.x * MAXB + t] += elem(t, lr);
+    }
+    store_ssq(p, r, part, ssq_at(p, nxt));
   }
-  store_ssq(p, r, part, ssq_at(p, nxt));
 }
 
 // --- dense SwiGLU gate/up: h = silu(inv*Wg U) * (inv*Wu U) -> hi/lo
@@ -2475,15 +2671,16 @@ __device__ __noinline__ void phase_gateup(KParams& pk, int l_layer, int wait_idx
     sb.pairs_of(mg, mu, F);
   }
   builder_done(p, sb, -1);
-  gemv_phase(p, wait_idx, p.H, ssq_at(p, 2 * l_layer + 1), EPI_BY_KIND, 0, 0, nullptr);
-  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-  for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
-    int t = e % B, sr = e / B;
-    if ((sr >> 4) & 1) continue;  // up slots carry no output
-    int m, row;
-    if (!slot_row(sr >> 4, sr & 15, m, row)) continue;
-    put_hilo(r, h_at(p, l_layer), F, t, row, GSM.out[sr][t]);
-  }
+  gemv_passes(p, wait_idx, p.H, ssq_at(p, 2 * l_layer + 1), [&](int s0, int s1) {
+    rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+    for (int e = threadIdx.x; e < (s1 - s0) * 16 * B; e += NT) {
+      int t = e % B, sr = e / B;
+      if ((sr >> 4) & 1) continue;  // up slots carry no output (passes start on even slots)
+      int m, row;
+      if (!slot_row(s0 + (sr >> 4), sr & 15, m, row)) continue;
+      put_hilo(r, h_at(p, l_layer), F, t, row, GSM.out[sr][t]);
+    }
+  });
 }
 
 // ------------------------------------------------------------------ MoE
@@ -2530,18 +2727,19 @@ __device__ __noinline__ void phase_moe_a(KParams& pk, int l_layer, int wait_idx)
     }
   }
   builder_done(p, sb, -1);
-  gemv_phase(p, wait_idx, p.H, ssq_at(p, 2 * l_layer + 1), EPI_BY_KIND, 0, 0, nullptr);
-  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-  for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
-    int t = e % B, sr = e / B;
-    int si = sr >> 4;
-    bool pair = GSM.grp[si / TG].kind == GK_PAIR;
-    if (pair && (si & 1)) continue;  // up slots carry no output
-    int m, row;
-    if (!slot_row(si, sr & 15, m, row)) continue;
-    if (pair) put_hilo(r, hs_at(p, l_layer), p.shared_ffn, t, row, GSM.out[sr][t]);
-    else st_f32(r, p.off_rl + (uint32_t)(t * p.n_experts + row) * 4u, GSM.out[sr][t]);
-  }
+  gemv_passes(p, wait_idx, p.H, ssq_at(p, 2 * l_layer + 1), [&](int s0, int s1) {
+    rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+    for (int e = threadIdx.x; e < (s1 - s0) * 16 * B; e += NT) {
+      int t = e % B, sr = e / B;
+      int si = s0 + (sr >> 4);
+      bool pair = GSM.grp[si / TG].kind == GK_PAIR;
+      if (pair && (si & 1)) continue;  // up slots carry no output
+      int m, row;
+      if (!slot_row(si, sr & 15, m, row)) continue;
+      if (pair) put_hilo(r, hs_at(p, l_layer), p.shared_ffn, t, row, GSM.out[sr][t]);
+      else st_f32(r, p.off_rl + (uint32_t)(t * p.n_experts + row) * 4u, GSM.out[sr][t]);
+    }
+  });
 }
 
 // Routing of every token from the router logits (fp32, written by phase A):
@@ -2600,8 +2798,8 @@ __device__ __noinline__ void compute_routes(KParams& pk, int layer) {
   __syncthreads();
   // the chosen experts' weight pointers (the slot builders read them here)
   for (int i = threadIdx.x; i < RSM.nu * 3; i += NT) RSM.ex[i / 3][i % 3] = RSM.exall[RSM.u[i / 3]][i % 3];
-  if (threadIdx.x < B * k) {
-    int t = threadIdx.x / k, j = threadIdx.x % k;
+  for (int e = threadIdx.x; e < B * k; e += NT) {
+    int t = e / k, j = e % k;
     RSM.wt[t][RSM.pos[RSM.ids[t][j]]] = RSM.w[t][j];
     if (blockIdx.x == 0 && p.out_ids) p.out_ids[((size_t)layer * B + t) * k + j] = RSM.ids[t][j];
   }
@@ -2621,16 +2819,17 @@ __device__ __noinline__ void phase_moe_b(KParams& pk, int l_layer, int wait_idx)
     sb.expert_pairs(m0, nu, p.expert_ffn);
   }
   builder_done(p, sb, -1);
-  gemv_phase(p, wait_idx, p.H, ssq_at(p, 2 * l_layer + 1), EPI_BY_KIND, 0, 0, nullptr);
-  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-  for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
-    int t = e % B, sr = e / B;
-    if ((sr >> 4) & 1) continue;
-    int m, row;
-    if (!slot_row(sr >> 4, sr & 15, m, row)) continue;
-    int j = GSM.mats[m].tag;
-    put_hilo(r, hr_at(p, l_layer) + (uint32_t)j * p.hr_stride, p.expert_ffn, t, row, GSM.out[sr][t] * RSM.wt[t][j]);
-  }
+  gemv_passes(p, wait_idx, p.H, ssq_at(p, 2 * l_layer + 1), [&](int s0, int s1) {
+    rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
+    for (int e = threadIdx.x; e < (s1 - s0) * 16 * B; e += NT) {
+      int t = e % B, sr = e / B;
+      if ((sr >> 4) & 1) continue;
+      int m, row;
+      if (!slot_row(s0 + (sr >> 4), sr & 15, m, row)) continue;
+      int j = GSM.mats[m].tag;
+      put_hilo(r, hr_at(p, l_layer) + (uint32_t)j * p.hr_stride, p.expert_ffn, t, row, GSM.out[sr][t] * RSM.wt[t][j]);
+    }
+  });
 }
 
 // --- final norm + LM head: logits, per-WG argmax candidates
@@ -2645,34 +2844,69 @@ __device__ __noinline__ void phase_lmhead(KParams& pk, int wait_idx) {
     sb.singles_of(m, p.V);
   }
   builder_done(p, sb, -1);
-  gemv_phase(p, wait_idx, p.H, ssq_at(p, 2 * p.n_layers), EPI_BY_KIND, 0, 0, nullptr);
-  static_assert(sizeof(GemvSmem::in) >= 2 * sizeof(float) * NT * MAXB, "argmax scratch reuses the input staging");
-  float* bv = &GSM.in[0][0];             // [NT][MAXB] best value (the input staging is unused here)
-  int* bi = (int*)(bv + NT * MAXB);      // [NT][MAXB] best index
-  for (int t = 0; t < MAXB; ++t) { bv[threadIdx.x * MAXB + t] = -INFINITY; bi[threadIdx.x * MAXB + t] = 0x7FFFFFFF; }
-  for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
-    int t = e % B, sr = e / B;
-    int m, v;
-    if (!slot_row(sr >> 4, sr & 15, m, v)) continue;
-    float lg = GSM.out[sr][t];
-    p.logits[(size_t)t * p.V + v] = lg;
-    float& cb = bv[threadIdx.x * MAXB + t];
-    int& ci = bi[threadIdx.x * MAXB + t];
-    if (lg > cb || (lg == cb && v < ci)) { cb = lg; ci = v; }
-  }
-  __syncthreads();
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-  if (threadIdx.x < B) {
-    int t = threadIdx.x;
-    float best = -INFINITY;
-    int idx = 0x7FFFFFFF;
-    for (int i = 0; i < NT; ++i) {
-      float v = bv[i * MAXB + t];
-      int k = bi[i * MAXB + t];
-      if (v > best || (v == best && k < idx)) { best = v; idx = k; }
+  if constexpr (WIDE) {
+    // thread tid keeps the best logit of token tid % 64 over its rows of
+    // every pass; then the four waves' candidates of a token, in order
+    float cb = -INFINITY;
+    int ci = 0x7FFFFFFF;
+    const int t = threadIdx.x & 63;
+    gemv_passes(p, wait_idx, p.H, ssq_at(p, 2 * p.n_layers), [&](int s0, int s1) {
+      if (t >= B) return;
+      for (int sr = threadIdx.x >> 6; sr < (s1 - s0) * 16; sr += NT / 64) {
+        int m, v;
+        if (!slot_row(s0 + (sr >> 4), sr & 15, m, v)) continue;
+        const float lg = GSM.out[sr][t];
+        p.logits[(size_t)t * p.V + v] = lg;
+        if (lg > cb || (lg == cb && v < ci)) { cb = lg; ci = v; }
+      }
+    });
+    float* bv = (float*)GSM.red;  // [NT]
+    int* bi = (int*)(bv + NT);    // [NT]
+    __syncthreads();
+    bv[threadIdx.x] = cb;
+    bi[threadIdx.x] = ci;
+    __syncthreads();
+    if (threadIdx.x < B) {
+      float best = -INFINITY;
+      int idx = 0x7FFFFFFF;
+      for (int w = 0; w < NW; ++w) {
+        const float v = bv[64 * w + t];
+        const int k = bi[64 * w + t];
+        if (v > best || (v == best && k < idx)) { best = v; idx = k; }
+      }
+      st_f32(r, p.off_cand + (uint32_t)(blockIdx.x * MAXB + t) * 8u, best);
+      st_u32(r, p.off_cand + (uint32_t)(blockIdx.x * MAXB + t) * 8u + 4u, (uint32_t)idx);
     }
-    st_f32(r, p.off_cand + (uint32_t)(blockIdx.x * MAXB + t) * 8u, best);
-    st_u32(r, p.off_cand + (uint32_t)(blockIdx.x * MAXB + t) * 8u + 4u, (uint32_t)idx);
+  } else {
+    gemv_phase(p, wait_idx, p.H, ssq_at(p, 2 * p.n_layers), EPI_BY_KIND, 0, 0, nullptr);
+    static_assert(WIDE || sizeof(GemvSmem::in) >= 2 * sizeof(float) * NT * MAXB, "argmax scratch reuses the input staging");
+    float* bv = &GSM.in[0][0];             // [NT][MAXB] best value (the input staging is unused here)
+    int* bi = (int*)(bv + NT * MAXB);      // [NT][MAXB] best index
+    for (int t = 0; t < MAXB; ++t) { bv[threadIdx.x * MAXB + t] = -INFINITY; bi[threadIdx.x * MAXB + t] = 0x7FFFFFFF; }
+    for (int e = threadIdx.x; e < GSM.nslots * 16 * B; e += NT) {
+      int t = e % B, sr = e / B;
+      int m, v;
+      if (!slot_row(sr >> 4, sr & 15, m, v)) continue;
+      float lg = GSM.out[sr][t];
+      p.logits[(size_t)t * p.V + v] = lg;
+      float& cb = bv[threadIdx.x * MAXB + t];
+      int& ci = bi[threadIdx.x * MAXB + t];
+      if (lg > cb || (lg == cb && v < ci)) { cb = lg; ci = v; }
+    }
+    __syncthreads();
+    if (threadIdx.x < B) {
+      int t = threadIdx.x;
+      float best = -INFINITY;
+      int idx = 0x7FFFFFFF;
+      for (int i = 0; i < NT; ++i) {
+        float v = bv[i * MAXB + t];
+        int k = bi[i * MAXB + t];
+        if (v > best || (v == best && k < idx)) { best = v; idx = k; }
+      }
+      st_f32(r, p.off_cand + (uint32_t)(blockIdx.x * MAXB + t) * 8u, best);
+      st_u32(r, p.off_cand + (uint32_t)(blockIdx.x * MAXB + t) * 8u + 4u, (uint32_t)idx);
+    }
   }
 }
 
@@ -2749,7 +2983,7 @@ __device__ __forceinline__ void run_one_phase(KParams& pk, int layer, int phase)
 }
 
 // ===================================================================== kernel
-extern "C" __global__ __launch_bounds__(NT) void md_megakernel(Params p_arg) {
+extern "C" __global__ __launch_bounds__(NT) void MD_KERNEL(Params p_arg) {
   KParams& p = *(KParams*)__builtin_amdgcn_kernarg_segment_ptr();
   (void)p_arg;
   if (p.B < 1 || p.B > MAXB) return;
@@ -2855,6 +3089,7 @@ extern "C" __global__ __launch_bounds__(NT) void md_megakernel(Params p_arg) {
 // ===================================================================== launch helpers
 namespace md {
 
+#if MD_MAXB == 8
 // Tiled weight layout (see the GEMV section): one thread per 16-byte chunk of
 // the packed output.  Chunk c of block (t, s) holds row t*16 + 4*(c/16) + c%4,
 // columns s*32 + 8*((c%16)/4) .. +7; rows past the matrix are zero.
@@ -2883,21 +3118,22 @@ hipError_t launch_pack(const void* src, void* dst, int64_t rows, int64_t cols, h
                      rows, cols);
   return hipGetLastError();
 }
+#endif
 
 // All of the kernel's LDS is static (md_smem): launches ask for no dynamic LDS.
-hipError_t launch_megakernel(const Params& p, int grid, hipStream_t stream) {
+hipError_t MD_BUILD_NAME(launch_megakernel)(const Params& p, int grid, hipStream_t stream) {
   void* args[] = {(void*)&p};
-  return hipLaunchCooperativeKernel((const void*)md_megakernel, dim3(grid), dim3(NT), args, 0u, stream);
+  return hipLaunchCooperativeKernel((const void*)MD_KERNEL, dim3(grid), dim3(NT), args, 0u, stream);
 }
 
 // One decode step as a sequence of phase launches on `stream`.
-hipError_t launch_multilaunch(const Params& p, const int* kinds, int grid, hipStream_t stream) {
+hipError_t MD_BUILD_NAME(launch_multilaunch)(const Params& p, const int* kinds, int grid, hipStream_t stream) {
   const unsigned smem = 0u;
   Params q = p;
   auto go = [&](int layer, int phase, int g) {
     q.ml_layer = layer;
     q.ml_phase = phase;
-    hipLaunchKernelGGL(md_megakernel, dim3(g), dim3(NT), smem, stream, q);
+    hipLaunchKernelGGL(MD_KERNEL, dim3(g), dim3(NT), smem, stream, q);
   };
   go(-1, PH_EMBED, grid);
   for (int l = 0; l < p.n_layers; ++l) {
@@ -2932,6 +3168,7 @@ hipError_t launch_multilaunch(const Params& p, const int* kinds, int grid, hipSt
   return hipGetLastError();
 }
 
+#if MD_MAXB == 8
 // ===================================================================== KV movement
 // Copies between attention-cache pages and between sequence slots, for
 // callers that fork a sequence or move its cache (copy-on-write of a shared
@@ -3031,8 +3268,10 @@ hipError_t launch_fill_u32(void* dst, uint32_t v, uint32_t n_words, hipStream_t 
   return hipGetLastError();
 }
 
-hipError_t megakernel_occupancy(int* blocks_per_cu) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, (const void*)md_megakernel, NT, 0);
+#endif
+
+hipError_t MD_BUILD_NAME(megakernel_occupancy)(int* blocks_per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, (const void*)MD_KERNEL, NT, 0);
 }
 
 }  // namespace md

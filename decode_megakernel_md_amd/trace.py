@@ -1,7 +1,7 @@
 """In-kernel phase trace: record per-workgroup wall-clock stamps around every
 sync point of a step (md_set_trace) and summarise phase and wait times.
 
-    python -m decode_megakernel_md_amd.trace [--workload dense_27b] [--batches 1,8]
+    python -m decode_megakernel_md_amd.trace [--workload dense_27b] [--batches 1,8] [--max-batch 64]
 
 prints, per phase kind, the median and slowest workgroup's time per layer,
 the release latency of its sync point (last arrival to median wait end) and
@@ -109,8 +109,11 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="dense_27b")
     ap.add_argument("--batches", default="1,8")
+    ap.add_argument("--max-batch", type=int, default=0, help="sequence slots (above 8: the 64-row kernel build)")
     args = ap.parse_args()
     w = WL.get(args.workload)
+    if args.max_batch:
+        w = w.replace(max_batch=args.max_batch)
     m = DeviceModel(w)
     for B in [int(b) for b in args.batches.split(",")]:
         toks = torch.tensor(synth.tokens(w, B), device=m.device)

@@ -1,7 +1,7 @@
 /*
  * md.h -- C ABI of the MI355X decode megakernel library (libmd.so).
  *
- * One decode step of a whole transformer / MoE decoder for a batch of 1..8
+ * One decode step of a whole transformer / MoE decoder for a batch of 1..64
  * sequences runs as ONE persistent HIP launch on gfx950: embedding, and per
  * layer RMSNorm, attention (GQA, or multi-head latent attention / gated delta
  * rule chosen by layer index), router, shared and routed SwiGLU experts and
@@ -61,7 +61,15 @@ typedef enum {
  * of width ffn_dim; otherwise each layer routes every token to top_k of
  * n_experts SwiGLU experts of width expert_ffn (softmax over all experts,
  * renormalised over the chosen ones when norm_topk) plus n_shared always-on
- * experts of width shared_ffn. */
+ * experts of width shared_ffn.
+ *
+ * max_batch (1..64) is the number of sequence slots.  Models with max_batch
+ * <= 8 run on the library's 8-row kernel build, which also runs the verify
+ * step; larger ones on its 64-row build (decode only: section "Future work"
+ * of the post, higher concurrency), whose step reads every weight once for
+ * all the sequences and whose workspace holds 64 token rows.  On the 64-row
+ * build a GQA model has at most 8 kv heads and a MoE model's experts that a
+ * step's tokens may choose, min(n_experts, 64 * top_k), are at most 36. */
 typedef struct md_config {
   int32_t n_layers, hidden, vocab, max_batch, max_ctx;
   float rms_eps, rope_theta;
@@ -132,7 +140,7 @@ size_t md_workspace_bytes(const md_config* cfg);
  *              (RMS-normalised latent, then the rotated key part)
  *   KDA layer: state fp32[Bm][kda_heads][kda_dk][kda_dv]
  * Sequence b of a batch uses slot b.  Returns 0 (md_last_error says why) for
- * an invalid cfg, batch outside [1, 8] or a capacity the cfg does not allow.
+ * an invalid cfg, batch outside [1, 64] or a capacity the cfg does not allow.
  *
  * Paged configurations (cfg->kv_page = P > 0, cfg->kv_pages = N) give the
  * size of a page pool instead: the GQA and MLA regions hold N pages of P
@@ -256,7 +264,8 @@ md_status md_decode_step_multilaunch(md_model* m, const int32_t* tokens, const i
  *              per layer and row, in descending router order
  * Delta-rule states are committed as they stand after token a-1 (the
  * per-token states pass through the workspace).  batch must be 1.  Out-of-
- * range tokens or positions are reported by md_get_device_status. */
+ * range tokens or positions are reported by md_get_device_status.  Models
+ * with max_batch > 8 return MD_EUNSUPPORTED. */
 md_status md_verify_step(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv_cache,
                          float* out_logits, int32_t* out_accept_len, int32_t* out_next_token,
                          int32_t* out_expert_ids, int32_t batch, int32_t n_tok, void* hip_stream);

@@ -166,7 +166,8 @@ def kv_rows_dev(m, positions, B):
 def compare_kv_rows(w, kv_gpu, kv_ref, positions, B):
     """New cache rows.  Layer 0's row depends only on the embedding and the
     layer's weights, so GPU (fp32) and oracle (fp64) values round to the same
-    bf16 or to neighbours: at most 1 ulp apart.  Deeper rows inherit the
+    bf16 or to neighbours: at most 1 ulp apart (entries far below the row's
+    RMS: within 2^-12 of it).  Deeper rows inherit the
     residual's fp32-vs-fp64 difference: 1 ulp plus 1e-3 of the row's RMS.
     kv_gpu: full host caches (DeviceModel.kv_host) or kv_rows_dev's rows."""
     from tests.ref_numpy import widen
@@ -199,7 +200,13 @@ def compare_kv_rows(w, kv_gpu, kv_ref, positions, B):
             r = ref[l][:, b]
             d_ulp = np.abs(a.astype(np.int32) - r.astype(np.int32))
             if l == 0:
-                assert d_ulp.max() <= 1, f"layer 0 b={b}: cache row differs by {d_ulp.max()} ulp"
+                # within 1 ulp, or (an entry much smaller than its row, from a
+                # cancelling dot product over inputs split into two bf16
+                # halves, about 16 significant bits) within 2^-12 of the row's RMS
+                af, rf = widen(a), widen(r)
+                rms = np.sqrt(np.mean(rf ** 2, axis=-1, keepdims=True))
+                bad = (d_ulp > 1) & (np.abs(af - rf) > 2.0 ** -12 * rms)
+                assert not bad.any(), f"layer 0 b={b}: {int(bad.sum())} cache entries beyond 1 ulp (max {d_ulp.max()})"
             else:
                 af, rf = widen(a), widen(r)
                 rms = np.sqrt(np.mean(rf ** 2, axis=-1, keepdims=True))

@@ -73,12 +73,12 @@ def test_kv_bytes_match_the_documented_layout():
         c = _lib.config_from(w)
         assert L.md_kv_bytes(ctypes.byref(c), w.max_batch, w.max_ctx) == total, name
         # other slot counts and capacities: the same layout with those sizes
-        for B, C in ((1, w.max_ctx), (3, w.max_ctx + 32), (8, 64)):
+        for B, C in ((1, w.max_ctx), (3, w.max_ctx + 32), (8, 64), (64, 64)):
             _, t2 = WL.kv_layout(w.replace(max_batch=B, max_ctx=C))
             assert L.md_kv_bytes(ctypes.byref(c), B, C) == t2, (name, B, C)
     c = _lib.config_from(WL.mini_dense())
     assert L.md_kv_bytes(ctypes.byref(c), 0, 64) == 0 and "batch" in _err()
-    assert L.md_kv_bytes(ctypes.byref(c), 9, 64) == 0
+    assert L.md_kv_bytes(ctypes.byref(c), 65, 64) == 0
     assert L.md_kv_bytes(ctypes.byref(c), 2, 80) == 0     # not a multiple of the 32-position V tiles
 
 
@@ -123,7 +123,7 @@ def test_paged_entry_point_argument_checks():
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("max_batch", 9, _lib.MD_EINVAL),
+    ("max_batch", 65, _lib.MD_EINVAL),
     ("max_batch", 0, _lib.MD_EINVAL),
     ("hidden", 330, _lib.MD_EUNSUPPORTED),
     ("head_dim", 96, _lib.MD_EUNSUPPORTED),
@@ -158,8 +158,9 @@ def test_moe_and_hybrid_limits():
 
 def test_kv_head_count_fits_the_attention_counters():
     """The GQA attention phase counts each (row, kv head)'s finished chunks in
-    one word of a 288-word sync point: 8 rows x 36 kv heads fit, 37 do not
-    (they would spill into the next layer's counters)."""
+    one word of a sync point: 288 words for up to 8 rows (8 x 36 kv heads
+    fit, 37 do not: they would spill into the next layer's counters), 544
+    for up to 64 rows (max_batch > 8: 8 kv heads fit, 9 do not)."""
     L = _lib.lib()
     h = P()
     ok = _cfg("mini_dense", n_q_heads=36, n_kv_heads=36, head_dim=64)
@@ -168,6 +169,31 @@ def test_kv_head_count_fits_the_attention_counters():
     assert L.md_workspace_bytes(ctypes.byref(bad)) == 0
     assert L.md_init_model(ctypes.byref(bad), None, 0, None, 0, None, ctypes.byref(h)) == _lib.MD_EUNSUPPORTED
     assert "kv heads" in _err()
+    ok = _cfg("mini_dense", max_batch=64, n_q_heads=8, n_kv_heads=8, head_dim=64)
+    assert L.md_workspace_bytes(ctypes.byref(ok)) > 0
+    bad = _cfg("mini_dense", max_batch=9, n_q_heads=9, n_kv_heads=9, head_dim=64)
+    assert L.md_workspace_bytes(ctypes.byref(bad)) == 0
+    assert "kv heads" in _err()
+
+
+def test_wide_batch_workspace_and_expert_limit():
+    """max_batch > 8 runs on the 64-row kernel build: the activation buffers
+    hold 64 token rows whatever the model's max_batch, and the routed-expert
+    union of a step may reach min(n_experts, 64 * top_k) experts, two matrices
+    each, of the 72 a phase's tables hold."""
+    L = _lib.lib()
+    h = P()
+    w8 = L.md_workspace_bytes(ctypes.byref(_cfg("mini_dense", max_batch=8)))
+    w9 = L.md_workspace_bytes(ctypes.byref(_cfg("mini_dense", max_batch=9)))
+    w64 = L.md_workspace_bytes(ctypes.byref(_cfg("mini_dense", max_batch=64)))
+    assert 0 < w8 < w9 == w64
+    assert L.md_workspace_bytes(ctypes.byref(_cfg("mini_moe", max_batch=64))) > 0   # 12 experts
+    c = _cfg("mini_moe", n_experts=37, max_batch=8)       # union <= 8 * 3 = 24 experts
+    assert L.md_workspace_bytes(ctypes.byref(c)) > 0
+    c = _cfg("mini_moe", n_experts=37, max_batch=16)      # union up to all 37
+    assert L.md_workspace_bytes(ctypes.byref(c)) == 0
+    assert L.md_init_model(ctypes.byref(c), None, 0, None, 0, None, ctypes.byref(h)) == _lib.MD_EUNSUPPORTED
+    assert "distinct experts" in _err()
 
 
 def test_init_argument_checks_before_any_device_call():

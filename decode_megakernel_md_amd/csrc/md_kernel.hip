@@ -289,11 +289,16 @@ __device__ __forceinline__ KvLoc kv_loc(KParams& pk, int s, int pos) {
 // pointer argument) so that accesses compile to LDS instructions.  It is a
 // static array: functions reach it at a fixed address (dynamic LDS would be
 // found through a per-kernel offset table in memory, a load in the stream).
-constexpr size_t MD_SMEM_BYTES = 130 * 1024;
+// (the 64-row build takes nearly all of the CU's 160 KB: its epilogue
+// staging holds 64 tokens per row)
+constexpr size_t MD_SMEM_BYTES = WIDE ? 160 * 1024 - 256 : 130 * 1024;
 __shared__ __attribute__((aligned(16))) char md_smem[MD_SMEM_BYTES];
 
 constexpr int CMAX_DEV = 256;    // largest chunk count per (sequence, kv head)
-constexpr int TG = 2;            // slots per group (share one B operand load); even: SwiGLU pairs
+// slots per group (they share every B operand load); even: SwiGLU pairs.
+// 4 in the 64-row build: twice the weight bytes per k-step for the same B
+// operands (its ring is only GDS = 2 deep)
+constexpr int TG = WIDE ? 4 : 2;
 // k-steps in flight per wave: 8 (measured: 4 and 8 stream equally fast,
 // deeper is slower); fewer in the 64-row build, whose ring holds 8 B
 // operands per k-step
@@ -301,7 +306,8 @@ constexpr int GDS = WIDE ? 2 : 8;
 constexpr int MAXSLOT = 96;      // slots per workgroup and phase
 constexpr int MAXGRP = MAXSLOT / TG;
 constexpr int MAXMAT = 72;       // matrices per phase
-constexpr int STAGE_ROWS = 768 * 8 / MAXB;  // epilogue staging rows per workgroup (of MAXB tokens)
+constexpr int STAGE_ROWS = WIDE ? 192 : 768;  // epilogue staging rows per workgroup (of MAXB tokens)
+constexpr int IN_ROWS = WIDE ? 96 : 768;       // input staging rows (scratch of the MLA phases)
 constexpr int MIN_KS = NW;       // every wave needs a k-step of every group
 
 struct RowSplit {
@@ -352,7 +358,7 @@ struct GemvSmem {
   // written after it ends, so the stream itself issues no other memory
   // operation.  Indexed by slot row (slot*16 + row-in-slot) or, in phases
   // that own residual rows, by row - first owned row.
-  float in[STAGE_ROWS][MAXB];
+  float in[IN_ROWS][MAXB];
   float out[STAGE_ROWS][MAXB];
   float gain[STAGE_ROWS];
   float inv[MAXB];

@@ -10,7 +10,10 @@ Batch 1 gives `value`; batch 8 is reported beside it.
 
 Prints one JSON line.  `roofline.achieved` = algorithmic bytes of one step
 (active weights + KV rows read) / mean duration of one megakernel launch,
-timed with HIP events on the launch stream.
+timed with HIP events on the launch stream.  `extra` holds the hybrid MoE
+model at batch 1 and 8, its verify step, paged-cache runs of both models and
+both models with 64 sequence slots (the library's 64-row kernel build) at
+batches of 16 to 64.
 """
 from __future__ import annotations
 
@@ -399,6 +402,12 @@ def main():
             pres, _ = decode_bench(wp, [1, 8], ps, args.warmup, multilaunch=False, block_table=bt.astype(np.int32))
             extra[wp.name] = {"steps": ps, "kv_page": page, "kv_pages": wp.kv_pages,
                               "batches": {str(B): pres[B] for B in pres}}
+        # more than 8 sequences: models with 64 slots run on the 64-row build
+        for base, bs in ((WL.dense_27b(), [16, 32, 64]), (WL.hybrid_moe(), [16, 64])):
+            ww = base.replace(name=base.name + "_b64", max_batch=64)
+            wsteps = min(8, ww.max_ctx - ww.context - args.warmup)
+            wres, _ = decode_bench(ww, bs, wsteps, args.warmup, multilaunch=False)
+            extra[ww.name] = {"steps": wsteps, "max_batch": 64, "batches": {str(B): wres[B] for B in wres}}
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(w, layers=w.mla_every if w.attn_kind == 1 else 8)

@@ -2,6 +2,7 @@
 
     python -m decode_megakernel_md_amd.profile_run [--workload dense_27b] [--batch 1] [--steps 3]
                                                     [--multilaunch | --compare] [--copy-mib 1024]
+                                                    [--max-batch 64]
 
 First a plain device-to-device copy of --copy-mib MiB (its byte count is
 known, so HBM counters read for it calibrate the counters read for the
@@ -39,6 +40,7 @@ def main():
     ap.add_argument("--multilaunch", action="store_true")
     ap.add_argument("--compare", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--max-batch", type=int, default=0, help="sequence slots (above 8: the 64-row kernel build)")
     args = ap.parse_args()
     import torch
     import synth
@@ -58,6 +60,8 @@ def main():
     print(f"# calibration copy: {n} bytes read, {n} bytes written", flush=True)
 
     w = WL.get(args.workload)
+    if args.max_batch:
+        w = w.replace(name=w.name + f"_b{args.max_batch}", max_batch=args.max_batch)
     m = DeviceModel(w)
     B = args.batch
     toks = torch.empty((args.steps + 1, B), dtype=torch.int32, device=dev)

@@ -115,16 +115,16 @@ def kernel_source_hash() -> str:
 
 
 def traffic_record(fetch_csv: str, write_csv: str, workload: str, batch: int) -> Dict:
-    """HBM bytes per md_megakernel launch from a FETCH_SIZE and a WRITE_SIZE
+    """HBM bytes per megakernel launch (either build) from a FETCH_SIZE and a WRITE_SIZE
     run.  Both counters are in KiB per dispatch; the calibration copy of
     COPY_BYTES read and written gives each counter's bytes-per-unit factor."""
     out = {"workload": workload, "batch": batch, "kernel_sha256": kernel_source_hash()}
     for name, path in (("fetch", fetch_csv), ("write", write_csv)):
         rows = list(csv.DictReader(open(path)))
         copy = sum(float(r["Counter_Value"]) for r in rows if COPY_KERNEL in r["Kernel_Name"])
-        mk = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"] == "md_megakernel"]
+        mk = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"] in ("md_megakernel", "md_megakernel_w64")]
         if copy <= 0 or not mk:
-            raise ValueError(f"{path}: no calibration copy or no md_megakernel dispatch")
+            raise ValueError(f"{path}: no calibration copy or no megakernel dispatch")
         factor = COPY_BYTES / (copy * 1024.0)
         out[name + "_kib_per_dispatch"] = sum(mk) / len(mk)
         out[name + "_factor"] = factor

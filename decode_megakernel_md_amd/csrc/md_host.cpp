@@ -338,6 +338,20 @@ struct md_model {
   bool wide = false;            // runs on the 64-row build (max_batch > 8)
 };
 
+// Whether the routed gate/up phase of a step of `rows` token rows streams
+// every expert: when the tokens are expected to leave fewer than half an
+// expert unchosen (uniform routing: E (1 - k/E)^rows < 0.5), streaming them
+// all costs almost no bytes and lets the stream start before the routing is
+// known.  Needs room for every expert in the routed hidden buffers and the
+// phase's matrix table.
+static int moe_all_experts(const md_config* c, int rows) {
+  if (c->n_experts <= 0) return 0;
+  const int E = c->n_experts, k = c->top_k;
+  const int nu_max = E < row_stride(c) * k ? E : row_stride(c) * k;
+  if (nu_max < E || 2 * E > 72) return 0;
+  return (double)E * pow(1.0 - (double)k / (double)E, (double)rows) < 0.5 ? 1 : 0;
+}
+
 // One decode or verify step on the model's kernel build.
 static hipError_t launch_step(const md_model* m, const Params& p, hipStream_t stream) {
   return m->wide ? launch_megakernel_w64(p, m->grid, stream) : launch_megakernel(p, m->grid, stream);
@@ -546,6 +560,7 @@ static md_status fill_params(md_model* m, const int32_t* tokens, const int32_t* 
   p.n_experts = c->n_experts; p.top_k = c->top_k; p.expert_ffn = c->expert_ffn; p.n_shared = c->n_shared;
   p.shared_ffn = c->shared_ffn; p.norm_topk = c->norm_topk;
   p.B = batch;
+  p.moe_all = moe_all_experts(c, batch);
   p.attn_chunks = attn_chunks(c, m->grid, batch);
   p.tokens = tokens; p.positions = positions; p.kv = (uint8_t*)kv; p.logits = out_logits;
   p.out_tokens = out_tokens; p.out_ids = out_ids;
@@ -666,6 +681,7 @@ static md_status verify_step(md_model* m, const int32_t* tokens, const int32_t* 
   if (st != MD_OK) return st;
   const md_config* c = &m->cfg;
   p.B = n_tok;
+  p.moe_all = moe_all_experts(c, n_tok);
   p.verify = 1;
   p.out_accept = out_accept_len;
   p.out_next = out_next_token;

@@ -2795,6 +2795,7 @@ __device__ __noinline__ void compute_routes(KParams& pk, int layer) {
   if (threadIdx.x < 64) {  // U = the union, ascending; expert e (lane e) sits at popcount of the ids below it
     uint64_t mask = 0;
     for (int t = 0; t < B; ++t) mask |= RSM.mask[t];
+    if (p.moe_all) mask = E == 64 ? ~0ull : (1ull << E) - 1ull;  // every expert streams (weight 0 if unchosen)
     const bool in = (mask >> lane) & 1ull;
     const int at = __popcll(mask & ((1ull << lane) - 1ull));
     if (in) RSM.u[at] = lane;
@@ -2812,20 +2813,27 @@ __device__ __noinline__ void compute_routes(KParams& pk, int layer) {
   __syncthreads();
 }
 
-__device__ __noinline__ void phase_moe_b(KParams& pk, int l_layer, int wait_idx) {
+// route_after (p.moe_all): every expert's gate/up streams, so the tables
+// need no routing and the first k-steps are requested before the wait for
+// the router logits; the routing runs after the stream, before the outputs
+// are scaled (experts no token chose get weight 0).  Otherwise the routing
+// is done and the chosen experts' union is streamed.
+__device__ __noinline__ void phase_moe_b(KParams& pk, int l_layer, int wait_idx, bool route_after) {
   PARAMS;
   KLayer& L = layer_ref(p, l_layer);
   const int B = p.B;
   SlotBuilder sb;
+  if (route_after) __syncthreads();  // every expert's pointers (prefetch_experts) are in LDS
   if (threadIdx.x < 64) {
     sb.start();
     sb.begin(u_at(p, 2 * l_layer + 1), p.H, GK_PAIR);
-    const int nu = __builtin_amdgcn_readfirstlane(RSM.nu);
-    const int m0 = sb.expert_mats<2>(RSM.ex, nu, 0, p.expert_ffn, p.H, true);
+    const int nu = route_after ? p.n_experts : __builtin_amdgcn_readfirstlane(RSM.nu);
+    const int m0 = sb.expert_mats<2>(route_after ? RSM.exall : RSM.ex, nu, 0, p.expert_ffn, p.H, true);
     sb.expert_pairs(m0, nu, p.expert_ffn);
   }
   builder_done(p, sb, -1);
   gemv_passes(p, wait_idx, p.H, ssq_at(p, 2 * l_layer + 1), [&](int s0, int s1) {
+    if (route_after && s0 == 0) compute_routes(p, l_layer);
     rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
     for (int e = threadIdx.x; e < (s1 - s0) * 16 * B; e += NT) {
       int t = e % B, sr = e / B;
@@ -2970,7 +2978,7 @@ __device__ __forceinline__ void run_one_phase(KParams& pk, int layer, int phase)
     case PH_GATEUP: phase_gateup(p, l_layer, -1); break;
     case PH_DOWN: phase_residual(p, l_layer, RES_DENSE_DOWN, g_next, -1); break;
     case PH_MOE_A: phase_moe_a(p, l_layer, -1); break;
-    case PH_MOE_B: prefetch_experts(p, l); compute_routes(p, l); phase_moe_b(p, l_layer, -1); break;
+    case PH_MOE_B: prefetch_experts(p, l); compute_routes(p, l); phase_moe_b(p, l_layer, -1, false); break;
     case PH_MOE_C: prefetch_experts(p, l); compute_routes(p, l); phase_residual(p, l_layer, RES_MOE_DOWN, g_next, -1); break;
     case PH_KDA_PROJ: phase_kda_proj(p, l_layer, -1); break;
     case PH_KDA_REC: phase_kda_rec(p, l_layer); break;
@@ -3064,9 +3072,13 @@ extern "C" __global__ __launch_bounds__(NT) void MD_KERNEL(Params p_arg) {
       phase_moe_a(p, l_layer, sidx++);
       ARRIVE();
       prefetch_experts(p, l);
-      WAIT();
-      compute_routes(p, l);
-      phase_moe_b(p, l_layer, -1);
+      if (p.moe_all) {
+        phase_moe_b(p, l_layer, sidx++, true);
+      } else {
+        WAIT();
+        compute_routes(p, l);
+        phase_moe_b(p, l_layer, -1, false);
+      }
       ARRIVE();
       phase_residual(p, l_layer, RES_MOE_DOWN, g_next, sidx++);
       ARRIVE();

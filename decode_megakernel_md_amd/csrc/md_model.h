@@ -109,6 +109,8 @@ struct Params {
   unsigned spin_limit;
   uint64_t* trace;    // optional: per WG trace_n wall-clock stamps (phase end, then start after the wait)
   int trace_n;
+  int moe_all;        // 1: the routed gate/up phase streams every expert (the step's tokens are expected to
+                      // choose them all), so its stream starts before the routing is known
 };
 
 }  // namespace md

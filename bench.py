@@ -391,7 +391,8 @@ def main():
                                                 "unit": "GB/s", "frac": hres[B]["frac"],
                                                 "traffic": traffic_bytes("hybrid_moe", B)} for B in hres}}
         wv = WL.verify_hybrid()
-        extra[wv.name] = {"steps": 8, "verify": {str(a): r for a, r in verify_bench(wv, 8).items()}}
+        extra[wv.name] = {"steps": 8, "verify": {str(a): r for a, r in verify_bench(wv, 8).items()},
+                          "traffic": traffic_bytes("verify_hybrid", 8)}
         # paged attention caches: every sequence's pages scattered over a pool
         # in random order (the same bytes per step as the contiguous runs)
         for base, page in ((WL.dense_27b(), 128), (WL.hybrid_moe(), 32)):
@@ -407,7 +408,8 @@ def main():
             ww = base.replace(name=base.name + "_b64", max_batch=64)
             wsteps = min(8, ww.max_ctx - ww.context - args.warmup)
             wres, _ = decode_bench(ww, bs, wsteps, args.warmup, multilaunch=False)
-            extra[ww.name] = {"steps": wsteps, "max_batch": 64, "batches": {str(B): wres[B] for B in wres}}
+            extra[ww.name] = {"steps": wsteps, "max_batch": 64, "batches": {str(B): wres[B] for B in wres},
+                              "traffic": {str(B): traffic_bytes(base.name + "_b64", B) for B in wres}}
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(w, layers=w.mla_every if w.attn_kind == 1 else 8)

@@ -2,14 +2,16 @@
 
     python -m decode_megakernel_md_amd.profile_run [--workload dense_27b] [--batch 1] [--steps 3]
                                                     [--multilaunch | --compare] [--copy-mib 1024]
-                                                    [--max-batch 64]
+                                                    [--max-batch 64] [--verify]
 
 First a plain device-to-device copy of --copy-mib MiB (its byte count is
 known, so HBM counters read for it calibrate the counters read for the
 decode step), then --steps decode steps of the workload at the given batch
 and context, greedy tokens chained on the device.  --compare runs the steps
 once as the megakernel and, after a pause of 20 ms, once as the multi-launch
-baseline (one launch per phase), so that one kernel trace holds both."""
+baseline (one launch per phase), so that one kernel trace holds both.
+--verify runs --steps verify launches (an anchor and 7 uniform random drafts of
+sequence 0 at the workload's context) instead of decode steps."""
 from __future__ import annotations
 
 import argparse
@@ -41,6 +43,7 @@ def main():
     ap.add_argument("--compare", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--max-batch", type=int, default=0, help="sequence slots (above 8: the 64-row kernel build)")
+    ap.add_argument("--verify", action="store_true", help="verify launches (1 anchor + 7 drafts) instead of decode steps")
     args = ap.parse_args()
     import torch
     import synth
@@ -70,7 +73,21 @@ def main():
     ids = None
     if w.is_moe:
         ids = torch.empty((w.n_layers, B, w.top_k), dtype=torch.int32, device=dev)
-    modes = [False, True] if args.compare else [args.multilaunch]
+    if args.verify:
+        import numpy as np
+        n = 8
+        vt = torch.tensor(np.random.default_rng(5).integers(0, w.vocab, size=(1, n)).astype(np.int32), device=dev)
+        vp = torch.full((1,), w.context, dtype=torch.int32, device=dev)
+        vlog = torch.empty((1, n, w.vocab), dtype=torch.float32, device=dev)
+        acc = torch.empty((1,), dtype=torch.int32, device=dev)
+        nxt = torch.empty((1,), dtype=torch.int32, device=dev)
+        for s in range(args.steps):
+            m.verify(vt, vp, vlog, acc, nxt)
+        torch.cuda.synchronize()
+        m.device_status()
+        print(f"# {w.name}: {args.steps} verify launches of 1 + {n - 1} tokens", flush=True)
+        del vt, vp, vlog, acc, nxt
+    modes = [] if args.verify else ([False, True] if args.compare else [args.multilaunch])
     for ml in modes:
         for s in range(args.steps):
             pos = torch.full((B,), w.context + s, dtype=torch.int32, device=dev)

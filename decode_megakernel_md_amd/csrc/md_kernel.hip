@@ -2214,7 +2214,7 @@ __device__ __forceinline__ void mla_load_block(KParams& pk, i32x4 (&pf)[9], rsrc
 #pragma unroll
   for (int k = 0; k < 9; ++k) {
     const int c16 = (threadIdx.x >> 5) + 8 * k;
-    pf[k] = ld_x4<CP_SC1>(crs, t < a1 ? (row * MLA_QA + c16 * 8) * 2u : OOB);
+    pf[k] = ld_x4<0>(crs, t < a1 ? (row * MLA_QA + c16 * 8) * 2u : OOB);
   }
 }
 // Row-major copy, and the transposed copy of the latent chunks (k < 8): the
@@ -2244,7 +2244,13 @@ __device__ __forceinline__ void mla_store_block(const i32x4 (&pf)[9]) {
   }
 }
 
-__device__ __forceinline__ void phase_mla_attn(KParams& pk, int l_layer) {
+// The cache rows are read with the default policy (kept in the XCD's L2):
+// the rows of earlier steps were written in earlier launches, and this
+// step's new rows were written (written through) before the previous sync
+// point and read by nobody before, so no L2 holds an older copy of them.
+// The task's first two blocks are requested before the wait for the
+// absorbed queries (the rows are final by then); two blocks stay in flight.
+__device__ __forceinline__ void phase_mla_attn(KParams& pk, int l_layer, int wait_idx) {
   PARAMS;
   KLayer& L = layer_ref(p, l_layer);
   MlaSmem& sm = *(MlaSmem*)md_smem;
@@ -2254,16 +2260,26 @@ __device__ __forceinline__ void phase_mla_attn(KParams& pk, int l_layer) {
   const int h0 = 8 * wv;                      // scores and softmax: heads h0..h0+7
   const int hb = 16 * (wv & 1), db = 256 * (wv >> 1);  // P.C: heads hb..hb+15, dims db..db+255
   rsrc_t wr = make_rsrc_u(p.ws, p.ws_bytes);
-  for (int task = blockIdx.x; task < B * C; task += gridDim.x) {
-    const int c = task % C, b = task / C;
-    const int pos = row_pos(p, b);
+  const rsrc_t crs = make_rsrc_u(p.kv + L.kv_off, (uint32_t)((size_t)p.n_pages * p.pg_cap * MLA_QA * 2));
+  i32x4 pfA[9], pfB[9];  // blocks in flight
+  // task geometry: chunk c of row b, cache rows [a0, a1)
+  int b = 0, c = 0, pos = 0, a0 = 0, a1 = 0, sq = 0;
+  auto task_of = [&](int task) __attribute__((always_inline)) {
+    c = task % C;
+    b = task / C;
+    pos = row_pos(p, b);
     const int n = pos + 1;
     const int P = (n + C - 1) / C;
-    const int a0 = c * P < n ? c * P : n, a1 = (c + 1) * P < n ? (c + 1) * P : n;
-    const int sq = row_seq(p, b);
-    rsrc_t crs = make_rsrc_u(p.kv + L.kv_off, (uint32_t)((size_t)p.n_pages * p.pg_cap * MLA_QA * 2));
-    i32x4 pf[9];
-    if (a0 < a1) mla_load_block(p, pf, crs, sq, a0, a1);
+    a0 = c * P < n ? c * P : n;
+    a1 = (c + 1) * P < n ? (c + 1) * P : n;
+    sq = row_seq(p, b);
+    if (a0 < a1) mla_load_block(p, pfA, crs, sq, a0, a1);
+    if (a0 + 32 < a1) mla_load_block(p, pfB, crs, sq, a0 + 32, a1);
+  };
+  if ((int)blockIdx.x < B * C) task_of(blockIdx.x);
+  wait_point(p, wait_idx);
+  for (int task = blockIdx.x; task < B * C; task += gridDim.x) {
+    if (task != (int)blockIdx.x) task_of(task);
     // this wave's heads' absorbed queries as hi/lo B operands
     bf16x8 qb[MLA_KS];
     {
@@ -2290,11 +2306,12 @@ __device__ __forceinline__ void phase_mla_attn(KParams& pk, int l_layer) {
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) z[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (a0 < a1) mla_store_block(pf);
+    if (a0 < a1) mla_store_block(pfA);
     __syncthreads();
-    for (int blk = a0; blk < a1; blk += 32) {
-      const bool more = blk + 32 < a1;
-      if (more) mla_load_block(p, pf, crs, sq, blk + 32, a1);
+    // block blk (in LDS): its scores, softmax and P.C; nxt holds block
+    // blk + 32 (in flight), spare is free and takes block blk + 64
+    auto step = [&](const i32x4 (&nxt)[9], i32x4 (&spare)[9], int blk) __attribute__((always_inline)) {
+      if (blk + 64 < a1) mla_load_block(p, spare, crs, sq, blk + 64, a1);
       // scores of 32 positions x this wave's 8 heads
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -2346,10 +2363,14 @@ __device__ __forceinline__ void phase_mla_attn(KParams& pk, int l_layer) {
         }
       }
       __syncthreads();  // every wave is done with this block's rows, transposed copy and P
-      if (more) {
-        mla_store_block(pf);
+      if (blk + 32 < a1) {
+        mla_store_block(nxt);
         __syncthreads();
       }
+    };
+    for (int blk = a0; blk < a1; blk += 64) {
+      step(pfB, pfA, blk);
+      if (blk + 32 < a1) step(pfA, pfB, blk + 32);
     }
     // partials: (m, l) of the softmax heads by lane 0; z of the P.C heads, 4 dims per tile
 #pragma unroll
@@ -2986,7 +3007,7 @@ __device__ __forceinline__ void run_one_phase(KParams& pk, int layer, int phase)
     case PH_MLA_A: phase_mla_a(p, l_layer, -1); break;
     case PH_MLA_B: phase_mla_b(p, l_layer, -1); break;
     case PH_MLA_ABS: phase_mla_absorb(p, l_layer); break;
-    case PH_MLA_ATTN: phase_mla_attn(p, l_layer); break;
+    case PH_MLA_ATTN: phase_mla_attn(p, l_layer, -1); break;
     case PH_MLA_OUT: phase_mla_out(p, l_layer, 1); break;
     case PH_MLA_OUT2: phase_mla_out(p, l_layer, 2); break;
     case PH_MLA_O: phase_residual(p, l_layer, RES_MLA_O, L.ffn_norm, -1); break;
@@ -3054,8 +3075,7 @@ extern "C" __global__ __launch_bounds__(NT) void MD_KERNEL(Params p_arg) {
       WAIT();
       phase_mla_absorb(p, l_layer);
       ARRIVE();
-      WAIT();
-      phase_mla_attn(p, l_layer);
+      phase_mla_attn(p, l_layer, sidx++);
       ARRIVE();
       WAIT();
       phase_mla_out(p, l_layer, 3);

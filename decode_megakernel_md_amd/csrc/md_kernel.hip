@@ -2090,7 +2090,7 @@ __device__ __noinline__ void phase_mla_b(KParams& pk, int l_layer, int wait_idx)
 // Task (h, 128-column block of the latent); the tokens in tiles of 8 (one
 // tile up to 8 rows), so each slice of W_uk is read from memory once.  W_kvb is row-major [nh*(nope+v)][512]: head
 // h's rows are [W_uk,h (nope rows) | W_uv,h (v rows)].
-__device__ __noinline__ void phase_mla_absorb(KParams& pk, int l_layer) {
+__device__ __noinline__ void phase_mla_absorb(KParams& pk, int l_layer, int wait_idx) {
   PARAMS;
   KLayer& L = layer_ref(p, l_layer);
   const int B = p.B, nh = p.mla_h, nope = p.nope, QW = nope + MLA_RD, VW = nope + p.vdim;
@@ -2104,8 +2104,23 @@ __device__ __noinline__ void phase_mla_absorb(KParams& pk, int l_layer) {
   rsrc_t wrs = make_rsrc_u(L.mla_wkvb, (uint32_t)((size_t)nh * VW * MLA_KL * 2));
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int cg = lane & 15, rg = wv * 4 + (lane >> 4);  // 16 row groups x 16 column groups of 8
+  // this thread's rows rg, rg + 16, ... (nope <= 128: at most 8) of the
+  // task's W_uk slice, requested before the wait (the weights depend on no
+  // other workgroup) and used by every token tile
+  i32x4 wk[8];
+  auto load_w = [&](int task) __attribute__((always_inline)) {
+    const int h = task / NCB, cbk = task % NCB;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = rg + 16 * k;
+      wk[k] = ld_x4<0>(wrs, i < nope ? (uint32_t)(((h * VW + i) * MLA_KL) + 128 * cbk + 8 * cg) * 2u : OOB);
+    }
+  };
+  if ((int)blockIdx.x < ntask) load_w(blockIdx.x);
+  wait_point(p, wait_idx);
   for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
     const int h = task / NCB, cbk = task % NCB;
+    if (task != (int)blockIdx.x) load_w(task);
     for (int t0 = 0; t0 < B; t0 += AT) {
     const int Bt = B - t0 < AT ? B - t0 : AT;
     if (t0 > 0) __syncthreads();  // the previous tile's reads of qn and red are done
@@ -2119,8 +2134,11 @@ __device__ __noinline__ void phase_mla_absorb(KParams& pk, int l_layer) {
     for (int t = 0; t < AT; ++t)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[t][j] = 0.f;
-    for (int i = rg; i < nope; i += 16) {
-      i32x4 w = ld_x4<0>(wrs, (uint32_t)(((h * VW + i) * MLA_KL) + 128 * cbk + 8 * cg) * 2u);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = rg + 16 * k;
+      if (i >= nope) break;
+      const i32x4 w = wk[k];
       float wf[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -3006,7 +3024,7 @@ __device__ __forceinline__ void run_one_phase(KParams& pk, int layer, int phase)
     case PH_KDA_O: phase_residual(p, l_layer, RES_KDA_O, L.ffn_norm, -1); break;
     case PH_MLA_A: phase_mla_a(p, l_layer, -1); break;
     case PH_MLA_B: phase_mla_b(p, l_layer, -1); break;
-    case PH_MLA_ABS: phase_mla_absorb(p, l_layer); break;
+    case PH_MLA_ABS: phase_mla_absorb(p, l_layer, -1); break;
     case PH_MLA_ATTN: phase_mla_attn(p, l_layer, -1); break;
     case PH_MLA_OUT: phase_mla_out(p, l_layer, 1); break;
     case PH_MLA_OUT2: phase_mla_out(p, l_layer, 2); break;
@@ -3072,8 +3090,7 @@ extern "C" __global__ __launch_bounds__(NT) void MD_KERNEL(Params p_arg) {
       ARRIVE();
       phase_mla_b(p, l_layer, sidx++);
       ARRIVE();
-      WAIT();
-      phase_mla_absorb(p, l_layer);
+      phase_mla_absorb(p, l_layer, sidx++);
       ARRIVE();
       phase_mla_attn(p, l_layer, sidx++);
       ARRIVE();

@@ -1737,7 +1737,9 @@ struct KdaSmem {
 // Recurrence phase: task (b, h, 32-column slice of the state).  The slice
 // (dk x 32 fp32) is read once into registers -- thread (rg, j) holds rows
 // rg, rg+8, ... of column j -- updated there and written back in place.
-__device__ __noinline__ void phase_kda_rec(KParams& pk, int l_layer) {
+// The first task's state slice is requested before the wait: the state is
+// only read and written here, so it is final from the previous step.
+__device__ __noinline__ void phase_kda_rec(KParams& pk, int l_layer, int wait_idx) {
   PARAMS;
   KLayer& L = layer_ref(p, l_layer);
   KdaSmem& sm = *(KdaSmem*)md_smem;
@@ -1748,18 +1750,26 @@ __device__ __noinline__ void phase_kda_rec(KParams& pk, int l_layer) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int rg = threadIdx.x >> 5, jj = threadIdx.x & 31;
   rsrc_t wr = make_rsrc_u(p.ws, p.ws_bytes);
-  for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
+  float s[16];
+  auto load_state = [&](int task) __attribute__((always_inline)) {
     const int js = task % ns, h = (task / ns) % nh, b = task / (ns * nh);
-    const uint32_t base = p.off_kda + (uint32_t)(b * width) * 4u;
     float* S = (float*)(p.kv + L.kv_off) + (size_t)(b * nh + h) * dk * dv;
     rsrc_t srs = make_rsrc_u(S, (uint32_t)(dk * dv * 4));
-    float s[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       int i = rg + 8 * r;
       s[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
           srs, i < dk ? (uint32_t)(i * dv + 32 * js + jj) * 4u : OOB, 0, 0));
     }
+  };
+  if ((int)blockIdx.x < ntask) load_state(blockIdx.x);
+  wait_point(p, wait_idx);
+  for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
+    const int js = task % ns, h = (task / ns) % nh, b = task / (ns * nh);
+    const uint32_t base = p.off_kda + (uint32_t)(b * width) * 4u;
+    float* S = (float*)(p.kv + L.kv_off) + (size_t)(b * nh + h) * dk * dv;
+    rsrc_t srs = make_rsrc_u(S, (uint32_t)(dk * dv * 4));
+    if (task != (int)blockIdx.x) load_state(task);
     if (threadIdx.x < dk) {
       sm.q[threadIdx.x] = ld_f32(wr, base + (uint32_t)(h * dk + threadIdx.x) * 4u);
       sm.k[threadIdx.x] = ld_f32(wr, base + (uint32_t)(nh * dk + h * dk + threadIdx.x) * 4u);
@@ -3020,7 +3030,7 @@ __device__ __forceinline__ void run_one_phase(KParams& pk, int layer, int phase)
     case PH_MOE_B: prefetch_experts(p, l); compute_routes(p, l); phase_moe_b(p, l_layer, -1, false); break;
     case PH_MOE_C: prefetch_experts(p, l); compute_routes(p, l); phase_residual(p, l_layer, RES_MOE_DOWN, g_next, -1); break;
     case PH_KDA_PROJ: phase_kda_proj(p, l_layer, -1); break;
-    case PH_KDA_REC: phase_kda_rec(p, l_layer); break;
+    case PH_KDA_REC: phase_kda_rec(p, l_layer, -1); break;
     case PH_KDA_O: phase_residual(p, l_layer, RES_KDA_O, L.ffn_norm, -1); break;
     case PH_MLA_A: phase_mla_a(p, l_layer, -1); break;
     case PH_MLA_B: phase_mla_b(p, l_layer, -1); break;
@@ -3079,9 +3089,12 @@ extern "C" __global__ __launch_bounds__(NT) void MD_KERNEL(Params p_arg) {
     } else if (kind == LK_KDA) {
       phase_kda_proj(p, l_layer, sidx++);
       ARRIVE();
-      WAIT();
-      if (p.verify) phase_kda_rec_verify(p, l_layer);
-      else phase_kda_rec(p, l_layer);
+      if (p.verify) {
+        WAIT();
+        phase_kda_rec_verify(p, l_layer);
+      } else {
+        phase_kda_rec(p, l_layer, sidx++);
+      }
       ARRIVE();
       phase_residual(p, l_layer, RES_KDA_O, L.ffn_norm, sidx++);
       ARRIVE();

@@ -99,7 +99,9 @@ __device__ __forceinline__ unsigned class_members(int grp) { return (gridDim.x -
 
 // every wave: make this wave's stores complete, then the workgroup arrives
 // once.  The increment returns nothing, so nobody waits for it here.
-__device__ void arrive(KParams& pk, int idx) {
+// extra: the workgroup also counts itself on the extra line (a subset of
+// the grid whose outputs a later phase needs before the rest's).
+__device__ void arrive(KParams& pk, int idx, bool extra = false) {
   PARAMS;
   wait_stores();
   __builtin_amdgcn_s_barrier();
@@ -107,6 +109,7 @@ __device__ void arrive(KParams& pk, int idx) {
     unsigned* sp = sync_pt(p, idx);
     const int grp = blockIdx.x & (NGRP - 1);
     (void)__hip_atomic_fetch_add(sp + 32 * grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (extra) (void)__hip_atomic_fetch_add(sp + 32 * NGRP, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -145,6 +148,26 @@ __device__ void wait_all(KParams& pk, int idx) {
       __builtin_amdgcn_s_sleep(1);
       if (((++spins) & 1023u) == 0 && (spins > p.spin_limit || dev_failed(p))) {
         if (lane == 0) set_err(p, MDE_WATCHDOG);
+        break;
+      }
+    }
+  }
+  __builtin_amdgcn_s_barrier();
+}
+
+// wait until n workgroups have counted themselves on the extra line of sync
+// point idx (wave 0 polls, one word)
+__device__ void wait_extra(KParams& pk, int idx, unsigned n) {
+  PARAMS;
+  if (threadIdx.x < 64) {
+    unsigned* c = sync_pt(p, idx) + 32 * NGRP;
+    unsigned spins = 0;
+    while (true) {
+      const unsigned v = __builtin_amdgcn_readfirstlane(__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      if (v >= n) break;
+      __builtin_amdgcn_s_sleep(1);
+      if (((++spins) & 1023u) == 0 && (spins > p.spin_limit || dev_failed(p))) {
+        if (threadIdx.x == 0) set_err(p, MDE_WATCHDOG);
         break;
       }
     }
@@ -192,18 +215,23 @@ __device__ __forceinline__ void grid_sync(KParams& pk, int& sidx) {
 // done; wait_point once the next phase has issued what it may issue before
 // the other workgroups are done (its first weight loads).  idx < 0: no wait
 // (the multi-launch step, where the kernel boundary is the barrier).
-__device__ __forceinline__ void grid_arrive(KParams& pk, int sidx) {
+__device__ __forceinline__ void grid_arrive(KParams& pk, int sidx, bool extra = false) {
   PARAMS;
   stamp(p, 2 * sidx);
-  arrive(p, sidx);
+  arrive(p, sidx, extra);
+}
+// the phase after sync point idx begins (trace stamps only)
+__device__ __forceinline__ void enter_phase(KParams& pk, int idx) {
+  PARAMS;
+  stamp(p, 2 * idx + 1);
+  if (threadIdx.x == 0) md_cur_phase = idx + 1;
 }
 __device__ __forceinline__ void wait_point(KParams& pk, int idx) {
   PARAMS;
   if (idx < 0) return;
   pre_stamp(p, 5);
   wait_all(p, idx);
-  stamp(p, 2 * idx + 1);
-  if (threadIdx.x == 0) md_cur_phase = idx + 1;
+  enter_phase(p, idx);
 }
 
 // clear this WG's share of the other bank (used by the next step)
@@ -2748,7 +2776,23 @@ __device__ __noinline__ void phase_gateup(KParams& pk, int l_layer, int wait_idx
 // scaling each token's h by its routing weight (0 when it did not choose the
 // expert); the down projections of the shared and the routed experts then
 // run as one residual phase.
+// Phase B reads the same input as phase A and none of A's shared-expert
+// outputs (those are read by the down projection, whose wait for phase B's
+// arrivals covers them: every workgroup arrives at B after A).  So phase B
+// waits only for the router logits: when the router has workgroups of its
+// own, they count themselves on the extra line of phase A's sync point and
+// phase B waits for that count, not for the whole grid.
 
+// Workgroups that hold the router alone (the last ones, one 4-row quarter
+// each), or 0 when every workgroup holds router rows: the router's few
+// quarters go apart when there is a shared expert and the grid is more than
+// twice their count (a router quarter is a whole group of k-steps, which on
+// top of a shared-expert group would double that workgroup's stream).
+__device__ __forceinline__ int router_wgs(KParams& pk) {
+  PARAMS;
+  const int rq = (p.n_experts + 3) >> 2;
+  return p.n_shared > 0 && (int)gridDim.x > 2 * rq ? rq : 0;
+}
 
 __device__ __noinline__ void phase_moe_a(KParams& pk, int l_layer, int wait_idx) {
   PARAMS;
@@ -2757,11 +2801,8 @@ __device__ __noinline__ void phase_moe_a(KParams& pk, int l_layer, int wait_idx)
   SlotBuilder sb;
   if (threadIdx.x < 64) {
     sb.start(PL_MOE_A);
-    // The router's few quarters go to workgroups of their own (the last
-    // ones): a router quarter is a whole group of k-steps, which on top of
-    // a shared-expert group would double that workgroup's stream.
     const int G = gridDim.x, w = blockIdx.x, rq = (p.n_experts + 3) >> 2;
-    const bool apart = p.n_shared > 0 && G > 2 * rq;
+    const bool apart = router_wgs(p) > 0;
     if (p.n_shared > 0) {
       int mg = sb.mat(L.sh_gate, p.shared_ffn, p.H, 0);
       int mu = sb.mat(L.sh_up, p.shared_ffn, p.H, 0);
@@ -2815,28 +2856,45 @@ __device__ __noinline__ void compute_routes(KParams& pk, int layer) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int E = p.n_experts, k = p.top_k, B = p.B;
   rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-  for (int t = wv; t < B; t += NW) {
-    float lg = lane < E ? ld_f32(r, p.off_rl + (uint32_t)(t * E + lane) * 4u) : -INFINITY;
-    float mx0 = wave_max(lg);
-    float pe = lane < E ? __expf(lg - mx0) : 0.f;
-    float all = wave_sum(pe);
-    bool taken = false;
-    float sel = 0.f;
-    for (int j = 0; j < k; ++j) {
-      float key = (taken || lane >= E) ? -INFINITY : lg;
-      float mx = wave_max(key);
-      uint64_t bal = __ballot(!taken && lane < E && key == mx);
-      int e = bal ? (int)__builtin_ctzll(bal) : 0;
-      if (lane == e) taken = true;
-      float pj = __shfl(pe, e, 64);
-      sel += pj;
-      if (lane == 0) { RSM.ids[t][j] = e; RSM.w[t][j] = pj; }
+  // wave wv routes tokens wv, wv + NW, ...; all their logits are requested
+  // at once (one load latency, not one per token)
+  constexpr int TPW = MAXB / NW;
+  float lgs[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int t = wv + NW * i;
+    const uint32_t off = (t < B && lane < E) ? p.off_rl + (uint32_t)(t * E + lane) * 4u : OOB;
+    lgs[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CP_SC1));
+  }
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int t = wv + NW * i;
+    if (t >= B) break;
+    // lane e holds expert e (a NaN logit counts as -inf, so that the ranks
+    // below are a permutation)
+    const float lg = (lane < E && lgs[i] == lgs[i]) ? lgs[i] : -INFINITY;
+    const float mx0 = wave_max(lg);
+    const float pe = lane < E ? __expf(lg - mx0) : 0.f;
+    const float all = wave_sum(pe);
+    // rank of expert e: the experts with a larger logit, or an equal one and
+    // a lower id; the chosen are ranks 0 .. k-1, in that order
+    int rank = 0;
+    for (int j = 0; j < E; ++j) {
+      const float lj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lg), j));
+      rank += (lj > lg || (lj == lg && j < lane)) ? 1 : 0;
     }
-    float den = p.norm_topk ? sel : all;
+    const bool taken = lane < E && rank < k;
+    if (taken) { RSM.ids[t][rank] = lane; RSM.w[t][rank] = pe; }
     const uint64_t chosen = __ballot(taken);
     __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
     __builtin_amdgcn_wave_barrier();
-    if (lane < k) RSM.w[t][lane] = RSM.w[t][lane] / den;
+    float sel = 0.f;  // the chosen probabilities, larger first
+    for (int j = 0; j < k; ++j) sel += RSM.w[t][j];
+    const float den = p.norm_topk ? sel : all;
+    const float wj = lane < k ? RSM.w[t][lane] : 0.f;
+    __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+    __builtin_amdgcn_wave_barrier();
+    if (lane < k) RSM.w[t][lane] = wj / den;
     if (lane == 0) RSM.mask[t] = chosen;
   }
   for (int i = threadIdx.x; i < MAXB * 64; i += NT) RSM.wt[i >> 6][i & 63] = 0.f;
@@ -2862,11 +2920,21 @@ __device__ __noinline__ void compute_routes(KParams& pk, int layer) {
   __syncthreads();
 }
 
+// Wait for the router logits of phase A (sync point idx): its router
+// workgroups' count when it has them, else the whole grid.
+__device__ __forceinline__ void wait_router(KParams& pk, int idx) {
+  PARAMS;
+  const int nr = router_wgs(p);
+  if (nr > 0) wait_extra(p, idx, (unsigned)nr);
+  else wait_all(p, idx);
+}
+
 // route_after (p.moe_all): every expert's gate/up streams, so the tables
-// need no routing and the first k-steps are requested before the wait for
-// the router logits; the routing runs after the stream, before the outputs
-// are scaled (experts no token chose get weight 0).  Otherwise the routing
-// is done and the chosen experts' union is streamed.
+// need no routing and the stream waits for nobody (its input and scales were
+// ready for phase A); the routing runs after the stream, once the router
+// logits are there (sync point wait_idx), before the outputs are scaled
+// (experts no token chose get weight 0).  Otherwise the routing is done and
+// the chosen experts' union is streamed.
 __device__ __noinline__ void phase_moe_b(KParams& pk, int l_layer, int wait_idx, bool route_after) {
   PARAMS;
   KLayer& L = layer_ref(p, l_layer);
@@ -2881,8 +2949,12 @@ __device__ __noinline__ void phase_moe_b(KParams& pk, int l_layer, int wait_idx,
     sb.expert_pairs(m0, nu, p.expert_ffn);
   }
   builder_done(p, sb, -1);
-  gemv_passes(p, wait_idx, p.H, ssq_at(p, 2 * l_layer + 1), [&](int s0, int s1) {
-    if (route_after && s0 == 0) compute_routes(p, l_layer);
+  if (route_after && wait_idx >= 0) enter_phase(p, wait_idx);
+  gemv_passes(p, route_after ? -1 : wait_idx, p.H, ssq_at(p, 2 * l_layer + 1), [&](int s0, int s1) {
+    if (route_after && s0 == 0) {
+      if (wait_idx >= 0) wait_router(p, wait_idx);
+      compute_routes(p, l_layer);
+    }
     rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
     for (int e = threadIdx.x; e < (s1 - s0) * 16 * B; e += NT) {
       int t = e % B, sr = e / B;
@@ -3120,12 +3192,14 @@ extern "C" __global__ __launch_bounds__(NT) void MD_KERNEL(Params p_arg) {
       ARRIVE();
     } else {
       phase_moe_a(p, l_layer, sidx++);
-      ARRIVE();
+      grid_arrive(p, sidx, (int)blockIdx.x >= (int)gridDim.x - router_wgs(p));
       prefetch_experts(p, l);
       if (p.moe_all) {
         phase_moe_b(p, l_layer, sidx++, true);
       } else {
-        WAIT();
+        pre_stamp(p, 5);
+        wait_router(p, sidx);
+        enter_phase(p, sidx++);
         compute_routes(p, l);
         phase_moe_b(p, l_layer, -1, false);
       }

@@ -1,7 +1,7 @@
 """In-kernel phase trace: record per-workgroup wall-clock stamps around every
 sync point of a step (md_set_trace) and summarise phase and wait times.
 
-    python -m decode_megakernel_md_amd.trace [--workload dense_27b] [--batches 1,8] [--max-batch 64]
+    python -m decode_megakernel_md_amd.trace [--workload dense_27b] [--batches 1,8] [--max-batch 64] [--dump PREFIX]
 
 prints, per phase kind, the median and slowest workgroup's time per layer,
 the release latency of its sync point (last arrival to median wait end) and
@@ -110,6 +110,8 @@ def main():
     ap.add_argument("--workload", default="dense_27b")
     ap.add_argument("--batches", default="1,8")
     ap.add_argument("--max-batch", type=int, default=0, help="sequence slots (above 8: the 64-row kernel build)")
+    ap.add_argument("--dump", default="", help="also save the raw stamps (int64 [workgroup][slot], 100 MHz ticks) "
+                    "to DUMP_b<B>.npy")
     args = ap.parse_args()
     w = WL.get(args.workload)
     if args.max_batch:
@@ -128,6 +130,8 @@ def main():
         torch.cuda.synchronize()
         m.device_status()
         tr.stop()
+        if args.dump:
+            np.save(f"{args.dump}_b{B}.npy", tr.buf.cpu().numpy())
         out, total = tr.summary(phase_names(w))
         print(f"{w.name} B={B}: step {total:.1f} us (per layer below, us)")
         print("| phase | layers | work (median WG) | work (slowest WG) | release | wait end -> stamp 0 | "

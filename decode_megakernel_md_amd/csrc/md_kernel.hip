@@ -175,28 +175,74 @@ __device__ void wait_extra(KParams& pk, int idx, unsigned n) {
   __builtin_amdgcn_s_barrier();
 }
 
+// ---- trace stamps (optional, p.trace).  In the 8-row build the megakernel
+// keeps them in LDS during the step, as 32-bit ticks after its start, and
+// writes them out when it ends: a global store per stamp would be waited for
+// at the next function entry (the calling convention waits there for every
+// outstanding memory operation) and so lengthen what it measures.  Slots of
+// phases past TR_PH, the 64-row build and the multi-launch step store
+// directly.  LDS word i: main slot i (i < 2 TR_PH), else sub-phase slot
+// trace_n/2 + (i - 2 TR_PH); 0 = not recorded, else ticks + 1.
+constexpr int TR_PH = WIDE ? 0 : 640;
+constexpr int TR_WORDS = WIDE ? 1 : 10 * TR_PH;
+__shared__ uint32_t md_trace_lds[TR_WORDS];
+__shared__ uint64_t md_trace_t0;  // the step's start (0: stamps go to memory directly)
+
+__device__ __forceinline__ void trace_put(KParams& pk, int slot, int lds_i) {
+  PARAMS;
+  const uint64_t t = wall_clock64();
+  if (!WIDE && lds_i >= 0 && lds_i < TR_WORDS && md_trace_t0 != 0) md_trace_lds[lds_i] = (uint32_t)(t - md_trace_t0) + 1u;
+  else p.trace[(size_t)blockIdx.x * p.trace_n + slot] = t;
+}
+// the step's start: stamps from here on are kept in LDS
+__device__ __forceinline__ void trace_begin(KParams& pk) {
+  PARAMS;
+  if (threadIdx.x == 0) md_trace_t0 = 0;
+  if (!p.trace || p.trace_n <= 0) return;
+  for (int i = threadIdx.x; i < TR_WORDS; i += NT) md_trace_lds[i] = 0u;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint64_t t = wall_clock64();
+    p.trace[(size_t)blockIdx.x * p.trace_n + p.trace_n - 1] = t;
+    if (!WIDE) md_trace_t0 = t;
+  }
+}
+// write the kept stamps out (wave 0; thread 0 wrote them, so no barrier)
+__device__ void trace_flush(KParams& pk) {
+  PARAMS;
+  if (WIDE || !p.trace || threadIdx.x >= 64) return;
+  const uint64_t t0 = md_trace_t0;
+  if (t0 == 0) return;
+  for (int i = threadIdx.x; i < TR_WORDS; i += 64) {
+    const uint32_t v = md_trace_lds[i];
+    const int slot = i < 2 * TR_PH ? i : p.trace_n / 2 + (i - 2 * TR_PH);
+    if (v != 0u && slot < p.trace_n - 1) p.trace[(size_t)blockIdx.x * p.trace_n + slot] = t0 + (v - 1u);
+  }
+}
+
 __device__ __forceinline__ void stamp(KParams& pk, int slot) {
   PARAMS;
-  if (p.trace && threadIdx.x == 0 && slot < p.trace_n) p.trace[(size_t)blockIdx.x * p.trace_n + slot] = wall_clock64();
+  if (p.trace && threadIdx.x == 0 && slot < p.trace_n) trace_put(p, slot, slot < 2 * TR_PH ? slot : -1);
 }
 
 // Sub-phase stamps: slot trace_n/2 + 8*(phase index) + k, k < 8.  k < 4:
 // the phase's own, after its wait; k = 4: its slot tables are built, k = 5:
-// it starts waiting (both before the wait, while md_cur_phase still holds
-// the previous phase's index).
+// it starts waiting, k = 6: the previous phase's arrival is made, its stores
+// completed (4 to 6 before the wait, while md_cur_phase still holds the
+// previous phase's index).
 __shared__ int md_cur_phase;
 __device__ __forceinline__ void sub_stamp(KParams& pk, int k) {
   PARAMS;
   if (p.trace && threadIdx.x == 0) {
-    int slot = p.trace_n / 2 + 8 * md_cur_phase + k;
-    if (slot < p.trace_n - 1) p.trace[(size_t)blockIdx.x * p.trace_n + slot] = wall_clock64();
+    const int ph = md_cur_phase, slot = p.trace_n / 2 + 8 * ph + k;
+    if (slot < p.trace_n - 1) trace_put(p, slot, ph < TR_PH ? 2 * TR_PH + 8 * ph + k : -1);
   }
 }
 __device__ __forceinline__ void pre_stamp(KParams& pk, int k) {
   PARAMS;
   if (p.trace && threadIdx.x == 0) {
-    int slot = p.trace_n / 2 + 8 * (md_cur_phase + 1) + k;
-    if (slot < p.trace_n - 1) p.trace[(size_t)blockIdx.x * p.trace_n + slot] = wall_clock64();
+    const int ph = md_cur_phase + 1, slot = p.trace_n / 2 + 8 * ph + k;
+    if (slot < p.trace_n - 1) trace_put(p, slot, ph < TR_PH ? 2 * TR_PH + 8 * ph + k : -1);
   }
 }
 
@@ -219,6 +265,7 @@ __device__ __forceinline__ void grid_arrive(KParams& pk, int sidx, bool extra = 
   PARAMS;
   stamp(p, 2 * sidx);
   arrive(p, sidx, extra);
+  pre_stamp(p, 6);
 }
 // the phase after sync point idx begins (trace stamps only)
 __device__ __forceinline__ void enter_phase(KParams& pk, int idx) {
@@ -2798,6 +2845,11 @@ __device__ __noinline__ void phase_moe_a(KParams& pk, int l_layer, int wait_idx)
   PARAMS;
   KLayer& L = layer_ref(p, l_layer);
   const int B = p.B;
+  // every expert's weight pointers for phase B: requested now, entered into
+  // LDS once wave 0 has built the tables (the load hides behind the builder;
+  // phase B needs no load before its own tables)
+  const int nep = 3 * p.n_experts;
+  const uint16_t* ep = (int)threadIdx.x < nep ? L.experts[threadIdx.x] : nullptr;
   SlotBuilder sb;
   if (threadIdx.x < 64) {
     sb.start(PL_MOE_A);
@@ -2822,6 +2874,7 @@ __device__ __noinline__ void phase_moe_a(KParams& pk, int l_layer, int wait_idx)
       sb.singles_in(mr, q);
     }
   }
+  if ((int)threadIdx.x < nep) RSM.exall[threadIdx.x / 3][threadIdx.x % 3] = ep;
   builder_done(p, sb, -1);
   gemv_passes(p, wait_idx, p.H, ssq_at(p, 2 * l_layer + 1), [&](int s0, int s1) {
     rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
@@ -3125,11 +3178,14 @@ extern "C" __global__ __launch_bounds__(NT) void MD_KERNEL(Params p_arg) {
   if (threadIdx.x < NPLAN) PLANS[threadIdx.x].valid = 0;
   __syncthreads();
   if (p.ml_phase >= 0) {  // one phase of the multi-launch step
-    if (threadIdx.x == 0) md_cur_phase = 0;
+    if (threadIdx.x == 0) {
+      md_cur_phase = 0;
+      md_trace_t0 = 0;
+    }
     run_one_phase(p, p.ml_layer, p.ml_phase);
     return;
   }
-  if (p.trace && threadIdx.x == 0 && p.trace_n > 0) p.trace[(size_t)blockIdx.x * p.trace_n + p.trace_n - 1] = wall_clock64();
+  trace_begin(p);
   clear_next_bank(p);
   int sidx = 0;
   if (threadIdx.x == 0) md_cur_phase = 0;
@@ -3192,8 +3248,17 @@ extern "C" __global__ __launch_bounds__(NT) void MD_KERNEL(Params p_arg) {
       ARRIVE();
     } else {
       phase_moe_a(p, l_layer, sidx++);
-      grid_arrive(p, sidx, (int)blockIdx.x >= (int)gridDim.x - router_wgs(p));
-      prefetch_experts(p, l);
+      if (router_wgs(p) == 0) {
+        ARRIVE();
+      } else {
+        // nobody waits for phase A's whole grid: phase B needs the router
+        // logits only, and the down projection, which reads A's outputs,
+        // waits for phase B's arrivals (each made after this workgroup's A
+        // stores have completed).  Only the router workgroups arrive, on the
+        // extra line; the others go on without waiting for their stores.
+        stamp(p, 2 * sidx);
+        if ((int)blockIdx.x >= (int)gridDim.x - router_wgs(p)) arrive(p, sidx, true);
+      }
       if (p.moe_all) {
         phase_moe_b(p, l_layer, sidx++, true);
       } else {
@@ -3207,13 +3272,17 @@ extern "C" __global__ __launch_bounds__(NT) void MD_KERNEL(Params p_arg) {
       phase_residual(p, l_layer, RES_MOE_DOWN, g_next, sidx++);
       ARRIVE();
     }
-    if (dev_failed(p)) return;
+    if (dev_failed(p)) {
+      trace_flush(p);
+      return;
+    }
   }
   phase_lmhead(p, sidx++);
   if (p.verify) {
     ARRIVE();
     WAIT();
     verify_finish(p);
+    trace_flush(p);
     return;
   }
 #undef WAIT
@@ -3224,6 +3293,7 @@ extern "C" __global__ __launch_bounds__(NT) void MD_KERNEL(Params p_arg) {
   if (threadIdx.x == 0) ((int*)md_smem)[0] = last;
   __syncthreads();
   if (((int*)md_smem)[0]) final_argmax(p);
+  trace_flush(p);
 }
 
 }  // namespace md

@@ -10,7 +10,8 @@ the medians of the phase's own sub-stamps: the end of the wait to stamp 0
 stamp 0 to stamps 1, 2, 3 (streams: 2 = stream done; attention: 3 = this
 workgroup's blocks done, 1 = its partial stored, 2 = combine done); and,
 measured from the workgroup's arrival at the previous sync point, when its
-slot tables were built and when it started to wait (after the prefetch)."""
+previous phase's stores had completed (its arrival made), when its slot
+tables were built and when it started to wait (after the prefetch)."""
 from __future__ import annotations
 
 import ctypes
@@ -76,7 +77,7 @@ class Tracer:
         # previous phase's work ends at t[2(s-1)]
         wait_ends = [start] + [t[:, 2 * s + 1] for s in range(ns - 1)]
         prev_ends = [start] + [t[:, 2 * s] for s in range(ns - 1)]
-        keys = ("med", "max", "release", "to_s0", "s0_s1", "s0_s2", "s0_s3", "arr_built", "arr_wait")
+        keys = ("med", "max", "release", "to_s0", "s0_s1", "s0_s2", "s0_s3", "arr_done", "arr_built", "arr_wait")
         for s, nm in enumerate(names):
             d = out.setdefault(nm, dict({"n": 0}, **{k: 0.0 for k in keys}))
             d["n"] += 1
@@ -89,6 +90,8 @@ class Tracer:
                 for k, key in ((1, "s0_s1"), (2, "s0_s2"), (3, "s0_s3")):
                     if ok(k):
                         d[key] += float(np.median(sub[:, s, k] - sub[:, s, 0]))
+            if ok(6):
+                d["arr_done"] += float(np.median(sub[:, s, 6] - prev_ends[s]))
             if ok(4):
                 d["arr_built"] += float(np.median(sub[:, s, 4] - prev_ends[s]))
             if ok(5):
@@ -110,8 +113,8 @@ def main():
     ap.add_argument("--workload", default="dense_27b")
     ap.add_argument("--batches", default="1,8")
     ap.add_argument("--max-batch", type=int, default=0, help="sequence slots (above 8: the 64-row kernel build)")
-    ap.add_argument("--dump", default="", help="also save the raw stamps (int64 [workgroup][slot], 100 MHz ticks) "
-                    "to DUMP_b<B>.npy")
+    ap.add_argument("--dump", default="", help="also save every workgroup's stamps (100 MHz ticks from the first "
+                    "workgroup's start, -1: not recorded) to DUMP_b<B>.npz")
     args = ap.parse_args()
     w = WL.get(args.workload)
     if args.max_batch:
@@ -131,17 +134,24 @@ def main():
         m.device_status()
         tr.stop()
         if args.dump:
-            np.save(f"{args.dump}_b{B}.npy", tr.buf.cpu().numpy())
+            raw = tr.buf.cpu().numpy()
+            ns = len(phase_names(w))
+            h = tr.n // 2
+            t0 = raw[:, -1].min()
+            rel = lambda a: np.where(a > 0, a - t0, -1).astype(np.int32)  # noqa: E731
+            np.savez_compressed(f"{args.dump}_b{B}.npz", main=rel(raw[:, : 2 * ns]),
+                                sub=rel(raw[:, h: h + 8 * ns]), start=rel(raw[:, -1]), names=np.array(phase_names(w)))
         out, total = tr.summary(phase_names(w))
         print(f"{w.name} B={B}: step {total:.1f} us (per layer below, us)")
         print("| phase | layers | work (median WG) | work (slowest WG) | release | wait end -> stamp 0 | "
-              "stamp 0 -> 1 | stamp 0 -> 2 | stamp 0 -> 3 | prev arrival -> tables built | prev arrival -> wait |")
-        print("|---|---|---|---|---|---|---|---|---|---|---|")
+              "stamp 0 -> 1 | stamp 0 -> 2 | stamp 0 -> 3 | prev arrival -> stores done | prev arrival -> tables built | "
+              "prev arrival -> wait |")
+        print("|---|---|---|---|---|---|---|---|---|---|---|---|")
         for k, d in out.items():
             n = d["n"]
             print(f"| {k} | {n} | {d['med'] / n:.1f} | {d['max'] / n:.1f} | {d['release'] / n:.1f} | "
                   f"{d['to_s0'] / n:.1f} | {d['s0_s1'] / n:.1f} | {d['s0_s2'] / n:.1f} | {d['s0_s3'] / n:.1f} | "
-                  f"{d['arr_built'] / n:.1f} | {d['arr_wait'] / n:.1f} |")
+                  f"{d['arr_done'] / n:.1f} | {d['arr_built'] / n:.1f} | {d['arr_wait'] / n:.1f} |")
         sys.stdout.flush()
         del tr
     m.close()

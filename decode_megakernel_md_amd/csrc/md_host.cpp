@@ -258,7 +258,7 @@ WsLayout ws_layout(const md_config* c) {
   w.ou = take(w.ou_stride * L);
   w.h_stride = align256(2 * 2 * RS * (size_t)F);
   w.h = take(w.h_stride * L);
-  w.rl = take(4 * (size_t)RS * (c->n_experts > 0 ? c->n_experts : 1));
+  w.rl = take(8 * (size_t)RS * (c->n_experts > 0 ? c->n_experts : 1));
   w.hs_stride = align256(2 * 2 * RS * (size_t)(c->n_shared > 0 ? c->shared_ffn : 1));
   w.hs = take(w.hs_stride * L);
   int nu = c->n_experts < RS * c->top_k ? c->n_experts : RS * c->top_k;
@@ -327,6 +327,7 @@ struct md_model {
   size_t ws_bytes = 0;
   int grid = 0;
   int bank = 0;
+  uint32_t step_seq = 0;  // steps enqueued so far (tags the router logits of each step)
   hipStream_t last_stream = nullptr;
   std::vector<int> kinds;  // layer kinds (host copy of the layer table's)
   uint64_t* trace = nullptr;
@@ -595,6 +596,7 @@ static md_status fill_params(md_model* m, const int32_t* tokens, const int32_t* 
   p.spin_limit = 1u << 22;
   p.trace = m->trace;
   p.trace_n = m->trace_n;
+  p.step_seq = m->step_seq++;
   return MD_OK;
 }
 
@@ -641,6 +643,9 @@ md_status md_decode_step_noalloc(md_model* m, const int32_t* tokens, const int32
   hipError_t e = launch_fill_u32(s + w.sync, 0u, (uint32_t)((size_t)w.n_sync * sp_words(&m->cfg)), stream);
   if (e == hipSuccess) e = launch_fill_u32(s + w.err, 0u, 1u, stream);
   if (e == hipSuccess) e = launch_fill_u32(s + w.zero, 0u, 1024u / 4u, stream);
+  // router logits carry the step's tag; another model's entries could match it
+  if (e == hipSuccess && m->cfg.n_experts > 0)
+    e = launch_fill_u32(s + w.rl, 0u, (uint32_t)(2 * (size_t)row_stride(&m->cfg) * m->cfg.n_experts), stream);
   if (e != hipSuccess) return fail(MD_EHIP, "clearing the static scratch: %s", hipGetErrorString(e));
   e = launch_step(m, p, stream);
   if (e != hipSuccess) return fail(MD_EHIP, "megakernel launch: %s", hipGetErrorString(e));

@@ -99,9 +99,7 @@ __device__ __forceinline__ unsigned class_members(int grp) { return (gridDim.x -
 
 // every wave: make this wave's stores complete, then the workgroup arrives
 // once.  The increment returns nothing, so nobody waits for it here.
-// extra: the workgroup also counts itself on the extra line (a subset of
-// the grid whose outputs a later phase needs before the rest's).
-__device__ void arrive(KParams& pk, int idx, bool extra = false) {
+__device__ void arrive(KParams& pk, int idx) {
   PARAMS;
   wait_stores();
   __builtin_amdgcn_s_barrier();
@@ -109,7 +107,6 @@ __device__ void arrive(KParams& pk, int idx, bool extra = false) {
     unsigned* sp = sync_pt(p, idx);
     const int grp = blockIdx.x & (NGRP - 1);
     (void)__hip_atomic_fetch_add(sp + 32 * grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (extra) (void)__hip_atomic_fetch_add(sp + 32 * NGRP, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -148,26 +145,6 @@ __device__ void wait_all(KParams& pk, int idx) {
       __builtin_amdgcn_s_sleep(1);
       if (((++spins) & 1023u) == 0 && (spins > p.spin_limit || dev_failed(p))) {
         if (lane == 0) set_err(p, MDE_WATCHDOG);
-        break;
-      }
-    }
-  }
-  __builtin_amdgcn_s_barrier();
-}
-
-// wait until n workgroups have counted themselves on the extra line of sync
-// point idx (wave 0 polls, one word)
-__device__ void wait_extra(KParams& pk, int idx, unsigned n) {
-  PARAMS;
-  if (threadIdx.x < 64) {
-    unsigned* c = sync_pt(p, idx) + 32 * NGRP;
-    unsigned spins = 0;
-    while (true) {
-      const unsigned v = __builtin_amdgcn_readfirstlane(__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      if (v >= n) break;
-      __builtin_amdgcn_s_sleep(1);
-      if (((++spins) & 1023u) == 0 && (spins > p.spin_limit || dev_failed(p))) {
-        if (threadIdx.x == 0) set_err(p, MDE_WATCHDOG);
         break;
       }
     }
@@ -261,10 +238,10 @@ __device__ __forceinline__ void grid_sync(KParams& pk, int& sidx) {
 // done; wait_point once the next phase has issued what it may issue before
 // the other workgroups are done (its first weight loads).  idx < 0: no wait
 // (the multi-launch step, where the kernel boundary is the barrier).
-__device__ __forceinline__ void grid_arrive(KParams& pk, int sidx, bool extra = false) {
+__device__ __forceinline__ void grid_arrive(KParams& pk, int sidx) {
   PARAMS;
   stamp(p, 2 * sidx);
-  arrive(p, sidx, extra);
+  arrive(p, sidx);
   pre_stamp(p, 6);
 }
 // the phase after sync point idx begins (trace stamps only)
@@ -740,6 +717,17 @@ __device__ __forceinline__ void slot_src(int si, int lq, uint32_t lchunk, int wv
                                          uint32_t& pstep) {
   int gq = GSM.slots[si].gq[lq];
   int m = GSM.slots[si].m[lq];
+  if (gq < 0) {
+    // An empty quarter's lanes read the bytes of a filled quarter of the same
+    // k-step: the slot's first (quarters fill in order), or, for an empty
+    // slot, the first of its group (never empty).  Its rows are never
+    // stored, and the lines are those its instruction or the group's other
+    // instruction reads anyway: no extra traffic, and no single line that
+    // every workgroup's empty lanes would read (a hot cache channel).
+    const int s2 = GSM.slots[si].gq[0] >= 0 ? si : si - si % TG;
+    gq = GSM.slots[s2].gq[0];
+    m = GSM.slots[s2].m[0];
+  }
   bool lv = gq >= 0;
   uint64_t W = GSM.mats[m].w, ts = GSM.mats[m].tstride;
   pa = lv ? W + (uint64_t)(gq >> 2) * ts + (uint64_t)((gq & 3) * 256) + lchunk + (uint64_t)wv * 1024u : zero_addr;
@@ -1051,6 +1039,26 @@ __device__ __forceinline__ bool slot_row(int si, int rr, int& m, int& row) {
   return row < GSM.mats[m].N;
 }
 
+// Post-stream writer over 4-row quarters, for slots [s0, s1) of a staging
+// pass: fn(si, sr0, t, m, row0, n) for every quarter of slot si that holds
+// rows (rows row0 .. row0+n-1 of matrix m, n <= 4, staged at rows sr0 ..
+// sr0+n-1) and every token t < B.  Consecutive threads take consecutive
+// quarters of one token, so their stores are consecutive in memory.
+template <class F>
+__device__ __forceinline__ void for_quarters(int s0, int s1, int B, F fn) {
+  const int nq = (s1 - s0) * 4;
+  for (int e = threadIdx.x; e < nq * B; e += NT) {
+    const int sq = e % nq, t = e / nq;
+    const int si = s0 + (sq >> 2), qq = sq & 3;
+    const int gq = GSM.slots[si].gq[qq];
+    if (gq < 0) continue;
+    const int m = GSM.slots[si].m[qq];
+    const int row0 = gq * 4, n = GSM.mats[m].N - row0;
+    if (n <= 0) continue;
+    fn(si, 4 * sq, t, m, row0, n < 4 ? n : 4);
+  }
+}
+
 // Rows of an N-row output this workgroup owns: 4-row quarters
 // [Q*w/G, Q*(w+1)/G), the split every projection uses.  The residual x is
 // private to the owner of its rows, so every phase that touches x must use
@@ -1095,6 +1103,22 @@ __device__ __forceinline__ void put_hilo(rsrc_t r, uint32_t u_off, int K, int t,
   split_hilo(v, hi, lo);
   st_u16(r, u_off + (uint32_t)((0 * MAXB + t) * K + k) * 2u, hi);
   st_u16(r, u_off + (uint32_t)((1 * MAXB + t) * K + k) * 2u, lo);
+}
+// The same for elements k0 .. k0+n-1 (n <= 4; k0 a multiple of 4): one
+// 8-byte store per part when n = 4.
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void put_hilo4(rsrc_t r, uint32_t u_off, int K, int t, int k0, const float (&v)[4], int n) {
+  if (n == 4) {
+    uint16_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) split_hilo(v[i], h[i], l[i]);
+    const u32x2 hv = {(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+    const u32x2 lv = {(uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16)};
+    __builtin_amdgcn_raw_buffer_store_b64(hv, r, u_off + (uint32_t)((0 * MAXB + t) * K + k0) * 2u, 0, CP_SC1);
+    __builtin_amdgcn_raw_buffer_store_b64(lv, r, u_off + (uint32_t)((1 * MAXB + t) * K + k0) * 2u, 0, CP_SC1);
+  } else {
+    for (int i = 0; i < n; ++i) put_hilo(r, u_off, K, t, k0 + i, v[i]);
+  }
 }
 
 // This workgroup's sum of squares of x per token (partials [NT][MAXB] in
@@ -1166,6 +1190,39 @@ __device__ __noinline__ void phase_embed(KParams& pk) {
   }
 }
 
+// Router logit entries: {f32 logit, u32 tag}, tag = 2 (step_seq * n_layers
+// + layer) + 1 (odd: a cleared entry never matches).  One 8-byte atomic store
+// each, so a reader never sees a logit with another entry's tag.
+__device__ __forceinline__ uint32_t rl_tag(KParams& pk, int layer) {
+  PARAMS;
+  return ((p.step_seq * (uint32_t)p.n_layers + (uint32_t)layer) << 1) | 1u;
+}
+__device__ __forceinline__ uint64_t* rl_entry(KParams& pk, int t, int e) {
+  PARAMS;
+  return (uint64_t*)(p.ws + p.off_rl + (size_t)(t * p.n_experts + e) * 8u);
+}
+__device__ __forceinline__ void put_logit(KParams& pk, int layer, int t, int e, float v) {
+  PARAMS;
+  const uint64_t x = (uint64_t)__float_as_uint(v) | ((uint64_t)rl_tag(p, layer) << 32);
+  __hip_atomic_store(rl_entry(p, t, e), x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The entries a routing wave reads: tokens wv, wv + NW, ... (lane = expert).
+constexpr int RTPW = MAXB / NW;
+struct RouteIn {
+  uint64_t v[RTPW];
+};
+__device__ __forceinline__ void route_load(KParams& pk, RouteIn& in) {
+  PARAMS;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < RTPW; ++i) {
+    const int t = wv + NW * i;
+    in.v[i] = (t < p.B && lane < p.n_experts)
+                  ? __hip_atomic_load(rl_entry(p, t, lane), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                  : 0ull;
+  }
+}
+
 // ------------------------------------------------------------ shared stream
 // Every weight-streaming phase runs through gemv_phase: one copy of the
 // stream loop and of the group epilogue, shared by all of them, so that the
@@ -1211,14 +1268,19 @@ __device__ __forceinline__ void gemv_epi(int g, int rb, int j, int kind, int B, 
 // written once the wait is over).
 // Groups [g0, g1) only (g1 < 0: to the end): one pass of a phase whose
 // slot rows do not all fit the staging at once (64-row steps).
-__device__ __noinline__ void gemv_phase(KParams& pk, int wait_idx, int inv_n, uint32_t inv_off, int kind, int r0,
-                                        int nrow, const uint16_t* g_next, int g0 = 0, int g1 = -1) {
+__device__ __noinline__ RouteIn gemv_phase(KParams& pk, int wait_idx, int inv_n, uint32_t inv_off, int kind, int r0,
+                                           int nrow, const uint16_t* g_next, int g0 = 0, int g1 = -1,
+                                           bool route_in = false) {
   PARAMS;
   const int B = p.B, H = p.H;
   if (g1 < 0) g1 = __builtin_amdgcn_readfirstlane(GSM.ngroups);
   const int s0 = TG * g0;
   GemvStream<NBT> gs;
   gemv_begin(gs, p.ws, p.ws_bytes, p.off_zero, B, g0, g1);
+  // route_in: the router logits too, behind the first weight loads (they
+  // arrive while the stream runs and are returned after it)
+  RouteIn rin = {};
+  if (route_in) route_load(p, rin);
   float xv[4], gv[4];
   if (kind == EPI_RESIDUAL) {
     // buffer loads: an offset past the resource reads 0, so no load is
@@ -1256,6 +1318,7 @@ __device__ __noinline__ void gemv_phase(KParams& pk, int wait_idx, int inv_n, ui
   sub_stamp(p, 0);
   gemv_run(p, gs, inv_n, inv_off, [=](int g, int rb, int j) { gemv_epi(g, rb, j, kind, B, r0, s0); });
   sub_stamp(p, 2);
+  return rin;
 }
 
 // A slot-staged phase in staging passes: groups [g0, g1) per pass (one pass
@@ -2779,9 +2842,26 @@ __device__ __noinline__ void phase_residual(KParams& pk, int l_layer, int mode, 
     static_assert(WIDE || sizeof(GemvSmem::red) >= sizeof(float) * (NT + NW) * MAXB, "partial sums reuse the reduction scratch");
     float* part = (float*)GSM.red;  // [NT][MAXB]
     for (int t = 0; t < MAXB; ++t) part[threadIdx.x * MAXB + t] = 0.f;
-    for (int e = threadIdx.x; e < nrow * B; e += NT) {
-      int t = e % B, lr = e / B;
-      part[threadIdx.x * MAXB + t] += elem(t, lr);
+    // four consecutive rows of one token per thread (owned rows start on a
+    // multiple of 4): one 16-byte store of x and one 8-byte store per part of U
+    const int nq = (nrow + 3) >> 2;
+    for (int e = threadIdx.x; e < nq * B; e += NT) {
+      const int q = e % nq, t = e / nq, lr0 = 4 * q;
+      const int n = nrow - lr0 < 4 ? nrow - lr0 : 4;
+      float x[4], u[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = i < n ? GSM.out[lr0 + i][t] : 0.f;
+        u[i] = i < n ? GSM.gain[lr0 + i] * x[i] : 0.f;
+      }
+      float* xp = p.x + t * H + r0 + lr0;
+      if (n == 4) {
+        *(f32x4*)xp = f32x4{x[0], x[1], x[2], x[3]};
+      } else {
+        for (int i = 0; i < n; ++i) xp[i] = x[i];
+      }
+      put_hilo4(r, u_next, H, t, r0 + lr0, u, n);
+      part[threadIdx.x * MAXB + t] += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
     }
     store_ssq(p, r, part, ssq_at(p, nxt));
   }
@@ -2803,13 +2883,13 @@ __device__ __noinline__ void phase_gateup(KParams& pk, int l_layer, int wait_idx
   builder_done(p, sb, -1);
   gemv_passes(p, wait_idx, p.H, ssq_at(p, 2 * l_layer + 1), [&](int s0, int s1) {
     rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-    for (int e = threadIdx.x; e < (s1 - s0) * 16 * B; e += NT) {
-      int t = e % B, sr = e / B;
-      if ((sr >> 4) & 1) continue;  // up slots carry no output (passes start on even slots)
-      int m, row;
-      if (!slot_row(s0 + (sr >> 4), sr & 15, m, row)) continue;
-      put_hilo(r, h_at(p, l_layer), F, t, row, GSM.out[sr][t]);
-    }
+    for_quarters(s0, s1, B, [&](int si, int sr0, int t, int m, int row0, int n) {
+      if (si & 1) return;  // up slots carry no output (passes start on even slots)
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = GSM.out[sr0 + i][t];
+      put_hilo4(r, h_at(p, l_layer), F, t, row0, v, n);
+    });
   });
 }
 
@@ -2825,10 +2905,11 @@ __device__ __noinline__ void phase_gateup(KParams& pk, int l_layer, int wait_idx
 // run as one residual phase.
 // Phase B reads the same input as phase A and none of A's shared-expert
 // outputs (those are read by the down projection, whose wait for phase B's
-// arrivals covers them: every workgroup arrives at B after A).  So phase B
-// waits only for the router logits: when the router has workgroups of its
-// own, they count themselves on the extra line of phase A's sync point and
-// phase B waits for that count, not for the whole grid.
+// arrivals covers them: every workgroup arrives at B after A).  It needs
+// only the router logits, and those carry their own proof of freshness: each
+// 8-byte entry holds the logit and a tag naming the step and the layer, so a
+// reader checks the tags of what it read (and reads again until they match)
+// instead of waiting at a sync point.  Phase A has no arrival.
 
 // Workgroups that hold the router alone (the last ones, one 4-row quarter
 // each), or 0 when every workgroup holds router rows: the router's few
@@ -2878,16 +2959,18 @@ __device__ __noinline__ void phase_moe_a(KParams& pk, int l_layer, int wait_idx)
   builder_done(p, sb, -1);
   gemv_passes(p, wait_idx, p.H, ssq_at(p, 2 * l_layer + 1), [&](int s0, int s1) {
     rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-    for (int e = threadIdx.x; e < (s1 - s0) * 16 * B; e += NT) {
-      int t = e % B, sr = e / B;
-      int si = s0 + (sr >> 4);
-      bool pair = GSM.grp[si / TG].kind == GK_PAIR;
-      if (pair && (si & 1)) continue;  // up slots carry no output
-      int m, row;
-      if (!slot_row(si, sr & 15, m, row)) continue;
-      if (pair) put_hilo(r, hs_at(p, l_layer), p.shared_ffn, t, row, GSM.out[sr][t]);
-      else st_f32(r, p.off_rl + (uint32_t)(t * p.n_experts + row) * 4u, GSM.out[sr][t]);
-    }
+    for_quarters(s0, s1, B, [&](int si, int sr0, int t, int m, int row0, int n) {
+      const bool pair = GSM.grp[si / TG].kind == GK_PAIR;
+      if (pair && (si & 1)) return;  // up slots carry no output
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = GSM.out[sr0 + i][t];
+      if (pair) {
+        put_hilo4(r, hs_at(p, l_layer), p.shared_ffn, t, row0, v, n);
+      } else {
+        for (int i = 0; i < n; ++i) put_logit(p, l_layer, t, row0 + i, v[i]);
+      }
+    });
   });
 }
 
@@ -2904,23 +2987,34 @@ __device__ __forceinline__ void prefetch_experts(KParams& pk, int layer) {
   for (int i = threadIdx.x; i < p.n_experts * 3; i += NT) RSM.exall[i / 3][i % 3] = L.experts[i];
 }
 
-__device__ __noinline__ void compute_routes(KParams& pk, int layer) {
+// in: this wave's entries as route_load read them (requested earlier, so
+// their latency overlaps other work); read again until every tag is this
+// layer's.
+__device__ __noinline__ void compute_routes(KParams& pk, int layer, RouteIn in) {
   PARAMS;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int E = p.n_experts, k = p.top_k, B = p.B;
-  rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-  // wave wv routes tokens wv, wv + NW, ...; all their logits are requested
-  // at once (one load latency, not one per token)
-  constexpr int TPW = MAXB / NW;
-  float lgs[TPW];
+  const uint32_t tag = rl_tag(p, layer);
+  for (unsigned spins = 0;; ++spins) {
+    bool ok = true;
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int t = wv + NW * i;
-    const uint32_t off = (t < B && lane < E) ? p.off_rl + (uint32_t)(t * E + lane) * 4u : OOB;
-    lgs[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CP_SC1));
+    for (int i = 0; i < RTPW; ++i) {
+      const int t = wv + NW * i;
+      if (t < B && lane < E && (uint32_t)(in.v[i] >> 32) != tag) ok = false;
+    }
+    if (__all(ok)) break;
+    if (((spins + 1) & 1023u) == 0 && (spins > p.spin_limit || dev_failed(p))) {
+      if (lane == 0) set_err(p, MDE_WATCHDOG);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    route_load(p, in);
   }
+  float lgs[RTPW];
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) {
+  for (int i = 0; i < RTPW; ++i) lgs[i] = __uint_as_float((uint32_t)in.v[i]);
+#pragma unroll
+  for (int i = 0; i < RTPW; ++i) {
     const int t = wv + NW * i;
     if (t >= B) break;
     // lane e holds expert e (a NaN logit counts as -inf, so that the ranks
@@ -2973,27 +3067,17 @@ __device__ __noinline__ void compute_routes(KParams& pk, int layer) {
   __syncthreads();
 }
 
-// Wait for the router logits of phase A (sync point idx): its router
-// workgroups' count when it has them, else the whole grid.
-__device__ __forceinline__ void wait_router(KParams& pk, int idx) {
-  PARAMS;
-  const int nr = router_wgs(p);
-  if (nr > 0) wait_extra(p, idx, (unsigned)nr);
-  else wait_all(p, idx);
-}
-
 // route_after (p.moe_all): every expert's gate/up streams, so the tables
 // need no routing and the stream waits for nobody (its input and scales were
-// ready for phase A); the routing runs after the stream, once the router
-// logits are there (sync point wait_idx), before the outputs are scaled
-// (experts no token chose get weight 0).  Otherwise the routing is done and
-// the chosen experts' union is streamed.
-__device__ __noinline__ void phase_moe_b(KParams& pk, int l_layer, int wait_idx, bool route_after) {
+// ready for phase A); the router logits are requested behind the stream's
+// first weight loads (8-row build) and the routing runs after the stream,
+// before the outputs are scaled (experts no token chose get weight 0).
+// Otherwise the routing is done and the chosen experts' union is streamed.
+__device__ __noinline__ void phase_moe_b(KParams& pk, int l_layer, bool route_after) {
   PARAMS;
-  KLayer& L = layer_ref(p, l_layer);
   const int B = p.B;
   SlotBuilder sb;
-  if (route_after) __syncthreads();  // every expert's pointers (prefetch_experts) are in LDS
+  if (route_after) __syncthreads();  // every expert's pointers (loaded in phase A) are in LDS
   if (threadIdx.x < 64) {
     sb.start();
     sb.begin(u_at(p, 2 * l_layer + 1), p.H, GK_PAIR);
@@ -3002,21 +3086,33 @@ __device__ __noinline__ void phase_moe_b(KParams& pk, int l_layer, int wait_idx,
     sb.expert_pairs(m0, nu, p.expert_ffn);
   }
   builder_done(p, sb, -1);
-  if (route_after && wait_idx >= 0) enter_phase(p, wait_idx);
-  gemv_passes(p, route_after ? -1 : wait_idx, p.H, ssq_at(p, 2 * l_layer + 1), [&](int s0, int s1) {
-    if (route_after && s0 == 0) {
-      if (wait_idx >= 0) wait_router(p, wait_idx);
-      compute_routes(p, l_layer);
-    }
+  auto post = [&](int s0, int s1) {
     rsrc_t r = make_rsrc_u(p.ws, p.ws_bytes);
-    for (int e = threadIdx.x; e < (s1 - s0) * 16 * B; e += NT) {
-      int t = e % B, sr = e / B;
-      if ((sr >> 4) & 1) continue;
-      int m, row;
-      if (!slot_row(s0 + (sr >> 4), sr & 15, m, row)) continue;
-      int j = GSM.mats[m].tag;
-      put_hilo(r, hr_at(p, l_layer) + (uint32_t)j * p.hr_stride, p.expert_ffn, t, row, GSM.out[sr][t] * RSM.wt[t][j]);
+    for_quarters(s0, s1, B, [&](int si, int sr0, int t, int m, int row0, int n) {
+      if (si & 1) return;  // up slots carry no output
+      const int j = GSM.mats[m].tag;
+      const float wj = RSM.wt[t][j];
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = GSM.out[sr0 + i][t] * wj;
+      put_hilo4(r, hr_at(p, l_layer) + (uint32_t)j * p.hr_stride, p.expert_ffn, t, row0, v, n);
+    });
+  };
+  if constexpr (!WIDE) {
+    if (route_after) {
+      const RouteIn in = gemv_phase(p, -1, p.H, ssq_at(p, 2 * l_layer + 1), EPI_BY_KIND, 0, 0, nullptr, 0, -1, true);
+      compute_routes(p, l_layer, in);
+      post(0, __builtin_amdgcn_readfirstlane(GSM.nslots));
+      return;
     }
+  }
+  gemv_passes(p, -1, p.H, ssq_at(p, 2 * l_layer + 1), [&](int s0, int s1) {
+    if (route_after && s0 == 0) {
+      RouteIn in;
+      route_load(p, in);
+      compute_routes(p, l_layer, in);
+    }
+    post(s0, s1);
   });
 }
 
@@ -3152,8 +3248,22 @@ __device__ __forceinline__ void run_one_phase(KParams& pk, int layer, int phase)
     case PH_GATEUP: phase_gateup(p, l_layer, -1); break;
     case PH_DOWN: phase_residual(p, l_layer, RES_DENSE_DOWN, g_next, -1); break;
     case PH_MOE_A: phase_moe_a(p, l_layer, -1); break;
-    case PH_MOE_B: prefetch_experts(p, l); compute_routes(p, l); phase_moe_b(p, l_layer, -1, false); break;
-    case PH_MOE_C: prefetch_experts(p, l); compute_routes(p, l); phase_residual(p, l_layer, RES_MOE_DOWN, g_next, -1); break;
+    case PH_MOE_B: {
+      prefetch_experts(p, l);
+      RouteIn in;
+      route_load(p, in);
+      compute_routes(p, l, in);
+      phase_moe_b(p, l_layer, false);
+      break;
+    }
+    case PH_MOE_C: {
+      prefetch_experts(p, l);
+      RouteIn in;
+      route_load(p, in);
+      compute_routes(p, l, in);
+      phase_residual(p, l_layer, RES_MOE_DOWN, g_next, -1);
+      break;
+    }
     case PH_KDA_PROJ: phase_kda_proj(p, l_layer, -1); break;
     case PH_KDA_REC: phase_kda_rec(p, l_layer, -1); break;
     case PH_KDA_O: phase_residual(p, l_layer, RES_KDA_O, L.ffn_norm, -1); break;
@@ -3248,25 +3358,18 @@ extern "C" __global__ __launch_bounds__(NT) void MD_KERNEL(Params p_arg) {
       ARRIVE();
     } else {
       phase_moe_a(p, l_layer, sidx++);
-      if (router_wgs(p) == 0) {
-        ARRIVE();
-      } else {
-        // nobody waits for phase A's whole grid: phase B needs the router
-        // logits only, and the down projection, which reads A's outputs,
-        // waits for phase B's arrivals (each made after this workgroup's A
-        // stores have completed).  Only the router workgroups arrive, on the
-        // extra line; the others go on without waiting for their stores.
-        stamp(p, 2 * sidx);
-        if ((int)blockIdx.x >= (int)gridDim.x - router_wgs(p)) arrive(p, sidx, true);
-      }
+      // no arrival, no wait: phase B validates the router logits' tags, and
+      // the down projection, which reads phase A's outputs, waits for phase
+      // B's arrivals (each made after this workgroup's A stores completed)
+      stamp(p, 2 * sidx);
+      enter_phase(p, sidx++);
       if (p.moe_all) {
-        phase_moe_b(p, l_layer, sidx++, true);
+        phase_moe_b(p, l_layer, true);
       } else {
-        pre_stamp(p, 5);
-        wait_router(p, sidx);
-        enter_phase(p, sidx++);
-        compute_routes(p, l);
-        phase_moe_b(p, l_layer, -1, false);
+        RouteIn in;
+        route_load(p, in);
+        compute_routes(p, l, in);
+        phase_moe_b(p, l_layer, false);
       }
       ARRIVE();
       phase_residual(p, l_layer, RES_MOE_DOWN, g_next, sidx++);

@@ -84,7 +84,7 @@ struct Params {
   uint32_t off_attn_ml; // attention partial (max, sum) fp32[MAXB][nq][C][2]
   uint32_t off_ou;    // hi/lo bf16[2][MAXB][nq*hd] per layer
   uint32_t off_h;     // hi/lo bf16[2][MAXB][F]           dense FFN hidden, per layer
-  uint32_t off_rl;    // fp32[MAXB][n_experts]             router logits
+  uint32_t off_rl;    // {f32, u32}[MAXB][n_experts]       router logits, each with its layer's tag
   uint32_t off_hs;    // hi/lo bf16[2][MAXB][shared_ffn]   shared expert hidden, per layer
   uint32_t off_hr;    // hi/lo bf16[nu][2][MAXB][expert_ffn] routed hidden (x routing weight), U order, per layer
   uint32_t hr_stride; // bytes per routed expert slot
@@ -111,6 +111,7 @@ struct Params {
   int trace_n;
   int moe_all;        // 1: the routed gate/up phase streams every expert (the step's tokens are expected to
                       // choose them all), so its stream starts before the routing is known
+  uint32_t step_seq;  // steps of this model enqueued before this one (router-logit tags)
 };
 
 }  // namespace md

@@ -2842,26 +2842,9 @@ __device__ __noinline__ void phase_residual(KParams& pk, int l_layer, int mode, 
     static_assert(WIDE || sizeof(GemvSmem::red) >= sizeof(float) * (NT + NW) * MAXB, "partial sums reuse the reduction scratch");
     float* part = (float*)GSM.red;  // [NT][MAXB]
     for (int t = 0; t < MAXB; ++t) part[threadIdx.x * MAXB + t] = 0.f;
-    // four consecutive rows of one token per thread (owned rows start on a
-    // multiple of 4): one 16-byte store of x and one 8-byte store per part of U
-    const int nq = (nrow + 3) >> 2;
-    for (int e = threadIdx.x; e < nq * B; e += NT) {
-      const int q = e % nq, t = e / nq, lr0 = 4 * q;
-      const int n = nrow - lr0 < 4 ? nrow - lr0 : 4;
-      float x[4], u[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[i] = i < n ? GSM.out[lr0 + i][t] : 0.f;
-        u[i] = i < n ? GSM.gain[lr0 + i] * x[i] : 0.f;
-      }
-      float* xp = p.x + t * H + r0 + lr0;
-      if (n == 4) {
-        *(f32x4*)xp = f32x4{x[0], x[1], x[2], x[3]};
-      } else {
-        for (int i = 0; i < n; ++i) xp[i] = x[i];
-      }
-      put_hilo4(r, u_next, H, t, r0 + lr0, u, n);
-      part[threadIdx.x * MAXB + t] += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+    for (int e = threadIdx.x; e < nrow * B; e += NT) {
+      int t = e % B, lr = e / B;
+      part[threadIdx.x * MAXB + t] += elem(t, lr);
     }
     store_ssq(p, r, part, ssq_at(p, nxt));
   }

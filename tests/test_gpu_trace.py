@@ -50,8 +50,8 @@ def test_traced_step_matches_and_stamps_are_ordered(torch_cuda, name, B, max_bat
     assert np.all(wends >= ends[:, :-1]), "a wait ended before this workgroup's own arrival"
     assert np.all(ends[:, 1:] >= wends), "a phase ended before its wait"
     # the last arrival of sync point s precedes every wait end on it (but
-    # after MoE phase A only the router workgroups arrive: the next phase
-    # waits for them alone)
+    # MoE phase A has no arrival: the next phase validates the router
+    # logits' tags instead of waiting)
     full = np.array([n != "moe_a" for n in names[:-1]])
     assert np.all(wends.min(axis=0)[full] >= ends[:, :-1].max(axis=0)[full])
     out, total = tr.summary(names)

@@ -98,12 +98,15 @@ __device__ __forceinline__ void set_err(KParams& pk, int code) {
 __device__ __forceinline__ unsigned class_members(int grp) { return (gridDim.x - grp + NGRP - 1) / NGRP; }
 
 // every wave: make this wave's stores complete, then the workgroup arrives
-// once.  The increment returns nothing, so nobody waits for it here.
+// once.  The increment returns nothing, so nobody waits for it here.  Wave 1
+// makes it: the next function entry waits for its completion in the issuing
+// wave, and wave 0 builds the next phase's tables right away.
+constexpr int ARRIVER = 64;
 __device__ void arrive(KParams& pk, int idx) {
   PARAMS;
   wait_stores();
   __builtin_amdgcn_s_barrier();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == ARRIVER) {
     unsigned* sp = sync_pt(p, idx);
     const int grp = blockIdx.x & (NGRP - 1);
     (void)__hip_atomic_fetch_add(sp + 32 * grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

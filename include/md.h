@@ -173,7 +173,11 @@ md_status md_init_model(const md_config* cfg, const void* const* weights, size_t
  *                chosen per layer and token, in descending router order
  * Token and position values live on the device and are checked there: an
  * out-of-range value sets the device error word (md_get_device_status) and
- * the step's outputs are undefined. */
+ * the step's outputs are undefined.  Each call alternates the model's bank
+ * of sync counters and advances its step counter (the tag of the router
+ * logits), both passed by value to the kernel: a HIP graph that captured
+ * this call would replay stale ones, so capture md_decode_step_noalloc,
+ * which clears what it relies on with kernels of its own. */
 md_status md_decode_step(md_model* m, const int32_t* tokens, const int32_t* positions, void* kv_cache,
                          float* out_logits, int32_t batch, int32_t* out_tokens, int32_t* out_expert_ids,
                          void* hip_stream);
@@ -186,9 +190,9 @@ md_status md_decode_step(md_model* m, const int32_t* tokens, const int32_t* posi
  * library's load until the process ends, instead of the model's workspace
  * (which still holds the layer table, expert pointers and rotary table
  * written by md_init_model).  The call allocates nothing and frees nothing;
- * it enqueues three small fill kernels (clearing the counters, error word and
- * zero line the step relies on: the array keeps whatever the last call on
- * this device left) and the megakernel.  Returns MD_ENOMEM, enqueuing
+ * it enqueues small fill kernels (clearing the counters, error word and zero
+ * line the step relies on, and for MoE models the tagged router logits: the
+ * array keeps whatever the last call on this device left) and the megakernel.  Returns MD_ENOMEM, enqueuing
  * nothing, when the model's step needs more scratch than the array holds
  * (md_workspace_bytes(cfg) > 128 MiB).  Every call on a device shares that
  * device's array: calls that overlap on one device (other streams, other

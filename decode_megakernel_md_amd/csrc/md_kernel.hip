@@ -1099,6 +1099,16 @@ __device__ __forceinline__ bool builder_done(KParams& pk, SlotBuilder& sb, int s
 
 
 // ===================================================================== phases
+// The weight-streaming phases.  8-row build: functions of their own (one copy
+// each, the stream function called from them).  64-row build: inlined into
+// the kernel, because as functions they must save every callee-saved vector
+// register they touch, which there goes to scratch memory (there are no free
+// accumulation registers to park them in) at every phase of every layer.
+#if MD_MAXB == 8
+#define MD_PHASE_FN __device__ __noinline__
+#else
+#define MD_PHASE_FN __device__ __forceinline__
+#endif
 
 // Write U[part][t][k] = hilo(v) for one element.
 __device__ __forceinline__ void put_hilo(rsrc_t r, uint32_t u_off, int K, int t, int k, float v) {
@@ -1347,7 +1357,7 @@ __device__ __forceinline__ void gemv_passes(KParams& pk, int wait_idx, int inv_n
 }
 
 // --- QKV projection (GQA): raw q, k, v (RMS-normalised input) -> qkv[t][row]
-__device__ __noinline__ void phase_qkv(KParams& pk, int l_layer, int wait_idx) {
+MD_PHASE_FN void phase_qkv(KParams& pk, int l_layer, int wait_idx) {
   PARAMS;
   KLayer& L = layer_ref(p, l_layer);
   const int B = p.B;
@@ -1836,7 +1846,7 @@ __device__ __forceinline__ void phase_attn_gqa(KParams& pk, int l_layer, int lay
 //   u = S^T k;  S <- alpha S + beta k (v - u)^T;  o = S^T q (updated S).
 // Projection phase: q, k, v and the two gate logits per head, one GEMV
 // over five matrices; kda[t] = [q (nh*dk) | k (nh*dk) | v (nh*dv) | a (nh) | b (nh)].
-__device__ __noinline__ void phase_kda_proj(KParams& pk, int l_layer, int wait_idx) {
+MD_PHASE_FN void phase_kda_proj(KParams& pk, int l_layer, int wait_idx) {
   PARAMS;
   KLayer& L = layer_ref(p, l_layer);
   const int B = p.B, nh = p.kda_h, dk = p.kda_dk, dv = p.kda_dv;
@@ -2125,7 +2135,7 @@ constexpr int MLA_KL = 512, MLA_RD = 64, MLA_QA = MLA_KL + MLA_RD, MLA_KS = MLA_
 // M1: c_q0 = W_qa xn (q_lora) and ckv = W_kva xn (kv_lora + rope).  c_q0 goes
 // out as U = hilo(g_q * c_q0) plus its partial sums of squares (the q norm),
 // ckv as fp32.
-__device__ __noinline__ void phase_mla_a(KParams& pk, int l_layer, int wait_idx) {
+MD_PHASE_FN void phase_mla_a(KParams& pk, int l_layer, int wait_idx) {
   PARAMS;
   KLayer& L = layer_ref(p, l_layer);
   const int B = p.B, QL = p.q_lora, KVR = MLA_QA;
@@ -2210,7 +2220,7 @@ __device__ void mla_cache_row(KParams& pk, int l_layer, int b) {
 
 // M2: q = W_qb RMSNorm(c_q0) (nh x (nope + rope)), and the new cache rows
 // (workgroup G-1-b writes sequence b's).
-__device__ __noinline__ void phase_mla_b(KParams& pk, int l_layer, int wait_idx) {
+MD_PHASE_FN void phase_mla_b(KParams& pk, int l_layer, int wait_idx) {
   PARAMS;
   KLayer& L = layer_ref(p, l_layer);
   const int B = p.B, nh = p.mla_h, QW = p.nope + MLA_RD;
@@ -2241,7 +2251,7 @@ __device__ __noinline__ void phase_mla_b(KParams& pk, int l_layer, int wait_idx)
 // Task (h, 128-column block of the latent); the tokens in tiles of 8 (one
 // tile up to 8 rows), so each slice of W_uk is read from memory once.  W_kvb is row-major [nh*(nope+v)][512]: head
 // h's rows are [W_uk,h (nope rows) | W_uv,h (v rows)].
-__device__ __noinline__ void phase_mla_absorb(KParams& pk, int l_layer, int wait_idx) {
+MD_PHASE_FN void phase_mla_absorb(KParams& pk, int l_layer, int wait_idx) {
   PARAMS;
   KLayer& L = layer_ref(p, l_layer);
   const int B = p.B, nh = p.mla_h, nope = p.nope, QW = nope + MLA_RD, VW = nope + p.vdim;
@@ -2784,7 +2794,7 @@ static_assert(ROUTE_OFF + sizeof(RouteSmem) <= PLAN_OFF, "LDS layout exceeds the
 // sum of squares of x.
 enum : int { RES_OPROJ = 0, RES_DENSE_DOWN = 1, RES_MOE_DOWN = 2, RES_MLA_O = 3, RES_KDA_O = 4 };
 
-__device__ __noinline__ void phase_residual(KParams& pk, int l_layer, int mode, const uint16_t* g_next, int wait_idx) {
+MD_PHASE_FN void phase_residual(KParams& pk, int l_layer, int mode, const uint16_t* g_next, int wait_idx) {
   PARAMS;
   KLayer& L = layer_ref(p, l_layer);
   const int B = p.B, H = p.H;
@@ -2854,7 +2864,7 @@ __device__ __noinline__ void phase_residual(KParams& pk, int l_layer, int mode, 
 }
 
 // --- dense SwiGLU gate/up: h = silu(inv*Wg U) * (inv*Wu U) -> hi/lo
-__device__ __noinline__ void phase_gateup(KParams& pk, int l_layer, int wait_idx) {
+MD_PHASE_FN void phase_gateup(KParams& pk, int l_layer, int wait_idx) {
   PARAMS;
   KLayer& L = layer_ref(p, l_layer);
   const int B = p.B, F = p.ffn;
@@ -2908,7 +2918,7 @@ __device__ __forceinline__ int router_wgs(KParams& pk) {
   return p.n_shared > 0 && (int)gridDim.x > 2 * rq ? rq : 0;
 }
 
-__device__ __noinline__ void phase_moe_a(KParams& pk, int l_layer, int wait_idx) {
+MD_PHASE_FN void phase_moe_a(KParams& pk, int l_layer, int wait_idx) {
   PARAMS;
   KLayer& L = layer_ref(p, l_layer);
   const int B = p.B;
@@ -3059,7 +3069,7 @@ __device__ __noinline__ void compute_routes(KParams& pk, int layer, RouteIn in) 
 // first weight loads (8-row build) and the routing runs after the stream,
 // before the outputs are scaled (experts no token chose get weight 0).
 // Otherwise the routing is done and the chosen experts' union is streamed.
-__device__ __noinline__ void phase_moe_b(KParams& pk, int l_layer, bool route_after) {
+MD_PHASE_FN void phase_moe_b(KParams& pk, int l_layer, bool route_after) {
   PARAMS;
   const int B = p.B;
   SlotBuilder sb;
@@ -3103,7 +3113,7 @@ __device__ __noinline__ void phase_moe_b(KParams& pk, int l_layer, bool route_af
 }
 
 // --- final norm + LM head: logits, per-WG argmax candidates
-__device__ __noinline__ void phase_lmhead(KParams& pk, int wait_idx) {
+MD_PHASE_FN void phase_lmhead(KParams& pk, int wait_idx) {
   PARAMS;
   const int B = p.B;
   SlotBuilder sb;
